@@ -1,0 +1,240 @@
+/*
+ * pkv.h -- C ABI of libpkv: PagedAttention decode on AMD Instinct MI355X (gfx950).
+ *
+ * Sources. The method is the one described on three web pages:
+ *   [P1] "vLLM 與 PagedAttention：高吞吐推理的關鍵" (blog-7wy.pages.dev)
+ *   [P2] vLLM overview, section "PagedAttention 的核心原理" (xiexianbin.cn)
+ *   [P3] "vLLM 与 PagedAttention：大模型高性能推理服务实战" (zhengtianqi.github.io)
+ * The pages describe the KV cache as fixed-size blocks of 16 tokens that sit anywhere in a
+ * shared pool, reached through a per-sequence block table, allocated on demand, freed when a
+ * request finishes, and shared between sequences with a common prefix or beam history.
+ * They give no attention formula, no memory layout and no kernel; where this header fixes one
+ * it says so ("our reading").
+ *
+ * Conventions shared by every call
+ *   - Every call returns a pkv_status (int32). No C++ exception crosses this boundary.
+ *   - Device calls take plain device pointers and a hipStream_t passed as `void* stream`
+ *     (NULL = the default stream). They only enqueue work: the status covers host-side argument
+ *     checks and launch errors, not the kernels' completion. They allocate no device memory:
+ *     the caller owns every device buffer (inputs, outputs, caches, tables, workspace).
+ *   - Arguments are validated on the host before any HIP call; on an error nothing is launched.
+ *   - Device-resident indices (slot mappings, block tables, context lengths) are not read by the
+ *     host on the fast path. Kernels treat them defensively so that no value can make them
+ *     access memory out of bounds: see each call. Setting the environment variable PKV_CHECK=1
+ *     makes the device calls copy those indices to the host (synchronously), validate them
+ *     against the contract and return PKV_ERR_INDEX before launching if they break it.
+ *   - All device pointers must be 16-byte aligned (PKV_ERR_INVALID_ARG otherwise).
+ *   - Token positions, logical blocks and slots are 0-based (our reading: [P1] numbers tokens
+ *     from 1 in one figure and logical blocks from 0 in the block-table example).
+ *
+ * Cache layout (our reading; the pages fix only the 16-token block, [P1] §二 "具體運作方式",
+ * [P3] §3.2). Let E = element bytes (4 for f32, 2 for f16/bf16), X = 16 / E (elements in one
+ * 16-byte chunk), bs = 16 tokens per block, hd = head_dim, Hkv = number of KV heads, NB =
+ * number of physical blocks in the pool. One (block, kv-head) pair owns one contiguous "tile"
+ * of bs*hd elements in each cache:
+ *   k_cache: [NB][Hkv][hd/X][bs][X]   element (b, h, token t, dim d) at
+ *            ((b*Hkv + h)*(hd/X) + d/X)*bs*X + t*X + d%X
+ *   v_cache: [NB][Hkv][hd][bs]        element (b, h, token t, dim d) at
+ *            ((b*Hkv + h)*hd + d)*bs + t
+ * i.e. K is stored as 16-byte chunks of consecutive dims, token-minor, and V is stored
+ * dim-major with the 16 tokens of a block contiguous. Both choices make every per-lane load of
+ * the attention kernels a single contiguous 8- or 16-byte access. Token t of a sequence lives
+ * in its logical block t/bs, at offset t%bs inside the physical block the table names.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pkv_status;
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, negative size, bad combination      */
+  PKV_ERR_UNSUPPORTED = 2,   /* head_dim not in {64,128}, block size != 16, unknown dtype     */
+  PKV_ERR_OUT_OF_BLOCKS = 3, /* allocator: pool exhausted; the allocator state is unchanged   */
+  PKV_ERR_UNKNOWN_SEQ = 4,   /* allocator: sequence id not present                           */
+  PKV_ERR_SEQ_EXISTS = 5,    /* allocator: sequence id already present                       */
+  PKV_ERR_WORKSPACE = 6,     /* workspace pointer null or smaller than required               */
+  PKV_ERR_INDEX = 7,         /* PKV_CHECK=1 found a device index outside the contract         */
+  PKV_ERR_HIP = 8            /* a HIP runtime call or a kernel launch failed                  */
+};
+
+typedef int32_t pkv_dtype;
+enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 };
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* pkv_status_string(pkv_status status);
+
+/* Bytes of ONE cache tensor (k_cache or v_cache) for a pool of NB blocks; 0 on bad arguments. */
+size_t pkv_cache_bytes(int32_t NB, int32_t Hkv, int32_t hd, int32_t bs, pkv_dtype dtype);
+
+/* ------------------------------------------------------------------------------------------ */
+/* Cache write.                                                                              */
+/* [P1] §三 步驟二/步驟三: the new tokens' K/V are computed and written into the current block */
+/* (a fresh block is taken when it is full). The slot of token i, slot = block*bs + offset,  */
+/* is chosen by the allocator (pkv_alloc_append); this call only scatters.                   */
+/*   k, v          device, [T][Hkv][hd] contiguous, dtype `dtype` (read)                     */
+/*   k_cache, v_cache  device, cache layout above, NB blocks (written at the given slots only) */
+/*   slot_mapping  device int32 [T]; token i goes to block slot/bs, offset slot%bs.          */
+/*                 slot < 0 (padding) and slot >= NB*bs are skipped, so no value can write   */
+/*                 outside the caches. Two tokens with the same slot in one call is a caller */
+/*                 error: which one lands is undefined.                                       */
+/* The copy is bitwise. T == 0 is a no-op. Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED,  */
+/* PKV_ERR_INDEX (PKV_CHECK=1: slot >= NB*bs or duplicate non-negative slots), PKV_ERR_HIP.   */
+pkv_status pkv_write(const void* k, const void* v, void* k_cache, void* v_cache,
+                     const int32_t* slot_mapping, int32_t T, int32_t Hkv, int32_t hd, int32_t bs,
+                     int32_t NB, pkv_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* Decode attention.                                                                         */
+/* [P1] §三 步驟三 (last step) and §五 ("Attention Kernel ... 用塊表計算注意力"); [P2]         */
+/* "PagedAttention 的核心原理": each sequence's KV is logically contiguous but physically     */
+/* scattered; attention is computed by finding all previous KV through the block table. The  */
+/* pages give no formula; ours is scaled dot-product attention over the n = context_lens[i]   */
+/* tokens of sequence i (the token just written included):                                    */
+/*   out[i,h,:] = sum_t softmax_t(scale * q[i,h,:] . K_i[t,g(h),:]) * V_i[t,g(h),:]           */
+/* with g(h) = h / (Hq/Hkv) (grouped-query heads: contiguous groups of G = Hq/Hkv q heads     */
+/* share one kv head; G = 1 is multi-head attention). A row with n = 0 gives out = 0.          */
+/* Arithmetic: products and sums in fp32, softmax with max subtraction, output rounded to     */
+/* `dtype` to nearest-even. The result for a sequence depends only on its logical K/V: not on */
+/* which physical blocks hold them, whether they are shared, or on other sequences.           */
+/*   out, q        device, [B][Hq][hd] contiguous, dtype `dtype` (out written, q read)         */
+/*   block_tables  device int32 [B][max_blocks]; entry j of row i names the physical block of */
+/*                 tokens [j*bs, (j+1)*bs) of sequence i. Only entries j < ceil(n_i/bs) are   */
+/*                 read. An entry outside [0, NB) is never dereferenced: its tokens are       */
+/*                 skipped (the output is then undefined but no memory fault can occur).      */
+/*   context_lens  device int32 [B]; values are clamped to [0, max_context_len] on the device.*/
+/*   max_context_len  host bound on every n_i; must satisfy max_context_len <= max_blocks*bs. */
+/*   scale         the softmax scale (1/sqrt(hd) in the usual model).                          */
+/*   workspace     device scratch of at least pkv_decode_workspace_bytes(...) bytes, caller    */
+/*                 owned; contents on entry are ignored. May be NULL only when that size is 0. */
+/* Supported: hd in {64,128}, bs == 16, Hq % Hkv == 0, dtype f32/f16/bf16.                     */
+/* Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_INDEX          */
+/* (PKV_CHECK=1: an entry j < ceil(n_i/bs) outside [0,NB), or n_i outside [0,max_context_len]),*/
+/* PKV_ERR_HIP.                                                                                */
+pkv_status pkv_decode_attn(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                           int32_t Hq, int32_t Hkv, int32_t hd, int32_t bs, int32_t NB,
+                           int32_t max_blocks, int32_t max_context_len, float scale,
+                           pkv_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Partition length P (tokens, a multiple of bs) that pkv_decode_attn uses for this shape.    */
+/* Returns 0 on bad arguments.                                                                */
+int32_t pkv_decode_partition_tokens(int32_t B, int32_t Hq, int32_t Hkv, int32_t hd,
+                                    int32_t max_context_len, pkv_dtype dtype);
+
+/* Workspace bytes needed by pkv_decode_attn for this shape (0 when one partition covers     */
+/* max_context_len and no partials are needed). Same arguments as above.                      */
+size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t hd,
+                                  int32_t max_context_len, pkv_dtype dtype);
+
+/* ---- The two passes pkv_decode_attn is made of, exported so they can be run and checked    */
+/* ---- on their own. pkv_decode_attn(...) == pkv_decode_partition(P) then, if max_context_len */
+/* ---- > P, pkv_decode_merge(P), with P = pkv_decode_partition_tokens(...).                  */
+/*                                                                                            */
+/* Split-context layout (our design; the pages do not discuss kernels). Sequence i is cut     */
+/* into np_i = ceil(n_i / P) partitions of P tokens (the last one shorter). Let               */
+/* MP = ceil(max_context_len / P). The workspace holds three fp32 arrays:                      */
+/*   m  [B][Hq][MP]      at byte offset 0                                                      */
+/*   l  [B][Hq][MP]      at byte offset A = round_up(B*Hq*MP*4, 256)                           */
+/*   o  [B][Hq][MP][hd]  at byte offset 2*A                                                    */
+/* and pkv_decode_partials_bytes(B,Hq,hd,max_context_len,P) = 2*A + B*Hq*MP*hd*4.               */
+/* For partition j of sequence i and q head h, over its tokens t (s_t = scale*q.k_t):           */
+/*   m = max_t s_t,  l = sum_t exp(s_t - m),  o[:] = sum_t exp(s_t - m) * v_t[:]   (natural log).*/
+size_t pkv_decode_partials_bytes(int32_t B, int32_t Hq, int32_t hd, int32_t max_context_len,
+                                 int32_t part_tokens);
+
+/* Pass 1. Sequences with n_i <= P are finished here: out rows written, no partials. Sequences */
+/* with n_i > P get (m, l, o) for each of their np_i partitions in `partials`; their out rows  */
+/* are not touched. part_tokens must be a positive multiple of bs; partials must hold          */
+/* pkv_decode_partials_bytes(...) bytes (it may be NULL if max_context_len <= part_tokens).     */
+pkv_status pkv_decode_partition(void* out, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                                int32_t hd, int32_t bs, int32_t NB, int32_t max_blocks,
+                                int32_t max_context_len, float scale, pkv_dtype dtype,
+                                int32_t part_tokens, void* partials, size_t partials_bytes,
+                                void* stream);
+
+/* Pass 2: log-sum-exp merge. For each sequence with n_i > P and each q head:                   */
+/*   M = max_j m_j,  w_j = exp(m_j - M),  out = sum_j w_j o_j / sum_j w_j l_j                   */
+/* (a partition with m = -inf has weight 0), rounded to `dtype`. Rows with n_i <= P are not     */
+/* touched. Same partials layout as above.                                                      */
+pkv_status pkv_decode_merge(void* out, const void* partials, size_t partials_bytes,
+                            const int32_t* context_lens, int32_t B, int32_t Hq, int32_t hd,
+                            int32_t max_context_len, pkv_dtype dtype, int32_t part_tokens,
+                            void* stream);
+
+/* Attention-kernel selection, process-wide: 0 = automatic (matrix-core kernel for f16/bf16   */
+/* with 2 <= G <= 16, vector kernel otherwise), 1 = always the vector kernel, 2 = matrix-core  */
+/* kernel where supported (f16/bf16, G <= 16). Both give results within the same tolerance;   */
+/* exists so the two can be measured on the same shape. Returns the previous value.            */
+int32_t pkv_set_attn_kernel(int32_t which);
+
+/* ------------------------------------------------------------------------------------------ */
+/* Host block allocator (no GPU). [P1] §三 步驟一..四 and §二 "解決三大問題"; [P2] "按需分配",  */
+/* "共享和复用". Opaque handle, not thread-safe (one per scheduler thread).                    */
+/* Conventions (our reading where the pages are silent):                                       */
+/*  - The free list is a FIFO queue. It starts as free_order[0..NB-1] (NULL = 0,1,...,NB-1).    */
+/*    Allocation pops from the front; a block whose refcount drops to 0 is pushed to the back. */
+/*  - A sequence has a length n and a list of ceil(n/bs) blocks. Appending one token at length */
+/*    n takes a new block iff n % bs == 0 ([P1] §三 步驟三: write into the current block if it  */
+/*    has room, otherwise allocate a new one and update the table).                            */
+/*  - Sharing: pkv_alloc_fork makes the child point at all of the parent's blocks and adds one */
+/*    to each block's refcount ([P1] §二, three tables pointing at the same physical blocks).  */
+/*  - Copy-on-write: appending into a partially filled last block whose refcount is > 1 first  */
+/*    moves the appending sequence to a fresh block and reports the pair (src, dst); the      */
+/*    caller copies the tile contents (both caches) from src to dst before writing. A token   */
+/*    written by one sequence is therefore never visible to another.                          */
+/*  - Free ([P1] §三 步驟四): the sequence's blocks are visited in logical order, each refcount */
+/*    is decremented, and each block reaching 0 is pushed to the back of the free list.       */
+/*  - Every operation is atomic: on any error the allocator is unchanged.                     */
+typedef struct pkv_allocator pkv_allocator;
+
+/* NB > 0, bs > 0. free_order: NULL or a permutation of 0..NB-1 (else PKV_ERR_INVALID_ARG). */
+pkv_status pkv_alloc_create(int32_t NB, int32_t bs, const int32_t* free_order,
+                            pkv_allocator** out);
+void pkv_alloc_destroy(pkv_allocator* a);
+
+/* New sequence with an empty block table ([P1] §三 步驟一). seq must not exist. */
+pkv_status pkv_alloc_add_seq(pkv_allocator* a, int64_t seq);
+
+/* Append ntok[k] >= 0 tokens to sequence seqs[k], k = 0..n-1 (distinct ids), in that order.   */
+/* slots_out (host, sum(ntok) entries, may be NULL) receives the slot of every new token, in   */
+/* argument order. cow_src/cow_dst (host, capacity n, may be NULL together with n_cow) receive */
+/* the copy-on-write pairs, *n_cow their count. PKV_ERR_OUT_OF_BLOCKS if the pool cannot hold  */
+/* the whole batch (checked before anything changes).                                          */
+pkv_status pkv_alloc_append(pkv_allocator* a, int32_t n, const int64_t* seqs, const int32_t* ntok,
+                            int32_t* slots_out, int32_t* cow_src, int32_t* cow_dst,
+                            int32_t* n_cow);
+
+/* child becomes a new sequence sharing every block (and the length) of parent. */
+pkv_status pkv_alloc_fork(pkv_allocator* a, int64_t parent, int64_t child);
+
+/* Release the sequence and its blocks ([P1] §三 步驟四). */
+pkv_status pkv_alloc_free(pkv_allocator* a, int64_t seq);
+
+/* Export block tables for seqs[0..n-1]: block_tables_out [n][max_blocks] (host int32, entries */
+/* past a sequence's block count set to -1) and context_lens_out [n] (host int32). A sequence  */
+/* with more than max_blocks blocks gives PKV_ERR_INVALID_ARG.                                 */
+pkv_status pkv_alloc_tables(const pkv_allocator* a, int32_t n, const int64_t* seqs,
+                            int32_t max_blocks, int32_t* block_tables_out,
+                            int32_t* context_lens_out);
+
+int32_t pkv_alloc_num_free(const pkv_allocator* a);            /* free blocks                */
+int32_t pkv_alloc_refcount(const pkv_allocator* a, int32_t block); /* -1 if out of range      */
+/* Length of a sequence in tokens, or -1 if unknown. */
+int64_t pkv_alloc_seq_len(const pkv_allocator* a, int64_t seq);
+/* Copies up to cap entries of the free list, front first, into out; returns the list length. */
+int32_t pkv_alloc_free_list(const pkv_allocator* a, int32_t* out, int32_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

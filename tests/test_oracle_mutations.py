@@ -1,0 +1,94 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that its pins catch them.
+
+Each case patches one oracle function with a wrong variant (a dropped scale, a wrong
+kv-head mapping, an off-by-one gather, a transposed tile, an unweighted merge, a LIFO free
+list, a missing copy-on-write) and runs an existing pin, which must then fail.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import allocator as AL
+from oracle import attention as A
+from oracle import layout as L
+from tests import test_oracle_allocator as TAL
+from tests import test_oracle_attention as TA
+
+
+def _fails(fn, *args):
+    with pytest.raises(AssertionError):
+        fn(*args)
+
+
+def test_dropped_scale_is_caught(monkeypatch):
+    orig = A._dense_attention_one
+    monkeypatch.setattr(A, "_dense_attention_one", lambda q, K, V, scale: orig(q, K, V, 1.0))
+    _fails(TA.test_matches_torch_sdpa, "f32", 2, 2)
+
+
+def test_wrong_gqa_head_mapping_is_caught(monkeypatch):
+    def bad(q, k_cache, v_cache, block_tables, context_lens, *, scale, hkv, hd, bs, dtype,
+            num_blocks=None):
+        qf = L.to_f64(q, dtype)
+        B, hq, _ = qf.shape
+        out = np.zeros((B, hq, hd))
+        nbk = np.asarray(k_cache).size // (hkv * hd * bs)
+        for i in range(B):
+            n = int(context_lens[i])
+            if n == 0:
+                continue
+            K, V = A.gather_sequence(k_cache, v_cache, block_tables[i], n, num_blocks=nbk,
+                                     hkv=hkv, hd=hd, bs=bs, dtype=dtype)
+            for h in range(hq):
+                g = h % hkv  # wrong: interleaved instead of contiguous groups
+                out[i, h] = A._dense_attention_one(qf[i, h], K[:, g], V[:, g], scale)
+        return out
+    monkeypatch.setattr(A, "decode_attention", bad)
+    _fails(TA.test_matches_torch_sdpa, "f32", 8, 2)
+
+
+def test_off_by_one_gather_is_caught(monkeypatch):
+    orig = A.gather_sequence
+
+    def short(k_cache, v_cache, row, n, **kw):
+        K, V = orig(k_cache, v_cache, row, n, **kw)
+        if n > 1:
+            K[-1], V[-1] = K[-2], V[-2]  # last token read from the wrong slot
+        return K, V
+    monkeypatch.setattr(A, "gather_sequence", short)
+    _fails(TA.test_hand_example)
+
+
+def test_transposed_tile_is_caught(monkeypatch):
+    def bad_k(k_cache, block, hkv, hd, bs, dtype):
+        x = L.chunk_elems(dtype)
+        tile = np.asarray(k_cache).reshape(-1, hkv, bs, hd // x, x)[block]  # token-major: wrong
+        return tile.transpose(1, 0, 2, 3).reshape(bs, hkv, hd)
+    monkeypatch.setattr(L, "k_tile_tokens", bad_k)
+    _fails(TA.test_layout_reading_matches_header_formula, "f16")
+
+
+def test_unweighted_merge_is_caught(monkeypatch):
+    def bad(m, l, o):
+        return np.asarray(o).sum(0) / np.asarray(l).sum()
+    monkeypatch.setattr(A, "merge_partials", bad)
+    _fails(TA.test_partition_merge_equals_unsplit, 32)
+
+
+def test_lifo_free_list_is_caught(monkeypatch):
+    orig_free = AL.BlockAllocator.free_seq
+
+    def lifo_free(self, seq):
+        before = list(self.free)
+        orig_free(self, seq)
+        new = list(self.free)[len(before):]
+        self.free = AL.deque(list(reversed(new)) + before)
+    monkeypatch.setattr(AL.BlockAllocator, "free_seq", lifo_free)
+    _fails(TAL.test_p1_shared_blocks_example)
+
+
+def test_missing_copy_on_write_is_caught(monkeypatch):
+    monkeypatch.setattr(AL.BlockAllocator, "_needs",
+                        lambda self, seq, ntok: (False, -(-(self.length[seq] + ntok) // self.bs)
+                                                 - -(-self.length[seq] // self.bs)))
+    _fails(TAL.test_copy_on_write_pair_reported)
