@@ -70,6 +70,11 @@ enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 };
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* pkv_status_string(pkv_status status);
 
+/* Detail of the most recent PKV_ERR_HIP returned on the calling thread: which launch or runtime
+ * call failed and the HIP error text. Thread-local storage owned by the library, valid until the
+ * thread's next failing call; "" if none. */
+const char* pkv_last_error(void);
+
 /* Bytes of ONE cache tensor (k_cache or v_cache) for a pool of NB blocks; 0 on bad arguments. */
 size_t pkv_cache_bytes(int32_t NB, int32_t Hkv, int32_t hd, int32_t bs, pkv_dtype dtype);
 

@@ -1,0 +1,13 @@
+"""PagedAttention decode on AMD Instinct MI355X (gfx950).
+
+The work runs in ``libpkv.so`` (hand-written HIP kernels and a C++ block allocator behind the
+C ABI in ``include/pkv.h``); this package only marshals arguments. Importing it fails if the
+library has not been built (``python paged_kv_cache_459_amd/build.py``): there is no fallback.
+"""
+
+from ._lib import BF16, F16, F32, STATUS, PkvError, lib  # noqa: F401
+from .api import (BLOCK_SIZE, BlockAllocator, alloc_caches, cache_bytes,  # noqa: F401
+                  cache_shapes, pkv_decode_attn, pkv_decode_merge, pkv_decode_partials_bytes,
+                  pkv_decode_partition, pkv_decode_partition_tokens,
+                  pkv_decode_workspace_bytes, pkv_dtype, pkv_set_attn_kernel, pkv_write,
+                  split_partials)

@@ -1,0 +1,270 @@
+"""Python binding of libpkv with the same call names as the C ABI.
+
+Argument marshalling only: tensors are checked for device, dtype and contiguity, turned into
+pointers, and handed to the library together with the current HIP stream. Every step of the
+computation runs in the library's kernels (or, for the allocator, its C++ code).
+"""
+
+import ctypes
+import math
+
+import numpy as np
+import torch
+
+from ._lib import BF16, F16, F32, check, lib
+
+BLOCK_SIZE = 16
+_TORCH_TO_PKV = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+_ELEM_BYTES = {F32: 4, F16: 2, BF16: 2}
+
+
+def pkv_dtype(t):
+    try:
+        return _TORCH_TO_PKV[t.dtype if isinstance(t, torch.Tensor) else t]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype if isinstance(t, torch.Tensor) else t}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def cache_shapes(num_blocks, num_kv_heads, head_dim, dtype):
+    """Shapes of the K and V caches in the library's layout (see include/pkv.h)."""
+    x = 16 // _ELEM_BYTES[pkv_dtype(dtype)]
+    return ((num_blocks, num_kv_heads, head_dim // x, BLOCK_SIZE, x),
+            (num_blocks, num_kv_heads, head_dim, BLOCK_SIZE))
+
+
+def alloc_caches(num_blocks, num_kv_heads, head_dim, dtype, device="cuda", fill=None):
+    ks, vs = cache_shapes(num_blocks, num_kv_heads, head_dim, dtype)
+    k = torch.empty(ks, dtype=dtype, device=device)
+    v = torch.empty(vs, dtype=dtype, device=device)
+    if fill is not None:
+        k.fill_(fill)
+        v.fill_(fill)
+    return k, v
+
+
+def cache_bytes(num_blocks, num_kv_heads, head_dim, dtype):
+    return int(lib.pkv_cache_bytes(num_blocks, num_kv_heads, head_dim, BLOCK_SIZE,
+                                   pkv_dtype(dtype)))
+
+
+def _num_blocks(k_cache, num_kv_heads, head_dim):
+    per = num_kv_heads * head_dim * BLOCK_SIZE
+    if k_cache.numel() % per:
+        raise ValueError("k_cache size is not a whole number of blocks")
+    return k_cache.numel() // per
+
+
+def pkv_write(k, v, k_cache, v_cache, slot_mapping):
+    """Scatter k, v [T, Hkv, hd] into the caches at slot_mapping [T] (int32)."""
+    for t, n in ((k, "k"), (v, "v"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, n, dtype=k.dtype, device=k.device)
+    _need(slot_mapping, "slot_mapping", dtype=torch.int32, device=k.device)
+    T, hkv, hd = k.shape
+    if v.shape != k.shape or slot_mapping.numel() != T:
+        raise ValueError("k, v and slot_mapping shapes disagree")
+    nb = _num_blocks(k_cache, hkv, hd)
+    check(lib.pkv_write(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), T,
+                        hkv, hd, BLOCK_SIZE, nb, pkv_dtype(k), _stream(k.device)), "pkv_write")
+
+
+def pkv_decode_partition_tokens(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                                dtype):
+    return int(lib.pkv_decode_partition_tokens(batch, num_q_heads, num_kv_heads, head_dim,
+                                               max_context_len, pkv_dtype(dtype)))
+
+
+def pkv_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                               dtype):
+    return int(lib.pkv_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
+                                              max_context_len, pkv_dtype(dtype)))
+
+
+def pkv_decode_partials_bytes(batch, num_q_heads, head_dim, max_context_len, part_tokens):
+    return int(lib.pkv_decode_partials_bytes(batch, num_q_heads, head_dim, max_context_len,
+                                             part_tokens))
+
+
+def _decode_args(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads, out):
+    _need(q, "q")
+    dev = q.device
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, n, dtype=q.dtype, device=dev)
+    _need(block_tables, "block_tables", dtype=torch.int32, device=dev)
+    _need(context_lens, "context_lens", dtype=torch.int32, device=dev)
+    B, hq, hd = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype=q.dtype, device=dev)
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables must be [B, max_blocks] and context_lens [B]")
+    nb = _num_blocks(k_cache, num_kv_heads, hd)
+    return out, B, hq, hd, nb, block_tables.shape[1]
+
+
+def pkv_decode_attn(q, k_cache, v_cache, block_tables, context_lens, *, num_kv_heads, scale,
+                    max_context_len, out=None, workspace=None):
+    """out [B, Hq, hd] = paged decode attention. Allocates the workspace if none is given."""
+    out, B, hq, hd, nb, mb = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
+                                          num_kv_heads, out)
+    need = pkv_decode_workspace_bytes(B, hq, num_kv_heads, hd, max_context_len, q.dtype)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check(lib.pkv_decode_attn(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                              _ptr(block_tables), _ptr(context_lens), B, hq, num_kv_heads, hd,
+                              BLOCK_SIZE, nb, mb, max_context_len, float(scale), pkv_dtype(q),
+                              _ptr(workspace), ws_bytes, _stream(q.device)), "pkv_decode_attn")
+    return out
+
+
+def pkv_decode_partition(q, k_cache, v_cache, block_tables, context_lens, *, num_kv_heads,
+                         scale, max_context_len, part_tokens, partials, out=None):
+    """Pass 1 of split-context decode (see include/pkv.h). Returns out."""
+    out, B, hq, hd, nb, mb = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
+                                          num_kv_heads, out)
+    pbytes = partials.numel() * partials.element_size() if partials is not None else 0
+    check(lib.pkv_decode_partition(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                   _ptr(block_tables), _ptr(context_lens), B, hq, num_kv_heads,
+                                   hd, BLOCK_SIZE, nb, mb, max_context_len, float(scale),
+                                   pkv_dtype(q), part_tokens, _ptr(partials), pbytes,
+                                   _stream(q.device)), "pkv_decode_partition")
+    return out
+
+
+def pkv_decode_merge(out, partials, context_lens, *, max_context_len, part_tokens):
+    """Pass 2 of split-context decode: log-sum-exp merge into out."""
+    _need(out, "out")
+    _need(partials, "partials", device=out.device)
+    _need(context_lens, "context_lens", dtype=torch.int32, device=out.device)
+    B, hq, hd = out.shape
+    check(lib.pkv_decode_merge(_ptr(out), _ptr(partials),
+                               partials.numel() * partials.element_size(), _ptr(context_lens), B,
+                               hq, hd, max_context_len, pkv_dtype(out), part_tokens,
+                               _stream(out.device)), "pkv_decode_merge")
+    return out
+
+
+def split_partials(partials, batch, num_q_heads, head_dim, max_context_len, part_tokens):
+    """Views (m [B,Hq,MP], l [B,Hq,MP], o [B,Hq,MP,hd]) of a float32 partials buffer."""
+    mp = max(1, math.ceil(max_context_len / part_tokens))
+    cells = batch * num_q_heads * mp
+    a = (cells * 4 + 255) // 256 * 256
+    f = partials.view(torch.uint8)
+    m = f[:cells * 4].view(torch.float32).view(batch, num_q_heads, mp)
+    l = f[a:a + cells * 4].view(torch.float32).view(batch, num_q_heads, mp)
+    o = f[2 * a:2 * a + cells * head_dim * 4].view(torch.float32).view(batch, num_q_heads, mp,
+                                                                       head_dim)
+    return m, l, o
+
+
+def pkv_set_attn_kernel(which):
+    """0 automatic, 1 vector kernel, 2 matrix-core kernel. Returns the previous choice."""
+    return int(lib.pkv_set_attn_kernel(int(which)))
+
+
+# -------------------------------------------------------------------------------------------
+class BlockAllocator:
+    """Host block allocator (C++), see include/pkv.h. Not thread-safe."""
+
+    def __init__(self, num_blocks, block_size=BLOCK_SIZE, free_order=None):
+        h = ctypes.c_void_p()
+        order = None
+        if free_order is not None:
+            self._order = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
+            order = self._order.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        check(lib.pkv_alloc_create(num_blocks, block_size, order, ctypes.byref(h)),
+              "pkv_alloc_create")
+        self._h = h
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self):
+        if self._h:
+            lib.pkv_alloc_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add_seq(self, seq):
+        check(lib.pkv_alloc_add_seq(self._h, int(seq)), "pkv_alloc_add_seq")
+
+    def append(self, seqs, ntok, want_slots=True, slots_out=None):
+        """Returns (slots int32 [sum ntok], cow pairs int32 [n_cow, 2])."""
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        ntok = np.ascontiguousarray(np.asarray(ntok, dtype=np.int32))
+        n = len(seqs)
+        total = int(ntok.sum()) if n else 0
+        if want_slots:
+            slots = slots_out if slots_out is not None else np.empty(total, np.int32)
+        src = np.empty(max(n, 1), np.int32)
+        dst = np.empty(max(n, 1), np.int32)
+        ncow = ctypes.c_int32(0)
+        pi32 = ctypes.POINTER(ctypes.c_int32)
+        check(lib.pkv_alloc_append(
+            self._h, n, seqs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+            ntok.ctypes.data_as(pi32),
+            slots.ctypes.data_as(pi32) if want_slots else None,
+            src.ctypes.data_as(pi32), dst.ctypes.data_as(pi32), ctypes.byref(ncow)),
+            "pkv_alloc_append")
+        k = ncow.value
+        cows = np.stack([src[:k], dst[:k]], axis=1) if k else np.zeros((0, 2), np.int32)
+        return (slots if want_slots else None), cows
+
+    def fork(self, parent, child):
+        check(lib.pkv_alloc_fork(self._h, int(parent), int(child)), "pkv_alloc_fork")
+
+    def free(self, seq):
+        check(lib.pkv_alloc_free(self._h, int(seq)), "pkv_alloc_free")
+
+    def tables(self, seqs, max_blocks, tables_out=None, lens_out=None):
+        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        n = len(seqs)
+        tables = tables_out if tables_out is not None else np.empty((n, max_blocks), np.int32)
+        lens = lens_out if lens_out is not None else np.empty(n, np.int32)
+        pi32 = ctypes.POINTER(ctypes.c_int32)
+        check(lib.pkv_alloc_tables(self._h, n, seqs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                   max_blocks, tables.ctypes.data_as(pi32),
+                                   lens.ctypes.data_as(pi32)), "pkv_alloc_tables")
+        return tables, lens
+
+    def num_free(self):
+        return int(lib.pkv_alloc_num_free(self._h))
+
+    def refcount(self, block):
+        return int(lib.pkv_alloc_refcount(self._h, int(block)))
+
+    def seq_len(self, seq):
+        return int(lib.pkv_alloc_seq_len(self._h, int(seq)))
+
+    def free_list(self):
+        n = int(lib.pkv_alloc_free_list(self._h, None, 0))
+        out = np.empty(max(n, 1), np.int32)
+        lib.pkv_alloc_free_list(self._h, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n)
+        return out[:n].tolist()
