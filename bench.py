@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged decode hot path on one MI355X.
+
+One step = one decode step of every sequence in the batch, through the whole path:
+  1. allocate on demand: the C++ allocator appends one token per sequence (a fresh block for
+     sequences whose last block is full) and returns the new tokens' slots;
+  2. export the block tables and lengths into pinned host buffers and copy them (with the
+     slots) to the device;
+  3. pkv_write: scatter the new tokens' K/V into their slots;
+  4. paged decode attention: the partition pass, then (for sequences longer than one
+     partition) the log-sum-exp merge -- the two passes pkv_decode_attn is made of.
+
+Prints one JSON line: the metric (KV-read GB/s over the timed steps), decode tokens/s per
+layer, the roofline figure of the partition kernel (algorithmic bytes / its mean duration,
+measured with HIP events on the launch stream) and the oracle's throughput on a bounded
+sample of the same workload on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--workload llama2_7b]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "paged decode attn: KV-read GB/s and % of HBM peak; decode tokens/s per layer"
+WORKLOADS = ("llama2_7b", "qwen25_7b", "prefix_shared", "long_context")
+DESC = {
+    "llama2_7b": "Llama-2-7B-shaped single layer decode: MHA 32 x 128, f16, batch 64, "
+                 "context U[128,2048], blocks scattered in a pool of 1.1x need",
+    "qwen25_7b": "Qwen2.5-7B-shaped GQA decode: 28 q / 4 kv x 128, bf16, batch 256, context "
+                 "lognormal(median 1024, sigma 1) clipped to [16,32768]",
+    "prefix_shared": "prefix-shared decode: 128 seqs share a 2000-token prefix (125 blocks, "
+                     "refcount 128) + private tails U[16,512], MHA 32 x 128, bf16",
+    "long_context": "long-context continuous-batching step: 8 seqs at 32768 + 120 at "
+                    "U[64,4096], GQA 32 q / 8 kv x 128, bf16",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama2_7b", choices=WORKLOADS)
+    ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 vector, 2 matrix-core")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="oracle time budget for the CPU baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for f in ("pkv_attn.hip", "pkv_kernels.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_459_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, digest):
+    """HBM traffic per partition-kernel launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"attn_partition_{workload}_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_digest") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Workload:
+    """Sequences held by the C++ allocator plus device caches filled with seeded values."""
+
+    def __init__(self, name, total_steps, torch, pkv, W):
+        self.name = name
+        shape = self.shape = W.SHAPES[name]
+        rng = W.rng_for(shape.seed)
+        lens = W.draw_lengths(shape, rng)  # lengths after the first step's token
+        self.B, self.Hq, self.Hkv, self.hd = shape.B, shape.Hq, shape.Hkv, shape.hd
+        self.dt = W.torch_dtype(shape.dtype)
+        self.eb = 4 if shape.dtype == "f32" else 2
+        nb = W.pool_blocks(lens)
+        grow_blocks = sum(W.blocks_for(n + total_steps) - W.blocks_for(n) for n in lens)
+        if nb - sum(W.blocks_for(n) for n in lens) < grow_blocks:
+            nb += grow_blocks  # keep the run inside the pool
+        self.NB = nb
+        order = rng.permutation(nb).astype(np.int32)
+        self.alloc = pkv.BlockAllocator(nb, 16, order)
+        self.seqs = np.arange(self.B, dtype=np.int64)
+        if name == "prefix_shared":
+            prefix = W.PREFIX_TOKENS
+            parent = 10_000_000
+            self.alloc.add_seq(parent)
+            self.alloc.append([parent], [prefix], want_slots=False)
+            for s in self.seqs:
+                self.alloc.fork(parent, int(s))
+            self.alloc.free(parent)  # the children keep the prefix blocks alive
+            self.alloc.append(self.seqs, lens - 1 - prefix, want_slots=False)
+        else:
+            for s in self.seqs:
+                self.alloc.add_seq(int(s))
+            self.alloc.append(self.seqs, lens - 1, want_slots=False)
+        self.max_ctx = int(lens.max()) + total_steps
+        self.max_blocks = -(-self.max_ctx // 16)
+        dev = "cuda"
+        self.k_cache, self.v_cache = pkv.alloc_caches(nb, self.Hkv, self.hd, self.dt, dev)
+        self.k_cache.view(-1).copy_(W.device_normal((self.k_cache.numel(),), shape.dtype, 7001))
+        self.v_cache.view(-1).copy_(W.device_normal((self.v_cache.numel(),), shape.dtype, 7002))
+        self.q = W.device_normal((self.B, self.Hq, self.hd), shape.dtype, 7003)
+        self.k_new = W.device_normal((self.B, self.Hkv, self.hd), shape.dtype, 7004)
+        self.v_new = W.device_normal((self.B, self.Hkv, self.hd), shape.dtype, 7005)
+        self.out = torch.empty_like(self.q)
+        pin = dict(dtype=torch.int32, pin_memory=True)
+        self.tables_pin = torch.empty((self.B, self.max_blocks), **pin)
+        self.lens_pin = torch.empty((self.B,), **pin)
+        self.slots_pin = torch.empty((self.B,), **pin)
+        self.tables_np = self.tables_pin.numpy()
+        self.lens_np = self.lens_pin.numpy()
+        self.slots_np = self.slots_pin.numpy()
+        self.tables_dev = torch.empty((self.B, self.max_blocks), dtype=torch.int32, device=dev)
+        self.lens_dev = torch.empty((self.B,), dtype=torch.int32, device=dev)
+        self.slots_dev = torch.empty((self.B,), dtype=torch.int32, device=dev)
+        self.ones = np.ones(self.B, np.int32)
+        self.P = pkv.pkv_decode_partition_tokens(self.B, self.Hq, self.Hkv, self.hd,
+                                                 self.max_ctx, self.dt)
+        nbytes = pkv.pkv_decode_partials_bytes(self.B, self.Hq, self.hd, self.max_ctx, self.P)
+        self.partials = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        self.copied = torch.cuda.Event()
+        self.copied.record()
+        self.scale = 1.0 / math.sqrt(self.hd)
+
+    def kv_bytes(self, lens):
+        return int(lens.astype(np.int64).sum()) * 2 * self.Hkv * self.hd * self.eb
+
+    def qo_bytes(self):
+        return 2 * self.B * self.Hq * self.hd * self.eb
+
+
+def run_step(wl, pkv, events=None):
+    """One decode step (see the module docstring). Returns the sum of context lengths."""
+    wl.copied.synchronize()  # the previous step's copies have left the pinned buffers
+    wl.alloc.append(wl.seqs, wl.ones, slots_out=wl.slots_np)  # 1. allocate on demand
+    wl.alloc.tables(wl.seqs, wl.max_blocks, tables_out=wl.tables_np, lens_out=wl.lens_np)
+    wl.tables_dev.copy_(wl.tables_pin, non_blocking=True)  # 2. tables to the device
+    wl.lens_dev.copy_(wl.lens_pin, non_blocking=True)
+    wl.slots_dev.copy_(wl.slots_pin, non_blocking=True)
+    wl.copied.record()
+    pkv.pkv_write(wl.k_new, wl.v_new, wl.k_cache, wl.v_cache, wl.slots_dev)  # 3. cache write
+    if events is not None:
+        events[0].record()
+    pkv.pkv_decode_partition(wl.q, wl.k_cache, wl.v_cache, wl.tables_dev, wl.lens_dev,
+                             num_kv_heads=wl.Hkv, scale=wl.scale, max_context_len=wl.max_ctx,
+                             part_tokens=wl.P, partials=wl.partials, out=wl.out)  # 4a
+    if events is not None:
+        events[1].record()
+    if wl.max_ctx > wl.P:
+        pkv.pkv_decode_merge(wl.out, wl.partials, wl.lens_dev, max_context_len=wl.max_ctx,
+                             part_tokens=wl.P)  # 4b
+    if events is not None:
+        events[2].record()
+    return wl.lens_np.copy()
+
+
+def cpu_baseline(wl, torch, W, seconds):
+    """The oracle (float64 NumPy, one thread) on a bounded, seeded sample of the sequences."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as OA
+    rng = np.random.default_rng(12345)
+    order = rng.permutation(wl.B)
+    spent, done, kv = 0.0, 0, 0
+    tables, lens = wl.tables_np.copy(), wl.lens_np.copy()
+    with threadpool_limits(limits=1):
+        for i in order:
+            n = int(lens[i])
+            nbk = -(-n // 16)
+            ids = torch.from_numpy(tables[i, :nbk].astype(np.int64)).cuda()
+            kc = W.to_storage_numpy(wl.k_cache.index_select(0, ids), wl.shape.dtype)
+            vc = W.to_storage_numpy(wl.v_cache.index_select(0, ids), wl.shape.dtype)
+            q = W.to_storage_numpy(wl.q[i:i + 1], wl.shape.dtype)
+            t0 = time.perf_counter()
+            OA.decode_attention(q, kc.reshape(-1), vc.reshape(-1),
+                                np.arange(nbk, dtype=np.int32)[None], np.int32([n]),
+                                scale=wl.scale, hkv=wl.Hkv, hd=wl.hd, bs=16,
+                                dtype=wl.shape.dtype)
+            spent += time.perf_counter() - t0
+            done += 1
+            kv += n * 2 * wl.Hkv * wl.hd * wl.eb
+            if spent >= seconds:
+                break
+    return {"value": round(kv / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {wl.B} sequences (seeded order), {kv / 1e6:.1f} MB of K/V, "
+                      f"{spent:.1f} s of oracle time, one thread",
+            "tokens_per_s_per_layer": round(done / spent, 3)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world})", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import paged_kv_cache_459_amd as pkv
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    pkv.pkv_set_attn_kernel(args.kernel)
+    wl = Workload(args.workload, args.warmup + args.steps, torch, pkv, W)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        run_step(wl, pkv)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    lens_per_step = []
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        lens_per_step.append(run_step(wl, pkv, evs[k]))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    part_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    merge_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    kv = [wl.kv_bytes(lens) for lens in lens_per_step]
+    algo = [b + wl.qo_bytes() for b in kv]
+    ms_per_step = wall / args.steps * 1e3
+    value = sum(kv) / wall / 1e9
+    achieved = sum(algo) / (sum(part_ms) / 1e3) / 1e9
+    digest = kernel_source_digest()
+    traffic = measured_traffic(args.workload, digest)
+
+    if args.copy_calibration:  # a plain copy of known size, for the counter runs
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.shape.dtype,
+        "data": "synthetic (seeded N(0,1) values, seeded lengths and block placement)",
+        "config": {
+            "workload": args.workload,
+            "description": DESC[args.workload],
+            "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.hd,
+            "block_size": 16, "pool_blocks": wl.NB, "partition_tokens": wl.P,
+            "mean_context_len": round(float(np.mean([l.mean() for l in lens_per_step])), 1),
+            "attn_kernel": ["auto", "vector", "matrix-core"][args.kernel],
+        },
+        "tokens_per_s_per_layer": round(wl.B / (ms_per_step / 1e3), 1),
+        "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4),
+        "attn_partition_ms": round(float(np.mean(part_ms)), 4),
+        "attn_merge_ms": round(float(np.mean(merge_ms)), 4),
+        "attn_kv_gbs": round(sum(kv) / (sum(part_ms) + sum(merge_ms)) * 1e3 / 1e9, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "attn partition pass (vector or matrix-core kernel)",
+            "algorithmic_bytes_per_launch": int(np.mean(algo)),
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, torch, W, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
