@@ -7,11 +7,12 @@ One step = one decode step of every sequence in the batch, through the whole pat
   2. export the block tables and lengths into pinned host buffers and copy them (with the
      slots) to the device;
   3. pkv_write: scatter the new tokens' K/V into their slots;
-  4. paged decode attention: the partition pass, then (for sequences longer than one
-     partition) the log-sum-exp merge -- the two passes pkv_decode_attn is made of.
+  4. paged decode attention: the stream pass (every wave streams an equal share of the
+     batch's K/V tiles), then the log-sum-exp merge of the segments cut between waves -- the
+     two passes pkv_decode_attn is made of.
 
 Prints one JSON line: the metric (KV-read GB/s over the timed steps), decode tokens/s per
-layer, the roofline figure of the partition kernel (algorithmic bytes / its mean duration,
+layer, the roofline figure of the stream kernel (algorithmic bytes / its mean duration,
 measured with HIP events on the launch stream) and the oracle's throughput on a bounded
 sample of the same workload on the host cores.
 
@@ -70,9 +71,9 @@ def kernel_source_digest():
 
 
 def measured_traffic(workload, digest):
-    """HBM traffic per partition-kernel launch from the committed counter summary, if it was
+    """HBM traffic per stream-kernel launch from the committed counter summary, if it was
     taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"attn_partition_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"attn_stream_{workload}_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -136,10 +137,11 @@ class Workload:
         self.lens_dev = torch.empty((self.B,), dtype=torch.int32, device=dev)
         self.slots_dev = torch.empty((self.B,), dtype=torch.int32, device=dev)
         self.ones = np.ones(self.B, np.int32)
-        self.P = pkv.pkv_decode_partition_tokens(self.B, self.Hq, self.Hkv, self.hd,
-                                                 self.max_ctx, self.dt)
-        nbytes = pkv.pkv_decode_partials_bytes(self.B, self.Hq, self.hd, self.max_ctx, self.P)
-        self.partials = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        self.kernel = pkv.pkv_decode_kernel(self.Hq, self.Hkv, self.dt)
+        self.W = pkv.pkv_decode_num_workers(self.Hq, self.Hkv, self.hd, self.dt)
+        nbytes = pkv.pkv_decode_stream_workspace_bytes(self.B, self.Hq, self.Hkv, self.hd,
+                                                       self.dt, self.W)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         self.copied = torch.cuda.Event()
         self.copied.record()
         self.scale = 1.0 / math.sqrt(self.hd)
@@ -163,14 +165,12 @@ def run_step(wl, pkv, events=None):
     pkv.pkv_write(wl.k_new, wl.v_new, wl.k_cache, wl.v_cache, wl.slots_dev)  # 3. cache write
     if events is not None:
         events[0].record()
-    pkv.pkv_decode_partition(wl.q, wl.k_cache, wl.v_cache, wl.tables_dev, wl.lens_dev,
-                             num_kv_heads=wl.Hkv, scale=wl.scale, max_context_len=wl.max_ctx,
-                             part_tokens=wl.P, partials=wl.partials, out=wl.out)  # 4a
+    pkv.pkv_decode_stream(wl.q, wl.k_cache, wl.v_cache, wl.tables_dev, wl.lens_dev,
+                          num_kv_heads=wl.Hkv, scale=wl.scale, max_context_len=wl.max_ctx,
+                          num_workers=wl.W, workspace=wl.workspace, out=wl.out)  # 4a
     if events is not None:
         events[1].record()
-    if wl.max_ctx > wl.P:
-        pkv.pkv_decode_merge(wl.out, wl.partials, wl.lens_dev, max_context_len=wl.max_ctx,
-                             part_tokens=wl.P)  # 4b
+    pkv.pkv_decode_merge(wl.out, wl.workspace, num_kv_heads=wl.Hkv, num_workers=wl.W)  # 4b
     if events is not None:
         events[2].record()
     return wl.lens_np.copy()
@@ -272,13 +272,13 @@ def main():
             "workload": args.workload,
             "description": DESC[args.workload],
             "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv, "head_dim": wl.hd,
-            "block_size": 16, "pool_blocks": wl.NB, "partition_tokens": wl.P,
+            "block_size": 16, "pool_blocks": wl.NB, "stream_workers": wl.W,
             "mean_context_len": round(float(np.mean([l.mean() for l in lens_per_step])), 1),
-            "attn_kernel": ["auto", "vector", "matrix-core"][args.kernel],
+            "attn_kernel": ["", "vector", "matrix-core"][wl.kernel],
         },
         "tokens_per_s_per_layer": round(wl.B / (ms_per_step / 1e3), 1),
         "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4),
-        "attn_partition_ms": round(float(np.mean(part_ms)), 4),
+        "attn_stream_ms": round(float(np.mean(part_ms)), 4),
         "attn_merge_ms": round(float(np.mean(merge_ms)), 4),
         "attn_kv_gbs": round(sum(kv) / (sum(part_ms) + sum(merge_ms)) * 1e3 / 1e9, 2),
         "roofline": {
@@ -288,7 +288,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "attn partition pass (vector or matrix-core kernel)",
+            "kernel": f"attention stream pass ({['', 'vector', 'matrix-core'][wl.kernel]} kernel)",
             "algorithmic_bytes_per_launch": int(np.mean(algo)),
         },
     }

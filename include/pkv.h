@@ -106,19 +106,25 @@ pkv_status pkv_write(const void* k, const void* v, void* k_cache, void* v_cache,
 /* with g(h) = h / (Hq/Hkv) (grouped-query heads: contiguous groups of G = Hq/Hkv q heads     */
 /* share one kv head; G = 1 is multi-head attention). A row with n = 0 gives out = 0.          */
 /* Arithmetic: products and sums in fp32, softmax with max subtraction, output rounded to     */
-/* `dtype` to nearest-even. The result for a sequence depends only on its logical K/V: not on */
-/* which physical blocks hold them, whether they are shared, or on other sequences.           */
+/* `dtype` to nearest-even. Results are deterministic: the same inputs give the same bits,    */
+/* and they do not change with which physical blocks hold the K/V or whether blocks are       */
+/* shared. The order of the fp32 sums of a row follows the batch's lengths (see the stream    */
+/* pass below), so a sequence's result can differ in rounding between batches of different   */
+/* lengths; it never depends on other sequences' values.                                      */
 /*   out, q        device, [B][Hq][hd] contiguous, dtype `dtype` (out written, q read)         */
 /*   block_tables  device int32 [B][max_blocks]; entry j of row i names the physical block of */
 /*                 tokens [j*bs, (j+1)*bs) of sequence i. Only entries j < ceil(n_i/bs) are   */
-/*                 read. An entry outside [0, NB) is never dereferenced: its tokens are       */
-/*                 skipped (the output is then undefined but no memory fault can occur).      */
+/*                 read. An entry outside [0, NB) is never dereferenced for data: its tokens  */
+/*                 are skipped (the output is then undefined but no memory fault can occur).  */
 /*   context_lens  device int32 [B]; values are clamped to [0, max_context_len] on the device.*/
 /*   max_context_len  host bound on every n_i; must satisfy max_context_len <= max_blocks*bs. */
 /*   scale         the softmax scale (1/sqrt(hd) in the usual model).                          */
 /*   workspace     device scratch of at least pkv_decode_workspace_bytes(...) bytes, caller    */
 /*                 owned; contents on entry are ignored. May be NULL only when that size is 0. */
-/* Supported: hd in {64,128}, bs == 16, Hq % Hkv == 0, dtype f32/f16/bf16.                     */
+/* Supported: hd in {64,128}, bs == 16, Hq % Hkv == 0, dtype f32/f16/bf16. Batches of more     */
+/* than 8192 sequences (or of more tiles than int32 positions allow) run as several            */
+/* stream+merge launches over consecutive row ranges, reusing the workspace in stream order.  */
+/* The launch size comes from the calling thread's current HIP device.                        */
 /* Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_INDEX          */
 /* (PKV_CHECK=1: an entry j < ceil(n_i/bs) outside [0,NB), or n_i outside [0,max_context_len]),*/
 /* PKV_ERR_HIP.                                                                                */
@@ -128,57 +134,70 @@ pkv_status pkv_decode_attn(void* out, const void* q, const void* k_cache, const 
                            int32_t max_blocks, int32_t max_context_len, float scale,
                            pkv_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Partition length P (tokens, a multiple of bs) that pkv_decode_attn uses for this shape.    */
-/* Returns 0 on bad arguments.                                                                */
-int32_t pkv_decode_partition_tokens(int32_t B, int32_t Hq, int32_t Hkv, int32_t hd,
-                                    int32_t max_context_len, pkv_dtype dtype);
-
-/* Workspace bytes needed by pkv_decode_attn for this shape (0 when one partition covers     */
-/* max_context_len and no partials are needed). Same arguments as above.                      */
+/* Workspace bytes pkv_decode_attn needs for this shape on the current device (0 if B == 0 or */
+/* the arguments are invalid).                                                                 */
 size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t hd,
                                   int32_t max_context_len, pkv_dtype dtype);
 
-/* ---- The two passes pkv_decode_attn is made of, exported so they can be run and checked    */
-/* ---- on their own. pkv_decode_attn(...) == pkv_decode_partition(P) then, if max_context_len */
-/* ---- > P, pkv_decode_merge(P), with P = pkv_decode_partition_tokens(...).                  */
+/* ---- The two passes pkv_decode_attn is made of, exported so they can be run, timed and     */
+/* ---- checked on their own: pkv_decode_attn(...) == pkv_decode_stream(W) then               */
+/* ---- pkv_decode_merge(W) with W = pkv_decode_num_workers(...), per sub-batch.             */
 /*                                                                                            */
-/* Split-context layout (our design; the pages do not discuss kernels). Sequence i is cut     */
-/* into np_i = ceil(n_i / P) partitions of P tokens (the last one shorter). Let               */
-/* MP = ceil(max_context_len / P). The workspace holds three fp32 arrays:                      */
-/*   m  [B][Hq][MP]      at byte offset 0                                                      */
-/*   l  [B][Hq][MP]      at byte offset A = round_up(B*Hq*MP*4, 256)                           */
-/*   o  [B][Hq][MP][hd]  at byte offset 2*A                                                    */
-/* and pkv_decode_partials_bytes(B,Hq,hd,max_context_len,P) = 2*A + B*Hq*MP*hd*4.               */
-/* For partition j of sequence i and q head h, over its tokens t (s_t = scale*q.k_t):           */
-/*   m = max_t s_t,  l = sum_t exp(s_t - m),  o[:] = sum_t exp(s_t - m) * v_t[:]   (natural log).*/
-size_t pkv_decode_partials_bytes(int32_t B, int32_t Hq, int32_t hd, int32_t max_context_len,
-                                 int32_t part_tokens);
+/* Stream layout (our design; the pages do not discuss kernels). Let c_i = ceil(n_i/16) (n_i   */
+/* clamped as above), S_i = c_0 + ... + c_{i-1}, C = S_B. Each sequence has H "head slots":    */
+/* H = Hq with GS = 1 q head per slot for the vector kernel, H = Hkv with GS = G q heads per   */
+/* slot (q heads s*G .. s*G+G-1) for the matrix-core kernel (pkv_decode_kernel says which).   */
+/* Segment (i, s) is the sequence's c_i blocks for slot s, placed at stream positions          */
+/* [s*C + S_i, s*C + S_i + c_i) of a stream of T = H*C positions (one 16-token block each).    */
+/* Worker w (a wave; w in [0, W)) takes positions [w*per, min(T, (w+1)*per)), per =            */
+/* ceil(T/W). A segment inside one worker's range is finished by the stream pass (its out     */
+/* rows written). Every worker holding part of a segment that crosses a range boundary writes */
+/* a "piece" for each of the GS q heads into cell (w, slot): slot = 1 if the segment starts   */
+/* after w*per, else 0. Over the piece's tokens t (those of the segment's positions in w's    */
+/* range that are < n_i), with s2_t = scale * log2(e) * (q . k_t) (base-2 units):             */
+/*   m = max_t s2_t,   l = sum_t 2^(s2_t - m),   o[:] = sum_t 2^(s2_t - m) v_t[:].             */
+/* Workspace, bytes (A = round_up(x, 256)):                                                    */
+/*   seg  int32 [B+1]           S_0..S_B                 at 0                                  */
+/*   ml   float [W][2][GS][2]   (m, l) of cell (w,slot)   at A(4*(B+1))                         */
+/*   o    float [W][2][GS][hd]  o of cell (w, slot)      after ml, at + A(W*2*GS*2*4)          */
+/* pkv_decode_stream_workspace_bytes gives the total. Cells of workers that hold no cut       */
+/* segment are not written.                                                                   */
 
-/* Pass 1. Sequences with n_i <= P are finished here: out rows written, no partials. Sequences */
-/* with n_i > P get (m, l, o) for each of their np_i partitions in `partials`; their out rows  */
-/* are not touched. part_tokens must be a positive multiple of bs; partials must hold          */
-/* pkv_decode_partials_bytes(...) bytes (it may be NULL if max_context_len <= part_tokens).     */
-pkv_status pkv_decode_partition(void* out, const void* q, const void* k_cache,
-                                const void* v_cache, const int32_t* block_tables,
-                                const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
-                                int32_t hd, int32_t bs, int32_t NB, int32_t max_blocks,
-                                int32_t max_context_len, float scale, pkv_dtype dtype,
-                                int32_t part_tokens, void* partials, size_t partials_bytes,
-                                void* stream);
+/* Which kernel the stream pass uses for this shape under the current setting: 1 = vector,    */
+/* 2 = matrix core; 0 on bad arguments.                                                       */
+int32_t pkv_decode_kernel(int32_t Hq, int32_t Hkv, pkv_dtype dtype);
 
-/* Pass 2: log-sum-exp merge. For each sequence with n_i > P and each q head:                   */
-/*   M = max_j m_j,  w_j = exp(m_j - M),  out = sum_j w_j o_j / sum_j w_j l_j                   */
-/* (a partition with m = -inf has weight 0), rounded to `dtype`. Rows with n_i <= P are not     */
-/* touched. Same partials layout as above.                                                      */
-pkv_status pkv_decode_merge(void* out, const void* partials, size_t partials_bytes,
-                            const int32_t* context_lens, int32_t B, int32_t Hq, int32_t hd,
-                            int32_t max_context_len, pkv_dtype dtype, int32_t part_tokens,
-                            void* stream);
+/* W that fills the current device once with that kernel (a multiple of 4); 0 on error.       */
+int32_t pkv_decode_num_workers(int32_t Hq, int32_t Hkv, int32_t hd, pkv_dtype dtype);
+
+/* Workspace bytes of the stream layout for W = num_workers (a positive multiple of 4).       */
+size_t pkv_decode_stream_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t hd,
+                                         pkv_dtype dtype, int32_t num_workers);
+
+/* Pass 1: writes seg, the out rows of every segment inside one worker's range and of every  */
+/* sequence with n_i = 0, and the pieces of cut segments. B <= 8192 and B*max_blocks*H + W    */
+/* < 2^31 (else PKV_ERR_UNSUPPORTED). Other arguments and errors as pkv_decode_attn.          */
+pkv_status pkv_decode_stream(void* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             int32_t B, int32_t Hq, int32_t Hkv, int32_t hd, int32_t bs,
+                             int32_t NB, int32_t max_blocks, int32_t max_context_len,
+                             float scale, pkv_dtype dtype, int32_t num_workers, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Pass 2: for every cut segment and each of its GS q heads, combines the pieces of workers   */
+/* w_first..w_last in worker order (log-sum-exp): M = max m_w, a_w = 2^(m_w - M),             */
+/* out = sum_w a_w o_w / sum_w a_w l_w (a piece with m = -inf has weight 0), rounded to        */
+/* `dtype`. Reads seg and the pieces from the workspace the stream pass filled (same B, heads, */
+/* dtype, num_workers and kernel setting); writes only the rows of cut segments.              */
+pkv_status pkv_decode_merge(void* out, const void* workspace, size_t workspace_bytes, int32_t B,
+                            int32_t Hq, int32_t Hkv, int32_t hd, pkv_dtype dtype,
+                            int32_t num_workers, void* stream);
 
 /* Attention-kernel selection, process-wide: 0 = automatic (matrix-core kernel for f16/bf16   */
 /* with 2 <= G <= 16, vector kernel otherwise), 1 = always the vector kernel, 2 = matrix-core  */
 /* kernel where supported (f16/bf16, G <= 16). Both give results within the same tolerance;   */
-/* exists so the two can be measured on the same shape. Returns the previous value.            */
+/* exists so the two can be measured on the same shape. Returns the previous value (-1 and no */
+/* change for an unknown value).                                                              */
 int32_t pkv_set_attn_kernel(int32_t which);
 
 /* ------------------------------------------------------------------------------------------ */

@@ -18,7 +18,7 @@ softmax (the formula is the textbook one; the pages do not print any):
 
 Grouped-query heads: q head h reads kv head h // (Hq // Hkv). A sequence with n = 0 gives a
 zero row. The split-context pieces (``partition_partials`` / ``merge_partials``) restate the
-same sums over fixed-length token ranges and the standard log-sum-exp recombination.
+same sums over token ranges and the standard log-sum-exp recombination.
 """
 
 import numpy as np
@@ -88,40 +88,58 @@ def decode_attention_rows(q, k_cache, v_cache, block_tables, context_lens, rows,
     return sub
 
 
+def range_partials(q, k_cache, v_cache, block_tables, context_lens, *, seq, lo, hi, scale, hkv,
+                   hd, bs, dtype, num_blocks=None):
+    """Softmax pieces of one sequence over its token range [lo, min(hi, n)).
+
+    For every q head h, over the range's tokens t (s_t = scale * q . k_t):
+        m = max_t s_t,   l = sum_t exp(s_t - m),   o = sum_t exp(s_t - m) v_t.
+    An empty range gives m = -inf, l = 0, o = 0. Returns (m [Hq], l [Hq], o [Hq, hd]) float64.
+    """
+    qf = to_f64(q, dtype)
+    hq = qf.shape[1]
+    G = hq // hkv
+    if num_blocks is None:
+        num_blocks = np.asarray(k_cache).size // (hkv * hd * bs)
+    n = int(context_lens[seq])
+    hi = min(int(hi), n)
+    m = np.full(hq, -np.inf)
+    l = np.zeros(hq)
+    o = np.zeros((hq, hd))
+    if hi <= lo:
+        return m, l, o
+    K, V = gather_sequence(k_cache, v_cache, block_tables[seq], n, num_blocks=num_blocks,
+                           hkv=hkv, hd=hd, bs=bs, dtype=dtype)
+    for h in range(hq):
+        g = h // G
+        s = scale * (K[lo:hi, g, :] @ qf[seq, h])
+        m[h] = s.max()
+        p = np.exp(s - m[h])
+        l[h] = p.sum()
+        o[h] = p @ V[lo:hi, g, :]
+    return m, l, o
+
+
 def partition_partials(q, k_cache, v_cache, block_tables, context_lens, *, scale, hkv, hd, bs,
                        dtype, part_tokens, num_blocks=None):
     """Per-partition softmax pieces for split-context decode.
 
     Sequence i is cut into ceil(n_i / P) consecutive token ranges of P = part_tokens tokens
-    (the last one shorter). For range j and q head h, over its tokens t:
-        m = max_t s_t,   l = sum_t exp(s_t - m),   o = sum_t exp(s_t - m) v_t.
+    (the last one shorter); each range's (m, l, o) is ``range_partials`` of it.
     Returns a list over sequences of (m [np, Hq], l [np, Hq], o [np, Hq, hd]) float64 arrays.
     """
-    qf = to_f64(q, dtype)
-    B, hq, _ = qf.shape
-    G = hq // hkv
-    if num_blocks is None:
-        num_blocks = np.asarray(k_cache).size // (hkv * hd * bs)
     res = []
-    for i in range(B):
+    for i in range(len(context_lens)):
         n = int(context_lens[i])
-        nparts = (n + part_tokens - 1) // part_tokens
-        m = np.full((nparts, hq), -np.inf)
-        l = np.zeros((nparts, hq))
-        o = np.zeros((nparts, hq, hd))
-        if n:
-            K, V = gather_sequence(k_cache, v_cache, block_tables[i], n, num_blocks=num_blocks,
-                                   hkv=hkv, hd=hd, bs=bs, dtype=dtype)
-            for j in range(nparts):
-                lo, hi = j * part_tokens, min(n, (j + 1) * part_tokens)
-                for h in range(hq):
-                    g = h // G
-                    s = scale * (K[lo:hi, g, :] @ qf[i, h])
-                    m[j, h] = s.max()
-                    p = np.exp(s - m[j, h])
-                    l[j, h] = p.sum()
-                    o[j, h] = p @ V[lo:hi, g, :]
-        res.append((m, l, o))
+        parts = [range_partials(q, k_cache, v_cache, block_tables, context_lens, seq=i,
+                                lo=j * part_tokens, hi=(j + 1) * part_tokens, scale=scale,
+                                hkv=hkv, hd=hd, bs=bs, dtype=dtype, num_blocks=num_blocks)
+                 for j in range((n + part_tokens - 1) // part_tokens)]
+        hq = np.asarray(q).shape[1]
+        if parts:
+            res.append(tuple(np.stack(x) for x in zip(*parts)))
+        else:
+            res.append((np.zeros((0, hq)), np.zeros((0, hq)), np.zeros((0, hq, hd))))
     return res
 
 

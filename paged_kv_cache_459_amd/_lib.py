@@ -52,13 +52,14 @@ SIGNATURES = {
                           c_vp]),
     "pkv_decode_attn": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                 c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp, c_sz, c_vp]),
-    "pkv_decode_partition_tokens": (c_i32, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pkv_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
-    "pkv_decode_partials_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
-    "pkv_decode_partition": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32,
-                                     c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_i32, c_vp,
-                                     c_sz, c_vp]),
-    "pkv_decode_merge": (c_i32, [c_vp, c_vp, c_sz, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+    "pkv_decode_kernel": (c_i32, [c_i32, c_i32, c_i32]),
+    "pkv_decode_num_workers": (c_i32, [c_i32, c_i32, c_i32, c_i32]),
+    "pkv_decode_stream_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "pkv_decode_stream": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
+                                  c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_i32, c_vp, c_sz,
+                                  c_vp]),
+    "pkv_decode_merge": (c_i32, [c_vp, c_vp, c_sz, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                  c_vp]),
     "pkv_set_attn_kernel": (c_i32, [c_i32]),
     "pkv_alloc_create": (c_i32, [c_i32, c_i32, P_i32, ctypes.POINTER(c_vp)]),

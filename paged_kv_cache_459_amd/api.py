@@ -88,21 +88,26 @@ def pkv_write(k, v, k_cache, v_cache, slot_mapping):
                         hkv, hd, BLOCK_SIZE, nb, pkv_dtype(k), _stream(k.device)), "pkv_write")
 
 
-def pkv_decode_partition_tokens(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                                dtype):
-    return int(lib.pkv_decode_partition_tokens(batch, num_q_heads, num_kv_heads, head_dim,
-                                               max_context_len, pkv_dtype(dtype)))
-
-
 def pkv_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,
                                dtype):
     return int(lib.pkv_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
                                               max_context_len, pkv_dtype(dtype)))
 
 
-def pkv_decode_partials_bytes(batch, num_q_heads, head_dim, max_context_len, part_tokens):
-    return int(lib.pkv_decode_partials_bytes(batch, num_q_heads, head_dim, max_context_len,
-                                             part_tokens))
+def pkv_decode_kernel(num_q_heads, num_kv_heads, dtype):
+    """1 if the stream pass runs the vector kernel for this shape, 2 the matrix-core one."""
+    return int(lib.pkv_decode_kernel(num_q_heads, num_kv_heads, pkv_dtype(dtype)))
+
+
+def pkv_decode_num_workers(num_q_heads, num_kv_heads, head_dim, dtype):
+    """Waves of the stream pass that fill the current device once (a multiple of 4)."""
+    return int(lib.pkv_decode_num_workers(num_q_heads, num_kv_heads, head_dim, pkv_dtype(dtype)))
+
+
+def pkv_decode_stream_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, dtype,
+                                      num_workers):
+    return int(lib.pkv_decode_stream_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
+                                                     pkv_dtype(dtype), num_workers))
 
 
 def _decode_args(q, k_cache, v_cache, block_tables, context_lens, num_kv_heads, out):
@@ -140,44 +145,45 @@ def pkv_decode_attn(q, k_cache, v_cache, block_tables, context_lens, *, num_kv_h
     return out
 
 
-def pkv_decode_partition(q, k_cache, v_cache, block_tables, context_lens, *, num_kv_heads,
-                         scale, max_context_len, part_tokens, partials, out=None):
-    """Pass 1 of split-context decode (see include/pkv.h). Returns out."""
+def pkv_decode_stream(q, k_cache, v_cache, block_tables, context_lens, *, num_kv_heads, scale,
+                      max_context_len, num_workers, workspace, out=None):
+    """Pass 1 of decode attention (see include/pkv.h). Returns out."""
     out, B, hq, hd, nb, mb = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
                                           num_kv_heads, out)
-    pbytes = partials.numel() * partials.element_size() if partials is not None else 0
-    check(lib.pkv_decode_partition(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                   _ptr(block_tables), _ptr(context_lens), B, hq, num_kv_heads,
-                                   hd, BLOCK_SIZE, nb, mb, max_context_len, float(scale),
-                                   pkv_dtype(q), part_tokens, _ptr(partials), pbytes,
-                                   _stream(q.device)), "pkv_decode_partition")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check(lib.pkv_decode_stream(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(block_tables), _ptr(context_lens), B, hq, num_kv_heads, hd,
+                                BLOCK_SIZE, nb, mb, max_context_len, float(scale), pkv_dtype(q),
+                                num_workers, _ptr(workspace), ws_bytes, _stream(q.device)),
+          "pkv_decode_stream")
     return out
 
 
-def pkv_decode_merge(out, partials, context_lens, *, max_context_len, part_tokens):
-    """Pass 2 of split-context decode: log-sum-exp merge into out."""
+def pkv_decode_merge(out, workspace, *, num_kv_heads, num_workers):
+    """Pass 2 of decode attention: log-sum-exp merge of the cut segments' pieces into out."""
     _need(out, "out")
-    _need(partials, "partials", device=out.device)
-    _need(context_lens, "context_lens", dtype=torch.int32, device=out.device)
+    _need(workspace, "workspace", device=out.device)
     B, hq, hd = out.shape
-    check(lib.pkv_decode_merge(_ptr(out), _ptr(partials),
-                               partials.numel() * partials.element_size(), _ptr(context_lens), B,
-                               hq, hd, max_context_len, pkv_dtype(out), part_tokens,
-                               _stream(out.device)), "pkv_decode_merge")
+    check(lib.pkv_decode_merge(_ptr(out), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), B, hq, num_kv_heads,
+                               hd, pkv_dtype(out), num_workers, _stream(out.device)),
+          "pkv_decode_merge")
     return out
 
 
-def split_partials(partials, batch, num_q_heads, head_dim, max_context_len, part_tokens):
-    """Views (m [B,Hq,MP], l [B,Hq,MP], o [B,Hq,MP,hd]) of a float32 partials buffer."""
-    mp = max(1, math.ceil(max_context_len / part_tokens))
-    cells = batch * num_q_heads * mp
-    a = (cells * 4 + 255) // 256 * 256
-    f = partials.view(torch.uint8)
-    m = f[:cells * 4].view(torch.float32).view(batch, num_q_heads, mp)
-    l = f[a:a + cells * 4].view(torch.float32).view(batch, num_q_heads, mp)
-    o = f[2 * a:2 * a + cells * head_dim * 4].view(torch.float32).view(batch, num_q_heads, mp,
-                                                                       head_dim)
-    return m, l, o
+def split_workspace(workspace, batch, num_q_heads, num_kv_heads, head_dim, num_workers, kernel):
+    """Views (seg int32 [B+1], ml float32 [W, 2, GS, 2], o float32 [W, 2, GS, hd]) of a stream
+    workspace, for the kernel the stream pass used (1 vector, 2 matrix core)."""
+    gs = num_q_heads // num_kv_heads if kernel == 2 else 1
+    cells = num_workers * 2 * gs
+    a0 = ((batch + 1) * 4 + 255) // 256 * 256
+    a1 = (cells * 2 * 4 + 255) // 256 * 256
+    f = workspace.view(torch.uint8)
+    seg = f[:(batch + 1) * 4].view(torch.int32)
+    ml = f[a0:a0 + cells * 2 * 4].view(torch.float32).view(num_workers, 2, gs, 2)
+    o = f[a0 + a1:a0 + a1 + cells * head_dim * 4].view(torch.float32).view(num_workers, 2, gs,
+                                                                           head_dim)
+    return seg, ml, o
 
 
 def pkv_set_attn_kernel(which):

@@ -1,4 +1,4 @@
-// C ABI of libpkv: argument validation, launch heuristics and the split-context plumbing.
+// C ABI of libpkv: argument validation, launch sizing and the stream/merge plumbing.
 // Every check runs on the host before any HIP call; kernels only ever see validated shapes.
 
 #include <hip/hip_runtime_api.h>
@@ -50,31 +50,40 @@ size_t round_up256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 int32_t ceil_div(int32_t a, int32_t b) { return (a + b - 1) / b; }
 
-// Partition length for pkv_decode_attn. Every partition of P tokens becomes one work-group of
-// four waves, so P trades parallelism (short partitions) against per-wave pipeline length and
-// merge traffic (long partitions).
-int32_t choose_partition(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx, pkv_dtype dt) {
-  (void)B;
-  (void)Hq;
-  (void)Hkv;
-  (void)dt;
-  (void)max_ctx;
-  return 512;
+constexpr int32_t kMaxBatch = 8192;  // sequences per stream launch (LDS holds B+1 prefix sums)
+
+// Waves of the stream pass on the current device: the kernel's occupancy at the largest
+// launch-time LDS, times the compute units. Independent of B, so one workspace size serves
+// every sub-batch of a call.
+int32_t device_workers(pkv_dtype dt, int32_t hd, int32_t kernel) {
+  return pkv::default_workers(dt, hd, kernel, kMaxBatch);
 }
 
-struct Split {
-  int32_t P, MP;
-  size_t bytes_ml, bytes;  // size of m (and l) region, rounded; total bytes
+int32_t current_kernel(pkv_dtype dt, int32_t Hq, int32_t Hkv) {
+  return pkv::select_kernel(dt, Hq / Hkv, g_kernel_choice.load());
+}
+
+struct Layout {
+  int32_t H, GS;          // head slots per sequence, q heads per slot
+  size_t seg, ml, bytes;  // byte offsets of the (m, l) and o arrays; total size
 };
 
-Split split_layout(int32_t B, int32_t Hq, int32_t hd, int32_t max_ctx, int32_t P) {
-  Split s{};
-  s.P = P;
-  s.MP = max_ctx > 0 ? ceil_div(max_ctx, P) : 1;
-  const size_t cells = static_cast<size_t>(B) * Hq * s.MP;
-  s.bytes_ml = round_up256(cells * sizeof(float));
-  s.bytes = 2 * s.bytes_ml + cells * hd * sizeof(float);
-  return s;
+Layout stream_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t hd, int32_t kernel,
+                     int32_t W) {
+  Layout L{};
+  L.H = kernel == pkv::kMatrix ? Hkv : Hq;
+  L.GS = kernel == pkv::kMatrix ? Hq / Hkv : 1;
+  const size_t cells = static_cast<size_t>(W) * 2 * L.GS;
+  L.seg = round_up256(static_cast<size_t>(B + 1) * sizeof(int32_t));
+  L.ml = L.seg + round_up256(cells * 2 * sizeof(float));
+  L.bytes = L.ml + cells * hd * sizeof(float);
+  return L;
+}
+
+// Tile positions of a launch stay in int32: T + W <= B * max_blocks * H + W < 2^31.
+bool stream_fits(int32_t B, int32_t max_blocks, int32_t H, int32_t W) {
+  return B <= kMaxBatch &&
+         static_cast<int64_t>(B) * max_blocks * H + W < (int64_t{1} << 31);
 }
 
 // Host-side validation of device indices (PKV_CHECK=1 only; synchronous).
@@ -127,11 +136,12 @@ pkv_status validate_decode(const void* out, const void* q, const void* k_cache,
   return PKV_OK;
 }
 
-pkv::AttnParams make_params(void* out, const void* q, const void* k_cache, const void* v_cache,
-                            const int32_t* block_tables, const int32_t* context_lens, int32_t B,
-                            int32_t Hq, int32_t Hkv, int32_t hd, int32_t NB, int32_t max_blocks,
-                            int32_t max_ctx, float scale, const Split& s, void* partials) {
-  pkv::AttnParams p{};
+pkv::StreamParams make_params(void* out, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                              int32_t hd, int32_t NB, int32_t max_blocks, int32_t max_ctx,
+                              float scale, int32_t W, const Layout& L, void* workspace) {
+  pkv::StreamParams p{};
   p.out = out;
   p.q = q;
   p.k_cache = k_cache;
@@ -146,45 +156,41 @@ pkv::AttnParams make_params(void* out, const void* q, const void* k_cache, const
   p.max_blocks = max_blocks;
   p.max_ctx = max_ctx;
   p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
-  p.part_tokens = s.P;
-  p.max_parts = s.MP;
-  if (partials && s.MP > 1) {
-    char* base = static_cast<char*>(partials);
-    p.ws_m = reinterpret_cast<float*>(base);
-    p.ws_l = reinterpret_cast<float*>(base + s.bytes_ml);
-    p.ws_o = reinterpret_cast<float*>(base + 2 * s.bytes_ml);
-  }
+  p.num_workers = W;
+  char* base = static_cast<char*>(workspace);
+  p.ws_seg = reinterpret_cast<int32_t*>(base);
+  p.ws_ml = reinterpret_cast<float*>(base + L.seg);
+  p.ws_o = reinterpret_cast<float*>(base + L.ml);
   return p;
 }
 
-pkv_status partition_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
-                          const int32_t* block_tables, const int32_t* context_lens, int32_t B,
-                          int32_t Hq, int32_t Hkv, int32_t hd, int32_t bs, int32_t NB,
-                          int32_t max_blocks, int32_t max_ctx, float scale, pkv_dtype dtype,
-                          int32_t P, void* partials, size_t partials_bytes, void* stream,
-                          bool merge_after) {
+// One stream pass (and, if asked, its merge) over B <= kMaxBatch sequences.
+pkv_status stream_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                       int32_t Hq, int32_t Hkv, int32_t hd, int32_t bs, int32_t NB,
+                       int32_t max_blocks, int32_t max_ctx, float scale, pkv_dtype dtype,
+                       int32_t W, void* workspace, size_t workspace_bytes, void* stream,
+                       bool merge_after) {
   pkv_status st = validate_decode(out, q, k_cache, v_cache, block_tables, context_lens, B, Hq,
                                   Hkv, hd, bs, NB, max_blocks, max_ctx, scale, dtype);
   if (st != PKV_OK) return st;
-  if (P <= 0 || P % kBlockSize != 0 || P > kBlockSize * pkv::kMaxPartBlocks)
-    return PKV_ERR_INVALID_ARG;
-  const Split s = split_layout(B, Hq, hd, max_ctx, P);
-  if (s.MP > 65535) return PKV_ERR_INVALID_ARG;
+  if (W <= 0 || W % pkv::kWaves != 0) return PKV_ERR_INVALID_ARG;
+  const int32_t kernel = current_kernel(dtype, Hq, Hkv);
+  const Layout L = stream_layout(B, Hq, Hkv, hd, kernel, W);
+  if (!stream_fits(B, max_blocks, L.H, W)) return PKV_ERR_UNSUPPORTED;
   if (B == 0) return PKV_OK;
-  if (s.MP > 1 && (!partials || partials_bytes < s.bytes)) return PKV_ERR_WORKSPACE;
-  if (partials && !aligned16(partials)) return PKV_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < L.bytes) return PKV_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PKV_ERR_INVALID_ARG;
   auto hs = static_cast<hipStream_t>(stream);
   if (check_mode()) {
     st = check_decode_indices(block_tables, context_lens, B, NB, max_blocks, max_ctx, hs);
     if (st != PKV_OK) return st;
   }
-  const pkv::AttnParams p = make_params(out, q, k_cache, v_cache, block_tables, context_lens, B,
-                                        Hq, Hkv, hd, NB, max_blocks, max_ctx, scale, s, partials);
-  const int32_t kernel = pkv::select_kernel(dtype, Hq / Hkv, g_kernel_choice.load());
-  if (pkv::launch_partition(p, dtype, kernel, hs) != hipSuccess) return PKV_ERR_HIP;
-  if (merge_after && s.MP > 1) {
-    if (pkv::launch_merge(p, dtype, hs) != hipSuccess) return PKV_ERR_HIP;
-  }
+  const pkv::StreamParams p = make_params(out, q, k_cache, v_cache, block_tables, context_lens,
+                                          B, Hq, Hkv, hd, NB, max_blocks, max_ctx, scale, W, L,
+                                          workspace);
+  if (pkv::launch_stream(p, dtype, kernel, hs) != hipSuccess) return PKV_ERR_HIP;
+  if (merge_after && pkv::launch_merge(p, dtype, kernel, hs) != hipSuccess) return PKV_ERR_HIP;
   return PKV_OK;
 }
 
@@ -239,26 +245,30 @@ pkv_status pkv_write(const void* k, const void* v, void* k_cache, void* v_cache,
   return pkv::launch_write(p, dtype, hs) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
-int32_t pkv_decode_partition_tokens(int32_t B, int32_t Hq, int32_t Hkv, int32_t hd,
-                                    int32_t max_context_len, pkv_dtype dtype) {
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || !head_dim_ok(hd) || max_context_len < 0 ||
-      !dtype_ok(dtype))
-    return 0;
-  return choose_partition(B, Hq, Hkv, max_context_len, dtype);
+int32_t pkv_decode_kernel(int32_t Hq, int32_t Hkv, pkv_dtype dtype) {
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || !dtype_ok(dtype)) return 0;
+  return current_kernel(dtype, Hq, Hkv);
 }
 
-size_t pkv_decode_partials_bytes(int32_t B, int32_t Hq, int32_t hd, int32_t max_context_len,
-                                 int32_t part_tokens) {
-  if (B < 0 || Hq <= 0 || hd <= 0 || max_context_len < 0 || part_tokens <= 0) return 0;
-  const Split s = split_layout(B, Hq, hd, max_context_len, part_tokens);
-  return s.MP > 1 ? s.bytes : 0;
+int32_t pkv_decode_num_workers(int32_t Hq, int32_t Hkv, int32_t hd, pkv_dtype dtype) {
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || !dtype_ok(dtype) || !head_dim_ok(hd)) return 0;
+  return device_workers(dtype, hd, current_kernel(dtype, Hq, Hkv));
+}
+
+size_t pkv_decode_stream_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t hd,
+                                         pkv_dtype dtype, int32_t num_workers) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || !dtype_ok(dtype) || !head_dim_ok(hd) ||
+      num_workers <= 0 || num_workers % pkv::kWaves != 0)
+    return 0;
+  return stream_layout(B, Hq, Hkv, hd, current_kernel(dtype, Hq, Hkv), num_workers).bytes;
 }
 
 size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t hd,
                                   int32_t max_context_len, pkv_dtype dtype) {
-  const int32_t P = pkv_decode_partition_tokens(B, Hq, Hkv, hd, max_context_len, dtype);
-  if (P == 0) return 0;
-  return pkv_decode_partials_bytes(B, Hq, hd, max_context_len, P);
+  if (B <= 0 || max_context_len < 0) return 0;
+  const int32_t W = pkv_decode_num_workers(Hq, Hkv, hd, dtype);
+  if (W == 0) return 0;
+  return pkv_decode_stream_workspace_bytes(B < kMaxBatch ? B : kMaxBatch, Hq, Hkv, hd, dtype, W);
 }
 
 pkv_status pkv_decode_attn(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -267,51 +277,62 @@ pkv_status pkv_decode_attn(void* out, const void* q, const void* k_cache, const 
                            int32_t max_blocks, int32_t max_context_len, float scale,
                            pkv_dtype dtype, void* workspace, size_t workspace_bytes,
                            void* stream) {
-  if (!dtype_ok(dtype) || !head_dim_ok(hd)) return PKV_ERR_UNSUPPORTED;
-  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || max_context_len < 0 || B < 0) return PKV_ERR_INVALID_ARG;
-  const int32_t P = choose_partition(B, Hq, Hkv, max_context_len, dtype);
-  return partition_impl(out, q, k_cache, v_cache, block_tables, context_lens, B, Hq, Hkv, hd, bs,
-                        NB, max_blocks, max_context_len, scale, dtype, P, workspace,
-                        workspace_bytes, stream, /*merge_after=*/true);
-}
-
-pkv_status pkv_decode_partition(void* out, const void* q, const void* k_cache,
-                                const void* v_cache, const int32_t* block_tables,
-                                const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
-                                int32_t hd, int32_t bs, int32_t NB, int32_t max_blocks,
-                                int32_t max_context_len, float scale, pkv_dtype dtype,
-                                int32_t part_tokens, void* partials, size_t partials_bytes,
-                                void* stream) {
-  return partition_impl(out, q, k_cache, v_cache, block_tables, context_lens, B, Hq, Hkv, hd, bs,
-                        NB, max_blocks, max_context_len, scale, dtype, part_tokens, partials,
-                        partials_bytes, stream, /*merge_after=*/false);
-}
-
-pkv_status pkv_decode_merge(void* out, const void* partials, size_t partials_bytes,
-                            const int32_t* context_lens, int32_t B, int32_t Hq, int32_t hd,
-                            int32_t max_context_len, pkv_dtype dtype, int32_t part_tokens,
-                            void* stream) {
-  if (!dtype_ok(dtype) || !head_dim_ok(hd)) return PKV_ERR_UNSUPPORTED;
-  if (B < 0 || Hq <= 0 || Hq > 65535 || max_context_len < 0 || part_tokens <= 0 ||
-      part_tokens % kBlockSize)
-    return PKV_ERR_INVALID_ARG;
-  const Split s = split_layout(B, Hq, hd, max_context_len, part_tokens);
-  if (B == 0 || s.MP <= 1) return PKV_OK;  // nothing was split
-  if (!out || !context_lens || !aligned16(out) || (reinterpret_cast<uintptr_t>(context_lens) & 3u))
-    return PKV_ERR_INVALID_ARG;
-  if (!partials || partials_bytes < s.bytes) return PKV_ERR_WORKSPACE;
-  if (!aligned16(partials)) return PKV_ERR_INVALID_ARG;
-  auto hs = static_cast<hipStream_t>(stream);
-  if (check_mode()) {
-    std::vector<int32_t> l;
-    if (!copy_to_host(&l, context_lens, B, hs)) return PKV_ERR_HIP;
-    for (int32_t x : l)
-      if (x < 0 || x > max_context_len) return PKV_ERR_INDEX;
+  pkv_status st = validate_decode(out, q, k_cache, v_cache, block_tables, context_lens, B, Hq,
+                                  Hkv, hd, bs, NB, max_blocks, max_context_len, scale, dtype);
+  if (st != PKV_OK || B == 0) return st;
+  const int32_t W = pkv_decode_num_workers(Hq, Hkv, hd, dtype);
+  if (W == 0) {
+    (void)pkv::note_error("device occupancy query", hipErrorInvalidDevice);
+    return PKV_ERR_HIP;
   }
-  const pkv::AttnParams p = make_params(out, nullptr, nullptr, nullptr, nullptr, context_lens, B,
-                                        Hq, Hq, hd, 1, 1, max_context_len, 1.0f, s,
-                                        const_cast<void*>(partials));
-  return pkv::launch_merge(p, dtype, hs) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+  const Layout L = stream_layout(1, Hq, Hkv, hd, current_kernel(dtype, Hq, Hkv), W);
+  // Sub-batches: at most kMaxBatch sequences, and few enough tiles for int32 positions.
+  int32_t chunk = B < kMaxBatch ? B : kMaxBatch;
+  while (chunk > 0 && !stream_fits(chunk, max_blocks, L.H, W)) chunk /= 2;
+  if (chunk == 0) return PKV_ERR_UNSUPPORTED;
+  const size_t row_bytes = static_cast<size_t>(Hq) * hd * elem_bytes(dtype);
+  for (int32_t i0 = 0; i0 < B; i0 += chunk) {
+    const int32_t n = B - i0 < chunk ? B - i0 : chunk;
+    st = stream_impl(static_cast<char*>(out) + i0 * row_bytes,
+                     static_cast<const char*>(q) + i0 * row_bytes, k_cache, v_cache,
+                     block_tables + static_cast<size_t>(i0) * max_blocks, context_lens + i0, n,
+                     Hq, Hkv, hd, bs, NB, max_blocks, max_context_len, scale, dtype, W,
+                     workspace, workspace_bytes, stream, /*merge_after=*/true);
+    if (st != PKV_OK) return st;
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_decode_stream(void* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             int32_t B, int32_t Hq, int32_t Hkv, int32_t hd, int32_t bs,
+                             int32_t NB, int32_t max_blocks, int32_t max_context_len,
+                             float scale, pkv_dtype dtype, int32_t num_workers, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return stream_impl(out, q, k_cache, v_cache, block_tables, context_lens, B, Hq, Hkv, hd, bs,
+                     NB, max_blocks, max_context_len, scale, dtype, num_workers, workspace,
+                     workspace_bytes, stream, /*merge_after=*/false);
+}
+
+pkv_status pkv_decode_merge(void* out, const void* workspace, size_t workspace_bytes, int32_t B,
+                            int32_t Hq, int32_t Hkv, int32_t hd, pkv_dtype dtype,
+                            int32_t num_workers, void* stream) {
+  if (!dtype_ok(dtype) || !head_dim_ok(hd)) return PKV_ERR_UNSUPPORTED;
+  if (B < 0 || B > kMaxBatch || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Hq > 65535 ||
+      num_workers <= 0 || num_workers % pkv::kWaves != 0)
+    return PKV_ERR_INVALID_ARG;
+  if (B == 0) return PKV_OK;
+  if (!out || !aligned16(out)) return PKV_ERR_INVALID_ARG;
+  const int32_t kernel = current_kernel(dtype, Hq, Hkv);
+  const Layout L = stream_layout(B, Hq, Hkv, hd, kernel, num_workers);
+  if (!workspace || workspace_bytes < L.bytes) return PKV_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PKV_ERR_INVALID_ARG;
+  const pkv::StreamParams p = make_params(out, nullptr, nullptr, nullptr, nullptr, nullptr, B,
+                                          Hq, Hkv, hd, 1, 1, 0, 1.0f, num_workers, L,
+                                          const_cast<void*>(workspace));
+  return pkv::launch_merge(p, dtype, kernel, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PKV_OK
+             : PKV_ERR_HIP;
 }
 
 int32_t pkv_set_attn_kernel(int32_t which) {

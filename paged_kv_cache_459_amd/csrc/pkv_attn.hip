@@ -6,19 +6,38 @@
 // The formula (scaled dot product, max-subtracted softmax, fp32 accumulation) is the library's
 // documented contract; the pages give none.
 //
-// Work decomposition (our design). A work-group of NW waves owns one (sequence, head,
-// partition): the partition's P tokens are P/16 blocks, dealt round-robin to the waves. Each
-// wave streams whole (block, kv-head) tiles from HBM with coalesced 16-byte (8-byte for the
-// matrix-core V operand) loads, the next tile in flight while the current one is consumed,
-// and keeps an online-softmax state. The waves' states are merged through LDS in a fixed
-// order, so results never depend on timing or on physical placement. A sequence that fits in
-// one partition is finished here; longer ones leave (m, l, o) partials for merge_kernel.
+// Work decomposition (our design: balanced token streams). A "segment" is the K/V one
+// attention row reads: (sequence i, head slot h) with c_i = ceil(n_i/16) blocks, where the
+// head slot is a q head (vector kernel) or a kv head with its G q heads (matrix-core kernel).
+// All segments of the batch are laid end to end, in head-major order, as one sequence of
+// T = H * sum_i c_i (block, head) tiles. A persistent grid of W waves ("workers") cuts that
+// sequence into W equal contiguous ranges of per = ceil(T/W) tiles, so every wave streams the
+// same number of bytes however ragged the lengths are, and no work-group is launched empty.
+// A segment that lies inside one range is finished by its wave (output row written); a
+// segment cut by range boundaries leaves one (m, l, o) piece per wave that touched it, and
+// merge_kernel combines the pieces in wave order. Every result depends only on the batch's
+// lengths and contents, never on timing; placement and sharing of blocks do not change it.
 //
-// Scores are kept in base-2 units (scale folded with log2 e) so that every exponential is one
-// v_exp_f32. Masked tokens (past the sequence end inside its last block) are *selected* out:
-// score -inf and V element 0, never multiplied by zero, so NaN in unused slots cannot leak.
+// Work-groups are mapped so that each XCD (work-groups go round-robin over the 8 XCDs) owns a
+// contiguous eighth of the tile sequence: with head-major order an XCD's L2 sees the tiles of
+// a few heads only, so blocks shared between sequences (common prefixes, beams) are re-read
+// from that L2 instead of HBM.
+//
+// Per wave, tiles flow through one register buffer per operand with K and V staggered: the
+// next tile's K is requested as soon as this tile's scores are computed, and its V as soon as
+// this tile's V has been accumulated, so one tile of loads is always in flight while the
+// register footprint stays at one tile. K/V loads are non-temporal (streamed data, no reuse
+// inside a launch except through sharing). Scores are kept in base-2 units (scale folded with
+// log2 e) so every exponential is one v_exp_f32. Masked tokens (past the end of a sequence's
+// last block, or a whole block whose table entry is outside the pool) are *selected* out --
+// score -inf, V element 0 -- never multiplied by zero, so NaN in unused slots cannot leak.
 
 #include <hip/hip_runtime.h>
+
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <type_traits>
 
 #include "pkv_kernels.h"
 
@@ -26,8 +45,7 @@ namespace pkv {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
-constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kLog2e = 1.44269504088896340736f;
+constexpr int kThreads = kWaves * 64;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
@@ -36,8 +54,20 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Streaming loads of cache tiles (global_load ... nt).
+__device__ __forceinline__ uint4 load_nt16(const char* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load_nt8(const char* p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(v.x, v.y);
+}
 
 // Cross-lane moves inside a row of 16 lanes (DPP): quad permutations and row rotations.
 template <int CTRL>
@@ -73,17 +103,11 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Opaque to the optimiser: the value is "redefined" here, so no use of it (such as unpacking
-// 16-bit halves) can be hoisted above this point, e.g. next to a prefetch load, where it would
-// force an early wait for that load.
-__device__ __forceinline__ uint4 pinned(uint4 v) {
-  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
-  return v;
-}
-
 __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Per-dtype element access. DT: 0 = f32, 1 = f16, 2 = bf16.
 template <int DT>
@@ -145,101 +169,116 @@ struct Elem<2> {
   }
 };
 
-// Shared prologue: clamp the length and locate the partition (all values wave-uniform).
-struct PartInfo {
-  int n, nparts, t0, t1, nblk;
+__device__ __forceinline__ int clamp_len(const StreamParams& p, int i) {
+  return min(max(p.context_lens[i], 0), p.max_ctx);
+}
+
+// ---- Stream geometry ----------------------------------------------------------------------
+
+// Exclusive prefix sums of the per-sequence block counts c_i = ceil(n_i/16) into
+// pref[0..B]; pref[B] = C, the tiles of one head slot. Whole work-group; ends synchronised.
+__device__ void scan_block_counts(const StreamParams& p, int* pref) {
+  __shared__ int s_wsum[kWaves];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int carry = 0;
+  for (int base = 0; base < p.B; base += kThreads) {
+    const int i = base + threadIdx.x;
+    const int c = i < p.B ? (clamp_len(p, i) + kBlockSize - 1) / kBlockSize : 0;
+    int x = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) s_wsum[w] = x;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      before += ww < w ? s_wsum[ww] : 0;
+      total += s_wsum[ww];
+    }
+    if (i < p.B) pref[i] = carry + before + x - c;
+    carry += total;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) pref[p.B] = carry;
+  __syncthreads();
+}
+
+// Largest i in [0, B) with pref[i] <= r, given pref[B] > r (empty segments are skipped).
+__device__ __forceinline__ int find_seq(const int* pref, int B, int r) {
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pref[mid] <= r) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Everything a wave needs about one tile of its range, held one tile per lane.
+struct TileInfo {
+  int id;   // physical block to read (0 when the table entry is outside the pool)
+  int seq;  // sequence i
+  int hm;   // head slot << 16 | slot << 8 | whole << 7 | end << 6 | start << 5 | valid tokens
+};
+constexpr int kStart = 1 << 5, kEnd = 1 << 6, kWhole = 1 << 7;
+
+// Stream position t -> tile of segment (i, h): head-major order, t = h*C + pref[i] + j.
+__device__ __forceinline__ TileInfo tile_info(const StreamParams& p, const int* pref, int C,
+                                              int t, int t0, int t1) {
+  const int h = t / C;
+  const int r = t - h * C;
+  const int i = find_seq(pref, p.B, r);
+  const int j = r - pref[i];
+  const int c = pref[i + 1] - pref[i];
+  const int seg0 = h * C + pref[i];
+  const int n = clamp_len(p, i);
+  int valid = min(kBlockSize, n - kBlockSize * j);
+  int id = p.block_tables[static_cast<size_t>(i) * p.max_blocks + j];
+  if (id < 0 || id >= p.NB) {
+    id = 0;  // read (always in bounds) but no token of it counts
+    valid = 0;
+  }
+  const int start = (t == seg0) || (t == t0);
+  const int end = (t == seg0 + c - 1) || (t == t1 - 1);
+  const int whole = (seg0 >= t0) && (seg0 + c <= t1);
+  const int slot = seg0 <= t0 ? 0 : 1;
+  return TileInfo{id, i, (h << 16) | (slot << 8) | (whole << 7) | (end << 6) | (start << 5) | valid};
+}
+
+// This wave's worker index and tile range [t0, t1). Work-group b runs on XCD b % 8; logical
+// work-group (b % 8) * (grid / 8) + b / 8 gives each XCD a contiguous share of the workers.
+struct Range {
+  int worker, t0, t1;
 };
 
-__device__ __forceinline__ bool part_setup(const AttnParams& p, int seq, int part,
-                                           PartInfo* info) {
-  int n = p.context_lens[seq];
-  n = min(max(n, 0), p.max_ctx);
-  const int P = p.part_tokens;
-  const int nparts = (n + P - 1) / P;
-  if (part > 0 && part >= nparts) return false;  // partition 0 always runs: n = 0 gives zeros
-  const int t0 = part * P;
-  const int t1 = min(n, t0 + P);
-  const int nblk = t1 > t0 ? (t1 - t0 + kBlockSize - 1) / kBlockSize : 0;
-  *info = PartInfo{n, nparts, t0, t1, nblk};
-  return true;
+__device__ __forceinline__ Range worker_range(const StreamParams& p, int C, int H) {
+  const int grid = gridDim.x, b = blockIdx.x;
+  const int lwg = (grid % 8 == 0) ? (b % 8) * (grid / 8) + b / 8 : b;
+  const int worker = lwg * kWaves + uniform(threadIdx.x >> 6);
+  const int T = H * C;
+  const int per = (T + p.num_workers - 1) / p.num_workers;
+  const int t0 = min(T, worker * per);
+  const int t1 = min(T, t0 + per);
+  return Range{worker, t0, t1};
 }
 
-// Block-table staging: wave w of NW owns the partition's blocks w, w+NW, w+2NW, ...; lane k
-// of the wave holds the physical id of the wave's k-th block (one coalesced load of at most
-// 64 ids per wave). The block loop reads them with v_readlane, so an id lookup never waits on
-// memory. Ids outside [0, NB) become -1.
-template <int NW>
-__device__ __forceinline__ int stage_block_ids(const AttnParams& p, int seq, const PartInfo& pi,
-                                               int w, int lane) {
-  const int i = w + NW * lane;
-  if (i >= pi.nblk) return -1;
-  const int id = p.block_tables[static_cast<size_t>(seq) * p.max_blocks + pi.t0 / kBlockSize + i];
-  return (id >= 0 && id < p.NB) ? id : -1;
-}
-
-// k-th block of this wave: (physical id to read, valid tokens in it). An id outside the pool
-// reads block 0 (always in bounds) with no valid token, so it contributes nothing.
-template <int NW>
-__device__ __forceinline__ void wave_block(int ids, int k, int w, const PartInfo& pi, int* id,
-                                           int* valid) {
-  const int raw = __builtin_amdgcn_readlane(ids, k);
-  const int i = w + NW * k;
-  const int v = min(kBlockSize, pi.t1 - (pi.t0 + kBlockSize * i));
-  *id = raw >= 0 ? raw : 0;
-  *valid = raw >= 0 ? v : 0;
-}
-
-// The partition bounds are the same in every lane; saying so keeps the block loop on scalar
-// branches (the staging loop above would otherwise make them look lane-dependent).
-__device__ __forceinline__ void make_uniform(PartInfo* pi) {
-  pi->n = __builtin_amdgcn_readfirstlane(pi->n);
-  pi->nparts = __builtin_amdgcn_readfirstlane(pi->nparts);
-  pi->t0 = __builtin_amdgcn_readfirstlane(pi->t0);
-  pi->t1 = __builtin_amdgcn_readfirstlane(pi->t1);
-  pi->nblk = __builtin_amdgcn_readfirstlane(pi->nblk);
-}
-
-// Final combine of the NW waves' (m, l, o) for one head and one dim, in wave order.
-// m values are base-2 maxima; waves that saw no token have m = -inf and are skipped.
-template <int NW>
-__device__ __forceinline__ void combine_waves(const float* ms, const float* ls, const float* os,
-                                              int ostride, float* M_out, float* L_out,
-                                              float* O_out) {
-  float M = kNegInf;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) M = fmaxf(M, ms[w]);
-  float L = 0.f, O = 0.f;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    if (ms[w] != kNegInf) {
-      const float wt = exp2_fast(ms[w] - M);
-      L = fmaf(wt, ls[w], L);
-      O = fmaf(wt, os[w * ostride], O);
-    }
-  }
-  *M_out = M;
-  *L_out = L;
-  *O_out = O;
-}
-
+// Work-group 0 publishes the prefix sums for the merge pass and zeroes rows with n = 0.
 template <int DT>
-__device__ __forceinline__ void emit(const AttnParams& p, const PartInfo& pi, int seq, int h,
-                                     int part, int d, int hd, float M, float L, float O) {
-  const size_t row = static_cast<size_t>(seq) * p.Hq + h;
-  if (pi.nparts <= 1) {
-    Elem<DT>::put(p.out, row * hd + d, L > 0.f ? O / L : 0.f);
-  } else {
-    const size_t idx = row * p.max_parts + part;
-    if (d == 0) {
-      p.ws_m[idx] = M == kNegInf ? kNegInf : M * kLn2;
-      p.ws_l[idx] = L;
-    }
-    p.ws_o[idx * hd + d] = O;
+__device__ void publish_and_zero(const StreamParams& p, const int* pref) {
+  if (blockIdx.x != 0) return;
+  for (int i = threadIdx.x; i <= p.B; i += kThreads) p.ws_seg[i] = pref[i];
+  const int row = p.Hq * p.hd;
+  for (int i = 0; i < p.B; ++i) {
+    if (pref[i + 1] != pref[i]) continue;
+    for (int e = threadIdx.x; e < row; e += kThreads)
+      Elem<DT>::put(p.out, static_cast<size_t>(i) * row + e, 0.f);
   }
 }
 
 // ------------------------------------------------------------------------------------------
-// Vector kernel: one q head per work-group (G = 1, or f32, or G > 16).
+// Vector kernel: one q head per segment (G = 1, f32, or G > 16).
 //
 // Lane layout per (block, kv-head) tile (TILE bytes, NL = TILE/1024 loads of 16 B per lane):
 //  K load j: lane l reads bytes 1024 j + 16 l = chunk c = 4 j + l/16 of token l%16, so each
@@ -247,10 +286,10 @@ __device__ __forceinline__ void emit(const AttnParams& p, const PartInfo& pi, in
 //    chunk dots plus a sum over the 4 rows (lanes l, l^16, l^32, l^48).
 //  V load j: lane l reads V dim row d = j*64/LPR + l/LPR, tokens X*(l%LPR) .. +X, where a dim
 //    row of 16 tokens spans LPR = element-bytes lanes. The probabilities of those X tokens are
-//    broadcast through LDS; the per-lane accumulators are summed over the LPR lanes at the end.
-template <int DT, int HD, int NW>
-__global__ void __launch_bounds__(NW * 64)
-attn_vector_kernel(const AttnParams p) {
+//    broadcast through LDS; the per-lane sums are added over the LPR lanes at the end.
+template <int DT, int HD>
+__global__ void __launch_bounds__(kThreads)
+attn_vector_kernel(const StreamParams p) {
   using E = Elem<DT>;
   constexpr int EB = E::kBytes;
   constexpr int X = 16 / EB;
@@ -260,148 +299,139 @@ attn_vector_kernel(const AttnParams p) {
   constexpr int VROWS = 64 / LPR;
   static_assert(NL * VROWS == HD, "V lane layout must cover the head");
 
-  __shared__ float s_p[NW][kBlockSize];
-  __shared__ float s_o[NW][HD];
-  __shared__ float s_m[NW], s_l[NW];
+  extern __shared__ int s_pref[];
+  __shared__ float s_p[kWaves][kBlockSize];
 
-  const int seq = blockIdx.x, h = blockIdx.y, part = blockIdx.z;
+  scan_block_counts(p, s_pref);
+  publish_and_zero<DT>(p, s_pref);
+  const int C = s_pref[p.B];
+  const Range rg = worker_range(p, C, p.Hq);
+  if (rg.t0 >= rg.t1) return;
+
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  PartInfo pi;
-  if (!part_setup(p, seq, part, &pi)) return;
-  make_uniform(&pi);
-  const int ids = stage_block_ids<NW>(p, seq, pi, w, lane);
-  const int nmine = pi.nblk > w ? (pi.nblk - w + NW - 1) / NW : 0;  // blocks of this wave
-
+  const int w = uniform(threadIdx.x >> 6);
   const int G = p.Hq / p.Hkv;
-  const int kvh = h / G;
   const int row_id = lane >> 4, tok = lane & 15;
   const int vsub = lane % LPR;
+  const uint32_t lane_off = 16u * lane;
+  const size_t blk_stride = static_cast<size_t>(p.Hkv) * TILE;
 
   uint4 qv[NL];
-  {
-    const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const char*>(p.q) +
-                                                     (static_cast<size_t>(seq) * p.Hq + h) * HD * EB);
-#pragma unroll
-    for (int j = 0; j < NL; ++j) qv[j] = qp[4 * j + row_id];
-  }
-  const size_t head_off = static_cast<size_t>(kvh) * TILE;
-  const size_t blk_stride = static_cast<size_t>(p.Hkv) * TILE;
-  const char* kbase = static_cast<const char*>(p.k_cache) + head_off;
-  const char* vbase = static_cast<const char*>(p.v_cache) + head_off;
-  const uint32_t lane_off = 16u * lane;
-
   float m = kNegInf, lsum = 0.f;
   float acc[NL];
-#pragma unroll
-  for (int j = 0; j < NL; ++j) acc[j] = 0.f;
+  uint4 kr[NL], vr[NL];
 
-  struct Regs {
-    uint4 k[NL], v[NL];
-  };
-  auto load = [&](Regs& r, int id) {
-    const char* kt = kbase + static_cast<size_t>(id) * blk_stride;  // scalar tile base
-    const char* vt = vbase + static_cast<size_t>(id) * blk_stride;
-#pragma unroll
-    for (int j = 0; j < NL; ++j)
-      r.k[j] = *reinterpret_cast<const uint4*>(kt + (lane_off + 1024u * j));
-#pragma unroll
-    for (int j = 0; j < NL; ++j)
-      r.v[j] = *reinterpret_cast<const uint4*>(vt + (lane_off + 1024u * j));
-  };
-  auto consume = [&](const Regs& r, int valid) {
-    float s = 0.f;
-#pragma unroll
-    for (int j = 0; j < NL; ++j) s = E::dot(qv[j], r.k[j], s);
-    s += __shfl_xor(s, 16);
-    s += __shfl_xor(s, 32);
-    s *= p.scale_log2;
-    if (valid < kBlockSize) s = tok < valid ? s : kNegInf;
-    const float m_new = fmaxf(m, row_max16(s));
-    float alpha = exp2_fast(m - m_new);
-    float pr = exp2_fast(s - m_new);
-    if (valid < kBlockSize) {  // partly (or, for a bad table entry, wholly) masked block
-      alpha = m_new == kNegInf ? 1.f : alpha;
-      pr = tok < valid ? pr : 0.f;
-    }
-    lsum = fmaf(lsum, alpha, pr);
-    m = m_new;
-    if (lane < kBlockSize) s_p[w][lane] = pr;
-    wave_lds_sync();
-    float pv[X];
-#pragma unroll
-    for (int x = 0; x < X; ++x) pv[x] = s_p[w][X * vsub + x];
-#pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const uint4 vj = pinned(r.v[j]);
-      float a = acc[j] * alpha;
-#pragma unroll
-      for (int x = 0; x < X; ++x) {
-        float vx = E::get(vj, x);
-        if (valid < kBlockSize) vx = (X * vsub + x < valid) ? vx : 0.f;
-        a = fmaf(pv[x], vx, a);
-      }
-      acc[j] = a;
-    }
-    wave_lds_sync();
-  };
-  // Double-buffered stream over this wave's blocks: tile k+1 is in flight while tile k is
-  // consumed. Every load is unconditional inside its branch, so the wait counters stay exact.
-  Regs ra, rb;
-  int k = 0;
-  if (nmine > 0) {
-    int id, valid;
-    wave_block<NW>(ids, 0, w, pi, &id, &valid);
-    load(ra, id);
-    int va = valid;
-    while (true) {
-      if (k + 1 >= nmine) {
-        consume(ra, va);
-        break;
-      }
-      wave_block<NW>(ids, k + 1, w, pi, &id, &valid);
-      load(rb, id);
-      consume(ra, va);
-      const int vb = valid;
-      ++k;
-      if (k + 1 >= nmine) {
-        consume(rb, vb);
-        break;
-      }
-      wave_block<NW>(ids, k + 1, w, pi, &id, &valid);
-      load(ra, id);
-      consume(rb, vb);
-      va = valid;
-      ++k;
-    }
-  }
+  for (int cb = rg.t0; cb < rg.t1; cb += 64) {
+    const int cnt = uniform(min(64, rg.t1 - cb));
+    TileInfo ti{0, 0, 0};
+    if (lane < cnt) ti = tile_info(p, s_pref, C, cb + lane, rg.t0, rg.t1);
 
-  const float l = row_sum16(lsum);
+    // Tile k of the chunk: block id from lane k, kv head of its q head.
+    auto tile_base = [&](const void* cache, int k) {
+      const int id = uniform(__builtin_amdgcn_readlane(ti.id, k));
+      const int h = uniform(__builtin_amdgcn_readlane(ti.hm, k)) >> 16;
+      return static_cast<const char*>(cache) + static_cast<size_t>(id) * blk_stride +
+             static_cast<size_t>(h / G) * TILE;
+    };
+    auto load_k = [&](int k) {
+      const char* kt = tile_base(p.k_cache, k);
 #pragma unroll
-  for (int j = 0; j < NL; ++j) {
-    float a = acc[j];
-    if constexpr (LPR >= 2) a += dpp<kQuadSwap1>(a);
-    if constexpr (LPR >= 4) a += dpp<kQuadSwap2>(a);
-    acc[j] = a;
-  }
-  if (vsub == 0) {
+      for (int j = 0; j < NL; ++j) kr[j] = load_nt16(kt + (lane_off + 1024u * j));
+    };
+    auto load_v = [&](int k) {
+      const char* vt = tile_base(p.v_cache, k);
 #pragma unroll
-    for (int j = 0; j < NL; ++j) s_o[w][VROWS * j + lane / LPR] = acc[j];
-  }
-  if (lane == 0) {
-    s_m[w] = m;
-    s_l[w] = l;
-  }
-  __syncthreads();
-  for (int d = threadIdx.x; d < HD; d += NW * 64) {
-    float M, L, O;
-    combine_waves<NW>(s_m, s_l, &s_o[0][d], HD, &M, &L, &O);
-    emit<DT>(p, pi, seq, h, part, d, HD, M, L, O);
+      for (int j = 0; j < NL; ++j) vr[j] = load_nt16(vt + (lane_off + 1024u * j));
+    };
+
+    auto step = [&](int k, auto load_next) {
+      const int seq = uniform(__builtin_amdgcn_readlane(ti.seq, k));
+      const int hm = uniform(__builtin_amdgcn_readlane(ti.hm, k));
+      const int h = hm >> 16, valid = hm & 31;
+      if (hm & kStart) {  // first tile of a segment in this range: fresh state, its q
+        m = kNegInf;
+        lsum = 0.f;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) acc[j] = 0.f;
+        const uint4* qp = reinterpret_cast<const uint4*>(
+            static_cast<const char*>(p.q) + (static_cast<size_t>(seq) * p.Hq + h) * HD * EB);
+#pragma unroll
+        for (int j = 0; j < NL; ++j) qv[j] = qp[4 * j + row_id];
+      }
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < NL; ++j) s = E::dot(qv[j], kr[j], s);
+      if constexpr (decltype(load_next)::value) load_k(k + 1);
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      s *= p.scale_log2;
+      if (valid < kBlockSize) s = tok < valid ? s : kNegInf;
+      const float m_new = fmaxf(m, row_max16(s));
+      float alpha = exp2_fast(m - m_new);
+      float pr = exp2_fast(s - m_new);
+      if (valid < kBlockSize) {  // partly (or, for a bad table entry, wholly) masked block
+        alpha = m_new == kNegInf ? 1.f : alpha;
+        pr = tok < valid ? pr : 0.f;
+      }
+      lsum = fmaf(lsum, alpha, pr);
+      m = m_new;
+      if (lane < kBlockSize) s_p[w][lane] = pr;
+      wave_lds_sync();
+      float pv[X];
+#pragma unroll
+      for (int x = 0; x < X; ++x) pv[x] = s_p[w][X * vsub + x];
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        float a = acc[j] * alpha;
+#pragma unroll
+        for (int x = 0; x < X; ++x) {
+          float vx = E::get(vr[j], x);
+          if (valid < kBlockSize) vx = (X * vsub + x < valid) ? vx : 0.f;
+          a = fmaf(pv[x], vx, a);
+        }
+        acc[j] = a;
+      }
+      if constexpr (decltype(load_next)::value) load_v(k + 1);
+      wave_lds_sync();
+      if (hm & kEnd) {  // last tile of the segment in this range: emit
+        const float l = row_sum16(lsum);
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+          float a = acc[j];
+          if constexpr (LPR >= 2) a += dpp<kQuadSwap1>(a);
+          if constexpr (LPR >= 4) a += dpp<kQuadSwap2>(a);
+          acc[j] = a;
+        }
+        if (hm & kWhole) {  // the whole segment was ours: final output row
+          if (vsub == 0) {
+            const size_t row = (static_cast<size_t>(seq) * p.Hq + h) * HD;
+#pragma unroll
+            for (int j = 0; j < NL; ++j)
+              E::put(p.out, row + VROWS * j + lane / LPR, l > 0.f ? acc[j] / l : 0.f);
+          }
+        } else {  // a piece of a segment shared with neighbouring workers
+          const size_t cell = static_cast<size_t>(rg.worker) * 2 + ((hm >> 8) & 1);
+          if (vsub == 0) {
+#pragma unroll
+            for (int j = 0; j < NL; ++j) p.ws_o[cell * HD + VROWS * j + lane / LPR] = acc[j];
+          }
+          if (lane == 0) {
+            p.ws_ml[cell * 2] = m;
+            p.ws_ml[cell * 2 + 1] = l;
+          }
+        }
+      }
+    };
+
+    load_k(0);
+    load_v(0);
+    for (int k = 0; k + 1 < cnt; ++k) step(k, std::true_type{});
+    step(cnt - 1, std::false_type{});
   }
 }
 
 // ------------------------------------------------------------------------------------------
-// Matrix-core kernel: one kv head and its G <= 16 q heads per work-group (f16/bf16).
+// Matrix-core kernel: one kv head and its G <= 16 q heads per segment (f16/bf16).
 //
 // Per tile, S^T = K Q^T on v_mfma_f32_16x16x32 (HD/32 steps; A = the 16 K rows, B = the
 // group's q vectors, heads padded to 16 with zeros), then O^T += V^T P^T on
@@ -446,227 +476,233 @@ struct Mfma<2> {
   }
 };
 
-template <int DT, int HD, int NW>
-__global__ void __launch_bounds__(NW * 64)
-attn_matrix_kernel(const AttnParams p) {
+template <int DT, int HD>
+__global__ void __launch_bounds__(kThreads)
+attn_matrix_kernel(const StreamParams p) {
   using M16 = Mfma<DT>;
   constexpr int TILE = HD * kBlockSize * 2;
   constexpr int KS = HD / 32;  // QK steps
   constexpr int VT = HD / 16;  // PV dim tiles
-  constexpr int OSTR = HD + 4;  // padded LDS row (heads map to different banks)
 
-  __shared__ float s_o[NW][16][OSTR];
-  __shared__ float s_m[NW][16], s_l[NW][16];
+  extern __shared__ int s_pref[];
 
-  const int seq = blockIdx.x, kvh = blockIdx.y, part = blockIdx.z;
+  scan_block_counts(p, s_pref);
+  publish_and_zero<DT>(p, s_pref);
+  const int C = s_pref[p.B];
+  const Range rg = worker_range(p, C, p.Hkv);
+  if (rg.t0 >= rg.t1) return;
+
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  PartInfo pi;
-  if (!part_setup(p, seq, part, &pi)) return;
-  make_uniform(&pi);
-  const int ids = stage_block_ids<NW>(p, seq, pi, w, lane);
-  const int nmine = pi.nblk > w ? (pi.nblk - w + NW - 1) / NW : 0;  // blocks of this wave
-
   const int G = p.Hq / p.Hkv;
   const int hq = lane & 15, g = lane >> 4;
-
-  uint4 qb[KS];
-  if (hq < G) {
-    const uint4* qp = reinterpret_cast<const uint4*>(
-        static_cast<const char*>(p.q) + (static_cast<size_t>(seq) * p.Hq + kvh * G + hq) * HD * 2);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qb[s] = qp[4 * s + g];
-  } else {
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qb[s] = make_uint4(0, 0, 0, 0);
-  }
-  const size_t head_off = static_cast<size_t>(kvh) * TILE;
-  const size_t blk_stride = static_cast<size_t>(p.Hkv) * TILE;
-  const char* kbase = static_cast<const char*>(p.k_cache) + head_off;
-  const char* vbase = static_cast<const char*>(p.v_cache) + head_off;
   const uint32_t k_lane = 16u * lane;
   const uint32_t v_lane = 32u * hq + 8u * g;
+  const size_t blk_stride = static_cast<size_t>(p.Hkv) * TILE;
 
+  uint4 qb[KS];
   float m = kNegInf, lsum = 0.f;
   float4_t o[VT];
-#pragma unroll
-  for (int j = 0; j < VT; ++j) o[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+  uint4 kr[KS];
+  uint2 vr[VT];
 
-  struct Regs {
-    uint4 k[KS];
-    uint2 v[VT];
-  };
-  auto load = [&](Regs& r, int id) {
-    const char* kt = kbase + static_cast<size_t>(id) * blk_stride;  // scalar tile base
-    const char* vt = vbase + static_cast<size_t>(id) * blk_stride;
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      r.k[s] = *reinterpret_cast<const uint4*>(kt + (k_lane + 1024u * s));
-#pragma unroll
-    for (int j = 0; j < VT; ++j) r.v[j] = *reinterpret_cast<const uint2*>(vt + (v_lane + 512u * j));
-  };
-  auto consume = [&](const Regs& r, int valid) {
-    float4_t sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) sacc = M16::qk(r.k[s], qb[s], sacc);
-    float sc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sc[i] = sacc[i] * p.scale_log2;
-      if (valid < kBlockSize) sc[i] = (4 * g + i < valid) ? sc[i] : kNegInf;
-    }
-    float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float m_new = fmaxf(m, bm);
-    float alpha = exp2_fast(m - m_new);
-    float pr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(sc[i] - m_new);
-    if (valid < kBlockSize) {  // partly (or, for a bad table entry, wholly) masked block
-      alpha = m_new == kNegInf ? 1.f : alpha;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = (4 * g + i < valid) ? pr[i] : 0.f;
-    }
-    lsum = fmaf(lsum, alpha, (pr[0] + pr[1]) + (pr[2] + pr[3]));
-    m = m_new;
-    const uint2 pb = make_uint2(M16::pack2(pr[0], pr[1]), M16::pack2(pr[2], pr[3]));
-    uint2 vmask = make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
-    if (valid < kBlockSize) {
-      const int base = 4 * g;
-      vmask.x = (base + 0 < valid ? 0x0000FFFFu : 0u) | (base + 1 < valid ? 0xFFFF0000u : 0u);
-      vmask.y = (base + 2 < valid ? 0x0000FFFFu : 0u) | (base + 3 < valid ? 0xFFFF0000u : 0u);
-    }
-#pragma unroll
-    for (int j = 0; j < VT; ++j) {
-      const uint2 va = make_uint2(r.v[j].x & vmask.x, r.v[j].y & vmask.y);
-      o[j] = M16::pv(va, pb, o[j] * alpha);
-    }
-  };
-  // Double-buffered stream over this wave's blocks: tile k+1 is in flight while tile k is
-  // consumed. Every load is unconditional inside its branch, so the wait counters stay exact.
-  Regs ra, rb;
-  int k = 0;
-  if (nmine > 0) {
-    int id, valid;
-    wave_block<NW>(ids, 0, w, pi, &id, &valid);
-    load(ra, id);
-    int va = valid;
-    while (true) {
-      if (k + 1 >= nmine) {
-        consume(ra, va);
-        break;
-      }
-      wave_block<NW>(ids, k + 1, w, pi, &id, &valid);
-      load(rb, id);
-      consume(ra, va);
-      const int vb = valid;
-      ++k;
-      if (k + 1 >= nmine) {
-        consume(rb, vb);
-        break;
-      }
-      wave_block<NW>(ids, k + 1, w, pi, &id, &valid);
-      load(ra, id);
-      consume(rb, vb);
-      va = valid;
-      ++k;
-    }
-  }
+  for (int cb = rg.t0; cb < rg.t1; cb += 64) {
+    const int cnt = uniform(min(64, rg.t1 - cb));
+    TileInfo ti{0, 0, 0};
+    if (lane < cnt) ti = tile_info(p, s_pref, C, cb + lane, rg.t0, rg.t1);
 
-  float l = lsum + __shfl_xor(lsum, 16);
-  l += __shfl_xor(l, 32);
+    auto tile_base = [&](const void* cache, int k) {
+      const int id = uniform(__builtin_amdgcn_readlane(ti.id, k));
+      const int h = uniform(__builtin_amdgcn_readlane(ti.hm, k)) >> 16;
+      return static_cast<const char*>(cache) + static_cast<size_t>(id) * blk_stride +
+             static_cast<size_t>(h) * TILE;
+    };
+    auto load_k = [&](int k) {
+      const char* kt = tile_base(p.k_cache, k);
 #pragma unroll
-  for (int j = 0; j < VT; ++j) {
+      for (int s = 0; s < KS; ++s) kr[s] = load_nt16(kt + (k_lane + 1024u * s));
+    };
+    auto load_v = [&](int k) {
+      const char* vt = tile_base(p.v_cache, k);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s_o[w][hq][16 * j + 4 * g + e] = o[j][e];
-  }
-  if (g == 0) {
-    s_m[w][hq] = m;
-    s_l[w][hq] = l;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < G * HD; e += NW * 64) {
-    const int hh = e / HD, d = e % HD;
-    float ms[NW], ls[NW];
+      for (int j = 0; j < VT; ++j) vr[j] = load_nt8(vt + (v_lane + 512u * j));
+    };
+
+    auto step = [&](int k, auto load_next) {
+      const int seq = uniform(__builtin_amdgcn_readlane(ti.seq, k));
+      const int hm = uniform(__builtin_amdgcn_readlane(ti.hm, k));
+      const int kvh = hm >> 16, valid = hm & 31;
+      if (hm & kStart) {  // first tile of a segment in this range: fresh state, its q
+        m = kNegInf;
+        lsum = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      ms[ww] = s_m[ww][hh];
-      ls[ww] = s_l[ww][hh];
-    }
-    float M, L, O;
-    combine_waves<NW>(ms, ls, &s_o[0][hh][d], 16 * OSTR, &M, &L, &O);
-    emit<DT>(p, pi, seq, kvh * G + hh, part, d, HD, M, L, O);
+        for (int j = 0; j < VT; ++j) o[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+        if (hq < G) {
+          const uint4* qp = reinterpret_cast<const uint4*>(
+              static_cast<const char*>(p.q) +
+              (static_cast<size_t>(seq) * p.Hq + kvh * G + hq) * HD * 2);
+#pragma unroll
+          for (int s = 0; s < KS; ++s) qb[s] = qp[4 * s + g];
+        } else {
+#pragma unroll
+          for (int s = 0; s < KS; ++s) qb[s] = make_uint4(0, 0, 0, 0);
+        }
+      }
+      float4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) sacc = M16::qk(kr[s], qb[s], sacc);
+      if constexpr (decltype(load_next)::value) load_k(k + 1);
+      float sc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sc[i] = sacc[i] * p.scale_log2;
+        if (valid < kBlockSize) sc[i] = (4 * g + i < valid) ? sc[i] : kNegInf;
+      }
+      float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float m_new = fmaxf(m, bm);
+      float alpha = exp2_fast(m - m_new);
+      float pr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(sc[i] - m_new);
+      if (valid < kBlockSize) {  // partly (or, for a bad table entry, wholly) masked block
+        alpha = m_new == kNegInf ? 1.f : alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[i] = (4 * g + i < valid) ? pr[i] : 0.f;
+      }
+      lsum = fmaf(lsum, alpha, (pr[0] + pr[1]) + (pr[2] + pr[3]));
+      m = m_new;
+      const uint2 pb = make_uint2(M16::pack2(pr[0], pr[1]), M16::pack2(pr[2], pr[3]));
+      uint2 vmask = make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
+      if (valid < kBlockSize) {
+        const int base = 4 * g;
+        vmask.x = (base + 0 < valid ? 0x0000FFFFu : 0u) | (base + 1 < valid ? 0xFFFF0000u : 0u);
+        vmask.y = (base + 2 < valid ? 0x0000FFFFu : 0u) | (base + 3 < valid ? 0xFFFF0000u : 0u);
+      }
+#pragma unroll
+      for (int j = 0; j < VT; ++j) {
+        const uint2 va = make_uint2(vr[j].x & vmask.x, vr[j].y & vmask.y);
+        o[j] = M16::pv(va, pb, o[j] * alpha);
+      }
+      if constexpr (decltype(load_next)::value) load_v(k + 1);
+      if (hm & kEnd) {  // last tile of the segment in this range: emit
+        float l = lsum + __shfl_xor(lsum, 16);
+        l += __shfl_xor(l, 32);
+        if (hm & kWhole) {  // the whole segment was ours: final output rows
+          if (hq < G) {
+            const size_t row = (static_cast<size_t>(seq) * p.Hq + kvh * G + hq) * HD;
+#pragma unroll
+            for (int j = 0; j < VT; ++j) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                Elem<DT>::put(p.out, row + 16 * j + 4 * g + e, l > 0.f ? o[j][e] / l : 0.f);
+            }
+          }
+        } else if (hq < G) {  // a piece of a segment shared with neighbouring workers
+          const size_t cell = (static_cast<size_t>(rg.worker) * 2 + ((hm >> 8) & 1)) * G + hq;
+#pragma unroll
+          for (int j = 0; j < VT; ++j)
+            *reinterpret_cast<float4_t*>(p.ws_o + cell * HD + 16 * j + 4 * g) = o[j];
+          if (g == 0) {
+            p.ws_ml[cell * 2] = m;
+            p.ws_ml[cell * 2 + 1] = l;
+          }
+        }
+      }
+    };
+
+    load_k(0);
+    load_v(0);
+    for (int k = 0; k + 1 < cnt; ++k) step(k, std::true_type{});
+    step(cnt - 1, std::false_type{});
   }
 }
 
 // ------------------------------------------------------------------------------------------
-// Log-sum-exp merge of the partitions of sequences longer than one partition. One wave per
-// (sequence, q head); partitions are combined in index order (deterministic).
+// Merge of the pieces of segments cut by worker-range boundaries. One wave per segment
+// (sequence i, head slot h); the segment's GS q heads are done one after another, pieces
+// combined in worker order (deterministic). Segments inside one range, and empty ones, were
+// finished by the stream pass and are left alone.
 template <int DT, int HD>
 __global__ void __launch_bounds__(64)
-merge_kernel(const AttnParams p) {
+merge_kernel(const StreamParams p, int H, int GS) {
   constexpr int R = HD / 64;
-  const int seq = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-  int n = p.context_lens[seq];
-  n = min(max(n, 0), p.max_ctx);
-  const int nparts = (n + p.part_tokens - 1) / p.part_tokens;
-  if (nparts <= 1) return;  // finished by the partition pass
-  const size_t base = (static_cast<size_t>(seq) * p.Hq + h) * p.max_parts;
-  float M = kNegInf;
-  for (int j = lane; j < nparts; j += 64) M = fmaxf(M, p.ws_m[base + j]);
+  const int i = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int C = p.ws_seg[p.B];
+  const int s0 = p.ws_seg[i];
+  const int c = p.ws_seg[i + 1] - s0;
+  if (c == 0) return;
+  const int T = H * C;
+  const int per = (T + p.num_workers - 1) / p.num_workers;
+  const int tb = h * C + s0, te = tb + c;
+  const int wf = tb / per, wl = (te - 1) / per;
+  if (wf == wl) return;
+  for (int n = 0; n < GS; ++n) {
+    auto cell = [&](int wk) {
+      const int slot = (wk == wf && wf * per < tb) ? 1 : 0;
+      return (static_cast<size_t>(wk) * 2 + slot) * GS + n;
+    };
+    float M = kNegInf;
+    for (int wk = wf + lane; wk <= wl; wk += 64) M = fmaxf(M, p.ws_ml[cell(wk) * 2]);
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
-  float L = 0.f, O[R];
+    for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float L = 0.f, O[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) O[r] = 0.f;
-  for (int j = 0; j < nparts; ++j) {
-    const float mj = p.ws_m[base + j];
-    if (mj == kNegInf) continue;
-    const float wt = exp2_fast((mj - M) * kLog2e);
-    L = fmaf(wt, p.ws_l[base + j], L);
-    const float* oj = p.ws_o + (base + j) * HD;
+    for (int r = 0; r < R; ++r) O[r] = 0.f;
+    for (int wk = wf; wk <= wl; ++wk) {
+      const size_t cl = cell(wk);
+      const float mj = p.ws_ml[cl * 2];
+      if (mj == kNegInf) continue;  // a piece with no valid token
+      const float wt = exp2_fast(mj - M);
+      L = fmaf(wt, p.ws_ml[cl * 2 + 1], L);
+      const float* oj = p.ws_o + cl * HD;
 #pragma unroll
-    for (int r = 0; r < R; ++r) O[r] = fmaf(wt, oj[lane + 64 * r], O[r]);
+      for (int r = 0; r < R; ++r) O[r] = fmaf(wt, oj[lane + 64 * r], O[r]);
+    }
+    const size_t orow = (static_cast<size_t>(i) * p.Hq + h * GS + n) * HD;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      Elem<DT>::put(p.out, orow + lane + 64 * r, L > 0.f ? O[r] / L : 0.f);
   }
-  const size_t orow = (static_cast<size_t>(seq) * p.Hq + h) * HD;
-#pragma unroll
-  for (int r = 0; r < R; ++r) Elem<DT>::put(p.out, orow + lane + 64 * r, L > 0.f ? O[r] / L : 0.f);
 }
 
-constexpr int kWaves = 4;
+// ---- host side ------------------------------------------------------------------------------
 
 template <int DT, int HD>
-hipError_t launch_partition_t(const AttnParams& p, int32_t kernel, hipStream_t stream) {
-  (void)hipGetLastError();  // drop a stale status left by an earlier, unrelated runtime call
-  const dim3 block(kWaves * 64);
+const void* stream_kernel_ptr(int32_t kernel) {
+  if constexpr (DT != 0) {
+    if (kernel == kMatrix) return reinterpret_cast<const void*>(&attn_matrix_kernel<DT, HD>);
+  }
+  return reinterpret_cast<const void*>(&attn_vector_kernel<DT, HD>);
+}
+
+const void* stream_kernel(int32_t dtype, int32_t hd, int32_t kernel) {
+  switch (dtype) {
+    case 0: return hd == 64 ? stream_kernel_ptr<0, 64>(kVector) : stream_kernel_ptr<0, 128>(kVector);
+    case 1: return hd == 64 ? stream_kernel_ptr<1, 64>(kernel) : stream_kernel_ptr<1, 128>(kernel);
+    default: return hd == 64 ? stream_kernel_ptr<2, 64>(kernel) : stream_kernel_ptr<2, 128>(kernel);
+  }
+}
+
+template <int DT, int HD>
+void launch_stream_t(const StreamParams& p, int32_t kernel, dim3 grid, size_t lds,
+                     hipStream_t stream) {
   if constexpr (DT != 0) {
     if (kernel == kMatrix) {
-      const dim3 grid(p.B, p.Hkv, p.max_parts);
-      hipLaunchKernelGGL((attn_matrix_kernel<DT, HD, kWaves>), grid, block, 0, stream, p);
-      return note_error("attn_matrix_kernel launch", hipGetLastError());
+      hipLaunchKernelGGL((attn_matrix_kernel<DT, HD>), grid, dim3(kThreads), lds, stream, p);
+      return;
     }
   }
-  const dim3 grid(p.B, p.Hq, p.max_parts);
-  hipLaunchKernelGGL((attn_vector_kernel<DT, HD, kWaves>), grid, block, 0, stream, p);
-  return note_error("attn_vector_kernel launch", hipGetLastError());
+  hipLaunchKernelGGL((attn_vector_kernel<DT, HD>), grid, dim3(kThreads), lds, stream, p);
 }
 
 template <int DT>
-hipError_t launch_partition_d(const AttnParams& p, int32_t kernel, hipStream_t stream) {
-  return p.hd == 64 ? launch_partition_t<DT, 64>(p, kernel, stream)
-                    : launch_partition_t<DT, 128>(p, kernel, stream);
-}
-
-template <int DT>
-hipError_t launch_merge_d(const AttnParams& p, hipStream_t stream) {
-  (void)hipGetLastError();  // drop a stale status left by an earlier, unrelated runtime call
-  const dim3 grid(p.B, p.Hq);
+void launch_merge_t(const StreamParams& p, int H, int GS, hipStream_t stream) {
+  const dim3 grid(p.B, H);
   if (p.hd == 64)
-    hipLaunchKernelGGL((merge_kernel<DT, 64>), grid, dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((merge_kernel<DT, 64>), grid, dim3(64), 0, stream, p, H, GS);
   else
-    hipLaunchKernelGGL((merge_kernel<DT, 128>), grid, dim3(64), 0, stream, p);
-  return note_error("merge_kernel launch", hipGetLastError());
+    hipLaunchKernelGGL((merge_kernel<DT, 128>), grid, dim3(64), 0, stream, p, H, GS);
 }
 
 }  // namespace
@@ -677,21 +713,68 @@ int32_t select_kernel(int32_t dtype, int32_t G, int32_t request) {
   return G >= 2 ? kMatrix : kVector;
 }
 
-hipError_t launch_partition(const AttnParams& p, int32_t dtype, int32_t kernel,
-                            hipStream_t stream) {
-  switch (dtype) {
-    case 0: return launch_partition_d<0>(p, kVector, stream);
-    case 1: return launch_partition_d<1>(p, kernel, stream);
-    default: return launch_partition_d<2>(p, kernel, stream);
-  }
+size_t stream_lds_bytes(int32_t B) { return static_cast<size_t>(B + 1) * sizeof(int32_t); }
+
+int32_t default_workers(int32_t dtype, int32_t hd, int32_t kernel, int32_t B) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int, int, size_t>, int32_t> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const size_t lds = stream_lds_bytes(B);
+  const auto key = std::make_tuple(dev, static_cast<int>(dtype), static_cast<int>(hd),
+                                   static_cast<int>(kernel), lds);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, stream_kernel(dtype, hd, kernel),
+                                                   kThreads, lds) != hipSuccess ||
+      per_cu <= 0)
+    return 0;
+  int64_t grid = static_cast<int64_t>(cus) * per_cu;
+  if (grid >= 8) grid -= grid % 8;  // a whole number of work-groups per XCD
+  const int32_t workers = static_cast<int32_t>(grid * kWaves);
+  cache.emplace(key, workers);
+  return workers;
 }
 
-hipError_t launch_merge(const AttnParams& p, int32_t dtype, hipStream_t stream) {
+hipError_t launch_stream(const StreamParams& p, int32_t dtype, int32_t kernel,
+                         hipStream_t stream) {
+  (void)hipGetLastError();  // drop a stale status left by an earlier, unrelated runtime call
+  const dim3 grid(p.num_workers / kWaves);
+  const size_t lds = stream_lds_bytes(p.B);
   switch (dtype) {
-    case 0: return launch_merge_d<0>(p, stream);
-    case 1: return launch_merge_d<1>(p, stream);
-    default: return launch_merge_d<2>(p, stream);
+    case 0:
+      if (p.hd == 64) launch_stream_t<0, 64>(p, kVector, grid, lds, stream);
+      else launch_stream_t<0, 128>(p, kVector, grid, lds, stream);
+      break;
+    case 1:
+      if (p.hd == 64) launch_stream_t<1, 64>(p, kernel, grid, lds, stream);
+      else launch_stream_t<1, 128>(p, kernel, grid, lds, stream);
+      break;
+    default:
+      if (p.hd == 64) launch_stream_t<2, 64>(p, kernel, grid, lds, stream);
+      else launch_stream_t<2, 128>(p, kernel, grid, lds, stream);
+      break;
   }
+  return note_error(kernel == kMatrix ? "attn_matrix_kernel launch" : "attn_vector_kernel launch",
+                    hipGetLastError());
+}
+
+hipError_t launch_merge(const StreamParams& p, int32_t dtype, int32_t kernel,
+                        hipStream_t stream) {
+  (void)hipGetLastError();  // drop a stale status left by an earlier, unrelated runtime call
+  const int H = kernel == kMatrix ? p.Hkv : p.Hq;
+  const int GS = kernel == kMatrix ? p.Hq / p.Hkv : 1;
+  switch (dtype) {
+    case 0: launch_merge_t<0>(p, H, GS, stream); break;
+    case 1: launch_merge_t<1>(p, H, GS, stream); break;
+    default: launch_merge_t<2>(p, H, GS, stream); break;
+  }
+  return note_error("merge_kernel launch", hipGetLastError());
 }
 
 }  // namespace pkv

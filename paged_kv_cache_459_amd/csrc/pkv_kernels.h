@@ -4,12 +4,13 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <cstddef>
 #include <cstdint>
 
 namespace pkv {
 
-constexpr int kBlockSize = 16;      // tokens per block ([P3] §3.2; [P1] §二 example)
-constexpr int kMaxPartBlocks = 256;  // largest partition: 256 blocks = 4096 tokens
+constexpr int kBlockSize = 16;  // tokens per block ([P3] §3.2; [P1] §二 example)
+constexpr int kWaves = 4;       // waves per work-group of the attention stream kernels
 
 enum AttnKernel : int32_t { kAuto = 0, kVector = 1, kMatrix = 2 };
 
@@ -22,7 +23,8 @@ struct WriteParams {
   int32_t T, Hkv, hd, NB;
 };
 
-struct AttnParams {
+// Arguments of the attention stream pass and of the merge pass.
+struct StreamParams {
   void* out;
   const void* q;
   const void* k_cache;
@@ -31,23 +33,26 @@ struct AttnParams {
   const int32_t* context_lens;
   int32_t B, Hq, Hkv, hd, NB, max_blocks, max_ctx;
   float scale_log2;     // softmax scale times log2(e): scores are kept in base-2 units
-  int32_t part_tokens;  // P, a multiple of 16, at most 16 * kMaxPartBlocks
-  int32_t max_parts;    // MP = ceil(max_ctx / P), at least 1
-  float* ws_m;          // [B][Hq][MP] (natural-log units), null if MP == 1
-  float* ws_l;          // [B][Hq][MP]
-  float* ws_o;          // [B][Hq][MP][hd]
+  int32_t num_workers;  // W: waves of the stream pass, a positive multiple of kWaves
+  int32_t* ws_seg;      // [B + 1] prefix sums of block counts (written by the stream pass)
+  float* ws_ml;         // [W][2][GS][2]: (m, l) of each piece
+  float* ws_o;          // [W][2][GS][hd]: o of each piece
 };
 
 // dtype: 0 f32, 1 f16, 2 bf16 (pkv_dtype). Return the launch status (hipGetLastError).
 hipError_t launch_write(const WriteParams& p, int32_t dtype, hipStream_t stream);
-hipError_t launch_partition(const AttnParams& p, int32_t dtype, int32_t kernel,
-                            hipStream_t stream);
-hipError_t launch_merge(const AttnParams& p, int32_t dtype, hipStream_t stream);
+hipError_t launch_stream(const StreamParams& p, int32_t dtype, int32_t kernel,
+                         hipStream_t stream);
+hipError_t launch_merge(const StreamParams& p, int32_t dtype, int32_t kernel,
+                        hipStream_t stream);
 
 // Records the failing step and the HIP error text for pkv_last_error(); returns err.
 hipError_t note_error(const char* what, hipError_t err);
 
-// Which kernel launch_partition runs for this shape and request (kVector or kMatrix).
+// Which kernel the stream pass runs for this shape and request (kVector or kMatrix).
 int32_t select_kernel(int32_t dtype, int32_t G, int32_t request);
+
+// Waves that fill the current device once with the chosen stream kernel (0 on a HIP error).
+int32_t default_workers(int32_t dtype, int32_t hd, int32_t kernel, int32_t B);
 
 }  // namespace pkv

@@ -122,3 +122,38 @@ def sample_rows(lens, k, rng):
 
 def scale_for(hd):
     return 1.0 / math.sqrt(hd)
+
+
+# ---- the stream pass's cut of the batch into worker ranges (restated from include/pkv.h) ---
+
+def stream_cells(lens, H, W, max_ctx=None):
+    """Which segments the stream pass cuts, and where each piece goes.
+
+    Returns (whole, cut, seg): ``whole`` is the set of segments (i, s) finished inside one
+    worker's range, ``cut`` maps each cut segment to its pieces [(w, slot, tok_lo, tok_hi)] in
+    worker order, ``seg`` the prefix sums S_0..S_B of c_i = ceil(n_i / 16).
+    """
+    n = [min(max(int(x), 0), max_ctx if max_ctx is not None else int(x)) for x in lens]
+    c = [-(-x // 16) for x in n]
+    seg = np.concatenate([[0], np.cumsum(c)]).astype(np.int64)
+    C = int(seg[-1])
+    T = H * C
+    per = -(-T // W) if T else 1
+    whole, cut = set(), {}
+    for s in range(H):
+        for i, ci in enumerate(c):
+            if ci == 0:
+                continue
+            tb = s * C + int(seg[i])
+            te = tb + ci
+            wf, wl = tb // per, (te - 1) // per
+            if wf == wl:
+                whole.add((i, s))
+                continue
+            pieces = []
+            for w in range(wf, wl + 1):
+                a, b = max(tb, w * per), min(te, (w + 1) * per)
+                slot = 1 if tb > w * per else 0
+                pieces.append((w, slot, 16 * (a - tb), min(n[i], 16 * (b - tb))))
+            cut[(i, s)] = pieces
+    return whole, cut, seg

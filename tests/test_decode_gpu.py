@@ -171,95 +171,132 @@ def test_table_entries_past_the_length_are_ignored():
     np.testing.assert_array_equal(ref.view(np.uint8), got.view(np.uint8))
 
 
-@pytest.mark.parametrize("part", [16, 48, 64, 256, 512, 4096])
-@pytest.mark.parametrize("dtype,hq,hkv", [("f32", 2, 2), ("bf16", 8, 2), ("f16", 4, 4)])
-def test_split_context_any_partition_length(part, dtype, hq, hkv):
+def run_passes(p, d, scale, W, kernel=0, max_ctx=None, ws_fill=None):
+    """Stream pass then merge pass with W workers; returns (out, workspace, kernel used)."""
     m = pkv()
-    rng = np.random.default_rng(7)
-    p = H.random_problem(rng, [1, 16, 47, 64, 65, 300, 1025, 2000], hq, hkv, 128, dtype)
-    d = G.device_problem(p)
-    mc = 2000
-    scale = 0.08
-    nbytes = m.pkv_decode_partials_bytes(8, hq, 128, mc, part)
-    partials = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
-    out = torch.empty_like(d["q"])
-    m.pkv_decode_partition(d["q"], d["k_cache"], d["v_cache"], d["tables"], d["lens"],
-                           num_kv_heads=hkv, scale=scale, max_context_len=mc, part_tokens=part,
-                           partials=partials, out=out)
-    m.pkv_decode_merge(out, partials, d["lens"], max_context_len=mc, part_tokens=part)
-    torch.cuda.synchronize()
-    G.assert_close(G.gpu_f64(out, dtype), G.oracle_out(p, scale), dtype, f"P={part}")
-
-
-@pytest.mark.parametrize("dtype,hq,hkv,kernel", [("f32", 2, 2, 0), ("bf16", 8, 2, 0),
-                                                 ("bf16", 8, 2, 1), ("f16", 4, 4, 0)])
-def test_partition_partials_match_oracle(dtype, hq, hkv, kernel):
-    """(m, l, o) of every partition of every sequence longer than one partition."""
-    m = pkv()
-    rng = np.random.default_rng(8)
-    lens = [65, 100, 200, 513, 1000]
-    p = H.random_problem(rng, lens, hq, hkv, 128, dtype)
-    d = G.device_problem(p)
-    part, mc, scale = 64, 1000, 0.1
-    nbytes = m.pkv_decode_partials_bytes(5, hq, 128, mc, part)
-    partials = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
     prev = m.pkv_set_attn_kernel(kernel)
     try:
-        m.pkv_decode_partition(d["q"], d["k_cache"], d["v_cache"], d["tables"], d["lens"],
-                               num_kv_heads=hkv, scale=scale, max_context_len=mc,
-                               part_tokens=part, partials=partials)
+        dt = G.TORCH[p["dtype"]]
+        B = len(p["lengths"])
+        mc = max_ctx if max_ctx is not None else G.max_context(p["lengths"])
+        nbytes = m.pkv_decode_stream_workspace_bytes(B, p["hq"], p["hkv"], p["hd"], dt, W)
+        ws = torch.full((nbytes,), 0xFF if ws_fill is None else ws_fill, dtype=torch.uint8,
+                        device="cuda")
+        out = torch.full_like(d["q"], 7.0)
+        m.pkv_decode_stream(d["q"], d["k_cache"], d["v_cache"], d["tables"], d["lens"],
+                            num_kv_heads=p["hkv"], scale=scale, max_context_len=mc,
+                            num_workers=W, workspace=ws, out=out)
+        after_stream = out.clone()
+        m.pkv_decode_merge(out, ws, num_kv_heads=p["hkv"], num_workers=W)
         torch.cuda.synchronize()
+        used = m.pkv_decode_kernel(p["hq"], p["hkv"], dt)
     finally:
         m.pkv_set_attn_kernel(prev)
-    gm, gl, go = (x.cpu().double().numpy() for x in m.split_partials(partials, 5, hq, 128, mc,
-                                                                     part))
-    want = OA.partition_partials(p["q"], p["k_cache"], p["v_cache"], p["tables"], p["lengths"],
-                                 scale=scale, hkv=hkv, hd=128, bs=16, dtype=dtype,
-                                 part_tokens=part)
+    return out, after_stream, ws, used
+
+
+@pytest.mark.parametrize("W", [4, 8, 12, 36, 64, 256, 1024, 0])
+@pytest.mark.parametrize("dtype,hq,hkv,kernel", [("f32", 2, 2, 0), ("bf16", 8, 2, 0),
+                                                 ("f16", 4, 4, 0), ("bf16", 8, 2, 1)])
+def test_any_worker_count(W, dtype, hq, hkv, kernel):
+    """Stream + merge with few workers (long ranges, several segments per wave) to many (one
+    block per wave, every segment cut), against the oracle. W = 0: the device default."""
+    m = pkv()
+    print(f"[workers] W={W} {dtype} {hq}/{hkv} kernel={kernel}", flush=True)
+    rng = np.random.default_rng(7)
+    p = H.random_problem(rng, [1, 16, 47, 0, 64, 65, 300, 1025, 2000], hq, hkv, 128, dtype)
+    d = G.device_problem(p)
+    if W == 0:
+        prev = m.pkv_set_attn_kernel(kernel)
+        W = m.pkv_decode_num_workers(hq, hkv, 128, G.TORCH[dtype])
+        m.pkv_set_attn_kernel(prev)
+        assert W > 0 and W % 4 == 0
+    out, _, _, _ = run_passes(p, d, 0.08, W, kernel)
+    G.assert_close(G.gpu_f64(out, dtype), G.oracle_out(p, 0.08), dtype, f"W={W}")
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,kernel,W", [("f32", 2, 2, 0, 8), ("bf16", 8, 2, 0, 12),
+                                                   ("bf16", 8, 2, 1, 20), ("f16", 4, 4, 0, 16),
+                                                   ("f16", 7, 1, 0, 4)])
+def test_stream_pieces_match_oracle(dtype, hq, hkv, kernel, W):
+    """The stream pass alone: seg holds the prefix sums (exact); rows of segments inside one
+    range and rows with n = 0 are final; every piece of a cut segment is (m, l, o) over its
+    token range (m in base-2 units); rows of cut segments are left untouched."""
+    m = pkv()
+    rng = np.random.default_rng(8)
+    lens = [65, 100, 0, 200, 513, 1000, 3]
+    p = H.random_problem(rng, lens, hq, hkv, 128, dtype)
+    d = G.device_problem(p)
+    scale = 0.1
+    _, after, ws, used = run_passes(p, d, scale, W, kernel)
+    Hs, gs = (hkv, hq // hkv) if used == 2 else (hq, 1)
+    whole, cut, seg = G.stream_cells(lens, Hs, W)
+    assert cut, "this shape is meant to cut segments"
+    wseg, wml, wo = (x.cpu() for x in m.split_workspace(ws, len(lens), hq, hkv, 128, W, used))
+    np.testing.assert_array_equal(wseg.numpy(), seg.astype(np.int32))
+    got = G.gpu_f64(after, dtype)
+    want = G.oracle_out(p, scale)
+    for i, n in enumerate(lens):
+        if n == 0:
+            assert np.all(got[i] == 0)
+    for (i, s) in whole:
+        heads = list(range(s * gs, (s + 1) * gs))
+        G.assert_close(got[i, heads], want[i, heads], dtype, f"whole segment {(i, s)}")
     tol = G.TOL[dtype]
-    for i, (wm, wl, wo) in enumerate(want):
-        nparts = wm.shape[0]
-        for j in range(nparts):
-            for h in range(hq):
-                assert abs(gm[i, h, j] - wm[j, h]) <= 1e-4 * max(1.0, abs(wm[j, h])), (i, j, h)
-                assert abs(gl[i, h, j] - wl[j, h]) <= 1e-4 * wl[j, h], (i, j, h)
-                err = np.abs(go[i, h, j] / gl[i, h, j] - wo[j, h] / wl[j, h]).max()
-                assert err <= tol, (i, j, h, err)
+    for (i, s), pieces in cut.items():
+        heads = list(range(s * gs, (s + 1) * gs))
+        assert np.all(got[i, heads] == 7.0), "the stream pass must not write a cut row"
+        for (w, slot, lo, hi) in pieces:
+            om, ol, oo = OA.range_partials(p["q"], p["k_cache"], p["v_cache"], p["tables"],
+                                           p["lengths"], seq=i, lo=lo, hi=hi, scale=scale,
+                                           hkv=hkv, hd=128, bs=16, dtype=dtype)
+            for k, h in enumerate(heads):
+                gm = float(wml[w, slot, k, 0])
+                gl = float(wml[w, slot, k, 1])
+                go = wo[w, slot, k].double().numpy()
+                wm2 = om[h] / math.log(2.0)
+                assert abs(gm - wm2) <= 1e-4 * max(1.0, abs(wm2)), ((i, s), w, slot, h)
+                assert abs(gl - ol[h]) <= 1e-4 * ol[h], ((i, s), w, slot, h)
+                assert np.abs(go / gl - oo[h] / ol[h]).max() <= tol, ((i, s), w, slot, h)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 def test_merge_pass_alone(dtype):
-    """The merge kernel on partials written from the oracle (float32), against the oracle's
-    log-sum-exp recombination of those same values."""
+    """The merge kernel on a workspace written on the host (prefix sums of the lengths and
+    random pieces for every cut segment), against the oracle's log-sum-exp recombination of
+    those values; rows of uncut segments stay untouched."""
     m = pkv()
     rng = np.random.default_rng(9)
-    B, hq, hd, part, mc = 6, 3, 128, 64, 500
-    lens = np.array([0, 64, 65, 300, 499, 500], np.int32)
-    mp = -(-mc // part)
-    cells = B * hq * mp
-    a = -(-cells * 4 // 256) * 256
-    buf = np.zeros(2 * a + cells * hd * 4, np.uint8)
-    M = buf[:cells * 4].view(np.float32).reshape(B, hq, mp)
-    L = buf[a:a + cells * 4].view(np.float32).reshape(B, hq, mp)
-    O = buf[2 * a:].view(np.float32).reshape(B, hq, mp, hd)
-    M[:] = rng.normal(0, 3, M.shape).astype(np.float32)
-    L[:] = rng.uniform(0.5, 60, L.shape).astype(np.float32)
-    O[:] = (rng.normal(0, 1, O.shape) * L[..., None]).astype(np.float32)
-    M[3, 1, 2] = -np.inf  # an empty partition
-    L[3, 1, 2] = 0
-    O[3, 1, 2] = 0
+    hq, hkv, hd, W = 3, 3, 128, 8
+    lens = [0, 64, 65, 300, 499, 500]
+    B = len(lens)
+    whole, cut, seg = G.stream_cells(lens, hq, W)
+    nbytes = m.pkv_decode_stream_workspace_bytes(B, hq, hkv, hd, G.TORCH[dtype], W)
+    host = torch.zeros(nbytes, dtype=torch.uint8)
+    wseg, wml, wo = m.split_workspace(host, B, hq, hkv, hd, W, 1)
+    wseg.copy_(torch.from_numpy(seg.astype(np.int32)))
+    wml[..., 0] = torch.from_numpy(rng.normal(0, 3, (W, 2, 1)).astype(np.float32))
+    wml[..., 1] = torch.from_numpy(rng.uniform(0.5, 60, (W, 2, 1)).astype(np.float32))
+    wo.copy_(torch.from_numpy((rng.normal(0, 1, (W, 2, 1, hd)) *
+                               wml[..., 1:].numpy()).astype(np.float32)))
+    first = next(iter(cut.values()))[0]
+    wml[first[0], first[1], 0, 0] = -float("inf")  # a piece with no valid token
+    wml[first[0], first[1], 0, 1] = 0.0
+    wo[first[0], first[1], 0] = 0.0
     out = torch.full((B, hq, hd), 7.0, dtype=G.TORCH[dtype], device="cuda")
-    m.pkv_decode_merge(out, torch.from_numpy(buf).cuda(), torch.from_numpy(lens).cuda(),
-                       max_context_len=mc, part_tokens=part)
+    m.pkv_decode_merge(out, host.cuda(), num_kv_heads=hkv, num_workers=W)
     torch.cuda.synchronize()
     got = out.double().cpu().numpy()
-    for i, n in enumerate(lens):
-        npart = -(-int(n) // part)
+    for i in range(B):
         for h in range(hq):
-            if npart <= 1:
-                assert np.all(got[i, h] == 7.0)  # untouched: finished by the first pass
+            if (i, h) not in cut:
+                assert np.all(got[i, h] == 7.0)  # finished by the stream pass, or n = 0
                 continue
-            want = OA.merge_partials(M[i, h, :npart], L[i, h, :npart], O[i, h, :npart])
+            cells = [(w, slot) for (w, slot, _, _) in cut[(i, h)]]
+            M2 = np.array([float(wml[w, sl, 0, 0]) for w, sl in cells])
+            Lv = np.array([float(wml[w, sl, 0, 1]) for w, sl in cells])
+            Ov = np.stack([wo[w, sl, 0].double().numpy() for w, sl in cells])
+            want = OA.merge_partials(M2 * math.log(2.0), Lv, Ov)
             assert np.abs(got[i, h] - want).max() <= G.TOL[dtype] * max(1, np.abs(want).max())
 
 

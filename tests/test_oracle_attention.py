@@ -229,6 +229,24 @@ def test_partition_merge_equals_unsplit(part):
                                        rtol=0, atol=1e-12)
 
 
+def test_arbitrary_cuts_merge_to_unsplit():
+    """Any cut of [0, n) into consecutive token ranges (including empty and past-the-end
+    ones) recombines to the unsplit result."""
+    rng = np.random.default_rng(16)
+    p = H.random_problem(rng, [1, 37, 300], 6, 2, 64, "f16")
+    ref = run_oracle(p, scale=0.15)
+    for i, n in enumerate(p["lengths"]):
+        for trial in range(4):
+            cuts = sorted(set([0, int(n) + 5] + rng.integers(0, int(n) + 6, size=trial * 3).tolist()))
+            pieces = [A.range_partials(p["q"], p["k_cache"], p["v_cache"], p["tables"],
+                                       p["lengths"], seq=i, lo=a, hi=b, scale=0.15, hkv=2, hd=64,
+                                       bs=16, dtype="f16") for a, b in zip(cuts, cuts[1:])]
+            m, l, o = (np.stack(x) for x in zip(*pieces))
+            for h in range(6):
+                np.testing.assert_allclose(A.merge_partials(m[:, h], l[:, h], o[:, h]), ref[i, h],
+                                           rtol=0, atol=1e-12)
+
+
 def test_single_token_partition_closed_form():
     """Partitions of one token each: m = that token's score, l = 1, o = its V row."""
     rng = np.random.default_rng(15)
