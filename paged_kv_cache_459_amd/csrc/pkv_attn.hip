@@ -619,15 +619,17 @@ attn_matrix_kernel(const StreamParams p) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Merge of the pieces of segments cut by worker-range boundaries. One wave per segment
-// (sequence i, head slot h); the segment's GS q heads are done one after another, pieces
-// combined in worker order (deterministic). Segments inside one range, and empty ones, were
-// finished by the stream pass and are left alone.
+// Merge of the pieces of segments cut by worker-range boundaries. One wave per output row
+// (sequence i, q head hh of head slot hh / GS). The pieces' (m, l) are read one per lane and
+// weighted in parallel; o is accumulated over the pieces in worker order (deterministic),
+// with the loads of consecutive pieces issued back to back. Rows of segments inside one
+// range, and rows with n = 0, were finished by the stream pass and are left alone.
 template <int DT, int HD>
 __global__ void __launch_bounds__(64)
 merge_kernel(const StreamParams p, int H, int GS) {
   constexpr int R = HD / 64;
-  const int i = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int i = blockIdx.x, hh = blockIdx.y, lane = threadIdx.x;
+  const int h = hh / GS, n = hh - h * GS;
   const int C = p.ws_seg[p.B];
   const int s0 = p.ws_seg[i];
   const int c = p.ws_seg[i + 1] - s0;
@@ -637,33 +639,56 @@ merge_kernel(const StreamParams p, int H, int GS) {
   const int tb = h * C + s0, te = tb + c;
   const int wf = tb / per, wl = (te - 1) / per;
   if (wf == wl) return;
-  for (int n = 0; n < GS; ++n) {
-    auto cell = [&](int wk) {
-      const int slot = (wk == wf && wf * per < tb) ? 1 : 0;
-      return (static_cast<size_t>(wk) * 2 + slot) * GS + n;
-    };
-    float M = kNegInf;
-    for (int wk = wf + lane; wk <= wl; wk += 64) M = fmaxf(M, p.ws_ml[cell(wk) * 2]);
+  const int np = wl - wf + 1;
+  // cell of piece k (worker wf + k): slot 1 only for the first worker if the segment starts
+  // inside its range after other segments
+  const int slot0 = wf * per < tb ? 1 : 0;
+  auto cell = [&](int k) {
+    return (static_cast<size_t>(wf + k) * 2 + (k == 0 ? slot0 : 0)) * GS + n;
+  };
+  constexpr int U = 16;  // pieces whose o loads are in flight together
+  float M = kNegInf;
+  for (int k = lane; k < np; k += 64) M = fmaxf(M, p.ws_ml[cell(k) * 2]);
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float L = 0.f, O[R];
+  for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float Lpart = 0.f, O[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) O[r] = 0.f;
-    for (int wk = wf; wk <= wl; ++wk) {
-      const size_t cl = cell(wk);
-      const float mj = p.ws_ml[cl * 2];
-      if (mj == kNegInf) continue;  // a piece with no valid token
-      const float wt = exp2_fast(mj - M);
-      L = fmaf(wt, p.ws_ml[cl * 2 + 1], L);
-      const float* oj = p.ws_o + cl * HD;
-#pragma unroll
-      for (int r = 0; r < R; ++r) O[r] = fmaf(wt, oj[lane + 64 * r], O[r]);
+  for (int r = 0; r < R; ++r) O[r] = 0.f;
+  for (int base = 0; base < np; base += 64) {
+    float wt = 0.f;  // weight of piece base + lane; a piece with no valid token weighs 0
+    if (base + lane < np) {
+      const size_t cl = cell(base + lane);
+      const float mk = p.ws_ml[cl * 2];
+      wt = mk == kNegInf ? 0.f : exp2_fast(mk - M);
+      Lpart = fmaf(wt, p.ws_ml[cl * 2 + 1], Lpart);
     }
-    const size_t orow = (static_cast<size_t>(i) * p.Hq + h * GS + n) * HD;
+    const int cnt = uniform(min(64, np - base));
+    for (int k0 = 0; k0 < cnt; k0 += U) {
+      float ov[U][R];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-      Elem<DT>::put(p.out, orow + lane + 64 * r, L > 0.f ? O[r] / L : 0.f);
+      for (int u = 0; u < U; ++u) {  // independent loads (a piece past the end re-reads piece 0)
+        const float* ok = p.ws_o + cell(k0 + u < cnt ? base + k0 + u : 0) * HD;
+#pragma unroll
+        for (int r = 0; r < R; ++r) ov[u][r] = ok[lane + 64 * r];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (k0 + u < cnt) {
+          const float wk = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt), k0 + u));
+#pragma unroll
+          for (int r = 0; r < R; ++r) O[r] = fmaf(wk, ov[u][r], O[r]);
+        }
+      }
+    }
   }
+  float L = Lpart;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) L += __shfl_xor(L, off);
+  const size_t orow = (static_cast<size_t>(i) * p.Hq + hh) * HD;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    Elem<DT>::put(p.out, orow + lane + 64 * r, L > 0.f ? O[r] / L : 0.f);
 }
 
 // ---- host side ------------------------------------------------------------------------------
@@ -698,7 +723,7 @@ void launch_stream_t(const StreamParams& p, int32_t kernel, dim3 grid, size_t ld
 
 template <int DT>
 void launch_merge_t(const StreamParams& p, int H, int GS, hipStream_t stream) {
-  const dim3 grid(p.B, H);
+  const dim3 grid(p.B, H * GS);
   if (p.hd == 64)
     hipLaunchKernelGGL((merge_kernel<DT, 64>), grid, dim3(64), 0, stream, p, H, GS);
   else
