@@ -4,8 +4,9 @@
 One step = one decode step of every sequence in the batch, through the whole path:
   1. allocate on demand: the C++ allocator appends one token per sequence (a fresh block for
      sequences whose last block is full) and returns the new tokens' slots;
-  2. export the block tables and lengths into pinned host buffers and copy them (with the
-     slots) to the device;
+  2. bring the block tables (pinned host copy: the entries of the blocks just opened) and
+     the lengths up to date and copy them, with the slots, to the device on a copy stream
+     (double-buffered, so the copy overlaps the previous step's kernels);
   3. pkv_write: scatter the new tokens' K/V into their slots;
   4. paged decode attention: the stream pass (every wave streams an equal share of the
      batch's K/V tiles), then the log-sum-exp merge of the segments cut between waves -- the
@@ -138,6 +139,13 @@ class Workload:
         self.copied = [torch.cuda.Event() for _ in range(2)]
         self.done = [torch.cuda.Event() for _ in range(2)]
         self.step_no = 0
+        # Both sets start from a full export of the allocator's tables; after that each step
+        # only adds the blocks it opened (tables only grow in a decode loop without forks).
+        for lens_h, _, tables_h in self.host_views:
+            self.alloc.tables(self.seqs, self.max_blocks, tables_out=tables_h, lens_out=lens_h)
+        self.lens = self.host_views[0][0].copy()  # lengths before the next step's token
+        self.pending = [[], []]  # table entries set s has not received yet
+        self.rows = np.arange(self.B)
         self.ones = np.ones(self.B, np.int32)
         self.kernel = pkv.pkv_decode_kernel(self.Hq, self.Hkv, self.dt)
         self.W = pkv.pkv_decode_num_workers(self.Hq, self.Hkv, self.hd, self.dt)
@@ -176,7 +184,15 @@ def run_step(wl, torch, pkv, events=None):
     lens_h, slots_h, tables_h = wl.host_views[s]
     lens_d, slots_d, tables_d = wl.dev_views[s]
     wl.alloc.append(wl.seqs, wl.ones, slots_out=slots_h)  # 1. allocate on demand
-    wl.alloc.tables(wl.seqs, wl.max_blocks, tables_out=tables_h, lens_out=lens_h)
+    opened = wl.lens % 16 == 0  # the new token is the first of a fresh block
+    update = (wl.rows[opened], wl.lens[opened] // 16, slots_h[opened] // 16)
+    wl.lens += 1
+    wl.pending[0].append(update)
+    wl.pending[1].append(update)
+    for r, c, b in wl.pending[s]:  # 2. this set's table rows catch up, lengths refreshed
+        tables_h[r, c] = b
+    wl.pending[s].clear()
+    lens_h[:] = wl.lens
     with torch.cuda.stream(wl.copy_stream):  # 2. tables, lengths, slots to the device
         wl.dev[s].copy_(wl.pin[s], non_blocking=True)
         wl.copied[s].record(wl.copy_stream)
@@ -262,8 +278,12 @@ def main():
 
     part_ms = [e[0].elapsed_time(e[1]) for e in evs]
     merge_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    # A table only ever gains entries, so the final tables hold every step's blocks.
+    # A table only ever gains entries, so the final tables hold every step's blocks; they must
+    # be exactly what the allocator exports.
     final_tables = wl.host_views[wl.last_set][2].copy()
+    ref_tables, ref_lens = wl.alloc.tables(wl.seqs, wl.max_blocks)
+    assert np.array_equal(final_tables, ref_tables) and np.array_equal(wl.lens, ref_lens), \
+        "incremental block tables diverged from the allocator's export"
     kv_logical = [wl.kv_bytes(lens) for lens in lens_per_step]
     kv = [wl.unique_kv_bytes(lens, final_tables) for lens in lens_per_step]
     algo = [b + wl.qo_bytes() for b in kv]

@@ -65,10 +65,10 @@ SIGNATURES = {
     "pkv_alloc_create": (c_i32, [c_i32, c_i32, P_i32, ctypes.POINTER(c_vp)]),
     "pkv_alloc_destroy": (None, [c_vp]),
     "pkv_alloc_add_seq": (c_i32, [c_vp, c_i64]),
-    "pkv_alloc_append": (c_i32, [c_vp, c_i32, P_i64, P_i32, P_i32, P_i32, P_i32, P_i32]),
+    "pkv_alloc_append": (c_i32, [c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "pkv_alloc_fork": (c_i32, [c_vp, c_i64, c_i64]),
     "pkv_alloc_free": (c_i32, [c_vp, c_i64]),
-    "pkv_alloc_tables": (c_i32, [c_vp, c_i32, P_i64, c_i32, P_i32, P_i32]),
+    "pkv_alloc_tables": (c_i32, [c_vp, c_i32, c_vp, c_i32, c_vp, c_vp]),
     "pkv_alloc_num_free": (c_i32, [c_vp]),
     "pkv_alloc_refcount": (c_i32, [c_vp, c_i32]),
     "pkv_alloc_seq_len": (c_i64, [c_vp, c_i64]),

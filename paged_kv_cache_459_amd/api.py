@@ -46,6 +46,13 @@ def _need(t, name, dtype=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+def _as_c(a, dtype):
+    """A C-contiguous NumPy array of ``dtype`` (no copy when ``a`` already is one)."""
+    if isinstance(a, np.ndarray) and a.dtype == dtype and a.flags.c_contiguous:
+        return a
+    return np.ascontiguousarray(np.asarray(a, dtype=dtype))
+
+
 def cache_shapes(num_blocks, num_kv_heads, head_dim, dtype):
     """Shapes of the K and V caches in the library's layout (see include/pkv.h)."""
     x = 16 // _ELEM_BYTES[pkv_dtype(dtype)]
@@ -206,6 +213,8 @@ class BlockAllocator:
         self._h = h
         self.num_blocks = num_blocks
         self.block_size = block_size
+        self._cow = np.empty((2, 1), np.int32)  # copy-on-write pairs, reused across calls
+        self._ncow = ctypes.c_int32(0)
 
     def close(self):
         if self._h:
@@ -223,25 +232,22 @@ class BlockAllocator:
 
     def append(self, seqs, ntok, want_slots=True, slots_out=None):
         """Returns (slots int32 [sum ntok], cow pairs int32 [n_cow, 2])."""
-        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
-        ntok = np.ascontiguousarray(np.asarray(ntok, dtype=np.int32))
+        seqs = _as_c(seqs, np.int64)
+        ntok = _as_c(ntok, np.int32)
         n = len(seqs)
-        total = int(ntok.sum()) if n else 0
+        slots = None
         if want_slots:
-            slots = slots_out if slots_out is not None else np.empty(total, np.int32)
-        src = np.empty(max(n, 1), np.int32)
-        dst = np.empty(max(n, 1), np.int32)
-        ncow = ctypes.c_int32(0)
-        pi32 = ctypes.POINTER(ctypes.c_int32)
-        check(lib.pkv_alloc_append(
-            self._h, n, seqs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
-            ntok.ctypes.data_as(pi32),
-            slots.ctypes.data_as(pi32) if want_slots else None,
-            src.ctypes.data_as(pi32), dst.ctypes.data_as(pi32), ctypes.byref(ncow)),
-            "pkv_alloc_append")
-        k = ncow.value
-        cows = np.stack([src[:k], dst[:k]], axis=1) if k else np.zeros((0, 2), np.int32)
-        return (slots if want_slots else None), cows
+            slots = slots_out if slots_out is not None else np.empty(int(ntok.sum()), np.int32)
+        if self._cow.shape[1] < max(n, 1):
+            self._cow = np.empty((2, max(n, 1)), np.int32)
+        cow = self._cow
+        check(lib.pkv_alloc_append(self._h, n, seqs.ctypes.data, ntok.ctypes.data,
+                                   slots.ctypes.data if want_slots else None, cow[0].ctypes.data,
+                                   cow[1].ctypes.data, ctypes.byref(self._ncow)),
+              "pkv_alloc_append")
+        k = self._ncow.value
+        pairs = cow[:, :k].T.copy() if k else np.zeros((0, 2), np.int32)
+        return slots, pairs
 
     def fork(self, parent, child):
         check(lib.pkv_alloc_fork(self._h, int(parent), int(child)), "pkv_alloc_fork")
@@ -250,14 +256,12 @@ class BlockAllocator:
         check(lib.pkv_alloc_free(self._h, int(seq)), "pkv_alloc_free")
 
     def tables(self, seqs, max_blocks, tables_out=None, lens_out=None):
-        seqs = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64))
+        seqs = _as_c(seqs, np.int64)
         n = len(seqs)
         tables = tables_out if tables_out is not None else np.empty((n, max_blocks), np.int32)
         lens = lens_out if lens_out is not None else np.empty(n, np.int32)
-        pi32 = ctypes.POINTER(ctypes.c_int32)
-        check(lib.pkv_alloc_tables(self._h, n, seqs.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
-                                   max_blocks, tables.ctypes.data_as(pi32),
-                                   lens.ctypes.data_as(pi32)), "pkv_alloc_tables")
+        check(lib.pkv_alloc_tables(self._h, n, seqs.ctypes.data, max_blocks, tables.ctypes.data,
+                                   lens.ctypes.data), "pkv_alloc_tables")
         return tables, lens
 
     def num_free(self):

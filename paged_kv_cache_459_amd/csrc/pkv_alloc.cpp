@@ -24,6 +24,7 @@ namespace {
 struct Seq {
   std::vector<int32_t> blocks;  // physical blocks, logical order
   int64_t len = 0;              // tokens
+  uint64_t mark = 0;            // last append call that named this sequence (duplicate check)
 };
 
 }  // namespace
@@ -34,6 +35,8 @@ struct pkv_allocator {
   std::deque<int32_t> free_list;
   std::vector<int32_t> ref;
   std::unordered_map<int64_t, Seq> seqs;
+  uint64_t calls = 0;             // append calls so far (stamps Seq::mark)
+  std::vector<Seq*> batch;        // reused per append call
 
   // Blocks needed to append ntok tokens to s: a copy-on-write block when the last block is
   // partly filled and shared, plus the new blocks the extra tokens spill into.
@@ -93,17 +96,34 @@ pkv_status pkv_alloc_append(pkv_allocator* a, int32_t n, const int64_t* seqs, co
   if ((cow_src == nullptr) != (cow_dst == nullptr) || ((cow_src != nullptr) != (n_cow != nullptr)))
     return PKV_ERR_INVALID_ARG;
   // Validate everything and count the blocks the whole batch needs before changing anything.
-  std::vector<Seq*> ptr(n);
-  std::unordered_set<int64_t> distinct;
-  int64_t total = 0;
-  for (int32_t k = 0; k < n; ++k) {
+  // Duplicate ids are found by stamping each named sequence with this call's number; an id
+  // that is not present sends the check to a set, so that a repeated unknown id still reads
+  // as a duplicate (PKV_ERR_INVALID_ARG) before it reads as unknown.
+  for (int32_t k = 0; k < n; ++k)
     if (ntok[k] < 0) return PKV_ERR_INVALID_ARG;
-    if (!distinct.insert(seqs[k]).second) return PKV_ERR_INVALID_ARG;
-  }
+  std::vector<Seq*>& ptr = a->batch;
+  ptr.assign(n, nullptr);
+  const uint64_t call = ++a->calls;
+  bool unknown = false, dup = false;
   for (int32_t k = 0; k < n; ++k) {
     auto it = a->seqs.find(seqs[k]);
-    if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+    if (it == a->seqs.end()) {
+      unknown = true;
+      continue;
+    }
+    if (it->second.mark == call) dup = true;
+    it->second.mark = call;
     ptr[k] = &it->second;
+  }
+  if (unknown && !dup) {
+    std::unordered_set<int64_t> distinct;
+    for (int32_t k = 0; k < n; ++k)
+      if (!distinct.insert(seqs[k]).second) dup = true;
+  }
+  if (dup) return PKV_ERR_INVALID_ARG;
+  if (unknown) return PKV_ERR_UNKNOWN_SEQ;
+  int64_t total = 0;
+  for (int32_t k = 0; k < n; ++k) {
     bool cow;
     int64_t fresh;
     a->needs(*ptr[k], ntok[k], &cow, &fresh);
