@@ -215,35 +215,47 @@ def run_step(wl, torch, pkv, events=None):
 
 
 def cpu_baseline(wl, torch, W, seconds):
-    """The oracle (float64 NumPy, one thread) on a bounded, seeded sample of the sequences."""
+    """The oracle (float64 NumPy, one thread) on the last step's sequences, in a seeded order,
+    pass after pass until about ``seconds`` of oracle time have been spent."""
     from threadpoolctl import threadpool_limits
 
     from oracle import attention as OA
     rng = np.random.default_rng(12345)
     order = rng.permutation(wl.B)
-    spent, done, kv = 0.0, 0, 0
-    lens, tables = wl.host_views[wl.last_set][0].copy(), wl.host_views[wl.last_set][2].copy()
+    spent, done, kv, passes = 0.0, 0, 0, 0
+    lens = wl.host_views[wl.last_set][0].copy()
+    tables = wl.host_views[wl.last_set][2].copy()
+    inputs = {}
     with threadpool_limits(limits=1):
-        for i in order:
-            n = int(lens[i])
-            nbk = -(-n // 16)
-            ids = torch.from_numpy(tables[i, :nbk].astype(np.int64)).cuda()
-            kc = W.to_storage_numpy(wl.k_cache.index_select(0, ids), wl.shape.dtype)
-            vc = W.to_storage_numpy(wl.v_cache.index_select(0, ids), wl.shape.dtype)
-            q = W.to_storage_numpy(wl.q[i:i + 1], wl.shape.dtype)
-            t0 = time.perf_counter()
-            OA.decode_attention(q, kc.reshape(-1), vc.reshape(-1),
-                                np.arange(nbk, dtype=np.int32)[None], np.int32([n]),
-                                scale=wl.scale, hkv=wl.Hkv, hd=wl.hd, bs=16,
-                                dtype=wl.shape.dtype)
-            spent += time.perf_counter() - t0
-            done += 1
-            kv += n * 2 * wl.Hkv * wl.hd * wl.eb
-            if spent >= seconds:
+        while spent < seconds:
+            for i in order:
+                if i not in inputs:  # exact host copies of the sequence's blocks (untimed)
+                    n = int(lens[i])
+                    nbk = -(-n // 16)
+                    ids = torch.from_numpy(tables[i, :nbk].astype(np.int64)).cuda()
+                    inputs[i] = (n, nbk,
+                                 W.to_storage_numpy(wl.k_cache.index_select(0, ids),
+                                                    wl.shape.dtype).reshape(-1),
+                                 W.to_storage_numpy(wl.v_cache.index_select(0, ids),
+                                                    wl.shape.dtype).reshape(-1),
+                                 W.to_storage_numpy(wl.q[i:i + 1], wl.shape.dtype))
+                n, nbk, kc, vc, q = inputs[i]
+                t0 = time.perf_counter()
+                OA.decode_attention(q, kc, vc, np.arange(nbk, dtype=np.int32)[None],
+                                    np.int32([n]), scale=wl.scale, hkv=wl.Hkv, hd=wl.hd, bs=16,
+                                    dtype=wl.shape.dtype)
+                spent += time.perf_counter() - t0
+                done += 1
+                kv += n * 2 * wl.Hkv * wl.hd * wl.eb
+                if spent >= seconds:
+                    break
+            passes += 1
+            if passes > 1000:
                 break
     return {"value": round(kv / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {wl.B} sequences (seeded order), {kv / 1e6:.1f} MB of K/V, "
-                      f"{spent:.1f} s of oracle time, one thread",
+            "sample": f"{done} sequence-attentions over {passes} pass(es) of the step's {wl.B} "
+                      f"sequences in a seeded order, {kv / 1e6:.1f} MB of K/V, {spent:.1f} s of "
+                      f"oracle time on one thread (host copies of the blocks not timed)",
             "tokens_per_s_per_layer": round(done / spent, 3)}
 
 

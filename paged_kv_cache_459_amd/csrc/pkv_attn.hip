@@ -109,6 +109,27 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Makes the loaded value count as used here, so the wait for its load is placed here. Used on
+// the rare path that reloads q at a segment start: left pending, that load would make the
+// compiler's wait-count merge at the end of the branch wait for every load in flight (the
+// next tile's K and V included) before each tile's first multiply.
+__device__ __forceinline__ void settle(uint4& v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+
+// Opaque to the optimiser: the tile registers are "redefined" at the point of use, so no
+// computation on them (such as unpacking 16-bit halves) can be hoisted up next to the load
+// that fills them, where it would force an early wait for that load and serialise the
+// stream of tiles.
+__device__ __forceinline__ uint4 pinned(uint4 v) {
+  settle(v);
+  return v;
+}
+__device__ __forceinline__ uint2 pinned(uint2 v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y));
+  return v;
+}
+
 // Per-dtype element access. DT: 0 = f32, 1 = f16, 2 = bf16.
 template <int DT>
 struct Elem;
@@ -168,6 +189,24 @@ struct Elem<2> {
     static_cast<__bf16*>(base)[idx] = static_cast<__bf16>(x);
   }
 };
+
+// Zeroes the tokens of a 16-byte V chunk that are not valid. The chunk holds tokens
+// t0 .. t0 + 16/EB - 1 of one dim row; with EB = 2 each 32-bit word holds two tokens.
+template <int EB>
+__device__ __forceinline__ uint4 mask_tokens(uint4 v, int t0, int valid) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (EB == 2) {
+      const uint32_t lo = t0 + 2 * i < valid ? 0x0000FFFFu : 0u;
+      const uint32_t hi = t0 + 2 * i + 1 < valid ? 0xFFFF0000u : 0u;
+      w[i] &= lo | hi;
+    } else {
+      w[i] &= t0 + i < valid ? 0xFFFFFFFFu : 0u;
+    }
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
 
 __device__ __forceinline__ int clamp_len(const StreamParams& p, int i) {
   return min(max(p.context_lens[i], 0), p.max_ctx);
@@ -345,6 +384,7 @@ attn_vector_kernel(const StreamParams p) {
     };
 
     auto step = [&](int k, auto load_next) {
+      constexpr bool kLoadNext = decltype(load_next)::value;
       const int seq = uniform(__builtin_amdgcn_readlane(ti.seq, k));
       const int hm = uniform(__builtin_amdgcn_readlane(ti.hm, k));
       const int h = hm >> 16, valid = hm & 31;
@@ -357,11 +397,13 @@ attn_vector_kernel(const StreamParams p) {
             static_cast<const char*>(p.q) + (static_cast<size_t>(seq) * p.Hq + h) * HD * EB);
 #pragma unroll
         for (int j = 0; j < NL; ++j) qv[j] = qp[4 * j + row_id];
+#pragma unroll
+        for (int j = 0; j < NL; ++j) settle(qv[j]);
       }
       float s = 0.f;
 #pragma unroll
-      for (int j = 0; j < NL; ++j) s = E::dot(qv[j], kr[j], s);
-      if constexpr (decltype(load_next)::value) load_k(k + 1);
+      for (int j = 0; j < NL; ++j) s = E::dot(qv[j], pinned(kr[j]), s);
+      if constexpr (kLoadNext) load_k(k + 1);
       s += __shfl_xor(s, 16);
       s += __shfl_xor(s, 32);
       s *= p.scale_log2;
@@ -380,18 +422,21 @@ attn_vector_kernel(const StreamParams p) {
       float pv[X];
 #pragma unroll
       for (int x = 0; x < X; ++x) pv[x] = s_p[w][X * vsub + x];
+      uint4 vt[NL];
+#pragma unroll
+      for (int j = 0; j < NL; ++j) vt[j] = pinned(vr[j]);
+      if (valid < kBlockSize) {  // partly filled (or unreadable) block: zero the invalid tokens
+#pragma unroll
+        for (int j = 0; j < NL; ++j) vt[j] = mask_tokens<EB>(vt[j], X * vsub, valid);
+      }
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
         float a = acc[j] * alpha;
 #pragma unroll
-        for (int x = 0; x < X; ++x) {
-          float vx = E::get(vr[j], x);
-          if (valid < kBlockSize) vx = (X * vsub + x < valid) ? vx : 0.f;
-          a = fmaf(pv[x], vx, a);
-        }
+        for (int x = 0; x < X; ++x) a = fmaf(pv[x], E::get(vt[j], x), a);
         acc[j] = a;
       }
-      if constexpr (decltype(load_next)::value) load_v(k + 1);
+      if constexpr (kLoadNext) load_v(k + 1);
       wave_lds_sync();
       if (hm & kEnd) {  // last tile of the segment in this range: emit
         const float l = row_sum16(lsum);
@@ -546,10 +591,12 @@ attn_matrix_kernel(const StreamParams p) {
 #pragma unroll
           for (int s = 0; s < KS; ++s) qb[s] = make_uint4(0, 0, 0, 0);
         }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) settle(qb[s]);
       }
       float4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < KS; ++s) sacc = M16::qk(kr[s], qb[s], sacc);
+      for (int s = 0; s < KS; ++s) sacc = M16::qk(pinned(kr[s]), qb[s], sacc);
       if constexpr (decltype(load_next)::value) load_k(k + 1);
       float sc[4];
 #pragma unroll
@@ -573,17 +620,20 @@ attn_matrix_kernel(const StreamParams p) {
       lsum = fmaf(lsum, alpha, (pr[0] + pr[1]) + (pr[2] + pr[3]));
       m = m_new;
       const uint2 pb = make_uint2(M16::pack2(pr[0], pr[1]), M16::pack2(pr[2], pr[3]));
-      uint2 vmask = make_uint2(0xFFFFFFFFu, 0xFFFFFFFFu);
-      if (valid < kBlockSize) {
+      uint2 vt[VT];
+#pragma unroll
+      for (int j = 0; j < VT; ++j) vt[j] = pinned(vr[j]);
+      if (valid < kBlockSize) {  // partly filled (or unreadable) block: zero the invalid tokens
         const int base = 4 * g;
-        vmask.x = (base + 0 < valid ? 0x0000FFFFu : 0u) | (base + 1 < valid ? 0xFFFF0000u : 0u);
-        vmask.y = (base + 2 < valid ? 0x0000FFFFu : 0u) | (base + 3 < valid ? 0xFFFF0000u : 0u);
+        const uint32_t mx =
+            (base + 0 < valid ? 0x0000FFFFu : 0u) | (base + 1 < valid ? 0xFFFF0000u : 0u);
+        const uint32_t my =
+            (base + 2 < valid ? 0x0000FFFFu : 0u) | (base + 3 < valid ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int j = 0; j < VT; ++j) vt[j] = make_uint2(vt[j].x & mx, vt[j].y & my);
       }
 #pragma unroll
-      for (int j = 0; j < VT; ++j) {
-        const uint2 va = make_uint2(vr[j].x & vmask.x, vr[j].y & vmask.y);
-        o[j] = M16::pv(va, pb, o[j] * alpha);
-      }
+      for (int j = 0; j < VT; ++j) o[j] = M16::pv(vt[j], pb, o[j] * alpha);
       if constexpr (decltype(load_next)::value) load_v(k + 1);
       if (hm & kEnd) {  // last tile of the segment in this range: emit
         float l = lsum + __shfl_xor(lsum, 16);
