@@ -7,10 +7,10 @@ One step = one decode step of every sequence in the batch, through the whole pat
   2. bring the block tables (pinned host copy: the entries of the blocks just opened) and
      the lengths up to date and copy them, with the slots, to the device on a copy stream
      (double-buffered, so the copy overlaps the previous step's kernels);
-  3. pkv_write: scatter the new tokens' K/V into their slots;
-  4. paged decode attention: the stream pass (every wave streams an equal share of the
-     batch's K/V tiles), then the log-sum-exp merge of the segments cut between waves -- the
-     two passes pkv_decode_attn is made of.
+  3. + 4. the decode step's two kernels (pkv_decode_append_attn): the stream pass, which
+     attends with each sequence's new K/V taken from the step's input rows (every wave
+     streams an equal share of the batch's K/V tiles), then the merge pass: the log-sum-exp
+     merge of the segments cut between waves, and the stores of the new K/V into their slots.
 
 Prints one JSON line: the metric (KV-read GB/s over the timed steps), decode tokens/s per
 layer, the roofline figure of the stream kernel (algorithmic bytes / its mean duration,
@@ -173,7 +173,9 @@ class Workload:
         return int(best.sum()) * 2 * self.Hkv * self.hd * self.eb
 
     def qo_bytes(self):
-        return 2 * self.B * self.Hq * self.hd * self.eb
+        """q read and out written, plus the newest token's K/V read from k_new/v_new and
+        stored into its slot (the stream pass does the step's cache write)."""
+        return 2 * self.B * self.Hq * self.hd * self.eb + 4 * self.B * self.Hkv * self.hd * self.eb
 
 
 def run_step(wl, torch, pkv, events=None):
@@ -198,15 +200,19 @@ def run_step(wl, torch, pkv, events=None):
         wl.copied[s].record(wl.copy_stream)
     compute = torch.cuda.current_stream()
     compute.wait_event(wl.copied[s])
-    pkv.pkv_write(wl.k_new, wl.v_new, wl.k_cache, wl.v_cache, slots_d)  # 3. cache write
     if events is not None:
         events[0].record()
-    pkv.pkv_decode_stream(wl.q, wl.k_cache, wl.v_cache, tables_d, lens_d,
-                          num_kv_heads=wl.Hkv, scale=wl.scale, max_context_len=wl.max_ctx,
-                          num_workers=wl.W, workspace=wl.workspace, out=wl.out)  # 4a
+    # 3 + 4a. cache write of the newest tokens fused into the attention stream pass
+    pkv.pkv_decode_append_stream(wl.q, wl.k_new, wl.v_new, wl.k_cache, wl.v_cache, tables_d,
+                                 lens_d, num_kv_heads=wl.Hkv, scale=wl.scale,
+                                 max_context_len=wl.max_ctx, num_workers=wl.W,
+                                 workspace=wl.workspace, out=wl.out)
     if events is not None:
         events[1].record()
-    pkv.pkv_decode_merge(wl.out, wl.workspace, num_kv_heads=wl.Hkv, num_workers=wl.W)  # 4b
+    # 4b. merge of the cut segments, plus the stores of the new tokens into their slots
+    pkv.pkv_decode_append_merge(wl.out, wl.k_new, wl.v_new, wl.k_cache, wl.v_cache, tables_d,
+                                lens_d, wl.workspace, num_kv_heads=wl.Hkv,
+                                max_context_len=wl.max_ctx, num_workers=wl.W)
     if events is not None:
         events[2].record()
     wl.done[s].record()

@@ -134,6 +134,28 @@ pkv_status pkv_decode_attn(void* out, const void* q, const void* k_cache, const 
                            int32_t max_blocks, int32_t max_context_len, float scale,
                            pkv_dtype dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decode step with the cache write fused in ([P1] §三 步驟三: the new token's K/V go into the */
+/* current block, then attention runs over all of the sequence's tokens through the table).  */
+/* For every sequence i with n_i >= 1 whose table entry b = block_tables[i][(n_i-1)/bs] lies  */
+/* in [0, NB): the token at position n_i - 1 takes its K/V from k_new[i], v_new[i]; they are   */
+/* stored bitwise into slot (b, (n_i-1) % bs) of the caches -- the slot pkv_alloc_append gave */
+/* that token -- and the output is exactly that of pkv_decode_attn on the updated caches.     */
+/* The call therefore equals pkv_write(k_new, v_new, those slots) followed by pkv_decode_attn, */
+/* bit for bit, in one launch fewer (the stores ride in the merge pass). Caller contract: that slot is in a block no other        */
+/* sequence of the batch reads (an appending sequence owns its last block: pkv_alloc_append   */
+/* reports a copy-on-write pair otherwise).                                                   */
+/*   k_new, v_new  device, [B][Hkv][hd] contiguous, dtype `dtype` (read); row i is ignored     */
+/*                 when n_i = 0 or the entry is outside the pool (nothing is written then).    */
+/*   k_cache, v_cache  written at those slots only. Other arguments as pkv_decode_attn, which  */
+/*                 also gives the workspace size.                                              */
+pkv_status pkv_decode_append_attn(void* out, const void* q, const void* k_new,
+                                  const void* v_new, void* k_cache, void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int32_t B, int32_t Hq, int32_t Hkv, int32_t hd, int32_t bs,
+                                  int32_t NB, int32_t max_blocks, int32_t max_context_len,
+                                  float scale, pkv_dtype dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* Workspace bytes pkv_decode_attn needs for this shape on the current device (0 if B == 0 or */
 /* the arguments are invalid).                                                                 */
 size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t hd,
@@ -184,6 +206,21 @@ pkv_status pkv_decode_stream(void* out, const void* q, const void* k_cache, cons
                              float scale, pkv_dtype dtype, int32_t num_workers, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* The two passes of pkv_decode_append_attn. Pass 1 is pkv_decode_stream with each sequence's */
+/* newest token taken from k_new/v_new instead of its slot (same arguments as                  */
+/* pkv_decode_stream plus k_new, v_new as in pkv_decode_append_attn); it writes no cache.      */
+/* Pass 2, pkv_decode_append_merge, is pkv_decode_merge plus the stores of those rows into     */
+/* their slots (the caches are written only here: stores issued while the K/V tiles stream    */
+/* slow the stream down on this hardware). The caches and the output are complete after pass */
+/* 2; between the passes the caches still hold the old slot contents.                          */
+pkv_status pkv_decode_append_stream(void* out, const void* q, const void* k_new,
+                                    const void* v_new, void* k_cache, void* v_cache,
+                                    const int32_t* block_tables, const int32_t* context_lens,
+                                    int32_t B, int32_t Hq, int32_t Hkv, int32_t hd, int32_t bs,
+                                    int32_t NB, int32_t max_blocks, int32_t max_context_len,
+                                    float scale, pkv_dtype dtype, int32_t num_workers,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Pass 2: for every cut segment and each of its GS q heads, combines the pieces of workers   */
 /* w_first..w_last in worker order (log-sum-exp): M = max m_w, a_w = 2^(m_w - M),             */
 /* out = sum_w a_w o_w / sum_w a_w l_w (a piece with m = -inf has weight 0), rounded to        */
@@ -192,6 +229,14 @@ pkv_status pkv_decode_stream(void* out, const void* q, const void* k_cache, cons
 pkv_status pkv_decode_merge(void* out, const void* workspace, size_t workspace_bytes, int32_t B,
                             int32_t Hq, int32_t Hkv, int32_t hd, pkv_dtype dtype,
                             int32_t num_workers, void* stream);
+
+pkv_status pkv_decode_append_merge(void* out, const void* k_new, const void* v_new,
+                                   void* k_cache, void* v_cache, const int32_t* block_tables,
+                                   const int32_t* context_lens, int32_t NB, int32_t max_blocks,
+                                   int32_t max_context_len, const void* workspace,
+                                   size_t workspace_bytes, int32_t B, int32_t Hq, int32_t Hkv,
+                                   int32_t hd, pkv_dtype dtype, int32_t num_workers,
+                                   void* stream);
 
 /* Attention-kernel selection, process-wide: 0 = automatic (matrix-core kernel for f16/bf16   */
 /* with 2 <= G <= 16, vector kernel otherwise), 1 = always the vector kernel, 2 = matrix-core  */

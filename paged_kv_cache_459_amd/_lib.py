@@ -61,6 +61,15 @@ SIGNATURES = {
                                   c_vp]),
     "pkv_decode_merge": (c_i32, [c_vp, c_vp, c_sz, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                  c_vp]),
+    "pkv_decode_append_attn": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
+                                       c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32,
+                                       c_i32, c_vp, c_sz, c_vp]),
+    "pkv_decode_append_merge": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
+                                        c_i32, c_vp, c_sz, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                        c_i32, c_vp]),
+    "pkv_decode_append_stream": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
+                                         c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32,
+                                         c_i32, c_i32, c_vp, c_sz, c_vp]),
     "pkv_set_attn_kernel": (c_i32, [c_i32]),
     "pkv_alloc_create": (c_i32, [c_i32, c_i32, P_i32, ctypes.POINTER(c_vp)]),
     "pkv_alloc_destroy": (None, [c_vp]),

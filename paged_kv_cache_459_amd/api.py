@@ -152,6 +152,50 @@ def pkv_decode_attn(q, k_cache, v_cache, block_tables, context_lens, *, num_kv_h
     return out
 
 
+def _new_args(q, k_new, v_new, num_kv_heads):
+    B, _, hd = q.shape
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, n, dtype=q.dtype, device=q.device)
+        if tuple(t.shape) != (B, num_kv_heads, hd):
+            raise ValueError(f"{n} must be [B, num_kv_heads, head_dim]")
+
+
+def pkv_decode_append_attn(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, *,
+                           num_kv_heads, scale, max_context_len, out=None, workspace=None):
+    """Write each sequence's newest token (k_new, v_new [B, Hkv, hd]) into its slot, then
+    decode attention: pkv_write followed by pkv_decode_attn in one pass."""
+    out, B, hq, hd, nb, mb = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
+                                          num_kv_heads, out)
+    _new_args(q, k_new, v_new, num_kv_heads)
+    need = pkv_decode_workspace_bytes(B, hq, num_kv_heads, hd, max_context_len, q.dtype)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check(lib.pkv_decode_append_attn(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                     _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), B, hq,
+                                     num_kv_heads, hd, BLOCK_SIZE, nb, mb, max_context_len,
+                                     float(scale), pkv_dtype(q), _ptr(workspace), ws_bytes,
+                                     _stream(q.device)), "pkv_decode_append_attn")
+    return out
+
+
+def pkv_decode_append_stream(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, *,
+                             num_kv_heads, scale, max_context_len, num_workers, workspace,
+                             out=None):
+    """Pass 1 of pkv_decode_append_attn (see include/pkv.h). Returns out."""
+    out, B, hq, hd, nb, mb = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
+                                          num_kv_heads, out)
+    _new_args(q, k_new, v_new, num_kv_heads)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check(lib.pkv_decode_append_stream(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                       _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                       _ptr(context_lens), B, hq, num_kv_heads, hd, BLOCK_SIZE,
+                                       nb, mb, max_context_len, float(scale), pkv_dtype(q),
+                                       num_workers, _ptr(workspace), ws_bytes,
+                                       _stream(q.device)), "pkv_decode_append_stream")
+    return out
+
+
 def pkv_decode_stream(q, k_cache, v_cache, block_tables, context_lens, *, num_kv_heads, scale,
                       max_context_len, num_workers, workspace, out=None):
     """Pass 1 of decode attention (see include/pkv.h). Returns out."""
@@ -175,6 +219,28 @@ def pkv_decode_merge(out, workspace, *, num_kv_heads, num_workers):
                                workspace.numel() * workspace.element_size(), B, hq, num_kv_heads,
                                hd, pkv_dtype(out), num_workers, _stream(out.device)),
           "pkv_decode_merge")
+    return out
+
+
+def pkv_decode_append_merge(out, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                            workspace, *, num_kv_heads, max_context_len, num_workers):
+    """Pass 2 of pkv_decode_append_attn: the merge, plus the stores of the newest tokens' K/V
+    into their slots."""
+    _need(out, "out")
+    dev = out.device
+    B, hq, hd = out.shape
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, n, dtype=out.dtype, device=dev)
+    _need(block_tables, "block_tables", dtype=torch.int32, device=dev)
+    _need(context_lens, "context_lens", dtype=torch.int32, device=dev)
+    _need(workspace, "workspace", device=dev)
+    nb = _num_blocks(k_cache, num_kv_heads, hd)
+    check(lib.pkv_decode_append_merge(_ptr(out), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                      _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), nb,
+                                      block_tables.shape[1], max_context_len, _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), B, hq,
+                                      num_kv_heads, hd, pkv_dtype(out), num_workers,
+                                      _stream(dev)), "pkv_decode_append_merge")
     return out
 
 

@@ -136,8 +136,9 @@ pkv_status validate_decode(const void* out, const void* q, const void* k_cache,
   return PKV_OK;
 }
 
-pkv::StreamParams make_params(void* out, const void* q, const void* k_cache,
-                              const void* v_cache, const int32_t* block_tables,
+pkv::StreamParams make_params(void* out, const void* q, const void* k_new, const void* v_new,
+                              const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables,
                               const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
                               int32_t hd, int32_t NB, int32_t max_blocks, int32_t max_ctx,
                               float scale, int32_t W, const Layout& L, void* workspace) {
@@ -148,6 +149,8 @@ pkv::StreamParams make_params(void* out, const void* q, const void* k_cache,
   p.v_cache = v_cache;
   p.block_tables = block_tables;
   p.context_lens = context_lens;
+  p.k_new = k_new;
+  p.v_new = v_new;
   p.B = B;
   p.Hq = Hq;
   p.Hkv = Hkv;
@@ -165,7 +168,8 @@ pkv::StreamParams make_params(void* out, const void* q, const void* k_cache,
 }
 
 // One stream pass (and, if asked, its merge) over B <= kMaxBatch sequences.
-pkv_status stream_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+pkv_status stream_impl(void* out, const void* q, const void* k_new, const void* v_new,
+                       const void* k_cache, const void* v_cache,
                        const int32_t* block_tables, const int32_t* context_lens, int32_t B,
                        int32_t Hq, int32_t Hkv, int32_t hd, int32_t bs, int32_t NB,
                        int32_t max_blocks, int32_t max_ctx, float scale, pkv_dtype dtype,
@@ -174,6 +178,8 @@ pkv_status stream_impl(void* out, const void* q, const void* k_cache, const void
   pkv_status st = validate_decode(out, q, k_cache, v_cache, block_tables, context_lens, B, Hq,
                                   Hkv, hd, bs, NB, max_blocks, max_ctx, scale, dtype);
   if (st != PKV_OK) return st;
+  if ((k_new == nullptr) != (v_new == nullptr)) return PKV_ERR_INVALID_ARG;
+  if (k_new && B > 0 && (!aligned16(k_new) || !aligned16(v_new))) return PKV_ERR_INVALID_ARG;
   if (W <= 0 || W % pkv::kWaves != 0) return PKV_ERR_INVALID_ARG;
   const int32_t kernel = current_kernel(dtype, Hq, Hkv);
   const Layout L = stream_layout(B, Hq, Hkv, hd, kernel, W);
@@ -186,9 +192,9 @@ pkv_status stream_impl(void* out, const void* q, const void* k_cache, const void
     st = check_decode_indices(block_tables, context_lens, B, NB, max_blocks, max_ctx, hs);
     if (st != PKV_OK) return st;
   }
-  const pkv::StreamParams p = make_params(out, q, k_cache, v_cache, block_tables, context_lens,
-                                          B, Hq, Hkv, hd, NB, max_blocks, max_ctx, scale, W, L,
-                                          workspace);
+  const pkv::StreamParams p = make_params(out, q, k_new, v_new, k_cache, v_cache, block_tables,
+                                          context_lens, B, Hq, Hkv, hd, NB, max_blocks, max_ctx,
+                                          scale, W, L, workspace);
   if (pkv::launch_stream(p, dtype, kernel, hs) != hipSuccess) return PKV_ERR_HIP;
   if (merge_after && pkv::launch_merge(p, dtype, kernel, hs) != hipSuccess) return PKV_ERR_HIP;
   return PKV_OK;
@@ -271,12 +277,17 @@ size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t hd
   return pkv_decode_stream_workspace_bytes(B < kMaxBatch ? B : kMaxBatch, Hq, Hkv, hd, dtype, W);
 }
 
-pkv_status pkv_decode_attn(void* out, const void* q, const void* k_cache, const void* v_cache,
-                           const int32_t* block_tables, const int32_t* context_lens, int32_t B,
-                           int32_t Hq, int32_t Hkv, int32_t hd, int32_t bs, int32_t NB,
-                           int32_t max_blocks, int32_t max_context_len, float scale,
-                           pkv_dtype dtype, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+
+// pkv_decode_attn and pkv_decode_append_attn: stream + merge per sub-batch.
+pkv_status decode_all(void* out, const void* q, const void* k_new, const void* v_new,
+                      const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                      const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                      int32_t hd, int32_t bs, int32_t NB, int32_t max_blocks,
+                      int32_t max_context_len, float scale, pkv_dtype dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
   pkv_status st = validate_decode(out, q, k_cache, v_cache, block_tables, context_lens, B, Hq,
                                   Hkv, hd, bs, NB, max_blocks, max_context_len, scale, dtype);
   if (st != PKV_OK || B == 0) return st;
@@ -291,16 +302,47 @@ pkv_status pkv_decode_attn(void* out, const void* q, const void* k_cache, const 
   while (chunk > 0 && !stream_fits(chunk, max_blocks, L.H, W)) chunk /= 2;
   if (chunk == 0) return PKV_ERR_UNSUPPORTED;
   const size_t row_bytes = static_cast<size_t>(Hq) * hd * elem_bytes(dtype);
+  const size_t new_bytes = static_cast<size_t>(Hkv) * hd * elem_bytes(dtype);
   for (int32_t i0 = 0; i0 < B; i0 += chunk) {
     const int32_t n = B - i0 < chunk ? B - i0 : chunk;
     st = stream_impl(static_cast<char*>(out) + i0 * row_bytes,
-                     static_cast<const char*>(q) + i0 * row_bytes, k_cache, v_cache,
-                     block_tables + static_cast<size_t>(i0) * max_blocks, context_lens + i0, n,
-                     Hq, Hkv, hd, bs, NB, max_blocks, max_context_len, scale, dtype, W,
-                     workspace, workspace_bytes, stream, /*merge_after=*/true);
+                     static_cast<const char*>(q) + i0 * row_bytes,
+                     k_new ? static_cast<const char*>(k_new) + i0 * new_bytes : nullptr,
+                     v_new ? static_cast<const char*>(v_new) + i0 * new_bytes : nullptr,
+                     k_cache, v_cache, block_tables + static_cast<size_t>(i0) * max_blocks,
+                     context_lens + i0, n, Hq, Hkv, hd, bs, NB, max_blocks, max_context_len,
+                     scale, dtype, W, workspace, workspace_bytes, stream, /*merge_after=*/true);
     if (st != PKV_OK) return st;
   }
   return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_decode_attn(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                           int32_t Hq, int32_t Hkv, int32_t hd, int32_t bs, int32_t NB,
+                           int32_t max_blocks, int32_t max_context_len, float scale,
+                           pkv_dtype dtype, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return decode_all(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens, B,
+                    Hq, Hkv, hd, bs, NB, max_blocks, max_context_len, scale, dtype, workspace,
+                    workspace_bytes, stream);
+}
+
+pkv_status pkv_decode_append_attn(void* out, const void* q, const void* k_new,
+                                  const void* v_new, void* k_cache, void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int32_t B, int32_t Hq, int32_t Hkv, int32_t hd, int32_t bs,
+                                  int32_t NB, int32_t max_blocks, int32_t max_context_len,
+                                  float scale, pkv_dtype dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (B > 0 && (!k_new || !v_new)) return PKV_ERR_INVALID_ARG;
+  return decode_all(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, B, Hq,
+                    Hkv, hd, bs, NB, max_blocks, max_context_len, scale, dtype, workspace,
+                    workspace_bytes, stream);
 }
 
 pkv_status pkv_decode_stream(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -309,14 +351,33 @@ pkv_status pkv_decode_stream(void* out, const void* q, const void* k_cache, cons
                              int32_t NB, int32_t max_blocks, int32_t max_context_len,
                              float scale, pkv_dtype dtype, int32_t num_workers, void* workspace,
                              size_t workspace_bytes, void* stream) {
-  return stream_impl(out, q, k_cache, v_cache, block_tables, context_lens, B, Hq, Hkv, hd, bs,
-                     NB, max_blocks, max_context_len, scale, dtype, num_workers, workspace,
-                     workspace_bytes, stream, /*merge_after=*/false);
+  return stream_impl(out, q, nullptr, nullptr, k_cache, v_cache, block_tables, context_lens, B,
+                     Hq, Hkv, hd, bs, NB, max_blocks, max_context_len, scale, dtype,
+                     num_workers, workspace, workspace_bytes, stream, /*merge_after=*/false);
 }
 
-pkv_status pkv_decode_merge(void* out, const void* workspace, size_t workspace_bytes, int32_t B,
-                            int32_t Hq, int32_t Hkv, int32_t hd, pkv_dtype dtype,
-                            int32_t num_workers, void* stream) {
+pkv_status pkv_decode_append_stream(void* out, const void* q, const void* k_new,
+                                    const void* v_new, void* k_cache, void* v_cache,
+                                    const int32_t* block_tables, const int32_t* context_lens,
+                                    int32_t B, int32_t Hq, int32_t Hkv, int32_t hd, int32_t bs,
+                                    int32_t NB, int32_t max_blocks, int32_t max_context_len,
+                                    float scale, pkv_dtype dtype, int32_t num_workers,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (B > 0 && (!k_new || !v_new)) return PKV_ERR_INVALID_ARG;
+  return stream_impl(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, B, Hq,
+                     Hkv, hd, bs, NB, max_blocks, max_context_len, scale, dtype, num_workers,
+                     workspace, workspace_bytes, stream, /*merge_after=*/false);
+}
+
+}  // extern "C"
+
+namespace {
+
+pkv_status merge_impl(void* out, const void* k_new, const void* v_new, void* k_cache,
+                      void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                      int32_t NB, int32_t max_blocks, int32_t max_ctx, const void* workspace,
+                      size_t workspace_bytes, int32_t B, int32_t Hq, int32_t Hkv, int32_t hd,
+                      pkv_dtype dtype, int32_t num_workers, void* stream) {
   if (!dtype_ok(dtype) || !head_dim_ok(hd)) return PKV_ERR_UNSUPPORTED;
   if (B < 0 || B > kMaxBatch || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Hq > 65535 ||
       num_workers <= 0 || num_workers % pkv::kWaves != 0)
@@ -327,12 +388,43 @@ pkv_status pkv_decode_merge(void* out, const void* workspace, size_t workspace_b
   const Layout L = stream_layout(B, Hq, Hkv, hd, kernel, num_workers);
   if (!workspace || workspace_bytes < L.bytes) return PKV_ERR_WORKSPACE;
   if (!aligned16(workspace)) return PKV_ERR_INVALID_ARG;
-  const pkv::StreamParams p = make_params(out, nullptr, nullptr, nullptr, nullptr, nullptr, B,
-                                          Hq, Hkv, hd, 1, 1, 0, 1.0f, num_workers, L,
+  const pkv::StreamParams p = make_params(out, nullptr, k_new, v_new, k_cache, v_cache,
+                                          block_tables, context_lens, B, Hq, Hkv, hd, NB,
+                                          max_blocks, max_ctx, 1.0f, num_workers, L,
                                           const_cast<void*>(workspace));
   return pkv::launch_merge(p, dtype, kernel, static_cast<hipStream_t>(stream)) == hipSuccess
              ? PKV_OK
              : PKV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_decode_merge(void* out, const void* workspace, size_t workspace_bytes, int32_t B,
+                            int32_t Hq, int32_t Hkv, int32_t hd, pkv_dtype dtype,
+                            int32_t num_workers, void* stream) {
+  return merge_impl(out, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 1, 1, 0,
+                    workspace, workspace_bytes, B, Hq, Hkv, hd, dtype, num_workers, stream);
+}
+
+pkv_status pkv_decode_append_merge(void* out, const void* k_new, const void* v_new,
+                                   void* k_cache, void* v_cache, const int32_t* block_tables,
+                                   const int32_t* context_lens, int32_t NB, int32_t max_blocks,
+                                   int32_t max_context_len, const void* workspace,
+                                   size_t workspace_bytes, int32_t B, int32_t Hq, int32_t Hkv,
+                                   int32_t hd, pkv_dtype dtype, int32_t num_workers,
+                                   void* stream) {
+  if (B > 0 && (!k_new || !v_new || !k_cache || !v_cache || !block_tables || !context_lens ||
+                !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+                !aligned16(v_cache) || NB <= 0 || max_blocks <= 0 || max_context_len < 0 ||
+                static_cast<int64_t>(max_blocks) * kBlockSize < max_context_len ||
+                (reinterpret_cast<uintptr_t>(block_tables) & 3u) ||
+                (reinterpret_cast<uintptr_t>(context_lens) & 3u)))
+    return PKV_ERR_INVALID_ARG;
+  return merge_impl(out, k_new, v_new, k_cache, v_cache, block_tables, context_lens, NB,
+                    max_blocks, max_context_len, workspace, workspace_bytes, B, Hq, Hkv, hd,
+                    dtype, num_workers, stream);
 }
 
 int32_t pkv_set_attn_kernel(int32_t which) {

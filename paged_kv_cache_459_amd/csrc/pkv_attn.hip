@@ -129,6 +129,43 @@ __device__ __forceinline__ uint2 pinned(uint2 v) {
   asm volatile("" : "+v"(v.x), "+v"(v.y));
   return v;
 }
+__device__ __forceinline__ void settle(uint32_t& v) { asm volatile("" : "+v"(v)); }
+
+// Element e (lane-dependent) of a 16-byte chunk of EB-byte elements replaced by `bits`.
+template <int EB>
+__device__ __forceinline__ uint4 set_elem(uint4 v, int e, uint32_t bits) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (EB == 2) {
+      if (e >> 1 == i) w[i] = (e & 1) ? ((w[i] & 0x0000FFFFu) | (bits << 16))
+                                      : ((w[i] & 0xFFFF0000u) | (bits & 0xFFFFu));
+    } else {
+      if (e == i) w[i] = bits;
+    }
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+__device__ __forceinline__ uint2 set_elem2(uint2 v, int e, uint32_t bits) {
+  uint32_t w[2] = {v.x, v.y};
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    if (e >> 1 == i) w[i] = (e & 1) ? ((w[i] & 0x0000FFFFu) | (bits << 16))
+                                    : ((w[i] & 0xFFFF0000u) | (bits & 0xFFFFu));
+  return make_uint2(w[0], w[1]);
+}
+
+// Bits of element d of an EB-byte-element row.
+template <int EB>
+__device__ __forceinline__ uint32_t load_elem(const char* row, int d) {
+  if constexpr (EB == 2) return *reinterpret_cast<const uint16_t*>(row + 2 * d);
+  else return *reinterpret_cast<const uint32_t*>(row + 4 * d);
+}
+template <int EB>
+__device__ __forceinline__ void store_elem(char* row, int d, uint32_t bits) {
+  if constexpr (EB == 2) *reinterpret_cast<uint16_t*>(row + 2 * d) = static_cast<uint16_t>(bits);
+  else *reinterpret_cast<uint32_t*>(row + 4 * d) = bits;
+}
 
 // Per-dtype element access. DT: 0 = f32, 1 = f16, 2 = bf16.
 template <int DT>
@@ -259,9 +296,10 @@ __device__ __forceinline__ int find_seq(const int* pref, int B, int r) {
 struct TileInfo {
   int id;   // physical block to read (0 when the table entry is outside the pool)
   int seq;  // sequence i
-  int hm;   // head slot << 16 | slot << 8 | whole << 7 | end << 6 | start << 5 | valid tokens
+  int hm;   // head slot << 16 | last << 9 | slot << 8 | whole << 7 | end << 6 | start << 5 |
+            // valid tokens; last: the sequence's final block (holds its newest token)
 };
-constexpr int kStart = 1 << 5, kEnd = 1 << 6, kWhole = 1 << 7;
+constexpr int kStart = 1 << 5, kEnd = 1 << 6, kWhole = 1 << 7, kLast = 1 << 9;
 
 // Stream position t -> tile of segment (i, h): head-major order, t = h*C + pref[i] + j.
 __device__ __forceinline__ TileInfo tile_info(const StreamParams& p, const int* pref, int C,
@@ -283,7 +321,9 @@ __device__ __forceinline__ TileInfo tile_info(const StreamParams& p, const int* 
   const int end = (t == seg0 + c - 1) || (t == t1 - 1);
   const int whole = (seg0 >= t0) && (seg0 + c <= t1);
   const int slot = seg0 <= t0 ? 0 : 1;
-  return TileInfo{id, i, (h << 16) | (slot << 8) | (whole << 7) | (end << 6) | (start << 5) | valid};
+  const int last = j == c - 1;
+  return TileInfo{id, i, (h << 16) | (last << 9) | (slot << 8) | (whole << 7) | (end << 6) |
+                             (start << 5) | valid};
 }
 
 // This wave's worker index and tile range [t0, t1). Work-group b runs on XCD b % 8; logical
@@ -340,6 +380,8 @@ attn_vector_kernel(const StreamParams p) {
 
   extern __shared__ int s_pref[];
   __shared__ float s_p[kWaves][kBlockSize];
+  constexpr int NR = HD * EB / 16;  // 16-byte chunks in one token's K (or V) row of one head
+  __shared__ uint4 s_new[kWaves][2][NR];  // append mode: the segment's newest K and V rows
 
   scan_block_counts(p, s_pref);
   publish_and_zero<DT>(p, s_pref);
@@ -397,8 +439,31 @@ attn_vector_kernel(const StreamParams p) {
             static_cast<const char*>(p.q) + (static_cast<size_t>(seq) * p.Hq + h) * HD * EB);
 #pragma unroll
         for (int j = 0; j < NL; ++j) qv[j] = qp[4 * j + row_id];
+        // Append mode: the sequence's newest K and V rows for this head, staged in LDS now,
+        // under the same wait as q, for the final block (in whichever tile of this range).
+        uint4 nr = make_uint4(0, 0, 0, 0);
+        if (p.k_new != nullptr && lane < 2 * NR) {
+          const size_t row = (static_cast<size_t>(seq) * p.Hkv + h / G) * HD * EB;
+          const char* src = static_cast<const char*>(lane < NR ? p.k_new : p.v_new) + row;
+          nr = *reinterpret_cast<const uint4*>(src + 16 * (lane % NR));
+        }
 #pragma unroll
         for (int j = 0; j < NL; ++j) settle(qv[j]);
+        settle(nr);
+        if (p.k_new != nullptr) {
+          if (lane < 2 * NR) s_new[w][lane / NR][lane % NR] = nr;
+          wave_lds_sync();
+        }
+      }
+      // Append mode, final block of the sequence: the newest token (offset valid - 1) takes its
+      // K/V from the rows staged at the segment start, in place of whatever the tile read from
+      // its slot. The merge pass stores those rows into the slot for later steps (stores
+      // issued while the tiles stream measurably slow the stream down).
+      const bool append = p.k_new != nullptr && (hm & kLast) && valid > 0;
+      const int off = valid - 1;
+      if (append && tok == off) {  // the lanes holding the newest token's K chunks
+#pragma unroll
+        for (int j = 0; j < NL; ++j) kr[j] = s_new[w][0][4 * j + row_id];
       }
       float s = 0.f;
 #pragma unroll
@@ -425,6 +490,12 @@ attn_vector_kernel(const StreamParams p) {
       uint4 vt[NL];
 #pragma unroll
       for (int j = 0; j < NL; ++j) vt[j] = pinned(vr[j]);
+      if (append && vsub == off / X) {  // the lanes holding the newest token's V elements
+        const char* vn = reinterpret_cast<const char*>(&s_new[w][1][0]);
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+          vt[j] = set_elem<EB>(vt[j], off % X, load_elem<EB>(vn, VROWS * j + lane / LPR));
+      }
       if (valid < kBlockSize) {  // partly filled (or unreadable) block: zero the invalid tokens
 #pragma unroll
         for (int j = 0; j < NL; ++j) vt[j] = mask_tokens<EB>(vt[j], X * vsub, valid);
@@ -523,13 +594,15 @@ struct Mfma<2> {
 
 template <int DT, int HD>
 __global__ void __launch_bounds__(kThreads)
-attn_matrix_kernel(const StreamParams p) {
+__attribute__((amdgpu_waves_per_eu(3))) attn_matrix_kernel(const StreamParams p) {
   using M16 = Mfma<DT>;
   constexpr int TILE = HD * kBlockSize * 2;
   constexpr int KS = HD / 32;  // QK steps
   constexpr int VT = HD / 16;  // PV dim tiles
 
   extern __shared__ int s_pref[];
+  constexpr int NR = HD * 2 / 16;  // 16-byte chunks in one token's K (or V) row of one head
+  __shared__ uint4 s_new[kWaves][2][NR];  // append mode: the segment's newest K and V rows
 
   scan_block_counts(p, s_pref);
   publish_and_zero<DT>(p, s_pref);
@@ -538,6 +611,7 @@ attn_matrix_kernel(const StreamParams p) {
   if (rg.t0 >= rg.t1) return;
 
   const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
   const int G = p.Hq / p.Hkv;
   const int hq = lane & 15, g = lane >> 4;
   const uint32_t k_lane = 16u * lane;
@@ -591,8 +665,29 @@ attn_matrix_kernel(const StreamParams p) {
 #pragma unroll
           for (int s = 0; s < KS; ++s) qb[s] = make_uint4(0, 0, 0, 0);
         }
+        // Append mode: stage the sequence's newest K and V rows of this kv head (see the
+        // vector kernel).
+        uint4 nr = make_uint4(0, 0, 0, 0);
+        if (p.k_new != nullptr && lane < 2 * NR) {
+          const size_t row = (static_cast<size_t>(seq) * p.Hkv + kvh) * HD * 2;
+          const char* src = static_cast<const char*>(lane < NR ? p.k_new : p.v_new) + row;
+          nr = *reinterpret_cast<const uint4*>(src + 16 * (lane % NR));
+        }
 #pragma unroll
         for (int s = 0; s < KS; ++s) settle(qb[s]);
+        settle(nr);
+        if (p.k_new != nullptr) {
+          if (lane < 2 * NR) s_new[w][lane / NR][lane % NR] = nr;
+          wave_lds_sync();
+        }
+      }
+      // Append mode, final block of the sequence: see the vector kernel. Here K lane l holds
+      // token l%16, chunk 4s + l/16; V lane l holds dim 16j + l%16, tokens 4(l/16) .. +3.
+      const bool append = p.k_new != nullptr && (hm & kLast) && valid > 0;
+      const int off = valid - 1;
+      if (append && hq == off) {  // the lanes holding the newest token's K chunks
+#pragma unroll
+        for (int s = 0; s < KS; ++s) kr[s] = s_new[w][0][4 * s + g];
       }
       float4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -623,6 +718,11 @@ attn_matrix_kernel(const StreamParams p) {
       uint2 vt[VT];
 #pragma unroll
       for (int j = 0; j < VT; ++j) vt[j] = pinned(vr[j]);
+      if (append && g == off / 4) {  // the lanes holding the newest token's V elements
+        const char* vn = reinterpret_cast<const char*>(&s_new[w][1][0]);
+#pragma unroll
+        for (int j = 0; j < VT; ++j) vt[j] = set_elem2(vt[j], off % 4, load_elem<2>(vn, 16 * j + hq));
+      }
       if (valid < kBlockSize) {  // partly filled (or unreadable) block: zero the invalid tokens
         const int base = 4 * g;
         const uint32_t mx =
@@ -669,6 +769,37 @@ attn_matrix_kernel(const StreamParams p) {
 }
 
 // ------------------------------------------------------------------------------------------
+// Append mode, merge pass: one wave stores sequence i's newest K/V rows of kv head h (k_new,
+// v_new) into that token's slot (block_tables[i][(n_i-1)/16], offset (n_i-1)%16): the K row
+// as 16-byte chunks (chunk c at 256 c + 16 off in the tile), the V row as one element per dim
+// row of the dim-major tile. Nothing is stored for n_i = 0 or a final-block entry outside the
+// pool. The stream pass already used these rows in place of the slot's old contents.
+template <int DT, int HD>
+__device__ void store_new_token(const StreamParams& p, int i, int h) {
+  constexpr int EB = Elem<DT>::kBytes;
+  constexpr int CH = HD * EB / 16;  // 16-byte chunks per row
+  const int n = clamp_len(p, i);
+  if (n == 0) return;
+  const int blk = p.block_tables[static_cast<size_t>(i) * p.max_blocks + (n - 1) / kBlockSize];
+  if (blk < 0 || blk >= p.NB) return;
+  const int off = (n - 1) % kBlockSize;
+  const int lane = threadIdx.x;
+  const size_t tile = static_cast<size_t>(blk) * p.Hkv + h;
+  const size_t row = static_cast<size_t>(i) * p.Hkv + h;
+  if (lane < CH) {
+    const uint4 kk = reinterpret_cast<const uint4*>(p.k_new)[row * CH + lane];
+    reinterpret_cast<uint4*>(const_cast<void*>(p.k_cache))[(tile * CH + lane) * kBlockSize + off] = kk;
+  }
+  const char* vn = static_cast<const char*>(p.v_new) + row * HD * EB;
+  char* vtile = static_cast<char*>(const_cast<void*>(p.v_cache)) + tile * HD * kBlockSize * EB;
+#pragma unroll
+  for (int r = 0; r < HD / 64; ++r) {
+    const int d = lane + 64 * r;
+    store_elem<EB>(vtile, d * kBlockSize + off, load_elem<EB>(vn, d));
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // Merge of the pieces of segments cut by worker-range boundaries. One wave per output row
 // (sequence i, q head hh of head slot hh / GS). The pieces' (m, l) are read one per lane and
 // weighted in parallel; o is accumulated over the pieces in worker order (deterministic),
@@ -679,6 +810,7 @@ __global__ void __launch_bounds__(64)
 merge_kernel(const StreamParams p, int H, int GS) {
   constexpr int R = HD / 64;
   const int i = blockIdx.x, hh = blockIdx.y, lane = threadIdx.x;
+  if (p.k_new != nullptr && hh % (p.Hq / p.Hkv) == 0) store_new_token<DT, HD>(p, i, hh / (p.Hq / p.Hkv));
   const int h = hh / GS, n = hh - h * GS;
   const int C = p.ws_seg[p.B];
   const int s0 = p.ws_seg[i];

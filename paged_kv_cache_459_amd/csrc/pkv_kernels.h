@@ -31,6 +31,11 @@ struct StreamParams {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  // Append mode (both non-null): [B][Hkv][hd], the K/V of each sequence's newest token
+  // (position n_i - 1). The stream pass uses them in place of the slot's old contents; the
+  // merge pass stores them into the slot. Null: plain attention over the cache.
+  const void* k_new;
+  const void* v_new;
   int32_t B, Hq, Hkv, hd, NB, max_blocks, max_ctx;
   float scale_log2;     // softmax scale times log2(e): scores are kept in base-2 units
   int32_t num_workers;  // W: waves of the stream pass, a positive multiple of kWaves
