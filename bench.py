@@ -141,8 +141,9 @@ class Workload:
         self.step_no = 0
         # Both sets start from a full export of the allocator's tables; after that each step
         # only adds the blocks it opened (tables only grow in a decode loop without forks).
-        for lens_h, _, tables_h in self.host_views:
-            self.alloc.tables(self.seqs, self.max_blocks, tables_out=tables_h, lens_out=lens_h)
+        for lens_h, _, tables_h in self.host_views:  # shared blocks marked for cached loads
+            self.alloc.tables(self.seqs, self.max_blocks, tables_out=tables_h, lens_out=lens_h,
+                              mark_shared=True)
         self.lens = self.host_views[0][0].copy()  # lengths before the next step's token
         self.pending = [[], []]  # table entries set s has not received yet
         self.rows = np.arange(self.B)
@@ -231,6 +232,7 @@ def cpu_baseline(wl, torch, W, seconds):
     spent, done, kv, passes = 0.0, 0, 0, 0
     lens = wl.host_views[wl.last_set][0].copy()
     tables = wl.host_views[wl.last_set][2].copy()
+    tables = np.where(tables >= 0, tables & ~0x40000000, tables)  # drop the shared-block mark
     inputs = {}
     with threadpool_limits(limits=1):
         while spent < seconds:
@@ -299,11 +301,12 @@ def main():
     # A table only ever gains entries, so the final tables hold every step's blocks; they must
     # be exactly what the allocator exports.
     final_tables = wl.host_views[wl.last_set][2].copy()
-    ref_tables, ref_lens = wl.alloc.tables(wl.seqs, wl.max_blocks)
+    ref_tables, ref_lens = wl.alloc.tables(wl.seqs, wl.max_blocks, mark_shared=True)
     assert np.array_equal(final_tables, ref_tables) and np.array_equal(wl.lens, ref_lens), \
         "incremental block tables diverged from the allocator's export"
     kv_logical = [wl.kv_bytes(lens) for lens in lens_per_step]
-    kv = [wl.unique_kv_bytes(lens, final_tables) for lens in lens_per_step]
+    blocks = np.where(final_tables >= 0, final_tables & ~pkv.BLOCK_SHARED, final_tables)
+    kv = [wl.unique_kv_bytes(lens, blocks) for lens in lens_per_step]
     algo = [b + wl.qo_bytes() for b in kv]
     ms_per_step = wall / args.steps * 1e3
     value = sum(kv) / wall / 1e9

@@ -114,8 +114,10 @@ pkv_status pkv_write(const void* k, const void* v, void* k_cache, void* v_cache,
 /*   out, q        device, [B][Hq][hd] contiguous, dtype `dtype` (out written, q read)         */
 /*   block_tables  device int32 [B][max_blocks]; entry j of row i names the physical block of */
 /*                 tokens [j*bs, (j+1)*bs) of sequence i. Only entries j < ceil(n_i/bs) are   */
-/*                 read. An entry outside [0, NB) is never dereferenced for data: its tokens  */
-/*                 are skipped (the output is then undefined but no memory fault can occur).  */
+/*                 read. An entry may carry PKV_BLOCK_SHARED (see pkv_alloc_tables_marked):   */
+/*                 the block is the entry without it. An entry naming a block outside [0, NB) */
+/*                 is never dereferenced for data: its tokens are skipped (the output is then */
+/*                 undefined but no memory fault can occur).                                  */
 /*   context_lens  device int32 [B]; values are clamped to [0, max_context_len] on the device.*/
 /*   max_context_len  host bound on every n_i; must satisfy max_context_len <= max_blocks*bs. */
 /*   scale         the softmax scale (1/sqrt(hd) in the usual model).                          */
@@ -294,6 +296,20 @@ pkv_status pkv_alloc_free(pkv_allocator* a, int64_t seq);
 pkv_status pkv_alloc_tables(const pkv_allocator* a, int32_t n, const int64_t* seqs,
                             int32_t max_blocks, int32_t* block_tables_out,
                             int32_t* context_lens_out);
+
+/* Block-table entry mark: set on entries of blocks that several sequences share. The block  */
+/* is entry & ~PKV_BLOCK_SHARED; valid block ids stay below 2^27, so the mark never collides. */
+#define PKV_BLOCK_SHARED 0x40000000
+
+/* As pkv_alloc_tables, but the entry of every block whose reference count is above 1 carries */
+/* PKV_BLOCK_SHARED. The decode calls accept marked tables; the mark never changes a result,   */
+/* only the cache policy of the block's loads: marked blocks are read with ordinary (cached)  */
+/* loads so that the L2 keeps them for the other sequences that read them ([P1] §二: common    */
+/* prefixes point at the same physical blocks), unmarked blocks with streaming (non-temporal) */
+/* loads. An unmarked table is always correct; a mark on an unshared block only costs speed. */
+pkv_status pkv_alloc_tables_marked(const pkv_allocator* a, int32_t n, const int64_t* seqs,
+                                   int32_t max_blocks, int32_t* block_tables_out,
+                                   int32_t* context_lens_out);
 
 int32_t pkv_alloc_num_free(const pkv_allocator* a);            /* free blocks                */
 int32_t pkv_alloc_refcount(const pkv_allocator* a, int32_t block); /* -1 if out of range      */

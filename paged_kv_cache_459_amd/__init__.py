@@ -5,7 +5,7 @@ C ABI in ``include/pkv.h``); this package only marshals arguments. Importing it 
 library has not been built (``python paged_kv_cache_459_amd/build.py``): there is no fallback.
 """
 
-from ._lib import BF16, F16, F32, STATUS, PkvError, lib  # noqa: F401
+from ._lib import BF16, BLOCK_SHARED, F16, F32, STATUS, PkvError, lib  # noqa: F401
 from .api import (BLOCK_SIZE, BlockAllocator, alloc_caches, cache_bytes,  # noqa: F401
                   cache_shapes, pkv_decode_append_attn, pkv_decode_append_merge,
                   pkv_decode_append_stream,

@@ -19,6 +19,7 @@ STATUS = {
 }
 
 F32, F16, BF16 = 0, 1, 2
+BLOCK_SHARED = 0x40000000  # PKV_BLOCK_SHARED
 
 
 class PkvError(RuntimeError):
@@ -78,6 +79,7 @@ SIGNATURES = {
     "pkv_alloc_fork": (c_i32, [c_vp, c_i64, c_i64]),
     "pkv_alloc_free": (c_i32, [c_vp, c_i64]),
     "pkv_alloc_tables": (c_i32, [c_vp, c_i32, c_vp, c_i32, c_vp, c_vp]),
+    "pkv_alloc_tables_marked": (c_i32, [c_vp, c_i32, c_vp, c_i32, c_vp, c_vp]),
     "pkv_alloc_num_free": (c_i32, [c_vp]),
     "pkv_alloc_refcount": (c_i32, [c_vp, c_i32]),
     "pkv_alloc_seq_len": (c_i64, [c_vp, c_i64]),

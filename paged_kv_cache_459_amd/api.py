@@ -321,13 +321,16 @@ class BlockAllocator:
     def free(self, seq):
         check(lib.pkv_alloc_free(self._h, int(seq)), "pkv_alloc_free")
 
-    def tables(self, seqs, max_blocks, tables_out=None, lens_out=None):
+    def tables(self, seqs, max_blocks, tables_out=None, lens_out=None, mark_shared=False):
+        """Block tables [n, max_blocks] (pad -1) and lengths; with mark_shared, entries of
+        blocks shared by several sequences carry BLOCK_SHARED (pkv_alloc_tables_marked)."""
         seqs = _as_c(seqs, np.int64)
         n = len(seqs)
         tables = tables_out if tables_out is not None else np.empty((n, max_blocks), np.int32)
         lens = lens_out if lens_out is not None else np.empty(n, np.int32)
-        check(lib.pkv_alloc_tables(self._h, n, seqs.ctypes.data, max_blocks, tables.ctypes.data,
-                                   lens.ctypes.data), "pkv_alloc_tables")
+        fn = lib.pkv_alloc_tables_marked if mark_shared else lib.pkv_alloc_tables
+        check(fn(self._h, n, seqs.ctypes.data, max_blocks, tables.ctypes.data, lens.ctypes.data),
+              "pkv_alloc_tables")
         return tables, lens
 
     def num_free(self):

@@ -183,9 +183,13 @@ pkv_status pkv_alloc_free(pkv_allocator* a, int64_t seq) {
   return PKV_OK;
 }
 
-pkv_status pkv_alloc_tables(const pkv_allocator* a, int32_t n, const int64_t* seqs,
-                            int32_t max_blocks, int32_t* block_tables_out,
-                            int32_t* context_lens_out) {
+}  // extern "C"
+
+namespace {
+
+pkv_status export_tables(const pkv_allocator* a, int32_t n, const int64_t* seqs,
+                         int32_t max_blocks, int32_t* block_tables_out, int32_t* context_lens_out,
+                         bool mark_shared) {
   if (!a || n < 0 || max_blocks < 0 || (n > 0 && (!seqs || !block_tables_out || !context_lens_out)))
     return PKV_ERR_INVALID_ARG;
   std::vector<const Seq*> ptr(n);
@@ -201,11 +205,32 @@ pkv_status pkv_alloc_tables(const pkv_allocator* a, int32_t n, const int64_t* se
     int32_t* row = block_tables_out + static_cast<int64_t>(k) * max_blocks;
     const auto& b = ptr[k]->blocks;
     int32_t j = 0;
-    for (; j < static_cast<int32_t>(b.size()); ++j) row[j] = b[j];
+    if (mark_shared) {
+      for (; j < static_cast<int32_t>(b.size()); ++j)
+        row[j] = a->ref[b[j]] > 1 ? (b[j] | PKV_BLOCK_SHARED) : b[j];
+    } else {
+      for (; j < static_cast<int32_t>(b.size()); ++j) row[j] = b[j];
+    }
     for (; j < max_blocks; ++j) row[j] = -1;
     context_lens_out[k] = static_cast<int32_t>(ptr[k]->len);
   }
   return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_alloc_tables(const pkv_allocator* a, int32_t n, const int64_t* seqs,
+                            int32_t max_blocks, int32_t* block_tables_out,
+                            int32_t* context_lens_out) {
+  return export_tables(a, n, seqs, max_blocks, block_tables_out, context_lens_out, false);
+}
+
+pkv_status pkv_alloc_tables_marked(const pkv_allocator* a, int32_t n, const int64_t* seqs,
+                                   int32_t max_blocks, int32_t* block_tables_out,
+                                   int32_t* context_lens_out) {
+  return export_tables(a, n, seqs, max_blocks, block_tables_out, context_lens_out, true);
 }
 
 int32_t pkv_alloc_num_free(const pkv_allocator* a) {

@@ -107,8 +107,8 @@ pkv_status check_decode_indices(const int32_t* tables, const int32_t* lens, int3
     if (l[i] < 0 || l[i] > max_ctx) return PKV_ERR_INDEX;
     const int32_t nb = ceil_div(l[i], kBlockSize);
     for (int32_t j = 0; j < nb; ++j) {
-      const int32_t b = t[static_cast<size_t>(i) * max_blocks + j];
-      if (b < 0 || b >= NB) return PKV_ERR_INDEX;
+      const int32_t e = t[static_cast<size_t>(i) * max_blocks + j];
+      if (e < 0 || (e & ~pkv::kSharedBit) >= NB) return PKV_ERR_INDEX;
     }
   }
   return PKV_OK;

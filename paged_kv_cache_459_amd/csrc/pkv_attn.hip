@@ -68,6 +68,14 @@ __device__ __forceinline__ uint2 load_nt8(const char* p) {
   const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
   return make_uint2(v.x, v.y);
 }
+// Tiles of blocks marked shared are read with ordinary (cached) loads instead: other
+// sequences of the batch read them too, and the L2 should keep them.
+__device__ __forceinline__ uint4 load_tile16(const char* p, bool shared) {
+  return shared ? *reinterpret_cast<const uint4*>(p) : load_nt16(p);
+}
+__device__ __forceinline__ uint2 load_tile8(const char* p, bool shared) {
+  return shared ? *reinterpret_cast<const uint2*>(p) : load_nt8(p);
+}
 
 // Cross-lane moves inside a row of 16 lanes (DPP): quad permutations and row rotations.
 template <int CTRL>
@@ -296,10 +304,11 @@ __device__ __forceinline__ int find_seq(const int* pref, int B, int r) {
 struct TileInfo {
   int id;   // physical block to read (0 when the table entry is outside the pool)
   int seq;  // sequence i
-  int hm;   // head slot << 16 | last << 9 | slot << 8 | whole << 7 | end << 6 | start << 5 |
-            // valid tokens; last: the sequence's final block (holds its newest token)
+  int hm;   // head slot << 16 | shared << 10 | last << 9 | slot << 8 | whole << 7 | end << 6 |
+            // start << 5 | valid tokens; last: the sequence's final block (holds its newest
+            // token); shared: the table entry carries the shared-block mark
 };
-constexpr int kStart = 1 << 5, kEnd = 1 << 6, kWhole = 1 << 7, kLast = 1 << 9;
+constexpr int kStart = 1 << 5, kEnd = 1 << 6, kWhole = 1 << 7, kLast = 1 << 9, kShared = 1 << 10;
 
 // Stream position t -> tile of segment (i, h): head-major order, t = h*C + pref[i] + j.
 __device__ __forceinline__ TileInfo tile_info(const StreamParams& p, const int* pref, int C,
@@ -312,8 +321,10 @@ __device__ __forceinline__ TileInfo tile_info(const StreamParams& p, const int* 
   const int seg0 = h * C + pref[i];
   const int n = clamp_len(p, i);
   int valid = min(kBlockSize, n - kBlockSize * j);
-  int id = p.block_tables[static_cast<size_t>(i) * p.max_blocks + j];
-  if (id < 0 || id >= p.NB) {
+  const int raw = p.block_tables[static_cast<size_t>(i) * p.max_blocks + j];
+  const int shared = raw >= 0 && (raw & kSharedBit) ? 1 : 0;
+  int id = raw & ~kSharedBit;
+  if (raw < 0 || id >= p.NB) {
     id = 0;  // read (always in bounds) but no token of it counts
     valid = 0;
   }
@@ -322,8 +333,8 @@ __device__ __forceinline__ TileInfo tile_info(const StreamParams& p, const int* 
   const int whole = (seg0 >= t0) && (seg0 + c <= t1);
   const int slot = seg0 <= t0 ? 0 : 1;
   const int last = j == c - 1;
-  return TileInfo{id, i, (h << 16) | (last << 9) | (slot << 8) | (whole << 7) | (end << 6) |
-                             (start << 5) | valid};
+  return TileInfo{id, i, (h << 16) | (shared << 10) | (last << 9) | (slot << 8) | (whole << 7) |
+                             (end << 6) | (start << 5) | valid};
 }
 
 // This wave's worker index and tile range [t0, t1). Work-group b runs on XCD b % 8; logical
@@ -414,15 +425,20 @@ attn_vector_kernel(const StreamParams p) {
       return static_cast<const char*>(cache) + static_cast<size_t>(id) * blk_stride +
              static_cast<size_t>(h / G) * TILE;
     };
+    auto is_shared = [&](int k) {
+      return (uniform(__builtin_amdgcn_readlane(ti.hm, k)) & kShared) != 0;
+    };
     auto load_k = [&](int k) {
       const char* kt = tile_base(p.k_cache, k);
+      const bool sh = is_shared(k);
 #pragma unroll
-      for (int j = 0; j < NL; ++j) kr[j] = load_nt16(kt + (lane_off + 1024u * j));
+      for (int j = 0; j < NL; ++j) kr[j] = load_tile16(kt + (lane_off + 1024u * j), sh);
     };
     auto load_v = [&](int k) {
       const char* vt = tile_base(p.v_cache, k);
+      const bool sh = is_shared(k);
 #pragma unroll
-      for (int j = 0; j < NL; ++j) vr[j] = load_nt16(vt + (lane_off + 1024u * j));
+      for (int j = 0; j < NL; ++j) vr[j] = load_tile16(vt + (lane_off + 1024u * j), sh);
     };
 
     auto step = [&](int k, auto load_next) {
@@ -635,15 +651,20 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_matrix_kernel(const StreamParams p)
       return static_cast<const char*>(cache) + static_cast<size_t>(id) * blk_stride +
              static_cast<size_t>(h) * TILE;
     };
+    auto is_shared = [&](int k) {
+      return (uniform(__builtin_amdgcn_readlane(ti.hm, k)) & kShared) != 0;
+    };
     auto load_k = [&](int k) {
       const char* kt = tile_base(p.k_cache, k);
+      const bool sh = is_shared(k);
 #pragma unroll
-      for (int s = 0; s < KS; ++s) kr[s] = load_nt16(kt + (k_lane + 1024u * s));
+      for (int s = 0; s < KS; ++s) kr[s] = load_tile16(kt + (k_lane + 1024u * s), sh);
     };
     auto load_v = [&](int k) {
       const char* vt = tile_base(p.v_cache, k);
+      const bool sh = is_shared(k);
 #pragma unroll
-      for (int j = 0; j < VT; ++j) vr[j] = load_nt8(vt + (v_lane + 512u * j));
+      for (int j = 0; j < VT; ++j) vr[j] = load_tile8(vt + (v_lane + 512u * j), sh);
     };
 
     auto step = [&](int k, auto load_next) {
@@ -780,8 +801,9 @@ __device__ void store_new_token(const StreamParams& p, int i, int h) {
   constexpr int CH = HD * EB / 16;  // 16-byte chunks per row
   const int n = clamp_len(p, i);
   if (n == 0) return;
-  const int blk = p.block_tables[static_cast<size_t>(i) * p.max_blocks + (n - 1) / kBlockSize];
-  if (blk < 0 || blk >= p.NB) return;
+  const int raw = p.block_tables[static_cast<size_t>(i) * p.max_blocks + (n - 1) / kBlockSize];
+  const int blk = raw & ~kSharedBit;
+  if (raw < 0 || blk >= p.NB) return;
   const int off = (n - 1) % kBlockSize;
   const int lane = threadIdx.x;
   const size_t tile = static_cast<size_t>(blk) * p.Hkv + h;

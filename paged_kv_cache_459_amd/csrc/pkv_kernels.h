@@ -11,6 +11,9 @@ namespace pkv {
 
 constexpr int kBlockSize = 16;  // tokens per block ([P3] §3.2; [P1] §二 example)
 constexpr int kWaves = 4;       // waves per work-group of the attention stream kernels
+// Block-table entry bit marking a block that several sequences of the batch read (the
+// allocator's marked export sets it); the block id is the entry without it.
+constexpr int32_t kSharedBit = 0x40000000;
 
 enum AttnKernel : int32_t { kAuto = 0, kVector = 1, kMatrix = 2 };
 

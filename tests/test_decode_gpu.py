@@ -410,3 +410,58 @@ def test_full_size_sampled(name):
     want = G.sampled_oracle(fp, rows, scale)
     got = G.gpu_f64(out[rows], shape.dtype)
     G.assert_close(got, want, shape.dtype, f"{name} rows {rows}")
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,kernel", [("bf16", 4, 4, 0), ("bf16", 8, 2, 0),
+                                                 ("f16", 8, 2, 1), ("f32", 2, 2, 0)])
+def test_shared_block_mark_changes_nothing(dtype, hq, hkv, kernel):
+    """Entries marked as shared blocks (only the loads' cache policy differs) give the same
+    bits as the unmarked table, through the plain and the fused-append paths, and pass the
+    PKV_CHECK index validation."""
+    m = pkv()
+    rng = np.random.default_rng(12)
+    lens = [37, 512, 700, 1300, 16]
+    base = H.random_problem(rng, lens, hq, hkv, 128, dtype, nb=400)
+    seq_k = [x.copy() for x in base["seq_k"]]
+    seq_v = [x.copy() for x in base["seq_v"]]
+    for i in (2, 3):  # sequences 1..3 share sequence 1's first 32 blocks
+        seq_k[i][:512] = seq_k[1][:512]
+        seq_v[i][:512] = seq_v[1][:512]
+    tables = base["tables"].copy()
+    for i in (2, 3):
+        tables[i, :32] = tables[1, :32]
+    k, v = H.build_caches(seq_k, seq_v, tables, lens, 400, hkv, 128, 16, dtype)
+    p = dict(base, seq_k=seq_k, seq_v=seq_v, tables=tables, k_cache=k, v_cache=v)
+    marked = tables.copy()
+    marked[1:4, :32] |= m.BLOCK_SHARED
+    pm = dict(p, tables=marked)
+    out = W.to_storage_numpy(run_decode(p, G.device_problem(p), 0.1, kernel), dtype)
+    out_m = W.to_storage_numpy(run_decode(pm, G.device_problem(pm), 0.1, kernel), dtype)
+    np.testing.assert_array_equal(out.view(np.uint8), out_m.view(np.uint8))
+    G.assert_close(H.f64(out, dtype), G.oracle_out(p, 0.1), dtype, "shared prefix")
+    os.environ["PKV_CHECK"] = "1"
+    try:
+        run_decode(pm, G.device_problem(pm), 0.1, kernel)
+    finally:
+        del os.environ["PKV_CHECK"]
+    # fused append with the marked table: the newest tokens are in private blocks
+    B = len(lens)
+    k_new = W.normal_values(rng, (B, hkv, 128), dtype)
+    v_new = W.normal_values(rng, (B, hkv, 128), dtype)
+    res = []
+    for tb in (tables, marked):
+        d = G.device_problem(dict(p, tables=tb))
+        prev = m.pkv_set_attn_kernel(kernel)
+        try:
+            o = m.pkv_decode_append_attn(d["q"], G.to_dev(k_new, dtype), G.to_dev(v_new, dtype),
+                                         d["k_cache"], d["v_cache"], d["tables"], d["lens"],
+                                         num_kv_heads=hkv, scale=0.1,
+                                         max_context_len=G.max_context(lens))
+            torch.cuda.synchronize()
+        finally:
+            m.pkv_set_attn_kernel(prev)
+        res.append((W.to_storage_numpy(o, dtype).view(np.uint8),
+                    W.to_storage_numpy(d["k_cache"], dtype).reshape(-1).view(np.uint8),
+                    W.to_storage_numpy(d["v_cache"], dtype).reshape(-1).view(np.uint8)))
+    for a_, b_ in zip(*res):
+        np.testing.assert_array_equal(a_, b_)
