@@ -169,10 +169,14 @@ __device__ __forceinline__ uint32_t load_elem(const char* row, int d) {
   if constexpr (EB == 2) return *reinterpret_cast<const uint16_t*>(row + 2 * d);
   else return *reinterpret_cast<const uint32_t*>(row + 4 * d);
 }
+// Non-temporal element store: the merge pass's new-token stores are partial cache lines that,
+// left dirty in the L2, would be written back in the middle of the next step's stream.
 template <int EB>
-__device__ __forceinline__ void store_elem(char* row, int d, uint32_t bits) {
-  if constexpr (EB == 2) *reinterpret_cast<uint16_t*>(row + 2 * d) = static_cast<uint16_t>(bits);
-  else *reinterpret_cast<uint32_t*>(row + 4 * d) = bits;
+__device__ __forceinline__ void store_elem_nt(char* row, int d, uint32_t bits) {
+  if constexpr (EB == 2)
+    __builtin_nontemporal_store(static_cast<uint16_t>(bits), reinterpret_cast<uint16_t*>(row + 2 * d));
+  else
+    __builtin_nontemporal_store(bits, reinterpret_cast<uint32_t*>(row + 4 * d));
 }
 
 // Per-dtype element access. DT: 0 = f32, 1 = f16, 2 = bf16.
@@ -791,7 +795,7 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_matrix_kernel(const StreamParams p)
 
 // ------------------------------------------------------------------------------------------
 // Append mode, merge pass: one wave stores sequence i's newest K/V rows of kv head h (k_new,
-// v_new) into that token's slot (block_tables[i][(n_i-1)/16], offset (n_i-1)%16): the K row
+// v_new), with non-temporal stores, into that token's slot (block_tables[i][(n_i-1)/16], offset (n_i-1)%16): the K row
 // as 16-byte chunks (chunk c at 256 c + 16 off in the tile), the V row as one element per dim
 // row of the dim-major tile. Nothing is stored for n_i = 0 or a final-block entry outside the
 // pool. The stream pass already used these rows in place of the slot's old contents.
@@ -810,14 +814,16 @@ __device__ void store_new_token(const StreamParams& p, int i, int h) {
   const size_t row = static_cast<size_t>(i) * p.Hkv + h;
   if (lane < CH) {
     const uint4 kk = reinterpret_cast<const uint4*>(p.k_new)[row * CH + lane];
-    reinterpret_cast<uint4*>(const_cast<void*>(p.k_cache))[(tile * CH + lane) * kBlockSize + off] = kk;
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(const_cast<void*>(p.k_cache)) +
+                   (tile * CH + lane) * kBlockSize + off;
+    __builtin_nontemporal_store(u32x4_t{kk.x, kk.y, kk.z, kk.w}, dst);
   }
   const char* vn = static_cast<const char*>(p.v_new) + row * HD * EB;
   char* vtile = static_cast<char*>(const_cast<void*>(p.v_cache)) + tile * HD * kBlockSize * EB;
 #pragma unroll
   for (int r = 0; r < HD / 64; ++r) {
     const int d = lane + 64 * r;
-    store_elem<EB>(vtile, d * kBlockSize + off, load_elem<EB>(vn, d));
+    store_elem_nt<EB>(vtile, d * kBlockSize + off, load_elem<EB>(vn, d));
   }
 }
 

@@ -15,6 +15,8 @@
 namespace pkv {
 namespace {
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
 template <int EB>
 __global__ void __launch_bounds__(256)
 write_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v, uint4* __restrict__ kc,
@@ -36,17 +38,21 @@ write_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v, uint4* __
   const uint4 kk = k[gid];  // k is [T][Hkv][hd]: chunk (t, h, c) is chunk number gid
   const uint4 vv = v[gid];
   const size_t tile = static_cast<size_t>(b) * Hkv + h;
-  kc[(tile * chunks + c) * kBlockSize + off] = kk;
+  // Non-temporal stores: these are partial cache lines which, left dirty in the L2, would be
+  // written back in the middle of the next attention pass's stream of K/V tiles.
+  __builtin_nontemporal_store(u32x4_t{kk.x, kk.y, kk.z, kk.w},
+                              reinterpret_cast<u32x4_t*>(kc) + (tile * chunks + c) * kBlockSize + off);
   const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
   if constexpr (EB == 2) {
     uint16_t* vd = static_cast<uint16_t*>(vc) + (tile * hd + static_cast<size_t>(X) * c) * kBlockSize + off;
 #pragma unroll
     for (int x = 0; x < 8; ++x)
-      vd[x * kBlockSize] = static_cast<uint16_t>((w[x >> 1] >> ((x & 1) * 16)) & 0xFFFFu);
+      __builtin_nontemporal_store(static_cast<uint16_t>((w[x >> 1] >> ((x & 1) * 16)) & 0xFFFFu),
+                                  vd + x * kBlockSize);
   } else {
     uint32_t* vd = static_cast<uint32_t*>(vc) + (tile * hd + static_cast<size_t>(X) * c) * kBlockSize + off;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) vd[x * kBlockSize] = w[x];
+    for (int x = 0; x < 4; ++x) __builtin_nontemporal_store(w[x], vd + x * kBlockSize);
   }
 }
 
