@@ -22,7 +22,7 @@ paged cache. Modules:
 
 * ``layout``     -- where token t / dim d of a (block, kv head) tile lives in the caches.
 * ``attention``  -- gather + dense attention; partition partials and their log-sum-exp merge.
-* ``cache_write``-- the scatter of new tokens into their slots.
+* ``cache_write``-- the scatter of new tokens into their slots; the copy-on-write block copy.
 * ``allocator``  -- FIFO / refcount block allocator (allocate on demand, fork, free, COW).
 """
 

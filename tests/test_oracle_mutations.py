@@ -2,7 +2,7 @@
 
 Each case patches one oracle function with a wrong variant (a dropped scale, a wrong
 kv-head mapping, an off-by-one gather, a transposed tile, an unweighted merge, a LIFO free
-list, a missing copy-on-write) and runs an existing pin, which must then fail.
+list, a missing copy-on-write, a skipped, reversed or half block copy) and runs an existing pin, which must then fail.
 """
 
 import numpy as np
@@ -10,9 +10,11 @@ import pytest
 
 from oracle import allocator as AL
 from oracle import attention as A
+from oracle import cache_write as CW
 from oracle import layout as L
 from tests import test_oracle_allocator as TAL
 from tests import test_oracle_attention as TA
+from tests import test_oracle_beam as TB
 
 
 def _fails(fn, *args):
@@ -92,3 +94,27 @@ def test_missing_copy_on_write_is_caught(monkeypatch):
                         lambda self, seq, ntok: (False, -(-(self.length[seq] + ntok) // self.bs)
                                                  - -(-self.length[seq] // self.bs)))
     _fails(TAL.test_copy_on_write_pair_reported)
+
+
+def test_skipped_block_copy_is_caught(monkeypatch):
+    monkeypatch.setattr(CW, "copy_blocks",
+                        lambda kc, vc, pairs, **kw: (np.array(kc, copy=True),
+                                                     np.array(vc, copy=True)))
+    _fails(TB.test_beam_loop_keeps_every_beams_history, "f32")
+
+
+def test_reversed_block_copy_is_caught(monkeypatch):
+    orig = CW.copy_blocks
+    monkeypatch.setattr(CW, "copy_blocks",
+                        lambda kc, vc, pairs, **kw: orig(kc, vc, [(d, s) for s, d in pairs], **kw))
+    _fails(TB.test_beam_loop_keeps_every_beams_history, "f32")
+
+
+def test_copy_of_one_cache_only_is_caught(monkeypatch):
+    orig = CW.copy_blocks
+
+    def k_only(kc, vc, pairs, **kw):
+        k2, _ = orig(kc, vc, pairs, **kw)
+        return k2, np.array(vc, copy=True)
+    monkeypatch.setattr(CW, "copy_blocks", k_only)
+    _fails(TB.test_beam_loop_keeps_every_beams_history, "bf16")

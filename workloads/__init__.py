@@ -162,6 +162,13 @@ def beam_tables(group_tail_lens, free_order, beams=4, prefix_tokens=PREFIX_TOKEN
     return tables, np.asarray(lens, dtype=np.int32)
 
 
+def beam_parents(rng, groups, beams):
+    """Stand-in for beam selection (no model here): for each of ``groups`` groups, the parent
+    beam (0..beams-1) of each of its next ``beams`` beams, drawn uniformly with replacement
+    and sorted. int array [groups, beams]."""
+    return np.sort(rng.integers(0, beams, size=(groups, beams)), axis=1)
+
+
 def blocks_in_use(tables, lengths, bs=BLOCK_SIZE):
     used = set()
     for row, n in zip(tables, lengths):
