@@ -12,6 +12,11 @@ One step = one decode step of every sequence in the batch, through the whole pat
      streams an equal share of the batch's K/V tiles), then the merge pass: the log-sum-exp
      merge of the segments cut between waves, and the stores of the new K/V into their slots.
 
+Beam search (--workload beam_search) replaces step 1 by a beam re-selection: each group's
+next beams fork from seeded parents among its current beams (batched fork and free), each
+appends one token, and the step's copy-on-write pairs go to the device with the full table
+export; the step then runs pkv_copy_blocks on those pairs before the two kernels.
+
 Prints one JSON line: the metric (KV-read GB/s over the timed steps), decode tokens/s per
 layer, the roofline figure of the stream kernel (algorithmic bytes / its mean duration,
 measured with HIP events on the launch stream) and the oracle's throughput on a bounded
@@ -35,7 +40,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "paged decode attn: KV-read GB/s and % of HBM peak; decode tokens/s per layer"
-WORKLOADS = ("llama2_7b", "qwen25_7b", "prefix_shared", "long_context")
+WORKLOADS = ("llama2_7b", "qwen25_7b", "prefix_shared", "long_context", "beam_search")
 DESC = {
     "llama2_7b": "Llama-2-7B-shaped single layer decode: MHA 32 x 128, f16, batch 64, "
                  "context U[128,2048], blocks scattered in a pool of 1.1x need",
@@ -45,6 +50,10 @@ DESC = {
                      "refcount 128) + private tails U[16,512], MHA 32 x 128, bf16",
     "long_context": "long-context continuous-batching step: 8 seqs at 32768 + 120 at "
                     "U[64,4096], GQA 32 q / 8 kv x 128, bf16",
+    "beam_search": "beam search: 32 groups x 4 beams share a 2000-token prefix, a group's "
+                   "beams share its tail U[16,512]; every step re-selects each group's 4 beams "
+                   "(seeded parents, forks at unaligned lengths), appends one token per beam "
+                   "with copy-on-write of shared partly filled blocks, MHA 32 x 128, bf16",
 }
 
 
@@ -90,6 +99,7 @@ class Workload:
 
     def __init__(self, name, total_steps, torch, pkv, W):
         self.name = name
+        self.gen = W  # the seeded input generators
         shape = self.shape = W.SHAPES[name]
         rng = W.rng_for(shape.seed)
         lens = W.draw_lengths(shape, rng)  # lengths after the first step's token
@@ -104,7 +114,26 @@ class Workload:
         order = rng.permutation(nb).astype(np.int32)
         self.alloc = pkv.BlockAllocator(nb, 16, order)
         self.seqs = np.arange(self.B, dtype=np.int64)
-        if name == "prefix_shared":
+        self.beam = name == "beam_search"
+        self.cows = []  # copy-on-write pairs per timed step
+        self.cows_all = []  # and per step of the whole run (warm-up included)
+        if self.beam:
+            # the prefix, then per group its tail, then the group's beams forked from it (they
+            # share every block, the partly filled last one included, until they append)
+            parent = 10_000_000
+            self.alloc.add_seq(parent)
+            self.alloc.append([parent], [W.PREFIX_TOKENS], want_slots=False)
+            groups = self.B // W.BEAMS
+            roots = np.arange(parent + 1, parent + 1 + groups, dtype=np.int64)
+            self.alloc.fork_many(np.full(groups, parent, np.int64), roots)
+            self.alloc.free(parent)
+            self.alloc.append(roots, lens[::W.BEAMS] - 1 - W.PREFIX_TOKENS, want_slots=False)
+            self.alloc.fork_many(np.repeat(roots, W.BEAMS), self.seqs)
+            self.alloc.free_many(roots)
+            self.next_id = int(self.seqs[-1]) + 1
+            self.beam_rng = np.random.default_rng(shape.seed + 100)
+            self.group_base = (np.arange(groups) * W.BEAMS)[:, None]
+        elif name == "prefix_shared":
             prefix = W.PREFIX_TOKENS
             parent = 10_000_000
             self.alloc.add_seq(parent)
@@ -127,10 +156,11 @@ class Workload:
         self.k_new = W.device_normal((self.B, self.Hkv, self.hd), shape.dtype, 7004)
         self.v_new = W.device_normal((self.B, self.Hkv, self.hd), shape.dtype, 7005)
         self.out = torch.empty_like(self.q)
-        # Two sets of step buffers, each one packed int32 array [lens | slots | tables], in
+        # Two sets of step buffers, each one packed int32 array [lens | slots | copy-on-write
+        # sources | copy-on-write targets | tables], in
         # pinned host memory and on the device: the host prepares step k+1 and its copy runs on
         # a copy stream while step k's kernels run on the compute stream.
-        n_int = 2 * self.B + self.B * self.max_blocks
+        n_int = 4 * self.B + self.B * self.max_blocks
         self.pin = [torch.empty(n_int, dtype=torch.int32, pin_memory=True) for _ in range(2)]
         self.dev = [torch.empty(n_int, dtype=torch.int32, device=dev) for _ in range(2)]
         self.host_views = [self._views(t.numpy()) for t in self.pin]
@@ -159,7 +189,12 @@ class Workload:
 
     def _views(self, flat):
         B, mb = self.B, self.max_blocks
-        return flat[:B], flat[B:2 * B], flat[2 * B:].reshape(B, mb)
+        return flat[:B], flat[B:2 * B], flat[4 * B:].reshape(B, mb)
+
+    def cow_views(self, s):
+        """(host, device) views [2, B] of buffer set s's copy-on-write pairs."""
+        B = self.B
+        return self.pin[s].numpy()[2 * B:4 * B].reshape(2, B), self.dev[s][2 * B:4 * B].view(2, B)
 
     def kv_bytes(self, lens):
         return int(lens.astype(np.int64).sum()) * 2 * self.Hkv * self.hd * self.eb
@@ -179,13 +214,38 @@ class Workload:
         return 2 * self.B * self.Hq * self.hd * self.eb + 4 * self.B * self.Hkv * self.hd * self.eb
 
 
+def beam_reselect(wl, s):
+    """Beam-search host part of a step: every group's next beams fork from seeded parents
+    among its current beams, the old beams are freed, each new beam appends one token, and
+    buffer set s receives the full table export and the copy-on-write pairs. Returns the
+    number of pairs."""
+    lens_h, _, tables_h = wl.host_views[s]
+    cow_h, _ = wl.cow_views(s)
+    pick = wl.gen.beam_parents(wl.beam_rng, wl.group_base.shape[0], wl.gen.BEAMS)
+    parents = wl.seqs[(wl.group_base + pick).reshape(-1)]
+    children = np.arange(wl.next_id, wl.next_id + wl.B, dtype=np.int64)
+    wl.next_id += wl.B
+    wl.alloc.fork_many(parents, children)
+    wl.alloc.free_many(wl.seqs)
+    wl.seqs = children
+    _, cows = wl.alloc.append(wl.seqs, wl.ones, want_slots=False)
+    wl.alloc.tables(wl.seqs, wl.max_blocks, tables_out=tables_h, lens_out=lens_h,
+                    mark_shared=True)
+    n = len(cows)
+    cow_h[:, :n] = cows.T
+    wl.lens = lens_h.copy()
+    return n
+
+
 def run_step(wl, torch, pkv, events=None):
-    """One decode step (see the module docstring). Returns the context lengths it used."""
+    """One decode step (see the module docstring). Returns the context lengths it used and,
+    for beam search, the step's tables."""
     s = wl.step_no % 2
     wl.step_no += 1
     wl.done[s].synchronize()  # the step that last used buffer set s has finished
+    if wl.beam:
+        return run_beam_step(wl, torch, pkv, s, events)
     lens_h, slots_h, tables_h = wl.host_views[s]
-    lens_d, slots_d, tables_d = wl.dev_views[s]
     wl.alloc.append(wl.seqs, wl.ones, slots_out=slots_h)  # 1. allocate on demand
     opened = wl.lens % 16 == 0  # the new token is the first of a fresh block
     update = (wl.rows[opened], wl.lens[opened] // 16, slots_h[opened] // 16)
@@ -203,22 +263,49 @@ def run_step(wl, torch, pkv, events=None):
     compute.wait_event(wl.copied[s])
     if events is not None:
         events[0].record()
+        events[1].record()  # no copy-on-write in a decode loop without forks
+    attend(wl, pkv, s, events)
+    return lens_h.copy(), None
+
+
+def run_beam_step(wl, torch, pkv, s, events):
+    ncow = beam_reselect(wl, s)
+    wl.cows.append(ncow)
+    wl.cows_all.append(ncow)
+    with torch.cuda.stream(wl.copy_stream):  # tables, lengths, pairs to the device
+        wl.dev[s].copy_(wl.pin[s], non_blocking=True)
+        wl.copied[s].record(wl.copy_stream)
+    torch.cuda.current_stream().wait_event(wl.copied[s])
+    if events is not None:
+        events[0].record()
+    if ncow:  # copy-on-write: the shared blocks appenders moved off, copied to their new blocks
+        _, cow_d = wl.cow_views(s)
+        pkv.pkv_copy_blocks(wl.k_cache, wl.v_cache, cow_d[0, :ncow], cow_d[1, :ncow],
+                            num_kv_heads=wl.Hkv, head_dim=wl.hd)
+    if events is not None:
+        events[1].record()
+    attend(wl, pkv, s, events)
+    return wl.lens.copy(), wl.host_views[s][2].copy()
+
+
+def attend(wl, pkv, s, events):
+    """The step's two kernels on buffer set s (tables, lengths on the device)."""
+    lens_d, _, tables_d = wl.dev_views[s]
     # 3 + 4a. cache write of the newest tokens fused into the attention stream pass
     pkv.pkv_decode_append_stream(wl.q, wl.k_new, wl.v_new, wl.k_cache, wl.v_cache, tables_d,
                                  lens_d, num_kv_heads=wl.Hkv, scale=wl.scale,
                                  max_context_len=wl.max_ctx, num_workers=wl.W,
                                  workspace=wl.workspace, out=wl.out)
     if events is not None:
-        events[1].record()
+        events[2].record()
     # 4b. merge of the cut segments, plus the stores of the new tokens into their slots
     pkv.pkv_decode_append_merge(wl.out, wl.k_new, wl.v_new, wl.k_cache, wl.v_cache, tables_d,
                                 lens_d, wl.workspace, num_kv_heads=wl.Hkv,
                                 max_context_len=wl.max_ctx, num_workers=wl.W)
     if events is not None:
-        events[2].record()
+        events[3].record()
     wl.done[s].record()
     wl.last_set = s
-    return lens_h.copy()
 
 
 def cpu_baseline(wl, torch, W, seconds):
@@ -288,25 +375,31 @@ def main():
         run_step(wl, torch, pkv)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    lens_per_step = []
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    per_step = []
+    wl.cows.clear()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        lens_per_step.append(run_step(wl, torch, pkv, evs[k]))
+        per_step.append(run_step(wl, torch, pkv, evs[k]))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    part_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    merge_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    # A table only ever gains entries, so the final tables hold every step's blocks; they must
-    # be exactly what the allocator exports.
+    copy_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    part_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    merge_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    # The last tables sent must be exactly what the allocator exports (for the decode loop,
+    # whose tables only gain entries, this checks every incremental update).
     final_tables = wl.host_views[wl.last_set][2].copy()
     ref_tables, ref_lens = wl.alloc.tables(wl.seqs, wl.max_blocks, mark_shared=True)
     assert np.array_equal(final_tables, ref_tables) and np.array_equal(wl.lens, ref_lens), \
-        "incremental block tables diverged from the allocator's export"
+        "block tables sent to the device diverged from the allocator's export"
+
+    def unmarked(t):
+        return np.where(t >= 0, t & ~pkv.BLOCK_SHARED, t)
+    lens_per_step = [lens for lens, _ in per_step]
     kv_logical = [wl.kv_bytes(lens) for lens in lens_per_step]
-    blocks = np.where(final_tables >= 0, final_tables & ~pkv.BLOCK_SHARED, final_tables)
-    kv = [wl.unique_kv_bytes(lens, blocks) for lens in lens_per_step]
+    kv = [wl.unique_kv_bytes(lens, unmarked(final_tables if t is None else t))
+          for lens, t in per_step]
     algo = [b + wl.qo_bytes() for b in kv]
     ms_per_step = wall / args.steps * 1e3
     value = sum(kv) / wall / 1e9
@@ -361,6 +454,19 @@ def main():
             "algorithmic_bytes_per_launch": int(np.mean(algo)),
         },
     }
+    if wl.beam:
+        # copy-on-write copies: both caches, every kv head, read + written
+        pair_bytes = 4 * wl.Hkv * wl.hd * 16 * wl.eb
+        copied = sum(wl.cows) * pair_bytes
+        res["cow_copy"] = {
+            "kernel": "copy_blocks_kernel (pkv_copy_blocks)",
+            "pairs_per_step": round(float(np.mean(wl.cows)), 2),
+            "bytes_per_pair": pair_bytes,
+            "ms_per_step": round(float(np.mean(copy_ms)), 4),
+            "achieved_gbs": round(copied / (sum(copy_ms) / 1e3) / 1e9, 2) if copied else None,
+            "note": "measured between HIP events around the launch (includes its launch gap)",
+            "pairs_every_launch": [int(c) for c in wl.cows_all if c],
+        }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, torch, W, args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -95,6 +95,27 @@ pkv_status pkv_write(const void* k, const void* v, void* k_cache, void* v_cache,
                      const int32_t* slot_mapping, int32_t T, int32_t Hkv, int32_t hd, int32_t bs,
                      int32_t NB, pkv_dtype dtype, void* stream);
 
+/* Copy-on-write block copy.                                                                 */
+/* [P2] vLLM overview, "共享和复用" and the Beam Search item of "PagedAttention 的优势": beam  */
+/* candidates share the blocks of their common history. The pages leave open what happens    */
+/* when one of them appends into a shared, partly filled block; here pkv_alloc_append moves   */
+/* the appender to a fresh block and reports the pair (src, dst), and this call copies the    */
+/* data: for every pair i, every kv head's tile of block src[i] in both caches is copied      */
+/* bitwise into block dst[i] (the whole block, slots past the filled ones included). Run it   */
+/* before the write or attention that uses the new block, on the same stream.                 */
+/*   k_cache, v_cache  device, cache layout above, NB blocks (written at blocks dst[i] only)  */
+/*   src, dst      device int32 [n]. A pair with either entry outside [0, NB) is skipped      */
+/*                 (negative entries: padding). Caller contract: the non-skipped dst are      */
+/*                 distinct and none of them is also a src of the call (pkv_alloc_append's    */
+/*                 pairs satisfy both); otherwise the result is undefined, but every access   */
+/*                 stays inside the caches.                                                   */
+/* n == 0 is a no-op. Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED (also when one block    */
+/* of one cache exceeds 1 GiB), PKV_ERR_INDEX (PKV_CHECK=1: an entry >= NB, a repeated dst or */
+/* a dst that is also a src), PKV_ERR_HIP.                                                    */
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst,
+                           int32_t n, int32_t Hkv, int32_t hd, int32_t bs, int32_t NB,
+                           pkv_dtype dtype, void* stream);
+
 /* ------------------------------------------------------------------------------------------ */
 /* Decode attention.                                                                         */
 /* [P1] §三 步驟三 (last step) and §五 ("Attention Kernel ... 用塊表計算注意力"); [P2]         */
@@ -289,6 +310,17 @@ pkv_status pkv_alloc_fork(pkv_allocator* a, int64_t parent, int64_t child);
 
 /* Release the sequence and its blocks ([P1] §三 步驟四). */
 pkv_status pkv_alloc_free(pkv_allocator* a, int64_t seq);
+
+/* Batched forms for a beam-search re-selection ([P2] "PagedAttention 的优势", Beam Search:  */
+/* candidates share their common history): the same as pkv_alloc_fork(parents[k],          */
+/* children[k]) for k = 0..n-1, in order, resp. pkv_alloc_free(seqs[k]) in order (so blocks  */
+/* reach the free list in the same order), in one call. All-or-nothing: fork_many needs every */
+/* parent present before the call and every child absent and distinct (PKV_ERR_UNKNOWN_SEQ,  */
+/* PKV_ERR_SEQ_EXISTS); free_many needs distinct ids (PKV_ERR_INVALID_ARG), all present       */
+/* (PKV_ERR_UNKNOWN_SEQ). A failing call changes nothing.                                      */
+pkv_status pkv_alloc_fork_many(pkv_allocator* a, int32_t n, const int64_t* parents,
+                               const int64_t* children);
+pkv_status pkv_alloc_free_many(pkv_allocator* a, int32_t n, const int64_t* seqs);
 
 /* Export block tables for seqs[0..n-1]: block_tables_out [n][max_blocks] (host int32, entries */
 /* past a sequence's block count set to -1) and context_lens_out [n] (host int32). A sequence  */

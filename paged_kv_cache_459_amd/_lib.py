@@ -51,6 +51,8 @@ SIGNATURES = {
     "pkv_cache_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "pkv_write": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                           c_vp]),
+    "pkv_copy_blocks": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                c_vp]),
     "pkv_decode_attn": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                 c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp, c_sz, c_vp]),
     "pkv_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),
@@ -78,6 +80,8 @@ SIGNATURES = {
     "pkv_alloc_append": (c_i32, [c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "pkv_alloc_fork": (c_i32, [c_vp, c_i64, c_i64]),
     "pkv_alloc_free": (c_i32, [c_vp, c_i64]),
+    "pkv_alloc_fork_many": (c_i32, [c_vp, c_i32, c_vp, c_vp]),
+    "pkv_alloc_free_many": (c_i32, [c_vp, c_i32, c_vp]),
     "pkv_alloc_tables": (c_i32, [c_vp, c_i32, c_vp, c_i32, c_vp, c_vp]),
     "pkv_alloc_tables_marked": (c_i32, [c_vp, c_i32, c_vp, c_i32, c_vp, c_vp]),
     "pkv_alloc_num_free": (c_i32, [c_vp]),

@@ -95,6 +95,25 @@ def pkv_write(k, v, k_cache, v_cache, slot_mapping):
                         hkv, hd, BLOCK_SIZE, nb, pkv_dtype(k), _stream(k.device)), "pkv_write")
 
 
+def pkv_copy_blocks(k_cache, v_cache, src, dst, *, num_kv_heads, head_dim):
+    """Copy block src[i] to block dst[i] in both caches (every kv head), for each pair i.
+
+    src, dst: int32 device tensors of one length (the copy-on-write pairs that
+    BlockAllocator.append reports, uploaded)."""
+    _need(k_cache, "k_cache", device=k_cache.device)
+    _need(v_cache, "v_cache", dtype=k_cache.dtype, device=k_cache.device)
+    _need(src, "src", dtype=torch.int32, device=k_cache.device)
+    _need(dst, "dst", dtype=torch.int32, device=k_cache.device)
+    if src.numel() != dst.numel():
+        raise ValueError("src and dst lengths differ")
+    nb = _num_blocks(k_cache, num_kv_heads, head_dim)
+    if v_cache.numel() != k_cache.numel():
+        raise ValueError("k_cache and v_cache sizes differ")
+    check(lib.pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(src), _ptr(dst), src.numel(),
+                              num_kv_heads, head_dim, BLOCK_SIZE, nb, pkv_dtype(k_cache),
+                              _stream(k_cache.device)), "pkv_copy_blocks")
+
+
 def pkv_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,
                                dtype):
     return int(lib.pkv_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
@@ -320,6 +339,20 @@ class BlockAllocator:
 
     def free(self, seq):
         check(lib.pkv_alloc_free(self._h, int(seq)), "pkv_alloc_free")
+
+    def fork_many(self, parents, children):
+        """fork(parents[k], children[k]) for every k, in order, in one call (all-or-nothing)."""
+        p = _as_c(parents, np.int64)
+        c = _as_c(children, np.int64)
+        if p.shape != c.shape or p.ndim != 1:
+            raise ValueError("parents and children must be 1-D and of one length")
+        check(lib.pkv_alloc_fork_many(self._h, len(p), p.ctypes.data, c.ctypes.data),
+              "pkv_alloc_fork_many")
+
+    def free_many(self, seqs):
+        """free(seqs[k]) for every k, in order, in one call (all-or-nothing)."""
+        s = _as_c(seqs, np.int64)
+        check(lib.pkv_alloc_free_many(self._h, len(s), s.ctypes.data), "pkv_alloc_free_many")
 
     def tables(self, seqs, max_blocks, tables_out=None, lens_out=None, mark_shared=False):
         """Block tables [n, max_blocks] (pad -1) and lengths; with mark_shared, entries of

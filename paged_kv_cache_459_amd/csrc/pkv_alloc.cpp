@@ -183,6 +183,58 @@ pkv_status pkv_alloc_free(pkv_allocator* a, int64_t seq) {
   return PKV_OK;
 }
 
+pkv_status pkv_alloc_fork_many(pkv_allocator* a, int32_t n, const int64_t* parents,
+                               const int64_t* children) {
+  if (!a || n < 0 || (n > 0 && (!parents || !children))) return PKV_ERR_INVALID_ARG;
+  // All-or-nothing: every parent present before the call, every child absent and named once.
+  std::vector<const Seq*> from(n);
+  for (int32_t k = 0; k < n; ++k) {
+    auto it = a->seqs.find(parents[k]);
+    if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+    from[k] = &it->second;
+  }
+  std::unordered_set<int64_t> kids;
+  kids.reserve(static_cast<size_t>(n));
+  for (int32_t k = 0; k < n; ++k)
+    if (a->seqs.count(children[k]) || !kids.insert(children[k]).second) return PKV_ERR_SEQ_EXISTS;
+  std::vector<Seq> copies(n);  // copied before any insertion can move the parents
+  for (int32_t k = 0; k < n; ++k) {
+    copies[k].blocks = from[k]->blocks;
+    copies[k].len = from[k]->len;
+  }
+  a->seqs.reserve(a->seqs.size() + static_cast<size_t>(n));
+  for (int32_t k = 0; k < n; ++k) {
+    for (int32_t b : copies[k].blocks) a->ref[b] += 1;
+    a->seqs.emplace(children[k], std::move(copies[k]));
+  }
+  return PKV_OK;
+}
+
+pkv_status pkv_alloc_free_many(pkv_allocator* a, int32_t n, const int64_t* seqs) {
+  if (!a || n < 0 || (n > 0 && !seqs)) return PKV_ERR_INVALID_ARG;
+  // All-or-nothing: every id present and named once (stamped like pkv_alloc_append's check).
+  const uint64_t call = ++a->calls;
+  bool unknown = false, dup = false;
+  for (int32_t k = 0; k < n; ++k) {
+    auto it = a->seqs.find(seqs[k]);
+    if (it == a->seqs.end()) {
+      unknown = true;
+      continue;
+    }
+    if (it->second.mark == call) dup = true;
+    it->second.mark = call;
+  }
+  if (unknown && !dup) {
+    std::unordered_set<int64_t> distinct;
+    for (int32_t k = 0; k < n; ++k)
+      if (!distinct.insert(seqs[k]).second) dup = true;
+  }
+  if (dup) return PKV_ERR_INVALID_ARG;
+  if (unknown) return PKV_ERR_UNKNOWN_SEQ;
+  for (int32_t k = 0; k < n; ++k) pkv_alloc_free(a, seqs[k]);
+  return PKV_OK;
+}
+
 }  // extern "C"
 
 namespace {

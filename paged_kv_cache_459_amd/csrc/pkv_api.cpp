@@ -251,6 +251,36 @@ pkv_status pkv_write(const void* k, const void* v, void* k_cache, void* v_cache,
   return pkv::launch_write(p, dtype, hs) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst,
+                           int32_t n, int32_t Hkv, int32_t hd, int32_t bs, int32_t NB,
+                           pkv_dtype dtype, void* stream) {
+  if (!dtype_ok(dtype) || bs != kBlockSize || !head_dim_ok(hd)) return PKV_ERR_UNSUPPORTED;
+  if (n < 0 || Hkv <= 0 || NB <= 0 || static_cast<int64_t>(NB) * kBlockSize >= (int64_t{1} << 31))
+    return PKV_ERR_INVALID_ARG;
+  if (pkv::copy_blocks_grid_y(Hkv, hd, dtype) > 65535) return PKV_ERR_UNSUPPORTED;
+  if (n == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !src || !dst) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || (reinterpret_cast<uintptr_t>(src) & 3u) ||
+      (reinterpret_cast<uintptr_t>(dst) & 3u))
+    return PKV_ERR_INVALID_ARG;
+  auto hs = static_cast<hipStream_t>(stream);
+  if (check_mode()) {
+    std::vector<int32_t> s, d;
+    if (!copy_to_host(&s, src, n, hs) || !copy_to_host(&d, dst, n, hs)) return PKV_ERR_HIP;
+    std::unordered_set<int32_t> targets, sources;
+    for (int32_t i = 0; i < n; ++i) {
+      if (s[i] >= NB || d[i] >= NB) return PKV_ERR_INDEX;
+      if (s[i] < 0 || d[i] < 0) continue;  // padding pair
+      if (!targets.insert(d[i]).second) return PKV_ERR_INDEX;
+      sources.insert(s[i]);
+    }
+    for (int32_t t : targets)
+      if (sources.count(t)) return PKV_ERR_INDEX;
+  }
+  pkv::CopyParams p{k_cache, v_cache, src, dst, n, Hkv, hd, NB};
+  return pkv::launch_copy_blocks(p, dtype, hs) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 int32_t pkv_decode_kernel(int32_t Hq, int32_t Hkv, pkv_dtype dtype) {
   if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || !dtype_ok(dtype)) return 0;
   return current_kernel(dtype, Hq, Hkv);

@@ -26,6 +26,14 @@ struct WriteParams {
   int32_t T, Hkv, hd, NB;
 };
 
+struct CopyParams {
+  void* k_cache;
+  void* v_cache;
+  const int32_t* src;  // [n] device: block copied from
+  const int32_t* dst;  // [n] device: block copied to
+  int32_t n, Hkv, hd, NB;
+};
+
 // Arguments of the attention stream pass and of the merge pass.
 struct StreamParams {
   void* out;
@@ -49,6 +57,9 @@ struct StreamParams {
 
 // dtype: 0 f32, 1 f16, 2 bf16 (pkv_dtype). Return the launch status (hipGetLastError).
 hipError_t launch_write(const WriteParams& p, int32_t dtype, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyParams& p, int32_t dtype, hipStream_t stream);
+// Work-groups per block and cache of the copy kernel (grid.y; at most 65535 is launchable).
+int32_t copy_blocks_grid_y(int32_t Hkv, int32_t hd, int32_t dtype);
 hipError_t launch_stream(const StreamParams& p, int32_t dtype, int32_t kernel,
                          hipStream_t stream);
 hipError_t launch_merge(const StreamParams& p, int32_t dtype, int32_t kernel,

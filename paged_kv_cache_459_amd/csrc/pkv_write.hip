@@ -4,6 +4,8 @@
 // into the current block of its sequence; the allocator has already chosen the slot
 // (block * 16 + offset). The copy is bitwise.
 //
+// Also the copy-on-write block copy (below).
+//
 // One thread moves one 16-byte chunk (X = 16 / element-bytes consecutive dims of one head of
 // one token). The K chunk lands as one 16-byte store (the K tile keeps 16-byte chunks of dims,
 // token-minor); the V chunk is spread over the X dim rows of the dim-major V tile.
@@ -56,7 +58,63 @@ write_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v, uint4* __
   }
 }
 
+// Copy-on-write block copy. [P2] vLLM overview, "共享和复用" and the Beam Search item of
+// "PagedAttention 的优势": beam candidates share the blocks of their common history; before one
+// of them appends into a shared, partly filled block the allocator moves it to a fresh block
+// (dst) and this kernel copies the shared block (src) there: every kv head's tile, both
+// caches, bitwise, whole.
+//
+// A block is `chunks` consecutive 16-byte chunks of each cache (the (block, kv head) tiles of
+// one block are adjacent). Work-group (pair, y, cache) moves chunks [y*256*U, (y+1)*256*U) of
+// pair `pair` in cache `cache` (0 K, 1 V): U loads in flight per lane, then U stores. The
+// source is read with ordinary loads (the attention pass reads it next, through the other
+// sequences that share it); the destination is written with non-temporal stores.
+template <int U>
+__global__ void __launch_bounds__(256)
+copy_blocks_kernel(u32x4_t* __restrict__ kc, u32x4_t* __restrict__ vc,
+                   const int32_t* __restrict__ src, const int32_t* __restrict__ dst, int32_t NB,
+                   int32_t chunks) {
+  const int32_t s = src[blockIdx.x];
+  const int32_t d = dst[blockIdx.x];
+  if (s < 0 || s >= NB || d < 0 || d >= NB) return;  // padding, or outside the pool
+  u32x4_t* base = blockIdx.z == 0 ? kc : vc;
+  const u32x4_t* from = base + static_cast<size_t>(s) * chunks;
+  u32x4_t* to = base + static_cast<size_t>(d) * chunks;
+  const int first = static_cast<int>(blockIdx.y) * (256 * U);
+  const int i0 = first + static_cast<int>(threadIdx.x);
+  if (first + 256 * U <= chunks) {  // whole range inside the block (uniform branch)
+    u32x4_t r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) r[u] = from[i0 + u * 256];
+#pragma unroll
+    for (int u = 0; u < U; ++u) __builtin_nontemporal_store(r[u], to + i0 + u * 256);
+  } else {  // the block's last, partial range
+    for (int i = i0; i < chunks; i += 256) __builtin_nontemporal_store(from[i], to + i);
+  }
+}
+
+constexpr int kCopyUnroll = 4;
+
 }  // namespace
+
+hipError_t launch_copy_blocks(const CopyParams& p, int32_t dtype, hipStream_t stream) {
+  if (p.n == 0) return hipSuccess;
+  const int eb = dtype == 0 ? 4 : 2;
+  const int32_t chunks = p.Hkv * p.hd * eb;  // 16-byte chunks per block: Hkv*hd*16*eb / 16
+  const dim3 grid(static_cast<unsigned>(p.n),
+                  static_cast<unsigned>((chunks + 256 * kCopyUnroll - 1) / (256 * kCopyUnroll)),
+                  2);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(copy_blocks_kernel<kCopyUnroll>, grid, dim3(256), 0, stream,
+                     static_cast<u32x4_t*>(p.k_cache), static_cast<u32x4_t*>(p.v_cache), p.src,
+                     p.dst, p.NB, chunks);
+  return note_error("copy_blocks_kernel launch", hipGetLastError());
+}
+
+int32_t copy_blocks_grid_y(int32_t Hkv, int32_t hd, int32_t dtype) {
+  const int64_t chunks = static_cast<int64_t>(Hkv) * hd * (dtype == 0 ? 4 : 2);
+  return static_cast<int32_t>((chunks + 256 * kCopyUnroll - 1) / (256 * kCopyUnroll));
+}
 
 hipError_t launch_write(const WriteParams& p, int32_t dtype, hipStream_t stream) {
   const int eb = dtype == 0 ? 4 : 2;

@@ -176,3 +176,54 @@ def test_marked_tables_flag_exactly_the_shared_blocks():
             shared = o.refcount(e_p) > 1
             assert e_m == (e_p | BLOCK_SHARED if shared else e_p)
     assert (marked[0, :3] & BLOCK_SHARED).all() and not (marked[0, 3] & BLOCK_SHARED)
+
+
+def test_batched_fork_and_free_equal_the_single_calls():
+    """fork_many / free_many (a beam re-selection in one call each) leave exactly the state of
+    the single calls in order, including the free-list order; failing calls change nothing."""
+    rng = np.random.default_rng(151)
+    nb = 200
+    order = rng.permutation(nb)
+    nat, ora = Native(nb, BS, order), Oracle(nb, BS, order)
+    for s in range(4):
+        nat.add_seq(s)
+        ora.add_seq(s)
+    lens = [21, 16, 7, 40]
+    nat.append(range(4), lens)
+    ora.append(list(range(4)), lens)
+    live, next_id = [0, 1, 2, 3], 4
+    for _ in range(30):
+        parents = [live[int(i)] for i in rng.integers(0, len(live), size=6)]
+        children = list(range(next_id, next_id + 6))
+        next_id += 6
+        nat.fork_many(parents, children)
+        for p, c in zip(parents, children):
+            ora.fork(p, c)
+        nat.free_many(live)
+        for s in live:
+            ora.free_seq(s)
+        live = children
+        r_n = nat.append(live, [1] * len(live))
+        r_o = ora.append(live, [1] * len(live))
+        assert r_n[0].tolist() == r_o[0]
+        assert [tuple(c) for c in r_n[1].tolist()] == r_o[1]
+        same_state(nat, ora, live)
+    # errors: nothing changes
+    before = (nat.free_list(), [nat.refcount(b) for b in range(nb)])
+    for call, code in [(lambda: nat.fork_many([live[0], 999_999], [next_id, next_id + 1]), 4),
+                       (lambda: nat.fork_many([live[0], live[1]], [next_id, live[2]]), 5),
+                       (lambda: nat.fork_many([live[0], live[1]], [next_id, next_id]), 5),
+                       (lambda: nat.free_many([live[0], live[0]]), 1),
+                       (lambda: nat.free_many([live[0], 999_999]), 4),
+                       (lambda: nat.free_many([999_999, 999_999]), 1)]:
+        with pytest.raises(PkvError) as e:
+            call()
+        assert e.value.status == code
+        assert (nat.free_list(), [nat.refcount(b) for b in range(nb)]) == before
+        for s in live:
+            assert nat.seq_len(s) == ora.seq_len(s)
+    assert nat.seq_len(next_id) == -1
+    nat.fork_many([], [])
+    nat.free_many([])
+    nat.free_many(live)
+    assert nat.num_free() == nb

@@ -1,0 +1,191 @@
+"""pkv_copy_blocks (copy-on-write block copy) and a beam-search loop on the GPU, through the
+C ABI, against the oracle.
+
+* the copy is bit-exact over both whole caches against the oracle's copy, for f32/f16/bf16,
+  hd 64/128 and kv-head counts whose block size is below, equal to and a multiple of one
+  work-group's range (the partial-range path and the full-range path), with repeated sources
+  and padding / out-of-pool pairs (skipped);
+* beam search: beams forked at arbitrary lengths and re-selected every step, one token
+  appended per beam per step. The C++ allocator and the oracle's allocator run in lockstep
+  (slots, copy-on-write pairs and tables equal every step); on the device each step is
+  pkv_copy_blocks of the step's pairs, then pkv_decode_append_attn; on the host the oracle's
+  copy, write and attention. Every step's output matches within the tolerance and both
+  caches are bit-exact at the end.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import allocator as OAL
+from oracle import attention as OA
+from oracle import cache_write as CW
+from tests import gpu_helpers as G
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def pkv():
+    import paged_kv_cache_459_amd as m
+    return m
+
+
+def storage(t, dtype):
+    return W.to_storage_numpy(t, dtype).reshape(-1).view(np.uint8)
+
+
+def dev_i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+@pytest.mark.parametrize("dtype,hd,hkv", [
+    ("f32", 64, 1), ("f32", 128, 3), ("f16", 128, 4), ("bf16", 64, 1), ("bf16", 128, 32),
+    ("bf16", 128, 8), ("f16", 64, 5)])
+def test_copy_blocks_matches_oracle(dtype, hd, hkv):
+    m = pkv()
+    rng = np.random.default_rng(61 + hd + hkv)
+    nb = 40
+    print(f"[copy] {dtype} hd{hd} hkv{hkv} nb{nb}", flush=True)
+    size = nb * hkv * hd * 16
+    kc = W.normal_values(rng, (size,), dtype)
+    vc = W.normal_values(rng, (size,), dtype)
+    perm = rng.permutation(nb)
+    src = [int(b) for b in perm[:6]] + [int(perm[0]), int(perm[1]), -1, int(perm[2]), nb + 3]
+    dst = [int(b) for b in perm[6:12]] + [int(perm[12]), int(perm[13]), int(perm[14]), -1,
+                                            int(perm[15])]
+    want_k, want_v = CW.copy_blocks(kc, vc, list(zip(src, dst)), hkv=hkv, hd=hd, bs=16,
+                                    dtype=dtype)
+    ks, vs = m.cache_shapes(nb, hkv, hd, G.TORCH[dtype])
+    k_d = G.to_dev(kc, dtype).view(ks)
+    v_d = G.to_dev(vc, dtype).view(vs)
+    m.pkv_copy_blocks(k_d, v_d, dev_i32(src), dev_i32(dst), num_kv_heads=hkv, head_dim=hd)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(storage(k_d, dtype), want_k.view(np.uint8))
+    np.testing.assert_array_equal(storage(v_d, dtype), want_v.view(np.uint8))
+    # no pairs: nothing changes
+    m.pkv_copy_blocks(k_d, v_d, dev_i32([]), dev_i32([]), num_kv_heads=hkv, head_dim=hd)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(storage(k_d, dtype), want_k.view(np.uint8))
+
+
+def test_copy_many_pairs():
+    """Thousands of pairs in one launch (grid.x = pairs)."""
+    m = pkv()
+    dtype, hd, hkv, nb = "bf16", 128, 8, 6000
+    print(f"[copy] many pairs nb{nb}", flush=True)
+    ks, vs = m.cache_shapes(nb, hkv, hd, torch.bfloat16)
+    k_d = W.device_normal(ks, dtype, 71)
+    v_d = W.device_normal(vs, dtype, 72)
+    kc = W.to_storage_numpy(k_d, dtype).reshape(-1)
+    vc = W.to_storage_numpy(v_d, dtype).reshape(-1)
+    perm = np.random.default_rng(73).permutation(nb)
+    pairs = list(zip(perm[:2900].tolist(), perm[3000:5900].tolist()))
+    want_k, want_v = CW.copy_blocks(kc, vc, pairs, hkv=hkv, hd=hd, bs=16, dtype=dtype)
+    m.pkv_copy_blocks(k_d, v_d, dev_i32(perm[:2900]), dev_i32(perm[3000:5900]),
+                      num_kv_heads=hkv, head_dim=hd)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(storage(k_d, dtype), want_k.view(np.uint8))
+    np.testing.assert_array_equal(storage(v_d, dtype), want_v.view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,hd,kernel", [
+    ("bf16", 8, 2, 128, 0), ("f32", 4, 4, 64, 0), ("f16", 4, 4, 128, 0), ("bf16", 8, 2, 64, 1)])
+def test_beam_search_loop(dtype, hq, hkv, hd, kernel):
+    m = pkv()
+    print(f"[beam] {dtype} {hq}/{hkv} hd{hd} kernel={kernel}", flush=True)
+    groups, beams, steps, nb = 4, 4, 36, 160
+    prompt_lens = (21, 16, 7, 40)
+    rng = np.random.default_rng(81 + hd)
+    order = rng.permutation(nb).astype(np.int32)
+    ref = OAL.BlockAllocator(nb, 16, order)
+    alloc = m.BlockAllocator(nb, 16, order)
+    ks, vs = m.cache_shapes(nb, hkv, hd, G.TORCH[dtype])
+    size = nb * hkv * hd * 16
+    kc = np.full(size, H.NAN_BITS[dtype], H.STORAGE[dtype])
+    vc = np.full(size, H.NAN_BITS[dtype], H.STORAGE[dtype])
+    k_d = G.to_dev(kc, dtype).view(ks)
+    v_d = G.to_dev(vc, dtype).view(vs)
+    scale = 1.0 / math.sqrt(hd)
+    next_id = 0
+    live = []
+    for g in range(groups):  # prompt, written with pkv_write; then the group's beams
+        root = next_id
+        next_id += 1
+        ref.add_seq(root)
+        alloc.add_seq(root)
+        n = prompt_lens[g]
+        want_slots, _ = ref.append([root], [n])
+        slots, cows = alloc.append([root], [n])
+        assert list(slots) == want_slots and len(cows) == 0
+        k = W.normal_values(rng, (n, hkv, hd), dtype)
+        v = W.normal_values(rng, (n, hkv, hd), dtype)
+        kc, vc = CW.write_kv(k, v, kc, vc, np.int32(slots), hkv=hkv, hd=hd, bs=16, dtype=dtype)
+        m.pkv_write(G.to_dev(k, dtype), G.to_dev(v, dtype), k_d, v_d, dev_i32(slots))
+        row = []
+        for _ in range(beams):
+            ref.fork(root, next_id)
+            alloc.fork(root, next_id)
+            row.append(next_id)
+            next_id += 1
+        ref.free_seq(root)
+        alloc.free(root)
+        live.append(row)
+    total_cows = 0
+    prev = m.pkv_set_attn_kernel(kernel)
+    try:
+        for step in range(steps):
+            if step > 0:
+                parents = W.beam_parents(rng, groups, beams)
+                new_live = []
+                for g in range(groups):
+                    row = []
+                    for p in parents[g]:
+                        ref.fork(live[g][p], next_id)
+                        alloc.fork(live[g][p], next_id)
+                        row.append(next_id)
+                        next_id += 1
+                    for s in live[g]:
+                        ref.free_seq(s)
+                        alloc.free(s)
+                    new_live.append(row)
+                live = new_live
+            seqs = [s for row in live for s in row]
+            want_slots, want_cows = ref.append(seqs, [1] * len(seqs))
+            slots, cows = alloc.append(seqs, np.ones(len(seqs), np.int32))
+            assert list(slots) == want_slots
+            assert [tuple(c) for c in cows.tolist()] == want_cows
+            total_cows += len(cows)
+            mb = max(len(ref.blocks[s]) for s in seqs)
+            want_tables, want_lens = ref.tables(seqs, mb)
+            tables, lens = alloc.tables(seqs, mb)
+            np.testing.assert_array_equal(tables, np.int32(want_tables))
+            np.testing.assert_array_equal(lens, np.int32(want_lens))
+            q = W.normal_values(rng, (len(seqs), hq, hd), dtype)
+            k_new = W.normal_values(rng, (len(seqs), hkv, hd), dtype)
+            v_new = W.normal_values(rng, (len(seqs), hkv, hd), dtype)
+            # oracle: copy, write, attend
+            kc, vc = CW.copy_blocks(kc, vc, want_cows, hkv=hkv, hd=hd, bs=16, dtype=dtype)
+            kc, vc = CW.write_kv(k_new, v_new, kc, vc, np.int32(want_slots), hkv=hkv, hd=hd,
+                                 bs=16, dtype=dtype)
+            want = OA.decode_attention(q, kc, vc, tables, lens, scale=scale, hkv=hkv, hd=hd,
+                                       bs=16, dtype=dtype)
+            # device: copy, then the fused write + attention
+            if len(cows):
+                m.pkv_copy_blocks(k_d, v_d, dev_i32(cows[:, 0]), dev_i32(cows[:, 1]),
+                                  num_kv_heads=hkv, head_dim=hd)
+            out = m.pkv_decode_append_attn(G.to_dev(q, dtype), G.to_dev(k_new, dtype),
+                                           G.to_dev(v_new, dtype), k_d, v_d, dev_i32(tables),
+                                           dev_i32(lens), num_kv_heads=hkv, scale=scale,
+                                           max_context_len=int(lens.max()))
+            torch.cuda.synchronize()
+            G.assert_close(G.gpu_f64(out, dtype), want, dtype, f"beam step {step}")
+    finally:
+        m.pkv_set_attn_kernel(prev)
+    assert total_cows > 0
+    np.testing.assert_array_equal(storage(k_d, dtype), kc.view(np.uint8))
+    np.testing.assert_array_equal(storage(v_d, dtype), vc.view(np.uint8))
+    assert alloc.num_free() == ref.num_free()

@@ -52,11 +52,13 @@ SHAPES = {
     "qwen25_7b": Shape("qwen25_7b", 256, 28, 4, 128, "bf16", 3),
     "prefix_shared": Shape("prefix_shared", 128, 32, 32, 128, "bf16", 4),
     "long_context": Shape("long_context", 128, 32, 8, 128, "bf16", 5),
+    "beam_search": Shape("beam_search", 128, 32, 32, 128, "bf16", 6),
 }
 
 TINY_LENGTHS = (1, 15, 16, 37)
 TINY_POOL = 16
 PREFIX_TOKENS = 2000
+BEAMS = 4  # beams per group in the beam-search workload
 
 
 def rng_for(seed):
@@ -81,6 +83,9 @@ def draw_lengths(shape, rng, *, B=None):
         return (PREFIX_TOKENS + rng.integers(16, 512, size=B, endpoint=True)).astype(np.int32)
     if shape.name == "long_context":
         return long_context_lengths(rng, B=B)
+    if shape.name == "beam_search":  # B / BEAMS groups; a group's beams share its length
+        tails = rng.integers(16, 512, size=B // BEAMS, endpoint=True)
+        return np.repeat(PREFIX_TOKENS + tails, BEAMS).astype(np.int32)
     raise KeyError(shape.name)
 
 
