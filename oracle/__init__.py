@@ -24,6 +24,8 @@ paged cache. Modules:
 * ``attention``  -- gather + dense attention; partition partials and their log-sum-exp merge.
 * ``cache_write``-- the scatter of new tokens into their slots; the copy-on-write block copy.
 * ``allocator``  -- FIFO / refcount block allocator (allocate on demand, fork, free, COW).
+* ``utilisation``-- memory accounting: contiguous preallocation versus paged blocks.
+* ``batching``   -- the continuous-batching step loop (retire, admit + prompt write, decode).
 """
 
-from . import allocator, attention, cache_write, layout  # noqa: F401
+from . import allocator, attention, batching, cache_write, layout, utilisation  # noqa: F401

@@ -149,3 +149,10 @@ class BlockAllocator:
 
     def free_list(self):
         return list(self.free)
+
+    def usage(self):
+        """Memory accounting of the live sequences (``utilisation.paged_usage`` over them)."""
+        from .utilisation import paged_usage
+        seqs = list(self.blocks)
+        return paged_usage([self.blocks[s] for s in seqs], [self.length[s] for s in seqs],
+                           self.bs)

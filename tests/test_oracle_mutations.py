@@ -2,7 +2,8 @@
 
 Each case patches one oracle function with a wrong variant (a dropped scale, a wrong
 kv-head mapping, an off-by-one gather, a transposed tile, an unweighted merge, a LIFO free
-list, a missing copy-on-write, a skipped, reversed or half block copy) and runs an existing pin, which must then fail.
+list, a missing copy-on-write, a skipped, reversed or half block copy, shared blocks counted per owner, a reservation
+counted as used, admission without headroom or out of arrival order) and runs an existing pin, which must then fail.
 """
 
 import numpy as np
@@ -10,11 +11,15 @@ import pytest
 
 from oracle import allocator as AL
 from oracle import attention as A
+from oracle import batching as OB
 from oracle import cache_write as CW
 from oracle import layout as L
+from oracle import utilisation as U
 from tests import test_oracle_allocator as TAL
 from tests import test_oracle_attention as TA
+from tests import test_oracle_batching as TOB
 from tests import test_oracle_beam as TB
+from tests import test_oracle_utilisation as TU
 
 
 def _fails(fn, *args):
@@ -118,3 +123,35 @@ def test_copy_of_one_cache_only_is_caught(monkeypatch):
         return k2, np.array(vc, copy=True)
     monkeypatch.setattr(CW, "copy_blocks", k_only)
     _fails(TB.test_beam_loop_keeps_every_beams_history, "bf16")
+
+
+def test_shared_block_counted_per_owner_is_caught(monkeypatch):
+    def per_owner(tables, lengths, bs):
+        slots = sum(int(n) for n in lengths)
+        blocks = sum(-(-int(n) // bs) for n in lengths)
+        return dict(sequences=len(lengths), logical_tokens=slots, blocks_in_use=blocks,
+                    slots_filled=slots, utilisation=slots / (blocks * bs) if blocks else 0.0)
+    monkeypatch.setattr(U, "paged_usage", per_owner)
+    _fails(TU.test_shared_blocks_counted_once)
+
+
+def test_whole_reservation_counted_as_used_is_caught(monkeypatch):
+    monkeypatch.setattr(U, "contiguous_usage",
+                        lambda lengths, max_len: (len(lengths) * max_len,) * 2 + (1.0,))
+    _fails(TU.test_pages_worked_examples)
+
+
+def test_admission_without_headroom_is_caught(monkeypatch):
+    monkeypatch.setattr(OB.BatchingLoop, "_future_blocks", lambda self: 0)
+    with pytest.raises((AssertionError, AL.AllocError)):
+        TOB.test_loop_follows_its_rules(12, 4)
+
+
+def test_admission_out_of_order_is_caught(monkeypatch):
+    orig = OB.BatchingLoop.schedule
+
+    def lifo(self):
+        self.queue.sort(key=lambda r: (r.arrival > self.step_no, -r.rid))  # newest first
+        return orig(self)
+    monkeypatch.setattr(OB.BatchingLoop, "schedule", lifo)
+    _fails(TOB.test_loop_follows_its_rules, 40, 8)

@@ -174,6 +174,16 @@ def beam_parents(rng, groups, beams):
     return np.sort(rng.integers(0, beams, size=(groups, beams)), axis=1)
 
 
+def request_stream(rng, n, *, prompt=(1, 60), new=(1, 30), rate=0.5):
+    """A seeded stream of n requests for the continuous-batching loop: (id, prompt length,
+    max new tokens, arrival step). Lengths uniform in the inclusive ranges; arrivals a
+    Poisson process of ``rate`` requests per step (exponential gaps, rounded down)."""
+    p = rng.integers(prompt[0], prompt[1], size=n, endpoint=True)
+    m = rng.integers(new[0], new[1], size=n, endpoint=True)
+    arrival = np.floor(np.cumsum(rng.exponential(1.0 / rate, size=n))).astype(np.int64)
+    return [(i, int(p[i]), int(m[i]), int(arrival[i])) for i in range(n)]
+
+
 def blocks_in_use(tables, lengths, bs=BLOCK_SIZE):
     used = set()
     for row, n in zip(tables, lengths):
