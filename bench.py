@@ -40,7 +40,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "paged decode attn: KV-read GB/s and % of HBM peak; decode tokens/s per layer"
-WORKLOADS = ("llama2_7b", "qwen25_7b", "prefix_shared", "long_context", "beam_search")
+WORKLOADS = ("llama2_7b", "qwen25_7b", "prefix_shared", "long_context", "beam_search",
+             "continuous_batching")
 DESC = {
     "llama2_7b": "Llama-2-7B-shaped single layer decode: MHA 32 x 128, f16, batch 64, "
                  "context U[128,2048], blocks scattered in a pool of 1.1x need",
@@ -54,6 +55,12 @@ DESC = {
                    "beams share its tail U[16,512]; every step re-selects each group's 4 beams "
                    "(seeded parents, forks at unaligned lengths), appends one token per beam "
                    "with copy-on-write of shared partly filled blocks, MHA 32 x 128, bf16",
+    "continuous_batching": "continuous batching: Llama-2-7B-shaped layer (MHA 32 x 128, f16), at "
+                           "most 64 running, prompts U[64,1024], new tokens U[16,256], a "
+                           "backlog of 64 then 0.5 arrivals per step; a pool of 4096 blocks "
+                           "(half of 64 contiguous 2048-token reservations); each step retires, "
+                           "admits (prompt K/V written), then decodes every running request; "
+                           "300 untimed steps reach the steady state before the warm-up",
 }
 
 
@@ -311,14 +318,23 @@ def attend(wl, pkv, s, events):
 def cpu_baseline(wl, torch, W, seconds):
     """The oracle (float64 NumPy, one thread) on the last step's sequences, in a seeded order,
     pass after pass until about ``seconds`` of oracle time have been spent."""
+    return oracle_baseline(torch, W, seconds, wl.host_views[wl.last_set][0],
+                           wl.host_views[wl.last_set][2], wl.k_cache, wl.v_cache, wl.q,
+                           wl.Hkv, wl.hd, wl.shape.dtype, wl.scale)
+
+
+def oracle_baseline(torch, W, seconds, lens, tables, k_cache, v_cache, q_all, Hkv, hd, dtype,
+                    scale):
     from threadpoolctl import threadpool_limits
 
     from oracle import attention as OA
+    B = len(lens)
+    eb = 4 if dtype == "f32" else 2
     rng = np.random.default_rng(12345)
-    order = rng.permutation(wl.B)
+    order = rng.permutation(B)
     spent, done, kv, passes = 0.0, 0, 0, 0
-    lens = wl.host_views[wl.last_set][0].copy()
-    tables = wl.host_views[wl.last_set][2].copy()
+    lens = np.array(lens, copy=True)
+    tables = np.array(tables, copy=True)
     tables = np.where(tables >= 0, tables & ~0x40000000, tables)  # drop the shared-block mark
     inputs = {}
     with threadpool_limits(limits=1):
@@ -329,29 +345,158 @@ def cpu_baseline(wl, torch, W, seconds):
                     nbk = -(-n // 16)
                     ids = torch.from_numpy(tables[i, :nbk].astype(np.int64)).cuda()
                     inputs[i] = (n, nbk,
-                                 W.to_storage_numpy(wl.k_cache.index_select(0, ids),
-                                                    wl.shape.dtype).reshape(-1),
-                                 W.to_storage_numpy(wl.v_cache.index_select(0, ids),
-                                                    wl.shape.dtype).reshape(-1),
-                                 W.to_storage_numpy(wl.q[i:i + 1], wl.shape.dtype))
+                                 W.to_storage_numpy(k_cache.index_select(0, ids),
+                                                    dtype).reshape(-1),
+                                 W.to_storage_numpy(v_cache.index_select(0, ids),
+                                                    dtype).reshape(-1),
+                                 W.to_storage_numpy(q_all[i:i + 1], dtype))
                 n, nbk, kc, vc, q = inputs[i]
                 t0 = time.perf_counter()
                 OA.decode_attention(q, kc, vc, np.arange(nbk, dtype=np.int32)[None],
-                                    np.int32([n]), scale=wl.scale, hkv=wl.Hkv, hd=wl.hd, bs=16,
-                                    dtype=wl.shape.dtype)
+                                    np.int32([n]), scale=scale, hkv=Hkv, hd=hd, bs=16, dtype=dtype)
                 spent += time.perf_counter() - t0
                 done += 1
-                kv += n * 2 * wl.Hkv * wl.hd * wl.eb
+                kv += n * 2 * Hkv * hd * eb
                 if spent >= seconds:
                     break
             passes += 1
             if passes > 1000:
                 break
     return {"value": round(kv / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} sequence-attentions over {passes} pass(es) of the step's {wl.B} "
+            "sample": f"{done} sequence-attentions over {passes} pass(es) of the step's {B} "
                       f"sequences in a seeded order, {kv / 1e6:.1f} MB of K/V, {spent:.1f} s of "
                       f"oracle time on one thread (host copies of the blocks not timed)",
             "tokens_per_s_per_layer": round(done / spent, 3)}
+
+
+BATCHING = dict(max_batch=64, max_ctx=2048, pool_blocks=4096, prompt=(64, 1024),
+                new=(16, 256), rate=0.5, requests=4000, seed=7, settle_steps=300)
+
+
+def batching_main(args, torch, pkv, W):
+    """The continuous-batching workload: ContinuousBatch steps (retire, admit + prompt write,
+    decode), timed over K steps after W warm-up steps."""
+    from paged_kv_cache_459_amd.batching import ContinuousBatch
+    cfg = BATCHING
+    dtype, Hq, Hkv, hd = "f16", 32, 32, 128
+    dt = W.torch_dtype(dtype)
+    rng = np.random.default_rng(cfg["seed"])
+    reqs = W.request_stream(rng, cfg["requests"], prompt=cfg["prompt"], new=cfg["new"],
+                            rate=cfg["rate"])
+    nb = cfg["pool_blocks"]
+    k_cache, v_cache = pkv.alloc_caches(nb, Hkv, hd, dt)
+    k_cache.view(-1).copy_(W.device_normal((k_cache.numel(),), dtype, 7101))
+    v_cache.view(-1).copy_(W.device_normal((v_cache.numel(),), dtype, 7102))
+    loop = ContinuousBatch(k_cache, v_cache, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=hd,
+                           max_batch=cfg["max_batch"], max_context_len=cfg["max_ctx"],
+                           free_order=rng.permutation(nb).astype(np.int32))
+    for i, (rid, p, m, a) in enumerate(reqs):  # the first max_batch requests are a backlog
+        loop.submit(rid, p, m, 0 if i < cfg["max_batch"] else a + 1)
+    B = cfg["max_batch"]
+    q = W.device_normal((B, Hq, hd), dtype, 7103)
+    k_new = W.device_normal((B, Hkv, hd), dtype, 7104)
+    v_new = W.device_normal((B, Hkv, hd), dtype, 7105)
+    max_prompt = cfg["prompt"][1] * cfg["max_batch"]
+    k_prompt = W.device_normal((max_prompt, Hkv, hd), dtype, 7106)
+    v_prompt = W.device_normal((max_prompt, Hkv, hd), dtype, 7107)
+    out = torch.empty_like(q)
+    scale = 1.0 / math.sqrt(hd)
+    eb = 2
+
+    def step(ev=None, stats=None):
+        retired, admitted, T = loop.schedule()
+        if ev is not None:
+            ev[0].record()
+        if T:
+            loop.write_prompts(k_prompt[:T], v_prompt[:T])
+        n = len(loop.run_id)
+        if ev is not None:
+            ev[1].record()
+        loop.decode(q[:n], k_new[:n], v_new[:n], scale, out=out[:n],
+                    events=None if ev is None else ev[2:])
+        if stats is not None:
+            lens = loop.last_lens.copy()
+            u = loop.usage()
+            stats.append(dict(B=n, retired=len(retired), admitted=len(admitted), T=T,
+                              kv=int(lens.astype(np.int64).sum()) * 2 * Hkv * hd * eb,
+                              lens=lens, tables=loop.last_tables.copy(), usage=u))
+
+    for _ in range(cfg["settle_steps"] + args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    stats = []
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k], stats)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    write_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    part_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    merge_ms = [e[3].elapsed_time(e[4]) for e in evs]
+    kv = [st["kv"] for st in stats]  # no sharing: unique == logical
+    qo = [2 * st["B"] * Hq * hd * eb + 4 * st["B"] * Hkv * hd * eb for st in stats]
+    algo = [a + b for a, b in zip(kv, qo)]
+    ms_per_step = wall / args.steps * 1e3
+    tokens = sum(st["B"] for st in stats)
+    util_paged = [st["usage"]["utilisation"] for st in stats]
+    util_contig = [st["usage"]["logical_tokens"] / (st["usage"]["sequences"] * cfg["max_ctx"])
+                   for st in stats]
+    written = sum(st["T"] for st in stats) * 2 * Hkv * hd * eb
+    achieved = sum(algo) / (sum(part_ms) / 1e3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(sum(kv) / wall / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded request stream, seeded N(0,1) values and block placement)",
+        "config": {"workload": "continuous_batching", "description": DESC["continuous_batching"],
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": hd, "block_size": 16,
+                   "pool_blocks": nb, "max_batch": cfg["max_batch"],
+                   "max_context_len": cfg["max_ctx"], "stream_workers": loop.W,
+                   "attn_kernel": ["", "vector", "matrix-core"][loop.kernel]},
+        "tokens_per_s_per_layer": round(tokens / wall, 1),
+        "attn_stream_ms": round(float(np.mean(part_ms)), 4),
+        "attn_merge_ms": round(float(np.mean(merge_ms)), 4),
+        "batching": {
+            "mean_running": round(tokens / args.steps, 2),
+            "admitted_per_step": round(sum(st["admitted"] for st in stats) / args.steps, 3),
+            "retired_per_step": round(sum(st["retired"] for st in stats) / args.steps, 3),
+            "prompt_tokens_written_per_step": round(sum(st["T"] for st in stats) / args.steps, 1),
+            "prompt_write_ms_per_step": round(float(np.mean(write_ms)), 4),
+            "prompt_write_gbs": (round(written / (sum(write_ms) / 1e3) / 1e9, 2)
+                                 if written else None),
+            "mean_context_len": round(float(np.mean(np.concatenate([st["lens"] for st in stats]))),
+                                      1),
+            "kv_utilisation_paged": round(float(np.mean(util_paged)), 4),
+            "kv_utilisation_contiguous_2048": round(float(np.mean(util_contig)), 4),
+            "requests_the_pool_holds_contiguous": nb * 16 // cfg["max_ctx"],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("continuous_batching", kernel_source_digest()),
+            "kernel": f"attention stream pass ({['', 'vector', 'matrix-core'][loop.kernel]} "
+                      f"kernel)",
+            "algorithmic_bytes_per_launch": int(np.mean(algo)),
+        },
+    }
+    if not args.no_cpu_baseline:
+        last = stats[-1]
+        res["cpu_baseline"] = oracle_baseline(torch, W, args.cpu_seconds, last["lens"],
+                                              last["tables"], k_cache, v_cache, q, Hkv, hd,
+                                              dtype, scale)
+    print(json.dumps(res), flush=True)
 
 
 def main():
@@ -368,6 +513,9 @@ def main():
 
     torch.cuda.set_device(0)
     pkv.pkv_set_attn_kernel(args.kernel)
+    if args.workload == "continuous_batching":
+        batching_main(args, torch, pkv, W)
+        return
     wl = Workload(args.workload, args.warmup + args.steps, torch, pkv, W)
     torch.cuda.synchronize()
 

@@ -347,6 +347,13 @@ int32_t pkv_alloc_num_free(const pkv_allocator* a);            /* free blocks   
 int32_t pkv_alloc_refcount(const pkv_allocator* a, int32_t block); /* -1 if out of range      */
 /* Length of a sequence in tokens, or -1 if unknown. */
 int64_t pkv_alloc_seq_len(const pkv_allocator* a, int64_t seq);
+/* Memory accounting ([P1] §一 and §二 "內部碎片": a contiguous reservation wastes what a      */
+/* request does not use; with blocks only a sequence's last block can be partly empty).       */
+/* out (host, 4 entries) receives: live sequences; logical tokens (sum of their lengths);     */
+/* blocks in use (NB - free blocks); filled slots (over the blocks in use, the most tokens    */
+/* any owner keeps in the block, so a shared block counts once). Utilisation of the blocks in */
+/* use = filled / (blocks in use * bs). Errors: PKV_ERR_INVALID_ARG (null argument).          */
+pkv_status pkv_alloc_usage(const pkv_allocator* a, int64_t* out);
 /* Copies up to cap entries of the free list, front first, into out; returns the list length. */
 int32_t pkv_alloc_free_list(const pkv_allocator* a, int32_t* out, int32_t cap);
 

@@ -81,6 +81,7 @@ SIGNATURES = {
     "pkv_alloc_fork": (c_i32, [c_vp, c_i64, c_i64]),
     "pkv_alloc_free": (c_i32, [c_vp, c_i64]),
     "pkv_alloc_fork_many": (c_i32, [c_vp, c_i32, c_vp, c_vp]),
+    "pkv_alloc_usage": (c_i32, [c_vp, c_vp]),
     "pkv_alloc_free_many": (c_i32, [c_vp, c_i32, c_vp]),
     "pkv_alloc_tables": (c_i32, [c_vp, c_i32, c_vp, c_i32, c_vp, c_vp]),
     "pkv_alloc_tables_marked": (c_i32, [c_vp, c_i32, c_vp, c_i32, c_vp, c_vp]),

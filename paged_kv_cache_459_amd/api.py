@@ -375,6 +375,15 @@ class BlockAllocator:
     def seq_len(self, seq):
         return int(lib.pkv_alloc_seq_len(self._h, int(seq)))
 
+    def usage(self):
+        """dict(sequences, logical_tokens, blocks_in_use, slots_filled, utilisation)."""
+        out = np.zeros(4, np.int64)
+        check(lib.pkv_alloc_usage(self._h, out.ctypes.data), "pkv_alloc_usage")
+        seqs, logical, blocks, filled = (int(x) for x in out)
+        return dict(sequences=seqs, logical_tokens=logical, blocks_in_use=blocks,
+                    slots_filled=filled,
+                    utilisation=filled / (blocks * self.block_size) if blocks else 0.0)
+
     def free_list(self):
         n = int(lib.pkv_alloc_free_list(self._h, None, 0))
         out = np.empty(max(n, 1), np.int32)

@@ -1,0 +1,207 @@
+"""Continuous batching over the paged cache: the decode step loop.
+
+[P1] §四 "連續批次": requests leave the batch as soon as they are done and new ones join at any
+step; the paged cache allows it because blocks are taken on demand and released per request
+([P1] §三 步驟一..四). Admission rule (ours; the pages give none, and leave preemption to
+vLLM's tuning, so the rule never needs it):
+
+* waiting requests are served first-come first-served, never reordered;
+* a step is: (1) retire the running requests that produced their max new tokens (their
+  blocks go back to the pool); (2) admit queue heads that have arrived while fewer than
+  ``max_batch`` run and the free blocks cover the head's final size (prompt + max new tokens)
+  on top of what the running requests may still take; an admitted request's prompt slots are
+  allocated and its prompt K/V written (``pkv_write``); (3) decode: every running request, in
+  admission order, appends one token, whose K/V are stored and attended to in the fused
+  decode step (``pkv_decode_append_stream`` + ``pkv_decode_append_merge``).
+
+Host bookkeeping only: the allocator is the library's C++ allocator and every device step
+runs in the library's kernels. Host buffers for tables and slots are pinned and
+double-buffered, so the host may prepare the next step while the current one runs.
+"""
+
+import math
+
+import numpy as np
+import torch
+
+from . import api
+from .api import BLOCK_SIZE, BlockAllocator
+
+
+def _blocks(n):
+    return -(-np.asarray(n, dtype=np.int64) // BLOCK_SIZE)
+
+
+class ContinuousBatch:
+    def __init__(self, k_cache, v_cache, *, num_q_heads, num_kv_heads, head_dim, max_batch,
+                 max_context_len, free_order=None):
+        self.k_cache, self.v_cache = k_cache, v_cache
+        self.Hq, self.Hkv, self.hd = num_q_heads, num_kv_heads, head_dim
+        self.dtype = k_cache.dtype
+        self.device = k_cache.device
+        self.nb = api._num_blocks(k_cache, num_kv_heads, head_dim)
+        self.alloc = BlockAllocator(self.nb, BLOCK_SIZE, free_order)
+        self.max_batch = int(max_batch)
+        self.max_ctx = int(max_context_len)
+        self.max_blocks = int(_blocks(self.max_ctx))
+        # waiting queue (arrival order) and running requests (admission order)
+        self.queue = []
+        self.run_id = np.zeros(0, np.int64)
+        self.run_final = np.zeros(0, np.int64)  # prompt + max new tokens
+        self.run_new = np.zeros(0, np.int64)    # max new tokens
+        self.run_done = np.zeros(0, np.int64)   # tokens produced so far
+        self.step_no = 0
+        self.prompt_slots = None
+        # two sets of step buffers [lens | tables | prompt slots], pinned on the host and on
+        # the device; a step fills one set while the previous step's copies may still read
+        # the other
+        self._slot0 = self.max_batch + self.max_batch * self.max_blocks
+        n_int = self._slot0 + self.max_batch * self.max_ctx
+        self._pin = [torch.empty(n_int, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+        self._dev = [torch.empty(n_int, dtype=torch.int32, device=self.device) for _ in range(2)]
+        self._free = [torch.cuda.Event() for _ in range(2)]
+        self._set = 0
+        self._set_ready = False
+        self.kernel = api.pkv_decode_kernel(num_q_heads, num_kv_heads, self.dtype)
+        self.W = api.pkv_decode_num_workers(num_q_heads, num_kv_heads, head_dim, self.dtype)
+        ws = api.pkv_decode_stream_workspace_bytes(self.max_batch, num_q_heads, num_kv_heads,
+                                                   head_dim, self.dtype, self.W)
+        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=self.device)
+
+    # -- requests --------------------------------------------------------------------------
+    def submit(self, rid, prompt_len, max_new_tokens, arrival_step=0):
+        if prompt_len < 1 or max_new_tokens < 1:
+            raise ValueError("a request needs a prompt and at least one new token")
+        if prompt_len + max_new_tokens > self.max_ctx:
+            raise ValueError("request longer than max_context_len")
+        if _blocks(prompt_len + max_new_tokens) > self.nb:
+            raise ValueError("request larger than the whole pool")
+        self.queue.append((int(rid), int(prompt_len), int(max_new_tokens), int(arrival_step)))
+
+    def idle(self):
+        return not self.queue and len(self.run_id) == 0
+
+    def running(self):
+        return self.run_id.copy()
+
+    # -- phases 1 and 2 --------------------------------------------------------------------
+    def _take_set(self):
+        """The step's buffer set, once its previous copies have run."""
+        if not self._set_ready:
+            self._free[self._set].synchronize()
+            self._set_ready = True
+        return self._set
+
+    def _release_set(self):
+        self._free[self._set].record()
+        self._set ^= 1
+        self._set_ready = False
+
+    def schedule(self):
+        """Retire finished requests, admit arrived ones. Returns (retired ids, admitted
+        [(id, prompt_len)], number of prompt tokens to write)."""
+        finished = self.run_done >= self.run_new
+        retired = self.run_id[finished]
+        if len(retired):
+            self.alloc.free_many(retired)
+            keep = ~finished
+            self.run_id, self.run_final = self.run_id[keep], self.run_final[keep]
+            self.run_new, self.run_done = self.run_new[keep], self.run_done[keep]
+        # what the running requests may still take: final blocks minus the blocks they hold
+        held = _blocks(self.run_final - self.run_new + self.run_done)
+        reserve = int((_blocks(self.run_final) - held).sum())
+        free = self.alloc.num_free()
+        admitted = []
+        while self.queue and self.queue[0][3] <= self.step_no and \
+                len(self.run_id) + len(admitted) < self.max_batch:
+            rid, p, m, _ = self.queue[0]
+            need = int(_blocks(p + m))
+            if free - reserve < need:
+                break
+            self.queue.pop(0)
+            admitted.append((rid, p, m))
+            reserve += need - int(_blocks(p))
+            free -= int(_blocks(p))
+        prompt_tokens = sum(p for _, p, _ in admitted)
+        if admitted:
+            ids = np.array([a[0] for a in admitted], np.int64)
+            for rid in ids:
+                self.alloc.add_seq(int(rid))
+            s = self._take_set()
+            pin = self._pin[s].numpy()[self._slot0:self._slot0 + prompt_tokens]
+            self.alloc.append(ids, np.array([a[1] for a in admitted], np.int32), slots_out=pin)
+            self.prompt_slots = self._dev[s][self._slot0:self._slot0 + prompt_tokens]
+            self.prompt_slots.copy_(self._pin[s][self._slot0:self._slot0 + prompt_tokens],
+                                    non_blocking=True)
+            self.run_id = np.concatenate([self.run_id, ids])
+            self.run_final = np.concatenate([self.run_final,
+                                             [a[1] + a[2] for a in admitted]]).astype(np.int64)
+            self.run_new = np.concatenate([self.run_new, [a[2] for a in admitted]]).astype(np.int64)
+            self.run_done = np.concatenate([self.run_done, np.zeros(len(admitted), np.int64)])
+        else:
+            self.prompt_slots = None
+        return retired, [(a[0], a[1]) for a in admitted], prompt_tokens
+
+    def write_prompts(self, k, v):
+        """The admitted prompts' K/V, [T, Hkv, hd] in admission order (T from schedule())."""
+        if self.prompt_slots is None:
+            if k.shape[0]:
+                raise ValueError("no prompt was admitted this step")
+            return
+        api.pkv_write(k, v, self.k_cache, self.v_cache, self.prompt_slots)
+
+    # -- phase 3 ---------------------------------------------------------------------------
+    def decode(self, q, k_new, v_new, scale, out=None, events=None):
+        """One decode step of every running request (rows of q/k_new/v_new in admission
+        order). Returns out [B, Hq, hd]. ``events``: optional three torch.cuda.Events recorded
+        before the stream pass, between the passes and after the merge pass."""
+        B = len(self.run_id)
+        self.step_no += 1
+        if B == 0:
+            if self._set_ready:
+                self._release_set()
+            return q.new_empty((0, self.Hq, self.hd))
+        s = self._take_set()
+        flat = self._pin[s].numpy()
+        lens_h = flat[:B]
+        tables_h = flat[self.max_batch:self.max_batch + B * self.max_blocks].reshape(
+            B, self.max_blocks)
+        self.alloc.append(self.run_id, np.ones(B, np.int32), want_slots=False)
+        self.alloc.tables(self.run_id, self.max_blocks, tables_out=tables_h, lens_out=lens_h)
+        self.run_done += 1
+        dev = self._dev[s]
+        nt = self.max_batch + B * self.max_blocks
+        dev[:B].copy_(self._pin[s][:B], non_blocking=True)
+        dev[self.max_batch:nt].copy_(self._pin[s][self.max_batch:nt], non_blocking=True)
+        self._release_set()
+        lens_d = dev[:B]
+        tables_d = dev[self.max_batch:self.max_batch + B * self.max_blocks].view(
+            B, self.max_blocks)
+        if out is None:
+            out = torch.empty_like(q)
+        if events is not None:
+            events[0].record()
+        api.pkv_decode_append_stream(q, k_new, v_new, self.k_cache, self.v_cache, tables_d,
+                                     lens_d, num_kv_heads=self.Hkv, scale=scale,
+                                     max_context_len=self.max_ctx, num_workers=self.W,
+                                     workspace=self.workspace, out=out)
+        if events is not None:
+            events[1].record()
+        api.pkv_decode_append_merge(out, k_new, v_new, self.k_cache, self.v_cache, tables_d,
+                                    lens_d, self.workspace, num_kv_heads=self.Hkv,
+                                    max_context_len=self.max_ctx, num_workers=self.W)
+        if events is not None:
+            events[2].record()
+        self.last_tables = tables_h
+        self.last_lens = lens_h
+        return out
+
+    def usage(self):
+        return self.alloc.usage()
+
+    def close(self):
+        self.alloc.close()
+
+
+def default_scale(head_dim):
+    return 1.0 / math.sqrt(head_dim)

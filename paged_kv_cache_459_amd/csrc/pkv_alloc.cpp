@@ -10,6 +10,7 @@
 // order; per-block reference counts; copy-on-write of a shared, partly filled last block;
 // blocks released in logical order; every call all-or-nothing.
 
+#include <algorithm>
 #include <cstdint>
 #include <deque>
 #include <new>
@@ -298,6 +299,30 @@ int64_t pkv_alloc_seq_len(const pkv_allocator* a, int64_t seq) {
   if (!a) return -1;
   auto it = a->seqs.find(seq);
   return it == a->seqs.end() ? -1 : it->second.len;
+}
+
+pkv_status pkv_alloc_usage(const pkv_allocator* a, int64_t* out) {
+  if (!a || !out) return PKV_ERR_INVALID_ARG;
+  // filled slots of a block: the most tokens any owner keeps in it (owners of a shared block
+  // hold the same tokens there)
+  std::vector<int32_t> fill(static_cast<size_t>(a->nb), 0);
+  int64_t logical = 0;
+  for (const auto& kv : a->seqs) {
+    const Seq& s = kv.second;
+    logical += s.len;
+    for (size_t j = 0; j < s.blocks.size(); ++j) {
+      const int64_t f = std::min<int64_t>(a->bs, s.len - static_cast<int64_t>(j) * a->bs);
+      int32_t& cell = fill[static_cast<size_t>(s.blocks[j])];
+      if (f > cell) cell = static_cast<int32_t>(f);
+    }
+  }
+  int64_t filled = 0;
+  for (int32_t f : fill) filled += f;
+  out[0] = static_cast<int64_t>(a->seqs.size());
+  out[1] = logical;
+  out[2] = static_cast<int64_t>(a->nb) - static_cast<int64_t>(a->free_list.size());
+  out[3] = filled;
+  return PKV_OK;
 }
 
 int32_t pkv_alloc_free_list(const pkv_allocator* a, int32_t* out, int32_t cap) {

@@ -22,7 +22,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for must in ("pkv_write", "pkv_decode_attn", "pkv_alloc_create", "pkv_alloc_append",
                  "pkv_alloc_fork", "pkv_alloc_free", "pkv_alloc_tables", "pkv_decode_stream",
-                 "pkv_decode_merge", "pkv_copy_blocks"):
+                 "pkv_decode_merge", "pkv_copy_blocks", "pkv_alloc_usage"):
         assert must in names
 
 

@@ -1,5 +1,5 @@
 """The C++ allocator against the oracle allocator: identical tables, lengths, slots,
-copy-on-write pairs, refcounts and free lists after every operation of seeded random
+copy-on-write pairs, refcounts, free lists and memory accounting after every operation of seeded random
 operation sequences; the pages' worked examples; error codes and atomicity."""
 
 import json
@@ -19,6 +19,7 @@ CODE = {"INVALID_ARG": 1, "OUT_OF_BLOCKS": 3, "UNKNOWN_SEQ": 4, "SEQ_EXISTS": 5}
 
 def same_state(nat, ora, seqs):
     assert nat.num_free() == ora.num_free()
+    assert nat.usage() == ora.usage()
     assert nat.free_list() == ora.free_list()
     for b in range(ora.num_blocks):
         assert nat.refcount(b) == ora.refcount(b)

@@ -1,0 +1,87 @@
+"""The continuous-batching step loop on the GPU (ContinuousBatch: the C++ allocator, pkv_write
+for admitted prompts, the fused decode step) against the oracle's loop, in lockstep on one
+seeded request stream.
+
+Every step: the same requests retire and are admitted (the admission rule is implemented
+separately on both sides), the prompt slots, block tables and lengths are equal, the memory
+accounting is equal, and every decode output is within the tolerance of the oracle's. At the
+end both caches are bit-exact and every block is back in the pool.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import batching as OB
+from tests import gpu_helpers as G
+from tests import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dtype,hq,hkv,hd,nb,max_batch,kernel", [
+    ("bf16", 8, 2, 128, 48, 8, 0), ("f32", 4, 4, 64, 24, 6, 0), ("f16", 4, 4, 128, 200, 16, 0),
+    ("bf16", 8, 2, 64, 48, 8, 1)])
+def test_loop_matches_oracle(dtype, hq, hkv, hd, nb, max_batch, kernel):
+    import paged_kv_cache_459_amd as m
+    from paged_kv_cache_459_amd.batching import ContinuousBatch
+    print(f"[batching] {dtype} {hq}/{hkv} hd{hd} nb{nb} max_batch{max_batch} kernel={kernel}",
+          flush=True)
+    rng = np.random.default_rng(500 + nb + hd)
+    reqs = W.request_stream(rng, 40, prompt=(1, 70), new=(1, 40), rate=0.8)
+    order = rng.permutation(nb)
+    scale = 0.09
+    ref = OB.BatchingLoop(nb, 16, hkv, hd, dtype, max_batch=max_batch, free_order=order,
+                          storage_dtype=H.STORAGE[dtype], nan_fill=H.NAN_BITS[dtype])
+    k_cache, v_cache = m.alloc_caches(nb, hkv, hd, G.TORCH[dtype])
+    k_cache.view(-1).copy_(G.to_dev(ref.k_cache, dtype))
+    v_cache.view(-1).copy_(G.to_dev(ref.v_cache, dtype))
+    loop = ContinuousBatch(k_cache, v_cache, num_q_heads=hq, num_kv_heads=hkv, head_dim=hd,
+                           max_batch=max_batch, max_context_len=110, free_order=order)
+    for r in reqs:
+        ref.submit(*r)
+        loop.submit(*r)
+    prev = m.pkv_set_attn_kernel(kernel)
+    steps = 0
+    try:
+        while not ref.idle():
+            r_ret, r_adm, r_slots = ref.schedule()
+            retired, admitted, T = loop.schedule()
+            assert list(retired) == r_ret
+            assert admitted == [(a.rid, a.prompt_len) for a in r_adm]
+            assert T == len(r_slots)
+            if T:
+                np.testing.assert_array_equal(loop.prompt_slots.cpu().numpy(), r_slots)
+                k = W.normal_values(rng, (T, hkv, hd), dtype)
+                v = W.normal_values(rng, (T, hkv, hd), dtype)
+                ref.write_prompts(k, v, r_slots)
+                loop.write_prompts(G.to_dev(k, dtype), G.to_dev(v, dtype))
+            B = len(ref.running)
+            assert list(loop.running()) == [r.rid for r in ref.running]
+            q = W.normal_values(rng, (B, hq, hd), dtype)
+            kn = W.normal_values(rng, (B, hkv, hd), dtype)
+            vn = W.normal_values(rng, (B, hkv, hd), dtype)
+            want, _, tables, lens = ref.decode(q, kn, vn, scale)
+            out = loop.decode(G.to_dev(q, dtype), G.to_dev(kn, dtype), G.to_dev(vn, dtype),
+                              scale)
+            torch.cuda.synchronize()
+            if B:
+                np.testing.assert_array_equal(loop.last_lens, lens)
+                np.testing.assert_array_equal(loop.last_tables[:, :tables.shape[1]], tables)
+                assert np.all(loop.last_tables[:, tables.shape[1]:] == -1)
+                G.assert_close(G.gpu_f64(out, dtype), want, dtype, f"step {steps}")
+            assert loop.usage() == ref.alloc.usage()
+            steps += 1
+            assert steps < 1000
+    finally:
+        m.pkv_set_attn_kernel(prev)
+    assert loop.idle()
+    kc = W.to_storage_numpy(k_cache, dtype).reshape(-1)
+    vc = W.to_storage_numpy(v_cache, dtype).reshape(-1)
+    np.testing.assert_array_equal(kc.view(np.uint8), ref.k_cache.view(np.uint8))
+    np.testing.assert_array_equal(vc.view(np.uint8), ref.v_cache.view(np.uint8))
+    # the last requests retire at the next schedule
+    loop.schedule()
+    ref.schedule()
+    assert loop.alloc.num_free() == nb == ref.alloc.num_free()
