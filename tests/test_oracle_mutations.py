@@ -3,7 +3,8 @@
 Each case patches one oracle function with a wrong variant (a dropped scale, a wrong
 kv-head mapping, an off-by-one gather, a transposed tile, an unweighted merge, a LIFO free
 list, a missing copy-on-write, a skipped, reversed or half block copy, shared blocks counted per owner, a reservation
-counted as used, admission without headroom or out of arrival order) and runs an existing pin, which must then fail.
+counted as used, admission without headroom or out of arrival order, a prefix block matched without its
+parent) and runs an existing pin, which must then fail.
 """
 
 import numpy as np
@@ -19,6 +20,7 @@ from tests import test_oracle_allocator as TAL
 from tests import test_oracle_attention as TA
 from tests import test_oracle_batching as TOB
 from tests import test_oracle_beam as TB
+from tests import test_oracle_prefix_cache as TPC
 from tests import test_oracle_utilisation as TU
 
 
@@ -155,3 +157,32 @@ def test_admission_out_of_order_is_caught(monkeypatch):
         return orig(self)
     monkeypatch.setattr(OB.BatchingLoop, "schedule", lifo)
     _fails(TOB.test_loop_follows_its_rules, 40, 8)
+
+
+def test_prefix_match_without_parent_is_caught(monkeypatch):
+    """Index blocks by their own ids only (the parent dropped from the key)."""
+    class Parentless(dict):
+        def _k(self, key):
+            return (0, key[1])
+
+        def __getitem__(self, key):
+            return dict.__getitem__(self, self._k(key))
+
+        def __setitem__(self, key, value):
+            dict.__setitem__(self, self._k(key), value)
+
+        def __delitem__(self, key):
+            dict.__delitem__(self, self._k(key))
+
+        def __contains__(self, key):
+            return dict.__contains__(self, self._k(key))
+
+        def get(self, key, default=None):
+            return dict.get(self, self._k(key), default)
+    orig = AL.BlockAllocator.__init__
+
+    def init(self, *a, **kw):
+        orig(self, *a, **kw)
+        self.index = Parentless()
+    monkeypatch.setattr(AL.BlockAllocator, "__init__", init)
+    _fails(TPC.test_shared_blocks_hold_each_sequences_own_kv)
