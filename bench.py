@@ -41,7 +41,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "paged decode attn: KV-read GB/s and % of HBM peak; decode tokens/s per layer"
 WORKLOADS = ("llama2_7b", "qwen25_7b", "prefix_shared", "long_context", "beam_search",
-             "continuous_batching")
+             "continuous_batching", "prefix_cache")
 DESC = {
     "llama2_7b": "Llama-2-7B-shaped single layer decode: MHA 32 x 128, f16, batch 64, "
                  "context U[128,2048], blocks scattered in a pool of 1.1x need",
@@ -61,6 +61,11 @@ DESC = {
                            "(half of 64 contiguous 2048-token reservations); each step retires, "
                            "admits (prompt K/V written), then decodes every running request; "
                            "300 untimed steps reach the steady state before the warm-up",
+    "prefix_cache": "continuous batching with automatic prefix caching: Qwen2.5-7B-shaped layer "
+                    "(GQA 28 q / 4 kv x 128, bf16), at most 128 running, every prompt is one "
+                    "2000-token system prompt + U[16,256] own tokens, new tokens U[16,256], "
+                    "a backlog of 128 then 1 arrival per step; admission shares the cached "
+                    "system-prompt blocks and writes only the rest; 300 untimed steps first",
 }
 
 
@@ -369,39 +374,55 @@ def oracle_baseline(torch, W, seconds, lens, tables, k_cache, v_cache, q_all, Hk
             "tokens_per_s_per_layer": round(done / spent, 3)}
 
 
-BATCHING = dict(max_batch=64, max_ctx=2048, pool_blocks=4096, prompt=(64, 1024),
-                new=(16, 256), rate=0.5, requests=4000, seed=7, settle_steps=300)
+BATCHING = {
+    "continuous_batching": dict(shape=("f16", 32, 32, 128), max_batch=64, max_ctx=2048,
+                                pool_blocks=4096, prompt=(64, 1024), new=(16, 256), rate=0.5,
+                                requests=4000, seed=7, settle_steps=300, system=0),
+    "prefix_cache": dict(shape=("bf16", 28, 4, 128), max_batch=128, max_ctx=2560,
+                         pool_blocks=24576, prompt=(16, 256), new=(16, 256), rate=1.0,
+                         requests=4000, seed=8, settle_steps=300, system=2000),
+}
 
 
 def batching_main(args, torch, pkv, W):
-    """The continuous-batching workload: ContinuousBatch steps (retire, admit + prompt write,
-    decode), timed over K steps after W warm-up steps."""
+    """The continuous-batching workloads: ContinuousBatch steps (retire, admit + prompt
+    write, decode), timed over K steps after W warm-up steps."""
     from paged_kv_cache_459_amd.batching import ContinuousBatch
-    cfg = BATCHING
-    dtype, Hq, Hkv, hd = "f16", 32, 32, 128
+    cfg = BATCHING[args.workload]
+    dtype, Hq, Hkv, hd = cfg["shape"]
     dt = W.torch_dtype(dtype)
     rng = np.random.default_rng(cfg["seed"])
     reqs = W.request_stream(rng, cfg["requests"], prompt=cfg["prompt"], new=cfg["new"],
                             rate=cfg["rate"])
+    cache_on = cfg["system"] > 0
+    system = rng.integers(0, 32000, size=cfg["system"]).astype(np.int32)
     nb = cfg["pool_blocks"]
     k_cache, v_cache = pkv.alloc_caches(nb, Hkv, hd, dt)
     k_cache.view(-1).copy_(W.device_normal((k_cache.numel(),), dtype, 7101))
     v_cache.view(-1).copy_(W.device_normal((v_cache.numel(),), dtype, 7102))
     loop = ContinuousBatch(k_cache, v_cache, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=hd,
                            max_batch=cfg["max_batch"], max_context_len=cfg["max_ctx"],
-                           free_order=rng.permutation(nb).astype(np.int32))
+                           free_order=rng.permutation(nb).astype(np.int32),
+                           prefix_cache=cache_on)
     for i, (rid, p, m, a) in enumerate(reqs):  # the first max_batch requests are a backlog
-        loop.submit(rid, p, m, 0 if i < cfg["max_batch"] else a + 1)
+        arrival = 0 if i < cfg["max_batch"] else a + 1
+        if cache_on:
+            ids = np.concatenate([system, rng.integers(0, 32000, size=p).astype(np.int32)])
+            loop.submit(rid, len(ids), m, arrival, token_ids=ids)
+        else:
+            loop.submit(rid, p, m, arrival)
     B = cfg["max_batch"]
     q = W.device_normal((B, Hq, hd), dtype, 7103)
     k_new = W.device_normal((B, Hkv, hd), dtype, 7104)
     v_new = W.device_normal((B, Hkv, hd), dtype, 7105)
-    max_prompt = cfg["prompt"][1] * cfg["max_batch"]
+    max_prompt = (cfg["prompt"][1] + cfg["system"]) * cfg["max_batch"]
     k_prompt = W.device_normal((max_prompt, Hkv, hd), dtype, 7106)
     v_prompt = W.device_normal((max_prompt, Hkv, hd), dtype, 7107)
     out = torch.empty_like(q)
     scale = 1.0 / math.sqrt(hd)
     eb = 2
+
+    ids_rng = np.random.default_rng(cfg["seed"] + 1)
 
     def step(ev=None, stats=None):
         retired, admitted, T = loop.schedule()
@@ -412,12 +433,14 @@ def batching_main(args, torch, pkv, W):
         n = len(loop.run_id)
         if ev is not None:
             ev[1].record()
+        new_ids = ids_rng.integers(0, 32000, size=n).astype(np.int32) if cache_on else None
         loop.decode(q[:n], k_new[:n], v_new[:n], scale, out=out[:n],
-                    events=None if ev is None else ev[2:])
+                    events=None if ev is None else ev[2:], new_ids=new_ids)
         if stats is not None:
             lens = loop.last_lens.copy()
             u = loop.usage()
             stats.append(dict(B=n, retired=len(retired), admitted=len(admitted), T=T,
+                              prompt=sum(a[1] for a in admitted),
                               kv=int(lens.astype(np.int64).sum()) * 2 * Hkv * hd * eb,
                               lens=lens, tables=loop.last_tables.copy(), usage=u))
 
@@ -434,7 +457,16 @@ def batching_main(args, torch, pkv, W):
     write_ms = [e[0].elapsed_time(e[1]) for e in evs]
     part_ms = [e[2].elapsed_time(e[3]) for e in evs]
     merge_ms = [e[3].elapsed_time(e[4]) for e in evs]
-    kv = [st["kv"] for st in stats]  # no sharing: unique == logical
+    def unique(lens, tables):  # K+V bytes of the distinct cache slots read
+        t = np.where(tables >= 0, tables & ~pkv.BLOCK_SHARED, tables)
+        j = np.arange(t.shape[1])[None, :]
+        valid = np.clip(lens[:, None].astype(np.int64) - 16 * j, 0, 16)
+        best = np.zeros(nb, np.int64)
+        m = valid > 0
+        np.maximum.at(best, t[m], valid[m])
+        return int(best.sum()) * 2 * Hkv * hd * eb
+    kv_logical = [st["kv"] for st in stats]
+    kv = [unique(st["lens"], st["tables"]) for st in stats]
     qo = [2 * st["B"] * Hq * hd * eb + 4 * st["B"] * Hkv * hd * eb for st in stats]
     algo = [a + b for a, b in zip(kv, qo)]
     ms_per_step = wall / args.steps * 1e3
@@ -442,6 +474,7 @@ def batching_main(args, torch, pkv, W):
     util_paged = [st["usage"]["utilisation"] for st in stats]
     util_contig = [st["usage"]["logical_tokens"] / (st["usage"]["sequences"] * cfg["max_ctx"])
                    for st in stats]
+    sharing = [st["usage"]["logical_tokens"] / st["usage"]["slots_filled"] for st in stats]
     written = sum(st["T"] for st in stats) * 2 * Hkv * hd * eb
     achieved = sum(algo) / (sum(part_ms) / 1e3) / 1e9
     res = {
@@ -457,7 +490,7 @@ def batching_main(args, torch, pkv, W):
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic (seeded request stream, seeded N(0,1) values and block placement)",
-        "config": {"workload": "continuous_batching", "description": DESC["continuous_batching"],
+        "config": {"workload": args.workload, "description": DESC[args.workload],
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": hd, "block_size": 16,
                    "pool_blocks": nb, "max_batch": cfg["max_batch"],
                    "max_context_len": cfg["max_ctx"], "stream_workers": loop.W,
@@ -467,6 +500,9 @@ def batching_main(args, torch, pkv, W):
         "attn_merge_ms": round(float(np.mean(merge_ms)), 4),
         "batching": {
             "mean_running": round(tokens / args.steps, 2),
+            "prefix_cache": cache_on,
+            "prompt_tokens_admitted_per_step": round(sum(st["prompt"] for st in stats)
+                                                     / args.steps, 1),
             "admitted_per_step": round(sum(st["admitted"] for st in stats) / args.steps, 3),
             "retired_per_step": round(sum(st["retired"] for st in stats) / args.steps, 3),
             "prompt_tokens_written_per_step": round(sum(st["T"] for st in stats) / args.steps, 1),
@@ -478,6 +514,8 @@ def batching_main(args, torch, pkv, W):
             "kv_utilisation_paged": round(float(np.mean(util_paged)), 4),
             "kv_utilisation_contiguous_2048": round(float(np.mean(util_contig)), 4),
             "requests_the_pool_holds_contiguous": nb * 16 // cfg["max_ctx"],
+            "logical_tokens_per_filled_slot": round(float(np.mean(sharing)), 3),
+            "kv_bytes_per_step": {"unique": int(np.mean(kv)), "logical": int(np.mean(kv_logical))},
         },
         "roofline": {
             "bound": "hbm",
@@ -485,7 +523,7 @@ def batching_main(args, torch, pkv, W):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic("continuous_batching", kernel_source_digest()),
+            "traffic": measured_traffic(args.workload, kernel_source_digest()),
             "kernel": f"attention stream pass ({['', 'vector', 'matrix-core'][loop.kernel]} "
                       f"kernel)",
             "algorithmic_bytes_per_launch": int(np.mean(algo)),
@@ -513,7 +551,7 @@ def main():
 
     torch.cuda.set_device(0)
     pkv.pkv_set_attn_kernel(args.kernel)
-    if args.workload == "continuous_batching":
+    if args.workload in BATCHING:
         batching_main(args, torch, pkv, W)
         return
     wl = Workload(args.workload, args.warmup + args.steps, torch, pkv, W)

@@ -347,6 +347,36 @@ int32_t pkv_alloc_num_free(const pkv_allocator* a);            /* free blocks   
 int32_t pkv_alloc_refcount(const pkv_allocator* a, int32_t block); /* -1 if out of range      */
 /* Length of a sequence in tokens, or -1 if unknown. */
 int64_t pkv_alloc_seq_len(const pkv_allocator* a, int64_t seq);
+/* ---- Automatic prefix caching ([P1] §五 "前綴共享" and §八 "前綴快取": requests that begin  */
+/* ---- with the same tokens share that prefix's KV cache without being forked; [P3] §4.2:     */
+/* ---- a 2000-token system prompt reused by later requests). Our reading, full blocks only:   */
+/*  - a full block of a sequence whose token ids are all known is indexed by (the index entry */
+/*    of the block before it, or the empty prefix; its bs token ids), so two blocks match only */
+/*    when their whole prefixes match (ids are compared, not only hashed);                     */
+/*  - pkv_alloc_add_seq_tokens starts a sequence from its prompt's ids: it shares the longest  */
+/*    chain of indexed full blocks the prompt begins with (refcount + 1 each), takes fresh     */
+/*    blocks for the rest and indexes the prompt's new full blocks. The caller writes the K/V */
+/*    of tokens [*cached_out, n) only;                                                         */
+/*  - pkv_alloc_append_tokens is pkv_alloc_append plus the new tokens' ids (sum(ntok), in      */
+/*    argument order): blocks of indexed sequences that become full are indexed. A sequence   */
+/*    created by pkv_alloc_add_seq, or grown by pkv_alloc_append, is not indexed from then on; */
+/*    forks inherit the parent's state;                                                        */
+/*  - a freed indexed block keeps its entry and its FIFO place in the free list: a later hit  */
+/*    takes it back out (refcount 1); a fresh allocation that pops it drops the entry.         */
+/* Content equal to an indexed block's but in another block is not indexed twice.             */
+/* add_seq_tokens: slots_out (host, n entries, may be NULL) receives every prompt token's     */
+/* slot; *cached_out (may be NULL) the tokens found in the cache, a multiple of bs. Errors:    */
+/* PKV_ERR_INVALID_ARG, PKV_ERR_SEQ_EXISTS, PKV_ERR_OUT_OF_BLOCKS (nothing changes).           */
+pkv_status pkv_alloc_add_seq_tokens(pkv_allocator* a, int64_t seq, int32_t n,
+                                    const int32_t* token_ids, int32_t* slots_out,
+                                    int32_t* cached_out);
+pkv_status pkv_alloc_append_tokens(pkv_allocator* a, int32_t n, const int64_t* seqs,
+                                   const int32_t* ntok, const int32_t* token_ids,
+                                   int32_t* slots_out, int32_t* cow_src, int32_t* cow_dst,
+                                   int32_t* n_cow);
+/* Blocks whose content is indexed, in use or free (-1 for a null handle). */
+int32_t pkv_alloc_cached_blocks(const pkv_allocator* a);
+
 /* Memory accounting ([P1] §一 and §二 "內部碎片": a contiguous reservation wastes what a      */
 /* request does not use; with blocks only a sequence's last block can be partly empty).       */
 /* out (host, 4 entries) receives: live sequences; logical tokens (sum of their lengths);     */

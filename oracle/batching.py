@@ -21,6 +21,11 @@ leave to vLLM's tuning):
   3. decode: every running request, in admission order, appends one token: its K/V are
      written into the slot the allocator gives and attention runs over all of its tokens
      ([P1] §三 步驟三).
+
+With ``prefix_cache`` the requests carry their prompt's token ids: admission starts each
+sequence with ``add_seq_tokens`` (automatic prefix caching: the prompt's cached full blocks
+are shared and only the rest of the prompt is written) and decode appends with the new
+tokens' ids. The admission test is unchanged (a hit is not counted on).
 """
 
 import numpy as np
@@ -34,14 +39,17 @@ def blocks_for(n, bs):
 
 
 class Request:
-    def __init__(self, rid, prompt_len, max_new, arrival):
+    def __init__(self, rid, prompt_len, max_new, arrival, token_ids=None):
         self.rid, self.prompt_len, self.max_new, self.arrival = rid, prompt_len, max_new, arrival
+        self.token_ids = token_ids
         self.generated = 0
+        self.cached = 0
 
 
 class BatchingLoop:
     def __init__(self, num_blocks, bs, hkv, hd, dtype, *, max_batch, free_order=None,
-                 storage_dtype=None, nan_fill=None):
+                 storage_dtype=None, nan_fill=None, prefix_cache=False):
+        self.prefix_cache = prefix_cache
         self.alloc = BlockAllocator(num_blocks, bs, free_order)
         self.bs, self.hkv, self.hd, self.dtype = bs, hkv, hd, dtype
         self.max_batch = max_batch
@@ -52,9 +60,11 @@ class BatchingLoop:
         self.running = []   # admitted requests, admission order
         self.step_no = 0
 
-    def submit(self, rid, prompt_len, max_new, arrival):
+    def submit(self, rid, prompt_len, max_new, arrival, token_ids=None):
         assert prompt_len >= 1 and max_new >= 1
-        self.queue.append(Request(rid, prompt_len, max_new, arrival))
+        assert (token_ids is not None) == self.prefix_cache
+        assert token_ids is None or len(token_ids) == prompt_len
+        self.queue.append(Request(rid, prompt_len, max_new, arrival, token_ids))
 
     def _future_blocks(self):
         """Blocks the running requests may still take before they finish."""
@@ -65,8 +75,9 @@ class BatchingLoop:
         return total
 
     def schedule(self):
-        """Phases 1 and 2. Returns (retired ids, admitted requests, prompt slots in admission
-        order)."""
+        """Phases 1 and 2. Returns (retired ids, admitted requests, slots of the prompt tokens
+        to write, in admission order: with prefix caching, each request's tokens after its
+        cached ones)."""
         retired = [r.rid for r in self.running if r.generated == r.max_new]
         for rid in retired:
             self.alloc.free_seq(rid)
@@ -79,9 +90,13 @@ class BatchingLoop:
             if self.alloc.num_free() - self._future_blocks() < need:
                 break
             self.queue.pop(0)
-            self.alloc.add_seq(head.rid)
-            s, _ = self.alloc.append([head.rid], [head.prompt_len])
-            slots.extend(s)
+            if self.prefix_cache:
+                s, head.cached = self.alloc.add_seq_tokens(head.rid, head.token_ids)
+                slots.extend(s[head.cached:])
+            else:
+                self.alloc.add_seq(head.rid)
+                s, _ = self.alloc.append([head.rid], [head.prompt_len])
+                slots.extend(s)
             self.running.append(head)
             admitted.append(head)
         return retired, admitted, np.asarray(slots, np.int32)
@@ -92,16 +107,20 @@ class BatchingLoop:
             k, v, self.k_cache, self.v_cache, slots, hkv=self.hkv, hd=self.hd, bs=self.bs,
             dtype=self.dtype)
 
-    def decode(self, q, k_new, v_new, scale):
-        """Phase 3 for the running requests (admission order). Returns (out float64
-        [B, Hq, hd], the step's slots, tables, lengths)."""
+    def decode(self, q, k_new, v_new, scale, new_ids=None):
+        """Phase 3 for the running requests (admission order); new_ids: the new tokens' ids
+        (prefix caching). Returns (out float64 [B, Hq, hd], the step's slots, tables,
+        lengths)."""
         ids = [r.rid for r in self.running]
         if not ids:  # nothing runs this step
             self.step_no += 1
             return (np.zeros((0,) + np.shape(q)[1:]), np.zeros(0, np.int32),
                     np.zeros((0, 1), np.int32), np.zeros(0, np.int32))
-        slots, cows = self.alloc.append(ids, [1] * len(ids))
-        assert not cows  # no request here shares blocks
+        if self.prefix_cache:
+            slots, cows = self.alloc.append_tokens(ids, [1] * len(ids), list(new_ids))
+        else:
+            slots, cows = self.alloc.append(ids, [1] * len(ids))
+        assert not cows  # appends never land in a shared block (only full blocks are shared)
         self.k_cache, self.v_cache = cache_write.write_kv(
             k_new, v_new, self.k_cache, self.v_cache, np.asarray(slots, np.int32),
             hkv=self.hkv, hd=self.hd, bs=self.bs, dtype=self.dtype)

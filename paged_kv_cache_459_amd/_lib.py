@@ -82,6 +82,9 @@ SIGNATURES = {
     "pkv_alloc_free": (c_i32, [c_vp, c_i64]),
     "pkv_alloc_fork_many": (c_i32, [c_vp, c_i32, c_vp, c_vp]),
     "pkv_alloc_usage": (c_i32, [c_vp, c_vp]),
+    "pkv_alloc_add_seq_tokens": (c_i32, [c_vp, c_i64, c_i32, c_vp, c_vp, c_vp]),
+    "pkv_alloc_append_tokens": (c_i32, [c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "pkv_alloc_cached_blocks": (c_i32, [c_vp]),
     "pkv_alloc_free_many": (c_i32, [c_vp, c_i32, c_vp]),
     "pkv_alloc_tables": (c_i32, [c_vp, c_i32, c_vp, c_i32, c_vp, c_vp]),
     "pkv_alloc_tables_marked": (c_i32, [c_vp, c_i32, c_vp, c_i32, c_vp, c_vp]),

@@ -315,24 +315,53 @@ class BlockAllocator:
     def add_seq(self, seq):
         check(lib.pkv_alloc_add_seq(self._h, int(seq)), "pkv_alloc_add_seq")
 
-    def append(self, seqs, ntok, want_slots=True, slots_out=None):
-        """Returns (slots int32 [sum ntok], cow pairs int32 [n_cow, 2])."""
+    def append(self, seqs, ntok, want_slots=True, slots_out=None, token_ids=None):
+        """Returns (slots int32 [sum ntok], cow pairs int32 [n_cow, 2]). With token_ids (sum
+        ntok ids, argument order) it is pkv_alloc_append_tokens (prefix-cache indexing)."""
         seqs = _as_c(seqs, np.int64)
         ntok = _as_c(ntok, np.int32)
         n = len(seqs)
+        if len(ntok) != n:
+            raise ValueError("seqs and ntok lengths differ")
         slots = None
         if want_slots:
             slots = slots_out if slots_out is not None else np.empty(int(ntok.sum()), np.int32)
         if self._cow.shape[1] < max(n, 1):
             self._cow = np.empty((2, max(n, 1)), np.int32)
         cow = self._cow
-        check(lib.pkv_alloc_append(self._h, n, seqs.ctypes.data, ntok.ctypes.data,
-                                   slots.ctypes.data if want_slots else None, cow[0].ctypes.data,
-                                   cow[1].ctypes.data, ctypes.byref(self._ncow)),
-              "pkv_alloc_append")
+        sp = slots.ctypes.data if want_slots else None
+        if token_ids is None:
+            check(lib.pkv_alloc_append(self._h, n, seqs.ctypes.data, ntok.ctypes.data, sp,
+                                       cow[0].ctypes.data, cow[1].ctypes.data,
+                                       ctypes.byref(self._ncow)), "pkv_alloc_append")
+        else:
+            ids = _as_c(token_ids, np.int32)
+            if len(ids) != int(ntok.sum()):
+                raise ValueError("token_ids must hold sum(ntok) ids")
+            check(lib.pkv_alloc_append_tokens(self._h, n, seqs.ctypes.data, ntok.ctypes.data,
+                                              ids.ctypes.data, sp, cow[0].ctypes.data,
+                                              cow[1].ctypes.data, ctypes.byref(self._ncow)),
+                  "pkv_alloc_append_tokens")
         k = self._ncow.value
         pairs = cow[:, :k].T.copy() if k else np.zeros((0, 2), np.int32)
         return slots, pairs
+
+    def append_tokens(self, seqs, ntok, token_ids, want_slots=True, slots_out=None):
+        return self.append(seqs, ntok, want_slots, slots_out, token_ids=token_ids)
+
+    def add_seq_tokens(self, seq, token_ids, slots_out=None):
+        """New sequence holding a prompt (prefix caching). Returns (slots of every prompt
+        token, tokens found in the cache)."""
+        ids = _as_c(token_ids, np.int32)
+        slots = slots_out if slots_out is not None else np.empty(len(ids), np.int32)
+        cached = ctypes.c_int32(0)
+        check(lib.pkv_alloc_add_seq_tokens(self._h, int(seq), len(ids), ids.ctypes.data,
+                                           slots.ctypes.data, ctypes.byref(cached)),
+              "pkv_alloc_add_seq_tokens")
+        return slots, cached.value
+
+    def cached_blocks(self):
+        return int(lib.pkv_alloc_cached_blocks(self._h))
 
     def fork(self, parent, child):
         check(lib.pkv_alloc_fork(self._h, int(parent), int(child)), "pkv_alloc_fork")

@@ -14,6 +14,12 @@ vLLM's tuning, so the rule never needs it):
   admission order, appends one token, whose K/V are stored and attended to in the fused
   decode step (``pkv_decode_append_stream`` + ``pkv_decode_append_merge``).
 
+With ``prefix_cache=True`` requests carry their prompt's token ids and admission starts each
+sequence with ``add_seq_tokens`` (automatic prefix caching, [P1] §五 / §八, [P3] §4.2): the
+prompt's cached full blocks are shared and only the tokens after them are written; decode
+appends with the new tokens' ids so that filled blocks are indexed too. Tables are exported
+with shared blocks marked, so the attention kernels keep those in the L2.
+
 Host bookkeeping only: the allocator is the library's C++ allocator and every device step
 runs in the library's kernels. Host buffers for tables and slots are pinned and
 double-buffered, so the host may prepare the next step while the current one runs.
@@ -34,8 +40,9 @@ def _blocks(n):
 
 class ContinuousBatch:
     def __init__(self, k_cache, v_cache, *, num_q_heads, num_kv_heads, head_dim, max_batch,
-                 max_context_len, free_order=None):
+                 max_context_len, free_order=None, prefix_cache=False):
         self.k_cache, self.v_cache = k_cache, v_cache
+        self.prefix_cache = bool(prefix_cache)
         self.Hq, self.Hkv, self.hd = num_q_heads, num_kv_heads, head_dim
         self.dtype = k_cache.dtype
         self.device = k_cache.device
@@ -69,14 +76,20 @@ class ContinuousBatch:
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=self.device)
 
     # -- requests --------------------------------------------------------------------------
-    def submit(self, rid, prompt_len, max_new_tokens, arrival_step=0):
+    def submit(self, rid, prompt_len, max_new_tokens, arrival_step=0, token_ids=None):
+        if (token_ids is not None) != self.prefix_cache:
+            raise ValueError("token_ids are given exactly when prefix caching is on")
+        if token_ids is not None and len(token_ids) != prompt_len:
+            raise ValueError("token_ids must hold prompt_len ids")
         if prompt_len < 1 or max_new_tokens < 1:
             raise ValueError("a request needs a prompt and at least one new token")
         if prompt_len + max_new_tokens > self.max_ctx:
             raise ValueError("request longer than max_context_len")
         if _blocks(prompt_len + max_new_tokens) > self.nb:
             raise ValueError("request larger than the whole pool")
-        self.queue.append((int(rid), int(prompt_len), int(max_new_tokens), int(arrival_step)))
+        ids = None if token_ids is None else np.ascontiguousarray(token_ids, dtype=np.int32)
+        self.queue.append((int(rid), int(prompt_len), int(max_new_tokens), int(arrival_step),
+                           ids))
 
     def idle(self):
         return not self.queue and len(self.run_id) == 0
@@ -99,7 +112,9 @@ class ContinuousBatch:
 
     def schedule(self):
         """Retire finished requests, admit arrived ones. Returns (retired ids, admitted
-        [(id, prompt_len)], number of prompt tokens to write)."""
+        [(id, prompt_len)], number of prompt tokens to write). With prefix caching the tokens
+        to write are each admitted prompt's tokens after its cached ones, and
+        ``last_cached`` holds the cached counts."""
         finished = self.run_done >= self.run_new
         retired = self.run_id[finished]
         if len(retired):
@@ -110,37 +125,42 @@ class ContinuousBatch:
         # what the running requests may still take: final blocks minus the blocks they hold
         held = _blocks(self.run_final - self.run_new + self.run_done)
         reserve = int((_blocks(self.run_final) - held).sum())
-        free = self.alloc.num_free()
-        admitted = []
+        admitted, cached = [], []
+        T = 0
         while self.queue and self.queue[0][3] <= self.step_no and \
                 len(self.run_id) + len(admitted) < self.max_batch:
-            rid, p, m, _ = self.queue[0]
+            rid, p, m, _, ids = self.queue[0]
             need = int(_blocks(p + m))
-            if free - reserve < need:
+            if self.alloc.num_free() - reserve < need:
                 break
             self.queue.pop(0)
-            admitted.append((rid, p, m))
-            reserve += need - int(_blocks(p))
-            free -= int(_blocks(p))
-        prompt_tokens = sum(p for _, p, _ in admitted)
-        if admitted:
-            ids = np.array([a[0] for a in admitted], np.int64)
-            for rid in ids:
-                self.alloc.add_seq(int(rid))
             s = self._take_set()
-            pin = self._pin[s].numpy()[self._slot0:self._slot0 + prompt_tokens]
-            self.alloc.append(ids, np.array([a[1] for a in admitted], np.int32), slots_out=pin)
-            self.prompt_slots = self._dev[s][self._slot0:self._slot0 + prompt_tokens]
-            self.prompt_slots.copy_(self._pin[s][self._slot0:self._slot0 + prompt_tokens],
-                                    non_blocking=True)
-            self.run_id = np.concatenate([self.run_id, ids])
+            pin = self._pin[s].numpy()
+            if ids is not None:  # prefix caching: shares the cached full blocks
+                slots, c = self.alloc.add_seq_tokens(rid, ids)
+                pin[self._slot0 + T:self._slot0 + T + p - c] = slots[c:]
+            else:
+                c = 0
+                self.alloc.add_seq(rid)
+                self.alloc.append([rid], [p], slots_out=pin[self._slot0 + T:self._slot0 + T + p])
+            T += p - c
+            reserve += need - int(_blocks(p))
+            admitted.append((rid, p, m))
+            cached.append(c)
+        self.last_cached = cached
+        if T:
+            s = self._set
+            self.prompt_slots = self._dev[s][self._slot0:self._slot0 + T]
+            self.prompt_slots.copy_(self._pin[s][self._slot0:self._slot0 + T], non_blocking=True)
+        else:
+            self.prompt_slots = None
+        if admitted:
+            self.run_id = np.concatenate([self.run_id, [a[0] for a in admitted]]).astype(np.int64)
             self.run_final = np.concatenate([self.run_final,
                                              [a[1] + a[2] for a in admitted]]).astype(np.int64)
             self.run_new = np.concatenate([self.run_new, [a[2] for a in admitted]]).astype(np.int64)
             self.run_done = np.concatenate([self.run_done, np.zeros(len(admitted), np.int64)])
-        else:
-            self.prompt_slots = None
-        return retired, [(a[0], a[1]) for a in admitted], prompt_tokens
+        return retired, [(a[0], a[1]) for a in admitted], T
 
     def write_prompts(self, k, v):
         """The admitted prompts' K/V, [T, Hkv, hd] in admission order (T from schedule())."""
@@ -151,10 +171,13 @@ class ContinuousBatch:
         api.pkv_write(k, v, self.k_cache, self.v_cache, self.prompt_slots)
 
     # -- phase 3 ---------------------------------------------------------------------------
-    def decode(self, q, k_new, v_new, scale, out=None, events=None):
+    def decode(self, q, k_new, v_new, scale, out=None, events=None, new_ids=None):
         """One decode step of every running request (rows of q/k_new/v_new in admission
-        order). Returns out [B, Hq, hd]. ``events``: optional three torch.cuda.Events recorded
-        before the stream pass, between the passes and after the merge pass."""
+        order; new_ids: the new tokens' ids, with prefix caching). Returns out [B, Hq, hd].
+        ``events``: optional three torch.cuda.Events recorded before the stream pass, between
+        the passes and after the merge pass."""
+        if (new_ids is not None) != self.prefix_cache:
+            raise ValueError("new_ids are given exactly when prefix caching is on")
         B = len(self.run_id)
         self.step_no += 1
         if B == 0:
@@ -166,8 +189,10 @@ class ContinuousBatch:
         lens_h = flat[:B]
         tables_h = flat[self.max_batch:self.max_batch + B * self.max_blocks].reshape(
             B, self.max_blocks)
-        self.alloc.append(self.run_id, np.ones(B, np.int32), want_slots=False)
-        self.alloc.tables(self.run_id, self.max_blocks, tables_out=tables_h, lens_out=lens_h)
+        self.alloc.append(self.run_id, np.ones(B, np.int32), want_slots=False,
+                          token_ids=new_ids)
+        self.alloc.tables(self.run_id, self.max_blocks, tables_out=tables_h, lens_out=lens_h,
+                          mark_shared=True)
         self.run_done += 1
         dev = self._dev[s]
         nt = self.max_batch + B * self.max_blocks

@@ -9,10 +9,16 @@
 // Conventions the pages leave open (documented in pkv.h): FIFO free list seeded with a caller
 // order; per-block reference counts; copy-on-write of a shared, partly filled last block;
 // blocks released in logical order; every call all-or-nothing.
+//
+// Automatic prefix caching ([P1] §五 "前綴共享", §八 "前綴快取"; [P3] §4.2): full blocks of
+// sequences whose token ids are known are indexed by (node of the block before them, their
+// ids); a new sequence given its prompt's ids shares the longest indexed chain it begins
+// with. Freed indexed blocks stay in the free list (FIFO) and keep their entry until a fresh
+// allocation pops them; a hit takes a free one back out of the list, so the list is an
+// intrusive doubly linked list over block ids.
 
 #include <algorithm>
 #include <cstdint>
-#include <deque>
 #include <new>
 #include <unordered_map>
 #include <unordered_set>
@@ -26,18 +32,102 @@ struct Seq {
   std::vector<int32_t> blocks;  // physical blocks, logical order
   int64_t len = 0;              // tokens
   uint64_t mark = 0;            // last append call that named this sequence (duplicate check)
+  // prefix-cache tracking: only sequences whose every token id is known are indexed
+  bool tracked = false;
+  int64_t last_node = 0;         // node of the last indexed full block (0: the empty prefix)
+  std::vector<int32_t> pending;  // ids of the tokens in the partly filled last block
 };
+
+// An indexed full block: its content is (parent node, ids).
+struct Node {
+  int64_t parent;
+  int32_t block;
+  uint64_t hash;
+  std::vector<int32_t> ids;
+};
+
+uint64_t content_hash(int64_t parent, const int32_t* ids, int32_t n) {
+  uint64_t h = 0x9E3779B97F4A7C15ull ^ static_cast<uint64_t>(parent);
+  for (int32_t i = 0; i < n; ++i) {
+    h ^= static_cast<uint32_t>(ids[i]);
+    h *= 0x100000001B3ull;
+    h ^= h >> 29;
+  }
+  return h;
+}
 
 }  // namespace
 
 struct pkv_allocator {
   int32_t nb = 0;
   int32_t bs = 0;
-  std::deque<int32_t> free_list;
+  // free list: FIFO, intrusive doubly linked over block ids (-1 ends)
+  std::vector<int32_t> next, prev;
+  int32_t head = -1, tail = -1, nfree = 0;
   std::vector<int32_t> ref;
   std::unordered_map<int64_t, Seq> seqs;
   uint64_t calls = 0;             // append calls so far (stamps Seq::mark)
   std::vector<Seq*> batch;        // reused per append call
+  // prefix cache
+  std::unordered_multimap<uint64_t, int64_t> index;  // content hash -> node
+  std::unordered_map<int64_t, Node> nodes;
+  std::vector<int64_t> block_node;  // node indexing each block, 0 if none
+  int64_t next_node = 1;
+  int32_t cached = 0;               // blocks with an entry
+
+  void push_back(int32_t b) {
+    next[b] = -1;
+    prev[b] = tail;
+    if (tail >= 0) next[tail] = b; else head = b;
+    tail = b;
+    ++nfree;
+  }
+
+  void unlink(int32_t b) {
+    if (prev[b] >= 0) next[prev[b]] = next[b]; else head = next[b];
+    if (next[b] >= 0) prev[next[b]] = prev[b]; else tail = prev[b];
+    --nfree;
+  }
+
+  void drop_entry(int32_t b) {
+    const int64_t id = block_node[b];
+    if (id == 0) return;
+    auto it = nodes.find(id);
+    auto range = index.equal_range(it->second.hash);
+    for (auto r = range.first; r != range.second; ++r)
+      if (r->second == id) {
+        index.erase(r);
+        break;
+      }
+    nodes.erase(it);
+    block_node[b] = 0;
+    --cached;
+  }
+
+  // Node naming the content (parent, ids[0..bs)), or 0.
+  int64_t find(int64_t parent, const int32_t* ids) const {
+    const uint64_t h = content_hash(parent, ids, bs);
+    auto range = index.equal_range(h);
+    for (auto r = range.first; r != range.second; ++r) {
+      const Node& nd = nodes.at(r->second);
+      if (nd.parent == parent && std::equal(nd.ids.begin(), nd.ids.end(), ids)) return r->second;
+    }
+    return 0;
+  }
+
+  // Index full block `block` under (parent, ids); returns the node now naming that content
+  // (an existing one when the same content is indexed already).
+  int64_t enter(int64_t parent, const int32_t* ids, int32_t block) {
+    const int64_t have = find(parent, ids);
+    if (have) return have;
+    const int64_t id = next_node++;
+    const uint64_t h = content_hash(parent, ids, bs);
+    nodes.emplace(id, Node{parent, block, h, std::vector<int32_t>(ids, ids + bs)});
+    index.emplace(h, id);
+    block_node[block] = id;
+    ++cached;
+    return id;
+  }
 
   // Blocks needed to append ntok tokens to s: a copy-on-write block when the last block is
   // partly filled and shared, plus the new blocks the extra tokens spill into.
@@ -48,9 +138,11 @@ struct pkv_allocator {
     *fresh = want - have;
   }
 
+  // Fresh allocation: the free list's front, its index entry dropped (eviction).
   int32_t pop() {
-    const int32_t b = free_list.front();
-    free_list.pop_front();
+    const int32_t b = head;
+    unlink(b);
+    drop_entry(b);
     ref[b] = 1;
     return b;
   }
@@ -76,7 +168,10 @@ pkv_status pkv_alloc_create(int32_t NB, int32_t bs, const int32_t* free_order,
   a->nb = NB;
   a->bs = bs;
   a->ref.assign(NB, 0);
-  for (int32_t i = 0; i < NB; ++i) a->free_list.push_back(free_order ? free_order[i] : i);
+  a->next.assign(NB, -1);
+  a->prev.assign(NB, -1);
+  a->block_node.assign(NB, 0);
+  for (int32_t i = 0; i < NB; ++i) a->push_back(free_order ? free_order[i] : i);
   *out = a;
   return PKV_OK;
 }
@@ -90,9 +185,13 @@ pkv_status pkv_alloc_add_seq(pkv_allocator* a, int64_t seq) {
   return PKV_OK;
 }
 
-pkv_status pkv_alloc_append(pkv_allocator* a, int32_t n, const int64_t* seqs, const int32_t* ntok,
-                            int32_t* slots_out, int32_t* cow_src, int32_t* cow_dst,
-                            int32_t* n_cow) {
+}  // extern "C"
+
+namespace {
+
+pkv_status append_impl(pkv_allocator* a, int32_t n, const int64_t* seqs, const int32_t* ntok,
+                       const int32_t* token_ids, int32_t* slots_out, int32_t* cow_src,
+                       int32_t* cow_dst, int32_t* n_cow) {
   if (!a || n < 0 || (n > 0 && (!seqs || !ntok))) return PKV_ERR_INVALID_ARG;
   if ((cow_src == nullptr) != (cow_dst == nullptr) || ((cow_src != nullptr) != (n_cow != nullptr)))
     return PKV_ERR_INVALID_ARG;
@@ -130,7 +229,7 @@ pkv_status pkv_alloc_append(pkv_allocator* a, int32_t n, const int64_t* seqs, co
     a->needs(*ptr[k], ntok[k], &cow, &fresh);
     total += (cow ? 1 : 0) + fresh;
   }
-  if (total > static_cast<int64_t>(a->free_list.size())) return PKV_ERR_OUT_OF_BLOCKS;
+  if (total > a->nfree) return PKV_ERR_OUT_OF_BLOCKS;
 
   int32_t ncow = 0;
   int64_t out_pos = 0;
@@ -154,13 +253,85 @@ pkv_status pkv_alloc_append(pkv_allocator* a, int32_t n, const int64_t* seqs, co
       if (s.len % a->bs == 0) s.blocks.push_back(a->pop());  // current block full: a new one
       const int32_t blk = s.blocks[s.len / a->bs];
       if (slots_out) slots_out[out_pos] = blk * a->bs + static_cast<int32_t>(s.len % a->bs);
+      if (s.tracked && token_ids) {
+        s.pending.push_back(token_ids[out_pos]);
+        if (static_cast<int32_t>(s.pending.size()) == a->bs) {  // the block just filled
+          s.last_node = a->enter(s.last_node, s.pending.data(), blk);
+          s.pending.clear();
+        }
+      }
       ++out_pos;
       ++s.len;
+    }
+    if (ntok[k] > 0 && !token_ids) {  // tokens of unknown content: no longer indexed
+      s.tracked = false;
+      s.pending.clear();
     }
   }
   if (n_cow) *n_cow = ncow;
   return PKV_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_alloc_append(pkv_allocator* a, int32_t n, const int64_t* seqs, const int32_t* ntok,
+                            int32_t* slots_out, int32_t* cow_src, int32_t* cow_dst,
+                            int32_t* n_cow) {
+  return append_impl(a, n, seqs, ntok, nullptr, slots_out, cow_src, cow_dst, n_cow);
+}
+
+pkv_status pkv_alloc_append_tokens(pkv_allocator* a, int32_t n, const int64_t* seqs,
+                                   const int32_t* ntok, const int32_t* token_ids,
+                                   int32_t* slots_out, int32_t* cow_src, int32_t* cow_dst,
+                                   int32_t* n_cow) {
+  if (n > 0 && !token_ids) return PKV_ERR_INVALID_ARG;
+  return append_impl(a, n, seqs, ntok, token_ids, slots_out, cow_src, cow_dst, n_cow);
+}
+
+pkv_status pkv_alloc_add_seq_tokens(pkv_allocator* a, int64_t seq, int32_t n,
+                                    const int32_t* token_ids, int32_t* slots_out,
+                                    int32_t* cached_out) {
+  if (!a || n < 0 || (n > 0 && !token_ids)) return PKV_ERR_INVALID_ARG;
+  if (a->seqs.count(seq)) return PKV_ERR_SEQ_EXISTS;
+  const int32_t bs = a->bs;
+  // the longest indexed chain of full blocks the prompt begins with
+  std::vector<int32_t> hits;
+  int64_t parent = 0;
+  for (int32_t j = 0; j < n / bs; ++j) {
+    const int64_t node = a->find(parent, token_ids + static_cast<int64_t>(j) * bs);
+    if (!node) break;
+    hits.push_back(a->nodes.at(node).block);
+    parent = node;
+  }
+  int32_t revived = 0;
+  for (int32_t b : hits) revived += a->ref[b] == 0 ? 1 : 0;
+  const int64_t fresh = (static_cast<int64_t>(n) + bs - 1) / bs - static_cast<int64_t>(hits.size());
+  if (fresh > a->nfree - revived) return PKV_ERR_OUT_OF_BLOCKS;
+  Seq s;
+  s.blocks.reserve(hits.size() + static_cast<size_t>(fresh));
+  for (int32_t b : hits) {
+    if (a->ref[b] == 0) a->unlink(b);  // a free indexed block, revived
+    a->ref[b] += 1;
+    s.blocks.push_back(b);
+  }
+  for (int64_t i = 0; i < fresh; ++i) s.blocks.push_back(a->pop());
+  int64_t last = parent;
+  for (int32_t j = static_cast<int32_t>(hits.size()); j < n / bs; ++j)
+    last = a->enter(last, token_ids + static_cast<int64_t>(j) * bs, s.blocks[j]);
+  s.len = n;
+  s.tracked = true;
+  s.last_node = last;
+  s.pending.assign(token_ids + (n / bs) * bs, token_ids + n);
+  if (slots_out)
+    for (int32_t t = 0; t < n; ++t) slots_out[t] = s.blocks[t / bs] * bs + t % bs;
+  if (cached_out) *cached_out = static_cast<int32_t>(hits.size()) * bs;
+  a->seqs.emplace(seq, std::move(s));
+  return PKV_OK;
+}
+
+int32_t pkv_alloc_cached_blocks(const pkv_allocator* a) { return a ? a->cached : -1; }
 
 pkv_status pkv_alloc_fork(pkv_allocator* a, int64_t parent, int64_t child) {
   if (!a) return PKV_ERR_INVALID_ARG;
@@ -168,6 +339,7 @@ pkv_status pkv_alloc_fork(pkv_allocator* a, int64_t parent, int64_t child) {
   if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
   if (a->seqs.count(child)) return PKV_ERR_SEQ_EXISTS;
   Seq copy = it->second;
+  copy.mark = 0;
   for (int32_t b : copy.blocks) a->ref[b] += 1;
   a->seqs.emplace(child, std::move(copy));
   return PKV_OK;
@@ -178,7 +350,7 @@ pkv_status pkv_alloc_free(pkv_allocator* a, int64_t seq) {
   auto it = a->seqs.find(seq);
   if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
   for (int32_t b : it->second.blocks) {
-    if (--a->ref[b] == 0) a->free_list.push_back(b);
+    if (--a->ref[b] == 0) a->push_back(b);
   }
   a->seqs.erase(it);
   return PKV_OK;
@@ -200,8 +372,8 @@ pkv_status pkv_alloc_fork_many(pkv_allocator* a, int32_t n, const int64_t* paren
     if (a->seqs.count(children[k]) || !kids.insert(children[k]).second) return PKV_ERR_SEQ_EXISTS;
   std::vector<Seq> copies(n);  // copied before any insertion can move the parents
   for (int32_t k = 0; k < n; ++k) {
-    copies[k].blocks = from[k]->blocks;
-    copies[k].len = from[k]->len;
+    copies[k] = *from[k];
+    copies[k].mark = 0;
   }
   a->seqs.reserve(a->seqs.size() + static_cast<size_t>(n));
   for (int32_t k = 0; k < n; ++k) {
@@ -286,9 +458,7 @@ pkv_status pkv_alloc_tables_marked(const pkv_allocator* a, int32_t n, const int6
   return export_tables(a, n, seqs, max_blocks, block_tables_out, context_lens_out, true);
 }
 
-int32_t pkv_alloc_num_free(const pkv_allocator* a) {
-  return a ? static_cast<int32_t>(a->free_list.size()) : -1;
-}
+int32_t pkv_alloc_num_free(const pkv_allocator* a) { return a ? a->nfree : -1; }
 
 int32_t pkv_alloc_refcount(const pkv_allocator* a, int32_t block) {
   if (!a || block < 0 || block >= a->nb) return -1;
@@ -320,7 +490,7 @@ pkv_status pkv_alloc_usage(const pkv_allocator* a, int64_t* out) {
   for (int32_t f : fill) filled += f;
   out[0] = static_cast<int64_t>(a->seqs.size());
   out[1] = logical;
-  out[2] = static_cast<int64_t>(a->nb) - static_cast<int64_t>(a->free_list.size());
+  out[2] = static_cast<int64_t>(a->nb) - a->nfree;
   out[3] = filled;
   return PKV_OK;
 }
@@ -329,9 +499,9 @@ int32_t pkv_alloc_free_list(const pkv_allocator* a, int32_t* out, int32_t cap) {
   if (!a) return -1;
   int32_t i = 0;
   if (out) {
-    for (auto it = a->free_list.begin(); it != a->free_list.end() && i < cap; ++it) out[i++] = *it;
+    for (int32_t b = a->head; b >= 0 && i < cap; b = a->next[b]) out[i++] = b;
   }
-  return static_cast<int32_t>(a->free_list.size());
+  return a->nfree;
 }
 
 }  // extern "C"

@@ -228,3 +228,58 @@ def test_batched_fork_and_free_equal_the_single_calls():
     nat.free_many([])
     nat.free_many(live)
     assert nat.num_free() == nb
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_prefix_cache_operations_match_oracle(seed):
+    """Prompts drawn from a few shared prefixes (so that chains hit, revive freed blocks and
+    get evicted), decoding with and without ids, forks and frees: both allocators return the
+    same slots, cached counts and copy-on-write pairs, and hold the same state throughout."""
+    rng = np.random.default_rng(700 + seed)
+    nb = int(rng.integers(24, 80))
+    order = rng.permutation(nb)
+    nat, ora = Native(nb, BS, order), Oracle(nb, BS, order)
+    vocab = 50  # small, so that equal blocks under different parents occur
+    prefixes = [list(rng.integers(0, vocab, size=int(rng.integers(10, 70)))) for _ in range(4)]
+    next_seq = 0
+    for _ in range(800):
+        live = list(ora.blocks)
+        op = rng.integers(0, 10)
+        if op <= 2 or not live:
+            p = prefixes[int(rng.integers(len(prefixes)))]
+            toks = [int(t) for t in p] + [int(t) for t in
+                                          rng.integers(0, vocab, size=int(rng.integers(0, 24)))]
+            s = next_seq
+            next_seq += 1
+            r_n, r_o = both(lambda: nat.add_seq_tokens(s, toks),
+                            lambda: ora.add_seq_tokens(s, toks))
+            if r_o is not None:
+                assert r_n[0].tolist() == r_o[0] and r_n[1] == r_o[1]
+        elif op <= 5:
+            k = int(rng.integers(1, min(len(live), 4) + 1))
+            batch = [int(x) for x in rng.choice(live, size=k, replace=False)]
+            ntok = [int(rng.integers(0, 20)) for _ in batch]
+            ids = [int(t) for t in rng.integers(0, vocab, size=sum(ntok))]
+            r_n, r_o = both(lambda: nat.append_tokens(batch, ntok, ids),
+                            lambda: ora.append_tokens(batch, ntok, ids))
+            if r_o is not None:
+                assert r_n[0].tolist() == r_o[0]
+                assert [tuple(c) for c in r_n[1].tolist()] == r_o[1]
+        elif op == 6:
+            s = live[int(rng.integers(len(live)))]
+            both(lambda: nat.append([s], [3]), lambda: ora.append([s], [3]))
+        elif op == 7:
+            parent = live[int(rng.integers(len(live)))]
+            child = next_seq
+            next_seq += 1
+            both(lambda: nat.fork(parent, child), lambda: ora.fork(parent, child))
+        else:
+            s = live[int(rng.integers(len(live)))]
+            both(lambda: nat.free(s), lambda: ora.free_seq(s))
+        same_state(nat, ora, list(ora.blocks))
+        assert nat.cached_blocks() == ora.cached_blocks()
+    for s in list(ora.blocks):
+        nat.free(s)
+        ora.free_seq(s)
+    assert nat.num_free() == nb and nat.free_list() == ora.free_list()
+    assert nat.cached_blocks() == ora.cached_blocks()

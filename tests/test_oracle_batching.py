@@ -82,3 +82,62 @@ def test_loop_follows_its_rules(nb, max_batch):
     assert order == sorted(order)  # ids are in arrival order
     assert all(done[r[0]] == r[2] for r in reqs)
     assert loop.alloc.num_free() == nb
+
+
+def test_loop_with_prefix_cache():
+    """Requests share system prompts ([P3] §4.2); admission writes only the tokens after the
+    cached ones. With K/V from a model where position p depends on tokens 0..p, every decode
+    output equals dense attention over the model's K/V of that request's own tokens, and the
+    cache serves a large share of the prompt tokens."""
+    import hashlib
+    dtype, hq, hkv, hd, bs, scale = "f32", 4, 2, 64, 16, 0.125
+
+    def model_kv(tokens, p):
+        h = hashlib.sha256(np.asarray(tokens[:p + 1], np.int64).tobytes()).digest()
+        r = np.random.default_rng(int.from_bytes(h[:8], "little"))
+        return W.normal_values(r, (hkv, hd), dtype), W.normal_values(r, (hkv, hd), dtype)
+
+    rng = np.random.default_rng(450)
+    systems = [list(rng.integers(0, 1000, size=n)) for n in (70, 33)]
+    reqs = W.request_stream(rng, 24, prompt=(1, 30), new=(1, 20), rate=0.6)
+    nb = 60
+    loop = OB.BatchingLoop(nb, bs, hkv, hd, dtype, max_batch=6, free_order=rng.permutation(nb),
+                           storage_dtype=np.float32, nan_fill=np.float32(np.nan),
+                           prefix_cache=True)
+    toks = {}
+    for rid, p, m, a in reqs:
+        t = [int(x) for x in systems[rid % 2]] + [int(x) for x in rng.integers(0, 1000, size=p)]
+        toks[rid] = t
+        loop.submit(rid, len(t), m, a, token_ids=t)
+    prompt_total, cached_total = 0, 0
+    while not loop.idle():
+        _, admitted, slots = loop.schedule()
+        rows = []
+        for r in admitted:
+            prompt_total += r.prompt_len
+            cached_total += r.cached
+            rows += [model_kv(toks[r.rid], p) for p in range(r.cached, r.prompt_len)]
+        assert len(rows) == len(slots)
+        if rows:
+            loop.write_prompts(np.stack([x[0] for x in rows]), np.stack([x[1] for x in rows]),
+                               slots)
+        B = len(loop.running)
+        new_ids = [int(x) for x in rng.integers(0, 1000, size=B)]
+        kv = []
+        for r, i in zip(loop.running, new_ids):
+            toks[r.rid] = toks[r.rid] + [i]
+            kv.append(model_kv(toks[r.rid], len(toks[r.rid]) - 1))
+        q = W.normal_values(rng, (B, hq, hd), dtype)
+        kn = np.stack([x[0] for x in kv]) if kv else np.zeros((0, hkv, hd), np.float32)
+        vn = np.stack([x[1] for x in kv]) if kv else np.zeros((0, hkv, hd), np.float32)
+        out, _, _, lens = loop.decode(q, kn, vn, scale, new_ids=new_ids)
+        for i, r in enumerate(loop.running):
+            t = toks[r.rid]
+            assert lens[i] == len(t)
+            K = np.stack([model_kv(t, p)[0] for p in range(len(t))]).astype(np.float64)
+            V = np.stack([model_kv(t, p)[1] for p in range(len(t))]).astype(np.float64)
+            np.testing.assert_allclose(out[i], dense(q[i].astype(np.float64), K, V, scale,
+                                                     hq // hkv), atol=1e-12)
+    assert cached_total > 0.4 * prompt_total
+    loop.schedule()
+    assert loop.alloc.num_free() == nb
