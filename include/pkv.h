@@ -179,6 +179,70 @@ pkv_status pkv_decode_append_attn(void* out, const void* q, const void* k_new,
                                   float scale, pkv_dtype dtype, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* ---- Shared-prefix plans ([P1] §二 "解決三大問題" and [P2] "共享和复用": sequences with a   */
+/* ---- common prefix, such as a system prompt or beam candidates, point at the same physical  */
+/* ---- blocks). Attention over such blocks reads the same K/V for every sequence that shares */
+/* ---- them; a plan lets the decode step read it once for all of them.                       */
+/* A run is (members, logical blocks [j0, j1)): every member's table names the same block of  */
+/* the pool at each index of the range. pkv_decode_plan finds the batch's runs from host      */
+/* copies of its tables and lengths (entries may carry PKV_BLOCK_SHARED): sequences grouped by */
+/* their first block, each group of two or more extended while all of its members agree,     */
+/* then split where they part. A sequence's shared blocks are thus the first skip_s blocks of  */
+/* its table. The decode step then runs three kernels (pkv_decode_planned):                   */
+/*  1. shared pass: per unit (a chunk of up to 16 blocks of a run, up to 16/G of its members) */
+/*     and kv head, one read of each K/V tile and an MFMA contraction over all of the unit's  */
+/*     (member, q head) rows, each row masked at its own sequence's length -> one (m, l, o)   */
+/*     piece per row;                                                                          */
+/*  2. the stream pass over each sequence's remaining blocks (those after skip_s);            */
+/*  3. the merge: for planned sequences, their private pieces and shared pieces, in order.    */
+/* Results equal pkv_decode_attn's within rounding: the sums run in another order (the plan's), */
+/* deterministic for a given plan. The shared pass needs f16/bf16 and G = Hq/Hkv <= 16; for    */
+/* other shapes pkv_decode_plan returns a plan without runs (the planned call then does what  */
+/* the plain one does). Batches above 8192 sequences are not planned (PKV_ERR_UNSUPPORTED).    */
+/*                                                                                            */
+/* Plan layout (int32, built by pkv_decode_plan, read by the kernels): header[16] = {magic,    */
+/* B, H, GS, U, M, L, cells, chunk, 0...}, skip[B], blocks[B] (ceil(n/16) when planned),       */
+/* sh_ptr[B+1], units[U][6] = {ref_seq, b0, b1, member_off, member_cnt, cell_base},             */
+/* members[M], sh_list[L]. H / GS are the stream kernel's head slots and q heads per slot     */
+/* (pkv_decode_kernel: matrix-core -> Hkv, G; vector -> Hq, 1); a plan is tied to them and to  */
+/* B, so build it after choosing the kernel.                                                   */
+
+/* Upper bound on the int32 entries of a plan for B sequences of up to max_blocks blocks.     */
+size_t pkv_decode_plan_max_ints(int32_t B, int32_t max_blocks);
+
+/* Host only (no GPU). block_tables/context_lens: host int32 [B][max_blocks] / [B] (the same   */
+/* contents the device copies will hold). plan: host buffer of capacity ints; *plan_ints      */
+/* receives the plan's size (also when capacity is too small: PKV_ERR_WORKSPACE). Errors:      */
+/* PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED (dtype), PKV_ERR_WORKSPACE.                        */
+pkv_status pkv_decode_plan(const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                           int32_t max_blocks, int32_t max_context_len, int32_t Hq, int32_t Hkv,
+                           int32_t NB, pkv_dtype dtype, int32_t* plan, size_t capacity,
+                           size_t* plan_ints);
+
+/* Workspace bytes of pkv_decode_planned (stream cells plus B*H private and the plan's shared   */
+/* cells); 0 on bad arguments or a plan built for another shape.                              */
+size_t pkv_decode_planned_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t hd,
+                                          pkv_dtype dtype, int32_t num_workers,
+                                          const int32_t* plan, size_t plan_ints);
+
+/* The planned decode step. pass: 0 all three kernels in order, 1 the shared pass, 2 the       */
+/* stream pass, 3 the merge (run 1, 2, 3 in that order on one stream; exported to time them). */
+/* k_new/v_new NULL: attention as pkv_decode_attn; non-NULL: the fused step of                 */
+/* pkv_decode_append_attn (same contract; additionally no sequence's newest-token block may be */
+/* in a run, which the plan check enforces through blocks[] and skip[]). plan_host and        */
+/* plan_dev hold the same plan_ints entries (host, validated here; device, read by the        */
+/* kernels); context_lens and the tables must be those the plan was built from.                */
+/* num_workers as pkv_decode_stream. Errors: as pkv_decode_append_attn, plus                   */
+/* PKV_ERR_INVALID_ARG for a plan that fails the check or does not match the shapes.          */
+pkv_status pkv_decode_planned(int32_t pass, void* out, const void* q, const void* k_new,
+                              const void* v_new, void* k_cache, void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                              int32_t Hq, int32_t Hkv, int32_t hd, int32_t bs, int32_t NB,
+                              int32_t max_blocks, int32_t max_context_len, float scale,
+                              pkv_dtype dtype, const int32_t* plan_host, const int32_t* plan_dev,
+                              size_t plan_ints, int32_t num_workers, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* Workspace bytes pkv_decode_attn needs for this shape on the current device (0 if B == 0 or */
 /* the arguments are invalid).                                                                 */
 size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t hd,

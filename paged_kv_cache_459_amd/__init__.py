@@ -10,6 +10,8 @@ from .api import (BLOCK_SIZE, BlockAllocator, alloc_caches, cache_bytes,  # noqa
                   cache_shapes, pkv_copy_blocks, pkv_decode_append_attn, pkv_decode_append_merge,
                   pkv_decode_append_stream,
                   pkv_decode_attn, pkv_decode_kernel, pkv_decode_merge,
-                  pkv_decode_num_workers, pkv_decode_stream, pkv_decode_stream_workspace_bytes,
+                  pkv_decode_num_workers, pkv_decode_plan, pkv_decode_planned,
+                  pkv_decode_planned_workspace_bytes, pkv_decode_stream,
+                  pkv_decode_stream_workspace_bytes,
                   pkv_decode_workspace_bytes, pkv_dtype, pkv_set_attn_kernel, pkv_write,
                   split_workspace)

@@ -263,6 +263,65 @@ def pkv_decode_append_merge(out, k_new, v_new, k_cache, v_cache, block_tables, c
     return out
 
 
+def pkv_decode_plan(block_tables, context_lens, *, num_q_heads, num_kv_heads, num_blocks,
+                    max_context_len, dtype, out=None):
+    """Shared-prefix plan of a batch from HOST copies of its tables [B, max_blocks] and lengths
+    [B] (int32; table entries may carry BLOCK_SHARED). Returns an int32 NumPy array (a view of
+    ``out`` when that is large enough)."""
+    t = _as_c(block_tables, np.int32)
+    lens = _as_c(context_lens, np.int32)
+    if t.ndim != 2 or lens.shape != (t.shape[0],):
+        raise ValueError("block_tables must be [B, max_blocks] and context_lens [B]")
+    B, mb = t.shape
+    n = ctypes.c_size_t(0)
+    for _ in range(2):
+        cap = 0 if out is None else int(out.size)
+        st = lib.pkv_decode_plan(t.ctypes.data, lens.ctypes.data, B, mb, int(max_context_len),
+                                 num_q_heads, num_kv_heads, int(num_blocks), pkv_dtype(dtype),
+                                 out.ctypes.data if out is not None else None, cap,
+                                 ctypes.byref(n))
+        if st == 0:
+            return out[:n.value]
+        if st != 6:  # anything but a too-small buffer
+            check(st, "pkv_decode_plan")
+        out = np.empty(n.value, np.int32)
+    raise RuntimeError("pkv_decode_plan: plan size changed between calls")
+
+
+def pkv_decode_planned_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, dtype,
+                                       num_workers, plan):
+    p = _as_c(plan, np.int32)
+    return int(lib.pkv_decode_planned_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,
+                                                      pkv_dtype(dtype), num_workers,
+                                                      p.ctypes.data, p.size))
+
+
+def pkv_decode_planned(q, k_cache, v_cache, block_tables, context_lens, plan, plan_dev, *,
+                       num_kv_heads, scale, max_context_len, num_workers, workspace,
+                       k_new=None, v_new=None, out=None, passes=0):
+    """Decode step with a shared-prefix plan (see include/pkv.h). plan: the host plan (NumPy
+    int32), plan_dev: the same ints on the device (int32 tensor). With k_new / v_new it is the
+    fused newest-token step. passes: 0 all, 1 shared pass, 2 stream pass, 3 merge."""
+    out, B, hq, hd, nb, mb = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
+                                          num_kv_heads, out)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        _new_args(q, k_new, v_new, num_kv_heads)
+    p = _as_c(plan, np.int32)
+    _need(plan_dev, "plan_dev", dtype=torch.int32, device=q.device)
+    if plan_dev.numel() < p.size:
+        raise ValueError("plan_dev is shorter than the plan")
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check(lib.pkv_decode_planned(int(passes), _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                 _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                 _ptr(context_lens), B, hq, num_kv_heads, hd, BLOCK_SIZE, nb, mb,
+                                 max_context_len, float(scale), pkv_dtype(q), p.ctypes.data,
+                                 _ptr(plan_dev), p.size, num_workers, _ptr(workspace), ws_bytes,
+                                 _stream(q.device)), "pkv_decode_planned")
+    return out
+
+
 def split_workspace(workspace, batch, num_q_heads, num_kv_heads, head_dim, num_workers, kernel):
     """Views (seg int32 [B+1], ml float32 [W, 2, GS, 2], o float32 [W, 2, GS, hd]) of a stream
     workspace, for the kernel the stream pass used (1 vector, 2 matrix core)."""

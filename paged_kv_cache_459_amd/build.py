@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libpkv.so")
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 HIP_SOURCES = ["pkv_attn.hip", "pkv_write.hip"]
-HOST_SOURCES = ["pkv_api.cpp", "pkv_alloc.cpp"]
+HOST_SOURCES = ["pkv_api.cpp", "pkv_alloc.cpp", "pkv_plan.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result", f"-I{INCLUDE}"]
 # Code-object v5: the library runs inside PyTorch's bundled HIP runtime, which can be older than

@@ -68,12 +68,13 @@ struct Layout {
   size_t seg, ml, bytes;  // byte offsets of the (m, l) and o arrays; total size
 };
 
+// extra: cells past the workers' 2W (a plan's B*H private cells plus its shared cells).
 Layout stream_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t hd, int32_t kernel,
-                     int32_t W) {
+                     int32_t W, int64_t extra = 0) {
   Layout L{};
   L.H = kernel == pkv::kMatrix ? Hkv : Hq;
   L.GS = kernel == pkv::kMatrix ? Hq / Hkv : 1;
-  const size_t cells = static_cast<size_t>(W) * 2 * L.GS;
+  const size_t cells = (static_cast<size_t>(W) * 2 + static_cast<size_t>(extra)) * L.GS;
   L.seg = round_up256(static_cast<size_t>(B + 1) * sizeof(int32_t));
   L.ml = L.seg + round_up256(cells * 2 * sizeof(float));
   L.bytes = L.ml + cells * hd * sizeof(float);
@@ -279,6 +280,110 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, con
   }
   pkv::CopyParams p{k_cache, v_cache, src, dst, n, Hkv, hd, NB};
   return pkv::launch_copy_blocks(p, dtype, hs) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+size_t pkv_decode_plan_max_ints(int32_t B, int32_t max_blocks) {
+  if (B < 0 || max_blocks <= 0) return 0;
+  return pkv::kPlanHeader + 3 * static_cast<size_t>(B) + 1 +
+         static_cast<size_t>(pkv::kUnitInts + 2) * B * max_blocks;
+}
+
+pkv_status pkv_decode_plan(const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                           int32_t max_blocks, int32_t max_context_len, int32_t Hq, int32_t Hkv,
+                           int32_t NB, pkv_dtype dtype, int32_t* plan, size_t capacity,
+                           size_t* plan_ints) {
+  if (!dtype_ok(dtype)) return PKV_ERR_UNSUPPORTED;
+  if (B < 0 || B > kMaxBatch || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_blocks <= 0 ||
+      NB <= 0 || max_context_len < 0 ||
+      static_cast<int64_t>(max_blocks) * kBlockSize < max_context_len || !plan_ints)
+    return PKV_ERR_INVALID_ARG;
+  if (B > 0 && (!block_tables || !context_lens)) return PKV_ERR_INVALID_ARG;
+  const int32_t G = Hq / Hkv;
+  const int32_t kernel = current_kernel(dtype, Hq, Hkv);
+  const int32_t H = kernel == pkv::kMatrix ? Hkv : Hq;
+  const int32_t GS = kernel == pkv::kMatrix ? G : 1;
+  const bool share = dtype != PKV_F32 && G <= pkv::kRowsPerTile;  // the shared pass's reach
+  std::vector<int32_t> v;
+  pkv::plan_build(block_tables, context_lens, B, max_blocks, max_context_len, NB, H, GS, G,
+                  pkv::kPlanChunk, share, &v);
+  *plan_ints = v.size();
+  if (!plan || capacity < v.size()) return PKV_ERR_WORKSPACE;
+  std::memcpy(plan, v.data(), v.size() * sizeof(int32_t));
+  return PKV_OK;
+}
+
+size_t pkv_decode_planned_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t hd,
+                                          pkv_dtype dtype, int32_t num_workers,
+                                          const int32_t* plan, size_t plan_ints) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || !dtype_ok(dtype) || !head_dim_ok(hd) ||
+      num_workers <= 0 || num_workers % pkv::kWaves != 0 || !plan ||
+      plan_ints < static_cast<size_t>(pkv::kPlanHeader))
+    return 0;
+  const int32_t kernel = current_kernel(dtype, Hq, Hkv);
+  const Layout L0 = stream_layout(B, Hq, Hkv, hd, kernel, num_workers);
+  if (plan[0] != pkv::kPlanMagic || plan[1] != B || plan[2] != L0.H || plan[3] != L0.GS ||
+      plan[7] < 0)
+    return 0;
+  const int64_t extra = static_cast<int64_t>(B) * L0.H + plan[7];
+  return stream_layout(B, Hq, Hkv, hd, kernel, num_workers, extra).bytes;
+}
+
+pkv_status pkv_decode_planned(int32_t pass, void* out, const void* q, const void* k_new,
+                              const void* v_new, void* k_cache, void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                              int32_t Hq, int32_t Hkv, int32_t hd, int32_t bs, int32_t NB,
+                              int32_t max_blocks, int32_t max_context_len, float scale,
+                              pkv_dtype dtype, const int32_t* plan_host, const int32_t* plan_dev,
+                              size_t plan_ints, int32_t num_workers, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (pass < 0 || pass > 3) return PKV_ERR_INVALID_ARG;
+  pkv_status st = validate_decode(out, q, k_cache, v_cache, block_tables, context_lens, B, Hq,
+                                  Hkv, hd, bs, NB, max_blocks, max_context_len, scale, dtype);
+  if (st != PKV_OK) return st;
+  if ((k_new == nullptr) != (v_new == nullptr)) return PKV_ERR_INVALID_ARG;
+  if (k_new && B > 0 && (!aligned16(k_new) || !aligned16(v_new))) return PKV_ERR_INVALID_ARG;
+  if (num_workers <= 0 || num_workers % pkv::kWaves != 0) return PKV_ERR_INVALID_ARG;
+  if (B == 0) return PKV_OK;
+  const int32_t W = num_workers;
+  const int32_t G = Hq / Hkv;
+  const int32_t kernel = current_kernel(dtype, Hq, Hkv);
+  const Layout L0 = stream_layout(B, Hq, Hkv, hd, kernel, W);
+  if (!stream_fits(B, max_blocks, L0.H, W)) return PKV_ERR_UNSUPPORTED;
+  if (!plan_host || !plan_dev || (reinterpret_cast<uintptr_t>(plan_dev) & 3u))
+    return PKV_ERR_INVALID_ARG;
+  pkv::PlanView pv;
+  if (!pkv::plan_check(plan_host, plan_ints, B, max_blocks, L0.H, L0.GS, G, k_new != nullptr,
+                       &pv))
+    return PKV_ERR_INVALID_ARG;
+  if (pv.U > 0 && (dtype == PKV_F32 || G > pkv::kRowsPerTile)) return PKV_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(pv.U) * Hkv >= (int64_t{1} << 31) - pkv::kWaves * 8)
+    return PKV_ERR_UNSUPPORTED;
+  const Layout L = stream_layout(B, Hq, Hkv, hd, kernel, W, static_cast<int64_t>(B) * L0.H + pv.cells);
+  if (!workspace || workspace_bytes < L.bytes) return PKV_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PKV_ERR_INVALID_ARG;
+  auto hs = static_cast<hipStream_t>(stream);
+  if (check_mode()) {
+    st = check_decode_indices(block_tables, context_lens, B, NB, max_blocks, max_context_len, hs);
+    if (st != PKV_OK) return st;
+  }
+  pkv::StreamParams p = make_params(out, q, k_new, v_new, k_cache, v_cache, block_tables,
+                                    context_lens, B, Hq, Hkv, hd, NB, max_blocks,
+                                    max_context_len, scale, W, L, workspace);
+  const int32_t* base = plan_dev + pkv::kPlanHeader;
+  p.skip = base;
+  p.sh_ptr = base + 2 * static_cast<size_t>(B);
+  p.units = p.sh_ptr + B + 1;
+  p.members = p.units + static_cast<size_t>(pv.U) * pkv::kUnitInts;
+  p.sh_list = p.members + plan_host[5];
+  p.num_units = pv.U;
+  p.shared_cells = pv.cells;
+  if ((pass == 0 || pass == 1) && pkv::launch_shared(p, dtype, kernel, hs) != hipSuccess)
+    return PKV_ERR_HIP;
+  if ((pass == 0 || pass == 2) && pkv::launch_stream(p, dtype, kernel, hs) != hipSuccess)
+    return PKV_ERR_HIP;
+  if ((pass == 0 || pass == 3) && pkv::launch_merge(p, dtype, kernel, hs) != hipSuccess)
+    return PKV_ERR_HIP;
+  return PKV_OK;
 }
 
 int32_t pkv_decode_kernel(int32_t Hq, int32_t Hkv, pkv_dtype dtype) {

@@ -263,15 +263,18 @@ __device__ __forceinline__ int clamp_len(const StreamParams& p, int i) {
 
 // ---- Stream geometry ----------------------------------------------------------------------
 
-// Exclusive prefix sums of the per-sequence block counts c_i = ceil(n_i/16) into
-// pref[0..B]; pref[B] = C, the tiles of one head slot. Whole work-group; ends synchronised.
+// Exclusive prefix sums of the per-sequence block counts c_i = ceil(n_i/16) - skip_i (the
+// blocks after those a shared-prefix plan covers) into pref[0..B]; pref[B] = C, the tiles of
+// one head slot. Whole work-group; ends synchronised.
 __device__ void scan_block_counts(const StreamParams& p, int* pref) {
   __shared__ int s_wsum[kWaves];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int carry = 0;
   for (int base = 0; base < p.B; base += kThreads) {
     const int i = base + threadIdx.x;
-    const int c = i < p.B ? (clamp_len(p, i) + kBlockSize - 1) / kBlockSize : 0;
+    const int c = i < p.B ? max(0, (clamp_len(p, i) + kBlockSize - 1) / kBlockSize -
+                                     (p.skip != nullptr ? p.skip[i] : 0))
+                          : 0;
     int x = c;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -308,13 +311,17 @@ __device__ __forceinline__ int find_seq(const int* pref, int B, int r) {
 struct TileInfo {
   int id;   // physical block to read (0 when the table entry is outside the pool)
   int seq;  // sequence i
-  int hm;   // head slot << 16 | shared << 10 | last << 9 | slot << 8 | whole << 7 | end << 6 |
-            // start << 5 | valid tokens; last: the sequence's final block (holds its newest
-            // token); shared: the table entry carries the shared-block mark
+  int hm;   // head slot << 16 | piece << 11 | shared << 10 | last << 9 | slot << 8 |
+            // whole << 7 | end << 6 | start << 5 | valid tokens; last: the sequence's final
+            // block (holds its newest token); shared: the table entry carries the shared-block
+            // mark; piece: the sequence has shared-pass pieces, so even a whole segment leaves
+            // a piece (in its own cell) for the merge
 };
-constexpr int kStart = 1 << 5, kEnd = 1 << 6, kWhole = 1 << 7, kLast = 1 << 9, kShared = 1 << 10;
+constexpr int kStart = 1 << 5, kEnd = 1 << 6, kWhole = 1 << 7, kLast = 1 << 9, kShared = 1 << 10,
+              kPiece = 1 << 11;
 
-// Stream position t -> tile of segment (i, h): head-major order, t = h*C + pref[i] + j.
+// Stream position t -> tile of segment (i, h): head-major order, t = h*C + pref[i] + j; table
+// index j + skip_i.
 __device__ __forceinline__ TileInfo tile_info(const StreamParams& p, const int* pref, int C,
                                               int t, int t0, int t1) {
   const int h = t / C;
@@ -324,8 +331,9 @@ __device__ __forceinline__ TileInfo tile_info(const StreamParams& p, const int* 
   const int c = pref[i + 1] - pref[i];
   const int seg0 = h * C + pref[i];
   const int n = clamp_len(p, i);
-  int valid = min(kBlockSize, n - kBlockSize * j);
-  const int raw = p.block_tables[static_cast<size_t>(i) * p.max_blocks + j];
+  const int sk = p.skip != nullptr ? p.skip[i] : 0;
+  int valid = min(kBlockSize, n - kBlockSize * (j + sk));
+  const int raw = p.block_tables[static_cast<size_t>(i) * p.max_blocks + j + sk];
   const int shared = raw >= 0 && (raw & kSharedBit) ? 1 : 0;
   int id = raw & ~kSharedBit;
   if (raw < 0 || id >= p.NB) {
@@ -337,8 +345,9 @@ __device__ __forceinline__ TileInfo tile_info(const StreamParams& p, const int* 
   const int whole = (seg0 >= t0) && (seg0 + c <= t1);
   const int slot = seg0 <= t0 ? 0 : 1;
   const int last = j == c - 1;
-  return TileInfo{id, i, (h << 16) | (shared << 10) | (last << 9) | (slot << 8) | (whole << 7) |
-                             (end << 6) | (start << 5) | valid};
+  const int piece = sk > 0 ? 1 : 0;
+  return TileInfo{id, i, (h << 16) | (piece << 11) | (shared << 10) | (last << 9) | (slot << 8) |
+                             (whole << 7) | (end << 6) | (start << 5) | valid};
 }
 
 // This wave's worker index and tile range [t0, t1). Work-group b runs on XCD b % 8; logical
@@ -358,14 +367,15 @@ __device__ __forceinline__ Range worker_range(const StreamParams& p, int C, int 
   return Range{worker, t0, t1};
 }
 
-// Work-group 0 publishes the prefix sums for the merge pass and zeroes rows with n = 0.
+// Work-group 0 publishes the prefix sums for the merge pass and zeroes rows with n = 0 (a
+// planned sequence with no private block is finished by the merge).
 template <int DT>
 __device__ void publish_and_zero(const StreamParams& p, const int* pref) {
   if (blockIdx.x != 0) return;
   for (int i = threadIdx.x; i <= p.B; i += kThreads) p.ws_seg[i] = pref[i];
   const int row = p.Hq * p.hd;
   for (int i = 0; i < p.B; ++i) {
-    if (pref[i + 1] != pref[i]) continue;
+    if (clamp_len(p, i) != 0) continue;
     for (int e = threadIdx.x; e < row; e += kThreads)
       Elem<DT>::put(p.out, static_cast<size_t>(i) * row + e, 0.f);
   }
@@ -538,15 +548,18 @@ attn_vector_kernel(const StreamParams p) {
           if constexpr (LPR >= 4) a += dpp<kQuadSwap2>(a);
           acc[j] = a;
         }
-        if (hm & kWhole) {  // the whole segment was ours: final output row
+        if ((hm & kWhole) && !(hm & kPiece)) {  // the whole segment was ours: final output row
           if (vsub == 0) {
             const size_t row = (static_cast<size_t>(seq) * p.Hq + h) * HD;
 #pragma unroll
             for (int j = 0; j < NL; ++j)
               E::put(p.out, row + VROWS * j + lane / LPR, l > 0.f ? acc[j] / l : 0.f);
           }
-        } else {  // a piece of a segment shared with neighbouring workers
-          const size_t cell = static_cast<size_t>(rg.worker) * 2 + ((hm >> 8) & 1);
+        } else {  // a piece: of a segment shared with neighbouring workers, or of a planned one
+          const size_t cell =
+              (hm & kWhole) ? 2 * static_cast<size_t>(p.num_workers) +
+                                  static_cast<size_t>(seq) * p.Hq + h
+                            : static_cast<size_t>(rg.worker) * 2 + ((hm >> 8) & 1);
           if (vsub == 0) {
 #pragma unroll
             for (int j = 0; j < NL; ++j) p.ws_o[cell * HD + VROWS * j + lane / LPR] = acc[j];
@@ -763,7 +776,7 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_matrix_kernel(const StreamParams p)
       if (hm & kEnd) {  // last tile of the segment in this range: emit
         float l = lsum + __shfl_xor(lsum, 16);
         l += __shfl_xor(l, 32);
-        if (hm & kWhole) {  // the whole segment was ours: final output rows
+        if ((hm & kWhole) && !(hm & kPiece)) {  // the whole segment was ours: final output rows
           if (hq < G) {
             const size_t row = (static_cast<size_t>(seq) * p.Hq + kvh * G + hq) * HD;
 #pragma unroll
@@ -773,8 +786,11 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_matrix_kernel(const StreamParams p)
                 Elem<DT>::put(p.out, row + 16 * j + 4 * g + e, l > 0.f ? o[j][e] / l : 0.f);
             }
           }
-        } else if (hq < G) {  // a piece of a segment shared with neighbouring workers
-          const size_t cell = (static_cast<size_t>(rg.worker) * 2 + ((hm >> 8) & 1)) * G + hq;
+        } else if (hq < G) {  // a piece: of a segment cut between workers, or of a planned one
+          const size_t c0 = (hm & kWhole) ? 2 * static_cast<size_t>(p.num_workers) +
+                                                static_cast<size_t>(seq) * p.Hkv + kvh
+                                          : static_cast<size_t>(rg.worker) * 2 + ((hm >> 8) & 1);
+          const size_t cell = c0 * G + hq;
 #pragma unroll
           for (int j = 0; j < VT; ++j)
             *reinterpret_cast<float4_t*>(p.ws_o + cell * HD + 16 * j + 4 * g) = o[j];
@@ -790,6 +806,166 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_matrix_kernel(const StreamParams p)
     load_v(0);
     for (int k = 0; k + 1 < cnt; ++k) step(k, std::true_type{});
     step(cnt - 1, std::false_type{});
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Shared pass of a shared-prefix plan (f16/bf16, G <= 16). A unit is (a run's chunk of logical
+// blocks [b0, b1), up to 16/G of the run's members); its blocks are the same physical blocks
+// in every member's table, so one wave per (unit, kv head) reads each K/V tile once and
+// computes the attention piece of all of the unit's rows at once: row r = member r / G, q head
+// kvh*G + r % G. The arithmetic is the matrix-core kernel's (S^T = K Q^T, O^T += V^T P^T, P in
+// lanes), with one difference: each row masks the tokens at or past its own sequence's length
+// (members may end inside a shared, partly filled block). V tokens past every row's length are
+// zeroed (unused slots may hold anything). Tiles are read with cached loads: other units of
+// the same chunk (the next members, on the next waves) read them too.
+//
+// Waves map to (kv head, unit) unit-fastest, and work-groups are laid XCD-contiguously, so the
+// member tiles of one chunk run side by side on one XCD. Each row's (m, l, o) goes to its cell:
+// 2W + B*H + cell_base + member*H + head slot, row (q head % GS), in the stream pass's layout.
+template <int DT, int HD>
+__global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(3))) attn_shared_kernel(const StreamParams p, int H, int GS) {
+  using M16 = Mfma<DT>;
+  constexpr int TILE = HD * kBlockSize * 2;
+  constexpr int KS = HD / 32;  // QK steps
+  constexpr int VT = HD / 16;  // PV dim tiles
+
+  const int grid = gridDim.x, b = blockIdx.x;
+  const int lwg = (grid % 8 == 0) ? (b % 8) * (grid / 8) + b / 8 : b;
+  const int gw = lwg * kWaves + uniform(threadIdx.x >> 6);
+  const int U = p.num_units;
+  if (gw >= U * p.Hkv) return;
+  const int kvh = gw / U, u = gw - kvh * U;
+  const int32_t* e = p.units + static_cast<size_t>(u) * kUnitInts;
+  const int ref = uniform(e[0]), b0 = uniform(max(e[1], 0)), b1 = uniform(min(e[2], p.max_blocks));
+  const int moff = uniform(e[3]), mcnt = uniform(e[4]), cbase = uniform(e[5]);
+  if (ref < 0 || ref >= p.B || b0 >= b1) return;
+
+  const int lane = threadIdx.x & 63;
+  const int G = p.Hq / p.Hkv;
+  const int hq = lane & 15, g = lane >> 4;
+  const int mk = hq / G, jq = hq - mk * G;  // this lane's row: member mk, q head kvh*G + jq
+  int seq = -1;
+  if (hq < mcnt * G) seq = p.members[moff + mk];
+  const bool row_ok = seq >= 0 && seq < p.B;
+  const int n_row = row_ok ? clamp_len(p, seq) : 0;
+  // the rows' shortest and longest lengths: a tile ending at or before the shortest needs no
+  // masking; V tokens at or past the longest are read by no row
+  int nmin = row_ok ? n_row : 0x7fffffff, nmax = n_row;
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) {
+    nmin = min(nmin, __shfl_xor(nmin, off));
+    nmax = max(nmax, __shfl_xor(nmax, off));
+  }
+  nmin = uniform(nmin);
+  nmax = uniform(nmax);
+
+  const uint32_t k_lane = 16u * lane;
+  const uint32_t v_lane = 32u * hq + 8u * g;
+  const size_t blk_stride = static_cast<size_t>(p.Hkv) * TILE;
+  const int32_t* table = p.block_tables + static_cast<size_t>(ref) * p.max_blocks;
+
+  uint4 qb[KS];
+  if (row_ok) {
+    const uint4* qp = reinterpret_cast<const uint4*>(
+        static_cast<const char*>(p.q) + (static_cast<size_t>(seq) * p.Hq + kvh * G + jq) * HD * 2);
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) qb[s2] = qp[4 * s2 + g];
+  } else {
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) qb[s2] = make_uint4(0, 0, 0, 0);
+  }
+  float m = kNegInf, lsum = 0.f;
+  float4_t o[VT];
+#pragma unroll
+  for (int j = 0; j < VT; ++j) o[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+  uint4 kr[KS];
+  uint2 vr[VT];
+
+  // block t's id, or -1 when its entry names no block of the pool (then nothing of it counts)
+  auto block_id = [&](int t) {
+    const int raw = uniform(table[t]);
+    const int id = raw & ~kSharedBit;
+    return (raw < 0 || id >= p.NB) ? -1 : id;
+  };
+  auto load_k = [&](int id) {
+    const char* kt = static_cast<const char*>(p.k_cache) + static_cast<size_t>(max(id, 0)) * blk_stride +
+                     static_cast<size_t>(kvh) * TILE;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) kr[s2] = *reinterpret_cast<const uint4*>(kt + k_lane + 1024u * s2);
+  };
+  auto load_v = [&](int id) {
+    const char* vt = static_cast<const char*>(p.v_cache) + static_cast<size_t>(max(id, 0)) * blk_stride +
+                     static_cast<size_t>(kvh) * TILE;
+#pragma unroll
+    for (int j = 0; j < VT; ++j) vr[j] = *reinterpret_cast<const uint2*>(vt + v_lane + 512u * j);
+  };
+
+  int id = block_id(b0);
+  load_k(id);
+  load_v(id);
+  for (int t = b0; t < b1; ++t) {
+    const int next = t + 1 < b1 ? block_id(t + 1) : -1;
+    const bool full = id >= 0 && kBlockSize * (t + 1) <= nmin;  // every row sees all 16 tokens
+    const int row_valid = id < 0 ? 0 : min(kBlockSize, max(0, n_row - kBlockSize * t));
+    float4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) sacc = M16::qk(pinned(kr[s2]), qb[s2], sacc);
+    if (t + 1 < b1) load_k(next);
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[i] = sacc[i] * p.scale_log2;
+      if (!full) sc[i] = (4 * g + i < row_valid) ? sc[i] : kNegInf;
+    }
+    float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float m_new = fmaxf(m, bm);
+    float alpha = exp2_fast(m - m_new);
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(sc[i] - m_new);
+    if (!full) {  // partly masked rows (or a row with nothing valid yet)
+      alpha = m_new == kNegInf ? 1.f : alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = (4 * g + i < row_valid) ? pr[i] : 0.f;
+    }
+    lsum = fmaf(lsum, alpha, (pr[0] + pr[1]) + (pr[2] + pr[3]));
+    m = m_new;
+    const uint2 pb = make_uint2(M16::pack2(pr[0], pr[1]), M16::pack2(pr[2], pr[3]));
+    uint2 vt[VT];
+#pragma unroll
+    for (int j = 0; j < VT; ++j) vt[j] = pinned(vr[j]);
+    if (!full) {  // zero the V tokens no row reads
+      const int tv = id < 0 ? 0 : min(kBlockSize, max(0, nmax - kBlockSize * t));
+      const int base = 4 * g;
+      const uint32_t mx = (base + 0 < tv ? 0x0000FFFFu : 0u) | (base + 1 < tv ? 0xFFFF0000u : 0u);
+      const uint32_t my = (base + 2 < tv ? 0x0000FFFFu : 0u) | (base + 3 < tv ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int j = 0; j < VT; ++j) vt[j] = make_uint2(vt[j].x & mx, vt[j].y & my);
+    }
+#pragma unroll
+    for (int j = 0; j < VT; ++j) o[j] = M16::pv(vt[j], pb, o[j] * alpha);
+    if (t + 1 < b1) load_v(next);
+    id = next;
+  }
+  float l = lsum + __shfl_xor(lsum, 16);
+  l += __shfl_xor(l, 32);
+  if (!row_ok) return;
+  const int qh = kvh * G + jq;
+  const int slot = qh / GS, nr = qh - slot * GS;
+  const int rel = cbase + mk * H + slot;
+  if (rel < 0 || rel >= p.shared_cells) return;
+  const size_t cell = (2 * static_cast<size_t>(p.num_workers) + static_cast<size_t>(p.B) * H +
+                       static_cast<size_t>(rel)) * GS + nr;
+#pragma unroll
+  for (int j = 0; j < VT; ++j)
+    *reinterpret_cast<float4_t*>(p.ws_o + cell * HD + 16 * j + 4 * g) = o[j];
+  if (g == 0) {
+    p.ws_ml[cell * 2] = m;
+    p.ws_ml[cell * 2 + 1] = l;
   }
 }
 
@@ -833,6 +1009,9 @@ __device__ void store_new_token(const StreamParams& p, int i, int h) {
 // weighted in parallel; o is accumulated over the pieces in worker order (deterministic),
 // with the loads of consecutive pieces issued back to back. Rows of segments inside one
 // range, and rows with n = 0, were finished by the stream pass and are left alone.
+// With a shared-prefix plan, a planned sequence's row always merges here: its private pieces
+// (the workers' cells, or its own cell when one worker held the segment whole; none when all
+// of its blocks are shared) come first, then its shared-pass pieces in plan order.
 template <int DT, int HD>
 __global__ void __launch_bounds__(64)
 merge_kernel(const StreamParams p, int H, int GS) {
@@ -840,21 +1019,49 @@ merge_kernel(const StreamParams p, int H, int GS) {
   const int i = blockIdx.x, hh = blockIdx.y, lane = threadIdx.x;
   if (p.k_new != nullptr && hh % (p.Hq / p.Hkv) == 0) store_new_token<DT, HD>(p, i, hh / (p.Hq / p.Hkv));
   const int h = hh / GS, n = hh - h * GS;
+  const bool planned = p.skip != nullptr && p.skip[i] > 0;
   const int C = p.ws_seg[p.B];
   const int s0 = p.ws_seg[i];
   const int c = p.ws_seg[i + 1] - s0;
-  if (c == 0) return;
-  const int T = H * C;
-  const int per = (T + p.num_workers - 1) / p.num_workers;
-  const int tb = h * C + s0, te = tb + c;
-  const int wf = tb / per, wl = (te - 1) / per;
-  if (wf == wl) return;
-  const int np = wl - wf + 1;
-  // cell of piece k (worker wf + k): slot 1 only for the first worker if the segment starts
-  // inside its range after other segments
-  const int slot0 = wf * per < tb ? 1 : 0;
-  auto cell = [&](int k) {
-    return (static_cast<size_t>(wf + k) * 2 + (k == 0 ? slot0 : 0)) * GS + n;
+  int np_priv = 0, wf = 0, slot0 = 0;
+  bool own_cell = false;
+  if (c > 0) {
+    const int T = H * C;
+    const int per = (T + p.num_workers - 1) / p.num_workers;
+    const int tb = h * C + s0, te = tb + c;
+    wf = tb / per;
+    const int wl = (te - 1) / per;
+    if (wf == wl) {
+      if (!planned) return;
+      np_priv = 1;
+      own_cell = true;
+    } else {
+      np_priv = wl - wf + 1;
+      // cell of piece k (worker wf + k): slot 1 only for the first worker if the segment
+      // starts inside its range after other segments
+      slot0 = wf * per < tb ? 1 : 0;
+    }
+  } else if (!planned) {
+    return;
+  }
+  int sp0 = 0, nsh = 0;
+  if (planned) {
+    sp0 = p.sh_ptr[i];
+    nsh = p.sh_ptr[i + 1] - sp0;
+  }
+  const int np = np_priv + nsh;
+  const size_t wcells = 2 * static_cast<size_t>(p.num_workers);
+  const size_t shared0 = wcells + static_cast<size_t>(p.B) * H;
+  auto cell = [&](int k) -> size_t {
+    size_t c0;
+    if (k < np_priv) {
+      c0 = own_cell ? wcells + static_cast<size_t>(i) * H + h
+                    : static_cast<size_t>(wf + k) * 2 + (k == 0 ? slot0 : 0);
+    } else {  // a shared-pass piece (index kept inside the shared cells)
+      const int e = min(max(p.sh_list[sp0 + k - np_priv], 0), p.shared_cells - H);
+      c0 = shared0 + static_cast<size_t>(e) + h;
+    }
+    return c0 * GS + n;
   };
   constexpr int U = 16;  // pieces whose o loads are in flight together
   float M = kNegInf;
@@ -932,6 +1139,19 @@ void launch_stream_t(const StreamParams& p, int32_t kernel, dim3 grid, size_t ld
 }
 
 template <int DT>
+void launch_shared_t(const StreamParams& p, int H, int GS, hipStream_t stream) {
+  const int64_t waves = static_cast<int64_t>(p.num_units) * p.Hkv;
+  int64_t grid = (waves + kWaves - 1) / kWaves;
+  grid = (grid + 7) / 8 * 8;  // a multiple of 8 for the XCD-contiguous mapping
+  if (p.hd == 64)
+    hipLaunchKernelGGL((attn_shared_kernel<DT, 64>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kThreads), 0, stream, p, H, GS);
+  else
+    hipLaunchKernelGGL((attn_shared_kernel<DT, 128>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kThreads), 0, stream, p, H, GS);
+}
+
+template <int DT>
 void launch_merge_t(const StreamParams& p, int H, int GS, hipStream_t stream) {
   const dim3 grid(p.B, H * GS);
   if (p.hd == 64)
@@ -997,6 +1217,20 @@ hipError_t launch_stream(const StreamParams& p, int32_t dtype, int32_t kernel,
   }
   return note_error(kernel == kMatrix ? "attn_matrix_kernel launch" : "attn_vector_kernel launch",
                     hipGetLastError());
+}
+
+hipError_t launch_shared(const StreamParams& p, int32_t dtype, int32_t kernel,
+                         hipStream_t stream) {
+  if (p.num_units == 0) return hipSuccess;
+  (void)hipGetLastError();
+  const int H = kernel == kMatrix ? p.Hkv : p.Hq;
+  const int GS = kernel == kMatrix ? p.Hq / p.Hkv : 1;
+  switch (dtype) {
+    case 1: launch_shared_t<1>(p, H, GS, stream); break;
+    case 2: launch_shared_t<2>(p, H, GS, stream); break;
+    default: return note_error("attn_shared_kernel (f16/bf16 only)", hipErrorInvalidValue);
+  }
+  return note_error("attn_shared_kernel launch", hipGetLastError());
 }
 
 hipError_t launch_merge(const StreamParams& p, int32_t dtype, int32_t kernel,

@@ -6,6 +6,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <vector>
 
 namespace pkv {
 
@@ -16,6 +17,29 @@ constexpr int kWaves = 4;       // waves per work-group of the attention stream 
 constexpr int32_t kSharedBit = 0x40000000;
 
 enum AttnKernel : int32_t { kAuto = 0, kVector = 1, kMatrix = 2 };
+
+// Shared-prefix plans (pkv_plan.cpp): packed int32 arrays, layout documented in pkv.h.
+constexpr int32_t kPlanMagic = 0x504C4E31;
+constexpr int kPlanHeader = 16;
+constexpr int kUnitInts = 6;      // ref_seq, b0, b1, member_off, member_cnt, cell_base
+constexpr int kRowsPerTile = 16;  // rows of one MFMA tile of the shared pass
+constexpr int kPlanChunk = 16;    // blocks per unit of a run
+
+struct PlanView {
+  int32_t U = 0, cells = 0;
+  bool has_shared = false;
+};
+
+// Builds the plan of a batch from host copies of its tables and lengths (table entries may
+// carry the shared mark). H / GS: head slots and q heads per slot of the stream kernel.
+// share = false gives a plan without runs (every block private). Returns the number of units.
+int32_t plan_build(const int32_t* tables, const int32_t* lens, int32_t B, int32_t max_blocks,
+                   int32_t max_ctx, int32_t NB, int32_t H, int32_t GS, int32_t G, int32_t chunk,
+                   bool share, std::vector<int32_t>* out);
+// Validates a packed plan against a launch's shapes; fills v. append: the block of each
+// sequence's newest token must not be shared.
+bool plan_check(const int32_t* p, size_t n, int32_t B, int32_t max_blocks, int32_t H, int32_t GS,
+                int32_t G, bool append, PlanView* v);
 
 struct WriteParams {
   const void* k;
@@ -51,8 +75,17 @@ struct StreamParams {
   float scale_log2;     // softmax scale times log2(e): scores are kept in base-2 units
   int32_t num_workers;  // W: waves of the stream pass, a positive multiple of kWaves
   int32_t* ws_seg;      // [B + 1] prefix sums of block counts (written by the stream pass)
-  float* ws_ml;         // [W][2][GS][2]: (m, l) of each piece
-  float* ws_o;          // [W][2][GS][hd]: o of each piece
+  float* ws_ml;         // [cells][GS][2]: (m, l) of each piece
+  float* ws_o;          // [cells][GS][hd]: o of each piece
+  // Shared-prefix plan (all null / 0 without one). Cells of ws_ml / ws_o: [0, 2W) the
+  // workers' pieces; [2W, 2W + B*H) the piece of a planned sequence's private segment when one
+  // worker holds it whole; from 2W + B*H on, the shared pass's pieces.
+  const int32_t* skip;     // [B] leading blocks of each sequence covered by the shared pass
+  const int32_t* sh_ptr;   // [B + 1] CSR over sh_list
+  const int32_t* sh_list;  // shared-piece cells of each sequence (plus its head slot)
+  const int32_t* units;    // [U][kUnitInts]
+  const int32_t* members;  // batch rows of the units' members
+  int32_t num_units, shared_cells;
 };
 
 // dtype: 0 f32, 1 f16, 2 bf16 (pkv_dtype). Return the launch status (hipGetLastError).
@@ -64,6 +97,9 @@ hipError_t launch_stream(const StreamParams& p, int32_t dtype, int32_t kernel,
                          hipStream_t stream);
 hipError_t launch_merge(const StreamParams& p, int32_t dtype, int32_t kernel,
                         hipStream_t stream);
+// The shared pass of a plan (f16/bf16, G <= 16): p.num_units units on every kv head.
+hipError_t launch_shared(const StreamParams& p, int32_t dtype, int32_t kernel,
+                         hipStream_t stream);
 
 // Records the failing step and the HIP error text for pkv_last_error(); returns err.
 hipError_t note_error(const char* what, hipError_t err);

@@ -1,0 +1,185 @@
+// Shared-prefix plan of a decode batch (host side).
+//
+// [P1] §二 "解決三大問題" and [P2] "共享和复用": sequences with a common prefix (a system prompt,
+// beam candidates) point at the same physical blocks. Attention over such blocks is the same
+// K/V for every sequence that shares them, so it can be read once for all of them: the shared
+// pass (attn_shared_kernel) computes, per run of shared blocks, every member's (m, l, o) piece
+// over the run in one MFMA contraction (rows = members' q heads), the stream pass streams only
+// each sequence's private remainder, and the merge folds the pieces together.
+//
+// A run is (members, logical blocks [j0, j1)): every member's table names the same physical
+// block at each index of the range. Runs are found top-down: the batch's sequences grouped by
+// their first block; a group of two or more extends its run while all members have a block at
+// the next index and it is the same block; where they part (or some end) the group is split by
+// the block id at that index and each part of two or more continues. A sequence's shared
+// blocks are therefore a prefix of its table, skip_s blocks long. The work is one integer
+// compare per shared table entry.
+//
+// Packed int32 layout (see pkv.h): a 16-int header, then skip[B], blocks[B], sh_ptr[B+1],
+// units[U][6] = {ref_seq, b0, b1, member_off, member_cnt, cell_base}, members[], sh_list[].
+
+#include <algorithm>
+#include <cstdint>
+#include <map>
+#include <vector>
+
+#include "../../include/pkv.h"
+#include "pkv_kernels.h"
+
+namespace pkv {
+
+namespace {
+
+struct Run {
+  std::vector<int32_t> members;
+  int32_t j0, j1;
+};
+
+}  // namespace
+
+int32_t plan_build(const int32_t* tables, const int32_t* lens, int32_t B, int32_t max_blocks,
+                   int32_t max_ctx, int32_t NB, int32_t H, int32_t GS, int32_t G, int32_t chunk,
+                   bool share, std::vector<int32_t>* out) {
+  // a table entry's block, or -1 when it names no block of the pool (never shared)
+  auto entry = [&](int32_t s, int32_t j) {
+    const int32_t raw = tables[static_cast<int64_t>(s) * max_blocks + j];
+    const int32_t id = raw & ~kSharedBit;
+    return raw < 0 || id >= NB ? -1 : id;
+  };
+  std::vector<int32_t> c(B);
+  for (int32_t s = 0; s < B; ++s) {
+    const int32_t n = std::min(std::max(lens[s], 0), max_ctx);
+    c[s] = std::min((n + kBlockSize - 1) / kBlockSize, max_blocks);
+  }
+  std::vector<int32_t> skip(B, 0);
+  std::vector<Run> runs;
+  // groups of >= 2 members that agree on block index j, by block id (ordered: deterministic)
+  auto split = [&](const std::vector<int32_t>& from, int32_t j, std::vector<Run>* todo) {
+    std::map<int32_t, std::vector<int32_t>> by_block;
+    for (int32_t s : from)
+      if (c[s] > j && entry(s, j) >= 0) by_block[entry(s, j)].push_back(s);
+    for (auto& kv : by_block)
+      if (kv.second.size() >= 2) todo->push_back(Run{std::move(kv.second), j, j});
+  };
+  std::vector<Run> todo;
+  if (share) {
+    std::vector<int32_t> all(B);
+    for (int32_t s = 0; s < B; ++s) all[s] = s;
+    split(all, 0, &todo);
+  }
+  while (!todo.empty()) {
+    Run r = std::move(todo.back());
+    todo.pop_back();
+    const int32_t first = r.members[0];
+    int32_t e = r.j0;
+    for (;;) {
+      bool same = true;
+      for (int32_t s : r.members)
+        if (c[s] <= e || entry(s, e) != entry(first, e) || entry(s, e) < 0) {
+          same = false;
+          break;
+        }
+      if (!same) break;
+      ++e;
+    }
+    r.j1 = e;
+    for (int32_t s : r.members) skip[s] = e;
+    std::vector<int32_t> members = r.members;
+    runs.push_back(std::move(r));
+    split(members, e, &todo);
+  }
+  // deterministic order: by first member, then start block
+  std::sort(runs.begin(), runs.end(), [](const Run& a, const Run& b) {
+    return a.members[0] != b.members[0] ? a.members[0] < b.members[0] : a.j0 < b.j0;
+  });
+  const int32_t per_tile = std::max(1, kRowsPerTile / G);
+  std::vector<int32_t> units, members;
+  std::vector<std::vector<int32_t>> lists(B);
+  int32_t cells = 0;
+  for (const Run& r : runs) {
+    for (int32_t b0 = r.j0; b0 < r.j1; b0 += chunk) {
+      const int32_t b1 = std::min(r.j1, b0 + chunk);
+      for (size_t t = 0; t < r.members.size(); t += per_tile) {
+        const int32_t cnt = static_cast<int32_t>(std::min<size_t>(per_tile, r.members.size() - t));
+        units.insert(units.end(), {r.members[0], b0, b1, static_cast<int32_t>(members.size()), cnt,
+                                   cells});
+        for (int32_t k = 0; k < cnt; ++k) {
+          const int32_t s = r.members[t + k];
+          members.push_back(s);
+          lists[s].push_back(cells + k * H);
+        }
+        cells += cnt * H;
+      }
+    }
+  }
+  const int32_t U = static_cast<int32_t>(units.size() / kUnitInts);
+  std::vector<int32_t>& p = *out;
+  p.assign(kPlanHeader, 0);
+  p[0] = kPlanMagic;
+  p[1] = B;
+  p[2] = H;
+  p[3] = GS;
+  p[4] = U;
+  p[5] = static_cast<int32_t>(members.size());
+  int32_t nlist = 0;
+  for (const auto& l : lists) nlist += static_cast<int32_t>(l.size());
+  p[6] = nlist;
+  p[7] = cells;
+  p[8] = chunk;
+  p.insert(p.end(), skip.begin(), skip.end());
+  p.insert(p.end(), c.begin(), c.end());
+  int32_t acc = 0;
+  p.push_back(0);
+  for (int32_t s = 0; s < B; ++s) {
+    acc += static_cast<int32_t>(lists[s].size());
+    p.push_back(acc);
+  }
+  p.insert(p.end(), units.begin(), units.end());
+  p.insert(p.end(), members.begin(), members.end());
+  for (const auto& l : lists) p.insert(p.end(), l.begin(), l.end());
+  return U;
+}
+
+bool plan_check(const int32_t* p, size_t n, int32_t B, int32_t max_blocks, int32_t H, int32_t GS,
+                int32_t G, bool append, PlanView* v) {
+  if (n < static_cast<size_t>(kPlanHeader) || p[0] != kPlanMagic || p[1] != B || p[2] != H ||
+      p[3] != GS)
+    return false;
+  const int64_t U = p[4], M = p[5], L = p[6], cells = p[7];
+  if (U < 0 || M < 0 || L < 0 || cells < 0 || p[8] <= 0) return false;
+  const int64_t need = kPlanHeader + 3 * static_cast<int64_t>(B) + 1 + U * kUnitInts + M + L;
+  if (static_cast<int64_t>(n) != need || cells > (int64_t{1} << 30)) return false;
+  const int32_t* skip = p + kPlanHeader;
+  const int32_t* blocks = skip + B;
+  const int32_t* ptr = blocks + B;
+  const int32_t* units = ptr + B + 1;
+  const int32_t* members = units + U * kUnitInts;
+  const int32_t* list = members + M;
+  for (int32_t s = 0; s < B; ++s) {
+    if (skip[s] < 0 || blocks[s] < 0 || blocks[s] > max_blocks || skip[s] > blocks[s])
+      return false;
+    // the block of a sequence's newest token must stay private in append mode
+    if (append && blocks[s] > 0 && skip[s] >= blocks[s]) return false;
+    if (ptr[s + 1] < ptr[s]) return false;
+  }
+  if (ptr[0] != 0 || ptr[B] != L) return false;
+  const int32_t per_tile = std::max(1, kRowsPerTile / G);
+  for (int64_t u = 0; u < U; ++u) {
+    const int32_t* e = units + u * kUnitInts;
+    if (e[0] < 0 || e[0] >= B || e[1] < 0 || e[1] >= e[2] || e[2] > max_blocks) return false;
+    if (e[3] < 0 || e[4] < 1 || e[4] > per_tile || static_cast<int64_t>(e[3]) + e[4] > M)
+      return false;
+    if (e[5] < 0 || static_cast<int64_t>(e[5]) + static_cast<int64_t>(e[4]) * H > cells)
+      return false;
+  }
+  for (int64_t k = 0; k < M; ++k)
+    if (members[k] < 0 || members[k] >= B) return false;
+  for (int64_t k = 0; k < L; ++k)
+    if (list[k] < 0 || static_cast<int64_t>(list[k]) + H > cells) return false;
+  v->U = static_cast<int32_t>(U);
+  v->cells = static_cast<int32_t>(cells);
+  v->has_shared = L > 0;
+  return true;
+}
+
+}  // namespace pkv
