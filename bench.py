@@ -79,6 +79,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="oracle time budget for the CPU baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-plan", action="store_true",
+                    help="decode batches that share blocks without a shared-prefix plan")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -109,8 +111,11 @@ def measured_traffic(workload, digest):
 class Workload:
     """Sequences held by the C++ allocator plus device caches filled with seeded values."""
 
-    def __init__(self, name, total_steps, torch, pkv, W):
+    def __init__(self, name, total_steps, torch, pkv, W, plan=True):
         self.name = name
+        self.torch = torch
+        # shared-prefix plans for the batches that share blocks
+        self.planned = plan and name in ("prefix_shared", "beam_search")
         self.gen = W  # the seeded input generators
         shape = self.shape = W.SHAPES[name]
         rng = W.rng_for(shape.seed)
@@ -169,10 +174,13 @@ class Workload:
         self.v_new = W.device_normal((self.B, self.Hkv, self.hd), shape.dtype, 7005)
         self.out = torch.empty_like(self.q)
         # Two sets of step buffers, each one packed int32 array [lens | slots | copy-on-write
-        # sources | copy-on-write targets | tables], in
-        # pinned host memory and on the device: the host prepares step k+1 and its copy runs on
-        # a copy stream while step k's kernels run on the compute stream.
-        n_int = 4 * self.B + self.B * self.max_blocks
+        # sources | copy-on-write targets | tables | shared-prefix plan], in pinned host memory
+        # and on the device: the host prepares step k+1 and its copy runs on a copy stream
+        # while step k's kernels run on the compute stream.
+        self.plan0 = 4 * self.B + self.B * self.max_blocks
+        cap = int(pkv.lib.pkv_decode_plan_max_ints(self.B, self.max_blocks)) if self.planned else 0
+        n_int = self.plan0 + cap
+        self.plan_len = [0, 0]
         self.pin = [torch.empty(n_int, dtype=torch.int32, pin_memory=True) for _ in range(2)]
         self.dev = [torch.empty(n_int, dtype=torch.int32, device=dev) for _ in range(2)]
         self.host_views = [self._views(t.numpy()) for t in self.pin]
@@ -194,14 +202,38 @@ class Workload:
         self.W = pkv.pkv_decode_num_workers(self.Hq, self.Hkv, self.hd, self.dt)
         nbytes = pkv.pkv_decode_stream_workspace_bytes(self.B, self.Hq, self.Hkv, self.hd,
                                                        self.dt, self.W)
+        self.ws_dev = dev
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         for e in self.done:
             e.record()
         self.scale = 1.0 / math.sqrt(self.hd)
+        self.skips = []  # per timed step: each sequence's shared blocks (planned runs)
+
+    def planned_skip(self):
+        """Each sequence's blocks covered by the shared pass this step (zeros unplanned)."""
+        return self.step_skip if self.planned else np.zeros(self.B, np.int32)
+
+    def build_plan(self, s, pkv):
+        """Shared-prefix plan of buffer set s's tables and lengths, into its pinned region;
+        grows the workspace when the plan needs more. Returns the number of ints."""
+        lens_h, _, tables_h = self.host_views[s]
+        region = self.pin[s].numpy()[self.plan0:]
+        plan = pkv.pkv_decode_plan(tables_h, lens_h, num_q_heads=self.Hq, num_kv_heads=self.Hkv,
+                                   num_blocks=self.NB, max_context_len=self.max_ctx,
+                                   dtype=self.dt, out=region)
+        assert plan.base is not None and np.shares_memory(plan, region)
+        need = pkv.pkv_decode_planned_workspace_bytes(self.B, self.Hq, self.Hkv, self.hd,
+                                                      self.dt, self.W, plan)
+        if need > self.workspace.numel():
+            self.workspace = self.torch.empty(need, dtype=self.workspace.dtype,
+                                              device=self.ws_dev)
+        self.plan_len[s] = len(plan)
+        self.step_skip = plan[16:16 + self.B].copy()
+        return len(plan)
 
     def _views(self, flat):
         B, mb = self.B, self.max_blocks
-        return flat[:B], flat[B:2 * B], flat[4 * B:].reshape(B, mb)
+        return flat[:B], flat[B:2 * B], flat[4 * B:4 * B + B * mb].reshape(B, mb)
 
     def cow_views(self, s):
         """(host, device) views [2, B] of buffer set s's copy-on-write pairs."""
@@ -211,10 +243,13 @@ class Workload:
     def kv_bytes(self, lens):
         return int(lens.astype(np.int64).sum()) * 2 * self.Hkv * self.hd * self.eb
 
-    def unique_kv_bytes(self, lens, tables):
-        """K+V bytes of the distinct cache slots the step reads (shared blocks counted once)."""
+    def unique_kv_bytes(self, lens, tables, upto=None):
+        """K+V bytes of the distinct cache slots the step reads (shared blocks counted once);
+        with upto, only each sequence's first upto[i] blocks."""
         j = np.arange(tables.shape[1])[None, :]
         valid = np.clip(lens[:, None].astype(np.int64) - 16 * j, 0, 16)
+        if upto is not None:
+            valid = np.where(j < np.asarray(upto)[:, None], valid, 0)
         best = np.zeros(self.NB, np.int64)
         m = valid > 0
         np.maximum.at(best, tables[m], valid[m])
@@ -268,24 +303,26 @@ def run_step(wl, torch, pkv, events=None):
         tables_h[r, c] = b
     wl.pending[s].clear()
     lens_h[:] = wl.lens
-    with torch.cuda.stream(wl.copy_stream):  # 2. tables, lengths, slots to the device
-        wl.dev[s].copy_(wl.pin[s], non_blocking=True)
+    with torch.cuda.stream(wl.copy_stream):  # 2. tables, lengths, slots (and plan) to the device
+        if wl.planned:
+            n = wl.plan0 + wl.build_plan(s, pkv)
+            wl.dev[s][:n].copy_(wl.pin[s][:n], non_blocking=True)
+        else:
+            wl.dev[s].copy_(wl.pin[s], non_blocking=True)
         wl.copied[s].record(wl.copy_stream)
     compute = torch.cuda.current_stream()
     compute.wait_event(wl.copied[s])
-    if events is not None:
-        events[0].record()
-        events[1].record()  # no copy-on-write in a decode loop without forks
-    attend(wl, pkv, s, events)
-    return lens_h.copy(), None
+    attend(wl, pkv, s, events)  # no copy-on-write in a decode loop without forks
+    return lens_h.copy(), (tables_h.copy() if wl.planned else None), wl.planned_skip()
 
 
 def run_beam_step(wl, torch, pkv, s, events):
     ncow = beam_reselect(wl, s)
     wl.cows.append(ncow)
     wl.cows_all.append(ncow)
-    with torch.cuda.stream(wl.copy_stream):  # tables, lengths, pairs to the device
-        wl.dev[s].copy_(wl.pin[s], non_blocking=True)
+    n = wl.plan0 + (wl.build_plan(s, pkv) if wl.planned else 0)
+    with torch.cuda.stream(wl.copy_stream):  # tables, lengths, pairs (and plan) to the device
+        wl.dev[s][:n].copy_(wl.pin[s][:n], non_blocking=True)
         wl.copied[s].record(wl.copy_stream)
     torch.cuda.current_stream().wait_event(wl.copied[s])
     if events is not None:
@@ -294,28 +331,44 @@ def run_beam_step(wl, torch, pkv, s, events):
         _, cow_d = wl.cow_views(s)
         pkv.pkv_copy_blocks(wl.k_cache, wl.v_cache, cow_d[0, :ncow], cow_d[1, :ncow],
                             num_kv_heads=wl.Hkv, head_dim=wl.hd)
-    if events is not None:
-        events[1].record()
     attend(wl, pkv, s, events)
-    return wl.lens.copy(), wl.host_views[s][2].copy()
+    return wl.lens.copy(), wl.host_views[s][2].copy(), wl.planned_skip()
 
 
 def attend(wl, pkv, s, events):
-    """The step's two kernels on buffer set s (tables, lengths on the device)."""
+    """The step's kernels on buffer set s (tables, lengths and plan on the device): the
+    stream pass (with the newest tokens) and the merge (which also stores them), after the
+    shared pass when the batch is planned. Events: [1] before the shared pass, [2] before the
+    stream pass, [3] before the merge, [4] after it."""
     lens_d, _, tables_d = wl.dev_views[s]
-    # 3 + 4a. cache write of the newest tokens fused into the attention stream pass
-    pkv.pkv_decode_append_stream(wl.q, wl.k_new, wl.v_new, wl.k_cache, wl.v_cache, tables_d,
-                                 lens_d, num_kv_heads=wl.Hkv, scale=wl.scale,
-                                 max_context_len=wl.max_ctx, num_workers=wl.W,
-                                 workspace=wl.workspace, out=wl.out)
-    if events is not None:
-        events[2].record()
-    # 4b. merge of the cut segments, plus the stores of the new tokens into their slots
-    pkv.pkv_decode_append_merge(wl.out, wl.k_new, wl.v_new, wl.k_cache, wl.v_cache, tables_d,
-                                lens_d, wl.workspace, num_kv_heads=wl.Hkv,
-                                max_context_len=wl.max_ctx, num_workers=wl.W)
-    if events is not None:
-        events[3].record()
+
+    def mark(k):
+        if events is not None:
+            events[k].record()
+    if events is not None and wl.beam:
+        events[1].record()  # [0]: before the copy-on-write copies
+    elif events is not None:
+        events[0].record()  # [0] == [1]: no copy-on-write here
+    if wl.planned:
+        plan = wl.pin[s].numpy()[wl.plan0:wl.plan0 + wl.plan_len[s]]
+        plan_d = wl.dev[s][wl.plan0:wl.plan0 + wl.plan_len[s]]
+        pkv.pkv_decode_planned(wl.q, wl.k_cache, wl.v_cache, tables_d, lens_d, plan, plan_d,
+                               num_kv_heads=wl.Hkv, scale=wl.scale, max_context_len=wl.max_ctx,
+                               num_workers=wl.W, workspace=wl.workspace, k_new=wl.k_new,
+                               v_new=wl.v_new, out=wl.out,
+                               events=None if events is None else events[2:5])
+    else:  # [2] == [1]: no shared pass
+        # 3 + 4a. cache write of the newest tokens fused into the attention stream pass
+        pkv.pkv_decode_append_stream(wl.q, wl.k_new, wl.v_new, wl.k_cache, wl.v_cache, tables_d,
+                                     lens_d, num_kv_heads=wl.Hkv, scale=wl.scale,
+                                     max_context_len=wl.max_ctx, num_workers=wl.W,
+                                     workspace=wl.workspace, out=wl.out)
+        mark(3)
+        # 4b. merge of the cut segments, plus the stores of the new tokens into their slots
+        pkv.pkv_decode_append_merge(wl.out, wl.k_new, wl.v_new, wl.k_cache, wl.v_cache,
+                                    tables_d, lens_d, wl.workspace, num_kv_heads=wl.Hkv,
+                                    max_context_len=wl.max_ctx, num_workers=wl.W)
+        mark(4)
     wl.done[s].record()
     wl.last_set = s
 
@@ -554,14 +607,14 @@ def main():
     if args.workload in BATCHING:
         batching_main(args, torch, pkv, W)
         return
-    wl = Workload(args.workload, args.warmup + args.steps, torch, pkv, W)
+    wl = Workload(args.workload, args.warmup + args.steps, torch, pkv, W, plan=not args.no_plan)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
         run_step(wl, torch, pkv)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     per_step = []
     wl.cows.clear()
     t0 = time.perf_counter()
@@ -570,9 +623,16 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    copy_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    part_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    merge_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    # events a step does not record stand for the one before them (no copy, no shared pass)
+    for e in evs:
+        if not wl.beam:
+            e[1] = e[0]
+        if not wl.planned:
+            e[2] = e[1]
+    copy_ms = [e[0].elapsed_time(e[1]) if wl.beam else 0.0 for e in evs]
+    shared_ms = [e[1].elapsed_time(e[2]) if wl.planned else 0.0 for e in evs]
+    part_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    merge_ms = [e[3].elapsed_time(e[4]) for e in evs]
     # The last tables sent must be exactly what the allocator exports (for the decode loop,
     # whose tables only gain entries, this checks every incremental update).
     final_tables = wl.host_views[wl.last_set][2].copy()
@@ -582,14 +642,20 @@ def main():
 
     def unmarked(t):
         return np.where(t >= 0, t & ~pkv.BLOCK_SHARED, t)
-    lens_per_step = [lens for lens, _ in per_step]
+    lens_per_step = [lens for lens, _, _ in per_step]
     kv_logical = [wl.kv_bytes(lens) for lens in lens_per_step]
     kv = [wl.unique_kv_bytes(lens, unmarked(final_tables if t is None else t))
-          for lens, t in per_step]
-    algo = [b + wl.qo_bytes() for b in kv]
+          for lens, t, _ in per_step]
+    # with a plan: the unique bytes the shared pass reads (blocks before each skip) and the
+    # rest, which the stream pass reads
+    kv_shared = [wl.unique_kv_bytes(lens, unmarked(final_tables if t is None else t), upto=sk)
+                 for lens, t, sk in per_step]
+    kv_private = [a - b for a, b in zip(kv, kv_shared)]
+    algo = [b + wl.qo_bytes() for b in kv_private]
     ms_per_step = wall / args.steps * 1e3
     value = sum(kv) / wall / 1e9
     achieved = sum(algo) / (sum(part_ms) / 1e3) / 1e9
+    attn_ms = [a + b + c for a, b, c in zip(shared_ms, part_ms, merge_ms)]
     digest = kernel_source_digest()
     traffic = measured_traffic(args.workload, digest)
 
@@ -625,10 +691,9 @@ def main():
         "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4),
         "attn_stream_ms": round(float(np.mean(part_ms)), 4),
         "attn_merge_ms": round(float(np.mean(merge_ms)), 4),
-        "attn_kv_gbs": round(sum(kv) / (sum(part_ms) + sum(merge_ms)) * 1e3 / 1e9, 2),
+        "attn_kv_gbs": round(sum(kv) / sum(attn_ms) * 1e3 / 1e9, 2),
         "kv_bytes_per_step": {"unique": int(np.mean(kv)), "logical": int(np.mean(kv_logical))},
-        "attn_logical_kv_gbs": round(sum(kv_logical) / (sum(part_ms) + sum(merge_ms)) * 1e3 / 1e9,
-                                     2),
+        "attn_logical_kv_gbs": round(sum(kv_logical) / sum(attn_ms) * 1e3 / 1e9, 2),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -640,6 +705,21 @@ def main():
             "algorithmic_bytes_per_launch": int(np.mean(algo)),
         },
     }
+    if wl.planned:
+        sh = sum(kv_shared)
+        res["shared_prefix_plan"] = {
+            "shared_pass_ms": round(float(np.mean(shared_ms)), 4),
+            "shared_unique_bytes_per_step": int(np.mean(kv_shared)),
+            "private_unique_bytes_per_step": int(np.mean(kv_private)),
+            "shared_pass_gbs": round(sh / (sum(shared_ms) / 1e3) / 1e9, 2) if sh else None,
+            "attention_ms": round(float(np.mean(attn_ms)), 4),
+            "attention_unique_gbs": round((sum(kv) + args.steps * wl.qo_bytes())
+                                          / (sum(attn_ms) / 1e3) / 1e9, 2),
+            "attention_frac_of_hbm_peak": round((sum(kv) + args.steps * wl.qo_bytes())
+                                                / (sum(attn_ms) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "note": "three kernels per step (shared pass, stream pass over the private blocks, "
+                    "merge); roofline above is the stream pass over the private bytes",
+        }
     if wl.beam:
         # copy-on-write copies: both caches, every kv head, read + written
         pair_bytes = 4 * wl.Hkv * wl.hd * 16 * wl.eb

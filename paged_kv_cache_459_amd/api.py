@@ -298,10 +298,12 @@ def pkv_decode_planned_workspace_bytes(batch, num_q_heads, num_kv_heads, head_di
 
 def pkv_decode_planned(q, k_cache, v_cache, block_tables, context_lens, plan, plan_dev, *,
                        num_kv_heads, scale, max_context_len, num_workers, workspace,
-                       k_new=None, v_new=None, out=None, passes=0):
+                       k_new=None, v_new=None, out=None, passes=0, events=None):
     """Decode step with a shared-prefix plan (see include/pkv.h). plan: the host plan (NumPy
     int32), plan_dev: the same ints on the device (int32 tensor). With k_new / v_new it is the
-    fused newest-token step. passes: 0 all, 1 shared pass, 2 stream pass, 3 merge."""
+    fused newest-token step. passes: 0 all, 1 shared pass, 2 stream pass, 3 merge. events:
+    three torch.cuda.Events to record after the shared pass, the stream pass and the merge
+    (the three passes then run as three calls, arguments checked once)."""
     out, B, hq, hd, nb, mb = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
                                           num_kv_heads, out)
     if (k_new is None) != (v_new is None):
@@ -313,12 +315,16 @@ def pkv_decode_planned(q, k_cache, v_cache, block_tables, context_lens, plan, pl
     if plan_dev.numel() < p.size:
         raise ValueError("plan_dev is shorter than the plan")
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    check(lib.pkv_decode_planned(int(passes), _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new),
-                                 _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                                 _ptr(context_lens), B, hq, num_kv_heads, hd, BLOCK_SIZE, nb, mb,
-                                 max_context_len, float(scale), pkv_dtype(q), p.ctypes.data,
-                                 _ptr(plan_dev), p.size, num_workers, _ptr(workspace), ws_bytes,
-                                 _stream(q.device)), "pkv_decode_planned")
+    args = (_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+            _ptr(block_tables), _ptr(context_lens), B, hq, num_kv_heads, hd, BLOCK_SIZE, nb, mb,
+            max_context_len, float(scale), pkv_dtype(q), p.ctypes.data, _ptr(plan_dev), p.size,
+            num_workers, _ptr(workspace), ws_bytes, _stream(q.device))
+    if events is None:
+        check(lib.pkv_decode_planned(int(passes), *args), "pkv_decode_planned")
+    else:
+        for ps, ev in zip((1, 2, 3), events):
+            check(lib.pkv_decode_planned(ps, *args), "pkv_decode_planned")
+            ev.record()
     return out
 
 

@@ -375,7 +375,10 @@ __device__ void publish_and_zero(const StreamParams& p, const int* pref) {
   for (int i = threadIdx.x; i <= p.B; i += kThreads) p.ws_seg[i] = pref[i];
   const int row = p.Hq * p.hd;
   for (int i = 0; i < p.B; ++i) {
-    if (clamp_len(p, i) != 0) continue;
+    if (pref[i + 1] != pref[i]) continue;  // has blocks to stream (prefix sums are in LDS)
+    // no private block: n = 0 (zero the row), or a planned sequence whose every block is
+    // shared (skip > 0 implies n > 0; the merge writes the row)
+    if (p.skip != nullptr && p.skip[i] > 0) continue;
     for (int e = threadIdx.x; e < row; e += kThreads)
       Elem<DT>::put(p.out, static_cast<size_t>(i) * row + e, 0.f);
   }
@@ -846,10 +849,56 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_shared_kernel(const StreamParams p,
   const int G = p.Hq / p.Hkv;
   const int hq = lane & 15, g = lane >> 4;
   const int mk = hq / G, jq = hq - mk * G;  // this lane's row: member mk, q head kvh*G + jq
+  const uint32_t k_lane = 16u * lane;
+  const uint32_t v_lane = 32u * hq + 8u * g;
+  const size_t blk_stride = static_cast<size_t>(p.Hkv) * TILE;
+  const int32_t* table = p.block_tables + static_cast<size_t>(ref) * p.max_blocks;
+
+  // The chunk's block ids, one per lane (read once: a table read inside the loop would make
+  // every tile wait for all loads in flight). -1: the entry names no block of the pool (then
+  // nothing of the block counts).
+  int lane_id = -1;
+  if (lane < b1 - b0) {
+    const int raw = table[b0 + lane];
+    const int id = raw & ~kSharedBit;
+    lane_id = (raw < 0 || id >= p.NB) ? -1 : id;
+  }
+  auto block_id = [&](int t) { return uniform(__builtin_amdgcn_readlane(lane_id, t - b0)); };
+  auto load = [&](uint4 (&kr)[KS], uint2 (&vr)[VT], int id) {
+    const size_t base = static_cast<size_t>(max(id, 0)) * blk_stride + static_cast<size_t>(kvh) * TILE;
+    const char* kt = static_cast<const char*>(p.k_cache) + base;
+    const char* vt = static_cast<const char*>(p.v_cache) + base;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) kr[s2] = *reinterpret_cast<const uint4*>(kt + k_lane + 1024u * s2);
+#pragma unroll
+    for (int j = 0; j < VT; ++j) vr[j] = *reinterpret_cast<const uint2*>(vt + v_lane + 512u * j);
+  };
+  // Two tiles in flight (buffers a and b, alternating), requested before the rows' lookups
+  // below so that their latencies overlap.
+  uint4 ka[KS], kb[KS];
+  uint2 va[VT], vb[VT];
+  int ida = block_id(b0), idb = block_id(min(b0 + 1, b1 - 1));
+  load(ka, va, ida);
+  load(kb, vb, idb);
+
   int seq = -1;
   if (hq < mcnt * G) seq = p.members[moff + mk];
   const bool row_ok = seq >= 0 && seq < p.B;
+  uint4 qb[KS];
+  if (row_ok) {
+    const uint4* qp = reinterpret_cast<const uint4*>(
+        static_cast<const char*>(p.q) + (static_cast<size_t>(seq) * p.Hq + kvh * G + jq) * HD * 2);
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) qb[s2] = qp[4 * s2 + g];
+  } else {
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) qb[s2] = make_uint4(0, 0, 0, 0);
+  }
   const int n_row = row_ok ? clamp_len(p, seq) : 0;
+  // q settled here: a first use inside the loop would put its wait (for every load issued
+  // before it, the tiles included) at the top of each iteration
+#pragma unroll
+  for (int s2 = 0; s2 < KS; ++s2) settle(qb[s2]);
   // the rows' shortest and longest lengths: a tile ending at or before the shortest needs no
   // masking; V tokens at or past the longest are read by no row
   int nmin = row_ok ? n_row : 0x7fffffff, nmax = n_row;
@@ -861,58 +910,17 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_shared_kernel(const StreamParams p,
   nmin = uniform(nmin);
   nmax = uniform(nmax);
 
-  const uint32_t k_lane = 16u * lane;
-  const uint32_t v_lane = 32u * hq + 8u * g;
-  const size_t blk_stride = static_cast<size_t>(p.Hkv) * TILE;
-  const int32_t* table = p.block_tables + static_cast<size_t>(ref) * p.max_blocks;
-
-  uint4 qb[KS];
-  if (row_ok) {
-    const uint4* qp = reinterpret_cast<const uint4*>(
-        static_cast<const char*>(p.q) + (static_cast<size_t>(seq) * p.Hq + kvh * G + jq) * HD * 2);
-#pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) qb[s2] = qp[4 * s2 + g];
-  } else {
-#pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) qb[s2] = make_uint4(0, 0, 0, 0);
-  }
   float m = kNegInf, lsum = 0.f;
   float4_t o[VT];
 #pragma unroll
   for (int j = 0; j < VT; ++j) o[j] = float4_t{0.f, 0.f, 0.f, 0.f};
-  uint4 kr[KS];
-  uint2 vr[VT];
 
-  // block t's id, or -1 when its entry names no block of the pool (then nothing of it counts)
-  auto block_id = [&](int t) {
-    const int raw = uniform(table[t]);
-    const int id = raw & ~kSharedBit;
-    return (raw < 0 || id >= p.NB) ? -1 : id;
-  };
-  auto load_k = [&](int id) {
-    const char* kt = static_cast<const char*>(p.k_cache) + static_cast<size_t>(max(id, 0)) * blk_stride +
-                     static_cast<size_t>(kvh) * TILE;
-#pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) kr[s2] = *reinterpret_cast<const uint4*>(kt + k_lane + 1024u * s2);
-  };
-  auto load_v = [&](int id) {
-    const char* vt = static_cast<const char*>(p.v_cache) + static_cast<size_t>(max(id, 0)) * blk_stride +
-                     static_cast<size_t>(kvh) * TILE;
-#pragma unroll
-    for (int j = 0; j < VT; ++j) vr[j] = *reinterpret_cast<const uint2*>(vt + v_lane + 512u * j);
-  };
-
-  int id = block_id(b0);
-  load_k(id);
-  load_v(id);
-  for (int t = b0; t < b1; ++t) {
-    const int next = t + 1 < b1 ? block_id(t + 1) : -1;
+  auto compute = [&](const uint4 (&kr)[KS], const uint2 (&vr)[VT], int t, int id) {
     const bool full = id >= 0 && kBlockSize * (t + 1) <= nmin;  // every row sees all 16 tokens
     const int row_valid = id < 0 ? 0 : min(kBlockSize, max(0, n_row - kBlockSize * t));
     float4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) sacc = M16::qk(pinned(kr[s2]), qb[s2], sacc);
-    if (t + 1 < b1) load_k(next);
     float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -948,8 +956,17 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_shared_kernel(const StreamParams p,
     }
 #pragma unroll
     for (int j = 0; j < VT; ++j) o[j] = M16::pv(vt[j], pb, o[j] * alpha);
-    if (t + 1 < b1) load_v(next);
-    id = next;
+  };
+
+  // The reloads are unconditional (past the chunk they re-read its last block): loads issued
+  // on every path keep the wait counts exact, so a tile waits only for its own loads.
+  for (int t = b0; t < b1; t += 2) {
+    compute(ka, va, t, ida);
+    ida = block_id(min(t + 2, b1 - 1));
+    load(ka, va, ida);
+    if (t + 1 < b1) compute(kb, vb, t + 1, idb);
+    idb = block_id(min(t + 3, b1 - 1));
+    load(kb, vb, idb);
   }
   float l = lsum + __shfl_xor(lsum, 16);
   l += __shfl_xor(l, 32);

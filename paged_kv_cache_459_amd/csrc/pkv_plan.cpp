@@ -13,14 +13,14 @@
 // the next index and it is the same block; where they part (or some end) the group is split by
 // the block id at that index and each part of two or more continues. A sequence's shared
 // blocks are therefore a prefix of its table, skip_s blocks long. The work is one integer
-// compare per shared table entry.
+// compare per shared table entry, each member's row scanned contiguously.
 //
 // Packed int32 layout (see pkv.h): a 16-int header, then skip[B], blocks[B], sh_ptr[B+1],
 // units[U][6] = {ref_seq, b0, b1, member_off, member_cnt, cell_base}, members[], sh_list[].
 
 #include <algorithm>
 #include <cstdint>
-#include <map>
+#include <cstring>
 #include <vector>
 
 #include "../../include/pkv.h"
@@ -53,13 +53,25 @@ int32_t plan_build(const int32_t* tables, const int32_t* lens, int32_t B, int32_
   }
   std::vector<int32_t> skip(B, 0);
   std::vector<Run> runs;
-  // groups of >= 2 members that agree on block index j, by block id (ordered: deterministic)
+  // groups of >= 2 members that hold the same block at index j (sorted by block id, then
+  // member: deterministic)
+  std::vector<std::pair<int32_t, int32_t>> keyed;
   auto split = [&](const std::vector<int32_t>& from, int32_t j, std::vector<Run>* todo) {
-    std::map<int32_t, std::vector<int32_t>> by_block;
+    keyed.clear();
     for (int32_t s : from)
-      if (c[s] > j && entry(s, j) >= 0) by_block[entry(s, j)].push_back(s);
-    for (auto& kv : by_block)
-      if (kv.second.size() >= 2) todo->push_back(Run{std::move(kv.second), j, j});
+      if (c[s] > j && entry(s, j) >= 0) keyed.emplace_back(entry(s, j), s);
+    std::sort(keyed.begin(), keyed.end());
+    for (size_t a = 0; a < keyed.size();) {
+      size_t z = a + 1;
+      while (z < keyed.size() && keyed[z].first == keyed[a].first) ++z;
+      if (z - a >= 2) {
+        Run r{{}, j, j};
+        r.members.reserve(z - a);
+        for (size_t k = a; k < z; ++k) r.members.push_back(keyed[k].second);
+        todo->push_back(std::move(r));
+      }
+      a = z;
+    }
   };
   std::vector<Run> todo;
   if (share) {
@@ -70,17 +82,19 @@ int32_t plan_build(const int32_t* tables, const int32_t* lens, int32_t B, int32_
   while (!todo.empty()) {
     Run r = std::move(todo.back());
     todo.pop_back();
+    // the run ends where any member's row first differs from the first member's (rows are
+    // scanned contiguously), or ends
     const int32_t first = r.members[0];
-    int32_t e = r.j0;
-    for (;;) {
-      bool same = true;
-      for (int32_t s : r.members)
-        if (c[s] <= e || entry(s, e) != entry(first, e) || entry(s, e) < 0) {
-          same = false;
-          break;
-        }
-      if (!same) break;
-      ++e;
+    const int32_t* ref = tables + static_cast<int64_t>(first) * max_blocks;
+    int32_t e = r.j0;  // the first member's valid entries bound the run
+    while (e < c[first] && entry(first, e) >= 0) ++e;
+    for (int32_t s : r.members) {  // entries equal to a valid one are valid
+      const int32_t* row = tables + static_cast<int64_t>(s) * max_blocks;
+      const int32_t lim = std::min(e, c[s]);
+      int32_t k = r.j0;
+      while (k + 16 <= lim && std::memcmp(row + k, ref + k, 64) == 0) k += 16;  // fast path
+      while (k < lim && ((row[k] ^ ref[k]) & ~kSharedBit) == 0) ++k;
+      e = k;
     }
     r.j1 = e;
     for (int32_t s : r.members) skip[s] = e;
@@ -94,7 +108,7 @@ int32_t plan_build(const int32_t* tables, const int32_t* lens, int32_t B, int32_
   });
   const int32_t per_tile = std::max(1, kRowsPerTile / G);
   std::vector<int32_t> units, members;
-  std::vector<std::vector<int32_t>> lists(B);
+  std::vector<int32_t> count(B, 0);  // shared pieces per sequence
   int32_t cells = 0;
   for (const Run& r : runs) {
     for (int32_t b0 = r.j0; b0 < r.j1; b0 += chunk) {
@@ -104,12 +118,22 @@ int32_t plan_build(const int32_t* tables, const int32_t* lens, int32_t B, int32_
         units.insert(units.end(), {r.members[0], b0, b1, static_cast<int32_t>(members.size()), cnt,
                                    cells});
         for (int32_t k = 0; k < cnt; ++k) {
-          const int32_t s = r.members[t + k];
-          members.push_back(s);
-          lists[s].push_back(cells + k * H);
+          members.push_back(r.members[t + k]);
+          ++count[r.members[t + k]];
         }
         cells += cnt * H;
       }
+    }
+  }
+  // each sequence's piece cells, in unit order (CSR)
+  std::vector<int32_t> ptr(B + 1, 0);
+  for (int32_t s = 0; s < B; ++s) ptr[s + 1] = ptr[s] + count[s];
+  std::vector<int32_t> list(ptr[B]);
+  {
+    std::vector<int32_t> fill(ptr.begin(), ptr.end() - 1);
+    for (size_t u = 0; u < units.size(); u += kUnitInts) {
+      const int32_t off = units[u + 3], cnt = units[u + 4], base = units[u + 5];
+      for (int32_t k = 0; k < cnt; ++k) list[fill[members[off + k]]++] = base + k * H;
     }
   }
   const int32_t U = static_cast<int32_t>(units.size() / kUnitInts);
@@ -121,22 +145,15 @@ int32_t plan_build(const int32_t* tables, const int32_t* lens, int32_t B, int32_
   p[3] = GS;
   p[4] = U;
   p[5] = static_cast<int32_t>(members.size());
-  int32_t nlist = 0;
-  for (const auto& l : lists) nlist += static_cast<int32_t>(l.size());
-  p[6] = nlist;
+  p[6] = ptr[B];
   p[7] = cells;
   p[8] = chunk;
   p.insert(p.end(), skip.begin(), skip.end());
   p.insert(p.end(), c.begin(), c.end());
-  int32_t acc = 0;
-  p.push_back(0);
-  for (int32_t s = 0; s < B; ++s) {
-    acc += static_cast<int32_t>(lists[s].size());
-    p.push_back(acc);
-  }
+  p.insert(p.end(), ptr.begin(), ptr.end());
   p.insert(p.end(), units.begin(), units.end());
   p.insert(p.end(), members.begin(), members.end());
-  for (const auto& l : lists) p.insert(p.end(), l.begin(), l.end());
+  p.insert(p.end(), list.begin(), list.end());
   return U;
 }
 

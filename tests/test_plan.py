@@ -34,7 +34,7 @@ def parse(p, B):
     lst = p[o:o + L]; o += L
     assert o == len(p)
     return dict(H=int(p[2]), GS=int(p[3]), U=U, cells=cells, skip=skip, blocks=blocks, ptr=ptr,
-                units=units, members=members, list=lst)
+                units=units, members=members, list=lst, chunk=int(p[8]))
 
 
 def brute_skip(tables, lens, nb):
@@ -87,6 +87,15 @@ def case(rng, kind):
                 tables[s, pre:pre + tail] = tb
                 tables[s, pre + tail] = next(free)
                 lens[s] = n
+    elif kind == "wide":  # many sharers: more than 8 member tiles per chunk (several groups)
+        B, pre = 40, 11
+        lens = 16 * pre + rng.integers(1, 40, size=B)
+        tables = np.full((B, 16), -1, np.int32)
+        free = iter(rng.permutation(np.arange(pre, nb)))
+        for s in range(B):
+            tables[s, :pre] = np.arange(pre)
+            for j in range(pre, -(-int(lens[s]) // 16)):
+                tables[s, j] = next(free)
     else:  # mixed: shared partial last blocks, unrelated rows, empty rows, bad entries
         B = 10
         tables = np.full((B, 8), -1, np.int32)
@@ -103,7 +112,7 @@ def case(rng, kind):
     return tables, np.asarray(lens, np.int32), nb
 
 
-@pytest.mark.parametrize("kind", ["prefix", "beam", "mixed"])
+@pytest.mark.parametrize("kind", ["prefix", "beam", "mixed", "wide"])
 @pytest.mark.parametrize("hq,hkv,dt", [(8, 8, torch.float16), (28, 4, torch.bfloat16),
                                        (16, 8, torch.bfloat16), (32, 2, torch.bfloat16)])
 def test_plan_matches_brute_force(kind, hq, hkv, dt):
@@ -126,7 +135,7 @@ def test_plan_matches_brute_force(kind, hq, hkv, dt):
     cell = 0
     for u in P["units"]:
         ref, b0, b1, off, cnt, cbase = (int(x) for x in u)
-        assert cbase == cell and 1 <= cnt <= max(1, 16 // G) and b0 < b1 <= b0 + 16
+        assert cbase == cell and 1 <= cnt <= max(1, 16 // G) and b0 < b1 <= b0 + P["chunk"]
         mem = P["members"][off:off + cnt]
         assert len(set(mem.tolist())) == cnt
         for k, s in enumerate(mem):

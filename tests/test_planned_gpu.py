@@ -91,7 +91,7 @@ SHAPES = [("f16", 8, 8, 128, 0), ("bf16", 8, 8, 64, 0), ("bf16", 28, 4, 128, 0),
           ("f16", 32, 32, 128, 2), ("bf16", 4, 4, 64, 2)]
 
 
-@pytest.mark.parametrize("kind", ["prefix", "beam", "mixed"])
+@pytest.mark.parametrize("kind", ["prefix", "beam", "mixed", "wide"])
 @pytest.mark.parametrize("dtype,hq,hkv,hd,kernel", SHAPES)
 def test_planned_matches_oracle(kind, dtype, hq, hkv, hd, kernel):
     m = pkv()
