@@ -488,7 +488,7 @@ def batching_main(args, torch, pkv, W):
             ev[1].record()
         new_ids = ids_rng.integers(0, 32000, size=n).astype(np.int32) if cache_on else None
         loop.decode(q[:n], k_new[:n], v_new[:n], scale, out=out[:n],
-                    events=None if ev is None else ev[2:], new_ids=new_ids)
+                    events=None if ev is None else ev[2:6], new_ids=new_ids)
         if stats is not None:
             lens = loop.last_lens.copy()
             u = loop.usage()
@@ -500,7 +500,7 @@ def batching_main(args, torch, pkv, W):
     for _ in range(cfg["settle_steps"] + args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     stats = []
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -508,20 +508,26 @@ def batching_main(args, torch, pkv, W):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     write_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    part_ms = [e[2].elapsed_time(e[3]) for e in evs]
-    merge_ms = [e[3].elapsed_time(e[4]) for e in evs]
+    shared_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    part_ms = [e[3].elapsed_time(e[4]) for e in evs]
+    merge_ms = [e[4].elapsed_time(e[5]) for e in evs]
     def unique(lens, tables):  # K+V bytes of the distinct cache slots read
         t = np.where(tables >= 0, tables & ~pkv.BLOCK_SHARED, tables)
         j = np.arange(t.shape[1])[None, :]
         valid = np.clip(lens[:, None].astype(np.int64) - 16 * j, 0, 16)
         best = np.zeros(nb, np.int64)
-        m = valid > 0
+        m = (valid > 0) & (t >= 0)
         np.maximum.at(best, t[m], valid[m])
         return int(best.sum()) * 2 * Hkv * hd * eb
     kv_logical = [st["kv"] for st in stats]
     kv = [unique(st["lens"], st["tables"]) for st in stats]
+    # with a plan the stream pass reads only the unshared blocks: the blocks whose table entry
+    # is not marked shared (the plan's runs are exactly the shared prefixes of the tables)
+    kv_private = [unique(st["lens"], np.where(st["tables"] & 0x40000000, -1, st["tables"]))
+                  if cache_on else k for st, k in zip(stats, kv)]
     qo = [2 * st["B"] * Hq * hd * eb + 4 * st["B"] * Hkv * hd * eb for st in stats]
-    algo = [a + b for a, b in zip(kv, qo)]
+    algo = [a + b for a, b in zip(kv_private, qo)]
+    attn_ms = [a + b + c for a, b, c in zip(shared_ms, part_ms, merge_ms)]
     ms_per_step = wall / args.steps * 1e3
     tokens = sum(st["B"] for st in stats)
     util_paged = [st["usage"]["utilisation"] for st in stats]
@@ -551,6 +557,8 @@ def batching_main(args, torch, pkv, W):
         "tokens_per_s_per_layer": round(tokens / wall, 1),
         "attn_stream_ms": round(float(np.mean(part_ms)), 4),
         "attn_merge_ms": round(float(np.mean(merge_ms)), 4),
+        "attn_shared_ms": round(float(np.mean(shared_ms)), 4),
+        "attention_unique_gbs": round((sum(kv) + sum(qo)) / (sum(attn_ms) / 1e3) / 1e9, 2),
         "batching": {
             "mean_running": round(tokens / args.steps, 2),
             "prefix_cache": cache_on,

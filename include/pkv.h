@@ -196,9 +196,12 @@ pkv_status pkv_decode_append_attn(void* out, const void* q, const void* k_new,
 /*  2. the stream pass over each sequence's remaining blocks (those after skip_s);            */
 /*  3. the merge: for planned sequences, their private pieces and shared pieces, in order.    */
 /* Results equal pkv_decode_attn's within rounding: the sums run in another order (the plan's), */
-/* deterministic for a given plan. The shared pass needs f16/bf16 and G = Hq/Hkv <= 16; for    */
-/* other shapes pkv_decode_plan returns a plan without runs (the planned call then does what  */
-/* the plain one does). Batches above 8192 sequences are not planned (PKV_ERR_UNSUPPORTED).    */
+/* deterministic for a given plan. pkv_decode_plan puts runs in a plan only for f16/bf16 and  */
+/* G = Hq/Hkv <= max_group (0: the default, 4 -- at least four sequences share each 16-row    */
+/* tile; with fewer, the plain matrix-core pass, which re-reads shared blocks from the L2, is  */
+/* faster; at most 16); for other shapes it returns a plan without runs (the planned call then */
+/* does what the plain one does). Batches above 8192 sequences are not planned                */
+/* (PKV_ERR_UNSUPPORTED).                                                                     */
 /*                                                                                            */
 /* Plan layout (int32, built by pkv_decode_plan, read by the kernels): header[16] = {magic,    */
 /* B, H, GS, U, M, L, cells, chunk, 0...}, skip[B], blocks[B] (ceil(n/16) when planned),       */
@@ -213,11 +216,12 @@ size_t pkv_decode_plan_max_ints(int32_t B, int32_t max_blocks);
 /* Host only (no GPU). block_tables/context_lens: host int32 [B][max_blocks] / [B] (the same   */
 /* contents the device copies will hold). plan: host buffer of capacity ints; *plan_ints      */
 /* receives the plan's size (also when capacity is too small: PKV_ERR_WORKSPACE). Errors:      */
-/* PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED (dtype), PKV_ERR_WORKSPACE.                        */
+/* PKV_ERR_INVALID_ARG (also max_group outside [0, 16]), PKV_ERR_UNSUPPORTED (dtype),           */
+/* PKV_ERR_WORKSPACE.                                                                          */
 pkv_status pkv_decode_plan(const int32_t* block_tables, const int32_t* context_lens, int32_t B,
                            int32_t max_blocks, int32_t max_context_len, int32_t Hq, int32_t Hkv,
-                           int32_t NB, pkv_dtype dtype, int32_t* plan, size_t capacity,
-                           size_t* plan_ints);
+                           int32_t NB, pkv_dtype dtype, int32_t max_group, int32_t* plan,
+                           size_t capacity, size_t* plan_ints);
 
 /* Workspace bytes of pkv_decode_planned (stream cells plus B*H private and the plan's shared   */
 /* cells); 0 on bad arguments or a plan built for another shape.                              */

@@ -83,8 +83,8 @@ SIGNATURES = {
     "pkv_alloc_fork_many": (c_i32, [c_vp, c_i32, c_vp, c_vp]),
     "pkv_alloc_usage": (c_i32, [c_vp, c_vp]),
     "pkv_decode_plan_max_ints": (c_sz, [c_i32, c_i32]),
-    "pkv_decode_plan": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp,
-                                c_sz, ctypes.POINTER(c_sz)]),
+    "pkv_decode_plan": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                c_vp, c_sz, ctypes.POINTER(c_sz)]),
     "pkv_decode_planned_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp,
                                                    c_sz]),
     "pkv_decode_planned": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,

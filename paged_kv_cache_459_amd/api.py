@@ -264,10 +264,11 @@ def pkv_decode_append_merge(out, k_new, v_new, k_cache, v_cache, block_tables, c
 
 
 def pkv_decode_plan(block_tables, context_lens, *, num_q_heads, num_kv_heads, num_blocks,
-                    max_context_len, dtype, out=None):
+                    max_context_len, dtype, out=None, max_group=0):
     """Shared-prefix plan of a batch from HOST copies of its tables [B, max_blocks] and lengths
     [B] (int32; table entries may carry BLOCK_SHARED). Returns an int32 NumPy array (a view of
-    ``out`` when that is large enough)."""
+    ``out`` when that is large enough). max_group: largest Hq/Hkv that gets runs (0: the
+    library's default)."""
     t = _as_c(block_tables, np.int32)
     lens = _as_c(context_lens, np.int32)
     if t.ndim != 2 or lens.shape != (t.shape[0],):
@@ -278,8 +279,8 @@ def pkv_decode_plan(block_tables, context_lens, *, num_q_heads, num_kv_heads, nu
         cap = 0 if out is None else int(out.size)
         st = lib.pkv_decode_plan(t.ctypes.data, lens.ctypes.data, B, mb, int(max_context_len),
                                  num_q_heads, num_kv_heads, int(num_blocks), pkv_dtype(dtype),
-                                 out.ctypes.data if out is not None else None, cap,
-                                 ctypes.byref(n))
+                                 int(max_group), out.ctypes.data if out is not None else None,
+                                 cap, ctypes.byref(n))
         if st == 0:
             return out[:n.value]
         if st != 6:  # anything but a too-small buffer

@@ -63,7 +63,10 @@ class ContinuousBatch:
         # the device; a step fills one set while the previous step's copies may still read
         # the other
         self._slot0 = self.max_batch + self.max_batch * self.max_blocks
-        n_int = self._slot0 + self.max_batch * self.max_ctx
+        self._plan0 = self._slot0 + self.max_batch * self.max_ctx
+        plan_cap = (int(api.lib.pkv_decode_plan_max_ints(self.max_batch, self.max_blocks))
+                    if self.prefix_cache else 0)
+        n_int = self._plan0 + plan_cap
         self._pin = [torch.empty(n_int, dtype=torch.int32, pin_memory=True) for _ in range(2)]
         self._dev = [torch.empty(n_int, dtype=torch.int32, device=self.device) for _ in range(2)]
         self._free = [torch.cuda.Event() for _ in range(2)]
@@ -174,8 +177,9 @@ class ContinuousBatch:
     def decode(self, q, k_new, v_new, scale, out=None, events=None, new_ids=None):
         """One decode step of every running request (rows of q/k_new/v_new in admission
         order; new_ids: the new tokens' ids, with prefix caching). Returns out [B, Hq, hd].
-        ``events``: optional three torch.cuda.Events recorded before the stream pass, between
-        the passes and after the merge pass."""
+        ``events``: optional torch.cuda.Events: three (before the first kernel, after the stream
+        pass, after the merge) or four (before, after the shared pass, after the stream pass,
+        after the merge; with prefix caching the step runs a shared-prefix plan)."""
         if (new_ids is not None) != self.prefix_cache:
             raise ValueError("new_ids are given exactly when prefix caching is on")
         B = len(self.run_id)
@@ -198,6 +202,18 @@ class ContinuousBatch:
         nt = self.max_batch + B * self.max_blocks
         dev[:B].copy_(self._pin[s][:B], non_blocking=True)
         dev[self.max_batch:nt].copy_(self._pin[s][self.max_batch:nt], non_blocking=True)
+        plan = plan_d = None
+        if self.prefix_cache:  # requests share cached blocks: a shared-prefix plan
+            plan = api.pkv_decode_plan(tables_h, lens_h, num_q_heads=self.Hq,
+                                       num_kv_heads=self.Hkv, num_blocks=self.nb,
+                                       max_context_len=self.max_ctx, dtype=self.dtype,
+                                       out=flat[self._plan0:])
+            plan_d = dev[self._plan0:self._plan0 + len(plan)]
+            plan_d.copy_(self._pin[s][self._plan0:self._plan0 + len(plan)], non_blocking=True)
+            need = api.pkv_decode_planned_workspace_bytes(B, self.Hq, self.Hkv, self.hd,
+                                                          self.dtype, self.W, plan)
+            if need > self.workspace.numel():
+                self.workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
         self._release_set()
         lens_d = dev[:B]
         tables_d = dev[self.max_batch:self.max_batch + B * self.max_blocks].view(
@@ -206,17 +222,28 @@ class ContinuousBatch:
             out = torch.empty_like(q)
         if events is not None:
             events[0].record()
-        api.pkv_decode_append_stream(q, k_new, v_new, self.k_cache, self.v_cache, tables_d,
-                                     lens_d, num_kv_heads=self.Hkv, scale=scale,
-                                     max_context_len=self.max_ctx, num_workers=self.W,
-                                     workspace=self.workspace, out=out)
-        if events is not None:
-            events[1].record()
-        api.pkv_decode_append_merge(out, k_new, v_new, self.k_cache, self.v_cache, tables_d,
-                                    lens_d, self.workspace, num_kv_heads=self.Hkv,
-                                    max_context_len=self.max_ctx, num_workers=self.W)
-        if events is not None:
-            events[2].record()
+        if plan is not None:  # shared pass, stream pass, merge
+            ev = None if events is None else ([events[1], events[1], events[2]]
+                                              if len(events) == 3 else events[1:4])
+            api.pkv_decode_planned(q, self.k_cache, self.v_cache, tables_d, lens_d, plan, plan_d,
+                                   num_kv_heads=self.Hkv, scale=scale,
+                                   max_context_len=self.max_ctx, num_workers=self.W,
+                                   workspace=self.workspace, k_new=k_new, v_new=v_new, out=out,
+                                   events=ev)
+        else:
+            if events is not None and len(events) == 4:
+                events[1].record()  # no shared pass
+            api.pkv_decode_append_stream(q, k_new, v_new, self.k_cache, self.v_cache, tables_d,
+                                         lens_d, num_kv_heads=self.Hkv, scale=scale,
+                                         max_context_len=self.max_ctx, num_workers=self.W,
+                                         workspace=self.workspace, out=out)
+            if events is not None:
+                events[-2].record()
+            api.pkv_decode_append_merge(out, k_new, v_new, self.k_cache, self.v_cache, tables_d,
+                                        lens_d, self.workspace, num_kv_heads=self.Hkv,
+                                        max_context_len=self.max_ctx, num_workers=self.W)
+            if events is not None:
+                events[-1].record()
         self.last_tables = tables_h
         self.last_lens = lens_h
         return out

@@ -290,9 +290,10 @@ size_t pkv_decode_plan_max_ints(int32_t B, int32_t max_blocks) {
 
 pkv_status pkv_decode_plan(const int32_t* block_tables, const int32_t* context_lens, int32_t B,
                            int32_t max_blocks, int32_t max_context_len, int32_t Hq, int32_t Hkv,
-                           int32_t NB, pkv_dtype dtype, int32_t* plan, size_t capacity,
-                           size_t* plan_ints) {
+                           int32_t NB, pkv_dtype dtype, int32_t max_group, int32_t* plan,
+                           size_t capacity, size_t* plan_ints) {
   if (!dtype_ok(dtype)) return PKV_ERR_UNSUPPORTED;
+  if (max_group < 0 || max_group > pkv::kRowsPerTile) return PKV_ERR_INVALID_ARG;
   if (B < 0 || B > kMaxBatch || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_blocks <= 0 ||
       NB <= 0 || max_context_len < 0 ||
       static_cast<int64_t>(max_blocks) * kBlockSize < max_context_len || !plan_ints)
@@ -302,7 +303,10 @@ pkv_status pkv_decode_plan(const int32_t* block_tables, const int32_t* context_l
   const int32_t kernel = current_kernel(dtype, Hq, Hkv);
   const int32_t H = kernel == pkv::kMatrix ? Hkv : Hq;
   const int32_t GS = kernel == pkv::kMatrix ? G : 1;
-  const bool share = dtype != PKV_F32 && G <= pkv::kRowsPerTile;  // the shared pass's reach
+  // The shared pass reads a chunk once per tile of 16 / G members: for G > 4 (two sequences
+  // or fewer per tile) the matrix-core stream kernel, whose sharers re-read the blocks from
+  // the L2, is faster, so such batches get no runs.
+  const bool share = dtype != PKV_F32 && G <= (max_group ? max_group : pkv::kMaxPlannedGroup);
   std::vector<int32_t> v;
   pkv::plan_build(block_tables, context_lens, B, max_blocks, max_context_len, NB, H, GS, G,
                   pkv::kPlanChunk, share, &v);

@@ -24,6 +24,7 @@ constexpr int kPlanHeader = 16;
 constexpr int kUnitInts = 6;      // ref_seq, b0, b1, member_off, member_cnt, cell_base
 constexpr int kRowsPerTile = 16;  // rows of one MFMA tile of the shared pass
 constexpr int kPlanChunk = 16;    // blocks per unit of a run
+constexpr int kMaxPlannedGroup = 4;  // q heads per kv head up to which batches are planned
 
 struct PlanView {
   int32_t U = 0, cells = 0;

@@ -121,7 +121,8 @@ def test_plan_matches_brute_force(kind, hq, hkv, dt):
     B = len(lens)
     G = hq // hkv
     p = m.pkv_decode_plan(tables, lens, num_q_heads=hq, num_kv_heads=hkv, num_blocks=nb,
-                          max_context_len=16 * tables.shape[1], dtype=dt)
+                          max_context_len=16 * tables.shape[1], dtype=dt,
+                          max_group=16)
     P = parse(p, B)
     kernel = m.pkv_decode_kernel(hq, hkv, dt)
     assert (P["H"], P["GS"]) == ((hkv, G) if kernel == 2 else (hq, 1))
@@ -197,3 +198,17 @@ def test_corrupted_plans_are_refused_on_the_host():
     c = p.copy()
     c[HDR] = c[HDR + B]  # skip_0 = blocks_0
     assert call(c, append=True) == 1
+
+
+@pytest.mark.parametrize("hq,hkv,runs", [(8, 8, True), (16, 4, True), (28, 4, False),
+                                         (32, 2, False)])
+def test_default_group_threshold(hq, hkv, runs):
+    """By default only G <= 4 gets runs (at least four sequences per 16-row tile)."""
+    rng = np.random.default_rng(5)
+    tables, lens, nb = case(rng, "prefix")
+    p = m.pkv_decode_plan(tables, lens, num_q_heads=hq, num_kv_heads=hkv, num_blocks=nb,
+                          max_context_len=256, dtype=torch.bfloat16)
+    assert (parse(p, len(lens))["U"] > 0) == runs
+    with pytest.raises(m.PkvError):
+        m.pkv_decode_plan(tables, lens, num_q_heads=hq, num_kv_heads=hkv, num_blocks=nb,
+                          max_context_len=256, dtype=torch.bfloat16, max_group=17)

@@ -69,7 +69,7 @@ def run_planned(m, q, kc, vc, tables, lens, nb, hq, hkv, hd, dtype, scale, *, W=
     ld = torch.from_numpy(np.ascontiguousarray(lens, np.int32)).cuda()
     max_ctx = 16 * tables.shape[1]
     plan = m.pkv_decode_plan(tables, lens, num_q_heads=hq, num_kv_heads=hkv, num_blocks=nb,
-                             max_context_len=max_ctx, dtype=dt)
+                             max_context_len=max_ctx, dtype=dt, max_group=16)
     plan_dev = torch.from_numpy(plan.copy()).cuda()
     W = W or m.pkv_decode_num_workers(hq, hkv, hd, dt)
     nbytes = m.pkv_decode_planned_workspace_bytes(len(lens), hq, hkv, hd, dt, W, plan)
