@@ -493,6 +493,7 @@ def batching_main(args, torch, pkv, W):
             lens = loop.last_lens.copy()
             u = loop.usage()
             stats.append(dict(B=n, retired=len(retired), admitted=len(admitted), T=T,
+                              planned=getattr(loop, "last_plan_units", 0) > 0,
                               prompt=sum(a[1] for a in admitted),
                               kv=int(lens.astype(np.int64).sum()) * 2 * Hkv * hd * eb,
                               lens=lens, tables=loop.last_tables.copy(), usage=u))
@@ -524,12 +525,18 @@ def batching_main(args, torch, pkv, W):
     # with a plan the stream pass reads only the unshared blocks: the blocks whose table entry
     # is not marked shared (the plan's runs are exactly the shared prefixes of the tables)
     kv_private = [unique(st["lens"], np.where(st["tables"] & 0x40000000, -1, st["tables"]))
-                  if cache_on else k for st, k in zip(stats, kv)]
+                  if st["planned"] else k for st, k in zip(stats, kv)]
     qo = [2 * st["B"] * Hq * hd * eb + 4 * st["B"] * Hkv * hd * eb for st in stats]
     algo = [a + b for a, b in zip(kv_private, qo)]
     attn_ms = [a + b + c for a, b, c in zip(shared_ms, part_ms, merge_ms)]
     ms_per_step = wall / args.steps * 1e3
     tokens = sum(st["B"] for st in stats)
+    if args.copy_calibration:  # a plain copy of known size, for the counter runs
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     util_paged = [st["usage"]["utilisation"] for st in stats]
     util_contig = [st["usage"]["logical_tokens"] / (st["usage"]["sequences"] * cfg["max_ctx"])
                    for st in stats]
@@ -562,6 +569,7 @@ def batching_main(args, torch, pkv, W):
         "batching": {
             "mean_running": round(tokens / args.steps, 2),
             "prefix_cache": cache_on,
+            "planned_steps": sum(st["planned"] for st in stats),
             "prompt_tokens_admitted_per_step": round(sum(st["prompt"] for st in stats)
                                                      / args.steps, 1),
             "admitted_per_step": round(sum(st["admitted"] for st in stats) / args.steps, 3),

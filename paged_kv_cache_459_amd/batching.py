@@ -203,11 +203,13 @@ class ContinuousBatch:
         dev[:B].copy_(self._pin[s][:B], non_blocking=True)
         dev[self.max_batch:nt].copy_(self._pin[s][self.max_batch:nt], non_blocking=True)
         plan = plan_d = None
+        self.last_plan_units = 0
         if self.prefix_cache:  # requests share cached blocks: a shared-prefix plan
             plan = api.pkv_decode_plan(tables_h, lens_h, num_q_heads=self.Hq,
                                        num_kv_heads=self.Hkv, num_blocks=self.nb,
                                        max_context_len=self.max_ctx, dtype=self.dtype,
                                        out=flat[self._plan0:])
+            self.last_plan_units = int(plan[4])
             plan_d = dev[self._plan0:self._plan0 + len(plan)]
             plan_d.copy_(self._pin[s][self._plan0:self._plan0 + len(plan)], non_blocking=True)
             need = api.pkv_decode_planned_workspace_bytes(B, self.Hq, self.Hkv, self.hd,
