@@ -160,3 +160,42 @@ def merge_partials(m, l, o):
     M = m[keep].max()
     w = np.exp(m[keep] - M)
     return (w @ o[keep]) / (w @ l[keep])
+
+
+def prefill_attention(q, k_cache, v_cache, block_tables, context_lens, query_start, *, scale,
+                      hkv, hd, bs, dtype, num_blocks=None):
+    """Causal attention of a batch's new prompt tokens over their paged K/V, float64
+    [T, Hq, hd].
+
+    [P1] §三 步驟二 (預填充): the input tokens' K/V are written into the sequence's blocks
+    (a fresh block each time one fills) before attention. The pages do not write out the
+    prefill attention itself; ours is the textbook causal form, found through the same block
+    table as decode: sequence i holds context_lens[i] = n_i tokens in the cache, its new
+    tokens are the last t_i = query_start[i+1] - query_start[i] of them (positions n_i - t_i
+    .. n_i - 1; the earlier ones may have been cached before, e.g. a shared prefix or an
+    earlier chunk of the prompt), and q row query_start[i] + k, the token at position
+    p = n_i - t_i + k, attends over tokens 0..p of its sequence.
+    """
+    qf = to_f64(q, dtype)
+    T, hq, _ = qf.shape
+    assert hq % hkv == 0
+    G = hq // hkv
+    qs = [int(x) for x in query_start]
+    assert qs[0] == 0 and qs[-1] == T and all(a <= b for a, b in zip(qs, qs[1:]))
+    if num_blocks is None:
+        num_blocks = np.asarray(k_cache).size // (hkv * hd * bs)
+    out = np.zeros((T, hq, hd), dtype=np.float64)
+    for i in range(len(qs) - 1):
+        n, t = int(context_lens[i]), qs[i + 1] - qs[i]
+        if t == 0:
+            continue
+        assert 0 < t <= n
+        K, V = gather_sequence(k_cache, v_cache, block_tables[i], n, num_blocks=num_blocks,
+                               hkv=hkv, hd=hd, bs=bs, dtype=dtype)
+        for k in range(t):
+            p = n - t + k
+            for h in range(hq):
+                g = h // G
+                out[qs[i] + k, h] = _dense_attention_one(qf[qs[i] + k, h], K[:p + 1, g, :],
+                                                         V[:p + 1, g, :], scale)
+    return out

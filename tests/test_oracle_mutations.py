@@ -4,7 +4,7 @@ Each case patches one oracle function with a wrong variant (a dropped scale, a w
 kv-head mapping, an off-by-one gather, a transposed tile, an unweighted merge, a LIFO free
 list, a missing copy-on-write, a skipped, reversed or half block copy, shared blocks counted per owner, a reservation
 counted as used, admission without headroom or out of arrival order, a prefix block matched without its
-parent) and runs an existing pin, which must then fail.
+parent, a prefill without its causal mask or off by one) and runs an existing pin, which must then fail.
 """
 
 import numpy as np
@@ -20,6 +20,7 @@ from tests import test_oracle_allocator as TAL
 from tests import test_oracle_attention as TA
 from tests import test_oracle_batching as TOB
 from tests import test_oracle_beam as TB
+from tests import test_oracle_prefill as TPF
 from tests import test_oracle_prefix_cache as TPC
 from tests import test_oracle_utilisation as TU
 
@@ -186,3 +187,39 @@ def test_prefix_match_without_parent_is_caught(monkeypatch):
         self.index = Parentless()
     monkeypatch.setattr(AL.BlockAllocator, "__init__", init)
     _fails(TPC.test_shared_blocks_hold_each_sequences_own_kv)
+
+
+def _prefill_with_window(monkeypatch, window):
+    """Replace the oracle's prefill by one whose query at position p sees tokens
+    [0, window(p, n)) instead of [0, p + 1)."""
+    def bad(q, k_cache, v_cache, block_tables, context_lens, query_start, *, scale, hkv, hd,
+            bs, dtype, num_blocks=None):
+        qf = L.to_f64(q, dtype)
+        T, hq, _ = qf.shape
+        G = hq // hkv
+        nbk = np.asarray(k_cache).size // (hkv * hd * bs)
+        out = np.zeros((T, hq, hd))
+        qs = [int(x) for x in query_start]
+        for i in range(len(qs) - 1):
+            n, t = int(context_lens[i]), qs[i + 1] - qs[i]
+            if t == 0:
+                continue
+            K, V = A.gather_sequence(k_cache, v_cache, block_tables[i], n, num_blocks=nbk,
+                                     hkv=hkv, hd=hd, bs=bs, dtype=dtype)
+            for k in range(t):
+                e = max(1, window(n - t + k, n))
+                for h in range(hq):
+                    out[qs[i] + k, h] = A._dense_attention_one(qf[qs[i] + k, h], K[:e, h // G],
+                                                               V[:e, h // G], scale)
+        return out
+    monkeypatch.setattr(A, "prefill_attention", bad)
+
+
+def test_prefill_without_causal_mask_is_caught(monkeypatch):
+    _prefill_with_window(monkeypatch, lambda p, n: n)
+    _fails(TPF.test_first_token_returns_its_value_and_last_equals_decode, "f32", 2, 2)
+
+
+def test_prefill_causal_off_by_one_is_caught(monkeypatch):
+    _prefill_with_window(monkeypatch, lambda p, n: p)
+    _fails(TPF.test_brute_force_tiny)
