@@ -247,6 +247,52 @@ pkv_status pkv_decode_planned(int32_t pass, void* out, const void* q, const void
                               size_t plan_ints, int32_t num_workers, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------------------------ */
+/* Paged prefill attention. [P1] §三 步驟二 (預填充): a prompt's tokens are written to the      */
+/* cache and attended; with a cached prefix ([P2] "共享和复用", automatic prefix caching) or in     */
+/* chunks, only the last q_s of a sequence's n_s tokens are new. Causal rule: the new token at */
+/* position pos = n_s - q_s + k (k = 0..q_s-1) attends to its own sequence's tokens 0..pos,   */
+/* all read from the paged cache through the block table (pkv_write them first):             */
+/*   out[t][h] = softmax_j(scale * q[t][h] . K[s][h/G][j], j <= pos) . V[s][h/G][j]            */
+/* with t = query_start[s] + k the row of the new token. f16/bf16 only (matrix cores), G <= 16. */
+/*                                                                                            */
+/* The work is planned on the host (pkv_prefill_plan, from host copies of query_start and    */
+/* context_lens): tiles of consecutive rows of one sequence, each split into chunks of at most */
+/* 64 blocks when its last row sees more (then every row's chunks give (m, l, o) pieces that  */
+/* a merge combines in chunk order, as pkv_decode_merge does). Plan layout (int32):            */
+/* header[16] = {magic 0x50524631, T, H, GS, U, M, L, cells, chunk, S, tile_rows, 0...},       */
+/* skip[T] (1: the row is merged), vis[T] (pos + 1), ptr[T+1], units[U][6] = {sequence, b0,   */
+/* b1, member_off, member_cnt, cell_base (-1: written directly)}, members[M] (rows),           */
+/* list[L] (each merged row's piece cells, in chunk order); H = Hkv, GS = G.                  */
+
+/* Host only. query_start: [S+1] with query_start[0] = 0, non-decreasing; T = query_start[S].  */
+/* context_lens: [S], q_s <= n_s <= max_context_len <= 16*max_blocks. plan: host buffer of    */
+/* capacity ints; *plan_ints receives the plan's size (also with PKV_ERR_WORKSPACE when the   */
+/* capacity is too small). Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED (f32, G > 16),    */
+/* PKV_ERR_WORKSPACE.                                                                          */
+pkv_status pkv_prefill_plan(const int32_t* query_start, const int32_t* context_lens, int32_t S,
+                            int32_t max_blocks, int32_t max_context_len, int32_t Hq, int32_t Hkv,
+                            pkv_dtype dtype, int32_t* plan, size_t capacity, size_t* plan_ints);
+
+/* Workspace bytes of pkv_prefill_attn for this plan: cells*G*(2 + hd)*4 rounded up ((m, l)    */
+/* at 0, then o at round_up(cells*G*8, 256)); may be 0 (every tile direct). (size_t)-1 on bad   */
+/* arguments or a plan that is not a prefill plan.                                            */
+size_t pkv_prefill_workspace_bytes(int32_t Hq, int32_t Hkv, int32_t hd, const int32_t* plan,
+                                   size_t plan_ints);
+
+/* out, q: device [T][Hq][hd] in dtype (16-byte aligned). k_cache, v_cache, block_tables       */
+/* ([S][max_blocks] device int32) as pkv_decode_attn; the cache already holds every token     */
+/* attended. plan_host and plan_dev hold the same plan_ints entries, built for these           */
+/* query_start/context_lens and shapes. Writes only out (and the workspace). Errors:          */
+/* PKV_ERR_INVALID_ARG (shapes, pointers, a plan that fails the check), PKV_ERR_UNSUPPORTED,  */
+/* PKV_ERR_WORKSPACE, PKV_ERR_HIP. Stream-ordered, asynchronous.                               */
+pkv_status pkv_prefill_attn(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t S, int32_t T, int32_t Hq,
+                            int32_t Hkv, int32_t hd, int32_t bs, int32_t NB, int32_t max_blocks,
+                            int32_t max_context_len, float scale, pkv_dtype dtype,
+                            const int32_t* plan_host, const int32_t* plan_dev, size_t plan_ints,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes pkv_decode_attn needs for this shape on the current device (0 if B == 0 or */
 /* the arguments are invalid).                                                                 */
 size_t pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t hd,

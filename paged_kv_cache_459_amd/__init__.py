@@ -1,4 +1,4 @@
-"""PagedAttention decode on AMD Instinct MI355X (gfx950).
+"""PagedAttention decode (and paged prefill) on AMD Instinct MI355X (gfx950).
 
 The work runs in ``libpkv.so`` (hand-written HIP kernels and a C++ block allocator behind the
 C ABI in ``include/pkv.h``); this package only marshals arguments. Importing it fails if the
@@ -13,5 +13,5 @@ from .api import (BLOCK_SIZE, BlockAllocator, alloc_caches, cache_bytes,  # noqa
                   pkv_decode_num_workers, pkv_decode_plan, pkv_decode_planned,
                   pkv_decode_planned_workspace_bytes, pkv_decode_stream,
                   pkv_decode_stream_workspace_bytes,
-                  pkv_decode_workspace_bytes, pkv_dtype, pkv_set_attn_kernel, pkv_write,
-                  split_workspace)
+                  pkv_decode_workspace_bytes, pkv_dtype, pkv_prefill_attn, pkv_prefill_plan,
+                  pkv_prefill_workspace_bytes, pkv_set_attn_kernel, pkv_write, split_workspace)

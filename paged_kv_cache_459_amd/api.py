@@ -329,6 +329,76 @@ def pkv_decode_planned(q, k_cache, v_cache, block_tables, context_lens, plan, pl
     return out
 
 
+def pkv_prefill_plan(query_start, context_lens, *, num_q_heads, num_kv_heads, max_blocks,
+                     max_context_len, dtype, out=None):
+    """Prefill plan from HOST copies of query_start [S+1] and context_lens [S] (int32): the new
+    tokens of sequence s are the last query_start[s+1] - query_start[s] of its context_lens[s].
+    Returns an int32 NumPy array (a view of ``out`` when that is large enough)."""
+    qs = _as_c(query_start, np.int32)
+    lens = _as_c(context_lens, np.int32)
+    if qs.ndim != 1 or lens.shape != (qs.size - 1,):
+        raise ValueError("query_start must be [S+1] and context_lens [S]")
+    S = lens.size
+    n = ctypes.c_size_t(0)
+    for _ in range(2):
+        cap = 0 if out is None else int(out.size)
+        st = lib.pkv_prefill_plan(qs.ctypes.data, lens.ctypes.data, S, int(max_blocks),
+                                  int(max_context_len), num_q_heads, num_kv_heads,
+                                  pkv_dtype(dtype), out.ctypes.data if out is not None else None,
+                                  cap, ctypes.byref(n))
+        if st == 0:
+            return out[:n.value]
+        if st != 6:  # anything but a too-small buffer
+            check(st, "pkv_prefill_plan")
+        out = np.empty(n.value, np.int32)
+    raise RuntimeError("pkv_prefill_plan: plan size changed between calls")
+
+
+def pkv_prefill_workspace_bytes(num_q_heads, num_kv_heads, head_dim, plan):
+    p = _as_c(plan, np.int32)
+    n = int(lib.pkv_prefill_workspace_bytes(num_q_heads, num_kv_heads, head_dim, p.ctypes.data,
+                                            p.size))
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("not a prefill plan for these heads")
+    return n
+
+
+def pkv_prefill_attn(q, k_cache, v_cache, block_tables, plan, plan_dev, *, num_kv_heads, scale,
+                     max_context_len, workspace=None, out=None):
+    """out [T, Hq, hd] = causal attention of the T new prompt tokens over their sequences'
+    paged caches (see include/pkv.h). plan: the host plan from pkv_prefill_plan (NumPy int32),
+    plan_dev: the same ints on the device. Allocates the workspace if none is given."""
+    _need(q, "q")
+    dev = q.device
+    for t, name in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, name, dtype=q.dtype, device=dev)
+    _need(block_tables, "block_tables", dtype=torch.int32, device=dev)
+    _need(plan_dev, "plan_dev", dtype=torch.int32, device=dev)
+    if q.dim() != 3 or block_tables.dim() != 2:
+        raise ValueError("q must be [T, Hq, hd] and block_tables [S, max_blocks]")
+    T, hq, hd = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype=q.dtype, device=dev)
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    p = _as_c(plan, np.int32)
+    if plan_dev.numel() < p.size:
+        raise ValueError("plan_dev is shorter than the plan")
+    S, mb = block_tables.shape
+    nb = _num_blocks(k_cache, num_kv_heads, hd)
+    need = pkv_prefill_workspace_bytes(hq, num_kv_heads, hd, p)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    check(lib.pkv_prefill_attn(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(block_tables), S, T, hq, num_kv_heads, hd, BLOCK_SIZE, nb, mb,
+                               int(max_context_len), float(scale), pkv_dtype(q), p.ctypes.data,
+                               _ptr(plan_dev), p.size, _ptr(workspace), ws_bytes,
+                               _stream(dev)), "pkv_prefill_attn")
+    return out
+
+
 def split_workspace(workspace, batch, num_q_heads, num_kv_heads, head_dim, num_workers, kernel):
     """Views (seg int32 [B+1], ml float32 [W, 2, GS, 2], o float32 [W, 2, GS, hd]) of a stream
     workspace, for the kernel the stream pass used (1 vector, 2 matrix core)."""

@@ -81,6 +81,20 @@ Layout stream_layout(int32_t B, int32_t Hq, int32_t Hkv, int32_t hd, int32_t ker
   return L;
 }
 
+// Prefill workspace: (m, l) then o of the plan's cells (GS rows each); 0 bytes without cells.
+struct PrefillLayout {
+  size_t ml, o, bytes;
+};
+
+PrefillLayout prefill_layout(int64_t cells, int32_t GS, int32_t hd) {
+  PrefillLayout L{};
+  const size_t rows = static_cast<size_t>(cells) * GS;
+  L.ml = 0;
+  L.o = round_up256(rows * 2 * sizeof(float));
+  L.bytes = rows == 0 ? 0 : L.o + rows * hd * sizeof(float);
+  return L;
+}
+
 // Tile positions of a launch stay in int32: T + W <= B * max_blocks * H + W < 2^31.
 bool stream_fits(int32_t B, int32_t max_blocks, int32_t H, int32_t W) {
   return B <= kMaxBatch &&
@@ -165,6 +179,7 @@ pkv::StreamParams make_params(void* out, const void* q, const void* k_new, const
   p.ws_seg = reinterpret_cast<int32_t*>(base);
   p.ws_ml = reinterpret_cast<float*>(base + L.seg);
   p.ws_o = reinterpret_cast<float*>(base + L.ml);
+  p.table_rows = B;
   return p;
 }
 
@@ -381,11 +396,116 @@ pkv_status pkv_decode_planned(int32_t pass, void* out, const void* q, const void
   p.sh_list = p.members + plan_host[5];
   p.num_units = pv.U;
   p.shared_cells = pv.cells;
+  p.shared_base = 2 * W + B * L0.H;
   if ((pass == 0 || pass == 1) && pkv::launch_shared(p, dtype, kernel, hs) != hipSuccess)
     return PKV_ERR_HIP;
   if ((pass == 0 || pass == 2) && pkv::launch_stream(p, dtype, kernel, hs) != hipSuccess)
     return PKV_ERR_HIP;
   if ((pass == 0 || pass == 3) && pkv::launch_merge(p, dtype, kernel, hs) != hipSuccess)
+    return PKV_ERR_HIP;
+  return PKV_OK;
+}
+
+pkv_status pkv_prefill_plan(const int32_t* query_start, const int32_t* context_lens, int32_t S,
+                            int32_t max_blocks, int32_t max_context_len, int32_t Hq, int32_t Hkv,
+                            pkv_dtype dtype, int32_t* plan, size_t capacity, size_t* plan_ints) {
+  if (!dtype_ok(dtype)) return PKV_ERR_UNSUPPORTED;
+  if (S < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_blocks <= 0 || max_context_len < 0 ||
+      static_cast<int64_t>(max_blocks) * kBlockSize < max_context_len || !plan_ints ||
+      (S > 0 && (!query_start || !context_lens)))
+    return PKV_ERR_INVALID_ARG;
+  if (dtype == PKV_F32 || Hq / Hkv > pkv::kRowsPerTile) return PKV_ERR_UNSUPPORTED;
+  if (S == 0 ? (query_start && query_start[0] != 0) : query_start[0] != 0)
+    return PKV_ERR_INVALID_ARG;
+  for (int32_t s = 0; s < S; ++s) {
+    const int64_t q = static_cast<int64_t>(query_start[s + 1]) - query_start[s];
+    if (q < 0 || context_lens[s] < q || context_lens[s] > max_context_len)
+      return PKV_ERR_INVALID_ARG;
+  }
+  const int32_t T = S > 0 ? query_start[S] : 0;
+  if (static_cast<int64_t>(T) * Hq * 64 >= (int64_t{1} << 31)) return PKV_ERR_UNSUPPORTED;
+  const int32_t G = Hq / Hkv;
+  std::vector<int32_t> v;
+  const int32_t zero = 0;
+  pkv::prefill_plan_build(S > 0 ? query_start : &zero, context_lens, S, Hkv, G,
+                          pkv::kRowsPerTile / G, pkv::kMaxUnitBlocks, &v);
+  *plan_ints = v.size();
+  if (!plan || capacity < v.size()) return PKV_ERR_WORKSPACE;
+  std::memcpy(plan, v.data(), v.size() * sizeof(int32_t));
+  return PKV_OK;
+}
+
+size_t pkv_prefill_workspace_bytes(int32_t Hq, int32_t Hkv, int32_t hd, const int32_t* plan,
+                                   size_t plan_ints) {
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || !head_dim_ok(hd) || !plan ||
+      plan_ints < static_cast<size_t>(pkv::kPlanHeader) || plan[0] != pkv::kPrefillMagic ||
+      plan[2] != Hkv || plan[3] != Hq / Hkv || plan[7] < 0)
+    return static_cast<size_t>(-1);
+  return prefill_layout(plan[7], Hq / Hkv, hd).bytes;
+}
+
+pkv_status pkv_prefill_attn(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t S, int32_t T, int32_t Hq,
+                            int32_t Hkv, int32_t hd, int32_t bs, int32_t NB, int32_t max_blocks,
+                            int32_t max_context_len, float scale, pkv_dtype dtype,
+                            const int32_t* plan_host, const int32_t* plan_dev, size_t plan_ints,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype) || bs != kBlockSize || !head_dim_ok(hd)) return PKV_ERR_UNSUPPORTED;
+  if (S < 0 || T < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Hq > 65535 || NB <= 0 ||
+      max_blocks <= 0 || max_context_len < 0 ||
+      static_cast<int64_t>(max_blocks) * kBlockSize < max_context_len ||
+      static_cast<int64_t>(NB) * kBlockSize >= (int64_t{1} << 31) || !std::isfinite(scale))
+    return PKV_ERR_INVALID_ARG;
+  if (dtype == PKV_F32 || Hq / Hkv > pkv::kRowsPerTile) return PKV_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(T) * Hq * 64 >= (int64_t{1} << 31)) return PKV_ERR_UNSUPPORTED;
+  if (T == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !plan_host || !plan_dev)
+    return PKV_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (reinterpret_cast<uintptr_t>(block_tables) & 3u) ||
+      (reinterpret_cast<uintptr_t>(plan_dev) & 3u))
+    return PKV_ERR_INVALID_ARG;
+  const int32_t G = Hq / Hkv;
+  pkv::PlanView pv;
+  if (!pkv::prefill_plan_check(plan_host, plan_ints, T, S, max_blocks, max_context_len, Hkv, G,
+                               pkv::kRowsPerTile / G, pkv::kMaxUnitBlocks, &pv))
+    return PKV_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(pv.U) * Hkv >= (int64_t{1} << 31) - pkv::kWaves * 8)
+    return PKV_ERR_UNSUPPORTED;
+  const PrefillLayout L = prefill_layout(pv.cells, G, hd);
+  if (L.bytes > 0 && (!workspace || workspace_bytes < L.bytes)) return PKV_ERR_WORKSPACE;
+  if (L.bytes > 0 && !aligned16(workspace)) return PKV_ERR_INVALID_ARG;
+  auto hs = static_cast<hipStream_t>(stream);
+  pkv::StreamParams p{};
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.B = T;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.hd = hd;
+  p.NB = NB;
+  p.max_blocks = max_blocks;
+  p.max_ctx = max_context_len;
+  p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  char* ws = static_cast<char*>(workspace);
+  p.ws_ml = L.bytes > 0 ? reinterpret_cast<float*>(ws + L.ml) : nullptr;
+  p.ws_o = L.bytes > 0 ? reinterpret_cast<float*>(ws + L.o) : nullptr;
+  const int32_t* base = plan_dev + pkv::kPlanHeader;
+  p.skip = base;
+  p.row_vis = base + T;
+  p.sh_ptr = base + 2 * static_cast<size_t>(T);
+  p.units = p.sh_ptr + T + 1;
+  p.members = p.units + static_cast<size_t>(pv.U) * pkv::kUnitInts;
+  p.sh_list = p.members + plan_host[5];
+  p.num_units = pv.U;
+  p.shared_cells = pv.cells;
+  p.shared_base = 0;
+  p.table_rows = S;
+  if (pkv::launch_shared(p, dtype, pkv::kMatrix, hs) != hipSuccess) return PKV_ERR_HIP;
+  if (pv.has_shared && pkv::launch_merge(p, dtype, pkv::kMatrix, hs) != hipSuccess)
     return PKV_ERR_HIP;
   return PKV_OK;
 }

@@ -825,7 +825,10 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_matrix_kernel(const StreamParams p)
 //
 // Waves map to (kv head, unit) unit-fastest, and work-groups are laid XCD-contiguously, so the
 // member tiles of one chunk run side by side on one XCD. Each row's (m, l, o) goes to its cell:
-// 2W + B*H + cell_base + member*H + head slot, row (q head % GS), in the stream pass's layout.
+// shared_base + cell_base + member*H + head slot, row (q head % GS), in the stream pass's
+// layout. The same kernel serves prefill: rows are then new prompt tokens (member = q row),
+// each seeing its position + 1 tokens (row_vis), the unit's blocks from its sequence's table;
+// a unit with cell_base -1 holds all of its rows' tokens and writes their outputs directly.
 template <int DT, int HD>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(3))) attn_shared_kernel(const StreamParams p, int H, int GS) {
@@ -843,7 +846,7 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_shared_kernel(const StreamParams p,
   const int32_t* e = p.units + static_cast<size_t>(u) * kUnitInts;
   const int ref = uniform(e[0]), b0 = uniform(max(e[1], 0)), b1 = uniform(min(e[2], p.max_blocks));
   const int moff = uniform(e[3]), mcnt = uniform(e[4]), cbase = uniform(e[5]);
-  if (ref < 0 || ref >= p.B || b0 >= b1) return;
+  if (ref < 0 || ref >= p.table_rows || b0 >= b1) return;
 
   const int lane = threadIdx.x & 63;
   const int G = p.Hq / p.Hkv;
@@ -894,7 +897,10 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_shared_kernel(const StreamParams p,
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) qb[s2] = make_uint4(0, 0, 0, 0);
   }
-  const int n_row = row_ok ? clamp_len(p, seq) : 0;
+  // visible tokens: the row's sequence length (decode) or its position + 1 (prefill)
+  const int n_row = !row_ok ? 0
+                    : p.row_vis != nullptr ? min(max(p.row_vis[seq], 0), p.max_ctx)
+                                           : clamp_len(p, seq);
   // q settled here: a first use inside the loop would put its wait (for every load issued
   // before it, the tiles included) at the top of each iteration
 #pragma unroll
@@ -972,11 +978,19 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_shared_kernel(const StreamParams p,
   l += __shfl_xor(l, 32);
   if (!row_ok) return;
   const int qh = kvh * G + jq;
+  if (cbase < 0) {  // a direct unit (prefill): the unit saw all of its rows' tokens
+    const size_t orow = (static_cast<size_t>(seq) * p.Hq + qh) * HD;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int j = 0; j < VT; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Elem<DT>::put(p.out, orow + 16 * j + 4 * g + i, o[j][i] * inv);
+    return;
+  }
   const int slot = qh / GS, nr = qh - slot * GS;
   const int rel = cbase + mk * H + slot;
-  if (rel < 0 || rel >= p.shared_cells) return;
-  const size_t cell = (2 * static_cast<size_t>(p.num_workers) + static_cast<size_t>(p.B) * H +
-                       static_cast<size_t>(rel)) * GS + nr;
+  if (rel >= p.shared_cells) return;
+  const size_t cell = (static_cast<size_t>(p.shared_base) + static_cast<size_t>(rel)) * GS + nr;
 #pragma unroll
   for (int j = 0; j < VT; ++j)
     *reinterpret_cast<float4_t*>(p.ws_o + cell * HD + 16 * j + 4 * g) = o[j];
@@ -1037,9 +1051,10 @@ merge_kernel(const StreamParams p, int H, int GS) {
   if (p.k_new != nullptr && hh % (p.Hq / p.Hkv) == 0) store_new_token<DT, HD>(p, i, hh / (p.Hq / p.Hkv));
   const int h = hh / GS, n = hh - h * GS;
   const bool planned = p.skip != nullptr && p.skip[i] > 0;
-  const int C = p.ws_seg[p.B];
-  const int s0 = p.ws_seg[i];
-  const int c = p.ws_seg[i + 1] - s0;
+  // prefill has no stream pass (ws_seg null): shared-pass pieces only
+  const int C = p.ws_seg != nullptr ? p.ws_seg[p.B] : 0;
+  const int s0 = p.ws_seg != nullptr ? p.ws_seg[i] : 0;
+  const int c = p.ws_seg != nullptr ? p.ws_seg[i + 1] - s0 : 0;
   int np_priv = 0, wf = 0, slot0 = 0;
   bool own_cell = false;
   if (c > 0) {
@@ -1068,7 +1083,7 @@ merge_kernel(const StreamParams p, int H, int GS) {
   }
   const int np = np_priv + nsh;
   const size_t wcells = 2 * static_cast<size_t>(p.num_workers);
-  const size_t shared0 = wcells + static_cast<size_t>(p.B) * H;
+  const size_t shared0 = static_cast<size_t>(p.shared_base);
   auto cell = [&](int k) -> size_t {
     size_t c0;
     if (k < np_priv) {

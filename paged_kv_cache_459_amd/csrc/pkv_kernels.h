@@ -25,6 +25,8 @@ constexpr int kUnitInts = 6;      // ref_seq, b0, b1, member_off, member_cnt, ce
 constexpr int kRowsPerTile = 16;  // rows of one MFMA tile of the shared pass
 constexpr int kPlanChunk = 16;    // blocks per unit of a run
 constexpr int kMaxPlannedGroup = 4;  // q heads per kv head up to which batches are planned
+constexpr int kMaxUnitBlocks = 64;   // blocks of one unit (one block id per lane)
+constexpr int32_t kPrefillMagic = 0x50524631;
 
 struct PlanView {
   int32_t U = 0, cells = 0;
@@ -41,6 +43,19 @@ int32_t plan_build(const int32_t* tables, const int32_t* lens, int32_t B, int32_
 // sequence's newest token must not be shared.
 bool plan_check(const int32_t* p, size_t n, int32_t B, int32_t max_blocks, int32_t H, int32_t GS,
                 int32_t G, bool append, PlanView* v);
+// Prefill plan. Rows are the T = query_start[S] new prompt tokens, sequence s's being the last
+// q_s = query_start[s+1] - query_start[s] of its context_lens[s] tokens; the row at position
+// pos sees vis = pos + 1 tokens. Units cover (sequence, tile of up to tile_rows consecutive
+// rows, chunk of the blocks the tile's last row sees); a tile whose blocks fit one chunk has
+// one unit, marked direct (cell_base -1: its rows are written straight to the output), the
+// others give each row one piece per chunk it sees, merged afterwards. Layout: header (magic
+// kPrefillMagic, T, H, GS, U, M, L, cells, chunk, S, tile_rows), skip[T] (1: the row merges),
+// vis[T], sh_ptr[T+1], units[U][6], members[M] (rows), sh_list[L].
+void prefill_plan_build(const int32_t* query_start, const int32_t* lens, int32_t S, int32_t H,
+                        int32_t GS, int32_t tile_rows, int32_t chunk, std::vector<int32_t>* out);
+bool prefill_plan_check(const int32_t* p, size_t n, int32_t T, int32_t S, int32_t max_blocks,
+                        int32_t max_ctx, int32_t H, int32_t GS, int32_t max_tile_rows,
+                        int32_t max_chunk, PlanView* v);
 
 struct WriteParams {
   const void* k;
@@ -85,8 +100,14 @@ struct StreamParams {
   const int32_t* sh_ptr;   // [B + 1] CSR over sh_list
   const int32_t* sh_list;  // shared-piece cells of each sequence (plus its head slot)
   const int32_t* units;    // [U][kUnitInts]
-  const int32_t* members;  // batch rows of the units' members
+  const int32_t* members;  // q rows of the units' members (decode: sequences)
   int32_t num_units, shared_cells;
+  int32_t shared_base;     // first cell of the shared pieces (decode: 2W + B*H)
+  int32_t table_rows;      // rows of block_tables (decode: B)
+  // Prefill (null for decode): visible tokens of each row (its position + 1); the rows are
+  // then new prompt tokens, q and out are [T][Hq][hd], and there is no stream pass (ws_seg
+  // null for the merge).
+  const int32_t* row_vis;
 };
 
 // dtype: 0 f32, 1 f16, 2 bf16 (pkv_dtype). Return the launch status (hipGetLastError).

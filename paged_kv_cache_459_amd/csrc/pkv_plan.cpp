@@ -163,7 +163,7 @@ bool plan_check(const int32_t* p, size_t n, int32_t B, int32_t max_blocks, int32
       p[3] != GS)
     return false;
   const int64_t U = p[4], M = p[5], L = p[6], cells = p[7];
-  if (U < 0 || M < 0 || L < 0 || cells < 0 || p[8] <= 0) return false;
+  if (U < 0 || M < 0 || L < 0 || cells < 0 || p[8] <= 0 || p[8] > kMaxUnitBlocks) return false;
   const int64_t need = kPlanHeader + 3 * static_cast<int64_t>(B) + 1 + U * kUnitInts + M + L;
   if (static_cast<int64_t>(n) != need || cells > (int64_t{1} << 30)) return false;
   const int32_t* skip = p + kPlanHeader;
@@ -183,7 +183,9 @@ bool plan_check(const int32_t* p, size_t n, int32_t B, int32_t max_blocks, int32
   const int32_t per_tile = std::max(1, kRowsPerTile / G);
   for (int64_t u = 0; u < U; ++u) {
     const int32_t* e = units + u * kUnitInts;
-    if (e[0] < 0 || e[0] >= B || e[1] < 0 || e[1] >= e[2] || e[2] > max_blocks) return false;
+    if (e[0] < 0 || e[0] >= B || e[1] < 0 || e[1] >= e[2] || e[2] > max_blocks ||
+        e[2] - e[1] > p[8])
+      return false;
     if (e[3] < 0 || e[4] < 1 || e[4] > per_tile || static_cast<int64_t>(e[3]) + e[4] > M)
       return false;
     if (e[5] < 0 || static_cast<int64_t>(e[5]) + static_cast<int64_t>(e[4]) * H > cells)
@@ -191,6 +193,121 @@ bool plan_check(const int32_t* p, size_t n, int32_t B, int32_t max_blocks, int32
   }
   for (int64_t k = 0; k < M; ++k)
     if (members[k] < 0 || members[k] >= B) return false;
+  for (int64_t k = 0; k < L; ++k)
+    if (list[k] < 0 || static_cast<int64_t>(list[k]) + H > cells) return false;
+  v->U = static_cast<int32_t>(U);
+  v->cells = static_cast<int32_t>(cells);
+  v->has_shared = L > 0;
+  return true;
+}
+
+// ---- prefill ----------------------------------------------------------------------------
+//
+// [P1] §三 (the prompt's tokens are written to the cache, then attended) and the causal rule
+// of attention: the prompt token at position pos attends to positions 0..pos of its own
+// sequence, the cached prefix included. The same (m, l, o) pieces and merge as decode serve a
+// row whose visible blocks are split over several chunks.
+
+void prefill_plan_build(const int32_t* qs, const int32_t* lens, int32_t S, int32_t H, int32_t GS,
+                        int32_t tile_rows, int32_t chunk, std::vector<int32_t>* out) {
+  const int32_t T = qs[S];
+  std::vector<int32_t> skip(T, 0), vis(T, 0), count(T, 0);
+  std::vector<int32_t> units, members;
+  int32_t cells = 0;
+  for (int32_t s = 0; s < S; ++s) {
+    const int32_t q0 = qs[s], q = qs[s + 1] - q0, n = lens[s];
+    for (int32_t t = 0; t < q; ++t) vis[q0 + t] = n - q + t + 1;
+    for (int32_t a = 0; a < q; a += tile_rows) {
+      const int32_t cnt = std::min(tile_rows, q - a);
+      // the tile's last row sees the most blocks
+      const int32_t nb = (vis[q0 + a + cnt - 1] + kBlockSize - 1) / kBlockSize;
+      const bool direct = nb <= chunk;
+      for (int32_t b0 = 0; b0 < nb; b0 += chunk) {
+        const int32_t b1 = std::min(nb, b0 + chunk);
+        units.insert(units.end(), {s, b0, b1, static_cast<int32_t>(members.size()), cnt,
+                                   direct ? -1 : cells});
+        for (int32_t k = 0; k < cnt; ++k) {
+          const int32_t r = q0 + a + k;
+          members.push_back(r);
+          if (!direct && vis[r] > kBlockSize * b0) ++count[r];
+        }
+        if (!direct) cells += cnt * H;
+      }
+      if (!direct)
+        for (int32_t k = 0; k < cnt; ++k) skip[q0 + a + k] = 1;
+    }
+  }
+  // each merged row's piece cells, in unit order (CSR); a chunk wholly past a row's position
+  // gives it no piece
+  std::vector<int32_t> ptr(T + 1, 0);
+  for (int32_t r = 0; r < T; ++r) ptr[r + 1] = ptr[r] + count[r];
+  std::vector<int32_t> list(ptr[T]);
+  {
+    std::vector<int32_t> fill(ptr.begin(), ptr.end() - 1);
+    for (size_t u = 0; u < units.size(); u += kUnitInts) {
+      const int32_t b0 = units[u + 1], off = units[u + 3], cnt = units[u + 4], base = units[u + 5];
+      if (base < 0) continue;
+      for (int32_t k = 0; k < cnt; ++k) {
+        const int32_t r = members[off + k];
+        if (vis[r] > kBlockSize * b0) list[fill[r]++] = base + k * H;
+      }
+    }
+  }
+  std::vector<int32_t>& p = *out;
+  p.assign(kPlanHeader, 0);
+  p[0] = kPrefillMagic;
+  p[1] = T;
+  p[2] = H;
+  p[3] = GS;
+  p[4] = static_cast<int32_t>(units.size() / kUnitInts);
+  p[5] = static_cast<int32_t>(members.size());
+  p[6] = ptr[T];
+  p[7] = cells;
+  p[8] = chunk;
+  p[9] = S;
+  p[10] = tile_rows;
+  p.insert(p.end(), skip.begin(), skip.end());
+  p.insert(p.end(), vis.begin(), vis.end());
+  p.insert(p.end(), ptr.begin(), ptr.end());
+  p.insert(p.end(), units.begin(), units.end());
+  p.insert(p.end(), members.begin(), members.end());
+  p.insert(p.end(), list.begin(), list.end());
+}
+
+bool prefill_plan_check(const int32_t* p, size_t n, int32_t T, int32_t S, int32_t max_blocks,
+                        int32_t max_ctx, int32_t H, int32_t GS, int32_t max_tile_rows,
+                        int32_t max_chunk, PlanView* v) {
+  if (n < static_cast<size_t>(kPlanHeader) || p[0] != kPrefillMagic || p[1] != T || p[2] != H ||
+      p[3] != GS || p[9] != S)
+    return false;
+  const int64_t U = p[4], M = p[5], L = p[6], cells = p[7], chunk = p[8], rows = p[10];
+  if (U < 0 || M < 0 || L < 0 || cells < 0 || chunk <= 0 || chunk > max_chunk || rows <= 0 ||
+      rows > max_tile_rows)
+    return false;
+  const int64_t need = kPlanHeader + 3 * static_cast<int64_t>(T) + 1 + U * kUnitInts + M + L;
+  if (static_cast<int64_t>(n) != need || cells > (int64_t{1} << 30)) return false;
+  const int32_t* skip = p + kPlanHeader;
+  const int32_t* vis = skip + T;
+  const int32_t* ptr = vis + T;
+  const int32_t* units = ptr + T + 1;
+  const int32_t* members = units + U * kUnitInts;
+  const int32_t* list = members + M;
+  for (int32_t r = 0; r < T; ++r) {
+    if (skip[r] < 0 || skip[r] > 1 || vis[r] < 1 || vis[r] > max_ctx || ptr[r + 1] < ptr[r])
+      return false;
+  }
+  if (ptr[0] != 0 || ptr[T] != L) return false;
+  for (int64_t u = 0; u < U; ++u) {
+    const int32_t* e = units + u * kUnitInts;
+    if (e[0] < 0 || e[0] >= S || e[1] < 0 || e[1] >= e[2] || e[2] > max_blocks ||
+        e[2] - e[1] > chunk)
+      return false;
+    if (e[3] < 0 || e[4] < 1 || e[4] > rows || static_cast<int64_t>(e[3]) + e[4] > M) return false;
+    if (e[5] < -1 || (e[5] >= 0 && static_cast<int64_t>(e[5]) + static_cast<int64_t>(e[4]) * H > cells))
+      return false;
+  }
+  for (int64_t k = 0; k < M; ++k)
+    if (members[k] < 0 || members[k] >= T) return false;
   for (int64_t k = 0; k < L; ++k)
     if (list[k] < 0 || static_cast<int64_t>(list[k]) + H > cells) return false;
   v->U = static_cast<int32_t>(U);

@@ -1,0 +1,173 @@
+"""The prefill planner (pkv_prefill_plan, host code) against brute-force definitions.
+
+For batches mixing whole prompts, cached prefixes, single new tokens, empty sequences and
+rows that see more than one chunk (64 blocks):
+* row t of sequence s (t = query_start[s] + k) sees vis_t = n_s - q_s + k + 1 tokens;
+* the units naming t belong to t's sequence, hold consecutive rows of it (at most 16 / G),
+  and their block ranges tile [0, ceil(v / 16)) in order, v the largest vis of the tile;
+* a tile with one unit is direct (cell_base -1, the row is not merged); otherwise every
+  unit has cells, cells are handed out consecutively, and the row's piece list names exactly
+  the cells of the units whose range starts before vis_t, in unit order;
+* bad arguments are refused, and so is a corrupted plan, by pkv_prefill_attn before any
+  device work.
+"""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_459_amd as m
+from paged_kv_cache_459_amd import lib
+
+HDR = 16
+
+
+def parse(p):
+    T, U, M, L = int(p[1]), int(p[4]), int(p[5]), int(p[6])
+    o = HDR
+    skip = p[o:o + T]; o += T
+    vis = p[o:o + T]; o += T
+    ptr = p[o:o + T + 1]; o += T + 1
+    units = p[o:o + 6 * U].reshape(U, 6); o += 6 * U
+    members = p[o:o + M]; o += M
+    lst = p[o:o + L]; o += L
+    assert o == len(p)
+    return dict(T=T, H=int(p[2]), GS=int(p[3]), U=U, cells=int(p[7]), chunk=int(p[8]),
+                S=int(p[9]), rows=int(p[10]), skip=skip, vis=vis, ptr=ptr, units=units,
+                members=members, list=lst)
+
+
+def batch(kind, rng):
+    if kind == "whole":
+        n = np.array([1, 17, 40, 5, 100, 16], np.int32)
+        return n, n.copy()
+    if kind == "cached":
+        n = np.array([300, 64, 2100, 1500, 33, 1024 + 16 * 64 + 1], np.int32)
+        q = np.array([37, 1, 64, 200, 33, 9], np.int32)
+        return n, q
+    if kind == "empty":
+        n = np.array([10, 0, 50, 20], np.int32)
+        q = np.array([0, 0, 50, 3], np.int32)
+        return n, q
+    S = 12  # random
+    n = rng.integers(1, 3000, size=S).astype(np.int32)
+    q = np.array([rng.integers(0, x + 1) for x in n], np.int32)
+    return n, q
+
+
+@pytest.mark.parametrize("kind", ["whole", "cached", "empty", "random"])
+@pytest.mark.parametrize("hq,hkv", [(32, 32), (8, 2), (28, 4), (16, 1)])
+def test_prefill_plan_matches_brute_force(kind, hq, hkv):
+    rng = np.random.default_rng(900 + hq)
+    n, q = batch(kind, rng)
+    qs = np.concatenate([[0], np.cumsum(q)]).astype(np.int32)
+    mb = max(1, -(-int(n.max()) // 16))
+    p = m.pkv_prefill_plan(qs, n, num_q_heads=hq, num_kv_heads=hkv, max_blocks=mb,
+                           max_context_len=16 * mb, dtype=torch.bfloat16)
+    P = parse(p)
+    G = hq // hkv
+    T = int(qs[-1])
+    assert (P["T"], P["H"], P["GS"], P["S"]) == (T, hkv, G, len(n))
+    assert P["rows"] == 16 // G and P["chunk"] == 64
+    seq_of = np.repeat(np.arange(len(n)), q)
+    vis = np.array([n[s] - q[s] + (t - qs[s]) + 1 for t, s in zip(range(T), seq_of)], np.int64)
+    np.testing.assert_array_equal(P["vis"], vis)
+    ranges = [[] for _ in range(T)]
+    lists = [[] for _ in range(T)]
+    direct = [[] for _ in range(T)]
+    cell = 0
+    for u in P["units"]:
+        s, b0, b1, off, cnt, cbase = (int(x) for x in u)
+        rows = P["members"][off:off + cnt]
+        assert 1 <= cnt <= 16 // G and b0 < b1 and b1 - b0 <= 64
+        np.testing.assert_array_equal(rows, np.arange(rows[0], rows[0] + cnt))
+        assert np.all(seq_of[rows] == s)
+        assert b1 <= -(-int(vis[rows].max()) // 16)
+        if cbase >= 0:
+            assert cbase == cell
+            cell += cnt * hkv
+        for k, r in enumerate(rows):
+            ranges[r].append((b0, b1))
+            direct[r].append(cbase < 0)
+            if cbase >= 0 and vis[r] > 16 * b0:
+                lists[r].append(cbase + k * hkv)
+    assert cell == P["cells"]
+    for t in range(T):
+        rr = ranges[t]
+        assert rr[0][0] == 0 and all(a[1] == b[0] for a, b in zip(rr, rr[1:]))
+        assert rr[-1][1] >= -(-int(vis[t]) // 16)
+        if len(rr) == 1:
+            assert direct[t] == [True] and P["skip"][t] == 0
+        else:
+            assert not any(direct[t]) and P["skip"][t] == 1
+        assert P["list"][P["ptr"][t]:P["ptr"][t + 1]].tolist() == lists[t]
+    if kind == "cached":  # rows past 64 blocks are split, short ones are not
+        assert P["skip"].any() and not P["skip"].all()
+
+
+@pytest.mark.parametrize("qs,lens,dt,hq,hkv,status", [
+    ([1, 3], [3], torch.float16, 4, 4, 1),          # query_start[0] != 0
+    ([0, 5, 3], [5, 5], torch.float16, 4, 4, 1),    # decreasing
+    ([0, 6], [5], torch.float16, 4, 4, 1),          # more new tokens than the context
+    ([0, 2], [300], torch.float16, 4, 4, 1),        # context past max_context_len (256)
+    ([0, 2], [5], torch.float32, 4, 4, 2),          # f32: no matrix-core prefill
+    ([0, 2], [5], torch.bfloat16, 32, 1, 2),        # G > 16
+])
+def test_bad_arguments_are_refused(qs, lens, dt, hq, hkv, status):
+    n = ctypes.c_size_t(0)
+    q = np.asarray(qs, np.int32)
+    ln = np.asarray(lens, np.int32)
+    buf = np.empty(4096, np.int32)
+    st = lib.pkv_prefill_plan(q.ctypes.data, ln.ctypes.data, len(ln), 16, 256, hq, hkv,
+                              m.pkv_dtype(dt), buf.ctypes.data, buf.size, ctypes.byref(n))
+    assert st == status
+
+
+def test_corrupted_plans_are_refused_on_the_host():
+    n = np.array([300, 1500, 40], np.int32)
+    q = np.array([20, 100, 40], np.int32)
+    qs = np.concatenate([[0], np.cumsum(q)]).astype(np.int32)
+    T, S, mb = int(qs[-1]), 3, 96
+    p = m.pkv_prefill_plan(qs, n, num_q_heads=8, num_kv_heads=2, max_blocks=mb,
+                           max_context_len=16 * mb, dtype=torch.float16)
+    P = parse(p)
+    assert P["cells"] > 0  # the control below stops at the workspace check
+    buf = (ctypes.c_uint8 * (1 << 16))()
+    fake = ctypes.c_void_p((ctypes.addressof(buf) + 255) & ~255)
+
+    def call(plan):
+        # workspace_bytes = 0: a plan that passes the checks stops at PKV_ERR_WORKSPACE (6),
+        # so nothing here reaches a launch
+        c = np.ascontiguousarray(plan, np.int32)
+        assert c.size < HDR or c[7] != 0
+        return lib.pkv_prefill_attn(fake, fake, fake, fake, fake, S, T, 8, 2, 64, 16, 1000, mb,
+                                    16 * mb, 0.1, 1, c.ctypes.data, fake, c.size, None, 0, None)
+    assert call(p) == 6
+    o_units = HDR + 3 * T + 1
+    split = int(np.flatnonzero(P["units"][:, 1] > 0)[0])  # a second chunk (it has cells)
+    assert P["units"][split, 5] >= 0
+    o_split = o_units + 6 * split
+    bad = []
+    for idx, val in [(0, 0), (1, T + 1), (2, 8), (3, 1), (4, P["U"] + 1), (7, -1), (9, 2),
+                     (8, 65), (10, 5), (o_units, S), (o_units + 1, -1), (o_units + 2, mb + 1),
+                     (o_split + 1, 0), (o_split + 2, mb + 1), (o_units + 4, 0), (o_units + 4, 5),
+                     (o_split + 5, P["cells"]), (o_units + 5, -2), (HDR, 2), (HDR + T, 0),
+                     (HDR + T, 16 * mb + 1), (HDR + 2 * T, 1)]:
+        c = p.copy()
+        c[idx] = val
+        bad.append(c)
+    c = p.copy()
+    c[-1] = P["cells"]  # a piece cell past the cells
+    bad.append(c)
+    c = p.copy()
+    c[o_units + 6 * P["U"]] = T  # a member row past T
+    bad.append(c)
+    bad.append(p[:-1])  # truncated
+    for c in bad:
+        assert call(c) == 1
+    # a decode plan is not a prefill plan
+    dp = p.copy()
+    dp[0] = 0x504C4E31
+    assert call(dp) == 1

@@ -25,6 +25,8 @@ The named shapes follow the workloads the method is usually run on:
                   MHA 32 x 128, bf16 (and a beam variant: 32 groups x 4 beams)
   long_context    8 seqs at 32768 + 120 seqs U[64, 4096], 32 q / 8 kv x 128, bf16, one new
                   token per sequence written before attention
+  prefill         chunked prefill of 16 seqs: a cached prefix of U[0, 1536] tokens plus a new
+                  chunk of 512 tokens each (8192 query tokens), MHA 32 x 128, f16
 """
 
 import dataclasses
@@ -53,7 +55,10 @@ SHAPES = {
     "prefix_shared": Shape("prefix_shared", 128, 32, 32, 128, "bf16", 4),
     "long_context": Shape("long_context", 128, 32, 8, 128, "bf16", 5),
     "beam_search": Shape("beam_search", 128, 32, 32, 128, "bf16", 6),
+    "prefill": Shape("prefill", 16, 32, 32, 128, "f16", 7),
 }
+PREFILL_CHUNK = 512  # new tokens per sequence in the prefill workload
+PREFILL_CACHED = (0, 1536)  # cached-prefix tokens before the chunk, inclusive range
 
 TINY_LENGTHS = (1, 15, 16, 37)
 TINY_POOL = 16
@@ -87,6 +92,14 @@ def draw_lengths(shape, rng, *, B=None):
         tails = rng.integers(16, 512, size=B // BEAMS, endpoint=True)
         return np.repeat(PREFIX_TOKENS + tails, BEAMS).astype(np.int32)
     raise KeyError(shape.name)
+
+
+def prefill_lengths(rng, S, *, chunk=PREFILL_CHUNK, cached=PREFILL_CACHED):
+    """Chunked prefill: (context_lens, query_lens), each sequence a cached prefix drawn
+    U[cached] followed by ``chunk`` new tokens (context_lens count both)."""
+    pre = rng.integers(cached[0], cached[1], size=S, endpoint=True)
+    q = np.full(S, chunk, dtype=np.int32)
+    return (pre + q).astype(np.int32), q
 
 
 def long_context_lengths(rng, *, B=128, n_long=8, long_len=32768, lo=64, hi=4096, n_fresh=8):
