@@ -40,8 +40,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "paged decode attn: KV-read GB/s and % of HBM peak; decode tokens/s per layer"
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}  # MI355X dense matrix cores, published
+PREFILL_METRIC = "paged prefill attn: prompt tokens/s per layer and MFMA TFLOP/s"
 WORKLOADS = ("llama2_7b", "qwen25_7b", "prefix_shared", "long_context", "beam_search",
-             "continuous_batching", "prefix_cache")
+             "continuous_batching", "prefix_cache", "prefill")
 DESC = {
     "llama2_7b": "Llama-2-7B-shaped single layer decode: MHA 32 x 128, f16, batch 64, "
                  "context U[128,2048], blocks scattered in a pool of 1.1x need",
@@ -66,6 +68,10 @@ DESC = {
                     "2000-token system prompt + U[16,256] own tokens, new tokens U[16,256], "
                     "a backlog of 128 then 1 arrival per step; admission shares the cached "
                     "system-prompt blocks and writes only the rest; 300 untimed steps first",
+    "prefill": "chunked prefill, Llama-2-7B-shaped layer (MHA 32 x 128, f16): 16 sequences, "
+               "each a cached prefix of U[0,1536] tokens plus a new chunk of 512 (8192 query "
+               "tokens); each step writes the chunk's K/V (pkv_write) and runs causal "
+               "attention of the new tokens over the paged cache (pkv_prefill_attn)",
 }
 
 
@@ -606,6 +612,158 @@ def batching_main(args, torch, pkv, W):
     print(json.dumps(res), flush=True)
 
 
+def prefill_main(args, torch, pkv, W):
+    """The chunked-prefill workload: one step = pkv_write of the new tokens' K/V, then the
+    causal attention of those tokens over their sequences' paged caches."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as OA
+    shape = W.SHAPES["prefill"]
+    dtype, Hq, Hkv, hd = shape.dtype, shape.Hq, shape.Hkv, shape.hd
+    dt = W.torch_dtype(dtype)
+    rng = W.rng_for(shape.seed)
+    lens, qlens = W.prefill_lengths(rng, shape.B)
+    nb = W.pool_blocks(lens)
+    tables = W.place_sequences(lens, rng.permutation(nb).astype(np.int32))
+    mb = tables.shape[1]
+    max_ctx = 16 * mb
+    qs = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    T = int(qs[-1])
+    k_cache, v_cache = pkv.alloc_caches(nb, Hkv, hd, dt)
+    k_cache.view(-1).copy_(W.device_normal((k_cache.numel(),), dtype, 7201))
+    v_cache.view(-1).copy_(W.device_normal((v_cache.numel(),), dtype, 7202))
+    q = W.device_normal((T, Hq, hd), dtype, 7203)
+    k_new = W.device_normal((T, Hkv, hd), dtype, 7204)
+    v_new = W.device_normal((T, Hkv, hd), dtype, 7205)
+    # the new tokens' slots: row t of sequence s sits at position pos = n_s - q_s + k
+    slots = np.empty(T, np.int32)
+    vis = np.empty(T, np.int64)
+    for s_ in range(shape.B):
+        pos = np.arange(lens[s_] - qlens[s_], lens[s_])
+        slots[qs[s_]:qs[s_ + 1]] = tables[s_, pos // 16] * 16 + pos % 16
+        vis[qs[s_]:qs[s_ + 1]] = pos + 1
+    slots_dev = torch.from_numpy(slots).cuda()
+    tables_dev = torch.from_numpy(tables).cuda()
+    t0 = time.perf_counter()
+    for _ in range(5):
+        plan = pkv.pkv_prefill_plan(qs, lens, num_q_heads=Hq, num_kv_heads=Hkv, max_blocks=mb,
+                                    max_context_len=max_ctx, dtype=dt)
+    plan_ms = (time.perf_counter() - t0) / 5 * 1e3
+    plan_dev = torch.from_numpy(plan.copy()).cuda()
+    ws_bytes = pkv.pkv_prefill_workspace_bytes(Hq, Hkv, hd, plan)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    scale = 1.0 / math.sqrt(hd)
+    split_rows = int(plan[16:16 + T].sum())
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        pkv.pkv_write(k_new, v_new, k_cache, v_cache, slots_dev)
+        if ev is not None:
+            ev[1].record()
+        for ps in (1, 2):
+            pkv.pkv_prefill_attn(q, k_cache, v_cache, tables_dev, plan, plan_dev,
+                                 num_kv_heads=Hkv, scale=scale, max_context_len=max_ctx,
+                                 workspace=ws, out=out, passes=ps)
+            if ev is not None:
+                ev[1 + ps].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    write_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    merge_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    eb = 2
+    flops = 4.0 * hd * Hq * float(vis.sum())  # q.k and p.v over every visible key, per head
+    achieved = flops / (float(np.mean(attn_ms)) / 1e3) / 1e12
+    kv_bytes = int(lens.astype(np.int64).sum()) * 2 * Hkv * hd * eb
+    qo_bytes = 2 * T * Hq * hd * eb
+    if args.copy_calibration:  # a plain copy of known size, for the counter runs
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    ms_per_step = wall / args.steps * 1e3
+    res = {
+        "metric": PREFILL_METRIC,
+        "value": round(T / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded N(0,1) values, seeded lengths and block placement)",
+        "config": {"workload": "prefill", "description": DESC["prefill"], "sequences": shape.B,
+                   "query_tokens": T, "q_heads": Hq, "kv_heads": Hkv, "head_dim": hd,
+                   "block_size": 16, "pool_blocks": nb,
+                   "mean_context_len": round(float(lens.mean()), 1),
+                   "split_rows": split_rows, "plan_units": int(plan[4])},
+        "attn_ms": round(float(np.mean(attn_ms)), 4),
+        "merge_ms": round(float(np.mean(merge_ms)), 4),
+        "write_ms": round(float(np.mean(write_ms)), 4),
+        "plan_host_ms": round(plan_ms, 3),
+        "attention_tflops": round(flops / ((sum(attn_ms) + sum(merge_ms)) / args.steps / 1e3)
+                                  / 1e12, 2),
+        "attention_min_bytes_gbs": round((kv_bytes + qo_bytes) / (float(np.mean(attn_ms)) / 1e3)
+                                         / 1e9, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": MFMA_PEAK_TFLOPS[dtype],
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_PEAK_TFLOPS[dtype], 4),
+            "traffic": measured_traffic("prefill", kernel_source_digest()),
+            "kernel": "prefill attention pass (attn_shared_kernel, causal rows)",
+            "algorithmic_flops_per_launch": flops,
+        },
+    }
+    if not args.no_cpu_baseline:
+        # the oracle on whole sequences' new tokens, in a seeded order, until the budget is spent
+        order = np.random.default_rng(12345).permutation(shape.B)
+        spent, rows, fl, seqs = 0.0, 0, 0.0, 0
+        with threadpool_limits(limits=1):
+            for s_ in order:
+                n = int(lens[s_])
+                nbk = -(-n // 16)
+                ids = torch.from_numpy(tables[s_, :nbk].astype(np.int64)).cuda()
+                kc = W.to_storage_numpy(k_cache.index_select(0, ids), dtype).reshape(-1)
+                vc = W.to_storage_numpy(v_cache.index_select(0, ids), dtype).reshape(-1)
+                a, b = int(qs[s_]), int(qs[s_ + 1])
+                # a bounded slice of the sequence's rows: its last new tokens
+                take = min(b - a, 64)
+                qh = W.to_storage_numpy(q[b - take:b], dtype)
+                t1 = time.perf_counter()
+                OA.prefill_attention(qh, kc, vc, np.arange(nbk, dtype=np.int32)[None],
+                                     np.int32([n]), np.int32([0, take]), scale=scale, hkv=Hkv,
+                                     hd=hd, bs=16, dtype=dtype)
+                spent += time.perf_counter() - t1
+                rows += take
+                seqs += 1
+                fl += 4.0 * hd * Hq * float(vis[b - take:b].sum())
+                if spent >= args.cpu_seconds:
+                    break
+        res["cpu_baseline"] = {
+            "value": round(rows / spent, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the last 64 new tokens of {seqs} sequence(s) in a seeded order: "
+                      f"{rows} query tokens, {spent:.1f} s of oracle time on one thread (host "
+                      f"copies of the blocks not timed)",
+            "tflops": round(fl / spent / 1e12, 6)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -622,6 +780,9 @@ def main():
     pkv.pkv_set_attn_kernel(args.kernel)
     if args.workload in BATCHING:
         batching_main(args, torch, pkv, W)
+        return
+    if args.workload == "prefill":
+        prefill_main(args, torch, pkv, W)
         return
     wl = Workload(args.workload, args.warmup + args.steps, torch, pkv, W, plan=not args.no_plan)
     torch.cuda.synchronize()

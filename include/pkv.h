@@ -89,8 +89,9 @@ size_t pkv_cache_bytes(int32_t NB, int32_t Hkv, int32_t hd, int32_t bs, pkv_dtyp
 /*                 slot < 0 (padding) and slot >= NB*bs are skipped, so no value can write   */
 /*                 outside the caches. Two tokens with the same slot in one call is a caller */
 /*                 error: which one lands is undefined.                                       */
-/* The copy is bitwise. T == 0 is a no-op. Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED,  */
-/* PKV_ERR_INDEX (PKV_CHECK=1: slot >= NB*bs or duplicate non-negative slots), PKV_ERR_HIP.   */
+/* The copy is bitwise. T == 0 is a no-op. Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED  */
+/* (also Hkv > 65535), PKV_ERR_INDEX (PKV_CHECK=1: slot >= NB*bs or duplicate non-negative    */
+/* slots), PKV_ERR_HIP.                                                                        */
 pkv_status pkv_write(const void* k, const void* v, void* k_cache, void* v_cache,
                      const int32_t* slot_mapping, int32_t T, int32_t Hkv, int32_t hd, int32_t bs,
                      int32_t NB, pkv_dtype dtype, void* stream);
@@ -285,13 +286,16 @@ size_t pkv_prefill_workspace_bytes(int32_t Hq, int32_t Hkv, int32_t hd, const in
 /* attended. plan_host and plan_dev hold the same plan_ints entries, built for these           */
 /* query_start/context_lens and shapes. Writes only out (and the workspace). Errors:          */
 /* PKV_ERR_INVALID_ARG (shapes, pointers, a plan that fails the check), PKV_ERR_UNSUPPORTED,  */
-/* PKV_ERR_WORKSPACE, PKV_ERR_HIP. Stream-ordered, asynchronous.                               */
-pkv_status pkv_prefill_attn(void* out, const void* q, const void* k_cache, const void* v_cache,
-                            const int32_t* block_tables, int32_t S, int32_t T, int32_t Hq,
-                            int32_t Hkv, int32_t hd, int32_t bs, int32_t NB, int32_t max_blocks,
-                            int32_t max_context_len, float scale, pkv_dtype dtype,
-                            const int32_t* plan_host, const int32_t* plan_dev, size_t plan_ints,
-                            void* workspace, size_t workspace_bytes, void* stream);
+/* PKV_ERR_WORKSPACE, PKV_ERR_HIP. Stream-ordered, asynchronous. pass: 0 both kernels, 1 the  */
+/* attention pass (direct rows finished, pieces of split rows written), 2 the merge of the    */
+/* split rows (run 1 then 2 on one stream; exported to time them).                            */
+pkv_status pkv_prefill_attn(int32_t pass, void* out, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_tables, int32_t S,
+                            int32_t T, int32_t Hq, int32_t Hkv, int32_t hd, int32_t bs,
+                            int32_t NB, int32_t max_blocks, int32_t max_context_len, float scale,
+                            pkv_dtype dtype, const int32_t* plan_host, const int32_t* plan_dev,
+                            size_t plan_ints, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /* Workspace bytes pkv_decode_attn needs for this shape on the current device (0 if B == 0 or */
 /* the arguments are invalid).                                                                 */

@@ -93,7 +93,7 @@ SIGNATURES = {
     "pkv_prefill_plan": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_sz,
                                  ctypes.POINTER(c_sz)]),
     "pkv_prefill_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_vp, c_sz]),
-    "pkv_prefill_attn": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
+    "pkv_prefill_attn": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
                                  c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp, c_vp, c_sz, c_vp,
                                  c_sz, c_vp]),
     "pkv_alloc_add_seq_tokens": (c_i32, [c_vp, c_i64, c_i32, c_vp, c_vp, c_vp]),

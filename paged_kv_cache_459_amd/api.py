@@ -364,10 +364,11 @@ def pkv_prefill_workspace_bytes(num_q_heads, num_kv_heads, head_dim, plan):
 
 
 def pkv_prefill_attn(q, k_cache, v_cache, block_tables, plan, plan_dev, *, num_kv_heads, scale,
-                     max_context_len, workspace=None, out=None):
+                     max_context_len, workspace=None, out=None, passes=0):
     """out [T, Hq, hd] = causal attention of the T new prompt tokens over their sequences'
     paged caches (see include/pkv.h). plan: the host plan from pkv_prefill_plan (NumPy int32),
-    plan_dev: the same ints on the device. Allocates the workspace if none is given."""
+    plan_dev: the same ints on the device. Allocates the workspace if none is given.
+    passes: 0 both kernels, 1 the attention pass, 2 the merge of split rows."""
     _need(q, "q")
     dev = q.device
     for t, name in ((k_cache, "k_cache"), (v_cache, "v_cache")):
@@ -391,7 +392,7 @@ def pkv_prefill_attn(q, k_cache, v_cache, block_tables, plan, plan_dev, *, num_k
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    check(lib.pkv_prefill_attn(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+    check(lib.pkv_prefill_attn(int(passes), _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                _ptr(block_tables), S, T, hq, num_kv_heads, hd, BLOCK_SIZE, nb, mb,
                                int(max_context_len), float(scale), pkv_dtype(q), p.ctypes.data,
                                _ptr(plan_dev), p.size, _ptr(workspace), ws_bytes,

@@ -248,6 +248,7 @@ pkv_status pkv_write(const void* k, const void* v, void* k_cache, void* v_cache,
   if (!dtype_ok(dtype) || bs != kBlockSize || !head_dim_ok(hd)) return PKV_ERR_UNSUPPORTED;
   if (T < 0 || Hkv <= 0 || NB <= 0 || static_cast<int64_t>(NB) * kBlockSize >= (int64_t{1} << 31))
     return PKV_ERR_INVALID_ARG;
+  if (Hkv > 65535) return PKV_ERR_UNSUPPORTED;  // one grid row per kv head
   if (T == 0) return PKV_OK;
   if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PKV_ERR_INVALID_ARG;
   if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache) ||
@@ -444,12 +445,14 @@ size_t pkv_prefill_workspace_bytes(int32_t Hq, int32_t Hkv, int32_t hd, const in
   return prefill_layout(plan[7], Hq / Hkv, hd).bytes;
 }
 
-pkv_status pkv_prefill_attn(void* out, const void* q, const void* k_cache, const void* v_cache,
-                            const int32_t* block_tables, int32_t S, int32_t T, int32_t Hq,
-                            int32_t Hkv, int32_t hd, int32_t bs, int32_t NB, int32_t max_blocks,
-                            int32_t max_context_len, float scale, pkv_dtype dtype,
-                            const int32_t* plan_host, const int32_t* plan_dev, size_t plan_ints,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+pkv_status pkv_prefill_attn(int32_t pass, void* out, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_tables, int32_t S,
+                            int32_t T, int32_t Hq, int32_t Hkv, int32_t hd, int32_t bs,
+                            int32_t NB, int32_t max_blocks, int32_t max_context_len, float scale,
+                            pkv_dtype dtype, const int32_t* plan_host, const int32_t* plan_dev,
+                            size_t plan_ints, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (pass < 0 || pass > 2) return PKV_ERR_INVALID_ARG;
   if (!dtype_ok(dtype) || bs != kBlockSize || !head_dim_ok(hd)) return PKV_ERR_UNSUPPORTED;
   if (S < 0 || T < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Hq > 65535 || NB <= 0 ||
       max_blocks <= 0 || max_context_len < 0 ||
@@ -504,8 +507,10 @@ pkv_status pkv_prefill_attn(void* out, const void* q, const void* k_cache, const
   p.shared_cells = pv.cells;
   p.shared_base = 0;
   p.table_rows = S;
-  if (pkv::launch_shared(p, dtype, pkv::kMatrix, hs) != hipSuccess) return PKV_ERR_HIP;
-  if (pv.has_shared && pkv::launch_merge(p, dtype, pkv::kMatrix, hs) != hipSuccess)
+  if ((pass == 0 || pass == 1) && pkv::launch_shared(p, dtype, pkv::kMatrix, hs) != hipSuccess)
+    return PKV_ERR_HIP;
+  if ((pass == 0 || pass == 2) && pv.has_shared &&
+      pkv::launch_merge(p, dtype, pkv::kMatrix, hs) != hipSuccess)
     return PKV_ERR_HIP;
   return PKV_OK;
 }

@@ -6,9 +6,15 @@
 //
 // Also the copy-on-write block copy (below).
 //
-// One thread moves one 16-byte chunk (X = 16 / element-bytes consecutive dims of one head of
-// one token). The K chunk lands as one 16-byte store (the K tile keeps 16-byte chunks of dims,
-// token-minor); the V chunk is spread over the X dim rows of the dim-major V tile.
+// Work-group (g, h) writes rows [16g, 16g + 16) of kv head h. K: one 16-byte store per
+// chunk (the K tile keeps 16-byte chunks of dims, token-minor, so the rows of a run of
+// consecutive slots land side by side). V: the tile is dim-major ([hd][16 tokens]), so a row
+// scatters one element into each dim row; written element by element, a prompt becomes
+// millions of 2-byte partial writes. Instead the rows are cut into runs (consecutive rows
+// whose slots are consecutive in one block) and each run is written dim row by dim row: the
+// span of a dim row that a run covers goes out as a few wide stores, a whole block's span as
+// full 32-byte (f16/bf16) rows. The work-group owns the runs that start in its 16 rows; a run
+// is at most 16 rows long, so it has those rows' V in LDS (rows 16g .. 16g + 31).
 
 #include <hip/hip_runtime.h>
 
@@ -19,42 +25,107 @@ namespace {
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-template <int EB>
+template <int EB, int HD>
 __global__ void __launch_bounds__(256)
 write_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v, uint4* __restrict__ kc,
              void* __restrict__ vc, const int32_t* __restrict__ slots, int32_t T, int32_t Hkv,
-             int32_t hd, int32_t NB) {
-  constexpr int X = 16 / EB;
-  const int chunks = hd / X;  // 16-byte chunks in one token-head row
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t total = static_cast<int64_t>(T) * Hkv * chunks;
-  if (gid >= total) return;
-  const int c = static_cast<int>(gid % chunks);
-  const int64_t th = gid / chunks;
-  const int h = static_cast<int>(th % Hkv);
-  const int t = static_cast<int>(th / Hkv);
-  const int32_t slot = slots[t];
-  if (slot < 0 || slot >= NB * kBlockSize) return;  // padding, or outside the pool
-  const int b = slot / kBlockSize;
-  const int off = slot % kBlockSize;
-  const uint4 kk = k[gid];  // k is [T][Hkv][hd]: chunk (t, h, c) is chunk number gid
-  const uint4 vv = v[gid];
-  const size_t tile = static_cast<size_t>(b) * Hkv + h;
-  // Non-temporal stores: these are partial cache lines which, left dirty in the L2, would be
-  // written back in the middle of the next attention pass's stream of K/V tiles.
-  __builtin_nontemporal_store(u32x4_t{kk.x, kk.y, kk.z, kk.w},
-                              reinterpret_cast<u32x4_t*>(kc) + (tile * chunks + c) * kBlockSize + off);
-  const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-  if constexpr (EB == 2) {
-    uint16_t* vd = static_cast<uint16_t*>(vc) + (tile * hd + static_cast<size_t>(X) * c) * kBlockSize + off;
+             int32_t NB) {
+  constexpr int CH = HD * EB / 16;  // 16-byte chunks in one token-head row
+  constexpr int P = 256 / HD;       // threads per V dim row
+  constexpr int OP = kBlockSize / P;  // offsets (elements) of a dim row per thread
+  constexpr int OB = OP * EB;       // their bytes: 8, 16 or 32
+  __shared__ uint4 vrows[32 * CH];  // V of rows 16g .. 16g + 31, head h
+  __shared__ int32_t s_slot[33];    // slots of rows 16g - 1 .. 16g + 31; -1: none or invalid
+  __shared__ int32_t s_len[16];     // length of the run starting at row 16g + i (0: none)
+  const int tid = threadIdx.x, h = blockIdx.y;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int64_t limit = static_cast<int64_t>(NB) * kBlockSize;
+  if (tid < 33) {
+    const int64_t r = r0 - 1 + tid;
+    int32_t sl = -1;
+    if (r >= 0 && r < T) {
+      sl = slots[r];
+      if (sl < 0 || sl >= limit) sl = -1;  // padding, or outside the pool
+    }
+    s_slot[tid] = sl;
+  }
+  for (int i = tid; i < 32 * CH; i += 256) {
+    const int64_t r = r0 + i / CH;
+    if (r < T) vrows[i] = v[(r * Hkv + h) * CH + i % CH];
+  }
+  __syncthreads();
+  // K: rows fastest, so the chunks of a run's rows are contiguous across lanes. Non-temporal
+  // stores: partial cache lines left dirty in the L2 would be written back in the middle of
+  // the next attention pass's stream of K/V tiles.
+  for (int i = tid; i < 16 * CH; i += 256) {
+    const int rr = i % 16, c = i / 16;
+    const int64_t r = r0 + rr;
+    const int32_t sl = s_slot[rr + 1];
+    if (r >= T || sl < 0) continue;
+    const uint4 kk = k[(r * Hkv + h) * CH + c];
+    const size_t tile = static_cast<size_t>(sl / kBlockSize) * Hkv + h;
+    __builtin_nontemporal_store(u32x4_t{kk.x, kk.y, kk.z, kk.w},
+                                reinterpret_cast<u32x4_t*>(kc) + (tile * CH + c) * kBlockSize +
+                                    sl % kBlockSize);
+  }
+  if (tid < 16) {
+    // row j (index j in s_slot) continues the run of row j - 1: same block, next offset
+    auto cont = [&](int j) {
+      return s_slot[j] >= 0 && s_slot[j - 1] >= 0 && s_slot[j] == s_slot[j - 1] + 1 &&
+             s_slot[j] % kBlockSize != 0;
+    };
+    int len = 0;
+    if (s_slot[tid + 1] >= 0 && !cont(tid + 1)) {
+      len = 1;
+      while (tid + 1 + len < 33 && cont(tid + 1 + len)) ++len;
+    }
+    s_len[tid] = len;
+  }
+  __syncthreads();
+  const int d = tid / P, lo = (tid % P) * OP;  // this thread: dim row d, offsets [lo, lo + OP)
+  const char* vb = reinterpret_cast<const char*>(vrows);
+  for (int i = 0; i < 16; ++i) {
+    const int len = s_len[i];
+    if (len == 0) continue;
+    const int32_t sl = s_slot[i + 1];
+    const int o0 = sl % kBlockSize;
+    const size_t tile = static_cast<size_t>(sl / kBlockSize) * Hkv + h;
+    char* row = static_cast<char*>(vc) + ((tile * HD + d) * kBlockSize) * EB;
+    // offset o of the block comes from staged row i + (o - o0)
+    auto elem = [&](int o) -> const char* { return vb + ((i + o - o0) * CH * 16 + d * EB); };
+    if (o0 <= lo && lo + OP <= o0 + len) {  // the whole span: wide stores
+      uint32_t w[OB / 4];
 #pragma unroll
-    for (int x = 0; x < 8; ++x)
-      __builtin_nontemporal_store(static_cast<uint16_t>((w[x >> 1] >> ((x & 1) * 16)) & 0xFFFFu),
-                                  vd + x * kBlockSize);
-  } else {
-    uint32_t* vd = static_cast<uint32_t*>(vc) + (tile * hd + static_cast<size_t>(X) * c) * kBlockSize + off;
+      for (int x = 0; x < OB / 4; ++x) {
+        if constexpr (EB == 4) {
+          w[x] = *reinterpret_cast<const uint32_t*>(elem(lo + x));
+        } else {
+          const uint32_t a = *reinterpret_cast<const uint16_t*>(elem(lo + 2 * x));
+          const uint32_t b = *reinterpret_cast<const uint16_t*>(elem(lo + 2 * x + 1));
+          w[x] = a | (b << 16);
+        }
+      }
+      if constexpr (OB == 8) {
+        typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+        __builtin_nontemporal_store(u32x2_t{w[0], w[1]},
+                                    reinterpret_cast<u32x2_t*>(row + lo * EB));
+      } else {
 #pragma unroll
-    for (int x = 0; x < 4; ++x) __builtin_nontemporal_store(w[x], vd + x * kBlockSize);
+        for (int x = 0; x < OB / 16; ++x)
+          __builtin_nontemporal_store(u32x4_t{w[4 * x], w[4 * x + 1], w[4 * x + 2], w[4 * x + 3]},
+                                      reinterpret_cast<u32x4_t*>(row + lo * EB) + x);
+      }
+    } else {  // part of the span: element stores
+      const int a = max(lo, o0), b = min(lo + OP, o0 + len);
+      for (int o = a; o < b; ++o) {
+        if constexpr (EB == 4)
+          __builtin_nontemporal_store(*reinterpret_cast<const uint32_t*>(elem(o)),
+                                      reinterpret_cast<uint32_t*>(row) + o);
+        else
+          __builtin_nontemporal_store(*reinterpret_cast<const uint16_t*>(elem(o)),
+                                      reinterpret_cast<uint16_t*>(row) + o);
+      }
+    }
   }
 }
 
@@ -117,19 +188,22 @@ int32_t copy_blocks_grid_y(int32_t Hkv, int32_t hd, int32_t dtype) {
 }
 
 hipError_t launch_write(const WriteParams& p, int32_t dtype, hipStream_t stream) {
-  const int eb = dtype == 0 ? 4 : 2;
-  const int64_t total = static_cast<int64_t>(p.T) * p.Hkv * (p.hd * eb / 16);
-  if (total == 0) return hipSuccess;
+  if (p.T == 0) return hipSuccess;
   (void)hipGetLastError();  // drop a stale status left by an earlier, unrelated runtime call
-  const dim3 grid(static_cast<unsigned>((total + 255) / 256));
-  if (eb == 4)
-    hipLaunchKernelGGL(write_kernel<4>, grid, dim3(256), 0, stream,
-                       static_cast<const uint4*>(p.k), static_cast<const uint4*>(p.v),
-                       static_cast<uint4*>(p.k_cache), p.v_cache, p.slots, p.T, p.Hkv, p.hd, p.NB);
-  else
-    hipLaunchKernelGGL(write_kernel<2>, grid, dim3(256), 0, stream,
-                       static_cast<const uint4*>(p.k), static_cast<const uint4*>(p.v),
-                       static_cast<uint4*>(p.k_cache), p.v_cache, p.slots, p.T, p.Hkv, p.hd, p.NB);
+  const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(p.T) + 15) / 16),
+                  static_cast<unsigned>(p.Hkv));
+  auto args = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, static_cast<const uint4*>(p.k),
+                       static_cast<const uint4*>(p.v), static_cast<uint4*>(p.k_cache), p.v_cache,
+                       p.slots, p.T, p.Hkv, p.NB);
+  };
+  if (dtype == 0) {
+    if (p.hd == 64) args(write_kernel<4, 64>);
+    else args(write_kernel<4, 128>);
+  } else {
+    if (p.hd == 64) args(write_kernel<2, 64>);
+    else args(write_kernel<2, 128>);
+  }
   return note_error("write_kernel launch", hipGetLastError());
 }
 

@@ -142,7 +142,7 @@ def test_corrupted_plans_are_refused_on_the_host():
         # so nothing here reaches a launch
         c = np.ascontiguousarray(plan, np.int32)
         assert c.size < HDR or c[7] != 0
-        return lib.pkv_prefill_attn(fake, fake, fake, fake, fake, S, T, 8, 2, 64, 16, 1000, mb,
+        return lib.pkv_prefill_attn(0, fake, fake, fake, fake, fake, S, T, 8, 2, 64, 16, 1000, mb,
                                     16 * mb, 0.1, 1, c.ctypes.data, fake, c.size, None, 0, None)
     assert call(p) == 6
     o_units = HDR + 3 * T + 1

@@ -68,3 +68,88 @@ def test_nan_payload_copied_bitwise():
     torch.cuda.synchronize()
     assert int((kc.view(torch.int16) == 0x7E01).sum()) == 64
     assert int((vc.view(torch.int16) == -1).sum()) == 64
+
+
+def _prompt_slots(rng, nb, starts_lens):
+    """Slots of prompt chunks: each (start, length) is a sequence's new tokens at positions
+    start .. start + length - 1, through a table of distinct random blocks."""
+    perm = iter(rng.permutation(nb))
+    out = []
+    for start, n in starts_lens:
+        blocks = {}
+        for pos in range(start, start + n):
+            if pos // 16 not in blocks:
+                blocks[pos // 16] = next(perm)
+            out.append(blocks[pos // 16] * 16 + pos % 16)
+    return np.asarray(out, np.int32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("hd", [64, 128])
+def test_write_prompt_runs_bit_exact(dtype, hd):
+    """Prompt-shaped writes: runs of consecutive slots that start mid-block, fill whole
+    blocks, cross block and 16-row group boundaries, end mid-block; padding and out-of-pool
+    rows inside runs; a tail of T not a multiple of 16."""
+    import paged_kv_cache_459_amd as pkv
+    print(f"[write prompt runs] dtype={dtype} hd={hd}", flush=True)
+    rng = np.random.default_rng(300 + hd)
+    hkv, nb = 2, 80
+    slots = _prompt_slots(rng, nb, [(0, 16), (5, 40), (16, 32), (3, 1), (30, 77), (15, 2),
+                                    (0, 7), (9, 25)])
+    T = len(slots)
+    slots[20] = -1          # padding inside a run
+    slots[60] = nb * 16 + 5  # outside the pool inside a run
+    size = nb * hkv * hd * 16
+    kc = W.normal_values(rng, (size,), dtype)
+    vc = W.normal_values(rng, (size,), dtype)
+    k = W.normal_values(rng, (T, hkv, hd), dtype)
+    v = W.normal_values(rng, (T, hkv, hd), dtype)
+    want_k, want_v = CW.write_kv(k, v, kc, vc, slots, hkv=hkv, hd=hd, bs=16, dtype=dtype)
+    ks, vs = pkv.cache_shapes(nb, hkv, hd, G.TORCH[dtype])
+    dk = G.to_dev(kc, dtype).view(ks)
+    dv = G.to_dev(vc, dtype).view(vs)
+    pkv.pkv_write(G.to_dev(k, dtype), G.to_dev(v, dtype), dk, dv, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(W.to_storage_numpy(dk, dtype).reshape(-1).view(np.uint8),
+                                  want_k.view(np.uint8))
+    np.testing.assert_array_equal(W.to_storage_numpy(dv, dtype).reshape(-1).view(np.uint8),
+                                  want_v.view(np.uint8))
+
+
+def test_write_full_size_prompt_chunk():
+    """The chunked-prefill workload's write: 16 chunks of 512 tokens after U[0, 1536] cached
+    tokens, 32 kv heads x 128, f16; bit-exact on every touched block and no other block."""
+    import paged_kv_cache_459_amd as pkv
+    print("[write] 8192 prompt tokens x 32 heads f16", flush=True)
+    shape = W.SHAPES["prefill"]
+    rng = W.rng_for(shape.seed)
+    lens, qlens = W.prefill_lengths(rng, shape.B)
+    nb = W.pool_blocks(lens)
+    tables = W.place_sequences(lens, rng.permutation(nb).astype(np.int32))
+    slots = np.concatenate([tables[s, np.arange(lens[s] - qlens[s], lens[s]) // 16] * 16 +
+                            np.arange(lens[s] - qlens[s], lens[s]) % 16
+                            for s in range(shape.B)]).astype(np.int32)
+    T, hkv, hd = len(slots), shape.Hkv, shape.hd
+    kc, vc = pkv.alloc_caches(nb, hkv, hd, torch.float16)
+    kc.view(-1).copy_(W.device_normal((kc.numel(),), "f16", 31))
+    vc.view(-1).copy_(W.device_normal((vc.numel(),), "f16", 32))
+    k = W.device_normal((T, hkv, hd), "f16", 33)
+    v = W.device_normal((T, hkv, hd), "f16", 34)
+    touched = sorted(set((slots // 16).tolist()))
+    idx = torch.tensor(touched, dtype=torch.long, device="cuda")
+    kc0 = W.to_storage_numpy(kc.index_select(0, idx), "f16").reshape(-1)
+    vc0 = W.to_storage_numpy(vc.index_select(0, idx), "f16").reshape(-1)
+    before = (kc.clone(), vc.clone())
+    pkv.pkv_write(k, v, kc, vc, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    remap = {b: i for i, b in enumerate(touched)}
+    local = np.array([remap[s // 16] * 16 + s % 16 for s in slots], np.int32)
+    want_k, want_v = CW.write_kv(W.to_storage_numpy(k, "f16"), W.to_storage_numpy(v, "f16"),
+                                 kc0, vc0, local, hkv=hkv, hd=hd, bs=16, dtype="f16")
+    got_k = W.to_storage_numpy(kc.index_select(0, idx), "f16").reshape(-1)
+    got_v = W.to_storage_numpy(vc.index_select(0, idx), "f16").reshape(-1)
+    np.testing.assert_array_equal(got_k.view(np.uint8), want_k.view(np.uint8))
+    np.testing.assert_array_equal(got_v.view(np.uint8), want_v.view(np.uint8))
+    mask = torch.ones(nb, dtype=torch.bool, device="cuda")
+    mask[idx] = False
+    assert torch.equal(kc[mask], before[0][mask]) and torch.equal(vc[mask], before[1][mask])
