@@ -726,7 +726,7 @@ def prefill_main(args, torch, pkv, W):
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_PEAK_TFLOPS[dtype], 4),
             "traffic": measured_traffic("prefill", kernel_source_digest()),
-            "kernel": "prefill attention pass (attn_shared_kernel, causal rows)",
+            "kernel": "prefill attention pass (attn_prefill_kernel)",
             "algorithmic_flops_per_launch": flops,
         },
     }

@@ -429,7 +429,7 @@ pkv_status pkv_prefill_plan(const int32_t* query_start, const int32_t* context_l
   std::vector<int32_t> v;
   const int32_t zero = 0;
   pkv::prefill_plan_build(S > 0 ? query_start : &zero, context_lens, S, Hkv, G,
-                          pkv::kRowsPerTile / G, pkv::kMaxUnitBlocks, &v);
+                          pkv::prefill_tile_rows(G), pkv::kPrefillMaxBlocks, &v);
   *plan_ints = v.size();
   if (!plan || capacity < v.size()) return PKV_ERR_WORKSPACE;
   std::memcpy(plan, v.data(), v.size() * sizeof(int32_t));
@@ -471,10 +471,9 @@ pkv_status pkv_prefill_attn(int32_t pass, void* out, const void* q, const void* 
   const int32_t G = Hq / Hkv;
   pkv::PlanView pv;
   if (!pkv::prefill_plan_check(plan_host, plan_ints, T, S, max_blocks, max_context_len, Hkv, G,
-                               pkv::kRowsPerTile / G, pkv::kMaxUnitBlocks, &pv))
+                               pkv::prefill_tile_rows(G), pkv::kPrefillMaxBlocks, &pv))
     return PKV_ERR_INVALID_ARG;
-  if (static_cast<int64_t>(pv.U) * Hkv >= (int64_t{1} << 31) - pkv::kWaves * 8)
-    return PKV_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(pv.U) * Hkv >= (int64_t{1} << 31) - 8) return PKV_ERR_UNSUPPORTED;
   const PrefillLayout L = prefill_layout(pv.cells, G, hd);
   if (L.bytes > 0 && (!workspace || workspace_bytes < L.bytes)) return PKV_ERR_WORKSPACE;
   if (L.bytes > 0 && !aligned16(workspace)) return PKV_ERR_INVALID_ARG;
@@ -507,7 +506,7 @@ pkv_status pkv_prefill_attn(int32_t pass, void* out, const void* q, const void* 
   p.shared_cells = pv.cells;
   p.shared_base = 0;
   p.table_rows = S;
-  if ((pass == 0 || pass == 1) && pkv::launch_shared(p, dtype, pkv::kMatrix, hs) != hipSuccess)
+  if ((pass == 0 || pass == 1) && pkv::launch_prefill(p, dtype, hs) != hipSuccess)
     return PKV_ERR_HIP;
   if ((pass == 0 || pass == 2) && pv.has_shared &&
       pkv::launch_merge(p, dtype, pkv::kMatrix, hs) != hipSuccess)

@@ -27,6 +27,11 @@ constexpr int kPlanChunk = 16;    // blocks per unit of a run
 constexpr int kMaxPlannedGroup = 4;  // q heads per kv head up to which batches are planned
 constexpr int kMaxUnitBlocks = 64;   // blocks of one unit (one block id per lane)
 constexpr int32_t kPrefillMagic = 0x50524631;
+constexpr int kPrefillMaxBlocks = 512;  // blocks of one prefill unit (their ids sit in LDS)
+#ifndef PKV_PREFILL_RT
+#define PKV_PREFILL_RT 2
+#endif
+constexpr int kPrefillRowTiles = PKV_PREFILL_RT;  // 16-row tiles per wave of the prefill kernel
 
 struct PlanView {
   int32_t U = 0, cells = 0;
@@ -112,6 +117,10 @@ struct StreamParams {
 
 // dtype: 0 f32, 1 f16, 2 bf16 (pkv_dtype). Return the launch status (hipGetLastError).
 hipError_t launch_write(const WriteParams& p, int32_t dtype, hipStream_t stream);
+// Prefill attention pass (pkv_prefill.hip): units of the prefill plan, f16/bf16.
+hipError_t launch_prefill(const StreamParams& p, int32_t dtype, hipStream_t stream);
+// Prompt tokens per prefill unit for q-head group size G (a work-group's rows / G).
+int32_t prefill_tile_rows(int32_t G);
 hipError_t launch_copy_blocks(const CopyParams& p, int32_t dtype, hipStream_t stream);
 // Work-groups per block and cache of the copy kernel (grid.y; at most 65535 is launchable).
 int32_t copy_blocks_grid_y(int32_t Hkv, int32_t hd, int32_t dtype);

@@ -3,7 +3,7 @@ against the oracle's causal prefill (oracle.attention.prefill_attention), within
 for f16/bf16.
 
 Cases: whole prompts (first token sees only itself), cached prefixes and chunks whose rows see
-more than one 64-block chunk (pieces merged), single new tokens, empty sequences, sequences
+more than one 512-block chunk (pieces merged), single new tokens, empty sequences, sequences
 sharing their prefix blocks (prefix caching), MHA and GQA groups up to 16, head dims 64 and 128,
 unused slots holding NaN; and the 8192-token chunked-prefill workload at full size, on sampled
 rows. Every output starts as NaN, so a row the kernels never write fails the check.
@@ -72,8 +72,8 @@ def test_whole_prompts(dtype, hq, hkv, hd):
 @pytest.mark.parametrize("dtype,hq,hkv,hd", HEADS[:3] + [("bf16", 8, 1, 64)])
 def test_cached_prefixes_and_split_rows(dtype, hq, hkv, hd):
     print(f"[prefill cached/split] {dtype} {hq}/{hkv} hd{hd}", flush=True)
-    lens = [300, 64, 2100, 1500, 33, 2065, 4000]
-    qlens = [37, 1, 64, 200, 33, 9, 20]
+    lens = [300, 64, 2100, 1500, 33, 2065, 9000, 8300]
+    qlens = [37, 1, 64, 200, 33, 9, 20, 300]
     p, q, qs = problem(1300 + hq, lens, qlens, hq, hkv, hd, dtype)
     scale = G.scale_for(hd)
     got, plan = prefill_gpu(p, q, qs, scale, hq)

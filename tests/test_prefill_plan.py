@@ -1,9 +1,10 @@
 """The prefill planner (pkv_prefill_plan, host code) against brute-force definitions.
 
 For batches mixing whole prompts, cached prefixes, single new tokens, empty sequences and
-rows that see more than one chunk (64 blocks):
+rows that see more than one chunk (512 blocks):
 * row t of sequence s (t = query_start[s] + k) sees vis_t = n_s - q_s + k + 1 tokens;
-* the units naming t belong to t's sequence, hold consecutive rows of it (at most 16 / G),
+* the units naming t belong to t's sequence, hold consecutive rows of it (at most the
+  plan's tile size: a work-group's 64*RT rows / G, RT = 2 or 4),
   and their block ranges tile [0, ceil(v / 16)) in order, v the largest vis of the tile;
 * a tile with one unit is direct (cell_base -1, the row is not merged); otherwise every
   unit has cells, cells are handed out consecutively, and the row's piece list names exactly
@@ -44,7 +45,7 @@ def batch(kind, rng):
         n = np.array([1, 17, 40, 5, 100, 16], np.int32)
         return n, n.copy()
     if kind == "cached":
-        n = np.array([300, 64, 2100, 1500, 33, 1024 + 16 * 64 + 1], np.int32)
+        n = np.array([300, 64, 2100, 1500, 33, 8192 + 16 * 64 + 1], np.int32)
         q = np.array([37, 1, 64, 200, 33, 9], np.int32)
         return n, q
     if kind == "empty":
@@ -52,7 +53,7 @@ def batch(kind, rng):
         q = np.array([0, 0, 50, 3], np.int32)
         return n, q
     S = 12  # random
-    n = rng.integers(1, 3000, size=S).astype(np.int32)
+    n = rng.integers(1, 12000, size=S).astype(np.int32)
     q = np.array([rng.integers(0, x + 1) for x in n], np.int32)
     return n, q
 
@@ -70,7 +71,7 @@ def test_prefill_plan_matches_brute_force(kind, hq, hkv):
     G = hq // hkv
     T = int(qs[-1])
     assert (P["T"], P["H"], P["GS"], P["S"]) == (T, hkv, G, len(n))
-    assert P["rows"] == 16 // G and P["chunk"] == 64
+    assert P["rows"] in ((64 * 2) // G, (64 * 4) // G) and P["chunk"] == 512
     seq_of = np.repeat(np.arange(len(n)), q)
     vis = np.array([n[s] - q[s] + (t - qs[s]) + 1 for t, s in zip(range(T), seq_of)], np.int64)
     np.testing.assert_array_equal(P["vis"], vis)
@@ -81,7 +82,7 @@ def test_prefill_plan_matches_brute_force(kind, hq, hkv):
     for u in P["units"]:
         s, b0, b1, off, cnt, cbase = (int(x) for x in u)
         rows = P["members"][off:off + cnt]
-        assert 1 <= cnt <= 16 // G and b0 < b1 and b1 - b0 <= 64
+        assert 1 <= cnt <= P["rows"] and b0 < b1 and b1 - b0 <= 512
         np.testing.assert_array_equal(rows, np.arange(rows[0], rows[0] + cnt))
         assert np.all(seq_of[rows] == s)
         assert b1 <= -(-int(vis[rows].max()) // 16)
@@ -103,7 +104,7 @@ def test_prefill_plan_matches_brute_force(kind, hq, hkv):
         else:
             assert not any(direct[t]) and P["skip"][t] == 1
         assert P["list"][P["ptr"][t]:P["ptr"][t + 1]].tolist() == lists[t]
-    if kind == "cached":  # rows past 64 blocks are split, short ones are not
+    if kind == "cached":  # rows past 512 blocks are split, short ones are not
         assert P["skip"].any() and not P["skip"].all()
 
 
@@ -126,10 +127,10 @@ def test_bad_arguments_are_refused(qs, lens, dt, hq, hkv, status):
 
 
 def test_corrupted_plans_are_refused_on_the_host():
-    n = np.array([300, 1500, 40], np.int32)
+    n = np.array([300, 9000, 40], np.int32)
     q = np.array([20, 100, 40], np.int32)
     qs = np.concatenate([[0], np.cumsum(q)]).astype(np.int32)
-    T, S, mb = int(qs[-1]), 3, 96
+    T, S, mb = int(qs[-1]), 3, 576
     p = m.pkv_prefill_plan(qs, n, num_q_heads=8, num_kv_heads=2, max_blocks=mb,
                            max_context_len=16 * mb, dtype=torch.float16)
     P = parse(p)
@@ -151,9 +152,9 @@ def test_corrupted_plans_are_refused_on_the_host():
     o_split = o_units + 6 * split
     bad = []
     for idx, val in [(0, 0), (1, T + 1), (2, 8), (3, 1), (4, P["U"] + 1), (7, -1), (9, 2),
-                     (8, 65), (10, 5), (o_units, S), (o_units + 1, -1), (o_units + 2, mb + 1),
-                     (o_split + 1, 0), (o_split + 2, mb + 1), (o_units + 4, 0), (o_units + 4, 5),
-                     (o_split + 5, P["cells"]), (o_units + 5, -2), (HDR, 2), (HDR + T, 0),
+                     (8, 513), (10, 5), (o_units, S), (o_units + 1, -1), (o_units + 2, mb + 1),
+                     (o_split + 1, 0), (o_split + 2, mb + 1), (o_units + 4, 0),
+                     (o_units + 4, P["rows"] + 1), (o_split + 5, P["cells"]), (o_units + 5, -2), (HDR, 2), (HDR + T, 0),
                      (HDR + T, 16 * mb + 1), (HDR + 2 * T, 1)]:
         c = p.copy()
         c[idx] = val
