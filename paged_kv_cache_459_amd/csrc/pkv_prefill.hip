@@ -39,6 +39,9 @@ constexpr int kPW = 4;  // waves per work-group
 constexpr int kPThreads = kPW * 64;
 constexpr int kSB = 2;  // blocks per stage: one 32-token contraction
 constexpr float kNegInf = -__builtin_inff();
+// Running max before any visible token: finite, so 2^(x - m) needs no guard for rows that
+// have seen nothing yet (x = -inf gives 0, and the first visible scores always rescale).
+constexpr float kMaxInit = -3.0e38f;
 
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -62,6 +65,14 @@ struct Mma<1> {
   __device__ static __forceinline__ void put(void* base, size_t idx, float x) {
     static_cast<_Float16*>(base)[idx] = static_cast<_Float16>(x);
   }
+  // acc + the sum of the 8 packed probabilities, as rounded for the p.v contraction
+  __device__ static __forceinline__ float sum8(const uint4& pb, float acc) {
+    const half2_t one = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pb.x), one, acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pb.y), one, acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pb.z), one, acc, false);
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pb.w), one, acc, false);
+  }
 };
 
 template <>
@@ -77,9 +88,28 @@ struct Mma<2> {
   __device__ static __forceinline__ void put(void* base, size_t idx, float x) {
     static_cast<__bf16*>(base)[idx] = static_cast<__bf16>(x);
   }
+  __device__ static __forceinline__ float sum8(const uint4& pb, float acc) {
+    const bf16x2_t one = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pb.x), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pb.y), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pb.z), one, acc, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pb.w), one, acc, false);
+  }
 };
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Max over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes holding one row's scores),
+// with the gfx950 half-swaps: each returns the pair (own half copied, other half copied), so
+// the max of the pair is the max over the two halves.
+__device__ __forceinline__ float row_max4(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float m1 = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
+  const unsigned u1 = __builtin_bit_cast(unsigned, m1);
+  const auto b = __builtin_amdgcn_permlane16_swap(u1, u1, false, false);
+  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
+}
 
 // Zeroes the 16-bit tokens t0 + j (j < 8) of a V chunk with t0 + j >= valid.
 __device__ __forceinline__ uint4 keep_tokens(uint4 v, int t0, int valid) {
@@ -104,7 +134,12 @@ attn_prefill_kernel(const StreamParams p) {
   constexpr int VT = HD / 16;                // 16-dim tiles of the output
   constexpr int NCH = 2 * kSB * CHT / kPThreads;  // staged chunks per thread per stage
   static_assert(NCH * kPThreads == 2 * kSB * CHT, "stage size");
-  __shared__ __attribute__((aligned(16))) char s_kv[2][2][kSB][TILE];  // [buffer][K, V][block]
+  static_assert(kSB == 2, "one 32-token contraction per stage");
+  // Per buffer: the stage's K tiles as in the cache, then its V as one [HD][64 B] array: for
+  // dim d, 16-byte slot g ^ ((d & 15) >> 2) holds tokens 4g .. 4g+3 of the first block, then
+  // of the second. A lane's p.v operand is then one 16-byte read, and the 16 lanes reading a
+  // slot of dims 16j .. 16j+15 together touch all 64 banks once.
+  __shared__ __attribute__((aligned(16))) char s_kv[2][2 * kSB * TILE];
   __shared__ int32_t s_ids[kPrefillMaxBlocks];
   __shared__ int32_t s_vmax[kPW];
 
@@ -124,6 +159,10 @@ attn_prefill_kernel(const StreamParams p) {
   const int G = p.Hq / p.Hkv;
   const size_t blk_stride = static_cast<size_t>(p.Hkv) * TILE;
   const int nblk = b1 - b0;
+  // Scores are kept unscaled; c > 0 scales them to base-2 units inside the exponentials (a
+  // negative scale is carried by q's sign bits, flipped exactly on load).
+  const float c = fabsf(p.scale_log2);
+  const uint32_t qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
 
   const int32_t* table = p.block_tables + static_cast<size_t>(ref) * p.max_blocks;
   for (int i = tid; i < nblk; i += kPThreads) {
@@ -133,38 +172,41 @@ attn_prefill_kernel(const StreamParams p) {
   }
 
   // This lane's rows: row tile k holds local rows (w*RT + k)*16 + hq.
-  int seq[RT], jq[RT], mk[RT], n_row[RT], nmin[RT], nmax[RT];
+  int seq[RT], jq[RT], mk[RT], n_row[RT];
   uint4 qb[RT][KS];
-  int wmax = 0;
+  int wmax = 0, wmin = 0x7fffffff;
 #pragma unroll
   for (int k = 0; k < RT; ++k) {
     const int r = (w * RT + k) * 16 + hq;
     mk[k] = r / G;
     jq[k] = r - mk[k] * G;
-    int s = -1;
-    if (mk[k] < mcnt) s = p.members[moff + mk[k]];
-    seq[k] = (s >= 0 && s < p.B) ? s : -1;
+    int sq = -1;
+    if (mk[k] < mcnt) sq = p.members[moff + mk[k]];
+    seq[k] = (sq >= 0 && sq < p.B) ? sq : -1;
     n_row[k] = seq[k] < 0 ? 0 : min(max(p.row_vis[seq[k]], 0), p.max_ctx);
     if (seq[k] >= 0) {
       const uint4* qp = reinterpret_cast<const uint4*>(
           static_cast<const char*>(p.q) +
           (static_cast<size_t>(seq[k]) * p.Hq + kvh * G + jq[k]) * HD * 2);
 #pragma unroll
-      for (int s2 = 0; s2 < KS; ++s2) qb[k][s2] = qp[4 * s2 + g];
+      for (int s2 = 0; s2 < KS; ++s2) {
+        const uint4 v = qp[4 * s2 + g];
+        qb[k][s2] = make_uint4(v.x ^ qsign, v.y ^ qsign, v.z ^ qsign, v.w ^ qsign);
+      }
     } else {
 #pragma unroll
       for (int s2 = 0; s2 < KS; ++s2) qb[k][s2] = make_uint4(0, 0, 0, 0);
     }
-    int lo = seq[k] >= 0 ? n_row[k] : 0x7fffffff, hi = n_row[k];
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-      lo = min(lo, __shfl_xor(lo, off));
-      hi = max(hi, __shfl_xor(hi, off));
-    }
-    nmin[k] = uniform(lo);
-    nmax[k] = uniform(hi);
-    wmax = max(wmax, nmax[k]);
+    wmin = min(wmin, seq[k] >= 0 ? n_row[k] : 0x7fffffff);
+    wmax = max(wmax, n_row[k]);
   }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    wmin = min(wmin, __shfl_xor(wmin, off));
+    wmax = max(wmax, __shfl_xor(wmax, off));
+  }
+  wmin = uniform(wmin);  // the wave's shortest and longest visible lengths
+  wmax = uniform(wmax);
   if (lane == 0) s_vmax[w] = wmax;
   __syncthreads();  // s_ids, s_vmax
   int vmax = s_vmax[0];
@@ -177,8 +219,8 @@ attn_prefill_kernel(const StreamParams p) {
   auto stage_load = [&](uint4 (&r)[NCH], int t) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int c = tid + kPThreads * i;
-      const int tile = c / CHT, ci = c - tile * CHT;
+      const int ch = tid + kPThreads * i;
+      const int tile = ch / CHT, ci = ch - tile * CHT;
       const int kv = tile / kSB, sb = tile - kv * kSB;
       const int blk = t + sb;
       const int id = blk < b1 ? s_ids[blk - b0] : -1;
@@ -193,15 +235,22 @@ attn_prefill_kernel(const StreamParams p) {
   auto stage_store = [&](const uint4 (&r)[NCH], int buf, int t) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int c = tid + kPThreads * i;
-      const int tile = c / CHT, ci = c - tile * CHT;
+      const int ch = tid + kPThreads * i;
+      const int tile = ch / CHT, ci = ch - tile * CHT;
       const int kv = tile / kSB, sb = tile - kv * kSB;
       uint4 v = r[i];
-      const int tok0 = kBlockSize * (t + sb);
-      // V slots at or past every row's last visible token: zero (a V chunk is 8 tokens of one
-      // dim row of the dim-major tile)
-      if (kv == 1 && tok0 + kBlockSize > vmax) v = keep_tokens(v, 8 * (ci & 1), vmax - tok0);
-      *reinterpret_cast<uint4*>(&s_kv[buf][kv][sb][16 * ci]) = v;
+      if (kv == 0) {
+        *reinterpret_cast<uint4*>(&s_kv[buf][sb * TILE + 16 * ci]) = v;
+      } else {
+        // a V chunk: dim d = ci / 2, tokens 8h .. 8h+7 (h = ci & 1) of block sb: groups 2h, 2h+1
+        const int tok0 = kBlockSize * (t + sb), d = ci >> 1, h = ci & 1;
+        // slots at or past every row's last visible token: zero
+        if (tok0 + kBlockSize > vmax) v = keep_tokens(v, 8 * h, vmax - tok0);
+        char* row = &s_kv[buf][kSB * TILE + 64 * d + 8 * sb];
+        const int sw = (d & 15) >> 2;
+        *reinterpret_cast<uint2*>(row + 16 * ((2 * h) ^ sw)) = make_uint2(v.x, v.y);
+        *reinterpret_cast<uint2*>(row + 16 * ((2 * h + 1) ^ sw)) = make_uint2(v.z, v.w);
+      }
     }
   };
 
@@ -209,78 +258,102 @@ attn_prefill_kernel(const StreamParams p) {
   float4_t o[RT][VT];
 #pragma unroll
   for (int k = 0; k < RT; ++k) {
-    m[k] = kNegInf;
+    m[k] = kMaxInit;
     lsum[k] = 0.f;
 #pragma unroll
     for (int j = 0; j < VT; ++j) o[k][j] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
+  const int v_lane = 64 * hq + 16 * (g ^ (hq >> 2));
 
   auto compute = [&](int buf, int t) {
     if (kBlockSize * t >= wmax) return;  // nothing of the stage is visible to this wave
     const int ida = s_ids[t - b0];
     const int idb = t + 1 < b1 ? s_ids[t + 1 - b0] : -1;
-    const char* ka = s_kv[buf][0][0];
-    const char* kb = s_kv[buf][0][1];
-    const char* va = s_kv[buf][1][0];
-    const char* vb = s_kv[buf][1][1];
+    const char* kt = s_kv[buf];
+    const char* vt = s_kv[buf] + kSB * TILE;
     uint4 kfa[KS], kfb[KS], vf[VT];
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) {
-      kfa[s2] = *reinterpret_cast<const uint4*>(ka + 1024 * s2 + 16 * lane);
-      kfb[s2] = *reinterpret_cast<const uint4*>(kb + 1024 * s2 + 16 * lane);
+      kfa[s2] = *reinterpret_cast<const uint4*>(kt + 1024 * s2 + 16 * lane);
+      kfb[s2] = *reinterpret_cast<const uint4*>(kt + TILE + 1024 * s2 + 16 * lane);
     }
 #pragma unroll
-    for (int j = 0; j < VT; ++j) {
-      const uint2 x = *reinterpret_cast<const uint2*>(va + 512 * j + 32 * hq + 8 * g);
-      const uint2 y = *reinterpret_cast<const uint2*>(vb + 512 * j + 32 * hq + 8 * g);
-      vf[j] = make_uint4(x.x, x.y, y.x, y.y);
-    }
+    for (int j = 0; j < VT; ++j) vf[j] = *reinterpret_cast<const uint4*>(vt + 1024 * j + v_lane);
+    // S^T of every row tile (independent accumulation chains, interleaved)
+    float4_t sa[RT], sbv[RT];
 #pragma unroll
     for (int k = 0; k < RT; ++k) {
-      if (kBlockSize * t >= nmax[k]) continue;
-      float4_t sa = {0.f, 0.f, 0.f, 0.f}, sbv = {0.f, 0.f, 0.f, 0.f};
+      sa[k] = float4_t{0.f, 0.f, 0.f, 0.f};
+      sbv[k] = float4_t{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
-      for (int s2 = 0; s2 < KS; ++s2) {
-        sa = MM::mul(kfa[s2], qb[k][s2], sa);
-        sbv = MM::mul(kfb[s2], qb[k][s2], sbv);
+    for (int s2 = 0; s2 < KS; ++s2)
+#pragma unroll
+      for (int k = 0; k < RT; ++k) {
+        sa[k] = MM::mul(kfa[s2], qb[k][s2], sa[k]);
+        sbv[k] = MM::mul(kfb[s2], qb[k][s2], sbv[k]);
       }
-      float x[8];
+    float x[RT][8];
+#pragma unroll
+    for (int k = 0; k < RT; ++k)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[i] = sa[i] * p.scale_log2;
-        x[4 + i] = sbv[i] * p.scale_log2;
+        x[k][i] = sa[k][i];
+        x[k][4 + i] = sbv[k][i];
       }
-      const bool full = ida >= 0 && idb >= 0 && kBlockSize * (t + 2) <= nmin[k];
-      if (!full) {
+    // every row of the wave sees all 32 tokens: no masking
+    const bool full = ida >= 0 && idb >= 0 && kBlockSize * (t + 2) <= wmin;
+    if (!full) {
+#pragma unroll
+      for (int k = 0; k < RT; ++k) {
         const int ra = ida < 0 ? 0 : min(kBlockSize, max(0, n_row[k] - kBlockSize * t));
         const int rb = idb < 0 ? 0 : min(kBlockSize, max(0, n_row[k] - kBlockSize * (t + 1)));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          x[i] = 4 * g + i < ra ? x[i] : kNegInf;
-          x[4 + i] = 4 * g + i < rb ? x[4 + i] : kNegInf;
+          x[k][i] = 4 * g + i < ra ? x[k][i] : kNegInf;
+          x[k][4 + i] = 4 * g + i < rb ? x[k][4 + i] : kNegInf;
         }
       }
-      float bm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      const float mn = fmaxf(m[k], bm);
-      float alpha = __builtin_amdgcn_exp2f(m[k] - mn);
+    }
+    float bm[RT];
+    bool grow = false;
+#pragma unroll
+    for (int k = 0; k < RT; ++k) {
+      const float v = fmaxf(fmaxf(fmaxf(x[k][0], x[k][1]), fmaxf(x[k][2], x[k][3])),
+                            fmaxf(fmaxf(x[k][4], x[k][5]), fmaxf(x[k][6], x[k][7])));
+      bm[k] = row_max4(v) * c;  // base-2 units (c > 0 keeps the order)
+      grow = grow || bm[k] > m[k];
+    }
+    // Exact running max (the largest probability of a row is exactly 1, so its token's weight
+    // carries no rounding in the 16-bit p.v operand); the rescale is skipped, wave-uniformly,
+    // when no row's max rose.
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int k = 0; k < RT; ++k) {
+        const float mn = fmaxf(m[k], bm[k]);
+        const float alpha = __builtin_amdgcn_exp2f(m[k] - mn);
+        m[k] = mn;
+        lsum[k] *= alpha;
+#pragma unroll
+        for (int j = 0; j < VT; ++j) o[k][j] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < RT; ++k) {
       float pr[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - mn);
-      if (!full && mn == kNegInf) {  // nothing visible to this row yet
-        alpha = 1.f;
+      for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(x[k][i], c, -m[k]));
+      if (!full) {  // masked tokens: probability 0 whatever the scale (-inf * 0 would be NaN)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pr[i] = 0.f;
+        for (int i = 0; i < 8; ++i) pr[i] = x[k][i] == kNegInf ? 0.f : pr[i];
       }
-      lsum[k] = fmaf(lsum[k], alpha, ((pr[0] + pr[1]) + (pr[2] + pr[3])) +
-                                         ((pr[4] + pr[5]) + (pr[6] + pr[7])));
-      m[k] = mn;
       const uint4 pb = make_uint4(MM::pack2(pr[0], pr[1]), MM::pack2(pr[2], pr[3]),
                                   MM::pack2(pr[4], pr[5]), MM::pack2(pr[6], pr[7]));
+      // the row sum takes the probabilities as rounded for the contraction: numerator and
+      // denominator then weigh every token alike
+      lsum[k] = MM::sum8(pb, lsum[k]);
 #pragma unroll
-      for (int j = 0; j < VT; ++j) o[k][j] = MM::mul(vf[j], pb, o[k][j] * alpha);
+      for (int j = 0; j < VT; ++j) o[k][j] = MM::mul(vf[j], pb, o[k][j]);
     }
   };
 
@@ -319,7 +392,7 @@ attn_prefill_kernel(const StreamParams p) {
       for (int j = 0; j < VT; ++j)
         *reinterpret_cast<float4_t*>(p.ws_o + cell * HD + 16 * j + 4 * g) = o[k][j];
       if (g == 0) {
-        p.ws_ml[cell * 2] = m[k];
+        p.ws_ml[cell * 2] = l > 0.f ? m[k] : kNegInf;  // no visible token: an empty piece
         p.ws_ml[cell * 2 + 1] = l;
       }
     }

@@ -91,6 +91,18 @@ def test_empty_sequences_and_single_tokens(dtype, hq, hkv, hd):
     G.assert_close(got, oracle(p, q, qs, 0.2), dtype, "empty sequences")
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.09])
+def test_zero_and_negative_scale(scale):
+    """scale 0: every visible token weighs the same (the mean of V); a negative scale flips
+    the scores (carried by q's sign bits in the kernel)."""
+    print(f"[prefill scale] {scale}", flush=True)
+    lens = [40, 300, 17]
+    qlens = [40, 100, 3]
+    p, q, qs = problem(1450, lens, qlens, 8, 2, 128, "bf16")
+    got, _ = prefill_gpu(p, q, qs, scale, 8)
+    G.assert_close(got, oracle(p, q, qs, scale), "bf16", f"scale {scale}")
+
+
 def test_no_new_tokens_is_a_no_op():
     import paged_kv_cache_459_amd as m
     lens = [10, 20]
