@@ -12,7 +12,8 @@
 // of the kv head's group), 16*RT per wave as RT row tiles of 16. The unit's blocks stream
 // through LDS two at a time (double-buffered): each K/V tile is read from memory once per
 // work-group and from LDS once per wave, and every fragment read from LDS feeds the RT row
-// tiles' contractions. Both contractions run on 16x16x32 matrix-core instructions:
+// tiles' contractions; each stage's loads are issued two stages ahead. Both contractions run
+// on 16x16x32 matrix-core instructions:
 //   S^T (16 tokens x 16 rows) = K (16 x hd) . Q^T, per block;
 //   O^T (16 dims x 16 rows) += V^T (16 dims x 32 tokens) . P^T, over the stage's two blocks,
 // with the contraction index k = 8g + i standing for token 4g + i of the first block (i < 4)
@@ -38,6 +39,7 @@ namespace {
 constexpr int kPW = 4;  // waves per work-group
 constexpr int kPThreads = kPW * 64;
 constexpr int kSB = 2;  // blocks per stage: one 32-token contraction
+constexpr int kNBuf = 4;  // LDS stage buffers (loads run kNBuf - 1 stages ahead)
 constexpr float kNegInf = -__builtin_inff();
 // Running max before any visible token: finite, so 2^(x - m) needs no guard for rows that
 // have seen nothing yet (x = -inf gives 0, and the first visible scores always rescale).
@@ -123,23 +125,50 @@ __device__ __forceinline__ uint4 keep_tokens(uint4 v, int t0, int valid) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// One lane's 16 bytes from global memory straight into LDS (gfx950 global_load_lds_dwordx4):
+// the wave's 64 lanes fill the 1 KB at LDS byte address `lds` (wave-uniform, through M0) in
+// lane order. Issued as inline assembly so that the compiler neither tracks it nor adds its
+// own (conservative: every later LDS read) waits; the kernel waits on vmcnt itself.
+__device__ __forceinline__ void load_lds16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds)
+               : "memory", "m0");
+}
+
+// Barrier of the stage loop: orders LDS only (a full __syncthreads would also wait for every
+// load to LDS still in flight, the later stages' included). Each wave's reads of the previous
+// stage have completed (lgkmcnt) before it passes, so that stage's buffer may be reloaded.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Waits until at most n of this wave's vector-memory operations are outstanding (they
+// complete in order), n a multiple of the per-stage count; only the values used here.
+template <int NCH>
+__device__ __forceinline__ void wait_stages(int ahead) {
+  // s_waitcnt: vmcnt in bits [3:0] (and [15:14]), expcnt [6:4] and lgkmcnt [11:8] left at max
+  if (ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NCH));
+  else if (ahead == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | NCH);
+  else __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 template <int DT, int HD, int RT>
 __global__ void __launch_bounds__(kPThreads)
 __attribute__((amdgpu_waves_per_eu(RT >= 4 ? 1 : 2, RT >= 4 ? 1 : 2)))
 attn_prefill_kernel(const StreamParams p) {
   using MM = Mma<DT>;
   constexpr int TILE = HD * kBlockSize * 2;  // bytes of one (block, kv head) K or V tile
-  constexpr int CHT = TILE / 16;             // 16-byte chunks per tile
+  constexpr int PPT = TILE / 1024;           // 1 KB pieces per tile (one wave-wide load each)
   constexpr int KS = HD / 32;                // contraction steps of q . k
   constexpr int VT = HD / 16;                // 16-dim tiles of the output
-  constexpr int NCH = 2 * kSB * CHT / kPThreads;  // staged chunks per thread per stage
-  static_assert(NCH * kPThreads == 2 * kSB * CHT, "stage size");
+  constexpr int STAGE = 2 * kSB * TILE;      // bytes of one stage: K, then V, of its blocks
+  constexpr int NCH = STAGE / 1024 / kPW;    // loads per thread per stage
+  static_assert(NCH * kPW * 1024 == STAGE && 2 * NCH <= 15, "stage size");
   static_assert(kSB == 2, "one 32-token contraction per stage");
-  // Per buffer: the stage's K tiles as in the cache, then its V as one [HD][64 B] array: for
-  // dim d, 16-byte slot g ^ ((d & 15) >> 2) holds tokens 4g .. 4g+3 of the first block, then
-  // of the second. A lane's p.v operand is then one 16-byte read, and the 16 lanes reading a
-  // slot of dims 16j .. 16j+15 together touch all 64 banks once.
-  __shared__ __attribute__((aligned(16))) char s_kv[2][2 * kSB * TILE];
+  __shared__ __attribute__((aligned(1024))) char s_kv[kNBuf][STAGE];
   __shared__ int32_t s_ids[kPrefillMaxBlocks];
   __shared__ int32_t s_vmax[kPW];
 
@@ -214,43 +243,36 @@ attn_prefill_kernel(const StreamParams p) {
   for (int i = 1; i < kPW; ++i) vmax = max(vmax, s_vmax[i]);
   vmax = uniform(vmax);
 
-  // Staging: chunk c of a stage is chunk c % CHT of tile c / CHT, tiles ordered K of the
-  // stage's blocks, then V of them.
-  auto stage_load = [&](uint4 (&r)[NCH], int t) {
+  // Staging: the stage's blocks a (t) and b (t + 1) go straight from memory to LDS, each
+  // wave-wide load moving one 1 KB piece of a tile; the lanes' source addresses place the
+  // 16-byte chunks (bank-swizzled for the reads below):
+  //   K tile: slot 16c + pos holds chunk c (dims 8c .. 8c+7) of token t, pos = t for block a
+  //           and (t + 4) & 15 for block b;
+  //   V tile: slot 2d + (h ^ ((d >> 3) & 1)) holds tokens 8h .. 8h+7 of dim d.
+  // An entry naming no block of the pool (or a block past the unit) is read from block 0 and
+  // masked when computed.
+  auto issue = [&](int t, int buf) {
+    const int id0 = uniform(max(s_ids[t - b0], 0));
+    const int id1 = uniform(t + 1 < b1 ? max(s_ids[t + 1 - b0], 0) : 0);
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int ch = tid + kPThreads * i;
-      const int tile = ch / CHT, ci = ch - tile * CHT;
-      const int kv = tile / kSB, sb = tile - kv * kSB;
-      const int blk = t + sb;
-      const int id = blk < b1 ? s_ids[blk - b0] : -1;
-      r[i] = make_uint4(0, 0, 0, 0);
-      if (id >= 0) {
-        const char* src = static_cast<const char*>(kv ? p.v_cache : p.k_cache) +
-                          static_cast<size_t>(id) * blk_stride + static_cast<size_t>(kvh) * TILE;
-        r[i] = *reinterpret_cast<const uint4*>(src + 16 * ci);
-      }
-    }
-  };
-  auto stage_store = [&](const uint4 (&r)[NCH], int buf, int t) {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int ch = tid + kPThreads * i;
-      const int tile = ch / CHT, ci = ch - tile * CHT;
-      const int kv = tile / kSB, sb = tile - kv * kSB;
-      uint4 v = r[i];
+      const int piece = w + kPW * i;  // wave-uniform
+      const int tile = piece / PPT, sigma = (piece % PPT) * 64 + lane;
+      const int kv = tile / kSB, sb = tile % kSB;
+      int src;
       if (kv == 0) {
-        *reinterpret_cast<uint4*>(&s_kv[buf][sb * TILE + 16 * ci]) = v;
+        const int cc = sigma >> 4, pos = sigma & 15;
+        src = 256 * cc + 16 * (sb == 0 ? pos : ((pos - 4) & 15));
       } else {
-        // a V chunk: dim d = ci / 2, tokens 8h .. 8h+7 (h = ci & 1) of block sb: groups 2h, 2h+1
-        const int tok0 = kBlockSize * (t + sb), d = ci >> 1, h = ci & 1;
-        // slots at or past every row's last visible token: zero
-        if (tok0 + kBlockSize > vmax) v = keep_tokens(v, 8 * h, vmax - tok0);
-        char* row = &s_kv[buf][kSB * TILE + 64 * d + 8 * sb];
-        const int sw = (d & 15) >> 2;
-        *reinterpret_cast<uint2*>(row + 16 * ((2 * h) ^ sw)) = make_uint2(v.x, v.y);
-        *reinterpret_cast<uint2*>(row + 16 * ((2 * h + 1) ^ sw)) = make_uint2(v.z, v.w);
+        const int d = sigma >> 1, h = (sigma & 1) ^ ((d >> 3) & 1);
+        src = 32 * d + 16 * h;
       }
+      const char* base = static_cast<const char*>(kv ? p.v_cache : p.k_cache) +
+                         static_cast<size_t>(sb == 0 ? id0 : id1) * blk_stride +
+                         static_cast<size_t>(kvh) * TILE;
+      const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+          (__attribute__((address_space(3))) char*)(&s_kv[buf][piece * 1024])));
+      load_lds16(base + src, static_cast<uint32_t>(uniform(static_cast<int>(lds))));
     }
   };
 
@@ -263,23 +285,40 @@ attn_prefill_kernel(const StreamParams p) {
 #pragma unroll
     for (int j = 0; j < VT; ++j) o[k][j] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
-  const int v_lane = 64 * hq + 16 * (g ^ (hq >> 2));
+  // q . k runs as two 16-token contractions whose K rows are permuted so that lane (hq, g)
+  // ends with the scores of 8 consecutive tokens of one block: block g >> 1, tokens
+  // 8 (g & 1) .. +7 (the first four from contraction 1, the rest from contraction 2). Row m
+  // of contraction 1 is token (m & 3) + 8 ((m >> 2) & 1) of block m >> 3; contraction 2 adds 4.
+  const int rm = lane & 15, kg = lane >> 4;
+  const int rblk = rm >> 3, rt1 = (rm & 3) + 8 * ((rm >> 2) & 1), rt2 = rt1 + 4;
+  const int k_off1 = rblk * TILE + 256 * kg + 16 * (rblk ? (rt1 + 4) & 15 : rt1);
+  const int k_off2 = rblk * TILE + 256 * kg + 16 * (rblk ? (rt2 + 4) & 15 : rt2);
+  // p.v: lane (dim 16j + hq, g) takes tokens 8 (g & 1) .. +7 of block g >> 1 in one read
+  const int v_off = kSB * TILE + (g >> 1) * TILE + 32 * hq + 16 * ((g & 1) ^ ((hq >> 3) & 1));
+  const int tok_lane = kBlockSize * (g >> 1) + 8 * (g & 1);  // first token of this lane's 8
 
   auto compute = [&](int buf, int t) {
     if (kBlockSize * t >= wmax) return;  // nothing of the stage is visible to this wave
     const int ida = s_ids[t - b0];
     const int idb = t + 1 < b1 ? s_ids[t + 1 - b0] : -1;
-    const char* kt = s_kv[buf];
-    const char* vt = s_kv[buf] + kSB * TILE;
-    uint4 kfa[KS], kfb[KS], vf[VT];
+    const char* st = s_kv[buf];
+    uint4 kf1[KS], kf2[KS], vf[VT];
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) {
-      kfa[s2] = *reinterpret_cast<const uint4*>(kt + 1024 * s2 + 16 * lane);
-      kfb[s2] = *reinterpret_cast<const uint4*>(kt + TILE + 1024 * s2 + 16 * lane);
+      kf1[s2] = *reinterpret_cast<const uint4*>(st + k_off1 + 1024 * s2);
+      kf2[s2] = *reinterpret_cast<const uint4*>(st + k_off2 + 1024 * s2);
     }
 #pragma unroll
-    for (int j = 0; j < VT; ++j) vf[j] = *reinterpret_cast<const uint4*>(vt + 1024 * j + v_lane);
-    // S^T of every row tile (independent accumulation chains, interleaved)
+    for (int j = 0; j < VT; ++j) vf[j] = *reinterpret_cast<const uint4*>(st + v_off + 512 * j);
+    // this lane's 8 tokens: valid (a block of the pool) and their first logical index
+    const bool lane_blk_ok = (g >> 1) == 0 ? ida >= 0 : idb >= 0;
+    const int tok0 = kBlockSize * t + tok_lane;
+    if (!(ida >= 0 && idb >= 0 && kBlockSize * (t + 2) <= vmax)) {
+      // V slots at or past every row's last visible token, or of no block: zero
+      const int nv = lane_blk_ok ? min(8, max(0, vmax - tok0)) : 0;
+#pragma unroll
+      for (int j = 0; j < VT; ++j) vf[j] = keep_tokens(vf[j], 0, nv);
+    }
     float4_t sa[RT], sbv[RT];
 #pragma unroll
     for (int k = 0; k < RT; ++k) {
@@ -290,8 +329,8 @@ attn_prefill_kernel(const StreamParams p) {
     for (int s2 = 0; s2 < KS; ++s2)
 #pragma unroll
       for (int k = 0; k < RT; ++k) {
-        sa[k] = MM::mul(kfa[s2], qb[k][s2], sa[k]);
-        sbv[k] = MM::mul(kfb[s2], qb[k][s2], sbv[k]);
+        sa[k] = MM::mul(kf1[s2], qb[k][s2], sa[k]);
+        sbv[k] = MM::mul(kf2[s2], qb[k][s2], sbv[k]);
       }
     float x[RT][8];
 #pragma unroll
@@ -306,13 +345,9 @@ attn_prefill_kernel(const StreamParams p) {
     if (!full) {
 #pragma unroll
       for (int k = 0; k < RT; ++k) {
-        const int ra = ida < 0 ? 0 : min(kBlockSize, max(0, n_row[k] - kBlockSize * t));
-        const int rb = idb < 0 ? 0 : min(kBlockSize, max(0, n_row[k] - kBlockSize * (t + 1)));
+        const int nr = lane_blk_ok ? min(8, max(0, n_row[k] - tok0)) : 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[k][i] = 4 * g + i < ra ? x[k][i] : kNegInf;
-          x[k][4 + i] = 4 * g + i < rb ? x[k][4 + i] : kNegInf;
-        }
+        for (int i = 0; i < 8; ++i) x[k][i] = i < nr ? x[k][i] : kNegInf;
       }
     }
     float bm[RT];
@@ -357,18 +392,17 @@ attn_prefill_kernel(const StreamParams p) {
     }
   };
 
-  uint4 stg[NCH];
+  // kNBuf LDS buffers, loads issued kNBuf - 1 stages ahead. Stage s waits for its own loads
+  // (the later stages' may stay in flight), then the barrier publishes them and tells that
+  // every wave is done with stage s - 1, whose buffer the loads of stage s + kNBuf - 1 reuse.
   const int nst = (nblk + kSB - 1) / kSB;
-  stage_load(stg, b0);
-  stage_store(stg, 0, b0);
-  __syncthreads();
+  constexpr int PD = kNBuf - 1;
+  for (int q = 0; q < PD && q < nst; ++q) issue(b0 + kSB * q, q);
   for (int s = 0; s < nst; ++s) {
-    const int t = b0 + kSB * s;
-    const bool more = s + 1 < nst;
-    if (more) stage_load(stg, t + kSB);  // in flight while this stage is computed
-    compute(s & 1, t);
-    if (more) stage_store(stg, (s + 1) & 1, t + kSB);
-    __syncthreads();
+    wait_stages<NCH>(min(PD - 1, nst - 1 - s));
+    lds_barrier();
+    if (s + PD < nst) issue(b0 + kSB * (s + PD), (s + PD) % kNBuf);
+    compute(s % kNBuf, b0 + kSB * s);
   }
 
 #pragma unroll
