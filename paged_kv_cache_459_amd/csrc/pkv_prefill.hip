@@ -44,6 +44,12 @@ constexpr float kNegInf = -__builtin_inff();
 // Running max before any visible token: finite, so 2^(x - m) needs no guard for rows that
 // have seen nothing yet (x = -inf gives 0, and the first visible scores always rescale).
 constexpr float kMaxInit = -3.0e38f;
+// Lazy rescaling: a row's running max (base-2 units) is raised, and its sums rescaled, only
+// when a stage's scores exceed it by more than this, so most stages skip the rescale.
+// Probabilities then stay <= 2^8 (exact range for f16/bf16, far from fp32 overflow in the
+// sums); the row sum adds the probabilities as rounded for the p.v contraction, so numerator
+// and denominator weigh every token alike whatever the running max.
+constexpr float kLazy = 8.f;
 
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -144,6 +150,14 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
+
+// LDS placement swizzles (see the staging comment in the kernel).
+__device__ __forceinline__ int kpos(int t, int blk) { return t ^ (((t >> 3) & 1) << 2) ^ (blk << 3); }
+// the token at slot position pos (inverse of kpos: bit 3 of pos is bit 3 of t ^ blk)
+__device__ __forceinline__ int ktok(int pos, int blk) {
+  return pos ^ (blk << 3) ^ ((((pos >> 3) & 1) ^ blk) << 2);
+}
+__device__ __forceinline__ int vswz(int d) { return ((d >> 2) ^ (d >> 3)) & 1; }
 
 // Waits until at most n of this wave's vector-memory operations are outstanding (they
 // complete in order), n a multiple of the per-stage count; only the values used here.
@@ -246,9 +260,11 @@ attn_prefill_kernel(const StreamParams p) {
   // Staging: the stage's blocks a (t) and b (t + 1) go straight from memory to LDS, each
   // wave-wide load moving one 1 KB piece of a tile; the lanes' source addresses place the
   // 16-byte chunks (bank-swizzled for the reads below):
-  //   K tile: slot 16c + pos holds chunk c (dims 8c .. 8c+7) of token t, pos = t for block a
-  //           and (t + 4) & 15 for block b;
-  //   V tile: slot 2d + (h ^ ((d >> 3) & 1)) holds tokens 8h .. 8h+7 of dim d.
+  //   K tile: slot 16c + pos holds chunk c (dims 8c .. 8c+7) of token t,
+  //           pos = t ^ (4 * bit 3 of t) ^ (8 * block), block 0 for a, 1 for b;
+  //   V tile: slot 2d + (h ^ bit 2 of d ^ bit 3 of d) holds tokens 8h .. 8h+7 of dim d.
+  // Each group of 8 (and of 16) lanes of the reads below then covers distinct 16-byte columns
+  // of the LDS banks.
   // An entry naming no block of the pool (or a block past the unit) is read from block 0 and
   // masked when computed.
   auto issue = [&](int t, int buf) {
@@ -262,9 +278,9 @@ attn_prefill_kernel(const StreamParams p) {
       int src;
       if (kv == 0) {
         const int cc = sigma >> 4, pos = sigma & 15;
-        src = 256 * cc + 16 * (sb == 0 ? pos : ((pos - 4) & 15));
+        src = 256 * cc + 16 * ktok(pos, sb);
       } else {
-        const int d = sigma >> 1, h = (sigma & 1) ^ ((d >> 3) & 1);
+        const int d = sigma >> 1, h = (sigma & 1) ^ vswz(d);
         src = 32 * d + 16 * h;
       }
       const char* base = static_cast<const char*>(kv ? p.v_cache : p.k_cache) +
@@ -291,10 +307,10 @@ attn_prefill_kernel(const StreamParams p) {
   // of contraction 1 is token (m & 3) + 8 ((m >> 2) & 1) of block m >> 3; contraction 2 adds 4.
   const int rm = lane & 15, kg = lane >> 4;
   const int rblk = rm >> 3, rt1 = (rm & 3) + 8 * ((rm >> 2) & 1), rt2 = rt1 + 4;
-  const int k_off1 = rblk * TILE + 256 * kg + 16 * (rblk ? (rt1 + 4) & 15 : rt1);
-  const int k_off2 = rblk * TILE + 256 * kg + 16 * (rblk ? (rt2 + 4) & 15 : rt2);
+  const int k_off1 = rblk * TILE + 256 * kg + 16 * kpos(rt1, rblk);
+  const int k_off2 = rblk * TILE + 256 * kg + 16 * kpos(rt2, rblk);
   // p.v: lane (dim 16j + hq, g) takes tokens 8 (g & 1) .. +7 of block g >> 1 in one read
-  const int v_off = kSB * TILE + (g >> 1) * TILE + 32 * hq + 16 * ((g & 1) ^ ((hq >> 3) & 1));
+  const int v_off = kSB * TILE + (g >> 1) * TILE + 32 * hq + 16 * ((g & 1) ^ vswz(hq));
   const int tok_lane = kBlockSize * (g >> 1) + 8 * (g & 1);  // first token of this lane's 8
 
   auto compute = [&](int buf, int t) {
@@ -357,12 +373,9 @@ attn_prefill_kernel(const StreamParams p) {
       const float v = fmaxf(fmaxf(fmaxf(x[k][0], x[k][1]), fmaxf(x[k][2], x[k][3])),
                             fmaxf(fmaxf(x[k][4], x[k][5]), fmaxf(x[k][6], x[k][7])));
       bm[k] = row_max4(v) * c;  // base-2 units (c > 0 keeps the order)
-      grow = grow || bm[k] > m[k];
+      grow = grow || bm[k] > m[k] + kLazy;
     }
-    // Exact running max (the largest probability of a row is exactly 1, so its token's weight
-    // carries no rounding in the 16-bit p.v operand); the rescale is skipped, wave-uniformly,
-    // when no row's max rose.
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform
 #pragma unroll
       for (int k = 0; k < RT; ++k) {
         const float mn = fmaxf(m[k], bm[k]);
