@@ -53,7 +53,8 @@ bool plan_check(const int32_t* p, size_t n, int32_t B, int32_t max_blocks, int32
 // pos sees vis = pos + 1 tokens. Units cover (sequence, tile of up to tile_rows consecutive
 // rows, chunk of the blocks the tile's last row sees); a tile whose blocks fit one chunk has
 // one unit, marked direct (cell_base -1: its rows are written straight to the output), the
-// others give each row one piece per chunk it sees, merged afterwards. Layout: header (magic
+// others give each row one piece per chunk it sees, merged afterwards. Units are ordered
+// longest first (stable), cells handed out in that order. Layout: header (magic
 // kPrefillMagic, T, H, GS, U, M, L, cells, chunk, S, tile_rows), skip[T] (1: the row merges),
 // vis[T], sh_ptr[T+1], units[U][6], members[M] (rows), sh_list[L].
 void prefill_plan_build(const int32_t* query_start, const int32_t* lens, int32_t S, int32_t H,

@@ -237,6 +237,27 @@ void prefill_plan_build(const int32_t* qs, const int32_t* lens, int32_t S, int32
         for (int32_t k = 0; k < cnt; ++k) skip[q0 + a + k] = 1;
     }
   }
+  // Longest units first (stable: a row's chunks keep their order): work-groups are dispatched
+  // in unit order, so the last ones to start, which set the launch's tail, are the short
+  // ones. Cells are then handed out in that order.
+  {
+    const size_t U = units.size() / kUnitInts;
+    std::vector<int32_t> order(U);
+    for (size_t u = 0; u < U; ++u) order[u] = static_cast<int32_t>(u);
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+      return units[a * kUnitInts + 2] - units[a * kUnitInts + 1] >
+             units[b * kUnitInts + 2] - units[b * kUnitInts + 1];
+    });
+    std::vector<int32_t> sorted;
+    sorted.reserve(units.size());
+    int32_t next = 0;
+    for (int32_t u : order) {
+      const int32_t* e = &units[static_cast<size_t>(u) * kUnitInts];
+      sorted.insert(sorted.end(), {e[0], e[1], e[2], e[3], e[4], e[5] < 0 ? -1 : next});
+      if (e[5] >= 0) next += e[4] * H;
+    }
+    units.swap(sorted);
+  }
   // each merged row's piece cells, in unit order (CSR); a chunk wholly past a row's position
   // gives it no piece
   std::vector<int32_t> ptr(T + 1, 0);

@@ -267,25 +267,33 @@ attn_prefill_kernel(const StreamParams p) {
   // of the LDS banks.
   // An entry naming no block of the pool (or a block past the unit) is read from block 0 and
   // masked when computed.
+  // each lane's source offset inside its tile, per piece (the same for every stage)
+  int src_off[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int piece = w + kPW * i;
+    const int tile = piece / PPT, sigma = (piece % PPT) * 64 + lane;
+    const int kv = tile / kSB, sb = tile % kSB;
+    if (kv == 0) {
+      src_off[i] = 256 * (sigma >> 4) + 16 * ktok(sigma & 15, sb);
+    } else {
+      const int d = sigma >> 1;
+      src_off[i] = 32 * d + 16 * ((sigma & 1) ^ vswz(d));
+    }
+  }
+  const char* k_head = static_cast<const char*>(p.k_cache) + static_cast<size_t>(kvh) * TILE;
+  const char* v_head = static_cast<const char*>(p.v_cache) + static_cast<size_t>(kvh) * TILE;
   auto issue = [&](int t, int buf) {
     const int id0 = uniform(max(s_ids[t - b0], 0));
     const int id1 = uniform(t + 1 < b1 ? max(s_ids[t + 1 - b0], 0) : 0);
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int piece = w + kPW * i;  // wave-uniform
-      const int tile = piece / PPT, sigma = (piece % PPT) * 64 + lane;
+      const int tile = piece / PPT;
       const int kv = tile / kSB, sb = tile % kSB;
-      int src;
-      if (kv == 0) {
-        const int cc = sigma >> 4, pos = sigma & 15;
-        src = 256 * cc + 16 * ktok(pos, sb);
-      } else {
-        const int d = sigma >> 1, h = (sigma & 1) ^ vswz(d);
-        src = 32 * d + 16 * h;
-      }
-      const char* base = static_cast<const char*>(kv ? p.v_cache : p.k_cache) +
-                         static_cast<size_t>(sb == 0 ? id0 : id1) * blk_stride +
-                         static_cast<size_t>(kvh) * TILE;
+      const char* base = (kv ? v_head : k_head) + static_cast<size_t>(sb == 0 ? id0 : id1) *
+                                                       blk_stride;
+      const int src = src_off[i];
       const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
           (__attribute__((address_space(3))) char*)(&s_kv[buf][piece * 1024])));
       load_lds16(base + src, static_cast<uint32_t>(uniform(static_cast<int>(lds))));
