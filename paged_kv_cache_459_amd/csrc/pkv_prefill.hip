@@ -107,16 +107,21 @@ struct Mma<2> {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Max of scores (no NaN reaches it: masked scores are replaced by -inf first). The
+// NaN-propagating maximum maps to gfx950's v_maximum3_f32 and needs no quieting of its inputs,
+// which fmaxf does in IEEE mode (two extra instructions per comparison).
+__device__ __forceinline__ float smax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Max over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes holding one row's scores),
 // with the gfx950 half-swaps: each returns the pair (own half copied, other half copied), so
 // the max of the pair is the max over the two halves.
 __device__ __forceinline__ float row_max4(float v) {
   const unsigned u = __builtin_bit_cast(unsigned, v);
   const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  const float m1 = fmaxf(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
+  const float m1 = smax(__builtin_bit_cast(float, a[0]), __builtin_bit_cast(float, a[1]));
   const unsigned u1 = __builtin_bit_cast(unsigned, m1);
   const auto b = __builtin_amdgcn_permlane16_swap(u1, u1, false, false);
-  return fmaxf(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
+  return smax(__builtin_bit_cast(float, b[0]), __builtin_bit_cast(float, b[1]));
 }
 
 // Zeroes the 16-bit tokens t0 + j (j < 8) of a V chunk with t0 + j >= valid.
@@ -378,9 +383,10 @@ attn_prefill_kernel(const StreamParams p) {
     bool grow = false;
 #pragma unroll
     for (int k = 0; k < RT; ++k) {
-      const float v = fmaxf(fmaxf(fmaxf(x[k][0], x[k][1]), fmaxf(x[k][2], x[k][3])),
-                            fmaxf(fmaxf(x[k][4], x[k][5]), fmaxf(x[k][6], x[k][7])));
-      bm[k] = row_max4(v) * c;  // base-2 units (c > 0 keeps the order)
+      const float v = row_max4(smax(smax(smax(x[k][0], x[k][1]), smax(x[k][2], x[k][3])),
+                                    smax(smax(x[k][4], x[k][5]), smax(x[k][6], x[k][7]))));
+      // base-2 units (c >= 0 keeps the order); nothing visible stays -inf even for c = 0
+      bm[k] = v == kNegInf ? kNegInf : v * c;
       grow = grow || bm[k] > m[k] + kLazy;
     }
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform
