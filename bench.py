@@ -92,18 +92,23 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_digest():
+def kernel_source_digest(workload="llama2_7b"):
+    """Digest of the kernel sources a workload's dominant kernel is built from (a change
+    there makes its committed counter figures stale)."""
+    files = (("pkv_prefill.hip", "pkv_kernels.h") if workload == "prefill"
+             else ("pkv_attn.hip", "pkv_kernels.h"))
     h = hashlib.sha256()
-    for f in ("pkv_attn.hip", "pkv_kernels.h"):
+    for f in files:
         with open(os.path.join(ROOT, "paged_kv_cache_459_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload, digest):
-    """HBM traffic per stream-kernel launch from the committed counter summary, if it was
-    taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"attn_stream_{workload}_traffic.json")
+    """HBM traffic per launch of the workload's dominant kernel from the committed counter
+    summary, if it was taken on the current kernel source; else None."""
+    name = "attn_prefill" if workload == "prefill" else f"attn_stream_{workload}"
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
@@ -598,7 +603,7 @@ def batching_main(args, torch, pkv, W):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.workload, kernel_source_digest()),
+            "traffic": measured_traffic(args.workload, kernel_source_digest(args.workload)),
             "kernel": f"attention stream pass ({['', 'vector', 'matrix-core'][loop.kernel]} "
                       f"kernel)",
             "algorithmic_bytes_per_launch": int(np.mean(algo)),
@@ -725,7 +730,7 @@ def prefill_main(args, torch, pkv, W):
             "peak": MFMA_PEAK_TFLOPS[dtype],
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_PEAK_TFLOPS[dtype], 4),
-            "traffic": measured_traffic("prefill", kernel_source_digest()),
+            "traffic": measured_traffic("prefill", kernel_source_digest("prefill")),
             "kernel": "prefill attention pass (attn_prefill_kernel)",
             "algorithmic_flops_per_launch": flops,
         },
@@ -833,7 +838,7 @@ def main():
     value = sum(kv) / wall / 1e9
     achieved = sum(algo) / (sum(part_ms) / 1e3) / 1e9
     attn_ms = [a + b + c for a, b, c in zip(shared_ms, part_ms, merge_ms)]
-    digest = kernel_source_digest()
+    digest = kernel_source_digest(args.workload)
     traffic = measured_traffic(args.workload, digest)
 
     if args.copy_calibration:  # a plain copy of known size, for the counter runs
