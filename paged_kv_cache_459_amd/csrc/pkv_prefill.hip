@@ -20,10 +20,11 @@
 // and token 4g + i - 4 of the second: exactly the tokens whose scores the lane already holds
 // from the S^T tiles, so P needs no shuffle. Online softmax per row, in base-2 units.
 //
-// Masking: a row sees tokens < its position + 1 (row_vis); scores of other tokens are
-// selected to -inf. V slots at or past the work-group's last visible token are zeroed when
-// staged (unused slots may hold anything; a zero probability times NaN would still be NaN),
-// and blocks whose table entry names no block of the pool are staged as zeros and masked.
+// Masking: a row sees tokens < its position + 1 (row_vis); other tokens get probability 0
+// (selected, not multiplied). K and V slots at or past the work-group's last visible token,
+// and blocks whose table entry names no block of the pool, are zeroed in LDS once staged
+// (unused slots may hold anything; a zero probability times NaN would still be NaN), so every
+// score is finite and the row max may include tokens a row does not see.
 //
 // A unit holding all of its rows' blocks writes their outputs directly; a unit that is one
 // chunk of a longer range (more than kPrefillMaxBlocks blocks) leaves (m, l, o) pieces that
@@ -271,7 +272,7 @@ attn_prefill_kernel(const StreamParams p) {
   // Each group of 8 (and of 16) lanes of the reads below then covers distinct 16-byte columns
   // of the LDS banks.
   // An entry naming no block of the pool (or a block past the unit) is read from block 0 and
-  // masked when computed.
+  // zeroed by the fix-up below.
   // each lane's source offset inside its tile, per piece (the same for every stage)
   int src_off[NCH];
 #pragma unroll
@@ -302,6 +303,26 @@ attn_prefill_kernel(const StreamParams p) {
       const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
           (__attribute__((address_space(3))) char*)(&s_kv[buf][piece * 1024])));
       load_lds16(base + src, static_cast<uint32_t>(uniform(static_cast<int>(lds))));
+    }
+  };
+
+  // Zeroes, in the staged copy of stage t, the K and V slots of tokens at or past vmax and of
+  // entries naming no block (-1).
+  auto fixup = [&](int buf, int t, int ida, int idb) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int piece = w + kPW * i;
+      const int tile = piece / PPT, sigma = (piece % PPT) * 64 + lane;
+      const int kv = tile / kSB, sb = tile % kSB;
+      const int lim = (sb == 0 ? ida : idb) < 0 ? 0 : vmax - kBlockSize * (t + sb);
+      if (lim >= kBlockSize) continue;
+      uint4* slot = reinterpret_cast<uint4*>(&s_kv[buf][piece * 1024 + 16 * lane]);
+      if (kv == 0) {
+        if (ktok(sigma & 15, sb) >= lim) *slot = make_uint4(0, 0, 0, 0);
+      } else {
+        const int d = sigma >> 1;
+        *slot = keep_tokens(*slot, 8 * ((sigma & 1) ^ vswz(d)), lim);
+      }
     }
   };
 
@@ -342,12 +363,6 @@ attn_prefill_kernel(const StreamParams p) {
     // this lane's 8 tokens: valid (a block of the pool) and their first logical index
     const bool lane_blk_ok = (g >> 1) == 0 ? ida >= 0 : idb >= 0;
     const int tok0 = kBlockSize * t + tok_lane;
-    if (!(ida >= 0 && idb >= 0 && kBlockSize * (t + 2) <= vmax)) {
-      // V slots at or past every row's last visible token, or of no block: zero
-      const int nv = lane_blk_ok ? min(8, max(0, vmax - tok0)) : 0;
-#pragma unroll
-      for (int j = 0; j < VT; ++j) vf[j] = keep_tokens(vf[j], 0, nv);
-    }
     float4_t sa[RT], sbv[RT];
 #pragma unroll
     for (int k = 0; k < RT; ++k) {
@@ -369,24 +384,17 @@ attn_prefill_kernel(const StreamParams p) {
         x[k][i] = sa[k][i];
         x[k][4 + i] = sbv[k][i];
       }
-    // every row of the wave sees all 32 tokens: no masking
+    // Every score is finite here (slots past the work-group's last visible token, and blocks
+    // outside the pool, were zeroed in LDS), so the row max may include tokens a row does not
+    // see: it only keeps the exponentials in range. Invisible tokens get probability 0 below.
     const bool full = ida >= 0 && idb >= 0 && kBlockSize * (t + 2) <= wmin;
-    if (!full) {
-#pragma unroll
-      for (int k = 0; k < RT; ++k) {
-        const int nr = lane_blk_ok ? min(8, max(0, n_row[k] - tok0)) : 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[k][i] = i < nr ? x[k][i] : kNegInf;
-      }
-    }
     float bm[RT];
     bool grow = false;
 #pragma unroll
     for (int k = 0; k < RT; ++k) {
       const float v = row_max4(smax(smax(smax(x[k][0], x[k][1]), smax(x[k][2], x[k][3])),
                                     smax(smax(x[k][4], x[k][5]), smax(x[k][6], x[k][7]))));
-      // base-2 units (c >= 0 keeps the order); nothing visible stays -inf even for c = 0
-      bm[k] = v == kNegInf ? kNegInf : v * c;
+      bm[k] = v * c;  // base-2 units (c >= 0 keeps the order)
       grow = grow || bm[k] > m[k] + kLazy;
     }
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform
@@ -405,9 +413,10 @@ attn_prefill_kernel(const StreamParams p) {
       float pr[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(x[k][i], c, -m[k]));
-      if (!full) {  // masked tokens: probability 0 whatever the scale (-inf * 0 would be NaN)
+      if (!full) {  // tokens past the row's position (or of no block): probability 0
+        const int nr = lane_blk_ok ? min(8, max(0, n_row[k] - tok0)) : 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pr[i] = x[k][i] == kNegInf ? 0.f : pr[i];
+        for (int i = 0; i < 8; ++i) pr[i] = i < nr ? pr[i] : 0.f;
       }
       const uint4 pb = make_uint4(MM::pack2(pr[0], pr[1]), MM::pack2(pr[2], pr[3]),
                                   MM::pack2(pr[4], pr[5]), MM::pack2(pr[6], pr[7]));
@@ -426,10 +435,20 @@ attn_prefill_kernel(const StreamParams p) {
   constexpr int PD = kNBuf - 1;
   for (int q = 0; q < PD && q < nst; ++q) issue(b0 + kSB * q, q);
   for (int s = 0; s < nst; ++s) {
+    const int t = b0 + kSB * s;
     wait_stages<NCH>(min(PD - 1, nst - 1 - s));
     lds_barrier();
+    // A stage holding slots at or past the work-group's last visible token (its last), a
+    // block outside the pool or no second block: zero those K and V slots in LDS once, for
+    // every wave (unused slots may hold anything, NaN included).
+    const int ida = s_ids[t - b0];
+    const int idb = t + 1 < b1 ? s_ids[t + 1 - b0] : -1;
+    if (!(ida >= 0 && idb >= 0 && kBlockSize * (t + 2) <= vmax)) {
+      fixup(s % kNBuf, t, ida, idb);
+      lds_barrier();
+    }
     if (s + PD < nst) issue(b0 + kSB * (s + PD), (s + PD) % kNBuf);
-    compute(s % kNBuf, b0 + kSB * s);
+    compute(s % kNBuf, t);
   }
 
 #pragma unroll
