@@ -12,8 +12,9 @@
 // of the kv head's group), 16*RT per wave as RT row tiles of 16. The unit's blocks stream
 // through LDS two at a time (double-buffered): each K/V tile is read from memory once per
 // work-group and from LDS once per wave, and every fragment read from LDS feeds the RT row
-// tiles' contractions; each stage's loads are issued two stages ahead. Both contractions run
-// on 16x16x32 matrix-core instructions:
+// tiles' contractions; loads run three stages ahead, and each wave issues the next stage's
+// q . k before the current stage's softmax. Both contractions run on 16x16x32 matrix-core
+// instructions:
 //   S^T (16 tokens x 16 rows) = K (16 x hd) . Q^T, per block;
 //   O^T (16 dims x 16 rows) += V^T (16 dims x 32 tokens) . P^T, over the stage's two blocks,
 // with the contraction index k = 8g + i standing for token 4g + i of the first block (i < 4)
@@ -347,23 +348,15 @@ attn_prefill_kernel(const StreamParams p) {
   const int v_off = kSB * TILE + (g >> 1) * TILE + 32 * hq + 16 * ((g & 1) ^ vswz(hq));
   const int tok_lane = kBlockSize * (g >> 1) + 8 * (g & 1);  // first token of this lane's 8
 
-  auto compute = [&](int buf, int t) {
-    if (kBlockSize * t >= wmax) return;  // nothing of the stage is visible to this wave
-    const int ida = s_ids[t - b0];
-    const int idb = t + 1 < b1 ? s_ids[t + 1 - b0] : -1;
+  // q . k of one stage (both blocks, every row tile) into (sa, sbv)
+  auto qk = [&](int buf, float4_t (&sa)[RT], float4_t (&sbv)[RT]) {
     const char* st = s_kv[buf];
-    uint4 kf1[KS], kf2[KS], vf[VT];
+    uint4 kf1[KS], kf2[KS];
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) {
       kf1[s2] = *reinterpret_cast<const uint4*>(st + k_off1 + 1024 * s2);
       kf2[s2] = *reinterpret_cast<const uint4*>(st + k_off2 + 1024 * s2);
     }
-#pragma unroll
-    for (int j = 0; j < VT; ++j) vf[j] = *reinterpret_cast<const uint4*>(st + v_off + 512 * j);
-    // this lane's 8 tokens: valid (a block of the pool) and their first logical index
-    const bool lane_blk_ok = (g >> 1) == 0 ? ida >= 0 : idb >= 0;
-    const int tok0 = kBlockSize * t + tok_lane;
-    float4_t sa[RT], sbv[RT];
 #pragma unroll
     for (int k = 0; k < RT; ++k) {
       sa[k] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -376,6 +369,20 @@ attn_prefill_kernel(const StreamParams p) {
         sa[k] = MM::mul(kf1[s2], qb[k][s2], sa[k]);
         sbv[k] = MM::mul(kf2[s2], qb[k][s2], sbv[k]);
       }
+  };
+
+  // Softmax and p . v of stage t from its scores (sa, sbv).
+  auto finish = [&](int buf, int t, const float4_t (&sa)[RT], const float4_t (&sbv)[RT]) {
+    if (kBlockSize * t >= wmax) return;  // nothing of the stage is visible to this wave
+    const int ida = s_ids[t - b0];
+    const int idb = t + 1 < b1 ? s_ids[t + 1 - b0] : -1;
+    const char* st = s_kv[buf];
+    uint4 vf[VT];
+#pragma unroll
+    for (int j = 0; j < VT; ++j) vf[j] = *reinterpret_cast<const uint4*>(st + v_off + 512 * j);
+    // this lane's 8 tokens: valid (a block of the pool) and their first logical index
+    const bool lane_blk_ok = (g >> 1) == 0 ? ida >= 0 : idb >= 0;
+    const int tok0 = kBlockSize * t + tok_lane;
     float x[RT][8];
 #pragma unroll
     for (int k = 0; k < RT; ++k)
@@ -428,27 +435,48 @@ attn_prefill_kernel(const StreamParams p) {
     }
   };
 
-  // kNBuf LDS buffers, loads issued kNBuf - 1 stages ahead. Stage s waits for its own loads
-  // (the later stages' may stay in flight), then the barrier publishes them and tells that
-  // every wave is done with stage s - 1, whose buffer the loads of stage s + kNBuf - 1 reuse.
-  const int nst = (nblk + kSB - 1) / kSB;
-  constexpr int PD = kNBuf - 1;
-  for (int q = 0; q < PD && q < nst; ++q) issue(b0 + kSB * q, q);
-  for (int s = 0; s < nst; ++s) {
+  // Stage s lands: this wave's loads of it are done (at most `ahead` later stages in flight),
+  // the barrier publishes every wave's, and a stage holding slots at or past the work-group's
+  // last visible token (its last), a block outside the pool or no second block has those K
+  // and V slots zeroed in LDS once, for every wave (unused slots may hold anything, NaN too).
+  auto land = [&](int s, int ahead) {
     const int t = b0 + kSB * s;
-    wait_stages<NCH>(min(PD - 1, nst - 1 - s));
+    wait_stages<NCH>(ahead);
     lds_barrier();
-    // A stage holding slots at or past the work-group's last visible token (its last), a
-    // block outside the pool or no second block: zero those K and V slots in LDS once, for
-    // every wave (unused slots may hold anything, NaN included).
     const int ida = s_ids[t - b0];
     const int idb = t + 1 < b1 ? s_ids[t + 1 - b0] : -1;
     if (!(ida >= 0 && idb >= 0 && kBlockSize * (t + 2) <= vmax)) {
       fixup(s % kNBuf, t, ida, idb);
       lds_barrier();
     }
-    if (s + PD < nst) issue(b0 + kSB * (s + PD), (s + PD) % kNBuf);
-    compute(s % kNBuf, t);
+  };
+
+  // Pipeline. Loads run kNBuf - 1 stages ahead into kNBuf LDS buffers. Within a wave, the
+  // q . k contractions of stage s + 1 are issued before the softmax of stage s, so the matrix
+  // cores work while the VALU does; stage s + 1 therefore lands (and the loads of stage
+  // s + kNBuf - 1 go into the buffer of stage s - 1, which every wave finished before that
+  // landing's barrier) before stage s is finished.
+  const int nst = (nblk + kSB - 1) / kSB;
+  constexpr int PD = kNBuf - 1;
+  for (int q = 0; q < PD && q < nst; ++q) issue(b0 + kSB * q, q);
+  land(0, min(PD - 1, nst - 1));
+  float4_t sa0[RT], sb0[RT], sa1[RT], sb1[RT];
+  if (kBlockSize * b0 < wmax) qk(0, sa0, sb0);
+  auto step = [&](int s, const float4_t (&ca)[RT], const float4_t (&cb)[RT], float4_t (&na)[RT],
+                  float4_t (&nb)[RT]) {
+    const int t = b0 + kSB * s;
+    if (s + 1 < nst) {
+      land(s + 1, min(PD - 2, nst - 2 - s));
+      if (s + PD < nst) issue(b0 + kSB * (s + PD), (s + PD) % kNBuf);
+      if (kBlockSize * (t + kSB) < wmax) qk((s + 1) % kNBuf, na, nb);
+      __builtin_amdgcn_sched_barrier(0);  // keep those contractions ahead of the softmax
+    }
+    finish(s % kNBuf, t, ca, cb);
+  };
+  for (int s = 0; s < nst; s += 2) {
+    step(s, sa0, sb0, sa1, sb1);
+    if (s + 1 >= nst) break;
+    step(s + 1, sa1, sb1, sa0, sb0);
   }
 
 #pragma unroll
