@@ -826,9 +826,7 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_matrix_kernel(const StreamParams p)
 // Waves map to (kv head, unit) unit-fastest, and work-groups are laid XCD-contiguously, so the
 // member tiles of one chunk run side by side on one XCD. Each row's (m, l, o) goes to its cell:
 // shared_base + cell_base + member*H + head slot, row (q head % GS), in the stream pass's
-// layout. The same kernel serves prefill: rows are then new prompt tokens (member = q row),
-// each seeing its position + 1 tokens (row_vis), the unit's blocks from its sequence's table;
-// a unit with cell_base -1 holds all of its rows' tokens and writes their outputs directly.
+// layout.
 template <int DT, int HD>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(3))) attn_shared_kernel(const StreamParams p, int H, int GS) {
@@ -846,7 +844,7 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_shared_kernel(const StreamParams p,
   const int32_t* e = p.units + static_cast<size_t>(u) * kUnitInts;
   const int ref = uniform(e[0]), b0 = uniform(max(e[1], 0)), b1 = uniform(min(e[2], p.max_blocks));
   const int moff = uniform(e[3]), mcnt = uniform(e[4]), cbase = uniform(e[5]);
-  if (ref < 0 || ref >= p.table_rows || b0 >= b1) return;
+  if (ref < 0 || ref >= p.B || b0 >= b1) return;
 
   const int lane = threadIdx.x & 63;
   const int G = p.Hq / p.Hkv;
@@ -897,10 +895,7 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_shared_kernel(const StreamParams p,
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) qb[s2] = make_uint4(0, 0, 0, 0);
   }
-  // visible tokens: the row's sequence length (decode) or its position + 1 (prefill)
-  const int n_row = !row_ok ? 0
-                    : p.row_vis != nullptr ? min(max(p.row_vis[seq], 0), p.max_ctx)
-                                           : clamp_len(p, seq);
+  const int n_row = row_ok ? clamp_len(p, seq) : 0;
   // q settled here: a first use inside the loop would put its wait (for every load issued
   // before it, the tiles included) at the top of each iteration
 #pragma unroll
@@ -978,18 +973,9 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_shared_kernel(const StreamParams p,
   l += __shfl_xor(l, 32);
   if (!row_ok) return;
   const int qh = kvh * G + jq;
-  if (cbase < 0) {  // a direct unit (prefill): the unit saw all of its rows' tokens
-    const size_t orow = (static_cast<size_t>(seq) * p.Hq + qh) * HD;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-    for (int j = 0; j < VT; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Elem<DT>::put(p.out, orow + 16 * j + 4 * g + i, o[j][i] * inv);
-    return;
-  }
   const int slot = qh / GS, nr = qh - slot * GS;
   const int rel = cbase + mk * H + slot;
-  if (rel >= p.shared_cells) return;
+  if (rel < 0 || rel >= p.shared_cells) return;
   const size_t cell = (static_cast<size_t>(p.shared_base) + static_cast<size_t>(rel)) * GS + nr;
 #pragma unroll
   for (int j = 0; j < VT; ++j)

@@ -109,7 +109,7 @@ struct StreamParams {
   const int32_t* members;  // q rows of the units' members (decode: sequences)
   int32_t num_units, shared_cells;
   int32_t shared_base;     // first cell of the shared pieces (decode: 2W + B*H)
-  int32_t table_rows;      // rows of block_tables (decode: B)
+  int32_t table_rows;      // rows of block_tables (decode: B; prefill: sequences)
   // Prefill (null for decode): visible tokens of each row (its position + 1); the rows are
   // then new prompt tokens, q and out are [T][Hq][hd], and there is no stream pass (ws_seg
   // null for the merge).
