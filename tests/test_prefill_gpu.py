@@ -142,6 +142,29 @@ def test_shared_prefix_blocks(dtype, hq, hkv, hd):
     G.assert_close(got, oracle(p, q, qs, G.scale_for(hd)), dtype, "shared prefix")
 
 
+def _sampled_check(lens, qlens, tables, qs, k_cache, v_cache, q, out, rows, *, hkv, hd, dtype,
+                   scale, what):
+    """Oracle of the listed (sequence, q row) pairs, each as a one-token prefill of its own
+    visible prefix (the same definition: the row at position p sees tokens 0..p), from exact
+    host copies of just the blocks they see."""
+    vis = [int(lens[s]) - (int(qs[s + 1]) - t) + 1 for s, t in rows]
+    used = sorted({int(x) for (s, _), v in zip(rows, vis) for x in tables[s][:-(-v // 16)]})
+    remap = {b: i for i, b in enumerate(used)}
+    idx = torch.tensor(used, dtype=torch.long, device="cuda")
+    kc = W.to_storage_numpy(k_cache.index_select(0, idx), dtype).reshape(-1)
+    vc = W.to_storage_numpy(v_cache.index_select(0, idx), dtype).reshape(-1)
+    smb = max(-(-v // 16) for v in vis)
+    st = np.full((len(rows), smb), -1, np.int32)
+    for i, ((s, _), v) in enumerate(zip(rows, vis)):
+        st[i, :-(-v // 16)] = [remap[int(x)] for x in tables[s][:-(-v // 16)]]
+    qr = W.to_storage_numpy(q[[t for _, t in rows]], dtype)
+    want = OA.prefill_attention(qr, kc, vc, st, np.array(vis, np.int32),
+                                np.arange(len(rows) + 1, dtype=np.int32), scale=scale,
+                                hkv=hkv, hd=hd, bs=16, dtype=dtype)
+    got = G.gpu_f64(out[[t for _, t in rows]], dtype)
+    G.assert_close(got, want, dtype, what)
+
+
 def test_full_size_chunked_prefill_sampled():
     """The chunked-prefill workload (16 sequences, 512 new tokens after U[0, 1536] cached,
     MHA 32 x 128, f16) at full size; sampled rows against the oracle, each as a one-token
@@ -175,19 +198,42 @@ def test_full_size_chunked_prefill_sampled():
         a, b = int(qs[s]), int(qs[s + 1])
         rows += [(int(s), a), (int(s), b - 1)] + [(int(s), int(t)) for t in
                                                    rng.integers(a, b, size=2)]
-    vis = [int(lens[s]) - (int(qs[s + 1]) - t) + 1 for s, t in rows]
-    used = sorted({int(x) for (s, _), v in zip(rows, vis) for x in tables[s][:-(-v // 16)]})
-    remap = {b: i for i, b in enumerate(used)}
-    idx = torch.tensor(used, dtype=torch.long, device="cuda")
-    kc = W.to_storage_numpy(k_cache.index_select(0, idx), "f16").reshape(-1)
-    vc = W.to_storage_numpy(v_cache.index_select(0, idx), "f16").reshape(-1)
-    smb = max(-(-v // 16) for v in vis)
-    st = np.full((len(rows), smb), -1, np.int32)
-    for i, ((s, _), v) in enumerate(zip(rows, vis)):
-        st[i, :-(-v // 16)] = [remap[int(x)] for x in tables[s][:-(-v // 16)]]
-    qr = W.to_storage_numpy(q[[t for _, t in rows]], "f16")
-    want = OA.prefill_attention(qr, kc, vc, st, np.array(vis, np.int32),
-                                np.arange(len(rows) + 1, dtype=np.int32), scale=scale,
-                                hkv=shape.Hkv, hd=shape.hd, bs=16, dtype="f16")
-    got = G.gpu_f64(out[[t for _, t in rows]], "f16")
-    G.assert_close(got, want, "f16", "full-size prefill, sampled rows")
+    _sampled_check(lens, qlens, tables, qs, k_cache, v_cache, q, out, rows, hkv=shape.Hkv,
+                   hd=shape.hd, dtype="f16", scale=scale, what="full-size prefill, sampled rows")
+
+
+def test_long_contexts_split_over_chunks_sampled():
+    """Maximum sizes: prompts chunked at the end of 32768- and 20000-token contexts (rows see
+    up to four 512-block chunks, merged), next to a whole 4096-token prompt, GQA 32 q / 8 kv
+    x 128, bf16; sampled rows against the oracle."""
+    import paged_kv_cache_459_amd as m
+    print("[prefill long contexts] 32768 / 20000 / 4096, GQA 32/8 bf16", flush=True)
+    hq, hkv, hd = 32, 8, 128
+    rng = np.random.default_rng(1600)
+    lens = np.array([32768, 20000, 4096], np.int32)
+    qlens = np.array([300, 64, 4096], np.int32)
+    nb = W.pool_blocks(lens)
+    tables = W.place_sequences(lens, rng.permutation(nb).astype(np.int32))
+    mb = tables.shape[1]
+    qs = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    T = int(qs[-1])
+    k_cache, v_cache = m.alloc_caches(nb, hkv, hd, torch.bfloat16)
+    k_cache.view(-1).copy_(W.device_normal((k_cache.numel(),), "bf16", 1601))
+    v_cache.view(-1).copy_(W.device_normal((v_cache.numel(),), "bf16", 1602))
+    q = W.device_normal((T, hq, hd), "bf16", 1603)
+    plan = m.pkv_prefill_plan(qs, lens, num_q_heads=hq, num_kv_heads=hkv, max_blocks=mb,
+                              max_context_len=16 * mb, dtype=torch.bfloat16)
+    assert int(plan[7]) > 0  # split rows: pieces and merge
+    out = torch.full_like(q, float("nan"))
+    scale = G.scale_for(hd)
+    m.pkv_prefill_attn(q, k_cache, v_cache, torch.from_numpy(tables).cuda(), plan,
+                       torch.from_numpy(plan.copy()).cuda(), num_kv_heads=hkv, scale=scale,
+                       max_context_len=16 * mb, out=out)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    rows = []
+    for s in range(3):
+        a, b = int(qs[s]), int(qs[s + 1])
+        rows += [(s, a), (s, b - 1), (s, int(rng.integers(a, b)))]
+    _sampled_check(lens, qlens, tables, qs, k_cache, v_cache, q, out, rows, hkv=hkv, hd=hd,
+                   dtype="bf16", scale=scale, what="long-context prefill, sampled rows")
