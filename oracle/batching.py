@@ -17,7 +17,8 @@ leave to vLLM's tuning):
      the free blocks cover the head's final size (prompt + max new tokens, in blocks) on top
      of what the running requests may still take before they finish, the head joins: its
      sequence is created, its prompt's slots are allocated and its prompt K/V written
-     ([P1] §三 步驟一..二). The first head that does not fit stops admission for the step;
+     ([P1] §三 步驟一..二); optionally (``prefill``) the written prompt tokens are then
+     attended, causally. The first head that does not fit stops admission for the step;
   3. decode: every running request, in admission order, appends one token: its K/V are
      written into the slot the allocator gives and attention runs over all of its tokens
      ([P1] §三 步驟三).
@@ -106,6 +107,23 @@ class BatchingLoop:
         self.k_cache, self.v_cache = cache_write.write_kv(
             k, v, self.k_cache, self.v_cache, slots, hkv=self.hkv, hd=self.hd, bs=self.bs,
             dtype=self.dtype)
+
+    def prefill(self, q, admitted, scale):
+        """Phase 2's attention, after the write: the admitted prompts' written tokens (each
+        prompt's tokens after its cached ones), q [T, Hq, hd] in admission order, attend
+        causally over their own prompts ([P1] §三 步驟二; the causal reading of
+        attention.prefill_attention). Returns float64 [T, Hq, hd]."""
+        if not admitted:
+            return np.zeros((0,) + np.shape(q)[1:])
+        ids = [a.rid for a in admitted]
+        mb = max(len(self.alloc.blocks[i]) for i in ids)
+        tables, lens = self.alloc.tables(ids, mb)
+        tables = np.asarray(tables, np.int32).reshape(len(ids), mb)
+        qs = np.concatenate([[0], np.cumsum([a.prompt_len - a.cached for a in admitted])])
+        return attention.prefill_attention(q, self.k_cache, self.v_cache, tables,
+                                           np.asarray(lens, np.int32), qs.astype(np.int32),
+                                           scale=scale, hkv=self.hkv, hd=self.hd, bs=self.bs,
+                                           dtype=self.dtype)
 
     def decode(self, q, k_new, v_new, scale, new_ids=None):
         """Phase 3 for the running requests (admission order); new_ids: the new tokens' ids

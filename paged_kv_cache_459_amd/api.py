@@ -329,6 +329,9 @@ def pkv_decode_planned(q, k_cache, v_cache, block_tables, context_lens, plan, pl
     return out
 
 
+PREFILL_MAX_BLOCKS = 512  # blocks of one prefill unit (longer rows are split and merged)
+
+
 def pkv_prefill_plan(query_start, context_lens, *, num_q_heads, num_kv_heads, max_blocks,
                      max_context_len, dtype, out=None):
     """Prefill plan from HOST copies of query_start [S+1] and context_lens [S] (int32): the new

@@ -10,7 +10,9 @@ vLLM's tuning, so the rule never needs it):
   blocks go back to the pool); (2) admit queue heads that have arrived while fewer than
   ``max_batch`` run and the free blocks cover the head's final size (prompt + max new tokens)
   on top of what the running requests may still take; an admitted request's prompt slots are
-  allocated and its prompt K/V written (``pkv_write``); (3) decode: every running request, in
+  allocated and its prompt K/V written (``pkv_write``), and, if the caller asks
+  (``prefill``), the written prompt tokens are attended causally (``pkv_prefill_attn``, the
+  cached prefix included); (3) decode: every running request, in
   admission order, appends one token, whose K/V are stored and attended to in the fused
   decode step (``pkv_decode_append_stream`` + ``pkv_decode_append_merge``).
 
@@ -151,6 +153,7 @@ class ContinuousBatch:
             admitted.append((rid, p, m))
             cached.append(c)
         self.last_cached = cached
+        self.last_admitted = [(a[0], a[1], c) for a, c in zip(admitted, cached)]
         if T:
             s = self._set
             self.prompt_slots = self._dev[s][self._slot0:self._slot0 + T]
@@ -172,6 +175,67 @@ class ContinuousBatch:
                 raise ValueError("no prompt was admitted this step")
             return
         api.pkv_write(k, v, self.k_cache, self.v_cache, self.prompt_slots)
+
+    def prefill(self, q, scale, out=None, events=None):
+        """Causal attention of the prompt tokens written this step (after write_prompts, before
+        decode): q [T, Hq, hd] in the rows of write_prompts (each admitted prompt's tokens
+        after its cached ones) attends over its own prompt, cached prefix included
+        (pkv_prefill_attn). Returns out [T, Hq, hd]. ``events``: optional two
+        torch.cuda.Events recorded before and after the attention."""
+        adm = getattr(self, "last_admitted", [])
+        T = sum(p - c for _, p, c in adm)
+        if q.shape[0] != T:
+            raise ValueError(f"q has {q.shape[0]} rows, the admitted prompts {T} tokens")
+        if T == 0:
+            return q.new_empty((0, self.Hq, self.hd))
+        A, mb = len(adm), self.max_blocks
+        if not hasattr(self, "_pf_pin"):  # two pinned/device sets: tables, lengths, plan
+            tmax = self.max_batch * self.max_ctx
+            cap = (16 + 3 * tmax + 1 +
+                   8 * tmax * max(1, -(-mb // api.PREFILL_MAX_BLOCKS)))
+            self._pf_n = self.max_batch * mb + 2 * self.max_batch + 1
+            n = self._pf_n + cap
+            self._pf_pin = [torch.empty(n, dtype=torch.int32, pin_memory=True) for _ in range(2)]
+            self._pf_dev = [torch.empty(n, dtype=torch.int32, device=self.device)
+                            for _ in range(2)]
+            self._pf_free = [torch.cuda.Event() for _ in range(2)]
+            self._pf_set = 0
+            self._pf_ws = None
+        s = self._pf_set
+        self._pf_free[s].synchronize()  # the copies that last read this set have run
+        pin = self._pf_pin[s].numpy()
+        tab = pin[:A * mb].reshape(A, mb)
+        o = self.max_batch * mb
+        lens = pin[o:o + A]
+        qs = pin[o + self.max_batch:o + self.max_batch + A + 1]
+        self.alloc.tables(np.array([a[0] for a in adm], np.int64), mb, tables_out=tab,
+                          lens_out=lens, mark_shared=True)
+        qs[0] = 0
+        qs[1:] = np.cumsum([p - c for _, p, c in adm])
+        plan = api.pkv_prefill_plan(qs, lens, num_q_heads=self.Hq, num_kv_heads=self.Hkv,
+                                    max_blocks=mb, max_context_len=self.max_ctx,
+                                    dtype=self.dtype, out=pin[self._pf_n:])
+        if plan.ctypes.data != pin[self._pf_n:].ctypes.data:
+            raise RuntimeError("prefill plan larger than its pinned buffer")
+        dev = self._pf_dev[s]
+        dev[:A * mb].copy_(self._pf_pin[s][:A * mb], non_blocking=True)
+        end = self._pf_n + len(plan)
+        dev[self._pf_n:end].copy_(self._pf_pin[s][self._pf_n:end], non_blocking=True)
+        self._pf_free[s].record()
+        self._pf_set ^= 1
+        need = api.pkv_prefill_workspace_bytes(self.Hq, self.Hkv, self.hd, plan)
+        if need and (self._pf_ws is None or self._pf_ws.numel() < need):
+            self._pf_ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        if events is not None:
+            events[0].record()
+        out = api.pkv_prefill_attn(q, self.k_cache, self.v_cache, dev[:A * mb].view(A, mb),
+                                   plan, dev[self._pf_n:end], num_kv_heads=self.Hkv,
+                                   scale=scale, max_context_len=self.max_ctx,
+                                   workspace=self._pf_ws if need else None, out=out)
+        if events is not None:
+            events[1].record()
+        self.last_prefill_tables = tab.copy()
+        return out
 
     # -- phase 3 ---------------------------------------------------------------------------
     def decode(self, q, k_new, v_new, scale, out=None, events=None, new_ids=None):

@@ -1,7 +1,8 @@
 """The continuous-batching step loop on the GPU (ContinuousBatch: the C++ allocator, pkv_write
-for admitted prompts, the fused decode step) against the oracle's loop, in lockstep on one
-seeded request stream; also with automatic prefix caching (requests sharing system prompts:
-the same cached counts, only the uncached prompt tokens written).
+for admitted prompts, their causal prefill attention, the fused decode step) against the
+oracle's loop, in lockstep on one seeded request stream; also with automatic prefix caching
+(requests sharing system prompts: the same cached counts, only the uncached prompt tokens
+written and attended, over their prompts cached prefix included).
 
 Every step: the same requests retire and are admitted (the admission rule is implemented
 separately on both sides), the prompt slots, block tables and lengths are equal, the memory
@@ -48,7 +49,7 @@ def test_loop_matches_oracle(dtype, hq, hkv, hd, nb, max_batch, kernel):
         ref.submit(*r)
         loop.submit(*r)
     prev = m.pkv_set_attn_kernel(kernel)
-    steps = 0
+    steps = prefills = 0
     try:
         while not ref.idle():
             r_ret, r_adm, r_slots = ref.schedule()
@@ -62,6 +63,13 @@ def test_loop_matches_oracle(dtype, hq, hkv, hd, nb, max_batch, kernel):
                 v = W.normal_values(rng, (T, hkv, hd), dtype)
                 ref.write_prompts(k, v, r_slots)
                 loop.write_prompts(G.to_dev(k, dtype), G.to_dev(v, dtype))
+                if dtype != "f32":  # the admitted prompts' causal attention
+                    qp = W.normal_values(rng, (T, hq, hd), dtype)
+                    want_p = ref.prefill(qp, r_adm, scale)
+                    got_p = loop.prefill(G.to_dev(qp, dtype), scale)
+                    torch.cuda.synchronize()
+                    G.assert_close(G.gpu_f64(got_p, dtype), want_p, dtype, f"prefill {steps}")
+                    prefills += 1
             B = len(ref.running)
             assert list(loop.running()) == [r.rid for r in ref.running]
             q = W.normal_values(rng, (B, hq, hd), dtype)
@@ -82,6 +90,7 @@ def test_loop_matches_oracle(dtype, hq, hkv, hd, nb, max_batch, kernel):
             assert steps < 1000
     finally:
         m.pkv_set_attn_kernel(prev)
+    assert dtype == "f32" or prefills > 0
     assert loop.idle()
     kc = W.to_storage_numpy(k_cache, dtype).reshape(-1)
     vc = W.to_storage_numpy(v_cache, dtype).reshape(-1)
@@ -134,6 +143,12 @@ def test_loop_with_prefix_cache_matches_oracle(dtype, hq, hkv, hd, kernel):
                 v = W.normal_values(rng, (T, hkv, hd), dtype)
                 ref.write_prompts(k, v, r_slots)
                 loop.write_prompts(G.to_dev(k, dtype), G.to_dev(v, dtype))
+                # the uncached prompt tokens attend over their prompts, cached prefix included
+                qp = W.normal_values(rng, (T, hq, hd), dtype)
+                want_p = ref.prefill(qp, r_adm, 0.1)
+                got_p = loop.prefill(G.to_dev(qp, dtype), 0.1)
+                torch.cuda.synchronize()
+                G.assert_close(G.gpu_f64(got_p, dtype), want_p, dtype, "prefix-cached prefill")
             B = len(ref.running)
             new_ids = [int(x) for x in rng.integers(0, 1000, size=B)]
             q = W.normal_values(rng, (B, hq, hd), dtype)
