@@ -87,6 +87,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-plan", action="store_true",
                     help="decode batches that share blocks without a shared-prefix plan")
+    ap.add_argument("--with-prefill", action="store_true",
+                    help="batching workloads: each step also runs the admitted prompts' causal "
+                         "prefill attention (a full serving step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -485,6 +488,9 @@ def batching_main(args, torch, pkv, W):
     out = torch.empty_like(q)
     scale = 1.0 / math.sqrt(hd)
     eb = 2
+    q_prompt = (W.device_normal((max_prompt, Hq, hd), dtype, 7108) if args.with_prefill
+                else None)
+    pf_out = torch.empty_like(q_prompt) if args.with_prefill else None
 
     ids_rng = np.random.default_rng(cfg["seed"] + 1)
 
@@ -492,8 +498,17 @@ def batching_main(args, torch, pkv, W):
         retired, admitted, T = loop.schedule()
         if ev is not None:
             ev[0].record()
+        pf_flops = 0.0
         if T:
             loop.write_prompts(k_prompt[:T], v_prompt[:T])
+            if args.with_prefill:  # the written prompt tokens attend over their prompts
+                loop.prefill(q_prompt[:T], scale, out=pf_out[:T],
+                             events=None if ev is None else ev[6:8])
+                for _, p, c in loop.last_admitted:
+                    pf_flops += 4.0 * hd * Hq * (p * (p + 1) / 2 - c * (c + 1) / 2)
+        if ev is not None and args.with_prefill and not T:
+            ev[6].record()
+            ev[7].record()
         n = len(loop.run_id)
         if ev is not None:
             ev[1].record()
@@ -504,6 +519,7 @@ def batching_main(args, torch, pkv, W):
             lens = loop.last_lens.copy()
             u = loop.usage()
             stats.append(dict(B=n, retired=len(retired), admitted=len(admitted), T=T,
+                              pf_flops=pf_flops,
                               planned=getattr(loop, "last_plan_units", 0) > 0,
                               prompt=sum(a[1] for a in admitted),
                               kv=int(lens.astype(np.int64).sum()) * 2 * Hkv * hd * eb,
@@ -512,7 +528,7 @@ def batching_main(args, torch, pkv, W):
     for _ in range(cfg["settle_steps"] + args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
     stats = []
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -520,6 +536,7 @@ def batching_main(args, torch, pkv, W):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     write_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    prefill_ms = [e[6].elapsed_time(e[7]) for e in evs] if args.with_prefill else None
     shared_ms = [e[2].elapsed_time(e[3]) for e in evs]
     part_ms = [e[3].elapsed_time(e[4]) for e in evs]
     merge_ms = [e[4].elapsed_time(e[5]) for e in evs]
@@ -568,6 +585,7 @@ def batching_main(args, torch, pkv, W):
         "dtype": dtype,
         "data": "synthetic (seeded request stream, seeded N(0,1) values and block placement)",
         "config": {"workload": args.workload, "description": DESC[args.workload],
+                   "with_prefill": bool(args.with_prefill),
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": hd, "block_size": 16,
                    "pool_blocks": nb, "max_batch": cfg["max_batch"],
                    "max_context_len": cfg["max_ctx"], "stream_workers": loop.W,
@@ -596,6 +614,13 @@ def batching_main(args, torch, pkv, W):
             "requests_the_pool_holds_contiguous": nb * 16 // cfg["max_ctx"],
             "logical_tokens_per_filled_slot": round(float(np.mean(sharing)), 3),
             "kv_bytes_per_step": {"unique": int(np.mean(kv)), "logical": int(np.mean(kv_logical))},
+        },
+        "prefill": None if prefill_ms is None else {
+            "note": "each step also attends the admitted prompts' tokens causally "
+                    "(pkv_prefill_attn); prompt_write_ms_per_step includes it",
+            "ms_per_step": round(float(np.mean(prefill_ms)), 4),
+            "tflops": (round(sum(st["pf_flops"] for st in stats) / (sum(prefill_ms) / 1e3)
+                             / 1e12, 2) if sum(prefill_ms) > 0 else None),
         },
         "roofline": {
             "bound": "hbm",

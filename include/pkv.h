@@ -259,8 +259,10 @@ pkv_status pkv_decode_planned(int32_t pass, void* out, const void* q, const void
 /*                                                                                            */
 /* The work is planned on the host (pkv_prefill_plan, from host copies of query_start and    */
 /* context_lens): tiles of consecutive rows of one sequence, each split into chunks of at most */
-/* 64 blocks when its last row sees more (then every row's chunks give (m, l, o) pieces that  */
-/* a merge combines in chunk order, as pkv_decode_merge does). Plan layout (int32):            */
+/* `chunk` blocks when its last row sees more (then every row's chunks give (m, l, o) pieces   */
+/* that a merge combines in chunk order, as pkv_decode_merge does). chunk is 512, halved      */
+/* (down to 64) while the launch would have fewer than 1024 (unit, kv head) work-groups.      */
+/* Plan layout (int32):                                                                        */
 /* header[16] = {magic 0x50524631, T, H, GS, U, M, L, cells, chunk, S, tile_rows, 0...},       */
 /* skip[T] (1: the row is merged), vis[T] (pos + 1), ptr[T+1], units[U][6] = {sequence, b0,   */
 /* b1, member_off, member_cnt, cell_base (-1: written directly)}, members[M] (rows),           */

@@ -428,8 +428,10 @@ pkv_status pkv_prefill_plan(const int32_t* query_start, const int32_t* context_l
   const int32_t G = Hq / Hkv;
   std::vector<int32_t> v;
   const int32_t zero = 0;
-  pkv::prefill_plan_build(S > 0 ? query_start : &zero, context_lens, S, Hkv, G,
-                          pkv::prefill_tile_rows(G), pkv::kPrefillMaxBlocks, &v);
+  const int32_t* qsp = S > 0 ? query_start : &zero;
+  const int32_t chunk = pkv::prefill_chunk(qsp, context_lens, S, Hkv, pkv::prefill_tile_rows(G),
+                                           pkv::kPrefillMaxBlocks, pkv::kPrefillMinGroups);
+  pkv::prefill_plan_build(qsp, context_lens, S, Hkv, G, pkv::prefill_tile_rows(G), chunk, &v);
   *plan_ints = v.size();
   if (!plan || capacity < v.size()) return PKV_ERR_WORKSPACE;
   std::memcpy(plan, v.data(), v.size() * sizeof(int32_t));

@@ -28,6 +28,11 @@ constexpr int kMaxPlannedGroup = 4;  // q heads per kv head up to which batches 
 constexpr int kMaxUnitBlocks = 64;   // blocks of one unit (one block id per lane)
 constexpr int32_t kPrefillMagic = 0x50524631;
 constexpr int kPrefillMaxBlocks = 512;  // blocks of one prefill unit (their ids sit in LDS)
+constexpr int kPrefillMinChunk = 64;    // shortest unit the planner cuts to fill the device
+// Work-groups a prefill launch should have before units are cut shorter: two waves of the
+// 512 that MI355X holds at once (256 compute units, two work-groups each). Units are not cut
+// below 64 blocks: shorter ones cost more in pieces and merging than they gain.
+constexpr int64_t kPrefillMinGroups = 1024;
 #ifndef PKV_PREFILL_RT
 #define PKV_PREFILL_RT 2
 #endif
@@ -59,6 +64,12 @@ bool plan_check(const int32_t* p, size_t n, int32_t B, int32_t max_blocks, int32
 // vis[T], sh_ptr[T+1], units[U][6], members[M] (rows), sh_list[L].
 void prefill_plan_build(const int32_t* query_start, const int32_t* lens, int32_t S, int32_t H,
                         int32_t GS, int32_t tile_rows, int32_t chunk, std::vector<int32_t>* out);
+// The unit length (blocks) of a prefill plan: the longest power-of-two fraction of max_chunk
+// (down to kPrefillMinChunk) for which the launch still has at least min_groups work-groups
+// (units * H). Small batches over long contexts are cut finer: their rows become pieces that
+// the merge combines, instead of a launch too small to fill the device.
+int32_t prefill_chunk(const int32_t* query_start, const int32_t* lens, int32_t S, int32_t H,
+                      int32_t tile_rows, int32_t max_chunk, int64_t min_groups);
 bool prefill_plan_check(const int32_t* p, size_t n, int32_t T, int32_t S, int32_t max_blocks,
                         int32_t max_ctx, int32_t H, int32_t GS, int32_t max_tile_rows,
                         int32_t max_chunk, PlanView* v);

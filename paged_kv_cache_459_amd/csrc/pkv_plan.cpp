@@ -208,6 +208,26 @@ bool plan_check(const int32_t* p, size_t n, int32_t B, int32_t max_blocks, int32
 // sequence, the cached prefix included. The same (m, l, o) pieces and merge as decode serve a
 // row whose visible blocks are split over several chunks.
 
+int32_t prefill_chunk(const int32_t* qs, const int32_t* lens, int32_t S, int32_t H,
+                      int32_t tile_rows, int32_t max_chunk, int64_t min_groups) {
+  // the tiles' block counts, as prefill_plan_build cuts them
+  std::vector<int32_t> nbs;
+  for (int32_t s = 0; s < S; ++s) {
+    const int32_t q = qs[s + 1] - qs[s], n = lens[s];
+    for (int32_t a = 0; a < q; a += tile_rows) {
+      const int32_t last = std::min(q, a + tile_rows) - 1;  // the tile's last row
+      nbs.push_back((n - q + last + 1 + kBlockSize - 1) / kBlockSize);
+    }
+  }
+  int32_t chunk = max_chunk;
+  for (; chunk > kPrefillMinChunk; chunk /= 2) {
+    int64_t units = 0;
+    for (int32_t nb : nbs) units += (nb + chunk - 1) / chunk;
+    if (units * H >= min_groups) break;
+  }
+  return chunk;
+}
+
 void prefill_plan_build(const int32_t* qs, const int32_t* lens, int32_t S, int32_t H, int32_t GS,
                         int32_t tile_rows, int32_t chunk, std::vector<int32_t>* out) {
   const int32_t T = qs[S];

@@ -65,7 +65,6 @@ def test_whole_prompts(dtype, hq, hkv, hd):
     p, q, qs = problem(1200 + hq, lens, lens, hq, hkv, hd, dtype)
     scale = G.scale_for(hd)
     got, plan = prefill_gpu(p, q, qs, scale, hq)
-    assert int(plan[7]) == 0  # every tile fits one chunk: written directly
     G.assert_close(got, oracle(p, q, qs, scale), dtype, "whole prompts")
 
 

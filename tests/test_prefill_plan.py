@@ -1,7 +1,7 @@
 """The prefill planner (pkv_prefill_plan, host code) against brute-force definitions.
 
 For batches mixing whole prompts, cached prefixes, single new tokens, empty sequences and
-rows that see more than one chunk (512 blocks):
+rows that see more than one chunk (512 blocks, cut shorter for small launches):
 * row t of sequence s (t = query_start[s] + k) sees vis_t = n_s - q_s + k + 1 tokens;
 * the units naming t belong to t's sequence, hold consecutive rows of it (at most the
   plan's tile size: a work-group's 64*RT rows / G, RT = 2 or 4),
@@ -71,7 +71,17 @@ def test_prefill_plan_matches_brute_force(kind, hq, hkv):
     G = hq // hkv
     T = int(qs[-1])
     assert (P["T"], P["H"], P["GS"], P["S"]) == (T, hkv, G, len(n))
-    assert P["rows"] in ((64 * 2) // G, (64 * 4) // G) and P["chunk"] == 512
+    assert P["rows"] in ((64 * 2) // G, (64 * 4) // G)
+    # the unit length: 512 blocks, halved (down to 64) while fewer than 1024 work-groups
+    nbs = []
+    for s_ in range(len(n)):
+        for a in range(0, int(q[s_]), P["rows"]):
+            last = min(int(q[s_]), a + P["rows"]) - 1
+            nbs.append(-(-(int(n[s_]) - int(q[s_]) + last + 1) // 16))
+    want = 512
+    while want > 64 and sum(-(-b // want) for b in nbs) * hkv < 1024:
+        want //= 2
+    assert P["chunk"] == want
     seq_of = np.repeat(np.arange(len(n)), q)
     vis = np.array([n[s] - q[s] + (t - qs[s]) + 1 for t, s in zip(range(T), seq_of)], np.int64)
     np.testing.assert_array_equal(P["vis"], vis)
@@ -82,7 +92,7 @@ def test_prefill_plan_matches_brute_force(kind, hq, hkv):
     for u in P["units"]:
         s, b0, b1, off, cnt, cbase = (int(x) for x in u)
         rows = P["members"][off:off + cnt]
-        assert 1 <= cnt <= P["rows"] and b0 < b1 and b1 - b0 <= 512
+        assert 1 <= cnt <= P["rows"] and b0 < b1 and b1 - b0 <= P["chunk"]
         np.testing.assert_array_equal(rows, np.arange(rows[0], rows[0] + cnt))
         assert np.all(seq_of[rows] == s)
         assert b1 <= -(-int(vis[rows].max()) // 16)
@@ -104,7 +114,7 @@ def test_prefill_plan_matches_brute_force(kind, hq, hkv):
         else:
             assert not any(direct[t]) and P["skip"][t] == 1
         assert P["list"][P["ptr"][t]:P["ptr"][t + 1]].tolist() == lists[t]
-    if kind == "cached":  # rows past 512 blocks are split, short ones are not
+    if kind == "cached":  # rows past the unit length are split, short ones are not
         assert P["skip"].any() and not P["skip"].all()
 
 
