@@ -145,9 +145,9 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, con
 /*   scale         the softmax scale (1/sqrt(hd) in the usual model).                          */
 /*   workspace     device scratch of at least pkv_decode_workspace_bytes(...) bytes, caller    */
 /*                 owned; contents on entry are ignored. May be NULL only when that size is 0. */
-/* Supported: hd in {64,128}, bs == 16, Hq % Hkv == 0, dtype f32/f16/bf16. Batches of more     */
-/* than 8192 sequences (or of more tiles than int32 positions allow) run as several            */
-/* stream+merge launches over consecutive row ranges, reusing the workspace in stream order.  */
+/* Supported: hd in {64,128}, bs == 16, Hq % Hkv == 0, Hq + Hkv <= 65535, dtype f32/f16/bf16. */
+/* Batches of more than 8192 sequences (or of more tiles than int32 positions allow) run as */
+/* several stream+merge launches over consecutive row ranges, reusing the workspace in order.*/
 /* The launch size comes from the calling thread's current HIP device.                        */
 /* Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_INDEX          */
 /* (PKV_CHECK=1: an entry j < ceil(n_i/bs) outside [0,NB), or n_i outside [0,max_context_len]),*/

@@ -1002,7 +1002,7 @@ __device__ void store_new_token(const StreamParams& p, int i, int h) {
   const int blk = raw & ~kSharedBit;
   if (raw < 0 || blk >= p.NB) return;
   const int off = (n - 1) % kBlockSize;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const size_t tile = static_cast<size_t>(blk) * p.Hkv + h;
   const size_t row = static_cast<size_t>(i) * p.Hkv + h;
   if (lane < CH) {
@@ -1023,18 +1023,31 @@ __device__ void store_new_token(const StreamParams& p, int i, int h) {
 // ------------------------------------------------------------------------------------------
 // Merge of the pieces of segments cut by worker-range boundaries. One wave per output row
 // (sequence i, q head hh of head slot hh / GS). The pieces' (m, l) are read one per lane and
-// weighted in parallel; o is accumulated over the pieces in worker order (deterministic),
-// with the loads of consecutive pieces issued back to back. Rows of segments inside one
-// range, and rows with n = 0, were finished by the stream pass and are left alone.
+// weighted in parallel; o is accumulated over the pieces in worker order (deterministic).
+// The o loads of the first U pieces are issued together with the (m, l) loads, before the
+// maximum is known, so a row with up to U pieces costs two dependent memory round trips after
+// the prefix sums. Rows of segments inside one range, and rows with n = 0, were finished by
+// the stream pass and are left alone.
 // With a shared-prefix plan, a planned sequence's row always merges here: its private pieces
 // (the workers' cells, or its own cell when one worker held the segment whole; none when all
 // of its blocks are shared) come first, then its shared-pass pieces in plan order.
+// Append mode: rows H * GS .. H * GS + Hkv - 1 are waves of their own that store each
+// sequence's newest K/V rows (one wave per kv head), concurrently with the merge waves.
+// A work-group holds kMergeWaves rows of one sequence (fewer, larger work-groups dispatch
+// faster than one per row); its waves never synchronise with each other.
+constexpr int kMergeWaves = 4;
+
 template <int DT, int HD>
-__global__ void __launch_bounds__(64)
-merge_kernel(const StreamParams p, int H, int GS) {
+__global__ void __launch_bounds__(64 * kMergeWaves)
+merge_kernel(const StreamParams p, int H, int GS, int rows) {
   constexpr int R = HD / 64;
-  const int i = blockIdx.x, hh = blockIdx.y, lane = threadIdx.x;
-  if (p.k_new != nullptr && hh % (p.Hq / p.Hkv) == 0) store_new_token<DT, HD>(p, i, hh / (p.Hq / p.Hkv));
+  const int i = blockIdx.x, lane = threadIdx.x & 63;
+  const int hh = blockIdx.y * kMergeWaves + uniform(threadIdx.x >> 6);
+  if (hh >= rows) return;
+  if (hh >= H * GS) {
+    store_new_token<DT, HD>(p, i, hh - H * GS);
+    return;
+  }
   const int h = hh / GS, n = hh - h * GS;
   const bool planned = p.skip != nullptr && p.skip[i] > 0;
   // prefill has no stream pass (ws_seg null): shared-pass pieces only
@@ -1082,8 +1095,39 @@ merge_kernel(const StreamParams p, int H, int GS) {
     return c0 * GS + n;
   };
   constexpr int U = 16;  // pieces whose o loads are in flight together
-  float M = kNegInf;
-  for (int k = lane; k < np; k += 64) M = fmaxf(M, p.ws_ml[cell(k) * 2]);
+  // o of pieces base + k0 .. + U - 1 (one past cnt re-reads piece 0: in bounds, unused);
+  // called only when the row has a piece
+  auto load_o = [&](float (&ov)[U][R], int base, int k0, int cnt) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float* ok = p.ws_o + cell(k0 + u < cnt ? base + k0 + u : 0) * HD;
+#pragma unroll
+      for (int r = 0; r < R; ++r) ov[u][r] = ok[lane + 64 * r];
+    }
+  };
+  auto accumulate = [&](const float (&ov)[U][R], float wt, int k0, int cnt, float (&O)[R]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (k0 + u < cnt) {
+        const float wk = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt), k0 + u));
+#pragma unroll
+        for (int r = 0; r < R; ++r) O[r] = fmaf(wk, ov[u][r], O[r]);
+      }
+    }
+  };
+  // Round trip 1 (after the prefix sums): (m, l) of pieces 0..63 and o of pieces 0..U-1.
+  float m0 = kNegInf, l0 = 0.f;
+  if (lane < np) {
+    const size_t cl = cell(lane);
+    m0 = p.ws_ml[cl * 2];
+    l0 = p.ws_ml[cl * 2 + 1];
+  }
+  const int cnt0 = uniform(min(64, np));
+  float ov0[U][R];
+  if (np > 0) load_o(ov0, 0, 0, cnt0);
+  float M = m0;
+  for (int k = 64 + lane; k < np; k += 64) M = fmaxf(M, p.ws_ml[cell(k) * 2]);
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
   float Lpart = 0.f, O[R];
@@ -1092,29 +1136,25 @@ merge_kernel(const StreamParams p, int H, int GS) {
   for (int base = 0; base < np; base += 64) {
     float wt = 0.f;  // weight of piece base + lane; a piece with no valid token weighs 0
     if (base + lane < np) {
-      const size_t cl = cell(base + lane);
-      const float mk = p.ws_ml[cl * 2];
+      float mk = m0, lk = l0;
+      if (base > 0) {
+        const size_t cl = cell(base + lane);
+        mk = p.ws_ml[cl * 2];
+        lk = p.ws_ml[cl * 2 + 1];
+      }
       wt = mk == kNegInf ? 0.f : exp2_fast(mk - M);
-      Lpart = fmaf(wt, p.ws_ml[cl * 2 + 1], Lpart);
+      Lpart = fmaf(wt, lk, Lpart);
     }
     const int cnt = uniform(min(64, np - base));
-    for (int k0 = 0; k0 < cnt; k0 += U) {
+    int k0 = 0;
+    if (base == 0) {  // the first U pieces' o is already in registers
+      accumulate(ov0, wt, 0, cnt, O);
+      k0 = U;
+    }
+    for (; k0 < cnt; k0 += U) {
       float ov[U][R];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {  // independent loads (a piece past the end re-reads piece 0)
-        const float* ok = p.ws_o + cell(k0 + u < cnt ? base + k0 + u : 0) * HD;
-#pragma unroll
-        for (int r = 0; r < R; ++r) ov[u][r] = ok[lane + 64 * r];
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (k0 + u < cnt) {
-          const float wk = __builtin_bit_cast(
-              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt), k0 + u));
-#pragma unroll
-          for (int r = 0; r < R; ++r) O[r] = fmaf(wk, ov[u][r], O[r]);
-        }
-      }
+      load_o(ov, base, k0, cnt);
+      accumulate(ov, wt, k0, cnt, O);
     }
   }
   float L = Lpart;
@@ -1171,11 +1211,15 @@ void launch_shared_t(const StreamParams& p, int H, int GS, hipStream_t stream) {
 
 template <int DT>
 void launch_merge_t(const StreamParams& p, int H, int GS, hipStream_t stream) {
-  const dim3 grid(p.B, H * GS);
+  // append mode: one more row per kv head for the newest tokens' stores
+  const int rows = H * GS + (p.k_new != nullptr ? p.Hkv : 0);
+  const dim3 grid(p.B, (rows + kMergeWaves - 1) / kMergeWaves);
   if (p.hd == 64)
-    hipLaunchKernelGGL((merge_kernel<DT, 64>), grid, dim3(64), 0, stream, p, H, GS);
+    hipLaunchKernelGGL((merge_kernel<DT, 64>), grid, dim3(64 * kMergeWaves), 0, stream, p, H,
+                       GS, rows);
   else
-    hipLaunchKernelGGL((merge_kernel<DT, 128>), grid, dim3(64), 0, stream, p, H, GS);
+    hipLaunchKernelGGL((merge_kernel<DT, 128>), grid, dim3(64 * kMergeWaves), 0, stream, p, H,
+                       GS, rows);
 }
 
 }  // namespace
