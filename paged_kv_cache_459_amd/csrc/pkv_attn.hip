@@ -34,6 +34,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -1095,14 +1096,16 @@ merge_kernel(const StreamParams p, int H, int GS, int rows) {
     return c0 * GS + n;
   };
   constexpr int U = 16;  // pieces whose o loads are in flight together
-  // o of pieces base + k0 .. + U - 1 (one past cnt re-reads piece 0: in bounds, unused);
-  // called only when the row has a piece
+  // o of pieces base + k0 .. + U - 1 that exist (cnt is wave-uniform: no load is issued for
+  // a missing piece, and the ones issued are all in flight together)
   auto load_o = [&](float (&ov)[U][R], int base, int k0, int cnt) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float* ok = p.ws_o + cell(k0 + u < cnt ? base + k0 + u : 0) * HD;
+      if (k0 + u < cnt) {
+        const float* ok = p.ws_o + cell(base + k0 + u) * HD;
 #pragma unroll
-      for (int r = 0; r < R; ++r) ov[u][r] = ok[lane + 64 * r];
+        for (int r = 0; r < R; ++r) ov[u][r] = ok[lane + 64 * r];
+      }
     }
   };
   auto accumulate = [&](const float (&ov)[U][R], float wt, int k0, int cnt, float (&O)[R]) {
@@ -1125,7 +1128,7 @@ merge_kernel(const StreamParams p, int H, int GS, int rows) {
   }
   const int cnt0 = uniform(min(64, np));
   float ov0[U][R];
-  if (np > 0) load_o(ov0, 0, 0, cnt0);
+  load_o(ov0, 0, 0, cnt0);
   float M = m0;
   for (int k = 64 + lane; k < np; k += 64) M = fmaxf(M, p.ws_ml[cell(k) * 2]);
 #pragma unroll
@@ -1251,6 +1254,10 @@ int32_t default_workers(int32_t dtype, int32_t hd, int32_t kernel, int32_t B) {
                                                    kThreads, lds) != hipSuccess ||
       per_cu <= 0)
     return 0;
+  // The matrix-core kernel streams fastest at two work-groups per compute unit (measured on
+  // the skewed GQA batches: three give more, shorter ranges, and more pieces to merge, for no
+  // gain in bandwidth); the vector kernel at what the occupancy allows.
+  if (kernel == kMatrix) per_cu = std::min(per_cu, 2);
   int64_t grid = static_cast<int64_t>(cus) * per_cu;
   if (grid >= 8) grid -= grid % 8;  // a whole number of work-groups per XCD
   const int32_t workers = static_cast<int32_t>(grid * kWaves);
