@@ -427,6 +427,7 @@ attn_vector_kernel(const StreamParams p) {
   const size_t blk_stride = static_cast<size_t>(p.Hkv) * TILE;
 
   uint4 qv[NL];
+  uint4 nr = make_uint4(0, 0, 0, 0);  // append mode: a chunk of the segment's newest K/V rows
   float m = kNegInf, lsum = 0.f;
   float acc[NL];
   uint4 kr[NL], vr[NL];
@@ -443,18 +444,32 @@ attn_vector_kernel(const StreamParams p) {
       return static_cast<const char*>(cache) + static_cast<size_t>(id) * blk_stride +
              static_cast<size_t>(h / G) * TILE;
     };
-    auto is_shared = [&](int k) {
-      return (uniform(__builtin_amdgcn_readlane(ti.hm, k)) & kShared) != 0;
-    };
+    // K of tile k; when tile k starts a segment, also that segment's q (the previous tile's
+    // scores are already computed, so the old q is dead) and, in append mode, its newest K/V
+    // rows, so they arrive with the tile instead of stalling the segment's first step.
     auto load_k = [&](int k) {
       const char* kt = tile_base(p.k_cache, k);
-      const bool sh = is_shared(k);
+      const bool sh = (uniform(__builtin_amdgcn_readlane(ti.hm, k)) & kShared) != 0;
 #pragma unroll
       for (int j = 0; j < NL; ++j) kr[j] = load_tile16(kt + (lane_off + 1024u * j), sh);
+      const int hmk = uniform(__builtin_amdgcn_readlane(ti.hm, k));
+      if (hmk & kStart) {
+        const int seq = uniform(__builtin_amdgcn_readlane(ti.seq, k));
+        const int h = hmk >> 16;
+        const uint4* qp = reinterpret_cast<const uint4*>(
+            static_cast<const char*>(p.q) + (static_cast<size_t>(seq) * p.Hq + h) * HD * EB);
+#pragma unroll
+        for (int j = 0; j < NL; ++j) qv[j] = qp[4 * j + row_id];
+        if (p.k_new != nullptr && lane < 2 * NR) {
+          const size_t row = (static_cast<size_t>(seq) * p.Hkv + h / G) * HD * EB;
+          const char* src = static_cast<const char*>(lane < NR ? p.k_new : p.v_new) + row;
+          nr = *reinterpret_cast<const uint4*>(src + 16 * (lane % NR));
+        }
+      }
     };
     auto load_v = [&](int k) {
       const char* vt = tile_base(p.v_cache, k);
-      const bool sh = is_shared(k);
+      const bool sh = (uniform(__builtin_amdgcn_readlane(ti.hm, k)) & kShared) != 0;
 #pragma unroll
       for (int j = 0; j < NL; ++j) vr[j] = load_tile16(vt + (lane_off + 1024u * j), sh);
     };
@@ -464,26 +479,15 @@ attn_vector_kernel(const StreamParams p) {
       const int seq = uniform(__builtin_amdgcn_readlane(ti.seq, k));
       const int hm = uniform(__builtin_amdgcn_readlane(ti.hm, k));
       const int h = hm >> 16, valid = hm & 31;
-      if (hm & kStart) {  // first tile of a segment in this range: fresh state, its q
+      if (hm & kStart) {  // first tile of a segment in this range: fresh state (its q came
+                          // with the tile's K)
         m = kNegInf;
         lsum = 0.f;
 #pragma unroll
         for (int j = 0; j < NL; ++j) acc[j] = 0.f;
-        const uint4* qp = reinterpret_cast<const uint4*>(
-            static_cast<const char*>(p.q) + (static_cast<size_t>(seq) * p.Hq + h) * HD * EB);
-#pragma unroll
-        for (int j = 0; j < NL; ++j) qv[j] = qp[4 * j + row_id];
-        // Append mode: the sequence's newest K and V rows for this head, staged in LDS now,
-        // under the same wait as q, for the final block (in whichever tile of this range).
-        uint4 nr = make_uint4(0, 0, 0, 0);
-        if (p.k_new != nullptr && lane < 2 * NR) {
-          const size_t row = (static_cast<size_t>(seq) * p.Hkv + h / G) * HD * EB;
-          const char* src = static_cast<const char*>(lane < NR ? p.k_new : p.v_new) + row;
-          nr = *reinterpret_cast<const uint4*>(src + 16 * (lane % NR));
-        }
-#pragma unroll
-        for (int j = 0; j < NL; ++j) settle(qv[j]);
-        settle(nr);
+        // Append mode: the sequence's newest K and V rows for this head, staged in LDS for
+        // the final block (in whichever tile of this range), after the previous tile's
+        // reads of the staging area.
         if (p.k_new != nullptr) {
           if (lane < 2 * NR) s_new[w][lane / NR][lane % NR] = nr;
           wave_lds_sync();
@@ -655,7 +659,10 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_matrix_kernel(const StreamParams p)
   const uint32_t v_lane = 32u * hq + 8u * g;
   const size_t blk_stride = static_cast<size_t>(p.Hkv) * TILE;
 
-  uint4 qb[KS];
+  uint4 qb[KS];  // the group's q vectors; lanes of padding heads (hq >= G) keep zeros
+#pragma unroll
+  for (int s = 0; s < KS; ++s) qb[s] = make_uint4(0, 0, 0, 0);
+  uint4 nr = make_uint4(0, 0, 0, 0);  // append mode: a chunk of the segment's newest K/V rows
   float m = kNegInf, lsum = 0.f;
   float4_t o[VT];
   uint4 kr[KS];
@@ -672,18 +679,34 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_matrix_kernel(const StreamParams p)
       return static_cast<const char*>(cache) + static_cast<size_t>(id) * blk_stride +
              static_cast<size_t>(h) * TILE;
     };
-    auto is_shared = [&](int k) {
-      return (uniform(__builtin_amdgcn_readlane(ti.hm, k)) & kShared) != 0;
-    };
+    // K of tile k; when tile k starts a segment, also its q and newest rows (see the vector
+    // kernel).
     auto load_k = [&](int k) {
       const char* kt = tile_base(p.k_cache, k);
-      const bool sh = is_shared(k);
+      const bool sh = (uniform(__builtin_amdgcn_readlane(ti.hm, k)) & kShared) != 0;
 #pragma unroll
       for (int s = 0; s < KS; ++s) kr[s] = load_tile16(kt + (k_lane + 1024u * s), sh);
+      const int hmk = uniform(__builtin_amdgcn_readlane(ti.hm, k));
+      if (hmk & kStart) {
+        const int seq = uniform(__builtin_amdgcn_readlane(ti.seq, k));
+        const int kvh = hmk >> 16;
+        if (hq < G) {
+          const uint4* qp = reinterpret_cast<const uint4*>(
+              static_cast<const char*>(p.q) +
+              (static_cast<size_t>(seq) * p.Hq + kvh * G + hq) * HD * 2);
+#pragma unroll
+          for (int s = 0; s < KS; ++s) qb[s] = qp[4 * s + g];
+        }
+        if (p.k_new != nullptr && lane < 2 * NR) {
+          const size_t row = (static_cast<size_t>(seq) * p.Hkv + kvh) * HD * 2;
+          const char* src = static_cast<const char*>(lane < NR ? p.k_new : p.v_new) + row;
+          nr = *reinterpret_cast<const uint4*>(src + 16 * (lane % NR));
+        }
+      }
     };
     auto load_v = [&](int k) {
       const char* vt = tile_base(p.v_cache, k);
-      const bool sh = is_shared(k);
+      const bool sh = (uniform(__builtin_amdgcn_readlane(ti.hm, k)) & kShared) != 0;
 #pragma unroll
       for (int j = 0; j < VT; ++j) vr[j] = load_tile8(vt + (v_lane + 512u * j), sh);
     };
@@ -692,32 +715,14 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_matrix_kernel(const StreamParams p)
       const int seq = uniform(__builtin_amdgcn_readlane(ti.seq, k));
       const int hm = uniform(__builtin_amdgcn_readlane(ti.hm, k));
       const int kvh = hm >> 16, valid = hm & 31;
-      if (hm & kStart) {  // first tile of a segment in this range: fresh state, its q
+      if (hm & kStart) {  // first tile of a segment in this range: fresh state (its q came
+                          // with the tile's K)
         m = kNegInf;
         lsum = 0.f;
 #pragma unroll
         for (int j = 0; j < VT; ++j) o[j] = float4_t{0.f, 0.f, 0.f, 0.f};
-        if (hq < G) {
-          const uint4* qp = reinterpret_cast<const uint4*>(
-              static_cast<const char*>(p.q) +
-              (static_cast<size_t>(seq) * p.Hq + kvh * G + hq) * HD * 2);
-#pragma unroll
-          for (int s = 0; s < KS; ++s) qb[s] = qp[4 * s + g];
-        } else {
-#pragma unroll
-          for (int s = 0; s < KS; ++s) qb[s] = make_uint4(0, 0, 0, 0);
-        }
         // Append mode: stage the sequence's newest K and V rows of this kv head (see the
         // vector kernel).
-        uint4 nr = make_uint4(0, 0, 0, 0);
-        if (p.k_new != nullptr && lane < 2 * NR) {
-          const size_t row = (static_cast<size_t>(seq) * p.Hkv + kvh) * HD * 2;
-          const char* src = static_cast<const char*>(lane < NR ? p.k_new : p.v_new) + row;
-          nr = *reinterpret_cast<const uint4*>(src + 16 * (lane % NR));
-        }
-#pragma unroll
-        for (int s = 0; s < KS; ++s) settle(qb[s]);
-        settle(nr);
         if (p.k_new != nullptr) {
           if (lane < 2 * NR) s_new[w][lane / NR][lane % NR] = nr;
           wave_lds_sync();
