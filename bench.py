@@ -26,6 +26,7 @@ sample of the same workload on the host cores.
 """
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -73,6 +74,57 @@ DESC = {
                "tokens); each step writes the chunk's K/V (pkv_write) and runs causal "
                "attention of the new tokens over the paged cache (pkv_prefill_attn)",
 }
+
+
+class TimingEvent:
+    """A HIP event used only for timing, with the record / elapsed_time interface of
+    torch.cuda.Event. It is created with hipEventDisableSystemFence: a default event's record
+    performs a system-scope fence (cache writeback and invalidation) between the kernels it
+    separates, which perturbs the kernels that follow it. The timed loop records several per
+    step. Created in the HIP runtime torch has loaded (the one libpkv runs in)."""
+    FLAGS = 0x20000000  # hipEventDisableSystemFence; timing stays enabled
+    _hip = None
+
+    @classmethod
+    def runtime(cls):
+        if cls._hip is None:
+            with open("/proc/self/maps") as f:
+                path = next((ln.split()[-1] for ln in f if "libamdhip64" in ln), None)
+            if path is None:
+                raise RuntimeError("the HIP runtime is not loaded (import torch first)")
+            hip = ctypes.CDLL(path)
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self):
+        self.ev = ctypes.c_void_p()
+        err = self.runtime().hipEventCreateWithFlags(ctypes.byref(self.ev), self.FLAGS)
+        if err:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: error {err}")
+
+    def record(self, stream=None):
+        import torch
+        handle = (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+        err = self._hip.hipEventRecord(self.ev, ctypes.c_void_p(handle))
+        if err:
+            raise RuntimeError(f"hipEventRecord failed: error {err}")
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end` (both recorded and completed)."""
+        ms = ctypes.c_float()
+        err = self._hip.hipEventElapsedTime(ctypes.byref(ms), self.ev, end.ev)
+        if err:
+            raise RuntimeError(f"hipEventElapsedTime failed: error {err}")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.ev:
+            self._hip.hipEventDestroy(self.ev)
 
 
 def parse():
@@ -528,7 +580,7 @@ def batching_main(args, torch, pkv, W):
     for _ in range(cfg["settle_steps"] + args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(8)] for _ in range(args.steps)]
     stats = []
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -702,7 +754,7 @@ def prefill_main(args, torch, pkv, W):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(4)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for k in range(args.steps):
         step(evs[k])
@@ -821,7 +873,7 @@ def main():
         run_step(wl, torch, pkv)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(5)] for _ in range(args.steps)]
     per_step = []
     wl.cows.clear()
     t0 = time.perf_counter()
