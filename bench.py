@@ -144,7 +144,14 @@ def parse():
                          "prefill attention (a full serving step)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
-    return ap.parse_args()
+    ap.add_argument("--duplicate-prefix", action="store_true",
+                    help="prefix_shared only: the duplicated-prefix control, where every "
+                         "sequence holds private copies of the prefix blocks (same shapes, "
+                         "lengths and contents; no block is shared)")
+    args = ap.parse_args()
+    if args.duplicate_prefix and args.workload != "prefix_shared":
+        ap.error("--duplicate-prefix applies to --workload prefix_shared")
+    return args
 
 
 def kernel_source_digest(workload="llama2_7b"):
@@ -177,11 +184,12 @@ def measured_traffic(workload, digest):
 class Workload:
     """Sequences held by the C++ allocator plus device caches filled with seeded values."""
 
-    def __init__(self, name, total_steps, torch, pkv, W, plan=True):
+    def __init__(self, name, total_steps, torch, pkv, W, plan=True, duplicate_prefix=False):
         self.name = name
         self.torch = torch
+        self.duplicate_prefix = duplicate_prefix and name == "prefix_shared"
         # shared-prefix plans for the batches that share blocks
-        self.planned = plan and name in ("prefix_shared", "beam_search")
+        self.planned = plan and name in ("prefix_shared", "beam_search") and not self.duplicate_prefix
         self.gen = W  # the seeded input generators
         shape = self.shape = W.SHAPES[name]
         rng = W.rng_for(shape.seed)
@@ -216,6 +224,12 @@ class Workload:
             self.next_id = int(self.seqs[-1]) + 1
             self.beam_rng = np.random.default_rng(shape.seed + 100)
             self.group_base = (np.arange(groups) * W.BEAMS)[:, None]
+        elif name == "prefix_shared" and self.duplicate_prefix:
+            # the control: every sequence allocates its own prefix blocks (filled below with
+            # copies of one sequence's prefix)
+            for s in self.seqs:
+                self.alloc.add_seq(int(s))
+            self.alloc.append(self.seqs, lens - 1, want_slots=False)
         elif name == "prefix_shared":
             prefix = W.PREFIX_TOKENS
             parent = 10_000_000
@@ -235,6 +249,14 @@ class Workload:
         self.k_cache, self.v_cache = pkv.alloc_caches(nb, self.Hkv, self.hd, self.dt, dev)
         self.k_cache.view(-1).copy_(W.device_normal((self.k_cache.numel(),), shape.dtype, 7001))
         self.v_cache.view(-1).copy_(W.device_normal((self.v_cache.numel(),), shape.dtype, 7002))
+        if self.duplicate_prefix:  # each sequence's prefix blocks hold sequence 0's prefix
+            tab, _ = self.alloc.tables(self.seqs, W.blocks_for(int(lens.max())))
+            pb = W.PREFIX_TOKENS // 16
+            src = torch.from_numpy(np.repeat(tab[:1, :pb], self.B - 1, axis=0).reshape(-1)
+                                   .astype(np.int64)).to(dev)
+            dst = torch.from_numpy(tab[1:, :pb].reshape(-1).astype(np.int64)).to(dev)
+            self.k_cache[dst] = self.k_cache[src]
+            self.v_cache[dst] = self.v_cache[src]
         self.q = W.device_normal((self.B, self.Hq, self.hd), shape.dtype, 7003)
         self.k_new = W.device_normal((self.B, self.Hkv, self.hd), shape.dtype, 7004)
         self.v_new = W.device_normal((self.B, self.Hkv, self.hd), shape.dtype, 7005)
@@ -866,7 +888,8 @@ def main():
     if args.workload == "prefill":
         prefill_main(args, torch, pkv, W)
         return
-    wl = Workload(args.workload, args.warmup + args.steps, torch, pkv, W, plan=not args.no_plan)
+    wl = Workload(args.workload, args.warmup + args.steps, torch, pkv, W, plan=not args.no_plan,
+                  duplicate_prefix=args.duplicate_prefix)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -945,6 +968,8 @@ def main():
             "block_size": 16, "pool_blocks": wl.NB, "stream_workers": wl.W,
             "mean_context_len": round(float(np.mean([l.mean() for l in lens_per_step])), 1),
             "attn_kernel": ["", "vector", "matrix-core"][wl.kernel],
+            "planned": wl.planned,
+            "duplicate_prefix": wl.duplicate_prefix,
         },
         "tokens_per_s_per_layer": round(wl.B / (ms_per_step / 1e3), 1),
         "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4),
