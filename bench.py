@@ -461,6 +461,35 @@ def attend(wl, pkv, s, events):
     wl.last_set = s
 
 
+def bandwidth_probe(torch, pkv, waves, reps=10):
+    """Attainable read bandwidth on this part (pkv_probe_read) with `waves` waves: 2 GiB of 4 KiB
+    tiles read with the stream pass's loads and none of its arithmetic, over consecutive tiles
+    (each wave a contiguous range) and over a random permutation (the decode path's gather
+    pattern); median of `reps` launches timed with HIP events, after the timed region."""
+    nbytes = 2 << 30
+    n = nbytes // 4096
+    base = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty(waves * 64, dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(99)
+    res = {"bytes_per_launch": nbytes, "waves": waves}
+    for name, ids in (("sequential_4k_tiles", np.arange(n)), ("random_4k_tiles", rng.permutation(n))):
+        d_ids = torch.from_numpy(ids.astype(np.int32)).cuda()
+        for _ in range(2):
+            pkv.pkv_probe_read(base, d_ids, num_workers=waves, sink=sink)
+        ms = []
+        for _ in range(reps):
+            e0, e1 = TimingEvent(), TimingEvent()
+            e0.record()
+            pkv.pkv_probe_read(base, d_ids, num_workers=waves, sink=sink)
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        res[f"{name}_gbs"] = round(nbytes / (float(np.median(ms)) / 1e3) / 1e9, 1)
+    del base, sink
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(wl, torch, W, seconds):
     """The oracle (float64 NumPy, one thread) on the last step's sequences, in a seeded order,
     pass after pass until about ``seconds`` of oracle time have been spent."""
@@ -1017,6 +1046,16 @@ def main():
             "note": "measured between HIP events around the launch (includes its launch gap)",
             "pairs_every_launch": [int(c) for c in wl.cows_all if c],
         }
+    # the best of a few wave counts (the probe keeps four tiles in flight per wave; fewer,
+    # fuller waves read fastest on this part)
+    runs = [bandwidth_probe(torch, pkv, w) for w in (1024, 2048, 4096)]
+    probe = {"bytes_per_launch": runs[0]["bytes_per_launch"]}
+    for pat in ("sequential_4k_tiles", "random_4k_tiles"):
+        best = max(runs, key=lambda r: r[f"{pat}_gbs"])
+        probe[f"{pat}_gbs"] = best[f"{pat}_gbs"]
+        probe[f"{pat}_waves"] = best["waves"]
+    probe["stream_frac_of_random_probe"] = round(achieved / probe["random_4k_tiles_gbs"], 4)
+    res["attainable_probe"] = probe
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, torch, W, args.cpu_seconds)
     print(json.dumps(res), flush=True)

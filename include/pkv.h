@@ -507,6 +507,23 @@ pkv_status pkv_alloc_usage(const pkv_allocator* a, int64_t* out);
 /* Copies up to cap entries of the free list, front first, into out; returns the list length. */
 int32_t pkv_alloc_free_list(const pkv_allocator* a, int32_t* out, int32_t cap);
 
+/* ------------------------------------------------------------------------------------------ */
+/* Read-bandwidth probe (measurement support; not part of the attention path). The pages give */
+/* no hardware figures; the decode path's roofline is quoted against the published HBM peak   */
+/* and, beside it, against what this probe reaches on the same part with the stream pass's    */
+/* access pattern and none of its arithmetic.                                                 */
+/* Wave w of num_workers reads the 4096-byte tiles tile_ids[w*per .. min(n, (w+1)*per)) of    */
+/* base (per = ceil(n / num_workers); tile t at byte 4096*t; ids clamped into                 */
+/* [0, base_bytes / 4096)), 16 bytes per lane per non-temporal load, and stores the XOR of the */
+/* 32-bit words each lane read to sink[w*64 + lane].                                          */
+/*   base        device, at least 4096 bytes, 16-byte aligned (read only)                     */
+/*   tile_ids    device int32 [n]                                                              */
+/*   sink        device uint32 [num_workers * 64] (written)                                    */
+/*   num_workers a positive multiple of 4                                                      */
+/* n == 0 is a no-op. Errors: PKV_ERR_INVALID_ARG, PKV_ERR_HIP.                               */
+pkv_status pkv_probe_read(const void* base, size_t base_bytes, const int32_t* tile_ids,
+                          int32_t n, int32_t num_workers, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

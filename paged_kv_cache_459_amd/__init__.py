@@ -14,4 +14,5 @@ from .api import (BLOCK_SIZE, BlockAllocator, alloc_caches, cache_bytes,  # noqa
                   pkv_decode_planned_workspace_bytes, pkv_decode_stream,
                   pkv_decode_stream_workspace_bytes,
                   pkv_decode_workspace_bytes, pkv_dtype, pkv_prefill_attn, pkv_prefill_plan,
-                  pkv_prefill_workspace_bytes, pkv_set_attn_kernel, pkv_write, split_workspace)
+                  pkv_prefill_workspace_bytes, pkv_probe_read, pkv_set_attn_kernel, pkv_write,
+                  split_workspace)

@@ -53,6 +53,7 @@ SIGNATURES = {
                           c_vp]),
     "pkv_copy_blocks": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                 c_vp]),
+    "pkv_probe_read": (c_i32, [c_vp, c_sz, c_vp, c_i32, c_i32, c_vp, c_vp]),
     "pkv_decode_attn": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                 c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_vp, c_sz, c_vp]),
     "pkv_decode_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32]),

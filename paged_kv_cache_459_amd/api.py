@@ -114,6 +114,23 @@ def pkv_copy_blocks(k_cache, v_cache, src, dst, *, num_kv_heads, head_dim):
                               _stream(k_cache.device)), "pkv_copy_blocks")
 
 
+def pkv_probe_read(base, tile_ids, *, num_workers, sink=None):
+    """Read-bandwidth probe (see include/pkv.h): wave w reads the 4096-byte tiles
+    tile_ids[w*per ..] of base with the stream pass's loads and writes the XOR of what each lane
+    read to sink[w*64 + lane]. Returns sink (uint32 values in an int32 tensor [W*64])."""
+    _need(base, "base", device=base.device)
+    _need(tile_ids, "tile_ids", dtype=torch.int32, device=base.device)
+    if sink is None:
+        sink = torch.empty(num_workers * 64, dtype=torch.int32, device=base.device)
+    _need(sink, "sink", dtype=torch.int32, device=base.device)
+    if sink.numel() < num_workers * 64:
+        raise ValueError("sink must hold num_workers * 64 words")
+    check(lib.pkv_probe_read(_ptr(base), base.numel() * base.element_size(), _ptr(tile_ids),
+                             tile_ids.numel(), num_workers, _ptr(sink), _stream(base.device)),
+          "pkv_probe_read")
+    return sink
+
+
 def pkv_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim, max_context_len,
                                dtype):
     return int(lib.pkv_decode_workspace_bytes(batch, num_q_heads, num_kv_heads, head_dim,

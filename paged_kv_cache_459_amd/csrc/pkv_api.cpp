@@ -6,6 +6,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <climits>
 #include <cstdlib>
 #include <cstdio>
 #include <cstring>
@@ -266,6 +267,21 @@ pkv_status pkv_write(const void* k, const void* v, void* k_cache, void* v_cache,
   }
   pkv::WriteParams p{k, v, k_cache, v_cache, slot_mapping, T, Hkv, hd, NB};
   return pkv::launch_write(p, dtype, hs) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+pkv_status pkv_probe_read(const void* base, size_t base_bytes, const int32_t* tile_ids,
+                          int32_t n, int32_t num_workers, uint32_t* sink, void* stream) {
+  if (n < 0 || num_workers <= 0 || num_workers % pkv::kWaves != 0) return PKV_ERR_INVALID_ARG;
+  if (n == 0) return PKV_OK;
+  const size_t tiles = base_bytes / 4096;
+  if (!base || !tile_ids || !sink || tiles == 0 || tiles > static_cast<size_t>(INT32_MAX) ||
+      !aligned16(base) || (reinterpret_cast<uintptr_t>(tile_ids) & 3u) ||
+      (reinterpret_cast<uintptr_t>(sink) & 3u))
+    return PKV_ERR_INVALID_ARG;
+  return pkv::launch_probe_read(base, static_cast<int32_t>(tiles), tile_ids, n, num_workers, sink,
+                                static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PKV_OK
+             : PKV_ERR_HIP;
 }
 
 pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst,

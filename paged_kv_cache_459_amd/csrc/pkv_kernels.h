@@ -144,6 +144,10 @@ hipError_t launch_merge(const StreamParams& p, int32_t dtype, int32_t kernel,
 hipError_t launch_shared(const StreamParams& p, int32_t dtype, int32_t kernel,
                          hipStream_t stream);
 
+// Read-bandwidth probe (pkv_probe.hip): tiles ids[0..n) of base, max_tile tiles of 4096 bytes.
+hipError_t launch_probe_read(const void* base, int32_t max_tile, const int32_t* ids, int32_t n,
+                             int32_t num_workers, uint32_t* sink, hipStream_t stream);
+
 // Records the failing step and the HIP error text for pkv_last_error(); returns err.
 hipError_t note_error(const char* what, hipError_t err);
 

@@ -179,3 +179,15 @@ def test_one_hip_runtime_per_process():
     for name in ("libamdhip64", "libhsa-runtime64"):
         files = {ln.split()[-1] for ln in maps if name in ln}
         assert len(files) == 1, files
+
+
+def test_probe_argument_errors():
+    """The read-bandwidth probe rejects bad shapes before any HIP call."""
+    from paged_kv_cache_459_amd import lib
+    _b, p = _fake()
+    assert lib.pkv_probe_read(p, 4096, p, 4, 6, p, None) == 1  # W not a multiple of 4
+    assert lib.pkv_probe_read(p, 4096, p, 4, 0, p, None) == 1
+    assert lib.pkv_probe_read(p, 4096, p, -1, 8, p, None) == 1
+    assert lib.pkv_probe_read(p, 4095, p, 4, 8, p, None) == 1  # no whole tile
+    assert lib.pkv_probe_read(None, 4096, p, 4, 8, p, None) == 1
+    assert lib.pkv_probe_read(p, 4096, p, 0, 8, p, None) == 0  # n == 0: no-op
