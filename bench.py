@@ -123,8 +123,11 @@ class TimingEvent:
         return ms.value
 
     def __del__(self):
-        if self._hip is not None and self.ev:
-            self._hip.hipEventDestroy(self.ev)
+        try:
+            if self._hip is not None and self.ev:
+                self._hip.hipEventDestroy(self.ev)
+        except Exception:  # interpreter shutdown: the runtime may already be gone
+            pass
 
 
 def parse():
