@@ -6,7 +6,8 @@ One step = one decode step of every sequence in the batch, through the whole pat
      sequences whose last block is full) and returns the new tokens' slots;
   2. bring the block tables (pinned host copy: the entries of the blocks just opened) and
      the lengths up to date and copy them, with the slots, to the device on a copy stream
-     (double-buffered, so the copy overlaps the previous step's kernels);
+     (double-buffered, so the copy overlaps the previous step's kernels; the host waits
+     for it before launching the kernels, so the compute stream has no cross-stream wait);
   3. + 4. the decode step's two kernels (pkv_decode_append_attn): the stream pass, which
      attends with each sequence's new K/V taken from the step's input rows (every wave
      streams an equal share of the batch's K/V tiles), then the merge pass: the log-sum-exp
@@ -401,8 +402,9 @@ def run_step(wl, torch, pkv, events=None):
         else:
             wl.dev[s].copy_(wl.pin[s], non_blocking=True)
         wl.copied[s].record(wl.copy_stream)
-    compute = torch.cuda.current_stream()
-    compute.wait_event(wl.copied[s])
+    # The host waits for the small upload (the device is still on the previous step), so the
+    # compute stream needs no cross-stream wait: a device-side wait measured 5 us per step.
+    wl.copied[s].synchronize()
     attend(wl, pkv, s, events)  # no copy-on-write in a decode loop without forks
     return lens_h.copy(), (tables_h.copy() if wl.planned else None), wl.planned_skip()
 
@@ -415,7 +417,7 @@ def run_beam_step(wl, torch, pkv, s, events):
     with torch.cuda.stream(wl.copy_stream):  # tables, lengths, pairs (and plan) to the device
         wl.dev[s][:n].copy_(wl.pin[s][:n], non_blocking=True)
         wl.copied[s].record(wl.copy_stream)
-    torch.cuda.current_stream().wait_event(wl.copied[s])
+    wl.copied[s].synchronize()  # as in run_step: waited on the host, not on the device
     if events is not None:
         events[0].record()
     if ncow:  # copy-on-write: the shared blocks appenders moved off, copied to their new blocks
