@@ -110,7 +110,12 @@ class TimingEvent:
 
     def record(self, stream=None):
         import torch
-        handle = (stream if stream is not None else torch.cuda.current_stream()).cuda_stream
+        if stream is not None:
+            handle = stream.cuda_stream
+        elif hasattr(torch._C, "_cuda_getCurrentRawStream"):  # no Stream object per record
+            handle = torch._C._cuda_getCurrentRawStream(torch.cuda.current_device())
+        else:
+            handle = torch.cuda.current_stream().cuda_stream
         err = self._hip.hipEventRecord(self.ev, ctypes.c_void_p(handle))
         if err:
             raise RuntimeError(f"hipEventRecord failed: error {err}")

@@ -29,8 +29,16 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+# The current stream's raw handle, without building a torch Stream object per call (a few
+# microseconds each, which a host-bound decode loop pays several times per step).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(device):
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    if _raw_stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    return ctypes.c_void_p(_raw_stream(idx))
 
 
 def _need(t, name, dtype=None, device=None):
