@@ -26,7 +26,8 @@ ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 HIP_SOURCES = ["pkv_attn.hip", "pkv_write.hip", "pkv_prefill.hip", "pkv_probe.hip"]
 HOST_SOURCES = ["pkv_api.cpp", "pkv_alloc.cpp", "pkv_plan.cpp"]
 
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result", f"-I{INCLUDE}"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result", "-Werror=inline-asm",
+          f"-I{INCLUDE}"]
 # Code-object v5: the library runs inside PyTorch's bundled HIP runtime, which can be older than
 # this compiler (ROCm 7.0 beside a ROCm 7.2 toolchain); v5 is the version that runtime
 # generation itself emits and loads.

@@ -141,12 +141,15 @@ __device__ __forceinline__ uint4 keep_tokens(uint4 v, int t0, int valid) {
 // One lane's 16 bytes from global memory straight into LDS (gfx950 global_load_lds_dwordx4):
 // the wave's 64 lanes fill the 1 KB at LDS byte address `lds` (wave-uniform, through M0) in
 // lane order. Issued as inline assembly so that the compiler neither tracks it nor adds its
-// own (conservative: every later LDS read) waits; the kernel waits on vmcnt itself.
+// own (conservative: every later LDS read) waits; the kernel waits on vmcnt itself. M0 is an
+// input operand bound to that register ("{m0}"), so the compiler sets it and knows its value;
+// the statement only reads it. The s_nop is the one wait state an LDS DMA needs after an SALU
+// write of M0, which the compiler cannot see through the statement.
 __device__ __forceinline__ void load_lds16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
-               : "v"(src), "s"(lds)
-               : "memory", "m0");
+               : "v"(src), "{m0}"(lds)
+               : "memory");
 }
 
 // Barrier of the stage loop: orders LDS only (a full __syncthreads would also wait for every
