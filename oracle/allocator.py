@@ -130,9 +130,16 @@ class BlockAllocator:
         for s in seqs:
             if s not in self.blocks:
                 raise AllocError("UNKNOWN_SEQ")
-        total = 0
+        # Count what the loop below takes: sharers of a partly filled block that append in
+        # this call move off it in argument order, so the last of them finds the refcount back
+        # at 1 and writes in place (no copy).
+        total, moved = 0, {}
         for s, t in zip(seqs, ntok):
             cow, new = self._needs(s, t)
+            if cow:
+                b = self.blocks[s][-1]
+                cow = self.ref[b] - moved.get(b, 0) > 1
+                moved[b] = moved.get(b, 0) + int(cow)
             total += int(cow) + new
         if total > len(self.free):
             raise AllocError("OUT_OF_BLOCKS")

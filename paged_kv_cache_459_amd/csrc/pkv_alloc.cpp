@@ -68,6 +68,7 @@ struct pkv_allocator {
   std::unordered_map<int64_t, Seq> seqs;
   uint64_t calls = 0;             // append calls so far (stamps Seq::mark)
   std::vector<Seq*> batch;        // reused per append call
+  std::unordered_map<int32_t, int32_t> moved;  // reused per append call (copy-on-write count)
   // prefix cache
   std::unordered_multimap<uint64_t, int64_t> index;  // content hash -> node
   std::unordered_map<int64_t, Node> nodes;
@@ -222,11 +223,21 @@ pkv_status append_impl(pkv_allocator* a, int32_t n, const int64_t* seqs, const i
   }
   if (dup) return PKV_ERR_INVALID_ARG;
   if (unknown) return PKV_ERR_UNKNOWN_SEQ;
+  // The count follows the loop below: sharers of a partly filled block that append in this
+  // call move off it one by one, so the last of them (refcount back to 1 by then) writes in
+  // place and takes no copy. `moved` holds, per such block, the sharers already counted off.
   int64_t total = 0;
+  std::unordered_map<int32_t, int32_t>& moved = a->moved;
+  moved.clear();
   for (int32_t k = 0; k < n; ++k) {
     bool cow;
     int64_t fresh;
     a->needs(*ptr[k], ntok[k], &cow, &fresh);
+    if (cow) {
+      int32_t& gone = moved[ptr[k]->blocks.back()];
+      cow = a->ref[ptr[k]->blocks.back()] - gone > 1;
+      gone += cow ? 1 : 0;
+    }
     total += (cow ? 1 : 0) + fresh;
   }
   if (total > a->nfree) return PKV_ERR_OUT_OF_BLOCKS;

@@ -147,6 +147,31 @@ def test_create_errors_and_out_of_blocks_atomic():
     assert e.value.status == 1
 
 
+@pytest.mark.parametrize("free_after", [2, 3])
+def test_sharers_of_a_partial_block_in_a_tight_pool(free_after):
+    # four beams share a partly filled block; appending one token each takes three copies
+    # (the last sharer writes in place), so three free blocks hold the batch and two do not
+    nb = 2 + 3 + free_after
+    nat, ora = Native(nb, BS), Oracle(nb, BS)
+    for a in (nat, ora):
+        a.add_seq(0)
+        a.append([0], [20])
+        for c in (1, 2, 3):
+            a.fork(0, c)
+        a.add_seq(9)
+        a.append([9], [3 * BS])
+    same_state(nat, ora, [0, 1, 2, 3, 9])
+    r_n, r_o = both(lambda: nat.append([0, 1, 2, 3], [1, 1, 1, 1]),
+                    lambda: ora.append([0, 1, 2, 3], [1, 1, 1, 1]))
+    if free_after == 3:
+        assert r_o is not None and len(r_o[1]) == 3
+        assert [tuple(c) for c in r_n[1].tolist()] == r_o[1]
+        assert r_n[0].tolist() == r_o[0]
+    else:
+        assert r_o is None
+    same_state(nat, ora, [0, 1, 2, 3, 9])
+
+
 def test_marked_tables_flag_exactly_the_shared_blocks():
     """pkv_alloc_tables_marked: the pages' three tables A/B/C ([P1] §二: blocks 1, 2 shared by
     all three, block 3 by A and B) come back with the shared-block mark on exactly the

@@ -211,3 +211,43 @@ def test_error_codes():
     with pytest.raises(AllocError) as e:
         a.tables([1], 2)
     assert e.value.code == "INVALID_ARG"
+
+
+def _beams_on_a_partial_block(nb, free_after):
+    """One sequence of 20 tokens (its second block holds 4) forked into 4 beams that share
+    both blocks, in a pool with `free_after` blocks left free."""
+    a = BlockAllocator(nb, BS)
+    a.add_seq(0)
+    a.append([0], [20])
+    for c in (1, 2, 3):
+        a.fork(0, c)
+    filler = nb - 2 - free_after
+    if filler:
+        a.add_seq("fill")
+        a.append(["fill"], [filler * BS])
+    assert a.num_free() == free_after and a.refcount(a.blocks[0][1]) == 4
+    return a
+
+
+def test_sharers_of_a_partial_block_need_one_copy_fewer_than_they_are():
+    # Copy-on-write moves an appender off a shared, partly filled block while others still
+    # hold it; the last sharer to append finds it no longer shared and writes in place. Four
+    # beams appending one token each therefore take exactly three blocks: a pool with three
+    # free blocks holds the batch.
+    a = _beams_on_a_partial_block(nb=8, free_after=3)
+    shared = a.blocks[0][1]
+    slots, cows = a.append([0, 1, 2, 3], [1, 1, 1, 1])
+    assert [src for src, _ in cows] == [shared] * 3 and a.num_free() == 0
+    assert a.blocks[3][1] == shared and a.refcount(shared) == 1
+    assert slots[3] == shared * BS + 4  # the last sharer writes into the block itself
+    assert len({s // BS for s in slots}) == 4
+
+
+def test_sharers_of_a_partial_block_fail_atomically_one_block_short():
+    a = _beams_on_a_partial_block(nb=7, free_after=2)
+    state = (a.free_list(), list(a.ref), dict(a.length), {s: list(b) for s, b in a.blocks.items()})
+    with pytest.raises(AllocError) as e:
+        a.append([0, 1, 2, 3], [1, 1, 1, 1])
+    assert e.value.code == "OUT_OF_BLOCKS"
+    assert (a.free_list(), list(a.ref), dict(a.length),
+            {s: list(b) for s, b in a.blocks.items()}) == state
