@@ -119,8 +119,8 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, con
 
 /* ------------------------------------------------------------------------------------------ */
 /* Decode attention.                                                                         */
-/* [P1] §三 步驟三 (last step) and §五 ("Attention Kernel ... 用塊表計算注意力"); [P2]         */
-/* "PagedAttention 的核心原理": each sequence's KV is logically contiguous but physically     */
+/* [P1] §三 步驟三 (last step) and §五 (the attention-kernel row of the component table);     */
+/* [P2] "PagedAttention 的核心原理": each sequence's KV is logically contiguous but physically */
 /* scattered; attention is computed by finding all previous KV through the block table. The  */
 /* pages give no formula; ours is scaled dot-product attention over the n = context_lens[i]   */
 /* tokens of sequence i (the token just written included):                                    */
@@ -145,7 +145,7 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, con
 /*   scale         the softmax scale (1/sqrt(hd) in the usual model).                          */
 /*   workspace     device scratch of at least pkv_decode_workspace_bytes(...) bytes, caller    */
 /*                 owned; contents on entry are ignored. May be NULL only when that size is 0. */
-/* Supported: hd in {64,128}, bs == 16, Hq % Hkv == 0, Hq + Hkv <= 65535, dtype f32/f16/bf16. */
+/* Supported: hd in {64,128}, bs == 16, Hq % Hkv == 0, Hq <= 32767, dtype f32/f16/bf16.       */
 /* Batches of more than 8192 sequences (or of more tiles than int32 positions allow) run as */
 /* several stream+merge launches over consecutive row ranges, reusing the workspace in order.*/
 /* The launch size comes from the calling thread's current HIP device.                        */

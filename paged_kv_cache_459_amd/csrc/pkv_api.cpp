@@ -141,7 +141,9 @@ pkv_status validate_decode(const void* out, const void* q, const void* k_cache,
       max_ctx < 0 || static_cast<int64_t>(max_blocks) * kBlockSize < max_ctx ||
       static_cast<int64_t>(NB) * kBlockSize >= (int64_t{1} << 31) || !std::isfinite(scale))
     return PKV_ERR_INVALID_ARG;
-  if (Hq + Hkv > 65535) return PKV_ERR_INVALID_ARG;  // merge grid rows: q heads + kv heads
+  // Head slots travel in the upper half of a signed 32-bit tile word (at most 32767), and the
+  // merge grid's rows are q heads plus kv heads (at most 65535): Hq <= 32767 covers both.
+  if (Hq > 32767) return PKV_ERR_INVALID_ARG;
   if (B == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return PKV_ERR_INVALID_ARG;
@@ -660,7 +662,7 @@ pkv_status merge_impl(void* out, const void* k_new, const void* v_new, void* k_c
                       size_t workspace_bytes, int32_t B, int32_t Hq, int32_t Hkv, int32_t hd,
                       pkv_dtype dtype, int32_t num_workers, void* stream) {
   if (!dtype_ok(dtype) || !head_dim_ok(hd)) return PKV_ERR_UNSUPPORTED;
-  if (B < 0 || B > kMaxBatch || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Hq + Hkv > 65535 ||
+  if (B < 0 || B > kMaxBatch || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Hq > 32767 ||
       num_workers <= 0 || num_workers % pkv::kWaves != 0)
     return PKV_ERR_INVALID_ARG;
   if (B == 0) return PKV_OK;

@@ -138,7 +138,6 @@ __device__ __forceinline__ uint2 pinned(uint2 v) {
   asm volatile("" : "+v"(v.x), "+v"(v.y));
   return v;
 }
-__device__ __forceinline__ void settle(uint32_t& v) { asm volatile("" : "+v"(v)); }
 
 // Element e (lane-dependent) of a 16-byte chunk of EB-byte elements replaced by `bits`.
 template <int EB>

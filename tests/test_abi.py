@@ -115,6 +115,9 @@ def test_decode_argument_errors():
     assert call(B=0) == 0
     assert call(NB=1 << 27) == 1  # NB * 16 >= 2^31
     assert call(Hq=1 << 16, Hkv=1 << 16) == 1  # more q heads than a grid dimension holds
+    # head slots are packed into the upper half of a signed tile word: at most 32767 q heads
+    assert call(Hq=32768, Hkv=32768) == 1
+    assert call(Hq=32768, Hkv=1) == 1
     mis = ctypes.c_void_p(p.value + 8)
     assert lib.pkv_decode_attn(mis, p, p, p, p, p, 2, 4, 2, 128, 16, 8, 4, 64, 0.1, 2, None, 0,
                                None) == 1
