@@ -71,7 +71,8 @@ enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 };
 const char* pkv_status_string(pkv_status status);
 
 /* Detail of the most recent PKV_ERR_HIP returned on the calling thread: which launch or runtime
- * call failed and the HIP error text. Thread-local storage owned by the library, valid until the
+ * call failed and the HIP error text (also set with the PKV_ERR_WORKSPACE of
+ * pkv_decode_append_attn_noalloc). Thread-local storage owned by the library, valid until the
  * thread's next failing call; "" if none. */
 const char* pkv_last_error(void);
 
@@ -179,6 +180,27 @@ pkv_status pkv_decode_append_attn(void* out, const void* q, const void* k_new,
                                   int32_t NB, int32_t max_blocks, int32_t max_context_len,
                                   float scale, pkv_dtype dtype, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/* pkv_decode_append_attn for callers that cannot allocate device memory (code under HIP graph */
+/* capture, tight serving loops, harnesses that forbid allocation): the same arguments without */
+/* the workspace, the same kernels and the same results, bit for bit. The stream/merge scratch */
+/* is a file-scope device array of the library, 40 MiB on each GPU the library runs on, held   */
+/* until the process ends; its address is looked up once per device on the first call there.  */
+/* The call allocates nothing (no hipMalloc, no host-side allocation either). Every call on a  */
+/* GPU shares that GPU's array: calls that overlap on one GPU (on different streams, or from   */
+/* different threads without ordering) race and give undefined results; calls ordered on one  */
+/* stream are safe (the scratch's contents on entry are ignored). PKV_CHECK index validation,  */
+/* which needs host buffers and a synchronization, is not performed by this call.              */
+/* Errors: as pkv_decode_append_attn; PKV_ERR_WORKSPACE when the shape needs more scratch than */
+/* the array holds (pkv_decode_workspace_bytes > 40 MiB; pkv_last_error() says how much);      */
+/* PKV_ERR_HIP if the array's address cannot be obtained.                                      */
+pkv_status pkv_decode_append_attn_noalloc(void* out, const void* q, const void* k_new,
+                                          const void* v_new, void* k_cache, void* v_cache,
+                                          const int32_t* block_tables,
+                                          const int32_t* context_lens, int32_t B, int32_t Hq,
+                                          int32_t Hkv, int32_t hd, int32_t bs, int32_t NB,
+                                          int32_t max_blocks, int32_t max_context_len,
+                                          float scale, pkv_dtype dtype, void* stream);
 
 /* ---- Shared-prefix plans ([P1] §二 "解決三大問題" and [P2] "共享和复用": sequences with a   */
 /* ---- common prefix, such as a system prompt or beam candidates, point at the same physical  */

@@ -68,6 +68,9 @@ SIGNATURES = {
     "pkv_decode_append_attn": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
                                        c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32,
                                        c_i32, c_vp, c_sz, c_vp]),
+    "pkv_decode_append_attn_noalloc": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                               c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                               c_i32, c_f32, c_i32, c_vp]),
     "pkv_decode_append_merge": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
                                         c_i32, c_vp, c_sz, c_i32, c_i32, c_i32, c_i32, c_i32,
                                         c_i32, c_vp]),

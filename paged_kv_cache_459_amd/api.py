@@ -223,6 +223,23 @@ def pkv_decode_append_attn(q, k_new, v_new, k_cache, v_cache, block_tables, cont
     return out
 
 
+def pkv_decode_append_attn_noalloc(q, k_new, v_new, k_cache, v_cache, block_tables,
+                                   context_lens, *, num_kv_heads, scale, max_context_len, out):
+    """pkv_decode_append_attn on the library's own per-device scratch: no workspace, and
+    nothing is allocated here either (out is required). Calls that overlap on one GPU race."""
+    _need(out, "out", dtype=q.dtype, device=q.device)
+    out, B, hq, hd, nb, mb = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
+                                          num_kv_heads, out)
+    _new_args(q, k_new, v_new, num_kv_heads)
+    check(lib.pkv_decode_append_attn_noalloc(_ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                             _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                             _ptr(context_lens), B, hq, num_kv_heads, hd,
+                                             BLOCK_SIZE, nb, mb, max_context_len, float(scale),
+                                             pkv_dtype(q), _stream(q.device)),
+          "pkv_decode_append_attn_noalloc")
+    return out
+
+
 def pkv_decode_append_stream(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, *,
                              num_kv_heads, scale, max_context_len, num_workers, workspace,
                              out=None):

@@ -20,6 +20,8 @@ namespace {
 thread_local char g_last_error[256] = "";
 }  // namespace
 
+void pkv::note_message(const char* what) { snprintf(g_last_error, sizeof g_last_error, "%s", what); }
+
 hipError_t pkv::note_error(const char* what, hipError_t err) {
   if (err != hipSuccess)
     snprintf(g_last_error, sizeof g_last_error, "%s: %s (%d)", what, hipGetErrorString(err),
@@ -193,7 +195,7 @@ pkv_status stream_impl(void* out, const void* q, const void* k_new, const void* 
                        int32_t Hq, int32_t Hkv, int32_t hd, int32_t bs, int32_t NB,
                        int32_t max_blocks, int32_t max_ctx, float scale, pkv_dtype dtype,
                        int32_t W, void* workspace, size_t workspace_bytes, void* stream,
-                       bool merge_after) {
+                       bool merge_after, bool index_checks = true) {
   pkv_status st = validate_decode(out, q, k_cache, v_cache, block_tables, context_lens, B, Hq,
                                   Hkv, hd, bs, NB, max_blocks, max_ctx, scale, dtype);
   if (st != PKV_OK) return st;
@@ -207,7 +209,7 @@ pkv_status stream_impl(void* out, const void* q, const void* k_new, const void* 
   if (!workspace || workspace_bytes < L.bytes) return PKV_ERR_WORKSPACE;
   if (!aligned16(workspace)) return PKV_ERR_INVALID_ARG;
   auto hs = static_cast<hipStream_t>(stream);
-  if (check_mode()) {
+  if (index_checks && check_mode()) {
     st = check_decode_indices(block_tables, context_lens, B, NB, max_blocks, max_ctx, hs);
     if (st != PKV_OK) return st;
   }
@@ -570,7 +572,7 @@ pkv_status decode_all(void* out, const void* q, const void* k_new, const void* v
                       const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
                       int32_t hd, int32_t bs, int32_t NB, int32_t max_blocks,
                       int32_t max_context_len, float scale, pkv_dtype dtype, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      size_t workspace_bytes, void* stream, bool index_checks = true) {
   pkv_status st = validate_decode(out, q, k_cache, v_cache, block_tables, context_lens, B, Hq,
                                   Hkv, hd, bs, NB, max_blocks, max_context_len, scale, dtype);
   if (st != PKV_OK || B == 0) return st;
@@ -594,7 +596,8 @@ pkv_status decode_all(void* out, const void* q, const void* k_new, const void* v
                      v_new ? static_cast<const char*>(v_new) + i0 * new_bytes : nullptr,
                      k_cache, v_cache, block_tables + static_cast<size_t>(i0) * max_blocks,
                      context_lens + i0, n, Hq, Hkv, hd, bs, NB, max_blocks, max_context_len,
-                     scale, dtype, W, workspace, workspace_bytes, stream, /*merge_after=*/true);
+                     scale, dtype, W, workspace, workspace_bytes, stream, /*merge_after=*/true,
+                     index_checks);
     if (st != PKV_OK) return st;
   }
   return PKV_OK;
@@ -626,6 +629,34 @@ pkv_status pkv_decode_append_attn(void* out, const void* q, const void* k_new,
   return decode_all(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, B, Hq,
                     Hkv, hd, bs, NB, max_blocks, max_context_len, scale, dtype, workspace,
                     workspace_bytes, stream);
+}
+
+pkv_status pkv_decode_append_attn_noalloc(void* out, const void* q, const void* k_new,
+                                          const void* v_new, void* k_cache, void* v_cache,
+                                          const int32_t* block_tables,
+                                          const int32_t* context_lens, int32_t B, int32_t Hq,
+                                          int32_t Hkv, int32_t hd, int32_t bs, int32_t NB,
+                                          int32_t max_blocks, int32_t max_context_len,
+                                          float scale, pkv_dtype dtype, void* stream) {
+  if (B > 0 && (!k_new || !v_new)) return PKV_ERR_INVALID_ARG;
+  pkv_status st = validate_decode(out, q, k_cache, v_cache, block_tables, context_lens, B, Hq,
+                                  Hkv, hd, bs, NB, max_blocks, max_context_len, scale, dtype);
+  if (st != PKV_OK || B == 0) return st;
+  const size_t need = pkv_decode_workspace_bytes(B, Hq, Hkv, hd, max_context_len, dtype);
+  if (need > pkv::kStaticScratchBytes) {
+    char msg[160];
+    snprintf(msg, sizeof msg,
+             "pkv_decode_append_attn_noalloc: this shape needs %zu bytes of scratch, more than "
+             "the %zu the library holds per device",
+             need, pkv::kStaticScratchBytes);
+    pkv::note_message(msg);
+    return PKV_ERR_WORKSPACE;
+  }
+  void* scratch = pkv::static_scratch();
+  if (scratch == nullptr) return PKV_ERR_HIP;
+  return decode_all(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, B, Hq,
+                    Hkv, hd, bs, NB, max_blocks, max_context_len, scale, dtype, scratch,
+                    pkv::kStaticScratchBytes, stream, /*index_checks=*/false);
 }
 
 pkv_status pkv_decode_stream(void* out, const void* q, const void* k_cache, const void* v_cache,

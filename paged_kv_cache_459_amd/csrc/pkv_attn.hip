@@ -42,7 +42,36 @@
 
 #include "pkv_kernels.h"
 
+// Device scratch of the allocation-free decode step (pkv_decode_append_attn_noalloc): one copy
+// per GPU, held until the process ends. Host code never passes this name to a kernel (on the
+// host it is only a stand-in for the symbol); it uses the address static_scratch() obtains
+// from the runtime for the current device.
+static __device__ __align__(256) char scratch[pkv::kStaticScratchBytes];
+
 namespace pkv {
+
+void* static_scratch() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (note_error("hipGetDevice", hipGetDevice(&dev)) != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    (void)note_error("static scratch: device index", hipErrorInvalidDevice);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {  // once per device, with that device current
+    void* ptr = nullptr;
+    if (note_error("hipGetSymbolAddress(scratch)",
+                   hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess ||
+        ptr == nullptr)
+      return nullptr;
+    addr[dev] = ptr;
+  }
+  return addr[dev];
+}
+
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();

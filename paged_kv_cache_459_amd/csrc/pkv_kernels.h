@@ -150,6 +150,17 @@ hipError_t launch_probe_read(const void* base, int32_t max_tile, const int32_t* 
 
 // Records the failing step and the HIP error text for pkv_last_error(); returns err.
 hipError_t note_error(const char* what, hipError_t err);
+// Records a message (no HIP error) for pkv_last_error().
+void note_message(const char* what);
+
+// Bytes of the file-scope device scratch array of the allocation-free decode step: enough for
+// the stream/merge workspace of every supported shape at the default worker count of a
+// 256-compute-unit part (at most 2048 matrix-core waves x 2 cells x 16 q heads x (128 + 2)
+// floats, plus 8193 prefix sums: 32.6 MiB).
+constexpr size_t kStaticScratchBytes = size_t{40} << 20;
+// Device address of that array on the current device (looked up once per device); nullptr on
+// a HIP error (recorded for pkv_last_error()).
+void* static_scratch();
 
 // Which kernel the stream pass runs for this shape and request (kVector or kMatrix).
 int32_t select_kernel(int32_t dtype, int32_t G, int32_t request);
