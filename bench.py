@@ -99,6 +99,7 @@ class TimingEvent:
             hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                 ctypes.c_void_p]
             hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
             cls._hip = hip
         return cls._hip
 
@@ -120,6 +121,12 @@ class TimingEvent:
         if err:
             raise RuntimeError(f"hipEventRecord failed: error {err}")
 
+    def synchronize(self):
+        """Block the host until the work recorded before this event has completed."""
+        err = self._hip.hipEventSynchronize(self.ev)
+        if err:
+            raise RuntimeError(f"hipEventSynchronize failed: error {err}")
+
     def elapsed_time(self, end):
         """Milliseconds from this event to `end` (both recorded and completed)."""
         ms = ctypes.c_float()
@@ -136,10 +143,26 @@ class TimingEvent:
             pass
 
 
+def ms_stats(ms):
+    """Mean, median, p10 and p90 of per-launch milliseconds."""
+    a = np.asarray(ms, dtype=np.float64)
+    return {"mean": round(float(a.mean()), 4), "median": round(float(np.median(a)), 4),
+            "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4), "n": int(a.size)}
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="record the per-kernel timing events on every n-th timed step (each "
+                         "event is a marker packet between kernels; the wall-clock step time "
+                         "is taken over every step)")
+    ap.add_argument("--flush", action="store_true",
+                    help="before each timed step, write a 1 GiB scratch buffer (flushes the L2s "
+                         "and the 256 MB last-level cache); value and ms_per_step then come from "
+                         "the step's kernels' event times instead of the wall clock")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama2_7b", choices=WORKLOADS)
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 vector, 2 matrix-core")
@@ -284,7 +307,9 @@ class Workload:
         self.dev_views = [self._views(t) for t in self.dev]
         self.copy_stream = torch.cuda.Stream()
         self.copied = [torch.cuda.Event() for _ in range(2)]
-        self.done = [torch.cuda.Event() for _ in range(2)]
+        # a step's completion (its device buffer set may then be refilled): fence-less events,
+        # like the timing ones, so the marker between steps does no cache writeback
+        self.done = [TimingEvent() for _ in range(2)]
         self.step_no = 0
         # Both sets start from a full export of the allocator's tables; after that each step
         # only adds the blocks it opened (tables only grow in a decode loop without forks).
@@ -974,25 +999,31 @@ def main():
         run_step(wl, torch, pkv)
     torch.cuda.synchronize()
 
-    evs = [[TimingEvent() for _ in range(5)] for _ in range(args.steps)]
+    # per-kernel timing events on every n-th timed step (every step with --flush)
+    every = 1 if args.flush else max(1, args.event_every)
+    timed = [k for k in range(args.steps) if k % every == 0]
+    evs = {k: [TimingEvent() for _ in range(5)] for k in timed}
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if args.flush else None
     per_step = []
     wl.cows.clear()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        per_step.append(run_step(wl, torch, pkv, evs[k]))
+        if scratch is not None:  # before the step's events: not part of the kernels' times
+            scratch.fill_(k & 0xFF)
+        per_step.append(run_step(wl, torch, pkv, evs.get(k)))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     # events a step does not record stand for the one before them (no copy, no shared pass)
-    for e in evs:
+    for e in evs.values():
         if not wl.beam:
             e[1] = e[0]
         if not wl.planned:
             e[2] = e[1]
-    copy_ms = [e[0].elapsed_time(e[1]) if wl.beam else 0.0 for e in evs]
-    shared_ms = [e[1].elapsed_time(e[2]) if wl.planned else 0.0 for e in evs]
-    part_ms = [e[2].elapsed_time(e[3]) for e in evs]
-    merge_ms = [e[3].elapsed_time(e[4]) for e in evs]
+    copy_ms = [evs[k][0].elapsed_time(evs[k][1]) if wl.beam else 0.0 for k in timed]
+    shared_ms = [evs[k][1].elapsed_time(evs[k][2]) if wl.planned else 0.0 for k in timed]
+    part_ms = [evs[k][2].elapsed_time(evs[k][3]) for k in timed]
+    merge_ms = [evs[k][3].elapsed_time(evs[k][4]) for k in timed]
     # The last tables sent must be exactly what the allocator exports (for the decode loop,
     # whose tables only gain entries, this checks every incremental update).
     final_tables = wl.host_views[wl.last_set][2].copy()
@@ -1011,11 +1042,19 @@ def main():
     kv_shared = [wl.unique_kv_bytes(lens, unmarked(final_tables if t is None else t), upto=sk)
                  for lens, t, sk in per_step]
     kv_private = [a - b for a, b in zip(kv, kv_shared)]
-    algo = [b + wl.qo_bytes() for b in kv_private]
-    ms_per_step = wall / args.steps * 1e3
-    value = sum(kv) / wall / 1e9
-    achieved = sum(algo) / (sum(part_ms) / 1e3) / 1e9
+    algo = [kv_private[k] + wl.qo_bytes() for k in timed]
     attn_ms = [a + b + c for a, b, c in zip(shared_ms, part_ms, merge_ms)]
+    kv_t = [kv[k] for k in timed]
+    kv_logical_t = [kv_logical[k] for k in timed]
+    kv_shared_t = [kv_shared[k] for k in timed]
+    if args.flush:  # the steps are separated by the flushes: the kernels' own times
+        step_ms = [a + b for a, b in zip(copy_ms, attn_ms)]
+        ms_per_step = float(np.mean(step_ms))
+        value = sum(kv_t) / (sum(step_ms) / 1e3) / 1e9
+    else:
+        ms_per_step = wall / args.steps * 1e3
+        value = sum(kv) / wall / 1e9
+    achieved = sum(algo) / (sum(part_ms) / 1e3) / 1e9
     digest = kernel_source_digest(args.workload)
     traffic = measured_traffic(args.workload, digest)
 
@@ -1053,9 +1092,21 @@ def main():
         "hbm_frac_of_step": round(value / HBM_PEAK_GBS, 4),
         "attn_stream_ms": round(float(np.mean(part_ms)), 4),
         "attn_merge_ms": round(float(np.mean(merge_ms)), 4),
-        "attn_kv_gbs": round(sum(kv) / sum(attn_ms) * 1e3 / 1e9, 2),
+        "attn_kv_gbs": round(sum(kv_t) / sum(attn_ms) * 1e3 / 1e9, 2),
         "kv_bytes_per_step": {"unique": int(np.mean(kv)), "logical": int(np.mean(kv_logical))},
-        "attn_logical_kv_gbs": round(sum(kv_logical) / sum(attn_ms) * 1e3 / 1e9, 2),
+        "attn_logical_kv_gbs": round(sum(kv_logical_t) / sum(attn_ms) * 1e3 / 1e9, 2),
+        "timing": {
+            "flushed": bool(args.flush),
+            "steps_with_kernel_events": len(timed),
+            "note": ("a 1 GiB scratch write before every timed step; value and ms_per_step are "
+                     "the step's kernels' event times" if args.flush else
+                     "back-to-back steps; value and ms_per_step are wall-clock over every step, "
+                     "kernel times from the events of every n-th step"),
+            "kernel_ms": {name: ms_stats(v) for name, v in
+                          (("stream", part_ms), ("merge", merge_ms), ("attention", attn_ms))
+                          + ((("shared", shared_ms),) if wl.planned else ())
+                          + ((("cow_copy", copy_ms),) if wl.beam else ())},
+        },
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -1068,16 +1119,16 @@ def main():
         },
     }
     if wl.planned:
-        sh = sum(kv_shared)
+        sh = sum(kv_shared_t)
         res["shared_prefix_plan"] = {
             "shared_pass_ms": round(float(np.mean(shared_ms)), 4),
             "shared_unique_bytes_per_step": int(np.mean(kv_shared)),
             "private_unique_bytes_per_step": int(np.mean(kv_private)),
             "shared_pass_gbs": round(sh / (sum(shared_ms) / 1e3) / 1e9, 2) if sh else None,
             "attention_ms": round(float(np.mean(attn_ms)), 4),
-            "attention_unique_gbs": round((sum(kv) + args.steps * wl.qo_bytes())
+            "attention_unique_gbs": round((sum(kv_t) + len(timed) * wl.qo_bytes())
                                           / (sum(attn_ms) / 1e3) / 1e9, 2),
-            "attention_frac_of_hbm_peak": round((sum(kv) + args.steps * wl.qo_bytes())
+            "attention_frac_of_hbm_peak": round((sum(kv_t) + len(timed) * wl.qo_bytes())
                                                 / (sum(attn_ms) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
             "note": "three kernels per step (shared pass, stream pass over the private blocks, "
                     "merge); roofline above is the stream pass over the private bytes",
@@ -1085,7 +1136,7 @@ def main():
     if wl.beam:
         # copy-on-write copies: both caches, every kv head, read + written
         pair_bytes = 4 * wl.Hkv * wl.hd * 16 * wl.eb
-        copied = sum(wl.cows) * pair_bytes
+        copied = sum(wl.cows[k] for k in timed) * pair_bytes
         res["cow_copy"] = {
             "kernel": "copy_blocks_kernel (pkv_copy_blocks)",
             "pairs_per_step": round(float(np.mean(wl.cows)), 2),
