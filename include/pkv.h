@@ -530,6 +530,122 @@ pkv_status pkv_alloc_usage(const pkv_allocator* a, int64_t* out);
 int32_t pkv_alloc_free_list(const pkv_allocator* a, int32_t* out, int32_t cap);
 
 /* ------------------------------------------------------------------------------------------ */
+/* Serving step engine: one call per decode step of a continuous batch or a beam search.      */
+/* [P1] §四 (連續批次) and §十一: finished requests leave the batch and new ones join at any     */
+/* step, so the GPU is not left waiting for a whole batch; §三 步驟一..四 for each request's     */
+/* blocks (allocated on demand, written, attended through the table, freed). [P2]             */
+/* "PagedAttention 的优势", Beam Search: candidates fork from the beams they extend and share  */
+/* their history's blocks. The engine drives a caller-owned pkv_allocator (borrowed: it must   */
+/* outlive the engine, and the caller must not change it between create and destroy except   */
+/* through the engine or while no step is in flight) and keeps the request queue, the running */
+/* set (admission order), two sets of pinned host + device staging buffers for the step's     */
+/* block tables, lengths, slots, copy-on-write pairs and plans, and its decode and prefill     */
+/* workspaces. A step is one host call that enqueues the upload of its staging set and all of */
+/* the step's kernels on the caller's stream and returns without waiting for them: the host   */
+/* prepares step k+1 while the kernels of step k run (a staging set is reused only after the  */
+/* step that last read it has finished; that wait is on the host). Every step of an engine    */
+/* must use the same stream. The engine allocates device and pinned memory at                 */
+/* create and grows it inside a step only when a step needs more than any before (a growth of */
+/* a workspace first drains the caller's stream). Not thread-safe; use it from one thread, on  */
+/* the HIP device current at create (PKV_ERR_INVALID_ARG otherwise).                           */
+/* Errors: the steps check their arguments and the running sequences' lengths before changing */
+/* anything; an error from the allocator or a launch after that (PKV_ERR_OUT_OF_BLOCKS cannot  */
+/* occur for admitted work, whose blocks admission reserved) leaves the engine's bookkeeping   */
+/* unspecified: destroy it.                                                                   */
+typedef struct pkv_engine pkv_engine;
+
+/* Shared-prefix plans (pkv_decode_plan, default max_group) for every decode step. */
+#define PKV_ENGINE_PLAN 1
+
+/* alloc: the allocator of the NB-block pool the caches hold (the caller keeps ownership).    */
+/* k_cache, v_cache: device caches in the layout above. max_batch: most running sequences     */
+/* (<= 8192); max_context_len: longest sequence, which fixes the tables' width                 */
+/* ceil(max_context_len/16). flags: 0 or PKV_ENGINE_PLAN. Errors: PKV_ERR_INVALID_ARG,          */
+/* PKV_ERR_UNSUPPORTED, PKV_ERR_HIP.                                                            */
+pkv_status pkv_engine_create(pkv_allocator* alloc, void* k_cache, void* v_cache, int32_t NB,
+                             int32_t Hq, int32_t Hkv, int32_t hd, pkv_dtype dtype,
+                             int32_t max_batch, int32_t max_context_len, int32_t flags,
+                             pkv_engine** out);
+/* Waits for the engine's steps in flight, then releases what the engine holds (not the        */
+/* allocator or the caches).                                                                  */
+void pkv_engine_destroy(pkv_engine* e);
+
+/* Queue a request (first come, first served). prompt_len >= 1, max_new_tokens >= 1, their sum */
+/* <= max_context_len and its blocks <= NB; arrival_step: the first step that may admit it.   */
+/* token_ids: NULL, or its prompt_len token ids (host, copied): admission then starts the      */
+/* sequence with pkv_alloc_add_seq_tokens (automatic prefix caching), else pkv_alloc_add_seq +  */
+/* pkv_alloc_append. rid: the sequence id it gets in the allocator (must then be free).        */
+pkv_status pkv_engine_submit(pkv_engine* e, int64_t rid, int32_t prompt_len,
+                             int32_t max_new_tokens, int32_t arrival_step,
+                             const int32_t* token_ids);
+
+/* Append existing allocator sequences to the running set (after the running ones, in order); */
+/* they never retire (beam search, or a decode loop the caller ends). PKV_ERR_UNKNOWN_SEQ,     */
+/* PKV_ERR_SEQ_EXISTS (already running or repeated), PKV_ERR_INVALID_ARG (more than max_batch).*/
+pkv_status pkv_engine_adopt(pkv_engine* e, int32_t n, const int64_t* seqs);
+
+/* Running sequence ids in row order into seqs (up to cap); returns their number (-1: NULL e). */
+int32_t pkv_engine_running(const pkv_engine* e, int64_t* seqs, int32_t cap);
+/* Requests waiting in the queue (-1: NULL e). */
+int32_t pkv_engine_queued(const pkv_engine* e);
+
+/* One continuous-batching step (step number k = the number of steps taken before):            */
+/*  1. retire: running requests that produced max_new_tokens tokens are freed                 */
+/*     (pkv_alloc_free_many, in row order) and leave the running set;                          */
+/*  2. admit: while the queue head has arrived (arrival_step <= k), fewer than max_batch run,  */
+/*     its whole prompt fits in the prompt rows not yet used this step (prompt_rows), and the   */
+/*     free blocks minus the blocks the running requests may still take cover                  */
+/*     ceil((prompt + max new) / 16), the head is started and its prompt slots taken; it joins */
+/*     the running set (our admission rule: the pages give none; no preemption is ever needed);*/
+/*  3. append one token to every running sequence (admitted ones included), with new_ids[i]   */
+/*     as its id when new_ids is given (pkv_alloc_append_tokens), and export the marked tables */
+/*     and lengths (plus a shared-prefix plan with PKV_ENGINE_PLAN);                           */
+/*  4. launch, on `stream`: pkv_write of the admitted prompts' uncached tokens                  */
+/*     (k_prompt/v_prompt rows 0..T-1, admission order); the copy-on-write copies, if any; the */
+/*     causal prefill attention of those tokens when q_prompt is given (pkv_prefill_attn,      */
+/*     q_prompt rows 0..T-1, prefill_out written; f16/bf16, G <= 16); the fused decode step of */
+/*     the B running rows (pkv_decode_planned with PKV_ENGINE_PLAN, else                       */
+/*     pkv_decode_append_stream + pkv_decode_append_merge): row i of q/k_new/v_new is running  */
+/*     sequence i's, out row i is written.                                                     */
+/* Buffers (device, dtype of the caches, 16-byte aligned): q, out [max_batch][Hq][hd]; k_new,  */
+/* v_new [max_batch][Hkv][hd]; k_prompt, v_prompt [prompt_rows][Hkv][hd]; q_prompt,            */
+/* prefill_out [prompt_rows][Hq][hd] or both NULL. Only the first B (resp. T) rows are read or */
+/* written. new_ids: host int32 [max_batch] or NULL. scale: softmax scale of both attentions.  */
+/* events: NULL or 8 hipEvent_t (each may be NULL) recorded on the stream: [0] before the      */
+/* upload of the step's staged tables, lengths, slots and plans (a small copy kernel that      */
+/* reads the pinned set), [1] after it, [2] after the prompt write, [3] after the copies, [4]  */
+/* after the prefill, [5] after the shared pass, [6] after the stream pass, [7] after the      */
+/* merge. info: NULL or host                                                                   */
+/* int64 [8] = {B, T, retired, admitted, plan units (-1: unplanned), copy-on-write pairs,      */
+/* queued after the step, k}.                                                                  */
+pkv_status pkv_engine_step(pkv_engine* e, const void* q, const void* k_new, const void* v_new,
+                           const int32_t* new_ids, void* out, const void* k_prompt,
+                           const void* v_prompt, int32_t prompt_rows, const void* q_prompt,
+                           void* prefill_out, float scale, void* const* events, int64_t* info,
+                           void* stream);
+
+/* One beam-search step over the running set (B beams): with parents (host int32 [B], each in */
+/* [0, B)) and children (host int64 [B], new distinct ids), new beam i forks from running beam */
+/* parents[i] as children[i] (pkv_alloc_fork_many), the old beams are freed (free_many, in row */
+/* order) and the children become the running set; with both NULL the running set stays. Then */
+/* steps 3 and 4 of pkv_engine_step without prompts: one token appended per beam, the         */
+/* copy-on-write pairs this reports copied (pkv_copy_blocks), the decode step launched. q,    */
+/* k_new, v_new, out, events, info as pkv_engine_step.                                         */
+pkv_status pkv_engine_beam_step(pkv_engine* e, const int32_t* parents, const int64_t* children,
+                                const void* q, const void* k_new, const void* v_new, void* out,
+                                float scale, void* const* events, int64_t* info, void* stream);
+
+/* What the last step did, into host buffers (each may be NULL; sizes from its info): retired */
+/* ids [retired], admitted (id, prompt_len, cached tokens) triples [3*admitted], prompt slots */
+/* [T], lengths [B] and marked tables [B][ceil(max_context_len/16)] as uploaded. Valid until  */
+/* the next step.                                                                              */
+pkv_status pkv_engine_last(const pkv_engine* e, int64_t* retired, int64_t* admitted,
+                           int32_t* prompt_slots, int32_t* lens, int32_t* tables);
+
+/* Waits (on the host) for every step in flight. */
+pkv_status pkv_engine_sync(pkv_engine* e);
+
+/* ------------------------------------------------------------------------------------------ */
 /* Read-bandwidth probe (measurement support; not part of the attention path). The pages give */
 /* no hardware figures; the decode path's roofline is quoted against the published HBM peak   */
 /* and, beside it, against what this probe reaches on the same part with the stream pass's    */

@@ -6,7 +6,7 @@ library has not been built (``python paged_kv_cache_459_amd/build.py``): there i
 """
 
 from ._lib import BF16, BLOCK_SHARED, F16, F32, STATUS, PkvError, lib  # noqa: F401
-from .api import (BLOCK_SIZE, BlockAllocator, alloc_caches, cache_bytes,  # noqa: F401
+from .api import (BLOCK_SIZE, ENGINE_PLAN, BlockAllocator, Engine, alloc_caches, cache_bytes,  # noqa: F401
                   cache_shapes, pkv_copy_blocks, pkv_decode_append_attn, pkv_decode_append_merge,
                   pkv_decode_append_attn_noalloc,
                   pkv_decode_append_stream,

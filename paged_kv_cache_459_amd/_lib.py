@@ -110,6 +110,19 @@ SIGNATURES = {
     "pkv_alloc_refcount": (c_i32, [c_vp, c_i32]),
     "pkv_alloc_seq_len": (c_i64, [c_vp, c_i64]),
     "pkv_alloc_free_list": (c_i32, [c_vp, P_i32, c_i32]),
+    "pkv_engine_create": (c_i32, [c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                  c_i32, c_i32, ctypes.POINTER(c_vp)]),
+    "pkv_engine_destroy": (None, [c_vp]),
+    "pkv_engine_submit": (c_i32, [c_vp, c_i64, c_i32, c_i32, c_i32, c_vp]),
+    "pkv_engine_adopt": (c_i32, [c_vp, c_i32, c_vp]),
+    "pkv_engine_running": (c_i32, [c_vp, c_vp, c_i32]),
+    "pkv_engine_queued": (c_i32, [c_vp]),
+    "pkv_engine_step": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_vp,
+                                c_f32, c_vp, c_vp, c_vp]),
+    "pkv_engine_beam_step": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_f32, c_vp, c_vp,
+                                     c_vp]),
+    "pkv_engine_last": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "pkv_engine_sync": (c_i32, [c_vp]),
 }
 
 

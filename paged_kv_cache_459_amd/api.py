@@ -600,3 +600,185 @@ class BlockAllocator:
         out = np.empty(max(n, 1), np.int32)
         lib.pkv_alloc_free_list(self._h, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n)
         return out[:n].tolist()
+
+
+ENGINE_PLAN = 1  # PKV_ENGINE_PLAN
+_ENGINE_EVENTS = 8
+
+
+def _event_handles(events, buf):
+    """Raw hipEvent_t handles of up to 8 events (objects with an ``ev`` handle, raw ints, or
+    None) into the ctypes array buf."""
+    for k in range(_ENGINE_EVENTS):
+        e = events[k] if k < len(events) else None
+        buf[k] = (e.ev.value if hasattr(e, "ev") else e) if e is not None else None
+    return buf
+
+
+class Engine:
+    """Serving step engine (C++, include/pkv.h): the request queue, the running set and the
+    step's staging live in the library, and one call runs a whole continuous-batching or
+    beam-search step (retire, admit, append, table and plan export and upload, launches).
+    Borrows ``allocator`` (kept alive here) and the caches. Not thread-safe."""
+
+    def __init__(self, allocator, k_cache, v_cache, *, num_q_heads, num_kv_heads, head_dim,
+                 max_batch, max_context_len, plan=False):
+        for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+            _need(t, name)
+        self.alloc = allocator
+        self.k_cache, self.v_cache = k_cache, v_cache
+        self.Hq, self.Hkv, self.hd = num_q_heads, num_kv_heads, head_dim
+        self.dtype = k_cache.dtype
+        self.device = k_cache.device
+        self.nb = _num_blocks(k_cache, num_kv_heads, head_dim)
+        self.max_batch, self.max_ctx = int(max_batch), int(max_context_len)
+        self.max_blocks = -(-self.max_ctx // BLOCK_SIZE)
+        h = ctypes.c_void_p()
+        check(lib.pkv_engine_create(allocator._h, _ptr(k_cache), _ptr(v_cache), self.nb,
+                                    num_q_heads, num_kv_heads, head_dim, pkv_dtype(k_cache),
+                                    self.max_batch, self.max_ctx, ENGINE_PLAN if plan else 0,
+                                    ctypes.byref(h)), "pkv_engine_create")
+        self._h = h
+        self.info = np.zeros(8, np.int64)
+        self._info_p = ctypes.c_void_p(self.info.ctypes.data)
+        self._ev = (ctypes.c_void_p * _ENGINE_EVENTS)()
+        self._ids = np.zeros(self.max_batch, np.int32)
+
+    def close(self):
+        if self._h:
+            lib.pkv_engine_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def submit(self, rid, prompt_len, max_new_tokens, arrival_step=0, token_ids=None):
+        ids = None
+        if token_ids is not None:
+            ids = _as_c(token_ids, np.int32)
+            if len(ids) != prompt_len:
+                raise ValueError("token_ids must hold prompt_len ids")
+        check(lib.pkv_engine_submit(self._h, int(rid), int(prompt_len), int(max_new_tokens),
+                                    int(arrival_step), None if ids is None else ids.ctypes.data),
+              "pkv_engine_submit")
+
+    def adopt(self, seqs):
+        s = _as_c(seqs, np.int64)
+        check(lib.pkv_engine_adopt(self._h, len(s), s.ctypes.data), "pkv_engine_adopt")
+
+    def running(self):
+        n = int(lib.pkv_engine_running(self._h, None, 0))
+        out = np.empty(n, np.int64)
+        lib.pkv_engine_running(self._h, out.ctypes.data, n)
+        return out
+
+    def queued(self):
+        return int(lib.pkv_engine_queued(self._h))
+
+    def _rows(self, t, name, heads):
+        _need(t, name, dtype=self.dtype, device=self.device)
+        if t.dim() != 3 or t.shape[1:] != (heads, self.hd) or t.shape[0] < self.max_batch:
+            raise ValueError(f"{name} must be [>= max_batch, {heads}, {self.hd}]")
+
+    def step(self, q, k_new, v_new, out, *, scale, k_prompt=None, v_prompt=None, q_prompt=None,
+             prefill_out=None, new_ids=None, events=None):
+        """pkv_engine_step. q/k_new/v_new/out hold max_batch rows (the first B are used);
+        k_prompt/v_prompt (and q_prompt/prefill_out, for the prefill attention) the prompt
+        rows, whose count bounds each step's admitted prompt tokens. new_ids: host int32
+        (max_batch entries, the first B used) or None. Returns info (int64 [8], overwritten by
+        the next step): B, T, retired, admitted, plan units, copy-on-write pairs, queued, step."""
+        self._rows(q, "q", self.Hq)
+        self._rows(out, "out", self.Hq)
+        self._rows(k_new, "k_new", self.Hkv)
+        self._rows(v_new, "v_new", self.Hkv)
+        rows = 0
+        if (k_prompt is None) != (v_prompt is None):
+            raise ValueError("give both k_prompt and v_prompt, or neither")
+        if k_prompt is not None:
+            for name, t in (("k_prompt", k_prompt), ("v_prompt", v_prompt)):
+                _need(t, name, dtype=self.dtype, device=self.device)
+                if t.dim() != 3 or t.shape[1:] != (self.Hkv, self.hd):
+                    raise ValueError(f"{name} must be [rows, {self.Hkv}, {self.hd}]")
+            rows = min(k_prompt.shape[0], v_prompt.shape[0])
+        if (q_prompt is None) != (prefill_out is None):
+            raise ValueError("give both q_prompt and prefill_out, or neither")
+        if q_prompt is not None:
+            for name, t in (("q_prompt", q_prompt), ("prefill_out", prefill_out)):
+                _need(t, name, dtype=self.dtype, device=self.device)
+                if t.dim() != 3 or t.shape[1:] != (self.Hq, self.hd) or t.shape[0] < rows:
+                    raise ValueError(f"{name} must be [>= prompt rows, {self.Hq}, {self.hd}]")
+        ids = None
+        if new_ids is not None:
+            n = len(new_ids)
+            if n > self.max_batch:
+                raise ValueError("more new_ids than max_batch")
+            self._ids[:n] = new_ids
+            ids = self._ids.ctypes.data
+        ev = _event_handles(events, self._ev) if events is not None else None
+        check(lib.pkv_engine_step(self._h, _ptr(q), _ptr(k_new), _ptr(v_new), ids, _ptr(out),
+                                  _ptr(k_prompt), _ptr(v_prompt), rows, _ptr(q_prompt),
+                                  _ptr(prefill_out), float(scale), ev, self._info_p,
+                                  _stream(self.device)), "pkv_engine_step")
+        return self.info
+
+    def beam_step(self, q, k_new, v_new, out, *, scale, parents=None, children=None,
+                  events=None):
+        """pkv_engine_beam_step: parents (int32 [B], rows of the running set) and children
+        (int64 [B], new ids), or neither. Returns info as step()."""
+        self._rows(q, "q", self.Hq)
+        self._rows(out, "out", self.Hq)
+        self._rows(k_new, "k_new", self.Hkv)
+        self._rows(v_new, "v_new", self.Hkv)
+        if (parents is None) != (children is None):
+            raise ValueError("give both parents and children, or neither")
+        p = c = None
+        if parents is not None:
+            p = _as_c(parents, np.int32)
+            c = _as_c(children, np.int64)
+            if p.shape != c.shape:
+                raise ValueError("parents and children must have one length")
+        ev = _event_handles(events, self._ev) if events is not None else None
+        check(lib.pkv_engine_beam_step(self._h, None if p is None else p.ctypes.data,
+                                       None if c is None else c.ctypes.data, _ptr(q),
+                                       _ptr(k_new), _ptr(v_new), _ptr(out), float(scale), ev,
+                                       self._info_p, _stream(self.device)),
+              "pkv_engine_beam_step")
+        return self.info
+
+    def last(self):
+        """What the last step did: dict(retired, admitted [(id, prompt_len, cached)],
+        prompt_slots, lens, tables (marked))."""
+        B, T, R, A = (int(x) for x in self.info[:4])
+        retired = np.empty(R, np.int64)
+        admitted = np.empty(3 * A, np.int64)
+        slots = np.empty(T, np.int32)
+        lens = np.empty(B, np.int32)
+        tables = np.empty((B, self.max_blocks), np.int32)
+        check(lib.pkv_engine_last(self._h, retired.ctypes.data, admitted.ctypes.data,
+                                  slots.ctypes.data, lens.ctypes.data, tables.ctypes.data),
+              "pkv_engine_last")
+        return dict(retired=retired, admitted=[tuple(int(x) for x in a)
+                                               for a in admitted.reshape(A, 3)],
+                    prompt_slots=slots, lens=lens, tables=tables)
+
+    def last_lens(self):
+        """Lengths the last step uploaded."""
+        lens = np.empty(int(self.info[0]), np.int32)
+        check(lib.pkv_engine_last(self._h, None, None, None, lens.ctypes.data, None),
+              "pkv_engine_last")
+        return lens
+
+    def last_tables(self):
+        """(lengths, marked tables) the last step uploaded."""
+        B = int(self.info[0])
+        lens = np.empty(B, np.int32)
+        tables = np.empty((B, self.max_blocks), np.int32)
+        check(lib.pkv_engine_last(self._h, None, None, None, lens.ctypes.data,
+                                  tables.ctypes.data), "pkv_engine_last")
+        return lens, tables
+
+    def sync(self):
+        check(lib.pkv_engine_sync(self._h), "pkv_engine_sync")

@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libpkv.so")
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 HIP_SOURCES = ["pkv_attn.hip", "pkv_write.hip", "pkv_prefill.hip", "pkv_probe.hip"]
-HOST_SOURCES = ["pkv_api.cpp", "pkv_alloc.cpp", "pkv_plan.cpp"]
+HOST_SOURCES = ["pkv_api.cpp", "pkv_alloc.cpp", "pkv_plan.cpp", "pkv_engine.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result", "-Werror=inline-asm",
           f"-I{INCLUDE}"]

@@ -25,6 +25,7 @@
 #include <vector>
 
 #include "../../include/pkv.h"
+#include "pkv_kernels.h"
 
 namespace {
 
@@ -454,6 +455,19 @@ pkv_status export_tables(const pkv_allocator* a, int32_t n, const int64_t* seqs,
 }
 
 }  // namespace
+
+int32_t pkv::alloc_row(const pkv_allocator* a, int64_t seq, int32_t from, int32_t max_blocks,
+                      int32_t* row, int64_t* len) {
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return -1;
+  const auto& b = it->second.blocks;
+  const int32_t n = static_cast<int32_t>(b.size());
+  if (n > max_blocks) return -1;
+  for (int32_t j = std::max(from, 0); j < n; ++j)
+    row[j] = a->ref[b[j]] > 1 ? (b[j] | PKV_BLOCK_SHARED) : b[j];
+  *len = it->second.len;
+  return n;
+}
 
 extern "C" {
 

@@ -134,6 +134,20 @@ hipError_t launch_prefill(const StreamParams& p, int32_t dtype, hipStream_t stre
 // Prompt tokens per prefill unit for q-head group size G (a work-group's rows / G).
 int32_t prefill_tile_rows(int32_t G);
 hipError_t launch_copy_blocks(const CopyParams& p, int32_t dtype, hipStream_t stream);
+// A step's staged data, read from a device-visible pinned host buffer (16-byte aligned):
+// small_n16 16-byte chunks at src to small_dst; dense_n16 chunks at src + dense_src (bytes)
+// to table + dense_dst (ints, a multiple of 4); then npairs (flat index, value) int32 pairs
+// at src + pairs_src (bytes) scattered into table (indices outside [0, table_ints) skipped).
+struct StageParams {
+  const char* src;
+  int32_t* small_dst;
+  int64_t small_n16;
+  int32_t* table;
+  int64_t table_ints;
+  int64_t dense_src, dense_dst, dense_n16;
+  int64_t pairs_src, npairs;
+};
+hipError_t launch_stage(const StageParams& p, hipStream_t stream);
 // Work-groups per block and cache of the copy kernel (grid.y; at most 65535 is launchable).
 int32_t copy_blocks_grid_y(int32_t Hkv, int32_t hd, int32_t dtype);
 hipError_t launch_stream(const StreamParams& p, int32_t dtype, int32_t kernel,
@@ -147,6 +161,17 @@ hipError_t launch_shared(const StreamParams& p, int32_t dtype, int32_t kernel,
 // Read-bandwidth probe (pkv_probe.hip): tiles ids[0..n) of base, max_tile tiles of 4096 bytes.
 hipError_t launch_probe_read(const void* base, int32_t max_tile, const int32_t* ids, int32_t n,
                              int32_t num_workers, uint32_t* sink, hipStream_t stream);
+
+}  // namespace pkv
+
+// Host allocator, internal access for the step engine (pkv_alloc.cpp).
+struct pkv_allocator;
+namespace pkv {
+// Entries [from, n) of sequence seq's table row into row (marked as pkv_alloc_tables_marked
+// marks them), with n its block count, returned; *len receives its length. -1 if the
+// sequence is unknown or has more than max_blocks blocks.
+int32_t alloc_row(const pkv_allocator* a, int64_t seq, int32_t from, int32_t max_blocks,
+                  int32_t* row, int64_t* len);
 
 // Records the failing step and the HIP error text for pkv_last_error(); returns err.
 hipError_t note_error(const char* what, hipError_t err);

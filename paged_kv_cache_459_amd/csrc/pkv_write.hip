@@ -182,6 +182,44 @@ hipError_t launch_copy_blocks(const CopyParams& p, int32_t dtype, hipStream_t st
   return note_error("copy_blocks_kernel launch", hipGetLastError());
 }
 
+namespace {
+
+// A step's staged host data (pinned host memory, read over the bus) into device memory, in
+// one launch: the small arrays (lengths, copy-on-write pairs, slots, plans) copied whole, a
+// dense range of block-table rows, and single changed table entries scattered. A kernel of
+// ours rather than a runtime copy: it is ordered in the step's stream like the step's other
+// kernels, without the runtime copy's extra synchronization around host memory.
+__global__ void __launch_bounds__(256) stage_kernel(const StageParams p) {
+  int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < p.small_n16) {
+    reinterpret_cast<uint4*>(p.small_dst)[i] = reinterpret_cast<const uint4*>(p.src)[i];
+    return;
+  }
+  i -= p.small_n16;
+  if (i < p.dense_n16) {
+    if (p.dense_dst + 4 * (i + 1) <= p.table_ints)
+      reinterpret_cast<uint4*>(p.table + p.dense_dst)[i] =
+          reinterpret_cast<const uint4*>(p.src + p.dense_src)[i];
+    return;
+  }
+  i -= p.dense_n16;
+  if (i < p.npairs) {
+    const int2 e = reinterpret_cast<const int2*>(p.src + p.pairs_src)[i];
+    if (e.x >= 0 && e.x < p.table_ints) p.table[e.x] = e.y;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_stage(const StageParams& p, hipStream_t stream) {
+  const int64_t n = p.small_n16 + p.dense_n16 + p.npairs;
+  if (n == 0) return hipSuccess;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(stage_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                     stream, p);
+  return note_error("stage_kernel launch", hipGetLastError());
+}
+
 int32_t copy_blocks_grid_y(int32_t Hkv, int32_t hd, int32_t dtype) {
   const int64_t chunks = static_cast<int64_t>(Hkv) * hd * (dtype == 0 ? 4 : 2);
   return static_cast<int32_t>((chunks + 256 * kCopyUnroll - 1) / (256 * kCopyUnroll));

@@ -1,13 +1,15 @@
-"""The continuous-batching step loop on the GPU (ContinuousBatch: the C++ allocator, pkv_write
-for admitted prompts, their causal prefill attention, the fused decode step) against the
-oracle's loop, in lockstep on one seeded request stream; also with automatic prefix caching
-(requests sharing system prompts: the same cached counts, only the uncached prompt tokens
-written and attended, over their prompts cached prefix included).
+"""The continuous-batching step loop on the GPU against the oracle's loop, in lockstep on one
+seeded request stream; also with automatic prefix caching (requests sharing system prompts:
+the same cached counts, only the uncached prompt tokens written and attended, over their
+prompts cached prefix included).
 
-Every step: the same requests retire and are admitted (the admission rule is implemented
-separately on both sides), the prompt slots, block tables and lengths are equal, the memory
-accounting is equal, and every decode output is within the tolerance of the oracle's. At the
-end both caches are bit-exact and every block is back in the pool.
+Every device step is one call into the library's engine (``pkv_engine_step`` through
+ContinuousBatch.step): retire, admit, the prompt write, the admitted prompts' causal prefill,
+the decode step. After each step: the same requests retired and were admitted (the admission
+rule is implemented separately on both sides), the prompt slots, block tables and lengths
+the engine uploaded are the oracle's, the memory accounting is equal, and every prefill and
+decode output is within the tolerance of the oracle's. At the end both caches are bit-exact
+and every block is back in the pool.
 """
 
 import numpy as np
@@ -24,6 +26,46 @@ pytestmark = pytest.mark.gpu
 
 def unmarked(t):
     return np.where(t >= 0, t & ~0x40000000, t)
+
+
+class DeviceRows:
+    """Preallocated device buffers the engine reads its rows from (like a serving loop's)."""
+
+    def __init__(self, dtype, max_batch, prompt_rows, hq, hkv, hd):
+        dt = G.TORCH[dtype]
+        self.dtype = dtype
+        self.q = torch.zeros((max_batch, hq, hd), dtype=dt, device="cuda")
+        self.kn = torch.zeros((max_batch, hkv, hd), dtype=dt, device="cuda")
+        self.vn = torch.zeros((max_batch, hkv, hd), dtype=dt, device="cuda")
+        self.out = torch.zeros((max_batch, hq, hd), dtype=dt, device="cuda")
+        self.kp = torch.zeros((prompt_rows, hkv, hd), dtype=dt, device="cuda")
+        self.vp = torch.zeros((prompt_rows, hkv, hd), dtype=dt, device="cuda")
+        self.qp = torch.zeros((prompt_rows, hq, hd), dtype=dt, device="cuda")
+        self.pf = torch.zeros((prompt_rows, hq, hd), dtype=dt, device="cuda")
+
+    def put(self, buf, host):
+        if len(host):
+            buf[:len(host)].copy_(G.to_dev(host, self.dtype).view(buf[:len(host)].shape))
+
+
+def check_step(loop, info, r_ret, r_adm, r_slots, ref, want, tables, lens, cached=False):
+    B, T = int(info[0]), int(info[1])
+    last = loop.last()
+    assert list(last["retired"]) == r_ret
+    got_adm = [(a, p) for a, p, _ in last["admitted"]]
+    assert got_adm == [(a.rid, a.prompt_len) for a in r_adm]
+    if cached:
+        assert [c for _, _, c in last["admitted"]] == [a.cached for a in r_adm]
+    assert T == len(r_slots)
+    np.testing.assert_array_equal(last["prompt_slots"], r_slots)
+    assert B == len(ref.running)
+    assert list(loop.running()) == [r.rid for r in ref.running]
+    if B:
+        np.testing.assert_array_equal(last["lens"], lens)
+        got = unmarked(last["tables"])
+        np.testing.assert_array_equal(got[:, :tables.shape[1]], tables)
+        assert np.all(got[:, tables.shape[1]:] == -1)
+    return B, T
 
 
 @pytest.mark.parametrize("dtype,hq,hkv,hd,nb,max_batch,kernel", [
@@ -43,63 +85,63 @@ def test_loop_matches_oracle(dtype, hq, hkv, hd, nb, max_batch, kernel):
     k_cache, v_cache = m.alloc_caches(nb, hkv, hd, G.TORCH[dtype])
     k_cache.view(-1).copy_(G.to_dev(ref.k_cache, dtype))
     v_cache.view(-1).copy_(G.to_dev(ref.v_cache, dtype))
+    prev = m.pkv_set_attn_kernel(kernel)  # before the engine: it sizes for the kernel
     loop = ContinuousBatch(k_cache, v_cache, num_q_heads=hq, num_kv_heads=hkv, head_dim=hd,
                            max_batch=max_batch, max_context_len=110, free_order=order)
+    rows = DeviceRows(dtype, max_batch, max_batch * 110, hq, hkv, hd)
     for r in reqs:
         ref.submit(*r)
         loop.submit(*r)
-    prev = m.pkv_set_attn_kernel(kernel)
     steps = prefills = 0
     try:
         while not ref.idle():
             r_ret, r_adm, r_slots = ref.schedule()
-            retired, admitted, T = loop.schedule()
-            assert list(retired) == r_ret
-            assert admitted == [(a.rid, a.prompt_len) for a in r_adm]
-            assert T == len(r_slots)
-            if T:
-                np.testing.assert_array_equal(loop.prompt_slots.cpu().numpy(), r_slots)
-                k = W.normal_values(rng, (T, hkv, hd), dtype)
-                v = W.normal_values(rng, (T, hkv, hd), dtype)
-                ref.write_prompts(k, v, r_slots)
-                loop.write_prompts(G.to_dev(k, dtype), G.to_dev(v, dtype))
-                if dtype != "f32":  # the admitted prompts' causal attention
-                    qp = W.normal_values(rng, (T, hq, hd), dtype)
-                    want_p = ref.prefill(qp, r_adm, scale)
-                    got_p = loop.prefill(G.to_dev(qp, dtype), scale)
-                    torch.cuda.synchronize()
-                    G.assert_close(G.gpu_f64(got_p, dtype), want_p, dtype, f"prefill {steps}")
-                    prefills += 1
+            T = len(r_slots)
+            k = W.normal_values(rng, (T, hkv, hd), dtype)
+            v = W.normal_values(rng, (T, hkv, hd), dtype)
+            ref.write_prompts(k, v, r_slots)
+            rows.put(rows.kp, k)
+            rows.put(rows.vp, v)
+            prefill = dtype != "f32"  # the admitted prompts' causal attention
+            if prefill:
+                qp = W.normal_values(rng, (T, hq, hd), dtype)
+                want_p = ref.prefill(qp, r_adm, scale)
+                rows.put(rows.qp, qp)
             B = len(ref.running)
-            assert list(loop.running()) == [r.rid for r in ref.running]
             q = W.normal_values(rng, (B, hq, hd), dtype)
             kn = W.normal_values(rng, (B, hkv, hd), dtype)
             vn = W.normal_values(rng, (B, hkv, hd), dtype)
             want, _, tables, lens = ref.decode(q, kn, vn, scale)
-            out = loop.decode(G.to_dev(q, dtype), G.to_dev(kn, dtype), G.to_dev(vn, dtype),
-                              scale)
+            rows.put(rows.q, q)
+            rows.put(rows.kn, kn)
+            rows.put(rows.vn, vn)
+            info = loop.step(rows.q, rows.kn, rows.vn, rows.out, scale=scale, k_prompt=rows.kp,
+                             v_prompt=rows.vp, q_prompt=rows.qp if prefill else None,
+                             prefill_out=rows.pf if prefill else None)
             torch.cuda.synchronize()
+            B, T = check_step(loop, info, r_ret, r_adm, r_slots, ref, want, tables, lens)
+            if prefill and T:
+                G.assert_close(G.gpu_f64(rows.pf[:T], dtype), want_p, dtype, f"prefill {steps}")
+                prefills += 1
             if B:
-                np.testing.assert_array_equal(loop.last_lens, lens)
-                got = unmarked(loop.last_tables)
-                np.testing.assert_array_equal(got[:, :tables.shape[1]], tables)
-                assert np.all(got[:, tables.shape[1]:] == -1)
-                G.assert_close(G.gpu_f64(out, dtype), want, dtype, f"step {steps}")
+                G.assert_close(G.gpu_f64(rows.out[:B], dtype), want, dtype, f"step {steps}")
             assert loop.usage() == ref.alloc.usage()
             steps += 1
             assert steps < 1000
+        kc = W.to_storage_numpy(k_cache, dtype).reshape(-1)
+        vc = W.to_storage_numpy(v_cache, dtype).reshape(-1)
+        np.testing.assert_array_equal(kc.view(np.uint8), ref.k_cache.view(np.uint8))
+        np.testing.assert_array_equal(vc.view(np.uint8), ref.v_cache.view(np.uint8))
+        # the last requests retire at the next step (nothing is left to run)
+        info = loop.step(rows.q, rows.kn, rows.vn, rows.out, scale=scale)
+        ref.schedule()
+        torch.cuda.synchronize()
+        assert int(info[0]) == 0 and loop.idle()
+        assert loop.alloc.num_free() == nb == ref.alloc.num_free()
     finally:
+        loop.close()
         m.pkv_set_attn_kernel(prev)
     assert dtype == "f32" or prefills > 0
-    assert loop.idle()
-    kc = W.to_storage_numpy(k_cache, dtype).reshape(-1)
-    vc = W.to_storage_numpy(v_cache, dtype).reshape(-1)
-    np.testing.assert_array_equal(kc.view(np.uint8), ref.k_cache.view(np.uint8))
-    np.testing.assert_array_equal(vc.view(np.uint8), ref.v_cache.view(np.uint8))
-    # the last requests retire at the next schedule
-    loop.schedule()
-    ref.schedule()
-    assert loop.alloc.num_free() == nb == ref.alloc.num_free()
 
 
 @pytest.mark.parametrize("dtype,hq,hkv,hd,kernel", [("bf16", 8, 2, 128, 0), ("f16", 4, 4, 64, 0),
@@ -119,56 +161,86 @@ def test_loop_with_prefix_cache_matches_oracle(dtype, hq, hkv, hd, kernel):
     k_cache, v_cache = m.alloc_caches(nb, hkv, hd, G.TORCH[dtype])
     k_cache.view(-1).copy_(G.to_dev(ref.k_cache, dtype))
     v_cache.view(-1).copy_(G.to_dev(ref.v_cache, dtype))
+    prev = m.pkv_set_attn_kernel(kernel)
     loop = ContinuousBatch(k_cache, v_cache, num_q_heads=hq, num_kv_heads=hkv, head_dim=hd,
                            max_batch=max_batch, max_context_len=140, free_order=order,
                            prefix_cache=True)
+    rows = DeviceRows(dtype, max_batch, max_batch * 140, hq, hkv, hd)
     for rid, p, mx, a in reqs:
         t = systems[rid % 3] + [int(x) for x in rng.integers(0, 1000, size=p)]
         ref.submit(rid, len(t), mx, a, token_ids=t)
         loop.submit(rid, len(t), mx, a, token_ids=t)
-    prev = m.pkv_set_attn_kernel(kernel)
-    hits = 0
+    hits = planned = 0
     try:
         while not ref.idle():
             r_ret, r_adm, r_slots = ref.schedule()
-            retired, admitted, T = loop.schedule()
-            assert list(retired) == r_ret
-            assert admitted == [(a.rid, a.prompt_len) for a in r_adm]
-            assert loop.last_cached == [a.cached for a in r_adm]
-            hits += sum(loop.last_cached)
-            assert T == len(r_slots)
-            if T:
-                np.testing.assert_array_equal(loop.prompt_slots.cpu().numpy(), r_slots)
-                k = W.normal_values(rng, (T, hkv, hd), dtype)
-                v = W.normal_values(rng, (T, hkv, hd), dtype)
-                ref.write_prompts(k, v, r_slots)
-                loop.write_prompts(G.to_dev(k, dtype), G.to_dev(v, dtype))
-                # the uncached prompt tokens attend over their prompts, cached prefix included
-                qp = W.normal_values(rng, (T, hq, hd), dtype)
-                want_p = ref.prefill(qp, r_adm, 0.1)
-                got_p = loop.prefill(G.to_dev(qp, dtype), 0.1)
-                torch.cuda.synchronize()
-                G.assert_close(G.gpu_f64(got_p, dtype), want_p, dtype, "prefix-cached prefill")
+            hits += sum(a.cached for a in r_adm)
+            T = len(r_slots)
+            k = W.normal_values(rng, (T, hkv, hd), dtype)
+            v = W.normal_values(rng, (T, hkv, hd), dtype)
+            ref.write_prompts(k, v, r_slots)
+            rows.put(rows.kp, k)
+            rows.put(rows.vp, v)
+            # the uncached prompt tokens attend over their prompts, cached prefix included
+            qp = W.normal_values(rng, (T, hq, hd), dtype)
+            want_p = ref.prefill(qp, r_adm, 0.1)
+            rows.put(rows.qp, qp)
             B = len(ref.running)
             new_ids = [int(x) for x in rng.integers(0, 1000, size=B)]
             q = W.normal_values(rng, (B, hq, hd), dtype)
             kn = W.normal_values(rng, (B, hkv, hd), dtype)
             vn = W.normal_values(rng, (B, hkv, hd), dtype)
             want, _, tables, lens = ref.decode(q, kn, vn, 0.1, new_ids=new_ids)
-            out = loop.decode(G.to_dev(q, dtype), G.to_dev(kn, dtype), G.to_dev(vn, dtype), 0.1,
-                              new_ids=np.int32(new_ids))
+            rows.put(rows.q, q)
+            rows.put(rows.kn, kn)
+            rows.put(rows.vn, vn)
+            info = loop.step(rows.q, rows.kn, rows.vn, rows.out, scale=0.1, k_prompt=rows.kp,
+                             v_prompt=rows.vp, q_prompt=rows.qp, prefill_out=rows.pf,
+                             new_ids=np.int32(new_ids))
             torch.cuda.synchronize()
+            B, T = check_step(loop, info, r_ret, r_adm, r_slots, ref, want, tables, lens,
+                              cached=True)
+            planned += int(info[4]) > 0
+            if T:
+                G.assert_close(G.gpu_f64(rows.pf[:T], dtype), want_p, dtype,
+                               "prefix-cached prefill")
             if B:
-                np.testing.assert_array_equal(loop.last_lens, lens)
-                np.testing.assert_array_equal(unmarked(loop.last_tables)[:, :tables.shape[1]],
-                                              tables)
-                G.assert_close(G.gpu_f64(out, dtype), want, dtype, "prefix-cached step")
+                G.assert_close(G.gpu_f64(rows.out[:B], dtype), want, dtype, "prefix-cached step")
             assert loop.usage() == ref.alloc.usage()
             assert loop.alloc.cached_blocks() == ref.alloc.cached_blocks()
+        kc = W.to_storage_numpy(k_cache, dtype).reshape(-1)
+        vc = W.to_storage_numpy(v_cache, dtype).reshape(-1)
+        np.testing.assert_array_equal(kc.view(np.uint8), ref.k_cache.view(np.uint8))
+        np.testing.assert_array_equal(vc.view(np.uint8), ref.v_cache.view(np.uint8))
     finally:
+        loop.close()
         m.pkv_set_attn_kernel(prev)
     assert hits > 0
-    kc = W.to_storage_numpy(k_cache, dtype).reshape(-1)
-    vc = W.to_storage_numpy(v_cache, dtype).reshape(-1)
-    np.testing.assert_array_equal(kc.view(np.uint8), ref.k_cache.view(np.uint8))
-    np.testing.assert_array_equal(vc.view(np.uint8), ref.v_cache.view(np.uint8))
+    assert planned > 0 or hq // hkv > 4  # steps with shared blocks ran a shared-prefix plan
+
+
+def test_prompt_rows_bound_admission():
+    """A queue head whose prompt does not fit in the step's prompt rows waits (first come,
+    first served kept): with room for one 40-token prompt per step, three queued requests are
+    admitted one per step, in order, each prompt's slots exactly the allocator's."""
+    import paged_kv_cache_459_amd as m
+    from paged_kv_cache_459_amd.batching import ContinuousBatch
+    dtype, hq, hkv, hd, nb = "bf16", 4, 4, 64, 32
+    print("[batching] prompt rows bound admission", flush=True)
+    k_cache, v_cache = m.alloc_caches(nb, hkv, hd, G.TORCH[dtype])
+    loop = ContinuousBatch(k_cache, v_cache, num_q_heads=hq, num_kv_heads=hkv, head_dim=hd,
+                           max_batch=4, max_context_len=64)
+    rows = DeviceRows(dtype, 4, 50, hq, hkv, hd)
+    try:
+        for rid in range(3):
+            loop.submit(rid, 40, 5)
+        admitted = []
+        for _ in range(3):
+            info = loop.step(rows.q, rows.kn, rows.vn, rows.out, scale=0.1, k_prompt=rows.kp,
+                             v_prompt=rows.vp)
+            assert int(info[1]) == 40 and int(info[3]) == 1
+            admitted += [a for a, _, _ in loop.last()["admitted"]]
+        torch.cuda.synchronize()
+        assert admitted == [0, 1, 2] and loop.engine.queued() == 0
+    finally:
+        loop.close()

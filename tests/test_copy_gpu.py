@@ -6,9 +6,11 @@ C ABI, against the oracle.
   work-group's range (the partial-range path and the full-range path), with repeated sources
   and padding / out-of-pool pairs (skipped);
 * beam search: beams forked at arbitrary lengths and re-selected every step, one token
-  appended per beam per step. The C++ allocator and the oracle's allocator run in lockstep
-  (slots, copy-on-write pairs and tables equal every step); on the device each step is
-  pkv_copy_blocks of the step's pairs, then pkv_decode_append_attn; on the host the oracle's
+  appended per beam per step. The engine's allocator and the oracle's allocator run in
+  lockstep (the uploaded tables and lengths and the number of copy-on-write pairs equal every
+  step); on the device each step is
+  one engine call (pkv_engine_beam_step: fork, free, append, pkv_copy_blocks of the step's
+  pairs, the fused decode step, also with a shared-prefix plan); on the host the oracle's
   copy, write and attention. Every step's output matches within the tolerance and both
   caches are bit-exact at the end.
 """
@@ -92,11 +94,12 @@ def test_copy_many_pairs():
     np.testing.assert_array_equal(storage(v_d, dtype), want_v.view(np.uint8))
 
 
-@pytest.mark.parametrize("dtype,hq,hkv,hd,kernel", [
-    ("bf16", 8, 2, 128, 0), ("f32", 4, 4, 64, 0), ("f16", 4, 4, 128, 0), ("bf16", 8, 2, 64, 1)])
-def test_beam_search_loop(dtype, hq, hkv, hd, kernel):
+@pytest.mark.parametrize("dtype,hq,hkv,hd,kernel,plan", [
+    ("bf16", 8, 2, 128, 0, False), ("f32", 4, 4, 64, 0, False), ("f16", 4, 4, 128, 0, False),
+    ("bf16", 8, 2, 64, 1, False), ("bf16", 8, 2, 128, 0, True), ("f16", 4, 4, 64, 0, True)])
+def test_beam_search_loop(dtype, hq, hkv, hd, kernel, plan):
     m = pkv()
-    print(f"[beam] {dtype} {hq}/{hkv} hd{hd} kernel={kernel}", flush=True)
+    print(f"[beam] {dtype} {hq}/{hkv} hd{hd} kernel={kernel} plan={plan}", flush=True)
     groups, beams, steps, nb = 4, 4, 36, 160
     prompt_lens = (21, 16, 7, 40)
     rng = np.random.default_rng(81 + hd)
@@ -134,36 +137,41 @@ def test_beam_search_loop(dtype, hq, hkv, hd, kernel):
         ref.free_seq(root)
         alloc.free(root)
         live.append(row)
-    total_cows = 0
+    # every device step is one engine call: re-selection (fork, free), append, copy-on-write
+    # copies, the fused decode step
+    B = groups * beams
     prev = m.pkv_set_attn_kernel(kernel)
+    eng = m.Engine(alloc, k_d, v_d, num_q_heads=hq, num_kv_heads=hkv, head_dim=hd,
+                   max_batch=B, max_context_len=16 * 8, plan=plan)
+    eng.adopt([s for row in live for s in row])
+    dt = G.TORCH[dtype]
+    q_d = torch.empty((B, hq, hd), dtype=dt, device="cuda")
+    kn_d = torch.empty((B, hkv, hd), dtype=dt, device="cuda")
+    vn_d = torch.empty((B, hkv, hd), dtype=dt, device="cuda")
+    out = torch.empty((B, hq, hd), dtype=dt, device="cuda")
+    total_cows = planned = 0
     try:
         for step in range(steps):
+            parents = children = None
             if step > 0:
-                parents = W.beam_parents(rng, groups, beams)
+                pick = W.beam_parents(rng, groups, beams)
+                parents = (np.arange(groups)[:, None] * beams + pick).reshape(-1)
+                children = np.arange(next_id, next_id + B, dtype=np.int64)
                 new_live = []
                 for g in range(groups):
                     row = []
-                    for p in parents[g]:
+                    for p in pick[g]:
                         ref.fork(live[g][p], next_id)
-                        alloc.fork(live[g][p], next_id)
                         row.append(next_id)
                         next_id += 1
                     for s in live[g]:
                         ref.free_seq(s)
-                        alloc.free(s)
                     new_live.append(row)
                 live = new_live
             seqs = [s for row in live for s in row]
             want_slots, want_cows = ref.append(seqs, [1] * len(seqs))
-            slots, cows = alloc.append(seqs, np.ones(len(seqs), np.int32))
-            assert list(slots) == want_slots
-            assert [tuple(c) for c in cows.tolist()] == want_cows
-            total_cows += len(cows)
             mb = max(len(ref.blocks[s]) for s in seqs)
             want_tables, want_lens = ref.tables(seqs, mb)
-            tables, lens = alloc.tables(seqs, mb)
-            np.testing.assert_array_equal(tables, np.int32(want_tables))
-            np.testing.assert_array_equal(lens, np.int32(want_lens))
             q = W.normal_values(rng, (len(seqs), hq, hd), dtype)
             k_new = W.normal_values(rng, (len(seqs), hkv, hd), dtype)
             v_new = W.normal_values(rng, (len(seqs), hkv, hd), dtype)
@@ -171,21 +179,30 @@ def test_beam_search_loop(dtype, hq, hkv, hd, kernel):
             kc, vc = CW.copy_blocks(kc, vc, want_cows, hkv=hkv, hd=hd, bs=16, dtype=dtype)
             kc, vc = CW.write_kv(k_new, v_new, kc, vc, np.int32(want_slots), hkv=hkv, hd=hd,
                                  bs=16, dtype=dtype)
-            want = OA.decode_attention(q, kc, vc, tables, lens, scale=scale, hkv=hkv, hd=hd,
-                                       bs=16, dtype=dtype)
-            # device: copy, then the fused write + attention
-            if len(cows):
-                m.pkv_copy_blocks(k_d, v_d, dev_i32(cows[:, 0]), dev_i32(cows[:, 1]),
-                                  num_kv_heads=hkv, head_dim=hd)
-            out = m.pkv_decode_append_attn(G.to_dev(q, dtype), G.to_dev(k_new, dtype),
-                                           G.to_dev(v_new, dtype), k_d, v_d, dev_i32(tables),
-                                           dev_i32(lens), num_kv_heads=hkv, scale=scale,
-                                           max_context_len=int(lens.max()))
+            want = OA.decode_attention(q, kc, vc, want_tables, want_lens, scale=scale, hkv=hkv,
+                                       hd=hd, bs=16, dtype=dtype)
+            q_d.copy_(G.to_dev(q, dtype).view(q_d.shape))
+            kn_d.copy_(G.to_dev(k_new, dtype).view(kn_d.shape))
+            vn_d.copy_(G.to_dev(v_new, dtype).view(vn_d.shape))
+            info = eng.beam_step(q_d, kn_d, vn_d, out, scale=scale, parents=parents,
+                                 children=children)
             torch.cuda.synchronize()
+            assert list(eng.running()) == seqs
+            assert int(info[0]) == B and int(info[5]) == len(want_cows)
+            planned += int(info[4]) > 0
+            last = eng.last()
+            tables = np.where(last["tables"] >= 0, last["tables"] & ~0x40000000, -1)
+            np.testing.assert_array_equal(tables[:, :mb], np.int32(want_tables))
+            assert np.all(tables[:, mb:] == -1)
+            np.testing.assert_array_equal(last["lens"], np.int32(want_lens))
+            total_cows += len(want_cows)
             G.assert_close(G.gpu_f64(out, dtype), want, dtype, f"beam step {step}")
+        eng.sync()
     finally:
+        eng.close()
         m.pkv_set_attn_kernel(prev)
     assert total_cows > 0
+    assert planned > 0 or not plan
     np.testing.assert_array_equal(storage(k_d, dtype), kc.view(np.uint8))
     np.testing.assert_array_equal(storage(v_d, dtype), vc.view(np.uint8))
     assert alloc.num_free() == ref.num_free()

@@ -4,7 +4,8 @@ Each benchmark workload at its real shape runs one decode step exactly as bench.
 it: each sequence's newest K/V (k_new, v_new) is substituted by the stream pass and stored by
 the merge pass (pkv_decode_append_stream + pkv_decode_append_merge at the device's default
 worker count), or, for the shared-prefix batches, the planned step (pkv_decode_planned with
-k_new, v_new). Then:
+k_new, v_new); the beam-search batch also as the step engine runs it (pkv_engine_beam_step:
+re-selection, append with copy-on-write copies, the planned step). Then:
 
 * every output row and head is compared with the oracle (its cache write, then dense
   attention over each sequence's gathered K/V), within the tolerance;
@@ -23,6 +24,7 @@ import pytest
 import torch
 
 import workloads as W
+from oracle import allocator as OAL
 from oracle import attention as OA
 from oracle import cache_write as CW
 from tests import gpu_helpers as G
@@ -146,3 +148,90 @@ def test_planned_step_every_row(name):
     print(f"[full size, planned step] {name}", flush=True)
     shape, lens, tables, nb = shared_problem(name, W.SHAPES[name].seed)
     step_and_check(m, shape, lens, tables, nb, 4000 + shape.seed, planned=True)
+
+
+def test_engine_beam_step_every_row():
+    """The beam-search workload's engine step at full size (128 beams in 32 groups sharing a
+    2000-token prefix, group tails U[16, 512]): the engine's allocator and the oracle's run the
+    same re-selection, then every row and head is checked and both caches bit for bit."""
+    m = pkv()
+    print("[full size, engine beam step] beam_search", flush=True)
+    shape = W.SHAPES["beam_search"]
+    B, hq, hkv, hd = shape.B, shape.Hq, shape.Hkv, shape.hd
+    rng = W.rng_for(shape.seed)
+    lens0 = W.draw_lengths(shape, rng)
+    nb = 2048
+    order = rng.permutation(nb).astype(np.int32)
+    ref = OAL.BlockAllocator(nb, 16, order)
+    alloc = m.BlockAllocator(nb, 16, order)
+    groups = B // W.BEAMS
+    parent = 10_000_000
+    roots = list(range(parent + 1, parent + 1 + groups))
+    seqs = list(range(B))
+    for a in (ref, alloc):  # prefix, group tails, beams (as the benchmark builds them)
+        a.add_seq(parent)
+        a.append([parent], [W.PREFIX_TOKENS])
+        for r in roots:
+            a.fork(parent, r)
+        (a.free_seq if a is ref else a.free)(parent)
+        a.append(roots, [int(n) - 1 - W.PREFIX_TOKENS for n in lens0[::W.BEAMS]])
+        for g, r in enumerate(roots):
+            for b in range(W.BEAMS):
+                a.fork(r, seqs[g * W.BEAMS + b])
+        for r in roots:
+            (a.free_seq if a is ref else a.free)(r)
+    dt = G.TORCH[shape.dtype]
+    max_ctx = int(lens0.max()) + 16
+    k_cache, v_cache = m.alloc_caches(nb, hkv, hd, dt)
+    k_cache.view(-1).copy_(W.device_normal((k_cache.numel(),), shape.dtype, 5001))
+    v_cache.view(-1).copy_(W.device_normal((v_cache.numel(),), shape.dtype, 5002))
+    q = W.device_normal((B, hq, hd), shape.dtype, 5003)
+    k_new = W.device_normal((B, hkv, hd), shape.dtype, 5004)
+    v_new = W.device_normal((B, hkv, hd), shape.dtype, 5005)
+    kc = W.to_storage_numpy(k_cache, shape.dtype).reshape(-1)
+    vc = W.to_storage_numpy(v_cache, shape.dtype).reshape(-1)
+    eng = m.Engine(alloc, k_cache, v_cache, num_q_heads=hq, num_kv_heads=hkv, head_dim=hd,
+                   max_batch=B, max_context_len=max_ctx, plan=True)
+    try:
+        eng.adopt(seqs)
+        pick = W.beam_parents(np.random.default_rng(shape.seed + 100), groups, W.BEAMS)
+        parents = (np.arange(groups)[:, None] * W.BEAMS + pick).reshape(-1)
+        children = np.arange(B, 2 * B, dtype=np.int64)
+        out = torch.empty_like(q)
+        info = eng.beam_step(q, k_new, v_new, out, scale=G.scale_for(hd), parents=parents,
+                             children=children)
+        torch.cuda.synchronize()
+        got_lens, got_tables = eng.last_tables()
+        assert int(info[4]) > 0, "the step should run a shared-prefix plan"
+        # the oracle's re-selection, append, copy-on-write copies and newest-token writes
+        for i in range(B):
+            ref.fork(seqs[parents[i]], int(children[i]))
+        for s_ in seqs:
+            ref.free_seq(s_)
+        kids = [int(c) for c in children]
+        slots, cows = ref.append(kids, [1] * B)
+        assert int(info[5]) == len(cows) > 0
+        mb = got_tables.shape[1]
+        tables, lens = ref.tables(kids, mb)
+        tables = np.int32(tables)
+        np.testing.assert_array_equal(np.where(got_tables >= 0, got_tables & ~0x40000000, -1),
+                                      tables)
+        np.testing.assert_array_equal(got_lens, np.int32(lens))
+        kc, vc = CW.copy_blocks(kc, vc, cows, hkv=hkv, hd=hd, bs=16, dtype=shape.dtype)
+        kn = W.to_storage_numpy(k_new, shape.dtype)
+        vn = W.to_storage_numpy(v_new, shape.dtype)
+        kc, vc = CW.write_kv(kn, vn, kc, vc, np.int32(slots), hkv=hkv, hd=hd, bs=16,
+                             dtype=shape.dtype)
+        np.testing.assert_array_equal(
+            W.to_storage_numpy(k_cache, shape.dtype).reshape(-1).view(np.uint8),
+            kc.view(np.uint8), err_msg="k_cache after the step")
+        np.testing.assert_array_equal(
+            W.to_storage_numpy(v_cache, shape.dtype).reshape(-1).view(np.uint8),
+            vc.view(np.uint8), err_msg="v_cache after the step")
+        got = G.gpu_f64(out, shape.dtype)
+        want = oracle_all_rows(W.to_storage_numpy(q, shape.dtype), kc, vc, tables,
+                               np.int32(lens), scale=G.scale_for(hd), hkv=hkv, hd=hd,
+                               dtype=shape.dtype)
+        G.assert_close(got, want, shape.dtype, f"engine beam step: all {B} rows x {hq} heads")
+    finally:
+        eng.close()
