@@ -193,7 +193,9 @@ attn_prefill_kernel(const StreamParams p) {
   static_assert(NCH * kPW * 1024 == STAGE && 2 * NCH <= 15, "stage size");
   static_assert(kSB == 2, "one 32-token contraction per stage");
   __shared__ __attribute__((aligned(1024))) char s_kv[kNBuf][STAGE];
-  __shared__ int32_t s_ids[kPrefillMaxBlocks];
+  // the unit's block ids (-1: no block of the pool), then -1 past its end, so that a stage's
+  // pair of ids is one aligned 8-byte read at an even index
+  __shared__ __attribute__((aligned(16))) int32_t s_ids[kPrefillMaxBlocks + 4];
   __shared__ int32_t s_vmax[kPW];
 
   const int grid = gridDim.x, wg = blockIdx.x;
@@ -218,10 +220,15 @@ attn_prefill_kernel(const StreamParams p) {
   const uint32_t qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
 
   const int32_t* table = p.block_tables + static_cast<size_t>(ref) * p.max_blocks;
-  for (int i = tid; i < nblk; i += kPThreads) {
-    const int raw = table[b0 + i];
-    const int id = raw & ~kSharedBit;
-    s_ids[i] = (raw < 0 || id >= p.NB) ? -1 : id;
+  const int nblk_even = (nblk + 1) & ~1;
+  for (int i = tid; i < nblk_even + 2; i += kPThreads) {
+    int v = -1;
+    if (i < nblk) {
+      const int raw = table[b0 + i];
+      const int id = raw & ~kSharedBit;
+      v = (raw < 0 || id >= p.NB) ? -1 : id;
+    }
+    s_ids[i] = v;
   }
 
   // This lane's rows: row tile k holds local rows (w*RT + k)*16 + hq.
@@ -293,9 +300,16 @@ attn_prefill_kernel(const StreamParams p) {
   }
   const char* k_head = static_cast<const char*>(p.k_cache) + static_cast<size_t>(kvh) * TILE;
   const char* v_head = static_cast<const char*>(p.v_cache) + static_cast<size_t>(kvh) * TILE;
-  auto issue = [&](int t, int buf) {
-    const int id0 = uniform(max(s_ids[t - b0], 0));
-    const int id1 = uniform(t + 1 < b1 ? max(s_ids[t + 1 - b0], 0) : 0);
+  // The two block ids of stage s (blocks b0 + 2s and b0 + 2s + 1; -1 for no block of the
+  // pool or past the unit), read from LDS as one pair. The loop keeps the ids of the stages
+  // in flight in registers: each stage's pair is read once, a step before it is needed, so
+  // that no LDS read in the loop waits on its own.
+  auto stage_ids = [&](int s) {
+    return *reinterpret_cast<const int2*>(&s_ids[min(2 * s, nblk_even)]);
+  };
+  auto issue = [&](int2 ids, int buf) {
+    const int id0 = uniform(max(ids.x, 0));
+    const int id1 = uniform(max(ids.y, 0));
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int piece = w + kPW * i;  // wave-uniform
@@ -374,11 +388,10 @@ attn_prefill_kernel(const StreamParams p) {
       }
   };
 
-  // Softmax and p . v of stage t from its scores (sa, sbv).
-  auto finish = [&](int buf, int t, const float4_t (&sa)[RT], const float4_t (&sbv)[RT]) {
+  // Softmax and p . v of stage t (block ids ida, idb) from its scores (sa, sbv).
+  auto finish = [&](int buf, int t, int ida, int idb, const float4_t (&sa)[RT],
+                    const float4_t (&sbv)[RT]) {
     if (kBlockSize * t >= wmax) return;  // nothing of the stage is visible to this wave
-    const int ida = s_ids[t - b0];
-    const int idb = t + 1 < b1 ? s_ids[t + 1 - b0] : -1;
     const char* st = s_kv[buf];
     uint4 vf[VT];
 #pragma unroll
@@ -442,12 +455,10 @@ attn_prefill_kernel(const StreamParams p) {
   // the barrier publishes every wave's, and a stage holding slots at or past the work-group's
   // last visible token (its last), a block outside the pool or no second block has those K
   // and V slots zeroed in LDS once, for every wave (unused slots may hold anything, NaN too).
-  auto land = [&](int s, int ahead) {
+  auto land = [&](int s, int ahead, int ida, int idb) {
     const int t = b0 + kSB * s;
     wait_stages<NCH>(ahead);
     lds_barrier();
-    const int ida = s_ids[t - b0];
-    const int idb = t + 1 < b1 ? s_ids[t + 1 - b0] : -1;
     if (!(ida >= 0 && idb >= 0 && kBlockSize * (t + 2) <= vmax)) {
       fixup(s % kNBuf, t, ida, idb);
       lds_barrier();
@@ -461,20 +472,44 @@ attn_prefill_kernel(const StreamParams p) {
   // landing's barrier) before stage s is finished.
   const int nst = (nblk + kSB - 1) / kSB;
   constexpr int PD = kNBuf - 1;
-  for (int q = 0; q < PD && q < nst; ++q) issue(b0 + kSB * q, q);
-  land(0, min(PD - 1, nst - 1));
+  static_assert(PD == 3, "the id registers below hold three stages");
+  // block ids of stages s, s + 1, s + 2 (wave-uniform), and the pair of stage s + 3 read ahead
+  int a0, a1, c0, c1, d0, d1;
+  {
+    const int2 i0 = stage_ids(0), i1 = stage_ids(1), i2 = stage_ids(2);
+    a0 = uniform(i0.x);
+    a1 = uniform(i0.y);
+    c0 = uniform(i1.x);
+    c1 = uniform(i1.y);
+    d0 = uniform(i2.x);
+    d1 = uniform(i2.y);
+  }
+  int2 ahead_ids = stage_ids(PD);
+  if (nst > 0) issue(make_int2(a0, a1), 0);
+  if (nst > 1) issue(make_int2(c0, c1), 1);
+  if (nst > 2) issue(make_int2(d0, d1), 2);
+  land(0, min(PD - 1, nst - 1), a0, a1);
   float4_t sa0[RT], sb0[RT], sa1[RT], sb1[RT];
   if (kBlockSize * b0 < wmax) qk(0, sa0, sb0);
   auto step = [&](int s, const float4_t (&ca)[RT], const float4_t (&cb)[RT], float4_t (&na)[RT],
                   float4_t (&nb)[RT]) {
     const int t = b0 + kSB * s;
+    // the ids of stage s + PD (read a step ago), and the read of the next step's
+    const int e0 = uniform(ahead_ids.x), e1 = uniform(ahead_ids.y);
+    ahead_ids = stage_ids(s + PD + 1);
     if (s + 1 < nst) {
-      land(s + 1, min(PD - 2, nst - 2 - s));
-      if (s + PD < nst) issue(b0 + kSB * (s + PD), (s + PD) % kNBuf);
+      land(s + 1, min(PD - 2, nst - 2 - s), c0, c1);
+      if (s + PD < nst) issue(make_int2(e0, e1), (s + PD) % kNBuf);
       if (kBlockSize * (t + kSB) < wmax) qk((s + 1) % kNBuf, na, nb);
       __builtin_amdgcn_sched_barrier(0);  // keep those contractions ahead of the softmax
     }
-    finish(s % kNBuf, t, ca, cb);
+    finish(s % kNBuf, t, a0, a1, ca, cb);
+    a0 = c0;
+    a1 = c1;
+    c0 = d0;
+    c1 = d1;
+    d0 = e0;
+    d1 = e1;
   };
   for (int s = 0; s < nst; s += 2) {
     step(s, sa0, sb0, sa1, sb1);
