@@ -895,9 +895,6 @@ def batching_main(args, torch, pkv, W):
 def prefill_main(args, torch, pkv, W):
     """The chunked-prefill workload: one step = pkv_write of the new tokens' K/V, then the
     causal attention of those tokens over their sequences' paged caches."""
-    from threadpoolctl import threadpool_limits
-
-    from oracle import attention as OA
     shape = W.SHAPES["prefill"]
     dtype, Hq, Hkv, hd = shape.dtype, shape.Hq, shape.Hkv, shape.hd
     dt = W.torch_dtype(dtype)
@@ -1012,6 +1009,9 @@ def prefill_main(args, torch, pkv, W):
     }
     if not args.no_cpu_baseline:
         # the oracle on whole sequences' new tokens, in a seeded order, until the budget is spent
+        from threadpoolctl import threadpool_limits
+
+        from oracle import attention as OA
         order = np.random.default_rng(12345).permutation(shape.B)
         spent, rows, fl, seqs = 0.0, 0, 0.0, 0
         with threadpool_limits(limits=1):

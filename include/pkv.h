@@ -403,6 +403,7 @@ pkv_status pkv_decode_append_merge(void* out, const void* k_new, const void* v_n
                                    int32_t hd, pkv_dtype dtype, int32_t num_workers,
                                    void* stream);
 
+/* Test and measurement hook, not part of the product path (no serving code needs it).      */
 /* Attention-kernel selection, process-wide: 0 = automatic (matrix-core kernel for f16/bf16   */
 /* with 2 <= G <= 16, vector kernel otherwise), 1 = always the vector kernel, 2 = matrix-core  */
 /* kernel where supported (f16/bf16, G <= 16). Both give results within the same tolerance;   */
@@ -646,6 +647,7 @@ pkv_status pkv_engine_last(const pkv_engine* e, int64_t* retired, int64_t* admit
 pkv_status pkv_engine_sync(pkv_engine* e);
 
 /* ------------------------------------------------------------------------------------------ */
+/* Measurement hook, not part of the product path.                                           */
 /* Read-bandwidth probe (measurement support; not part of the attention path). The pages give */
 /* no hardware figures; the decode path's roofline is quoted against the published HBM peak   */
 /* and, beside it, against what this probe reaches on the same part with the stream pass's    */
