@@ -472,23 +472,21 @@ attn_prefill_kernel(const StreamParams p) {
   // landing's barrier) before stage s is finished.
   const int nst = (nblk + kSB - 1) / kSB;
   constexpr int PD = kNBuf - 1;
-  static_assert(PD == 3, "the id registers below hold three stages");
-  // block ids of stages s, s + 1, s + 2 (wave-uniform), and the pair of stage s + 3 read ahead
-  int a0, a1, c0, c1, d0, d1;
-  {
-    const int2 i0 = stage_ids(0), i1 = stage_ids(1), i2 = stage_ids(2);
-    a0 = uniform(i0.x);
-    a1 = uniform(i0.y);
-    c0 = uniform(i1.x);
-    c1 = uniform(i1.y);
-    d0 = uniform(i2.x);
-    d1 = uniform(i2.y);
+  static_assert(PD >= 2, "the loop lands stage s + 1 while stage s + PD loads");
+  // block ids of stages s .. s + PD - 1 (wave-uniform), and the pair of stage s + PD read
+  // ahead
+  int r0[PD], r1[PD];
+#pragma unroll
+  for (int q = 0; q < PD; ++q) {
+    const int2 iq = stage_ids(q);
+    r0[q] = uniform(iq.x);
+    r1[q] = uniform(iq.y);
   }
   int2 ahead_ids = stage_ids(PD);
-  if (nst > 0) issue(make_int2(a0, a1), 0);
-  if (nst > 1) issue(make_int2(c0, c1), 1);
-  if (nst > 2) issue(make_int2(d0, d1), 2);
-  land(0, min(PD - 1, nst - 1), a0, a1);
+#pragma unroll
+  for (int q = 0; q < PD; ++q)
+    if (q < nst) issue(make_int2(r0[q], r1[q]), q);
+  land(0, min(PD - 1, nst - 1), r0[0], r1[0]);
   float4_t sa0[RT], sb0[RT], sa1[RT], sb1[RT];
   if (kBlockSize * b0 < wmax) qk(0, sa0, sb0);
   auto step = [&](int s, const float4_t (&ca)[RT], const float4_t (&cb)[RT], float4_t (&na)[RT],
@@ -498,18 +496,19 @@ attn_prefill_kernel(const StreamParams p) {
     const int e0 = uniform(ahead_ids.x), e1 = uniform(ahead_ids.y);
     ahead_ids = stage_ids(s + PD + 1);
     if (s + 1 < nst) {
-      land(s + 1, min(PD - 2, nst - 2 - s), c0, c1);
+      land(s + 1, min(PD - 2, nst - 2 - s), r0[1], r1[1]);
       if (s + PD < nst) issue(make_int2(e0, e1), (s + PD) % kNBuf);
       if (kBlockSize * (t + kSB) < wmax) qk((s + 1) % kNBuf, na, nb);
       __builtin_amdgcn_sched_barrier(0);  // keep those contractions ahead of the softmax
     }
-    finish(s % kNBuf, t, a0, a1, ca, cb);
-    a0 = c0;
-    a1 = c1;
-    c0 = d0;
-    c1 = d1;
-    d0 = e0;
-    d1 = e1;
+    finish(s % kNBuf, t, r0[0], r1[0], ca, cb);
+#pragma unroll
+    for (int q = 0; q + 1 < PD; ++q) {
+      r0[q] = r0[q + 1];
+      r1[q] = r1[q + 1];
+    }
+    r0[PD - 1] = e0;
+    r1[PD - 1] = e1;
   };
   for (int s = 0; s < nst; s += 2) {
     step(s, sa0, sb0, sa1, sb1);
