@@ -244,3 +244,68 @@ def test_prompt_rows_bound_admission():
         assert admitted == [0, 1, 2] and loop.engine.queued() == 0
     finally:
         loop.close()
+
+
+def test_loop_reusing_request_ids_matches_oracle():
+    """Request ids are reused as soon as their request retires (the engine tells rows apart by
+    more than the id): every retired id comes back at once as a new request, in lockstep with
+    the oracle's loop, and the tables, outputs and caches stay the oracle's."""
+    import paged_kv_cache_459_amd as m
+    from paged_kv_cache_459_amd.batching import ContinuousBatch
+    dtype, hq, hkv, hd, nb, max_batch = "bf16", 8, 2, 64, 64, 6
+    print("[batching] reused request ids", flush=True)
+    rng = np.random.default_rng(590)
+    order = rng.permutation(nb)
+    ref = OB.BatchingLoop(nb, 16, hkv, hd, dtype, max_batch=max_batch, free_order=order,
+                          storage_dtype=H.STORAGE[dtype], nan_fill=H.NAN_BITS[dtype])
+    k_cache, v_cache = m.alloc_caches(nb, hkv, hd, G.TORCH[dtype])
+    k_cache.view(-1).copy_(G.to_dev(ref.k_cache, dtype))
+    v_cache.view(-1).copy_(G.to_dev(ref.v_cache, dtype))
+    loop = ContinuousBatch(k_cache, v_cache, num_q_heads=hq, num_kv_heads=hkv, head_dim=hd,
+                           max_batch=max_batch, max_context_len=96, free_order=order)
+    rows = DeviceRows(dtype, max_batch, max_batch * 96, hq, hkv, hd)
+
+    def submit(rid, step):
+        p, mx = int(rng.integers(1, 50)), int(rng.integers(1, 20))
+        ref.submit(rid, p, mx, step)
+        loop.submit(rid, p, mx, step)
+    for rid in range(max_batch):
+        submit(rid, 0)
+    reused = steps = 0
+    try:
+        while not ref.idle():
+            r_ret, r_adm, r_slots = ref.schedule()
+            T = len(r_slots)
+            k = W.normal_values(rng, (T, hkv, hd), dtype)
+            v = W.normal_values(rng, (T, hkv, hd), dtype)
+            ref.write_prompts(k, v, r_slots)
+            rows.put(rows.kp, k)
+            rows.put(rows.vp, v)
+            B = len(ref.running)
+            q = W.normal_values(rng, (B, hq, hd), dtype)
+            kn = W.normal_values(rng, (B, hkv, hd), dtype)
+            vn = W.normal_values(rng, (B, hkv, hd), dtype)
+            want, _, tables, lens = ref.decode(q, kn, vn, 0.1)
+            rows.put(rows.q, q)
+            rows.put(rows.kn, kn)
+            rows.put(rows.vn, vn)
+            info = loop.step(rows.q, rows.kn, rows.vn, rows.out, scale=0.1, k_prompt=rows.kp,
+                             v_prompt=rows.vp)
+            torch.cuda.synchronize()
+            B, T = check_step(loop, info, r_ret, r_adm, r_slots, ref, want, tables, lens)
+            if B:
+                G.assert_close(G.gpu_f64(rows.out[:B], dtype), want, dtype, f"step {steps}")
+            assert loop.usage() == ref.alloc.usage()
+            steps += 1
+            for rid in r_ret:  # a retired id comes straight back, while requests remain
+                if reused < 40:
+                    submit(rid, steps)
+                    reused += 1
+            assert steps < 2000
+        kc = W.to_storage_numpy(k_cache, dtype).reshape(-1)
+        vc = W.to_storage_numpy(v_cache, dtype).reshape(-1)
+        np.testing.assert_array_equal(kc.view(np.uint8), ref.k_cache.view(np.uint8))
+        np.testing.assert_array_equal(vc.view(np.uint8), ref.v_cache.view(np.uint8))
+    finally:
+        loop.close()
+    assert reused == 40
