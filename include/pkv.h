@@ -465,6 +465,13 @@ pkv_status pkv_alloc_fork_many(pkv_allocator* a, int32_t n, const int64_t* paren
                                const int64_t* children);
 pkv_status pkv_alloc_free_many(pkv_allocator* a, int32_t n, const int64_t* seqs);
 
+/* A beam re-selection in one call: exactly pkv_alloc_fork_many(n, parents, children) followed */
+/* by pkv_alloc_free_many(n, old) (the same state afterwards, the same free-list order, the    */
+/* same checks, all before any change), without their copies: the old sequences' storage is    */
+/* reused for the children. Errors as those two calls.                                          */
+pkv_status pkv_alloc_replace_many(pkv_allocator* a, int32_t n, const int64_t* parents,
+                                  const int64_t* old, const int64_t* children);
+
 /* Export block tables for seqs[0..n-1]: block_tables_out [n][max_blocks] (host int32, entries */
 /* past a sequence's block count set to -1) and context_lens_out [n] (host int32). A sequence  */
 /* with more than max_blocks blocks gives PKV_ERR_INVALID_ARG.                                 */
@@ -639,7 +646,10 @@ pkv_status pkv_engine_beam_step(pkv_engine* e, const int32_t* parents, const int
 /* What the last step did, into host buffers (each may be NULL; sizes from its info): retired */
 /* ids [retired], admitted (id, prompt_len, cached tokens) triples [3*admitted], prompt slots */
 /* [T], lengths [B] and marked tables [B][ceil(max_context_len/16)] as uploaded. Valid until  */
-/* the next step.                                                                              */
+/* the next step. The block ids are exact; a mark (PKV_BLOCK_SHARED, a cache hint only) is     */
+/* refreshed where the engine re-reads an entry (a row's last blocks each step, a whole row   */
+/* when its sequence changes; a forked beam takes its parent's earlier entries as they were), */
+/* so it can lag a change in sharing: a shared block left unmarked, or the reverse.            */
 pkv_status pkv_engine_last(const pkv_engine* e, int64_t* retired, int64_t* admitted,
                            int32_t* prompt_slots, int32_t* lens, int32_t* tables);
 

@@ -104,6 +104,7 @@ SIGNATURES = {
     "pkv_alloc_append_tokens": (c_i32, [c_vp, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "pkv_alloc_cached_blocks": (c_i32, [c_vp]),
     "pkv_alloc_free_many": (c_i32, [c_vp, c_i32, c_vp]),
+    "pkv_alloc_replace_many": (c_i32, [c_vp, c_i32, c_vp, c_vp, c_vp]),
     "pkv_alloc_tables": (c_i32, [c_vp, c_i32, c_vp, c_i32, c_vp, c_vp]),
     "pkv_alloc_tables_marked": (c_i32, [c_vp, c_i32, c_vp, c_i32, c_vp, c_vp]),
     "pkv_alloc_num_free": (c_i32, [c_vp]),

@@ -565,6 +565,16 @@ class BlockAllocator:
         s = _as_c(seqs, np.int64)
         check(lib.pkv_alloc_free_many(self._h, len(s), s.ctypes.data), "pkv_alloc_free_many")
 
+    def replace_many(self, parents, old, children):
+        """fork_many(parents, children) then free_many(old), in one call (all-or-nothing)."""
+        p = _as_c(parents, np.int64)
+        o = _as_c(old, np.int64)
+        c = _as_c(children, np.int64)
+        if not (p.shape == o.shape == c.shape) or p.ndim != 1:
+            raise ValueError("parents, old and children must be 1-D and of one length")
+        check(lib.pkv_alloc_replace_many(self._h, len(p), p.ctypes.data, o.ctypes.data,
+                                         c.ctypes.data), "pkv_alloc_replace_many")
+
     def tables(self, seqs, max_blocks, tables_out=None, lens_out=None, mark_shared=False):
         """Block tables [n, max_blocks] (pad -1) and lengths; with mark_shared, entries of
         blocks shared by several sequences carry BLOCK_SHARED (pkv_alloc_tables_marked)."""

@@ -69,6 +69,7 @@ struct pkv_allocator {
   std::unordered_map<int64_t, Seq> seqs;
   uint64_t calls = 0;             // append calls so far (stamps Seq::mark)
   std::vector<Seq*> batch;        // reused per append call
+  std::vector<Seq> staged;        // reused per replace_many call (the children's contents)
   std::unordered_map<int32_t, int32_t> moved;  // reused per append call (copy-on-write count)
   // prefix cache
   std::unordered_multimap<uint64_t, int64_t> index;  // content hash -> node
@@ -417,6 +418,83 @@ pkv_status pkv_alloc_free_many(pkv_allocator* a, int32_t n, const int64_t* seqs)
   if (dup) return PKV_ERR_INVALID_ARG;
   if (unknown) return PKV_ERR_UNKNOWN_SEQ;
   for (int32_t k = 0; k < n; ++k) pkv_alloc_free(a, seqs[k]);
+  return PKV_OK;
+}
+
+pkv_status pkv_alloc_replace_many(pkv_allocator* a, int32_t n, const int64_t* parents,
+                                  const int64_t* old, const int64_t* children) {
+  if (!a || n < 0 || (n > 0 && (!parents || !old || !children))) return PKV_ERR_INVALID_ARG;
+  if (n == 0) return PKV_OK;
+  // The checks of fork_many(parents, children) then free_many(old), all before any change:
+  // parents present, children absent and distinct, old present (the children cannot be among
+  // them) and distinct.
+  std::vector<const Seq*> from(n);
+  for (int32_t k = 0; k < n; ++k) {
+    auto it = a->seqs.find(parents[k]);
+    if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+    from[k] = &it->second;
+  }
+  {
+    std::unordered_set<int64_t> kids;
+    kids.reserve(static_cast<size_t>(n));
+    for (int32_t k = 0; k < n; ++k)
+      if (a->seqs.count(children[k]) || !kids.insert(children[k]).second) return PKV_ERR_SEQ_EXISTS;
+  }
+  const uint64_t call = ++a->calls;
+  std::vector<Seq*> gone(n, nullptr);
+  bool unknown = false, dup = false;
+  for (int32_t k = 0; k < n; ++k) {
+    auto it = a->seqs.find(old[k]);
+    if (it == a->seqs.end()) {
+      unknown = true;
+      continue;
+    }
+    if (it->second.mark == call) dup = true;
+    it->second.mark = call;
+    gone[k] = &it->second;
+  }
+  if (unknown && !dup) {
+    std::unordered_set<int64_t> distinct;
+    for (int32_t k = 0; k < n; ++k)
+      if (!distinct.insert(old[k]).second) dup = true;
+  }
+  if (dup) return PKV_ERR_INVALID_ARG;
+  if (unknown) return PKV_ERR_UNKNOWN_SEQ;
+  // References. The two calls add one per child for each of its parent's blocks, then take
+  // one per freed sequence for each of its blocks, pushing a block on the free list when it
+  // reaches zero. Here each freed sequence's blocks change once, by its number of children
+  // minus one, in the same order: a block still reaches zero only at its last freed holder
+  // (before that, the holders not yet visited keep it above zero), so the free list receives
+  // the same blocks in the same order. Children of parents that are not freed add their one
+  // reference per block directly.
+  std::vector<const Seq*> by_ptr(from);
+  std::sort(by_ptr.begin(), by_ptr.end());
+  std::vector<const Seq*> freed(gone.begin(), gone.end());
+  std::sort(freed.begin(), freed.end());
+  for (int32_t k = 0; k < n; ++k)
+    if (!std::binary_search(freed.begin(), freed.end(), from[k]))
+      for (int32_t b : from[k]->blocks) a->ref[b] += 1;
+  if (a->staged.size() < static_cast<size_t>(n)) a->staged.resize(n);
+  for (int32_t k = 0; k < n; ++k) {  // the children's contents, before any parent goes
+    a->staged[k] = *from[k];
+    a->staged[k].mark = 0;
+  }
+  for (int32_t k = 0; k < n; ++k) {
+    const auto range = std::equal_range(by_ptr.begin(), by_ptr.end(), gone[k]);
+    const int32_t delta = static_cast<int32_t>(range.second - range.first) - 1;
+    if (delta == 0) continue;
+    for (int32_t b : gone[k]->blocks) {
+      a->ref[b] += delta;
+      if (a->ref[b] == 0) a->push_back(b);
+    }
+  }
+  // each old entry becomes a child's (its node and storage reused)
+  for (int32_t k = 0; k < n; ++k) {
+    auto node = a->seqs.extract(old[k]);
+    node.key() = children[k];
+    std::swap(node.mapped(), a->staged[k]);
+    a->seqs.insert(std::move(node));
+  }
   return PKV_OK;
 }
 

@@ -99,6 +99,7 @@ struct pkv_engine {
   int32_t rows_tracked = 0;  // rows whose serial is set
   std::vector<int32_t> rowbuf;
   std::vector<int32_t> pairs;  // (flat index, value) pairs of this step
+  std::vector<int32_t> snap, snap_nblk;  // the rows before a beam re-selection
 
   void* ws = nullptr;
   size_t ws_bytes = 0;
@@ -185,9 +186,12 @@ void record(void* const* events, int k, hipStream_t stream) {
 // Brings rows [0, B) of the mirror up to date with the allocator and collects the entries
 // that changed (as pairs) and the range of rows they lie in. A row that still holds the same
 // sequence is re-read from its old last block on (a copy-on-write may have replaced it, an
-// append may have opened the next); any other row is re-read whole. Entries past a row's
-// blocks are reset to -1. Lengths go to lens.
-pkv_status update_rows(pkv_engine* e, int32_t B, int32_t* lens, int32_t* r0, int32_t* r1) {
+// append may have opened the next). A row whose sequence was forked this step from the
+// sequence of row src[i] (beam re-selection; the rows as they were are in e->snap) takes that
+// row's blocks up to the parent's last and re-reads the rest; any other row is re-read whole.
+// Entries past a row's blocks are reset to -1. Lengths go to lens.
+pkv_status update_rows(pkv_engine* e, int32_t B, int32_t* lens, int32_t* r0, int32_t* r1,
+                       const int32_t* src) {
   const int32_t mb = e->mb;
   e->pairs.clear();
   *r0 = B;
@@ -195,14 +199,20 @@ pkv_status update_rows(pkv_engine* e, int32_t B, int32_t* lens, int32_t* r0, int
   for (int32_t i = 0; i < B; ++i) {
     const int64_t seq = e->run[i].rid;
     const bool same = e->row_serial[i] == e->run[i].serial;
-    const int32_t from = same ? std::max(0, e->row_nblk[i] - 1) : 0;
+    int32_t from = same ? std::max(0, e->row_nblk[i] - 1) : 0;
+    if (!same && src) {  // the parent's blocks before its last are the child's
+      const int32_t p = src[i];
+      from = std::max(0, e->snap_nblk[p] - 1);
+      std::memcpy(e->rowbuf.data(), e->snap.data() + static_cast<size_t>(p) * mb,
+                  static_cast<size_t>(from) * 4);
+    }
     int64_t len = 0;
     const int32_t n = pkv::alloc_row(e->alloc, seq, from, mb, e->rowbuf.data(), &len);
     if (n < 0) return PKV_ERR_INVALID_ARG;
     int32_t* m = e->mirror.data() + static_cast<size_t>(i) * mb;
     const int32_t upto = std::max(n, e->row_nblk[i]);
     bool changed = false;
-    for (int32_t j = from; j < upto; ++j) {
+    for (int32_t j = same ? from : 0; j < upto; ++j) {
       const int32_t v = j < n ? e->rowbuf[j] : -1;
       if (m[j] != v) {
         m[j] = v;
@@ -230,7 +240,8 @@ pkv_status update_rows(pkv_engine* e, int32_t B, int32_t* lens, int32_t* r0, int
 // when new_ids is given), update the table, plan, stage, launch. Prompt slots (T) and the
 // admitted rows' prefill data are already staged in set s at lay.slots / lay.pf_*.
 pkv_status decode_tail(pkv_engine* e, int s, Layout& lay, int32_t T, int32_t A,
-                       const int32_t* new_ids, const void* q, const void* k_new,
+                       const int32_t* src_rows, const int32_t* new_ids, const void* q,
+                       const void* k_new,
                        const void* v_new, void* out, const void* k_prompt, const void* v_prompt,
                        const void* q_prompt, void* prefill_out, float scale,
                        void* const* events, int64_t* info, hipStream_t stream) {
@@ -252,7 +263,7 @@ pkv_status decode_tail(pkv_engine* e, int s, Layout& lay, int32_t T, int32_t A,
                             H + lay.cow_dst, &ncow);
     if (st != PKV_OK) return st;
     for (auto& r : e->run) r.done += 1;
-    st = update_rows(e, B, H + lay.lens, &r0, &r1);
+    st = update_rows(e, B, H + lay.lens, &r0, &r1, src_rows);
     if (st != PKV_OK) return st;
   }
   // shared-prefix plan of the updated rows (runs only where the shape gains from them)
@@ -629,8 +640,8 @@ pkv_status pkv_engine_step(pkv_engine* e, const void* q, const void* k_new, cons
     e->queue.pop_front();
     ++A;
   }
-  return decode_tail(e, s, lay, T, A, new_ids, q, k_new, v_new, out, k_prompt, v_prompt,
-                     q_prompt, prefill_out, scale, events, info, hs);
+  return decode_tail(e, s, lay, T, A, nullptr, new_ids, q, k_new, v_new, out, k_prompt,
+                     v_prompt, q_prompt, prefill_out, scale, events, info, hs);
 }
 
 pkv_status pkv_engine_beam_step(pkv_engine* e, const int32_t* parents, const int64_t* children,
@@ -650,16 +661,21 @@ pkv_status pkv_engine_beam_step(pkv_engine* e, const int32_t* parents, const int
   e->retired.clear();
   e->admitted.clear();
   if (parents && B > 0) {
-    // every new beam i forks from running beam parents[i]; then the old beams are freed
+    // every new beam i forks from running beam parents[i]; then the old beams are freed (one
+    // allocator call); the rows as they were serve the children's rows
     std::vector<int64_t> par(B), old(B);
     for (int32_t i = 0; i < B; ++i) {
       par[i] = e->run[parents[i]].rid;
       old[i] = e->run[i].rid;
     }
-    pkv_status st = pkv_alloc_fork_many(e->alloc, B, par.data(), children);
+    pkv_status st = pkv_alloc_replace_many(e->alloc, B, par.data(), old.data(), children);
     if (st != PKV_OK) return st;
-    st = pkv_alloc_free_many(e->alloc, B, old.data());
-    if (st != PKV_OK) return st;
+    const size_t rows = static_cast<size_t>(B) * e->mb;
+    if (e->snap.size() < rows) e->snap.resize(rows);
+    std::memcpy(e->snap.data(), e->mirror.data(), rows * 4);
+    e->snap_nblk.assign(e->row_nblk.begin(), e->row_nblk.begin() + B);
+    for (int32_t i = 0; i < B; ++i)  // rows whose content the mirror does not track
+      if (e->row_serial[i] != e->run[i].serial) e->snap_nblk[i] = 0;
     std::vector<Running> next(B);
     for (int32_t i = 0; i < B; ++i) {
       next[i] = e->run[parents[i]];
@@ -670,8 +686,8 @@ pkv_status pkv_engine_beam_step(pkv_engine* e, const int32_t* parents, const int
   }
   Layout lay = small_layout(B);
   if (e->reserve(s, lay.slots + 64, 0) != hipSuccess) return PKV_ERR_HIP;
-  return decode_tail(e, s, lay, 0, 0, nullptr, q, k_new, v_new, out, nullptr, nullptr, nullptr,
-                     nullptr, scale, events, info, hs);
+  return decode_tail(e, s, lay, 0, 0, parents, nullptr, q, k_new, v_new, out, nullptr, nullptr,
+                     nullptr, nullptr, scale, events, info, hs);
 }
 
 pkv_status pkv_engine_last(const pkv_engine* e, int64_t* retired, int64_t* admitted,

@@ -308,3 +308,86 @@ def test_prefix_cache_operations_match_oracle(seed):
         ora.free_seq(s)
     assert nat.num_free() == nb and nat.free_list() == ora.free_list()
     assert nat.cached_blocks() == ora.cached_blocks()
+
+
+@pytest.mark.parametrize("tokens", [False, True])
+def test_replace_many_equals_fork_many_then_free_many(tokens):
+    """replace_many(parents, old, children) leaves exactly the state of fork_many then
+    free_many (free-list order, refcounts, tables, lengths, prefix-cache index), also for the
+    appends that follow and with prefix-cache-tracked sequences; failing calls change nothing."""
+    rng = np.random.default_rng(171 + tokens)
+    nb = 240
+    order = rng.permutation(nb)
+    a, b = Native(nb, BS, order), Native(nb, BS, order)  # a: replace_many, b: the two calls
+    lens = [21, 16, 7, 40, 33]
+    for s, n in enumerate(lens):
+        if tokens:
+            ids = rng.integers(0, 50, size=n).astype(np.int32)
+            ids[:16] = 7  # a shared first block between the tracked prompts
+            a.add_seq_tokens(s, ids)
+            b.add_seq_tokens(s, ids)
+        else:
+            a.add_seq(s)
+            b.add_seq(s)
+            a.append([s], [n])
+            b.append([s], [n])
+    live, next_id = list(range(len(lens))), len(lens)
+    for step in range(40):
+        parents = [live[int(i)] for i in rng.integers(0, len(live), size=len(live))]
+        old = live
+        children = list(range(next_id, next_id + len(live)))
+        next_id += len(live)
+        a.replace_many(parents, old, children)
+        b.fork_many(parents, children)
+        b.free_many(old)
+        live = children
+        assert a.free_list() == b.free_list()
+        assert all(a.refcount(x) == b.refcount(x) for x in range(nb))
+        assert a.usage() == b.usage() and a.cached_blocks() == b.cached_blocks()
+        mb = 16
+        ta, la = a.tables(live, mb)
+        tb, lb = b.tables(live, mb)
+        assert ta.tolist() == tb.tolist() and la.tolist() == lb.tolist()
+        new = rng.integers(0, 50, size=len(live)).astype(np.int32)
+        if tokens:
+            ra = a.append(live, [1] * len(live), token_ids=new)
+            rb = b.append(live, [1] * len(live), token_ids=new)
+        else:
+            ra = a.append(live, [1] * len(live))
+            rb = b.append(live, [1] * len(live))
+        assert ra[0].tolist() == rb[0].tolist() and ra[1].tolist() == rb[1].tolist()
+    for o in old:
+        assert a.seq_len(o) == -1
+    # a parent that stays (not among the freed) and a freed sequence that is no parent
+    for x in (a, b):
+        x.add_seq(next_id)
+        x.append([next_id], [5])
+    parents, old, children = [live[0], live[0]], [live[1], next_id], [next_id + 1, next_id + 2]
+    a.replace_many(parents, old, children)
+    b.fork_many(parents, children)
+    b.free_many(old)
+    live = [s_ for s_ in live if s_ != live[1]] + children
+    next_id += 3
+    assert a.free_list() == b.free_list()
+    assert all(a.refcount(x) == b.refcount(x) for x in range(nb))
+    ta, la = a.tables(live, 16)
+    tb, lb = b.tables(live, 16)
+    assert ta.tolist() == tb.tolist() and la.tolist() == lb.tolist()
+    # errors: nothing changes
+    before = (a.free_list(), [a.refcount(x) for x in range(nb)])
+    p2 = [live[0], live[1]]
+    for call, code in [(lambda: a.replace_many([live[0], 999_999], p2, [next_id, next_id + 1]), 4),
+                       (lambda: a.replace_many(p2, p2, [next_id, live[2]]), 5),
+                       (lambda: a.replace_many(p2, p2, [next_id, next_id]), 5),
+                       (lambda: a.replace_many(p2, [live[0], live[0]], [next_id, next_id + 1]), 1),
+                       (lambda: a.replace_many(p2, [live[0], 999_999], [next_id, next_id + 1]), 4)]:
+        with pytest.raises(PkvError) as e:
+            call()
+        assert e.value.status == code
+        assert (a.free_list(), [a.refcount(x) for x in range(nb)]) == before
+    assert a.seq_len(next_id) == -1
+    with pytest.raises(ValueError):
+        a.replace_many(p2, p2, [next_id])
+    a.replace_many([], [], [])
+    a.free_many(live)
+    assert a.num_free() == nb
