@@ -396,6 +396,10 @@ attn_prefill_kernel(const StreamParams p) {
     uint4 vf[VT];
 #pragma unroll
     for (int j = 0; j < VT; ++j) vf[j] = *reinterpret_cast<const uint4*>(st + v_off + 512 * j);
+    // The softmax runs at raised wave priority, up to the last row tile's contraction: the
+    // other wave of the SIMD (another work-group, in its own stage) then issues its matrix-core
+    // instructions in the gaps of this wave's VALU chain rather than in turn with it.
+    __builtin_amdgcn_s_setprio(3);
     // this lane's 8 tokens: valid (a block of the pool) and their first logical index
     const bool lane_blk_ok = (g >> 1) == 0 ? ida >= 0 : idb >= 0;
     const int tok0 = kBlockSize * t + tok_lane;
@@ -446,6 +450,7 @@ attn_prefill_kernel(const StreamParams p) {
       // the row sum takes the probabilities as rounded for the contraction: numerator and
       // denominator then weigh every token alike
       lsum[k] = MM::sum8(pb, lsum[k]);
+      if (k == RT - 1) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int j = 0; j < VT; ++j) o[k][j] = MM::mul(vf[j], pb, o[k][j]);
     }
