@@ -140,15 +140,17 @@ __device__ __forceinline__ uint4 keep_tokens(uint4 v, int t0, int valid) {
 
 // One lane's 16 bytes from global memory straight into LDS (gfx950 global_load_lds_dwordx4):
 // the wave's 64 lanes fill the 1 KB at LDS byte address `lds` (wave-uniform, through M0) in
-// lane order. Issued as inline assembly so that the compiler neither tracks it nor adds its
-// own (conservative: every later LDS read) waits; the kernel waits on vmcnt itself. M0 is an
-// input operand bound to that register ("{m0}"), so the compiler sets it and knows its value;
-// the statement only reads it. The s_nop is the one wait state an LDS DMA needs after an SALU
-// write of M0, which the compiler cannot see through the statement.
-__device__ __forceinline__ void load_lds16(const void* src, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+// lane order. The source is a wave-uniform base address in scalar registers plus the lane's
+// 32-bit byte offset, so a load needs no per-lane 64-bit address arithmetic. Issued as inline
+// assembly so that the compiler neither tracks it nor adds its own (conservative: every later
+// LDS read) waits; the kernel waits on vmcnt itself. M0 is an input operand bound to that
+// register ("{m0}"), so the compiler sets it and knows its value; the statement only reads it.
+// The s_nop is the one wait state an LDS DMA needs after an SALU write of M0, which the
+// compiler cannot see through the statement.
+__device__ __forceinline__ void load_lds16(const char* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(src), "{m0}"(lds)
+               : "v"(off), "s"(base), "{m0}"(lds)
                : "memory");
 }
 
@@ -315,12 +317,15 @@ attn_prefill_kernel(const StreamParams p) {
       const int piece = w + kPW * i;  // wave-uniform
       const int tile = piece / PPT;
       const int kv = tile / kSB, sb = tile % kSB;
-      const char* base = (kv ? v_head : k_head) + static_cast<size_t>(sb == 0 ? id0 : id1) *
-                                                       blk_stride;
-      const int src = src_off[i];
+      const uintptr_t addr = reinterpret_cast<uintptr_t>(kv ? v_head : k_head) +
+                             static_cast<uintptr_t>(sb == 0 ? id0 : id1) * blk_stride;
+      const uint32_t lo = static_cast<uint32_t>(uniform(static_cast<int>(addr & 0xffffffffu)));
+      const uint32_t hi = static_cast<uint32_t>(uniform(static_cast<int>(addr >> 32)));
+      const char* base = reinterpret_cast<const char*>((static_cast<uintptr_t>(hi) << 32) | lo);
       const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
           (__attribute__((address_space(3))) char*)(&s_kv[buf][piece * 1024])));
-      load_lds16(base + src, static_cast<uint32_t>(uniform(static_cast<int>(lds))));
+      load_lds16(base, static_cast<uint32_t>(src_off[i]),
+                 static_cast<uint32_t>(uniform(static_cast<int>(lds))));
     }
   };
 
@@ -415,19 +420,22 @@ attn_prefill_kernel(const StreamParams p) {
     // outside the pool, were zeroed in LDS), so the row max may include tokens a row does not
     // see: it only keeps the exponentials in range. Invisible tokens get probability 0 below.
     const bool full = ida >= 0 && idb >= 0 && kBlockSize * (t + 2) <= wmin;
-    float bm[RT];
+    // The lazy test needs no row maximum: a row's scores exceed its running max by more than
+    // kLazy exactly when one of its four lanes' own maxima does (c >= 0 keeps the order). The
+    // row maximum (across the lanes) is taken only on the rare stage that raises it.
+    float lm[RT];
     bool grow = false;
 #pragma unroll
     for (int k = 0; k < RT; ++k) {
-      const float v = row_max4(smax(smax(smax(x[k][0], x[k][1]), smax(x[k][2], x[k][3])),
-                                    smax(smax(x[k][4], x[k][5]), smax(x[k][6], x[k][7]))));
-      bm[k] = v * c;  // base-2 units (c >= 0 keeps the order)
-      grow = grow || bm[k] > m[k] + kLazy;
+      lm[k] = smax(smax(smax(x[k][0], x[k][1]), smax(x[k][2], x[k][3])),
+                   smax(smax(x[k][4], x[k][5]), smax(x[k][6], x[k][7])));
+      grow = grow || lm[k] * c > m[k] + kLazy;
     }
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform
 #pragma unroll
       for (int k = 0; k < RT; ++k) {
-        const float mn = fmaxf(m[k], bm[k]);
+        const float bm = row_max4(lm[k]) * c;  // base-2 units
+        const float mn = fmaxf(m[k], bm);
         const float alpha = __builtin_amdgcn_exp2f(m[k] - mn);
         m[k] = mn;
         lsum[k] *= alpha;
