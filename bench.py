@@ -154,7 +154,7 @@ def ms_stats(ms):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--event-every", type=int, default=4,
                     help="record the per-kernel timing events on every n-th timed step (each "
                          "event is a marker packet between kernels; the wall-clock step time "
@@ -163,7 +163,7 @@ def parse():
                     help="before each timed step, write a 1 GiB scratch buffer (flushes the L2s "
                          "and the 256 MB last-level cache); value and ms_per_step then come from "
                          "the step's kernels' event times instead of the wall clock")
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama2_7b", choices=WORKLOADS)
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 vector, 2 matrix-core")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -759,6 +759,7 @@ def batching_main(args, torch, pkv, W):
 
     for _ in range(cfg["settle_steps"] + args.warmup):
         step()
+    step([TimingEvent() for _ in range(8)])  # the event path warm before the timed region
     torch.cuda.synchronize()
     every = 1 if args.flush else max(1, args.event_every)
     timed = [k for k in range(args.steps) if k % every == 0]
@@ -968,6 +969,7 @@ def prefill_main(args, torch, pkv, W):
 
     for _ in range(args.warmup):
         step()
+    step([TimingEvent() for _ in range(4)])  # the event path warm before the timed region
     torch.cuda.synchronize()
     evs = [[TimingEvent() for _ in range(4)] for _ in range(args.steps)]
     t0 = time.perf_counter()
@@ -1084,7 +1086,7 @@ def main():
     if args.workload == "prefill":
         prefill_main(args, torch, pkv, W)
         return
-    wl = Workload(args.workload, args.warmup + args.steps, torch, pkv, W, plan=not args.no_plan,
+    wl = Workload(args.workload, args.warmup + 1 + args.steps, torch, pkv, W, plan=not args.no_plan,
                   duplicate_prefix=args.duplicate_prefix,
                   engine=args.driver == "engine" or (args.driver == "auto" and
                                                      args.workload == "beam_search"))
@@ -1092,6 +1094,9 @@ def main():
 
     for _ in range(args.warmup):
         run_step(wl, torch, pkv)
+    # one more, with timing events: the first record of an event has cost milliseconds of host
+    # time in a fresh process, which would otherwise land in the timed region
+    run_step(wl, torch, pkv, [TimingEvent() for _ in range(6)])
     torch.cuda.synchronize()
 
     # per-kernel timing events on every n-th timed step (every step with --flush)
