@@ -143,6 +143,27 @@ class TimingEvent:
             pass
 
 
+def flush_buffer(torch):
+    """1 GiB of device scratch for the cache flush (zeros, so that its sum is finite)."""
+    return torch.zeros(1 << 28, dtype=torch.float32, device="cuda")
+
+
+def flush(scratch):
+    """Evicts the batch from the L2s and the last-level cache by reading 1 GiB of other data. A
+    read leaves the caches holding clean lines, as other layers' reads would; a write would
+    leave up to the cache's size of dirty lines, whose write-back would then land in the timed
+    kernels."""
+    scratch.sum()
+
+
+def prime(torch, events):
+    """Records every timing event once, outside the timed region: a fresh event's first record
+    has cost about a millisecond of host time (the timed step's record then overwrites it)."""
+    for e in events:
+        e.record()
+    torch.cuda.synchronize()
+
+
 def ms_stats(ms):
     """Mean, median, p10 and p90 of per-launch milliseconds."""
     a = np.asarray(ms, dtype=np.float64)
@@ -160,9 +181,10 @@ def parse():
                          "event is a marker packet between kernels; the wall-clock step time "
                          "is taken over every step)")
     ap.add_argument("--flush", action="store_true",
-                    help="before each timed step, write a 1 GiB scratch buffer (flushes the L2s "
-                         "and the 256 MB last-level cache); value and ms_per_step then come from "
-                         "the step's kernels' event times instead of the wall clock")
+                    help="before each timed step, read a 1 GiB scratch buffer (evicts the batch "
+                         "from the L2s and the 256 MB last-level cache, leaving clean lines); value "
+                         "and ms_per_step then come from the step's kernels' event times instead "
+                         "of the wall clock")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama2_7b", choices=WORKLOADS)
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 vector, 2 matrix-core")
@@ -757,19 +779,21 @@ def batching_main(args, torch, pkv, W):
                               kv=int(lens.astype(np.int64).sum()) * 2 * Hkv * hd * eb,
                               lens=lens, tables=last["tables"], usage=u))
 
-    for _ in range(cfg["settle_steps"] + args.warmup):
-        step()
-    step([TimingEvent() for _ in range(8)])  # the event path warm before the timed region
-    torch.cuda.synchronize()
+    # events created and recorded once before the warm-up (see main)
     every = 1 if args.flush else max(1, args.event_every)
     timed = [k for k in range(args.steps) if k % every == 0]
     evs = {k: [TimingEvent() for _ in range(8)] for k in timed}
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if args.flush else None
+    prime(torch, [e for v in evs.values() for e in v])
+    scratch = flush_buffer(torch) if args.flush else None
+    for _ in range(cfg["settle_steps"] + args.warmup):
+        step()
+    step([TimingEvent() for _ in range(8)])  # the event path warm before the timed region
     stats = []
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         if scratch is not None:  # before the step's events: not part of the kernels' times
-            scratch.fill_(k & 0xFF)
+            flush(scratch)
         step(evs.get(k), stats)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -837,7 +861,7 @@ def batching_main(args, torch, pkv, W):
         "timing": {
             "flushed": bool(args.flush),
             "steps_with_kernel_events": len(timed),
-            "note": ("a 1 GiB scratch write before every timed step; value and ms_per_step are "
+            "note": ("a 1 GiB scratch read before every timed step; value and ms_per_step are "
                      "the step's kernels' event times" if args.flush else
                      "back-to-back steps; value and ms_per_step are wall-clock over every step, "
                      "kernel times from the events of every n-th step"),
@@ -967,11 +991,12 @@ def prefill_main(args, torch, pkv, W):
             if ev is not None:
                 ev[1 + ps].record()
 
+    evs = [[TimingEvent() for _ in range(4)] for _ in range(args.steps)]
+    prime(torch, [e for v in evs for e in v])  # before the warm-up (see main)
     for _ in range(args.warmup):
         step()
     step([TimingEvent() for _ in range(4)])  # the event path warm before the timed region
     torch.cuda.synchronize()
-    evs = [[TimingEvent() for _ in range(4)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for k in range(args.steps):
         step(evs[k])
@@ -1092,24 +1117,27 @@ def main():
                                                      args.workload == "beam_search"))
     torch.cuda.synchronize()
 
+    # per-kernel timing events on every n-th timed step (every step with --flush), created and
+    # recorded once before the warm-up: between the warm-up and the timed region the device
+    # then idles only for the host's few statements (after an idle millisecond, the first
+    # timed step's upload took a millisecond more)
+    every = 1 if args.flush else max(1, args.event_every)
+    timed = [k for k in range(args.steps) if k % every == 0]
+    evs = {k: [TimingEvent() for _ in range(6)] for k in timed}
+    prime(torch, [e for v in evs.values() for e in v])
+    scratch = flush_buffer(torch) if args.flush else None
     for _ in range(args.warmup):
         run_step(wl, torch, pkv)
     # one more, with timing events: the first record of an event has cost milliseconds of host
     # time in a fresh process, which would otherwise land in the timed region
     run_step(wl, torch, pkv, [TimingEvent() for _ in range(6)])
-    torch.cuda.synchronize()
-
-    # per-kernel timing events on every n-th timed step (every step with --flush)
-    every = 1 if args.flush else max(1, args.event_every)
-    timed = [k for k in range(args.steps) if k % every == 0]
-    evs = {k: [TimingEvent() for _ in range(6)] for k in timed}
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if args.flush else None
     per_step = []
     wl.cows.clear()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         if scratch is not None:  # before the step's events: not part of the kernels' times
-            scratch.fill_(k & 0xFF)
+            flush(scratch)
         per_step.append(run_step(wl, torch, pkv, evs.get(k)))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -1212,7 +1240,7 @@ def main():
         "timing": {
             "flushed": bool(args.flush),
             "steps_with_kernel_events": len(timed),
-            "note": ("a 1 GiB scratch write before every timed step; value and ms_per_step are "
+            "note": ("a 1 GiB scratch read before every timed step; value and ms_per_step are "
                      "the step's kernels' event times" if args.flush else
                      "back-to-back steps; value and ms_per_step are wall-clock over every step, "
                      "kernel times from the events of every n-th step"),

@@ -854,9 +854,8 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_matrix_kernel(const StreamParams p)
 // kvh*G + r % G. The arithmetic is the matrix-core kernel's (S^T = K Q^T, O^T += V^T P^T, P in
 // lanes), with one difference: each row masks the tokens at or past its own sequence's length
 // (members may end inside a shared, partly filled block). V tokens past every row's length are
-// zeroed (unused slots may hold anything). Tiles are read with cached loads where other units
-// of the same chunk (the next members, on the next waves) read them too, and with
-// non-temporal loads by a unit that is the only reader of its chunk.
+// zeroed (unused slots may hold anything). Tiles are read with cached loads: other units of
+// the same chunk (the next members, on the next waves) read them too.
 //
 // Waves map to (kv head, unit) unit-fastest, and work-groups are laid XCD-contiguously, so the
 // member tiles of one chunk run side by side on one XCD. Each row's (m, l, o) goes to its cell:
@@ -900,142 +899,125 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_shared_kernel(const StreamParams p,
     lane_id = (raw < 0 || id >= p.NB) ? -1 : id;
   }
   auto block_id = [&](int t) { return uniform(__builtin_amdgcn_readlane(lane_id, t - b0)); };
-  // A unit whose tile of rows is only partly filled is its run's last (or only) unit: no
-  // other unit reads its chunk, so its tiles stream with non-temporal loads; the units of a
-  // run with more members share the chunk through the L2 (cached loads). The two cases are
-  // separate copies of the whole pass, so that no branch sits between the loads.
-  auto run = [&](auto nt_t) {
-    auto load = [&](uint4 (&kr)[KS], uint2 (&vr)[VT], int id) {
-      constexpr bool kNT = decltype(nt_t)::value;
-      const size_t base =
-          static_cast<size_t>(max(id, 0)) * blk_stride + static_cast<size_t>(kvh) * TILE;
-      const char* kt = static_cast<const char*>(p.k_cache) + base;
-      const char* vt = static_cast<const char*>(p.v_cache) + base;
+  auto load = [&](uint4 (&kr)[KS], uint2 (&vr)[VT], int id) {
+    const size_t base = static_cast<size_t>(max(id, 0)) * blk_stride + static_cast<size_t>(kvh) * TILE;
+    const char* kt = static_cast<const char*>(p.k_cache) + base;
+    const char* vt = static_cast<const char*>(p.v_cache) + base;
 #pragma unroll
-      for (int s2 = 0; s2 < KS; ++s2) {
-        const char* a = kt + k_lane + 1024u * s2;
-        kr[s2] = kNT ? load_nt16(a) : *reinterpret_cast<const uint4*>(a);
-      }
+    for (int s2 = 0; s2 < KS; ++s2) kr[s2] = *reinterpret_cast<const uint4*>(kt + k_lane + 1024u * s2);
 #pragma unroll
-      for (int j = 0; j < VT; ++j) {
-        const char* a = vt + v_lane + 512u * j;
-        vr[j] = kNT ? load_nt8(a) : *reinterpret_cast<const uint2*>(a);
-      }
-    };
-    // Two tiles in flight (buffers a and b, alternating), requested before the rows' lookups
-    // below so that their latencies overlap.
-    uint4 ka[KS], kb[KS];
-    uint2 va[VT], vb[VT];
-    int ida = block_id(b0), idb = block_id(min(b0 + 1, b1 - 1));
-    load(ka, va, ida);
-    load(kb, vb, idb);
-
-    int seq = -1;
-    if (hq < mcnt * G) seq = p.members[moff + mk];
-    const bool row_ok = seq >= 0 && seq < p.B;
-    uint4 qb[KS];
-    if (row_ok) {
-      const uint4* qp = reinterpret_cast<const uint4*>(
-          static_cast<const char*>(p.q) +
-          (static_cast<size_t>(seq) * p.Hq + kvh * G + jq) * HD * 2);
-#pragma unroll
-      for (int s2 = 0; s2 < KS; ++s2) qb[s2] = qp[4 * s2 + g];
-    } else {
-#pragma unroll
-      for (int s2 = 0; s2 < KS; ++s2) qb[s2] = make_uint4(0, 0, 0, 0);
-    }
-    const int n_row = row_ok ? clamp_len(p, seq) : 0;
-    // q settled here: a first use inside the loop would put its wait (for every load issued
-    // before it, the tiles included) at the top of each iteration
-#pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) settle(qb[s2]);
-    // the rows' shortest and longest lengths: a tile ending at or before the shortest needs no
-    // masking; V tokens at or past the longest are read by no row
-    int nmin = row_ok ? n_row : 0x7fffffff, nmax = n_row;
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-      nmin = min(nmin, __shfl_xor(nmin, off));
-      nmax = max(nmax, __shfl_xor(nmax, off));
-    }
-    nmin = uniform(nmin);
-    nmax = uniform(nmax);
-
-    float m = kNegInf, lsum = 0.f;
-    float4_t o[VT];
-#pragma unroll
-    for (int j = 0; j < VT; ++j) o[j] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-    auto compute = [&](const uint4 (&kr)[KS], const uint2 (&vr)[VT], int t, int id) {
-      const bool full = id >= 0 && kBlockSize * (t + 1) <= nmin;  // every row sees all 16 tokens
-      const int row_valid = id < 0 ? 0 : min(kBlockSize, max(0, n_row - kBlockSize * t));
-      float4_t sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s2 = 0; s2 < KS; ++s2) sacc = M16::qk(pinned(kr[s2]), qb[s2], sacc);
-      float sc[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sc[i] = sacc[i] * p.scale_log2;
-        if (!full) sc[i] = (4 * g + i < row_valid) ? sc[i] : kNegInf;
-      }
-      float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      const float m_new = fmaxf(m, bm);
-      float alpha = exp2_fast(m - m_new);
-      float pr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(sc[i] - m_new);
-      if (!full) {  // partly masked rows (or a row with nothing valid yet)
-        alpha = m_new == kNegInf ? 1.f : alpha;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pr[i] = (4 * g + i < row_valid) ? pr[i] : 0.f;
-      }
-      lsum = fmaf(lsum, alpha, (pr[0] + pr[1]) + (pr[2] + pr[3]));
-      m = m_new;
-      const uint2 pb = make_uint2(M16::pack2(pr[0], pr[1]), M16::pack2(pr[2], pr[3]));
-      uint2 vt[VT];
-#pragma unroll
-      for (int j = 0; j < VT; ++j) vt[j] = pinned(vr[j]);
-      if (!full) {  // zero the V tokens no row reads
-        const int tv = id < 0 ? 0 : min(kBlockSize, max(0, nmax - kBlockSize * t));
-        const int base = 4 * g;
-        const uint32_t mx = (base + 0 < tv ? 0x0000FFFFu : 0u) | (base + 1 < tv ? 0xFFFF0000u : 0u);
-        const uint32_t my = (base + 2 < tv ? 0x0000FFFFu : 0u) | (base + 3 < tv ? 0xFFFF0000u : 0u);
-#pragma unroll
-        for (int j = 0; j < VT; ++j) vt[j] = make_uint2(vt[j].x & mx, vt[j].y & my);
-      }
-#pragma unroll
-      for (int j = 0; j < VT; ++j) o[j] = M16::pv(vt[j], pb, o[j] * alpha);
-    };
-
-    // The reloads are unconditional (past the chunk they re-read its last block): loads issued
-    // on every path keep the wait counts exact, so a tile waits only for its own loads.
-    for (int t = b0; t < b1; t += 2) {
-      compute(ka, va, t, ida);
-      ida = block_id(min(t + 2, b1 - 1));
-      load(ka, va, ida);
-      if (t + 1 < b1) compute(kb, vb, t + 1, idb);
-      idb = block_id(min(t + 3, b1 - 1));
-      load(kb, vb, idb);
-    }
-    float l = lsum + __shfl_xor(lsum, 16);
-    l += __shfl_xor(l, 32);
-    if (!row_ok) return;
-    const int qh = kvh * G + jq;
-    const int slot = qh / GS, nr = qh - slot * GS;
-    const int rel = cbase + mk * H + slot;
-    if (rel < 0 || rel >= p.shared_cells) return;
-    const size_t cell = (static_cast<size_t>(p.shared_base) + static_cast<size_t>(rel)) * GS + nr;
-#pragma unroll
-    for (int j = 0; j < VT; ++j)
-      *reinterpret_cast<float4_t*>(p.ws_o + cell * HD + 16 * j + 4 * g) = o[j];
-    if (g == 0) {
-      p.ws_ml[cell * 2] = m;
-      p.ws_ml[cell * 2 + 1] = l;
-    }
+    for (int j = 0; j < VT; ++j) vr[j] = *reinterpret_cast<const uint2*>(vt + v_lane + 512u * j);
   };
-  if (mcnt * G < kRowsPerTile) run(std::true_type{});
-  else run(std::false_type{});
+  // Two tiles in flight (buffers a and b, alternating), requested before the rows' lookups
+  // below so that their latencies overlap.
+  uint4 ka[KS], kb[KS];
+  uint2 va[VT], vb[VT];
+  int ida = block_id(b0), idb = block_id(min(b0 + 1, b1 - 1));
+  load(ka, va, ida);
+  load(kb, vb, idb);
+
+  int seq = -1;
+  if (hq < mcnt * G) seq = p.members[moff + mk];
+  const bool row_ok = seq >= 0 && seq < p.B;
+  uint4 qb[KS];
+  if (row_ok) {
+    const uint4* qp = reinterpret_cast<const uint4*>(
+        static_cast<const char*>(p.q) + (static_cast<size_t>(seq) * p.Hq + kvh * G + jq) * HD * 2);
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) qb[s2] = qp[4 * s2 + g];
+  } else {
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) qb[s2] = make_uint4(0, 0, 0, 0);
+  }
+  const int n_row = row_ok ? clamp_len(p, seq) : 0;
+  // q settled here: a first use inside the loop would put its wait (for every load issued
+  // before it, the tiles included) at the top of each iteration
+#pragma unroll
+  for (int s2 = 0; s2 < KS; ++s2) settle(qb[s2]);
+  // the rows' shortest and longest lengths: a tile ending at or before the shortest needs no
+  // masking; V tokens at or past the longest are read by no row
+  int nmin = row_ok ? n_row : 0x7fffffff, nmax = n_row;
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) {
+    nmin = min(nmin, __shfl_xor(nmin, off));
+    nmax = max(nmax, __shfl_xor(nmax, off));
+  }
+  nmin = uniform(nmin);
+  nmax = uniform(nmax);
+
+  float m = kNegInf, lsum = 0.f;
+  float4_t o[VT];
+#pragma unroll
+  for (int j = 0; j < VT; ++j) o[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const uint4 (&kr)[KS], const uint2 (&vr)[VT], int t, int id) {
+    const bool full = id >= 0 && kBlockSize * (t + 1) <= nmin;  // every row sees all 16 tokens
+    const int row_valid = id < 0 ? 0 : min(kBlockSize, max(0, n_row - kBlockSize * t));
+    float4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) sacc = M16::qk(pinned(kr[s2]), qb[s2], sacc);
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[i] = sacc[i] * p.scale_log2;
+      if (!full) sc[i] = (4 * g + i < row_valid) ? sc[i] : kNegInf;
+    }
+    float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float m_new = fmaxf(m, bm);
+    float alpha = exp2_fast(m - m_new);
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = exp2_fast(sc[i] - m_new);
+    if (!full) {  // partly masked rows (or a row with nothing valid yet)
+      alpha = m_new == kNegInf ? 1.f : alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = (4 * g + i < row_valid) ? pr[i] : 0.f;
+    }
+    lsum = fmaf(lsum, alpha, (pr[0] + pr[1]) + (pr[2] + pr[3]));
+    m = m_new;
+    const uint2 pb = make_uint2(M16::pack2(pr[0], pr[1]), M16::pack2(pr[2], pr[3]));
+    uint2 vt[VT];
+#pragma unroll
+    for (int j = 0; j < VT; ++j) vt[j] = pinned(vr[j]);
+    if (!full) {  // zero the V tokens no row reads
+      const int tv = id < 0 ? 0 : min(kBlockSize, max(0, nmax - kBlockSize * t));
+      const int base = 4 * g;
+      const uint32_t mx = (base + 0 < tv ? 0x0000FFFFu : 0u) | (base + 1 < tv ? 0xFFFF0000u : 0u);
+      const uint32_t my = (base + 2 < tv ? 0x0000FFFFu : 0u) | (base + 3 < tv ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int j = 0; j < VT; ++j) vt[j] = make_uint2(vt[j].x & mx, vt[j].y & my);
+    }
+#pragma unroll
+    for (int j = 0; j < VT; ++j) o[j] = M16::pv(vt[j], pb, o[j] * alpha);
+  };
+
+  // The reloads are unconditional (past the chunk they re-read its last block): loads issued
+  // on every path keep the wait counts exact, so a tile waits only for its own loads.
+  for (int t = b0; t < b1; t += 2) {
+    compute(ka, va, t, ida);
+    ida = block_id(min(t + 2, b1 - 1));
+    load(ka, va, ida);
+    if (t + 1 < b1) compute(kb, vb, t + 1, idb);
+    idb = block_id(min(t + 3, b1 - 1));
+    load(kb, vb, idb);
+  }
+  float l = lsum + __shfl_xor(lsum, 16);
+  l += __shfl_xor(l, 32);
+  if (!row_ok) return;
+  const int qh = kvh * G + jq;
+  const int slot = qh / GS, nr = qh - slot * GS;
+  const int rel = cbase + mk * H + slot;
+  if (rel < 0 || rel >= p.shared_cells) return;
+  const size_t cell = (static_cast<size_t>(p.shared_base) + static_cast<size_t>(rel)) * GS + nr;
+#pragma unroll
+  for (int j = 0; j < VT; ++j)
+    *reinterpret_cast<float4_t*>(p.ws_o + cell * HD + 16 * j + 4 * g) = o[j];
+  if (g == 0) {
+    p.ws_ml[cell * 2] = m;
+    p.ws_ml[cell * 2 + 1] = l;
+  }
 }
 
 // ------------------------------------------------------------------------------------------
