@@ -391,6 +391,9 @@ attn_prefill_kernel(const StreamParams p) {
         sa[k] = MM::mul(kf1[s2], qb[k][s2], sa[k]);
         sbv[k] = MM::mul(kf2[s2], qb[k][s2], sbv[k]);
       }
+    // every K fragment read issued before the first contraction waits on one
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * KS * RT, 0);
   };
 
   // Softmax and p . v of stage t (block ids ida, idb) from its scores (sa, sbv).
