@@ -199,6 +199,9 @@ def parse():
                          "staging kernel costs the device about 5 us per step)")
     ap.add_argument("--no-plan", action="store_true",
                     help="decode batches that share blocks without a shared-prefix plan")
+    ap.add_argument("--shared-launch", choices=("auto", "one", "two"), default="auto",
+                    help="planned batches: the shared pass and the stream pass as the library "
+                         "chooses per step (auto), in one launch, or in two")
     ap.add_argument("--with-prefill", action="store_true",
                     help="batching workloads: each step also runs the admitted prompts' causal "
                          "prefill attention (a full serving step)")
@@ -245,8 +248,9 @@ class Workload:
     """Sequences held by the C++ allocator plus device caches filled with seeded values."""
 
     def __init__(self, name, total_steps, torch, pkv, W, plan=True, duplicate_prefix=False,
-                 engine=True):
+                 engine=True, shared_launch="auto"):
         self.name = name
+        self.shared_launch = shared_launch
         self.torch = torch
         self.duplicate_prefix = duplicate_prefix and name == "prefix_shared"
         # shared-prefix plans for the batches that share blocks
@@ -365,8 +369,16 @@ class Workload:
         if engine:
             self.engine = pkv.Engine(self.alloc, self.k_cache, self.v_cache, num_q_heads=self.Hq,
                                      num_kv_heads=self.Hkv, head_dim=self.hd, max_batch=self.B,
-                                     max_context_len=self.max_ctx, plan=self.planned)
+                                     max_context_len=self.max_ctx, plan=self.planned,
+                                     shared_launch=shared_launch)
             self.engine.adopt(self.seqs)
+
+    def launches(self, plan, pkv):
+        """Launches (1 or 2) of the shared and stream passes the library's automatic choice
+        gives this plan."""
+        return pkv.pkv_decode_planned_launches(plan, batch=self.B, num_q_heads=self.Hq,
+                                               num_kv_heads=self.Hkv, max_blocks=self.max_blocks,
+                                               dtype=self.dt, num_workers=self.W)
 
     def planned_skip(self):
         """Each sequence's blocks covered by the shared pass this step (zeros unplanned)."""
@@ -555,11 +567,15 @@ def attend(wl, pkv, s, events):
     if wl.planned:
         plan = wl.pin[s].numpy()[wl.plan0:wl.plan0 + wl.plan_len[s]]
         plan_d = wl.dev[s][wl.plan0:wl.plan0 + wl.plan_len[s]]
+        form = wl.shared_launch
+        if form == "auto" and events is not None:  # the events between the kernels it runs
+            form = "one" if wl.launches(plan, pkv) == 1 else "two"
         pkv.pkv_decode_planned(wl.q, wl.k_cache, wl.v_cache, tables_d, lens_d, plan, plan_d,
                                num_kv_heads=wl.Hkv, scale=wl.scale, max_context_len=wl.max_ctx,
                                num_workers=wl.W, workspace=wl.workspace, k_new=wl.k_new,
                                v_new=wl.v_new, out=wl.out,
-                               events=None if events is None else events[2:5])
+                               events=None if events is None else events[2:5],
+                               shared_launch=form)
     else:  # [2] == [1]: no shared pass
         # 3 + 4a. cache write of the newest tokens fused into the attention stream pass
         pkv.pkv_decode_append_stream(wl.q, wl.k_new, wl.v_new, wl.k_cache, wl.v_cache, tables_d,
@@ -1112,7 +1128,7 @@ def main():
         prefill_main(args, torch, pkv, W)
         return
     wl = Workload(args.workload, args.warmup + 1 + args.steps, torch, pkv, W, plan=not args.no_plan,
-                  duplicate_prefix=args.duplicate_prefix,
+                  duplicate_prefix=args.duplicate_prefix, shared_launch=args.shared_launch,
                   engine=args.driver == "engine" or (args.driver == "auto" and
                                                      args.workload == "beam_search"))
     torch.cuda.synchronize()
@@ -1183,7 +1199,23 @@ def main():
     kv_shared = [wl.unique_kv_bytes(lens, unmarked(final_tables if t is None else t), upto=sk)
                  for lens, t, sk in per_step]
     kv_private = [a - b for a, b in zip(kv, kv_shared)]
-    algo = [kv_private[k] + wl.qo_bytes() for k in timed]
+    # planned steps: the shared and stream passes' launches per timed step (the automatic
+    # choice from each step's plan, rebuilt here from its tables and lengths). One launch: the
+    # roofline kernel reads every unique block; two: the stream pass reads the private ones
+    launches = [0] * len(timed)
+    if wl.planned:
+        for n, k in enumerate(timed):
+            lens_k, t_k, _ = per_step[k]
+            if wl.shared_launch != "auto":
+                launches[n] = 1 if wl.shared_launch == "one" else 2
+                continue
+            plan_k = pkv.pkv_decode_plan(final_tables if t_k is None else t_k, lens_k,
+                                         num_q_heads=wl.Hq, num_kv_heads=wl.Hkv,
+                                         num_blocks=wl.NB, max_context_len=wl.max_ctx,
+                                         dtype=wl.dt)
+            launches[n] = wl.launches(plan_k, pkv)
+    one_launch = wl.planned and all(x == 1 for x in launches)
+    algo = [(kv[k] if x == 1 else kv_private[k]) + wl.qo_bytes() for k, x in zip(timed, launches)]
     attn_ms = [a + b + c for a, b, c in zip(shared_ms, part_ms, merge_ms)]
     kv_t = [kv[k] for k in timed]
     kv_logical_t = [kv_logical[k] for k in timed]
@@ -1245,8 +1277,9 @@ def main():
                      "back-to-back steps; value and ms_per_step are wall-clock over every step, "
                      "kernel times from the events of every n-th step"),
             "kernel_ms": {name: ms_stats(v) for name, v in
-                          (("stream", part_ms), ("merge", merge_ms), ("attention", attn_ms))
-                          + ((("shared", shared_ms),) if wl.planned else ())
+                          (("shared_and_stream" if one_launch else "stream", part_ms),
+                           ("merge", merge_ms), ("attention", attn_ms))
+                          + ((("shared", shared_ms),) if wl.planned and not one_launch else ())
                           + ((("cow_copy", copy_ms),) if wl.beam else ())
                           + ((("staging_upload", staging_ms),) if staging_ms else ())
                           + ((("step", [a + b + c for a, b, c in
@@ -1260,24 +1293,32 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": f"attention stream pass ({['', 'vector', 'matrix-core'][wl.kernel]} kernel)",
+            "kernel": ("shared pass + stream pass, one launch (attn_fused_kernel)" if one_launch
+                       else f"attention stream pass ({['', 'vector', 'matrix-core'][wl.kernel]} "
+                            "kernel)"),
             "algorithmic_bytes_per_launch": int(np.mean(algo)),
         },
     }
     if wl.planned:
         sh = sum(kv_shared_t)
         res["shared_prefix_plan"] = {
-            "shared_pass_ms": round(float(np.mean(shared_ms)), 4),
+            "shared_launch": wl.shared_launch,
+            "launches_per_step": {"one": launches.count(1), "two": launches.count(2)},
+            "shared_pass_ms": None if one_launch else round(float(np.mean(shared_ms)), 4),
             "shared_unique_bytes_per_step": int(np.mean(kv_shared)),
             "private_unique_bytes_per_step": int(np.mean(kv_private)),
-            "shared_pass_gbs": round(sh / (sum(shared_ms) / 1e3) / 1e9, 2) if sh else None,
+            "shared_pass_gbs": (round(sh / (sum(shared_ms) / 1e3) / 1e9, 2)
+                                if sh and not one_launch else None),
             "attention_ms": round(float(np.mean(attn_ms)), 4),
             "attention_unique_gbs": round((sum(kv_t) + len(timed) * wl.qo_bytes())
                                           / (sum(attn_ms) / 1e3) / 1e9, 2),
             "attention_frac_of_hbm_peak": round((sum(kv_t) + len(timed) * wl.qo_bytes())
                                                 / (sum(attn_ms) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-            "note": "three kernels per step (shared pass, stream pass over the private blocks, "
-                    "merge); roofline above is the stream pass over the private bytes",
+            "note": ("two kernels per step (the shared pass and the stream pass over the "
+                     "private blocks in one launch, then the merge); roofline above is that "
+                     "launch over every unique byte" if one_launch else
+                     "three kernels per step (shared pass, stream pass over the private blocks, "
+                     "merge); roofline above is the stream pass over the private bytes"),
         }
     if wl.beam:
         # copy-on-write copies: both caches, every kv head, read + written

@@ -246,14 +246,30 @@ pkv_status pkv_decode_plan(const int32_t* block_tables, const int32_t* context_l
                            int32_t NB, pkv_dtype dtype, int32_t max_group, int32_t* plan,
                            size_t capacity, size_t* plan_ints);
 
+/* Launches (1 or 2) of the shared and stream passes that pkv_decode_planned's passes 0 and 4   */
+/* use for this plan: one where the one-launch kernel exists and the plan's shared pass reads  */
+/* at least as many (block, head) tiles as its stream pass (then the stream pass's short      */
+/* ranges fill the device beside the shared pass; where the stream pass dominates, the shared */
+/* pass's work-groups would start in its tail and lengthen it), else two; one for a plan      */
+/* without units. Host only; plan as for pkv_decode_planned (the same B, heads, dtype,        */
+/* max_blocks and num_workers). 0 on bad arguments or a plan that fails validation.            */
+int32_t pkv_decode_planned_launches(const int32_t* plan, size_t plan_ints, int32_t B,
+                                    int32_t Hq, int32_t Hkv, int32_t max_blocks,
+                                    pkv_dtype dtype, int32_t num_workers);
+
 /* Workspace bytes of pkv_decode_planned (stream cells plus B*H private and the plan's shared   */
 /* cells); 0 on bad arguments or a plan built for another shape.                              */
 size_t pkv_decode_planned_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t hd,
                                           pkv_dtype dtype, int32_t num_workers,
                                           const int32_t* plan, size_t plan_ints);
 
-/* The planned decode step. pass: 0 all three kernels in order, 1 the shared pass, 2 the       */
-/* stream pass, 3 the merge (run 1, 2, 3 in that order on one stream; exported to time them). */
+/* The planned decode step. pass: 0 the whole step (passes 4 and 3), 1 the shared pass, 2 the  */
+/* stream pass, 3 the merge, 4 the shared and stream passes as pkv_decode_planned_launches    */
+/* chooses (one launch or passes 1 and 2), 5 those two passes in one launch where it exists   */
+/* (exported to time them: run 1, 2, 3 or 4, 3 or 5, 3 in that order on one stream). The one  */
+/* launch exists for the vector stream kernel (G = 1, or pkv_set_attn_kernel(1)) with         */
+/* num_workers a multiple of 32; elsewhere pass 5 is passes 1 and 2. Every pass order gives    */
+/* bit-identical results.                                                                     */
 /* k_new/v_new NULL: attention as pkv_decode_attn; non-NULL: the fused step of                 */
 /* pkv_decode_append_attn (same contract; additionally no sequence's newest-token block may be */
 /* in a run, which the plan check enforces through blocks[] and skip[]). plan_host and        */
@@ -564,11 +580,17 @@ typedef struct pkv_engine pkv_engine;
 
 /* Shared-prefix plans (pkv_decode_plan, default max_group) for every decode step. */
 #define PKV_ENGINE_PLAN 1
+/* With PKV_ENGINE_PLAN: run the shared pass and the stream pass as two launches (passes 1 and */
+/* 2 of pkv_decode_planned), or as one (pass 5), rather than as pkv_decode_planned_launches    */
+/* chooses per step (pass 4). Same results; for measuring the forms. Not both.                */
+#define PKV_ENGINE_SPLIT_SHARED 2
+#define PKV_ENGINE_ONE_LAUNCH 4
 
 /* alloc: the allocator of the NB-block pool the caches hold (the caller keeps ownership).    */
 /* k_cache, v_cache: device caches in the layout above. max_batch: most running sequences     */
 /* (<= 8192); max_context_len: longest sequence, which fixes the tables' width                 */
-/* ceil(max_context_len/16). flags: 0 or PKV_ENGINE_PLAN. Errors: PKV_ERR_INVALID_ARG,          */
+/* ceil(max_context_len/16). flags: 0, PKV_ENGINE_PLAN, or PKV_ENGINE_PLAN with one of         */
+/* PKV_ENGINE_SPLIT_SHARED and PKV_ENGINE_ONE_LAUNCH. Errors: PKV_ERR_INVALID_ARG,               */
 /* PKV_ERR_UNSUPPORTED, PKV_ERR_HIP.                                                            */
 pkv_status pkv_engine_create(pkv_allocator* alloc, void* k_cache, void* v_cache, int32_t NB,
                              int32_t Hq, int32_t Hkv, int32_t hd, pkv_dtype dtype,
@@ -622,8 +644,10 @@ int32_t pkv_engine_queued(const pkv_engine* e);
 /* events: NULL or 8 hipEvent_t (each may be NULL) recorded on the stream: [0] before the      */
 /* upload of the step's staged tables, lengths, slots and plans (a small copy kernel that      */
 /* reads the pinned set), [1] after it, [2] after the prompt write, [3] after the copies, [4]  */
-/* after the prefill, [5] after the shared pass, [6] after the stream pass, [7] after the      */
-/* merge. info: NULL or host                                                                   */
+/* after the prefill, [5] after the shared pass (unless PKV_ENGINE_SPLIT_SHARED: before the   */
+/* shared and stream passes, one launch or two, so that [5]..[6] spans both), [6] after the   */
+/* stream pass, [7] after the merge.                                                           */
+/* info: NULL or host                                                                          */
 /* int64 [8] = {B, T, retired, admitted, plan units (-1: unplanned), copy-on-write pairs,      */
 /* queued after the step, k}.                                                                  */
 pkv_status pkv_engine_step(pkv_engine* e, const void* q, const void* k_new, const void* v_new,

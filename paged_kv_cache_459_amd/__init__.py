@@ -12,7 +12,8 @@ from .api import (BLOCK_SIZE, ENGINE_PLAN, BlockAllocator, Engine, alloc_caches,
                   pkv_decode_append_stream,
                   pkv_decode_attn, pkv_decode_kernel, pkv_decode_merge,
                   pkv_decode_num_workers, pkv_decode_plan, pkv_decode_planned,
-                  pkv_decode_planned_workspace_bytes, pkv_decode_stream,
+                  pkv_decode_planned_launches, pkv_decode_planned_workspace_bytes,
+                  pkv_decode_stream,
                   pkv_decode_stream_workspace_bytes,
                   pkv_decode_workspace_bytes, pkv_dtype, pkv_prefill_attn, pkv_prefill_plan,
                   pkv_prefill_workspace_bytes, pkv_probe_read, pkv_set_attn_kernel, pkv_write,

@@ -91,6 +91,8 @@ SIGNATURES = {
                                 c_vp, c_sz, ctypes.POINTER(c_sz)]),
     "pkv_decode_planned_workspace_bytes": (c_sz, [c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_vp,
                                                    c_sz]),
+    "pkv_decode_planned_launches": (c_i32, [c_vp, c_sz, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                            c_i32]),
     "pkv_decode_planned": (c_i32, [c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32,
                                    c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_f32, c_i32,
                                    c_vp, c_vp, c_sz, c_i32, c_vp, c_sz, c_vp]),

@@ -341,12 +341,18 @@ def pkv_decode_planned_workspace_bytes(batch, num_q_heads, num_kv_heads, head_di
 
 def pkv_decode_planned(q, k_cache, v_cache, block_tables, context_lens, plan, plan_dev, *,
                        num_kv_heads, scale, max_context_len, num_workers, workspace,
-                       k_new=None, v_new=None, out=None, passes=0, events=None):
+                       k_new=None, v_new=None, out=None, passes=0, events=None,
+                       shared_launch="auto"):
     """Decode step with a shared-prefix plan (see include/pkv.h). plan: the host plan (NumPy
     int32), plan_dev: the same ints on the device (int32 tensor). With k_new / v_new it is the
-    fused newest-token step. passes: 0 all, 1 shared pass, 2 stream pass, 3 merge. events:
-    three torch.cuda.Events to record after the shared pass, the stream pass and the merge
-    (the three passes then run as three calls, arguments checked once)."""
+    fused newest-token step. passes: 0 all, 1 shared pass, 2 stream pass, 3 merge, 4 shared
+    and stream pass as the library chooses, 5 those two in one launch. events: three
+    torch.cuda.Events to record after the shared pass, the stream pass and the merge; the
+    passes then run as separate calls, the shared and stream passes as shared_launch says:
+    "auto" (pass 4) or "one" (pass 5), the first event recorded before them, or "two" (passes
+    1 and 2)."""
+    if shared_launch not in ("auto", "one", "two"):
+        raise ValueError("shared_launch is 'auto', 'one' or 'two'")
     out, B, hq, hd, nb, mb = _decode_args(q, k_cache, v_cache, block_tables, context_lens,
                                           num_kv_heads, out)
     if (k_new is None) != (v_new is None):
@@ -364,11 +370,26 @@ def pkv_decode_planned(q, k_cache, v_cache, block_tables, context_lens, plan, pl
             num_workers, _ptr(workspace), ws_bytes, _stream(q.device))
     if events is None:
         check(lib.pkv_decode_planned(int(passes), *args), "pkv_decode_planned")
-    else:
+    elif shared_launch == "two":
         for ps, ev in zip((1, 2, 3), events):
             check(lib.pkv_decode_planned(ps, *args), "pkv_decode_planned")
             ev.record()
+    else:
+        events[0].record()
+        for ps, ev in zip((4 if shared_launch == "auto" else 5, 3), events[1:]):
+            check(lib.pkv_decode_planned(ps, *args), "pkv_decode_planned")
+            ev.record()
     return out
+
+
+def pkv_decode_planned_launches(plan, *, batch, num_q_heads, num_kv_heads, max_blocks, dtype,
+                                num_workers):
+    """Launches (1 or 2) of the shared and stream passes that pkv_decode_planned's automatic
+    choice gives this plan (host only; 0 for a plan that fails validation)."""
+    p = _as_c(plan, np.int32)
+    return int(lib.pkv_decode_planned_launches(p.ctypes.data, p.size, batch, num_q_heads,
+                                               num_kv_heads, max_blocks, pkv_dtype(dtype),
+                                               num_workers))
 
 
 PREFILL_MAX_BLOCKS = 512  # blocks of one prefill unit (longer rows are split and merged)
@@ -613,6 +634,8 @@ class BlockAllocator:
 
 
 ENGINE_PLAN = 1  # PKV_ENGINE_PLAN
+ENGINE_SPLIT_SHARED = 2  # PKV_ENGINE_SPLIT_SHARED
+ENGINE_ONE_LAUNCH = 4  # PKV_ENGINE_ONE_LAUNCH
 _ENGINE_EVENTS = 8
 
 
@@ -632,7 +655,7 @@ class Engine:
     Borrows ``allocator`` (kept alive here) and the caches. Not thread-safe."""
 
     def __init__(self, allocator, k_cache, v_cache, *, num_q_heads, num_kv_heads, head_dim,
-                 max_batch, max_context_len, plan=False):
+                 max_batch, max_context_len, plan=False, shared_launch="auto"):
         for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
             _need(t, name)
         self.alloc = allocator
@@ -646,7 +669,11 @@ class Engine:
         h = ctypes.c_void_p()
         check(lib.pkv_engine_create(allocator._h, _ptr(k_cache), _ptr(v_cache), self.nb,
                                     num_q_heads, num_kv_heads, head_dim, pkv_dtype(k_cache),
-                                    self.max_batch, self.max_ctx, ENGINE_PLAN if plan else 0,
+                                    self.max_batch, self.max_ctx,
+                                    (ENGINE_PLAN if plan else 0)
+                                    | ({"auto": 0, "one": ENGINE_ONE_LAUNCH,
+                                        "two": ENGINE_SPLIT_SHARED}[shared_launch]
+                                       if plan else 0),
                                     ctypes.byref(h)), "pkv_engine_create")
         self._h = h
         self.info = np.zeros(8, np.int64)

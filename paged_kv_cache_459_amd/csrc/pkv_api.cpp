@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -352,6 +353,51 @@ pkv_status pkv_decode_plan(const int32_t* block_tables, const int32_t* context_l
   return PKV_OK;
 }
 
+}  // extern "C"
+
+namespace pkv {
+
+// Launches of a validated plan's shared and stream passes under the automatic choice: one
+// where the one-launch kernel exists and the shared pass reads at least as many (block, head)
+// tiles as the stream pass, else two (one when the plan has no units: no shared pass). Where
+// the stream pass dominates, the shared pass's work-groups, which start as stream work-groups
+// end, lengthen the stream pass's tail; where the shared pass dominates, the stream pass's
+// short ranges fill the compute units beside it.
+int32_t planned_launches(const int32_t* plan, int32_t B, int32_t Hkv, int32_t dtype,
+                         int32_t kernel, int32_t W) {
+  const int32_t H = plan[2], U = plan[4];
+  if (U == 0) return 1;
+  if (!fused_kernel_exists(dtype, kernel, W)) return 2;
+  const int32_t* skip = plan + kPlanHeader;
+  const int32_t* blocks = skip + B;
+  const int32_t* units = blocks + 2 * static_cast<size_t>(B) + 1;  // past sh_ptr[B + 1]
+  int64_t stream_tiles = 0, shared_tiles = 0;
+  for (int32_t s = 0; s < B; ++s) stream_tiles += std::max(0, blocks[s] - skip[s]);
+  for (int32_t u = 0; u < U; ++u)
+    shared_tiles += units[static_cast<size_t>(u) * kUnitInts + 2] -
+                    units[static_cast<size_t>(u) * kUnitInts + 1];
+  return shared_tiles * Hkv >= stream_tiles * H ? 1 : 2;
+}
+
+}  // namespace pkv
+
+extern "C" {
+
+int32_t pkv_decode_planned_launches(const int32_t* plan, size_t plan_ints, int32_t B,
+                                    int32_t Hq, int32_t Hkv, int32_t max_blocks,
+                                    pkv_dtype dtype, int32_t num_workers) {
+  if (!plan || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_blocks <= 0 ||
+      !dtype_ok(dtype) || num_workers <= 0 || num_workers % pkv::kWaves != 0)
+    return 0;
+  const int32_t kernel = current_kernel(dtype, Hq, Hkv);
+  const int32_t G = Hq / Hkv;
+  const int32_t H = kernel == pkv::kMatrix ? Hkv : Hq;
+  const int32_t GS = kernel == pkv::kMatrix ? G : 1;
+  pkv::PlanView pv;
+  if (!pkv::plan_check(plan, plan_ints, B, max_blocks, H, GS, G, false, &pv)) return 0;
+  return pkv::planned_launches(plan, B, Hkv, dtype, kernel, num_workers);
+}
+
 size_t pkv_decode_planned_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t hd,
                                           pkv_dtype dtype, int32_t num_workers,
                                           const int32_t* plan, size_t plan_ints) {
@@ -376,7 +422,7 @@ pkv_status pkv_decode_planned(int32_t pass, void* out, const void* q, const void
                               pkv_dtype dtype, const int32_t* plan_host, const int32_t* plan_dev,
                               size_t plan_ints, int32_t num_workers, void* workspace,
                               size_t workspace_bytes, void* stream) {
-  if (pass < 0 || pass > 3) return PKV_ERR_INVALID_ARG;
+  if (pass < 0 || pass > 5) return PKV_ERR_INVALID_ARG;
   pkv_status st = validate_decode(out, q, k_cache, v_cache, block_tables, context_lens, B, Hq,
                                   Hkv, hd, bs, NB, max_blocks, max_context_len, scale, dtype);
   if (st != PKV_OK) return st;
@@ -418,9 +464,14 @@ pkv_status pkv_decode_planned(int32_t pass, void* out, const void* q, const void
   p.num_units = pv.U;
   p.shared_cells = pv.cells;
   p.shared_base = 2 * W + B * L0.H;
-  if ((pass == 0 || pass == 1) && pkv::launch_shared(p, dtype, kernel, hs) != hipSuccess)
+  const bool one = pass == 5 || ((pass == 0 || pass == 4) &&
+                                 pkv::planned_launches(plan_host, B, Hkv, dtype, kernel, W) == 1);
+  if (one && pkv::launch_fused(p, dtype, kernel, hs) != hipSuccess) return PKV_ERR_HIP;
+  if ((pass == 1 || (!one && (pass == 0 || pass == 4))) &&
+      pkv::launch_shared(p, dtype, kernel, hs) != hipSuccess)
     return PKV_ERR_HIP;
-  if ((pass == 0 || pass == 2) && pkv::launch_stream(p, dtype, kernel, hs) != hipSuccess)
+  if ((pass == 2 || (!one && (pass == 0 || pass == 4))) &&
+      pkv::launch_stream(p, dtype, kernel, hs) != hipSuccess)
     return PKV_ERR_HIP;
   if ((pass == 0 || pass == 3) && pkv::launch_merge(p, dtype, kernel, hs) != hipSuccess)
     return PKV_ERR_HIP;

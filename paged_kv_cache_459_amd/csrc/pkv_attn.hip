@@ -379,14 +379,16 @@ __device__ __forceinline__ TileInfo tile_info(const StreamParams& p, const int* 
                              (whole << 7) | (end << 6) | (start << 5) | valid};
 }
 
-// This wave's worker index and tile range [t0, t1). Work-group b runs on XCD b % 8; logical
-// work-group (b % 8) * (grid / 8) + b / 8 gives each XCD a contiguous share of the workers.
+// This wave's worker index and tile range [t0, t1), for work-group b of the stream pass's
+// grid work-groups. Work-group b runs on XCD b % 8 (when the stream pass's work-groups start
+// a launch, or follow a multiple of 8 others); logical work-group (b % 8) * (grid / 8) + b / 8
+// gives each XCD a contiguous share of the workers.
 struct Range {
   int worker, t0, t1;
 };
 
-__device__ __forceinline__ Range worker_range(const StreamParams& p, int C, int H) {
-  const int grid = gridDim.x, b = blockIdx.x;
+__device__ __forceinline__ Range worker_range(const StreamParams& p, int C, int H, int b,
+                                              int grid) {
   const int lwg = (grid % 8 == 0) ? (b % 8) * (grid / 8) + b / 8 : b;
   const int worker = lwg * kWaves + uniform(threadIdx.x >> 6);
   const int T = H * C;
@@ -399,8 +401,8 @@ __device__ __forceinline__ Range worker_range(const StreamParams& p, int C, int 
 // Work-group 0 publishes the prefix sums for the merge pass and zeroes rows with n = 0 (a
 // planned sequence with no private block is finished by the merge).
 template <int DT>
-__device__ void publish_and_zero(const StreamParams& p, const int* pref) {
-  if (blockIdx.x != 0) return;
+__device__ void publish_and_zero(const StreamParams& p, const int* pref, int b) {
+  if (b != 0) return;
   for (int i = threadIdx.x; i <= p.B; i += kThreads) p.ws_seg[i] = pref[i];
   const int row = p.Hq * p.hd;
   for (int i = 0; i < p.B; ++i) {
@@ -424,8 +426,7 @@ __device__ void publish_and_zero(const StreamParams& p, const int* pref) {
 //    row of 16 tokens spans LPR = element-bytes lanes. The probabilities of those X tokens are
 //    broadcast through LDS; the per-lane sums are added over the LPR lanes at the end.
 template <int DT, int HD>
-__global__ void __launch_bounds__(kThreads)
-attn_vector_kernel(const StreamParams p) {
+__device__ __forceinline__ void vector_pass(const StreamParams& p, int b, int grid) {
   using E = Elem<DT>;
   constexpr int EB = E::kBytes;
   constexpr int X = 16 / EB;
@@ -441,9 +442,9 @@ attn_vector_kernel(const StreamParams p) {
   __shared__ uint4 s_new[kWaves][2][NR];  // append mode: the segment's newest K and V rows
 
   scan_block_counts(p, s_pref);
-  publish_and_zero<DT>(p, s_pref);
+  publish_and_zero<DT>(p, s_pref, b);
   const int C = s_pref[p.B];
-  const Range rg = worker_range(p, C, p.Hq);
+  const Range rg = worker_range(p, C, p.Hq, b, grid);
   if (rg.t0 >= rg.t1) return;
 
   const int lane = threadIdx.x & 63;
@@ -615,6 +616,12 @@ attn_vector_kernel(const StreamParams p) {
   }
 }
 
+template <int DT, int HD>
+__global__ void __launch_bounds__(kThreads)
+attn_vector_kernel(const StreamParams p) {
+  vector_pass<DT, HD>(p, blockIdx.x, gridDim.x);
+}
+
 // ------------------------------------------------------------------------------------------
 // Matrix-core kernel: one kv head and its G <= 16 q heads per segment (f16/bf16).
 //
@@ -674,9 +681,9 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_matrix_kernel(const StreamParams p)
   __shared__ uint4 s_new[kWaves][2][NR];  // append mode: the segment's newest K and V rows
 
   scan_block_counts(p, s_pref);
-  publish_and_zero<DT>(p, s_pref);
+  publish_and_zero<DT>(p, s_pref, blockIdx.x);
   const int C = s_pref[p.B];
-  const Range rg = worker_range(p, C, p.Hkv);
+  const Range rg = worker_range(p, C, p.Hkv, blockIdx.x, gridDim.x);
   if (rg.t0 >= rg.t1) return;
 
   const int lane = threadIdx.x & 63;
@@ -862,14 +869,13 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_matrix_kernel(const StreamParams p)
 // shared_base + cell_base + member*H + head slot, row (q head % GS), in the stream pass's
 // layout.
 template <int DT, int HD>
-__global__ void __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(3))) attn_shared_kernel(const StreamParams p, int H, int GS) {
+__device__ __forceinline__ void shared_pass(const StreamParams& p, int H, int GS, int b,
+                                            int grid) {
   using M16 = Mfma<DT>;
   constexpr int TILE = HD * kBlockSize * 2;
   constexpr int KS = HD / 32;  // QK steps
   constexpr int VT = HD / 16;  // PV dim tiles
 
-  const int grid = gridDim.x, b = blockIdx.x;
   const int lwg = (grid % 8 == 0) ? (b % 8) * (grid / 8) + b / 8 : b;
   const int gw = lwg * kWaves + uniform(threadIdx.x >> 6);
   const int U = p.num_units;
@@ -1018,6 +1024,28 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_shared_kernel(const StreamParams p,
     p.ws_ml[cell * 2] = m;
     p.ws_ml[cell * 2 + 1] = l;
   }
+}
+
+template <int DT, int HD>
+__global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(3))) attn_shared_kernel(const StreamParams p, int H, int GS) {
+  shared_pass<DT, HD>(p, H, GS, blockIdx.x, gridDim.x);
+}
+
+// Shared pass and vector stream pass in one launch (G = 1): work-groups [0, stream_wgs) are the
+// stream pass's workers, the rest the shared pass's (unit, kv head) waves. The two write
+// disjoint cells and read only what both kernels read when launched apart, so every result is
+// bit-identical to the two-launch order. The stream work-groups come first: the dispatcher
+// starts them on every compute unit, and the shared pass's short work-groups take the slots
+// left beside them (at most 128 VGPRs, four waves per SIMD) and those that the stream pass
+// frees as it ends.
+template <int DT, int HD>
+__global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(4))) attn_fused_kernel(const StreamParams p, int H, int GS,
+                                                         int stream_wgs) {
+  const int b = blockIdx.x;
+  if (b < stream_wgs) vector_pass<DT, HD>(p, b, stream_wgs);
+  else shared_pass<DT, HD>(p, H, GS, b - stream_wgs, gridDim.x - stream_wgs);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1232,17 +1260,38 @@ void launch_stream_t(const StreamParams& p, int32_t kernel, dim3 grid, size_t ld
   hipLaunchKernelGGL((attn_vector_kernel<DT, HD>), grid, dim3(kThreads), lds, stream, p);
 }
 
+int64_t shared_wgs(const StreamParams& p);
+
 template <int DT>
 void launch_shared_t(const StreamParams& p, int H, int GS, hipStream_t stream) {
-  const int64_t waves = static_cast<int64_t>(p.num_units) * p.Hkv;
-  int64_t grid = (waves + kWaves - 1) / kWaves;
-  grid = (grid + 7) / 8 * 8;  // a multiple of 8 for the XCD-contiguous mapping
+  const int64_t grid = shared_wgs(p);
   if (p.hd == 64)
     hipLaunchKernelGGL((attn_shared_kernel<DT, 64>), dim3(static_cast<unsigned>(grid)),
                        dim3(kThreads), 0, stream, p, H, GS);
   else
     hipLaunchKernelGGL((attn_shared_kernel<DT, 128>), dim3(static_cast<unsigned>(grid)),
                        dim3(kThreads), 0, stream, p, H, GS);
+}
+
+// Work-groups of the shared pass: one wave per (unit, kv head), a multiple of 8 work-groups
+// for the XCD-contiguous mapping.
+int64_t shared_wgs(const StreamParams& p) {
+  const int64_t waves = static_cast<int64_t>(p.num_units) * p.Hkv;
+  const int64_t grid = (waves + kWaves - 1) / kWaves;
+  return (grid + 7) / 8 * 8;
+}
+
+template <int DT>
+void launch_fused_t(const StreamParams& p, int H, int GS, hipStream_t stream) {
+  const int stream_wgs = p.num_workers / kWaves;
+  const dim3 grid(static_cast<unsigned>(stream_wgs + shared_wgs(p)));
+  const size_t lds = stream_lds_bytes(p.B);
+  if (p.hd == 64)
+    hipLaunchKernelGGL((attn_fused_kernel<DT, 64>), grid, dim3(kThreads), lds, stream, p, H, GS,
+                       stream_wgs);
+  else
+    hipLaunchKernelGGL((attn_fused_kernel<DT, 128>), grid, dim3(kThreads), lds, stream, p, H,
+                       GS, stream_wgs);
 }
 
 template <int DT>
@@ -1333,6 +1382,23 @@ hipError_t launch_shared(const StreamParams& p, int32_t dtype, int32_t kernel,
     default: return note_error("attn_shared_kernel (f16/bf16 only)", hipErrorInvalidValue);
   }
   return note_error("attn_shared_kernel launch", hipGetLastError());
+}
+
+bool fused_kernel_exists(int32_t dtype, int32_t kernel, int32_t num_workers) {
+  return kernel == kVector && (dtype == 1 || dtype == 2) && num_workers > 0 &&
+         num_workers % (8 * kWaves) == 0;
+}
+
+hipError_t launch_fused(const StreamParams& p, int32_t dtype, int32_t kernel,
+                        hipStream_t stream) {
+  if (p.num_units == 0 || !fused_kernel_exists(dtype, kernel, p.num_workers)) {
+    const hipError_t e = launch_shared(p, dtype, kernel, stream);
+    return e != hipSuccess ? e : launch_stream(p, dtype, kernel, stream);
+  }
+  (void)hipGetLastError();
+  if (dtype == 1) launch_fused_t<1>(p, p.Hq, 1, stream);
+  else launch_fused_t<2>(p, p.Hq, 1, stream);
+  return note_error("attn_fused_kernel launch", hipGetLastError());
 }
 
 hipError_t launch_merge(const StreamParams& p, int32_t dtype, int32_t kernel,

@@ -388,15 +388,31 @@ pkv_status decode_tail(pkv_engine* e, int s, Layout& lay, int32_t T, int32_t A,
   record(events, 4, stream);
   if (B > 0) {
     if (planned) {
-      // with events the three passes are separate calls, so that the events fall between them
-      for (int pass = events ? 1 : 0; pass <= (events ? 3 : 0); ++pass) {
+      // The shared pass and the stream pass as one launch (PKV_ENGINE_ONE_LAUNCH, pass 5), as
+      // two (PKV_ENGINE_SPLIT_SHARED, passes 1 and 2), or as the library chooses for the plan
+      // (pass 0); then the merge (pass 3). With events the passes are separate calls, so that
+      // the events fall between the kernels (the automatic choice taken here); event 5 marks
+      // the start of the one launch.
+      bool split = (e->flags & PKV_ENGINE_SPLIT_SHARED) != 0;
+      bool one = (e->flags & PKV_ENGINE_ONE_LAUNCH) != 0;
+      if (events && !split && !one) {
+        const int32_t kernel = pkv_decode_kernel(Hq, Hkv, e->dtype);
+        (pkv::planned_launches(H + lay.plan, B, Hkv, e->dtype, kernel, e->W) == 1 ? one : split) =
+            true;
+      }
+      static const int32_t kWhole[] = {0}, kOne[] = {5, 3}, kSplit[] = {1, 2, 3};
+      const int32_t* passes = split ? kSplit : one ? kOne : kWhole;
+      const int np = split ? 3 : one ? 2 : 1;
+      if (events && one) record(events, 5, stream);
+      for (int k = 0; k < np; ++k) {
+        const int32_t pass = passes[k];
         pkv_status st = pkv_decode_planned(pass, out, q, k_new, v_new, e->k_cache, e->v_cache,
                                            e->dtab, D + lay.lens, B, Hq, Hkv, hd,
                                            pkv::kBlockSize, NB, mb, e->max_ctx, scale, e->dtype,
                                            H + lay.plan, D + lay.plan, plan_ints, e->W, e->ws,
                                            e->ws_bytes, stream);
         if (st != PKV_OK) return st;
-        if (pass) record(events, 4 + pass, stream);
+        if (events) record(events, pass == 5 ? 6 : 4 + pass, stream);
       }
     } else {
       record(events, 5, stream);
@@ -469,7 +485,8 @@ pkv_status pkv_engine_create(pkv_allocator* alloc, void* k_cache, void* v_cache,
   if (hd != 64 && hd != 128) return PKV_ERR_UNSUPPORTED;
   if (!alloc || !k_cache || !v_cache || NB <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 ||
       Hq > 32767 || max_batch <= 0 || max_batch > 8192 || max_context_len <= 0 ||
-      (flags & ~(PKV_ENGINE_PLAN)) != 0 ||
+      (flags & ~(PKV_ENGINE_PLAN | PKV_ENGINE_SPLIT_SHARED | PKV_ENGINE_ONE_LAUNCH)) != 0 ||
+      ((flags & PKV_ENGINE_SPLIT_SHARED) && (flags & PKV_ENGINE_ONE_LAUNCH)) ||
       (reinterpret_cast<uintptr_t>(k_cache) & 15u) || (reinterpret_cast<uintptr_t>(v_cache) & 15u))
     return PKV_ERR_INVALID_ARG;
   const int64_t mb = blocks_for(max_context_len);

@@ -157,6 +157,20 @@ hipError_t launch_merge(const StreamParams& p, int32_t dtype, int32_t kernel,
 // The shared pass of a plan (f16/bf16, G <= 16): p.num_units units on every kv head.
 hipError_t launch_shared(const StreamParams& p, int32_t dtype, int32_t kernel,
                          hipStream_t stream);
+// The one-launch kernel of the shared and stream passes exists for the vector stream kernel,
+// f16/bf16, with num_workers a multiple of 8 work-groups.
+bool fused_kernel_exists(int32_t dtype, int32_t kernel, int32_t num_workers);
+// Launches (1 or 2) of a validated decode plan's shared and stream passes under the automatic
+// choice (pkv_decode_planned_launches without the validation). plan: the packed plan; H is
+// read from its header; kernel: the stream kernel; W: the stream pass's workers.
+int32_t planned_launches(const int32_t* plan, int32_t B, int32_t Hkv, int32_t dtype,
+                         int32_t kernel, int32_t W);
+// The shared pass and the stream pass of a plan: one launch where that kernel exists (and
+// the plan has units), else the two launches in order. Same results either way.
+hipError_t launch_fused(const StreamParams& p, int32_t dtype, int32_t kernel,
+                        hipStream_t stream);
+// Dynamic LDS of the stream pass for B sequences (their prefix sums).
+size_t stream_lds_bytes(int32_t B);
 
 // Read-bandwidth probe (pkv_probe.hip): tiles ids[0..n) of base, max_tile tiles of 4096 bytes.
 hipError_t launch_probe_read(const void* base, int32_t max_tile, const int32_t* ids, int32_t n,

@@ -215,7 +215,8 @@ def test_engine_argument_errors():
     assert create(mb=0) == 1
     assert create(mb=8193) == 1
     assert create(ctx=0) == 1
-    assert create(flags=4) == 1
+    assert create(flags=8) == 1  # no such flag
+    assert create(flags=1 | 2 | 4) == 1  # two launches and one launch both asked for
     assert create(out=False) == 1
     assert create(k=ctypes.c_void_p(p.value + 4)) == 1
     assert lib.pkv_engine_submit(None, 0, 4, 4, 0, None) == 1

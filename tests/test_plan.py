@@ -212,3 +212,61 @@ def test_default_group_threshold(hq, hkv, runs):
     with pytest.raises(m.PkvError):
         m.pkv_decode_plan(tables, lens, num_q_heads=hq, num_kv_heads=hkv, num_blocks=nb,
                           max_context_len=256, dtype=torch.bfloat16, max_group=17)
+
+
+def _shared_then_private(B, shared, private, nb=200):
+    """B sequences holding the same `shared` blocks, then `private` blocks each (the last one
+    partly filled)."""
+    tables = np.full((B, shared + private), -1, np.int32)
+    nxt = shared
+    for s in range(B):
+        tables[s, :shared] = np.arange(shared)
+        tables[s, shared:] = np.arange(nxt, nxt + private)
+        nxt += private
+    lens = np.full(B, 16 * (shared + private) - 5, np.int64)
+    assert nxt <= nb
+    return tables, lens, nb
+
+
+@pytest.mark.parametrize("B,shared,private,hq,hkv,kernel,W,want", [
+    (4, 10, 1, 8, 8, 0, 1024, 1),   # the shared pass reads 10 tiles per head, the stream 4
+    (4, 2, 5, 8, 8, 0, 1024, 2),    # 2 against 20: the stream pass dominates
+    (4, 5, 5, 8, 8, 0, 1024, 2),    # 5 against 20
+    (2, 10, 5, 8, 8, 0, 1024, 1),   # 10 against 10: ties take one launch
+    (4, 0, 6, 8, 8, 0, 1024, 1),    # no runs: no shared pass, the stream pass alone
+    (4, 10, 1, 8, 8, 0, 1028, 2),   # workers not a multiple of 8 work-groups: no one launch
+    (4, 10, 1, 8, 4, 0, 1024, 2),   # G = 2: the matrix-core stream kernel has none
+    (4, 10, 1, 8, 4, 1, 1024, 1),   # G = 2 on the vector kernel: 10 x 4 against 4 x 8
+])
+def test_planned_launches_rule(B, shared, private, hq, hkv, kernel, W, want):
+    """The automatic choice of one or two launches for the shared and stream passes: one where
+    the one-launch kernel exists and the shared pass reads at least as many (block, head)
+    tiles as the stream pass (host only)."""
+    tables, lens, nb = _shared_then_private(B, shared, private)
+    prev = m.pkv_set_attn_kernel(kernel)
+    try:
+        p = m.pkv_decode_plan(tables, lens, num_q_heads=hq, num_kv_heads=hkv, num_blocks=nb,
+                              max_context_len=16 * tables.shape[1], dtype=torch.bfloat16)
+        assert (parse(p, B)["U"] > 0) == (shared > 0)
+        got = m.pkv_decode_planned_launches(p, batch=B, num_q_heads=hq, num_kv_heads=hkv,
+                                            max_blocks=tables.shape[1], dtype=torch.bfloat16,
+                                            num_workers=W)
+    finally:
+        m.pkv_set_attn_kernel(prev)
+    assert got == want
+
+
+def test_planned_launches_refuses_bad_plans():
+    tables, lens, nb = _shared_then_private(4, 10, 1)
+    p = m.pkv_decode_plan(tables, lens, num_q_heads=8, num_kv_heads=8, num_blocks=nb,
+                          max_context_len=16 * 11, dtype=torch.bfloat16)
+    args = dict(batch=4, num_q_heads=8, num_kv_heads=8, max_blocks=11, dtype=torch.bfloat16,
+                num_workers=1024)
+    assert m.pkv_decode_planned_launches(p, **args) == 1
+    assert m.pkv_decode_planned_launches(p, **dict(args, batch=5)) == 0  # plan for another B
+    assert m.pkv_decode_planned_launches(p, **dict(args, num_workers=1022)) == 0
+    assert m.pkv_decode_planned_launches(p, **dict(args, num_kv_heads=3)) == 0
+    bad = p.copy()
+    bad[0] ^= 1  # magic
+    assert m.pkv_decode_planned_launches(bad, **args) == 0
+    assert m.pkv_decode_planned_launches(p[:20], **args) == 0  # truncated
