@@ -864,8 +864,8 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_matrix_kernel(const StreamParams p)
 // zeroed (unused slots may hold anything). Tiles are read with cached loads: other units of
 // the same chunk (the next members, on the next waves) read them too.
 //
-// Waves map to (kv head, unit) unit-fastest, and work-groups are laid XCD-contiguously, so the
-// member tiles of one chunk run side by side on one XCD. Each row's (m, l, o) goes to its cell:
+// Waves map to (kv head, unit) per XCD (below), so that the member tiles of one chunk run side
+// by side on one XCD. Each row's (m, l, o) goes to its cell:
 // shared_base + cell_base + member*H + head slot, row (q head % GS), in the stream pass's
 // layout.
 template <int DT, int HD>
@@ -876,11 +876,27 @@ __device__ __forceinline__ void shared_pass(const StreamParams& p, int H, int GS
   constexpr int KS = HD / 32;  // QK steps
   constexpr int VT = HD / 16;  // PV dim tiles
 
-  const int lwg = (grid % 8 == 0) ? (b % 8) * (grid / 8) + b / 8 : b;
-  const int gw = lwg * kWaves + uniform(threadIdx.x >> 6);
+  // This wave's (kv head, unit). With a multiple of 8 kv heads, XCD x (work-group b runs on
+  // XCD b % 8) takes kv heads [x K, (x + 1) K), K = Hkv / 8, unit-major: the plan lists units
+  // longest first, so each XCD starts its longest units first and the waves that start late
+  // (as earlier ones end) are short ones, while the member tiles of one chunk (adjacent
+  // units) still run side by side on one XCD. Otherwise the units of a kv head run
+  // side by side, each XCD taking a contiguous share.
   const int U = p.num_units;
-  if (gw >= U * p.Hkv) return;
-  const int kvh = gw / U, u = gw - kvh * U;
+  int kvh, u;
+  if (p.Hkv % 8 == 0 && grid % 8 == 0) {
+    const int K = p.Hkv / 8;
+    const int j = (b / 8) * kWaves + uniform(threadIdx.x >> 6);
+    if (j >= U * K) return;
+    u = j / K;
+    kvh = (b % 8) * K + (j - u * K);
+  } else {
+    const int lwg = (grid % 8 == 0) ? (b % 8) * (grid / 8) + b / 8 : b;
+    const int gw = lwg * kWaves + uniform(threadIdx.x >> 6);
+    if (gw >= U * p.Hkv) return;
+    kvh = gw / U;
+    u = gw - kvh * U;
+  }
   const int32_t* e = p.units + static_cast<size_t>(u) * kUnitInts;
   const int ref = uniform(e[0]), b0 = uniform(max(e[1], 0)), b1 = uniform(min(e[2], p.max_blocks));
   const int moff = uniform(e[3]), mcnt = uniform(e[4]), cbase = uniform(e[5]);
@@ -1274,8 +1290,12 @@ void launch_shared_t(const StreamParams& p, int H, int GS, hipStream_t stream) {
 }
 
 // Work-groups of the shared pass: one wave per (unit, kv head), a multiple of 8 work-groups
-// for the XCD-contiguous mapping.
+// for the per-XCD mappings.
 int64_t shared_wgs(const StreamParams& p) {
+  if (p.Hkv % 8 == 0) {  // each XCD its eighth of the kv heads, for every unit
+    const int64_t per_xcd = static_cast<int64_t>(p.num_units) * (p.Hkv / 8);
+    return 8 * ((per_xcd + kWaves - 1) / kWaves);
+  }
   const int64_t waves = static_cast<int64_t>(p.num_units) * p.Hkv;
   const int64_t grid = (waves + kWaves - 1) / kWaves;
   return (grid + 7) / 8 * 8;

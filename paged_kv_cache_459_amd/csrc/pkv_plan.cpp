@@ -107,23 +107,35 @@ int32_t plan_build(const int32_t* tables, const int32_t* lens, int32_t B, int32_
     return a.members[0] != b.members[0] ? a.members[0] < b.members[0] : a.j0 < b.j0;
   });
   const int32_t per_tile = std::max(1, kRowsPerTile / G);
+  // Units: (run, chunk of its blocks, up to per_tile of its members). Listed longest first
+  // (stable, so the member tiles of one chunk stay adjacent): the shared pass starts them in
+  // this order, so the units that start late, as earlier ones end, are short ones.
+  struct Unit {
+    const Run* run;
+    int32_t b0, b1;
+    size_t t;  // first member (index into the run's members)
+  };
+  std::vector<Unit> order;
+  for (const Run& r : runs)
+    for (int32_t b0 = r.j0; b0 < r.j1; b0 += chunk)
+      for (size_t t = 0; t < r.members.size(); t += per_tile)
+        order.push_back(Unit{&r, b0, std::min(r.j1, b0 + chunk), t});
+  std::stable_sort(order.begin(), order.end(), [](const Unit& a, const Unit& b) {
+    return a.b1 - a.b0 > b.b1 - b.b0;
+  });
   std::vector<int32_t> units, members;
   std::vector<int32_t> count(B, 0);  // shared pieces per sequence
   int32_t cells = 0;
-  for (const Run& r : runs) {
-    for (int32_t b0 = r.j0; b0 < r.j1; b0 += chunk) {
-      const int32_t b1 = std::min(r.j1, b0 + chunk);
-      for (size_t t = 0; t < r.members.size(); t += per_tile) {
-        const int32_t cnt = static_cast<int32_t>(std::min<size_t>(per_tile, r.members.size() - t));
-        units.insert(units.end(), {r.members[0], b0, b1, static_cast<int32_t>(members.size()), cnt,
-                                   cells});
-        for (int32_t k = 0; k < cnt; ++k) {
-          members.push_back(r.members[t + k]);
-          ++count[r.members[t + k]];
-        }
-        cells += cnt * H;
-      }
+  for (const Unit& x : order) {
+    const Run& r = *x.run;
+    const int32_t cnt = static_cast<int32_t>(std::min<size_t>(per_tile, r.members.size() - x.t));
+    units.insert(units.end(), {r.members[0], x.b0, x.b1, static_cast<int32_t>(members.size()), cnt,
+                               cells});
+    for (int32_t k = 0; k < cnt; ++k) {
+      members.push_back(r.members[x.t + k]);
+      ++count[r.members[x.t + k]];
     }
+    cells += cnt * H;
   }
   // each sequence's piece cells, in unit order (CSR)
   std::vector<int32_t> ptr(B + 1, 0);
