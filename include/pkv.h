@@ -248,10 +248,10 @@ pkv_status pkv_decode_plan(const int32_t* block_tables, const int32_t* context_l
 
 /* Launches (1 or 2) of the shared and stream passes that pkv_decode_planned's passes 0 and 4   */
 /* use for this plan: one where the one-launch kernel exists and the plan's shared pass reads  */
-/* at least as many (block, head) tiles as its stream pass (then the stream pass's short      */
-/* ranges fill the device beside the shared pass; where the stream pass dominates, the shared */
-/* pass's work-groups would start in its tail and lengthen it), else two; one for a plan      */
-/* without units. Host only; plan as for pkv_decode_planned (the same B, heads, dtype,        */
+/* at least as many (block, head) tiles as its stream pass (the shared pass's work-groups     */
+/* start first, the stream pass's short ranges fill its tail; where the stream pass dominates */
+/* the one launch is no faster), else two; one for a plan without units. Host only; plan as   */
+/* for pkv_decode_planned (the same B, heads, dtype,                                          */
 /* max_blocks and num_workers). 0 on bad arguments or a plan that fails validation.            */
 int32_t pkv_decode_planned_launches(const int32_t* plan, size_t plan_ints, int32_t B,
                                     int32_t Hq, int32_t Hkv, int32_t max_blocks,

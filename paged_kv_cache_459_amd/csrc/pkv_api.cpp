@@ -359,10 +359,10 @@ namespace pkv {
 
 // Launches of a validated plan's shared and stream passes under the automatic choice: one
 // where the one-launch kernel exists and the shared pass reads at least as many (block, head)
-// tiles as the stream pass, else two (one when the plan has no units: no shared pass). Where
-// the stream pass dominates, the shared pass's work-groups, which start as stream work-groups
-// end, lengthen the stream pass's tail; where the shared pass dominates, the stream pass's
-// short ranges fill the compute units beside it.
+// tiles as the stream pass, else two (one when the plan has no units: no shared pass). In the
+// one launch the shared pass's work-groups start first and the stream pass's short ranges
+// fill its tail; where the stream pass dominates, the two passes in one launch measured no
+// faster than apart (they compete for the same memory path), so they stay apart.
 int32_t planned_launches(const int32_t* plan, int32_t B, int32_t Hkv, int32_t dtype,
                          int32_t kernel, int32_t W) {
   const int32_t H = plan[2], U = plan[4];

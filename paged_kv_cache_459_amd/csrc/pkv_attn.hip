@@ -1048,20 +1048,21 @@ __attribute__((amdgpu_waves_per_eu(3))) attn_shared_kernel(const StreamParams p,
   shared_pass<DT, HD>(p, H, GS, blockIdx.x, gridDim.x);
 }
 
-// Shared pass and vector stream pass in one launch (G = 1): work-groups [0, stream_wgs) are the
-// stream pass's workers, the rest the shared pass's (unit, kv head) waves. The two write
-// disjoint cells and read only what both kernels read when launched apart, so every result is
-// bit-identical to the two-launch order. The stream work-groups come first: the dispatcher
-// starts them on every compute unit, and the shared pass's short work-groups take the slots
-// left beside them (at most 128 VGPRs, four waves per SIMD) and those that the stream pass
-// frees as it ends.
+// Shared pass and vector stream pass in one launch (G = 1): the first gridDim.x - stream_wgs
+// work-groups are the shared pass's (unit, kv head) waves, the last stream_wgs the stream
+// pass's workers. The two write disjoint cells and read only what both read when launched
+// apart, so every result is bit-identical to the two-launch order. The form is used where the
+// shared pass dominates, so its work-groups start first (the dispatcher fills every compute
+// unit with them); the stream pass's short ranges then run as shared waves end and fill the
+// shared pass's tail. At most 128 VGPRs: four waves per SIMD.
 template <int DT, int HD>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(4))) attn_fused_kernel(const StreamParams p, int H, int GS,
                                                          int stream_wgs) {
   const int b = blockIdx.x;
-  if (b < stream_wgs) vector_pass<DT, HD>(p, b, stream_wgs);
-  else shared_pass<DT, HD>(p, H, GS, b - stream_wgs, gridDim.x - stream_wgs);
+  const int sh = gridDim.x - stream_wgs;  // a multiple of 8: the stream pass's XCD mapping holds
+  if (b >= sh) vector_pass<DT, HD>(p, b - sh, stream_wgs);
+  else shared_pass<DT, HD>(p, H, GS, b, sh);
 }
 
 // ------------------------------------------------------------------------------------------

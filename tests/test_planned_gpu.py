@@ -10,8 +10,8 @@ sharers see the same K/V; slots no sharer reaches hold NaN.
 * plain and fused (newest token appended) decode match the oracle within the tolerance, for
   both stream kernels, MHA and GQA (G = 1..16), hd 64/128, f16/bf16, and any worker count;
 * the fused step's caches are bit-exact against the oracle's write;
-* running the passes one by one (shared and stream pass as two launches or as one) gives the
-  same bits as one call;
+* the whole step, the passes apart and the shared and stream passes in one launch give the
+  same bits (output and, appending, caches);
 * a float32 plan (no runs) gives exactly the unplanned result;
 * the full-size prefix-shared and beam batches, sampled rows against the oracle.
 """
@@ -154,29 +154,38 @@ def test_planned_append_any_worker_count(W, kind, dtype, hq, hkv, hd, kernel):
 W_ = W  # the workloads module (the parameter above shadows the name W)
 
 
-@pytest.mark.parametrize("kind", ["beam", "mixed"])
+# append mode needs each newest token in a private block (the mixed batch shares whole rows)
+@pytest.mark.parametrize("kind,append", [("beam", False), ("mixed", False), ("beam", True),
+                                         ("prefix", True)])
 @pytest.mark.parametrize("dtype,hq,hkv,kernel", [("bf16", 8, 8, 0), ("f16", 28, 4, 0),
                                                  ("f16", 8, 4, 1)])
-def test_passes_one_by_one_equal_one_call(kind, dtype, hq, hkv, kernel):
-    """One call (the shared and stream passes in one launch where the vector kernel streams),
-    the passes one by one as two launches (1, 2, 3) and as one (4, 3): the same bits."""
+def test_pass_forms_give_the_same_bits(kind, append, dtype, hq, hkv, kernel):
+    """The whole step (pass 0), the passes apart (1, 2, 3) and the shared and stream passes in
+    one launch (5, 3; two launches where the vector stream kernel does not run): the same
+    output bits, and in append mode the same caches."""
     m = pkv()
-    print(f"[planned passes] {kind} {dtype} {hq}/{hkv} kernel={kernel}", flush=True)
+    print(f"[planned forms] append={append} {kind} {dtype} {hq}/{hkv} kernel={kernel}",
+          flush=True)
     rng = np.random.default_rng(970)
     tables, lens, nb = case(rng, kind)
     q, kc, vc = fill_shared(rng, tables, lens, nb, hq, hkv, 128, dtype)
+    B = len(lens)
+    kn = vn = None
+    if append:
+        kn = W_.normal_values(rng, (B, hkv, 128), dtype)
+        vn = W_.normal_values(rng, (B, hkv, 128), dtype)
     prev = m.pkv_set_attn_kernel(kernel)
     try:
-        a, _, _, _ = run_planned(m, q, kc, vc, tables, lens, nb, hq, hkv, 128, dtype, 0.1)
-        b, _, _, _ = run_planned(m, q, kc, vc, tables, lens, nb, hq, hkv, 128, dtype, 0.1,
-                                 passes=(1, 2, 3))
-        c, _, _, _ = run_planned(m, q, kc, vc, tables, lens, nb, hq, hkv, 128, dtype, 0.1,
-                                 passes=(4, 3))
+        runs = [run_planned(m, q, kc, vc, tables, lens, nb, hq, hkv, 128, dtype, 0.1,
+                            k_new=kn, v_new=vn, passes=ps)
+                for ps in ((0,), (1, 2, 3), (5, 3), (4, 3))]
     finally:
         m.pkv_set_attn_kernel(prev)
-    bits = [W_.to_storage_numpy(x, dtype).view(np.uint8) for x in (a, b, c)]
-    np.testing.assert_array_equal(bits[0], bits[1])
-    np.testing.assert_array_equal(bits[2], bits[1])
+    ref = runs[1]
+    for got in runs[:1] + runs[2:]:
+        for a, b in zip(got[:3], ref[:3]):  # out, k cache, v cache
+            np.testing.assert_array_equal(W_.to_storage_numpy(a, dtype).view(np.uint8),
+                                          W_.to_storage_numpy(b, dtype).view(np.uint8))
 
 
 def test_float32_plan_equals_unplanned_bits():
