@@ -157,26 +157,27 @@ W_ = W  # the workloads module (the parameter above shadows the name W)
 # append mode needs each newest token in a private block (the mixed batch shares whole rows)
 @pytest.mark.parametrize("kind,append", [("beam", False), ("mixed", False), ("beam", True),
                                          ("prefix", True)])
-@pytest.mark.parametrize("dtype,hq,hkv,kernel", [("bf16", 8, 8, 0), ("f16", 28, 4, 0),
-                                                 ("f16", 8, 4, 1)])
-def test_pass_forms_give_the_same_bits(kind, append, dtype, hq, hkv, kernel):
+@pytest.mark.parametrize("dtype,hq,hkv,hd,kernel", [
+    ("bf16", 8, 8, 128, 0), ("f16", 28, 4, 128, 0), ("f16", 8, 4, 128, 1), ("f16", 4, 4, 64, 0),
+    ("bf16", 8, 2, 64, 1)])
+def test_pass_forms_give_the_same_bits(kind, append, dtype, hq, hkv, hd, kernel):
     """The whole step (pass 0), the passes apart (1, 2, 3) and the shared and stream passes in
     one launch (5, 3; two launches where the vector stream kernel does not run): the same
     output bits, and in append mode the same caches."""
     m = pkv()
-    print(f"[planned forms] append={append} {kind} {dtype} {hq}/{hkv} kernel={kernel}",
+    print(f"[planned forms] append={append} {kind} {dtype} {hq}/{hkv} hd{hd} kernel={kernel}",
           flush=True)
     rng = np.random.default_rng(970)
     tables, lens, nb = case(rng, kind)
-    q, kc, vc = fill_shared(rng, tables, lens, nb, hq, hkv, 128, dtype)
+    q, kc, vc = fill_shared(rng, tables, lens, nb, hq, hkv, hd, dtype)
     B = len(lens)
     kn = vn = None
     if append:
-        kn = W_.normal_values(rng, (B, hkv, 128), dtype)
-        vn = W_.normal_values(rng, (B, hkv, 128), dtype)
+        kn = W_.normal_values(rng, (B, hkv, hd), dtype)
+        vn = W_.normal_values(rng, (B, hkv, hd), dtype)
     prev = m.pkv_set_attn_kernel(kernel)
     try:
-        runs = [run_planned(m, q, kc, vc, tables, lens, nb, hq, hkv, 128, dtype, 0.1,
+        runs = [run_planned(m, q, kc, vc, tables, lens, nb, hq, hkv, hd, dtype, 0.1,
                             k_new=kn, v_new=vn, passes=ps)
                 for ps in ((0,), (1, 2, 3), (5, 3), (4, 3))]
     finally:
