@@ -262,3 +262,81 @@ def test_full_size_prefix_shared(beams):
         want = OA.decode_attention(qh, kh, vh, np.arange(c, dtype=np.int32)[None],
                                    np.int32([n]), scale=0.088, hkv=hq, hd=hd, bs=16, dtype="bf16")
         G.assert_close(G.gpu_f64(out[s:s + 1], "bf16"), want, "bf16", f"row {s}")
+
+
+def random_tree_batch(rng, append, nb=3000):
+    """A batch whose tables form a random prefix tree: a run of blocks shared by a group, the
+    group split into up to four subgroups that each share a further run, and so on three
+    levels deep, then private tails. Lengths end anywhere in the last block (appending: every
+    sequence ends in a private block of its own)."""
+    B = int(rng.integers(2, 40))
+    rows = [[] for _ in range(B)]
+    free = iter(rng.permutation(nb).tolist())
+
+    def grow(members, depth):
+        shared = [next(free) for _ in range(int(rng.integers(0, 20)))]
+        for s in members:
+            rows[s] += shared
+        if depth < 3 and len(members) >= 2 and rng.random() < 0.7:
+            k = int(rng.integers(1, min(4, len(members)) + 1))
+            for part in np.array_split(rng.permutation(members), k):
+                if len(part):
+                    grow([int(x) for x in part], depth + 1)
+        else:
+            for s in members:
+                tail = int(rng.integers(1 if append else 0, 6))
+                rows[s] += [next(free) for _ in range(tail)]
+
+    grow(list(range(B)), 0)
+    mb = max(1, max(len(r) for r in rows))
+    tables = np.full((B, mb), -1, np.int32)
+    lens = np.zeros(B, np.int32)
+    for s, r in enumerate(rows):
+        tables[s, :len(r)] = r
+        lens[s] = 16 * (len(r) - 1) + int(rng.integers(1, 17)) if r else 0
+    return tables, lens, nb
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("dtype,hq,hkv,hd,kernel", [
+    ("bf16", 8, 8, 128, 0), ("f16", 16, 16, 64, 0), ("bf16", 4, 2, 128, 0),
+    ("f16", 8, 2, 128, 1), ("bf16", 32, 32, 128, 0)])
+def test_random_prefix_trees(seed, dtype, hq, hkv, hd, kernel):
+    """Random prefix trees, plain and appending, at several worker counts: the planned step
+    matches the oracle (the write too, appending), and its pass forms give the same bits."""
+    m = pkv()
+    rng = np.random.default_rng(5000 + seed)
+    append = seed % 2 == 1
+    tables, lens, nb = random_tree_batch(rng, append)
+    W = [None, 64, 36, 1024, None, 1024][seed]
+    print(f"[planned tree] seed={seed} B={len(lens)} append={append} W={W} {dtype} "
+          f"{hq}/{hkv} hd{hd} kernel={kernel}", flush=True)
+    q, kc, vc = fill_shared(rng, tables, lens, nb, hq, hkv, hd, dtype)
+    B = len(lens)
+    kn = vn = None
+    if append:
+        kn = W_.normal_values(rng, (B, hkv, hd), dtype)
+        vn = W_.normal_values(rng, (B, hkv, hd), dtype)
+    prev = m.pkv_set_attn_kernel(kernel)
+    try:
+        runs = [run_planned(m, q, kc, vc, tables, lens, nb, hq, hkv, hd, dtype, 0.09, W=W,
+                            k_new=kn, v_new=vn, passes=ps)
+                for ps in ((0,), (1, 2, 3), (5, 3))]
+    finally:
+        m.pkv_set_attn_kernel(prev)
+    for got in runs[1:]:
+        for a, b in zip(got[:3], runs[0][:3]):
+            np.testing.assert_array_equal(W_.to_storage_numpy(a, dtype).view(np.uint8),
+                                          W_.to_storage_numpy(b, dtype).view(np.uint8))
+    out, kd, vd, _ = runs[0]
+    if append:
+        slots = np.array([int(tables[s, (int(n) - 1) // 16]) * 16 + (int(n) - 1) % 16
+                          for s, n in enumerate(lens)], np.int32)
+        kc, vc = CW.write_kv(kn, vn, kc, vc, slots, hkv=hkv, hd=hd, bs=16, dtype=dtype)
+        np.testing.assert_array_equal(W_.to_storage_numpy(kd, dtype).reshape(-1).view(np.uint8),
+                                      kc.view(np.uint8))
+        np.testing.assert_array_equal(W_.to_storage_numpy(vd, dtype).reshape(-1).view(np.uint8),
+                                      vc.view(np.uint8))
+    want = OA.decode_attention(q, kc, vc, tables, lens, scale=0.09, hkv=hkv, hd=hd, bs=16,
+                               dtype=dtype)
+    G.assert_close(G.gpu_f64(out, dtype), want, dtype, f"tree seed {seed}")
