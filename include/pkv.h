@@ -643,10 +643,11 @@ int32_t pkv_engine_queued(const pkv_engine* e);
 /* written. new_ids: host int32 [max_batch] or NULL. scale: softmax scale of both attentions.  */
 /* events: NULL or 8 hipEvent_t (each may be NULL) recorded on the stream: [0] before the      */
 /* upload of the step's staged tables, lengths, slots and plans (a small copy kernel that      */
-/* reads the pinned set), [1] after it, [2] after the prompt write, [3] after the copies, [4]  */
-/* after the prefill, [5] after the shared pass (unless PKV_ENGINE_SPLIT_SHARED: before the   */
-/* shared and stream passes, one launch or two, so that [5]..[6] spans both), [6] after the   */
-/* stream pass, [7] after the merge.                                                           */
+/* reads the pinned set), [1] after it, [2] after the prompt write, [3] after the copies (a    */
+/* step with copies and no prompt write stages and copies in one launch: [1], [2] and [3]     */
+/* after it), [4] after the prefill, [5] after the shared pass (before the one launch of the  */
+/* shared and stream passes, when they are one), [6] after the stream pass (or that launch),  */
+/* [7] after the merge.                                                                        */
 /* info: NULL or host                                                                          */
 /* int64 [8] = {B, T, retired, admitted, plan units (-1: unplanned), copy-on-write pairs,      */
 /* queued after the step, k}.                                                                  */

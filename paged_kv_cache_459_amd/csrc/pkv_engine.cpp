@@ -359,22 +359,32 @@ pkv_status decode_tail(pkv_engine* e, int s, Layout& lay, int32_t T, int32_t A,
   sp.dense_n16 = dense ? static_cast<int64_t>((d1 - d0) / 4) : 0;
   sp.pairs_src = static_cast<int64_t>(lay.pairs * 4);
   sp.npairs = dense ? 0 : static_cast<int64_t>(npairs);
-  if (pkv::launch_stage(sp, stream) != hipSuccess) return PKV_ERR_HIP;
-  record(events, 1, stream);
   const int32_t* D = e->dsmall;
   const int32_t NB = e->NB, Hq = e->Hq, Hkv = e->Hkv, hd = e->hd;
-  if (T > 0) {
-    pkv_status st = pkv_write(k_prompt, v_prompt, e->k_cache, e->v_cache, D + lay.slots, T, Hkv,
-                              hd, pkv::kBlockSize, NB, e->dtype, stream);
-    if (st != PKV_OK) return st;
+  // With copy-on-write copies and no prompt write between them (a beam step), the staging and
+  // the copies are one launch, the copies reading their pairs from the pinned set.
+  if (T == 0 && ncow > 0 && pkv::copy_blocks_grid_y(Hkv, hd, e->dtype) <= 65535) {
+    const int32_t* Hp = static_cast<const int32_t*>(e->host_dev[s]);
+    pkv::CopyParams cp{e->k_cache, e->v_cache, Hp + lay.cow_src, Hp + lay.cow_dst, ncow, Hkv,
+                       hd, NB};
+    if (pkv::launch_stage_copy(sp, cp, e->dtype, stream) != hipSuccess) return PKV_ERR_HIP;
+    for (int k = 1; k <= 3; ++k) record(events, k, stream);
+  } else {
+    if (pkv::launch_stage(sp, stream) != hipSuccess) return PKV_ERR_HIP;
+    record(events, 1, stream);
+    if (T > 0) {
+      pkv_status st = pkv_write(k_prompt, v_prompt, e->k_cache, e->v_cache, D + lay.slots, T,
+                                Hkv, hd, pkv::kBlockSize, NB, e->dtype, stream);
+      if (st != PKV_OK) return st;
+    }
+    record(events, 2, stream);
+    if (ncow > 0) {
+      pkv_status st = pkv_copy_blocks(e->k_cache, e->v_cache, D + lay.cow_src, D + lay.cow_dst,
+                                      ncow, Hkv, hd, pkv::kBlockSize, NB, e->dtype, stream);
+      if (st != PKV_OK) return st;
+    }
+    record(events, 3, stream);
   }
-  record(events, 2, stream);
-  if (ncow > 0) {
-    pkv_status st = pkv_copy_blocks(e->k_cache, e->v_cache, D + lay.cow_src, D + lay.cow_dst,
-                                    ncow, Hkv, hd, pkv::kBlockSize, NB, e->dtype, stream);
-    if (st != PKV_OK) return st;
-  }
-  record(events, 3, stream);
   if (prefill) {
     // the admitted sequences are the last A rows; their rows (one decode token longer now)
     // hold every prompt block, and the plan's lengths are the prompt lengths

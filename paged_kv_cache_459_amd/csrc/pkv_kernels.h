@@ -148,6 +148,10 @@ struct StageParams {
   int64_t pairs_src, npairs;
 };
 hipError_t launch_stage(const StageParams& p, hipStream_t stream);
+// The staging and copy-on-write copies (pairs cp.src/cp.dst readable by the device: the pinned
+// staging set) in one launch; the copies touch no memory the staging writes.
+hipError_t launch_stage_copy(const StageParams& sp, const CopyParams& cp, int32_t dtype,
+                             hipStream_t stream);
 // Work-groups per block and cache of the copy kernel (grid.y; at most 65535 is launchable).
 int32_t copy_blocks_grid_y(int32_t Hkv, int32_t hd, int32_t dtype);
 hipError_t launch_stream(const StreamParams& p, int32_t dtype, int32_t kernel,

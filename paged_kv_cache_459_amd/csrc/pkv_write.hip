@@ -141,17 +141,18 @@ write_kernel(const uint4* __restrict__ k, const uint4* __restrict__ v, uint4* __
 // source is read with ordinary loads (the attention pass reads it next, through the other
 // sequences that share it); the destination is written with non-temporal stores.
 template <int U>
-__global__ void __launch_bounds__(256)
-copy_blocks_kernel(u32x4_t* __restrict__ kc, u32x4_t* __restrict__ vc,
-                   const int32_t* __restrict__ src, const int32_t* __restrict__ dst, int32_t NB,
-                   int32_t chunks) {
-  const int32_t s = src[blockIdx.x];
-  const int32_t d = dst[blockIdx.x];
+__device__ __forceinline__ void copy_block_range(u32x4_t* __restrict__ kc,
+                                                 u32x4_t* __restrict__ vc,
+                                                 const int32_t* __restrict__ src,
+                                                 const int32_t* __restrict__ dst, int32_t NB,
+                                                 int32_t chunks, int pair, int y, int cache) {
+  const int32_t s = src[pair];
+  const int32_t d = dst[pair];
   if (s < 0 || s >= NB || d < 0 || d >= NB) return;  // padding, or outside the pool
-  u32x4_t* base = blockIdx.z == 0 ? kc : vc;
+  u32x4_t* base = cache == 0 ? kc : vc;
   const u32x4_t* from = base + static_cast<size_t>(s) * chunks;
   u32x4_t* to = base + static_cast<size_t>(d) * chunks;
-  const int first = static_cast<int>(blockIdx.y) * (256 * U);
+  const int first = y * (256 * U);
   const int i0 = first + static_cast<int>(threadIdx.x);
   if (first + 256 * U <= chunks) {  // whole range inside the block (uniform branch)
     u32x4_t r[U];
@@ -162,6 +163,14 @@ copy_blocks_kernel(u32x4_t* __restrict__ kc, u32x4_t* __restrict__ vc,
   } else {  // the block's last, partial range
     for (int i = i0; i < chunks; i += 256) __builtin_nontemporal_store(from[i], to + i);
   }
+}
+
+template <int U>
+__global__ void __launch_bounds__(256)
+copy_blocks_kernel(u32x4_t* __restrict__ kc, u32x4_t* __restrict__ vc,
+                   const int32_t* __restrict__ src, const int32_t* __restrict__ dst, int32_t NB,
+                   int32_t chunks) {
+  copy_block_range<U>(kc, vc, src, dst, NB, chunks, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 constexpr int kCopyUnroll = 4;
@@ -189,8 +198,8 @@ namespace {
 // dense range of block-table rows, and single changed table entries scattered. A kernel of
 // ours rather than a runtime copy: it is ordered in the step's stream like the step's other
 // kernels, without the runtime copy's extra synchronization around host memory.
-__global__ void __launch_bounds__(256) stage_kernel(const StageParams p) {
-  int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+__device__ __forceinline__ void stage_part(const StageParams& p, int b) {
+  int64_t i = static_cast<int64_t>(b) * 256 + threadIdx.x;
   if (i < p.small_n16) {
     reinterpret_cast<uint4*>(p.small_dst)[i] = reinterpret_cast<const uint4*>(p.src)[i];
     return;
@@ -209,7 +218,47 @@ __global__ void __launch_bounds__(256) stage_kernel(const StageParams p) {
   }
 }
 
+__global__ void __launch_bounds__(256) stage_kernel(const StageParams p) {
+  stage_part(p, blockIdx.x);
+}
+
+// The staging and a step's copy-on-write copies in one launch, for a step with no other work
+// between them: work-groups [0, stage_wgs) stage, the others copy (pair, range, cache) in the
+// copy kernel's order. The copies read their pairs from the same pinned host memory the
+// staging reads (not from the staged device copy, which may not have landed), and touch only
+// cache blocks, which the staging does not.
+__global__ void __launch_bounds__(256)
+stage_copy_kernel(const StageParams sp, u32x4_t* __restrict__ kc, u32x4_t* __restrict__ vc,
+                  const int32_t* __restrict__ src, const int32_t* __restrict__ dst, int32_t NB,
+                  int32_t chunks, int32_t stage_wgs, int32_t grid_y) {
+  const int b = blockIdx.x;
+  if (b < stage_wgs) {
+    stage_part(sp, b);
+    return;
+  }
+  const int c = b - stage_wgs;
+  const int per_pair = 2 * grid_y;
+  copy_block_range<kCopyUnroll>(kc, vc, src, dst, NB, chunks, c / per_pair,
+                                (c % per_pair) % grid_y, (c % per_pair) / grid_y);
+}
+
 }  // namespace
+
+hipError_t launch_stage_copy(const StageParams& sp, const CopyParams& cp, int32_t dtype,
+                             hipStream_t stream) {
+  if (cp.n == 0) return launch_stage(sp, stream);
+  const int64_t n = sp.small_n16 + sp.dense_n16 + sp.npairs;
+  const int32_t stage_wgs = static_cast<int32_t>((n + 255) / 256);
+  const int eb = dtype == 0 ? 4 : 2;
+  const int32_t chunks = cp.Hkv * cp.hd * eb;
+  const int32_t grid_y = (chunks + 256 * kCopyUnroll - 1) / (256 * kCopyUnroll);
+  const int64_t grid = stage_wgs + static_cast<int64_t>(cp.n) * 2 * grid_y;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(stage_copy_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream,
+                     sp, static_cast<u32x4_t*>(cp.k_cache), static_cast<u32x4_t*>(cp.v_cache),
+                     cp.src, cp.dst, cp.NB, chunks, stage_wgs, grid_y);
+  return note_error("stage_copy_kernel launch", hipGetLastError());
+}
 
 hipError_t launch_stage(const StageParams& p, hipStream_t stream) {
   const int64_t n = p.small_n16 + p.dense_n16 + p.npairs;
