@@ -9,10 +9,11 @@ C ABI, against the oracle.
   appended per beam per step. The engine's allocator and the oracle's allocator run in
   lockstep (the uploaded tables and lengths and the number of copy-on-write pairs equal every
   step); on the device each step is
-  one engine call (pkv_engine_beam_step: fork, free, append, pkv_copy_blocks of the step's
-  pairs, the fused decode step, also with a shared-prefix plan); on the host the oracle's
-  copy, write and attention. Every step's output matches within the tolerance and both
-  caches are bit-exact at the end.
+  one engine call (pkv_engine_beam_step: fork, free, append, the staging and the step's
+  copy-on-write copies in one launch, the fused decode step, also with a shared-prefix plan,
+  its shared and stream passes in the automatic form, in one launch or in two); on the host
+  the oracle's copy, write and attention. Every step's output matches within the tolerance
+  and both caches are bit-exact at the end.
 """
 
 import math
@@ -94,12 +95,16 @@ def test_copy_many_pairs():
     np.testing.assert_array_equal(storage(v_d, dtype), want_v.view(np.uint8))
 
 
-@pytest.mark.parametrize("dtype,hq,hkv,hd,kernel,plan", [
-    ("bf16", 8, 2, 128, 0, False), ("f32", 4, 4, 64, 0, False), ("f16", 4, 4, 128, 0, False),
-    ("bf16", 8, 2, 64, 1, False), ("bf16", 8, 2, 128, 0, True), ("f16", 4, 4, 64, 0, True)])
-def test_beam_search_loop(dtype, hq, hkv, hd, kernel, plan):
+@pytest.mark.parametrize("dtype,hq,hkv,hd,kernel,plan,form", [
+    ("bf16", 8, 2, 128, 0, False, "auto"), ("f32", 4, 4, 64, 0, False, "auto"),
+    ("f16", 4, 4, 128, 0, False, "auto"), ("bf16", 8, 2, 64, 1, False, "auto"),
+    ("bf16", 8, 2, 128, 0, True, "auto"), ("f16", 4, 4, 64, 0, True, "auto"),
+    ("bf16", 8, 8, 128, 0, True, "one"), ("bf16", 8, 8, 128, 0, True, "two"),
+    ("f16", 8, 2, 128, 1, True, "one")])
+def test_beam_search_loop(dtype, hq, hkv, hd, kernel, plan, form):
     m = pkv()
-    print(f"[beam] {dtype} {hq}/{hkv} hd{hd} kernel={kernel} plan={plan}", flush=True)
+    print(f"[beam] {dtype} {hq}/{hkv} hd{hd} kernel={kernel} plan={plan} form={form}",
+          flush=True)
     groups, beams, steps, nb = 4, 4, 36, 160
     prompt_lens = (21, 16, 7, 40)
     rng = np.random.default_rng(81 + hd)
@@ -142,7 +147,7 @@ def test_beam_search_loop(dtype, hq, hkv, hd, kernel, plan):
     B = groups * beams
     prev = m.pkv_set_attn_kernel(kernel)
     eng = m.Engine(alloc, k_d, v_d, num_q_heads=hq, num_kv_heads=hkv, head_dim=hd,
-                   max_batch=B, max_context_len=16 * 8, plan=plan)
+                   max_batch=B, max_context_len=16 * 8, plan=plan, shared_launch=form)
     eng.adopt([s for row in live for s in row])
     dt = G.TORCH[dtype]
     q_d = torch.empty((B, hq, hd), dtype=dt, device="cuda")
