@@ -276,7 +276,9 @@ size_t pkv_decode_planned_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, in
 /* plan_dev hold the same plan_ints entries (host, validated here; device, read by the        */
 /* kernels); context_lens and the tables must be those the plan was built from.                */
 /* num_workers as pkv_decode_stream. Errors: as pkv_decode_append_attn, plus                   */
-/* PKV_ERR_INVALID_ARG for a plan that fails the check or does not match the shapes.          */
+/* PKV_ERR_INVALID_ARG for a plan that fails the check or does not match the shapes, and      */
+/* PKV_ERR_UNSUPPORTED for f32 or G > 16 with units, or when (units * Hkv + num_workers) * 64  */
+/* work-items would pass 2^31 - 1.                                                            */
 pkv_status pkv_decode_planned(int32_t pass, void* out, const void* q, const void* k_new,
                               const void* v_new, void* k_cache, void* v_cache,
                               const int32_t* block_tables, const int32_t* context_lens, int32_t B,
@@ -325,8 +327,9 @@ size_t pkv_prefill_workspace_bytes(int32_t Hq, int32_t Hkv, int32_t hd, const in
 /* ([S][max_blocks] device int32) as pkv_decode_attn; the cache already holds every token     */
 /* attended. plan_host and plan_dev hold the same plan_ints entries, built for these           */
 /* query_start/context_lens and shapes. Writes only out (and the workspace). Errors:          */
-/* PKV_ERR_INVALID_ARG (shapes, pointers, a plan that fails the check), PKV_ERR_UNSUPPORTED,  */
-/* PKV_ERR_WORKSPACE, PKV_ERR_HIP. Stream-ordered, asynchronous. pass: 0 both kernels, 1 the  */
+/* PKV_ERR_INVALID_ARG (shapes, pointers, a plan that fails the check), PKV_ERR_UNSUPPORTED   */
+/* (also when units * Hkv * 256 work-items would pass 2^31 - 1), PKV_ERR_WORKSPACE,           */
+/* PKV_ERR_HIP. Stream-ordered, asynchronous. pass: 0 both kernels, 1 the                     */
 /* attention pass (direct rows finished, pieces of split rows written), 2 the merge of the    */
 /* split rows (run 1 then 2 on one stream; exported to time them).                            */
 pkv_status pkv_prefill_attn(int32_t pass, void* out, const void* q, const void* k_cache,

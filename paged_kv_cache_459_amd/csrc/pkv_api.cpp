@@ -442,7 +442,9 @@ pkv_status pkv_decode_planned(int32_t pass, void* out, const void* q, const void
                        &pv))
     return PKV_ERR_INVALID_ARG;
   if (pv.U > 0 && (dtype == PKV_F32 || G > pkv::kRowsPerTile)) return PKV_ERR_UNSUPPORTED;
-  if (static_cast<int64_t>(pv.U) * Hkv >= (int64_t{1} << 31) - pkv::kWaves * 8)
+  // one wave per (unit, kv head), plus the stream workers in the one-launch form: the launch's
+  // work-items must stay within 32-bit grid indexing
+  if ((static_cast<int64_t>(pv.U) * Hkv + W + 8 * pkv::kWaves) * 64 > INT32_MAX)
     return PKV_ERR_UNSUPPORTED;
   const Layout L = stream_layout(B, Hq, Hkv, hd, kernel, W, static_cast<int64_t>(B) * L0.H + pv.cells);
   if (!workspace || workspace_bytes < L.bytes) return PKV_ERR_WORKSPACE;
@@ -546,7 +548,8 @@ pkv_status pkv_prefill_attn(int32_t pass, void* out, const void* q, const void* 
   if (!pkv::prefill_plan_check(plan_host, plan_ints, T, S, max_blocks, max_context_len, Hkv, G,
                                pkv::prefill_tile_rows(G), pkv::kPrefillMaxBlocks, &pv))
     return PKV_ERR_INVALID_ARG;
-  if (static_cast<int64_t>(pv.U) * Hkv >= (int64_t{1} << 31) - 8) return PKV_ERR_UNSUPPORTED;
+  // one work-group of 256 work-items per (unit, kv head): within 32-bit grid indexing
+  if (static_cast<int64_t>(pv.U) * Hkv * 256 > INT32_MAX) return PKV_ERR_UNSUPPORTED;
   const PrefillLayout L = prefill_layout(pv.cells, G, hd);
   if (L.bytes > 0 && (!workspace || workspace_bytes < L.bytes)) return PKV_ERR_WORKSPACE;
   if (L.bytes > 0 && !aligned16(workspace)) return PKV_ERR_INVALID_ARG;

@@ -253,6 +253,10 @@ hipError_t launch_stage_copy(const StageParams& sp, const CopyParams& cp, int32_
   const int32_t chunks = cp.Hkv * cp.hd * eb;
   const int32_t grid_y = (chunks + 256 * kCopyUnroll - 1) / (256 * kCopyUnroll);
   const int64_t grid = stage_wgs + static_cast<int64_t>(cp.n) * 2 * grid_y;
+  if (grid * 256 > INT32_MAX) {  // the flat grid would pass 32-bit indexing: launch apart
+    const hipError_t e = launch_stage(sp, stream);
+    return e != hipSuccess ? e : launch_copy_blocks(cp, dtype, stream);
+  }
   (void)hipGetLastError();
   hipLaunchKernelGGL(stage_copy_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream,
                      sp, static_cast<u32x4_t*>(cp.k_cache), static_cast<u32x4_t*>(cp.v_cache),

@@ -200,6 +200,30 @@ def test_corrupted_plans_are_refused_on_the_host():
     assert call(c, append=True) == 1
 
 
+def test_planned_grid_limit():
+    """A plan whose shared pass (one wave per unit and kv head) plus the stream workers would
+    pass 2^31 - 1 work-items is refused (PKV_ERR_UNSUPPORTED) before any device work; one unit
+    fewer passes every check and stops at the workspace (PKV_ERR_WORKSPACE)."""
+    B, H, W = 2, 16384, 64  # G = 1: the vector kernel, head slots = q heads
+    buf = (ctypes.c_uint8 * (1 << 16))()
+    fake = ctypes.c_void_p((ctypes.addressof(buf) + 255) & ~255)
+
+    def plan(U):
+        hdr = [0x504C4E31, B, H, 1, U, 1, 0, H, 16] + [0] * (HDR - 9)
+        skip, blocks, ptr = [1, 1], [1, 1], [0, 0, 0]
+        units = [0, 0, 1, 0, 1, 0] * U  # every unit: sequence 0's block 0, cells 0..H-1
+        return np.asarray(hdr + skip + blocks + ptr + units + [0], np.int32)
+
+    def call(q):
+        return lib.pkv_decode_planned(0, fake, fake, None, None, fake, fake, fake, fake, B, H,
+                                      H, 64, 16, 4, 1, 16, 0.1, 1, q.ctypes.data, fake, q.size,
+                                      W, fake, 0, None)
+    limit = (2**31 - 1) // 64 - W - 32  # largest units * Hkv allowed
+    ok = limit // H
+    assert call(plan(ok)) == 6
+    assert call(plan(ok + 1)) == 2
+
+
 @pytest.mark.parametrize("hq,hkv,runs", [(8, 8, True), (16, 4, True), (28, 4, False),
                                          (32, 2, False)])
 def test_default_group_threshold(hq, hkv, runs):
