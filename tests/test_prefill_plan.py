@@ -182,3 +182,26 @@ def test_corrupted_plans_are_refused_on_the_host():
     dp = p.copy()
     dp[0] = 0x504C4E31
     assert call(dp) == 1
+
+
+def test_prefill_grid_limit():
+    """A plan whose attention pass (one 256-work-item work-group per unit and kv head) would pass
+    2^31 - 1 work-items is refused (PKV_ERR_UNSUPPORTED) before any device work; one unit fewer
+    passes every check and stops at the workspace (PKV_ERR_WORKSPACE)."""
+    H = 16384  # MHA: kv heads = q heads, G = 1
+    buf = (ctypes.c_uint8 * (1 << 16))()
+    fake = ctypes.c_void_p((ctypes.addressof(buf) + 255) & ~255)
+
+    def plan(U):
+        hdr = [0x50524631, 1, H, 1, U, 1, 0, H, 1, 1, 128] + [0] * (16 - 11)
+        rows = [0] + [1] + [0, 0]  # skip[1], vis[1], ptr[2]
+        units = [0, 0, 1, 0, 1, 0] * U  # every unit: sequence 0's block 0, row 0, cells 0..H-1
+        return np.asarray(hdr + rows + units + [0], np.int32)
+
+    def call(q):
+        return lib.pkv_prefill_attn(0, fake, fake, fake, fake, fake, 1, 1, H, H, 64, 16, 4, 1,
+                                    16, 0.1, 1, q.ctypes.data, fake, q.size, fake, 0, None)
+    ok = ((2**31 - 1) // 256) // H
+    assert call(plan(ok)) == 6
+    assert call(plan(ok + 1)) == 2
+
